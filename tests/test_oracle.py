@@ -1,0 +1,24 @@
+"""The oracle against what the pages and mathematics fix (CPU only)."""
+import pytest
+
+import oracle.calculator as calc
+import oracle.verify as ov
+import oracle_pins as pins
+
+
+@pytest.mark.parametrize("pin", pins.ALL_ORACLE_PINS, ids=lambda f: f.__name__)
+def test_oracle_pin(pin):
+    pin(ov)
+
+
+@pytest.mark.parametrize("setting", pins.SETTINGS, ids=lambda s: "T%g-k%d-p%g" % (s["T"], s["top_k"], s["top_p"]))
+def test_chisq_emitted_tokens(setting):
+    pins.pin_chisq(ov, setting=setting)
+
+
+def test_constant_alpha_matches_calculator():
+    pins.pin_constant_alpha(ov, calc)
+
+
+def test_calculator():
+    pins.pin_calculator(calc)

@@ -1,0 +1,97 @@
+"""Planted mistakes in a copy of the oracle's source must fail a pin (CPU only).
+
+Each mutant is a one-line slip a careful author could make -- a flipped
+ratio, a wrong sign, an off-by-one, a dropped term, a wrong tie rule.  The
+mutated source is executed into a fresh module and the pins of
+oracle_pins.py run against it; the test passes when some pin rejects it.
+"""
+import types
+
+import pytest
+
+import oracle.calculator as calc
+import oracle.verify as real
+import oracle_pins as pins
+
+SRC = open(real.__file__).read()
+
+MUTANTS = [
+    ("accept ratio inverted", "ratio = a / b", "ratio = b / a"),
+    ("accept test reversed", "accept = u < min(1.0, ratio)", "accept = u > min(1.0, ratio)"),
+    ("residual sign flipped", "r = np.maximum(0.0, p_rows[n] - q_rows[n])",
+     "r = np.maximum(0.0, q_rows[n] - p_rows[n])"),
+    ("resample from p, not the residual", "r = np.maximum(0.0, p_rows[n] - q_rows[n])", "r = p_rows[n].copy()"),
+    ("clip dropped from the residual", "r = np.maximum(0.0, p_rows[n] - q_rows[n])",
+     "r = np.abs(p_rows[n] - q_rows[n])"),
+    ("bonus from the wrong row", "        r = p_rows[k].copy()", "        r = p_rows[k - 1].copy()"),
+    ("target row off by one in the test", "a = p_rows[j][x]", "a = p_rows[j + 1][x]"),
+    ("no stop at the first rejection", "        if not accept:\n            n = j\n            break",
+     "        if not accept:\n            n = j"),
+    ("zero-q draft always rejected", "            accept = a > 0.0", "            accept = False"),
+    ("empty-residual fallback not p", "        if r.sum() == 0.0:\n            r = p_rows[n].copy()",
+     "        if r.sum() == 0.0:\n            r = np.ones(V)"),
+    ("inverse CDF takes the left boundary", 'side="right"', 'side="left"'),
+    ("temperature multiplies", "/ np.float64(temperature)", "* np.float64(temperature)"),
+    ("ties go to the higher index", "np.lexsort((idx, -values))", "np.lexsort((-idx, -values))"),
+    ("nucleus keeps <= top_p", "kept_sorted = before < np.float64(top_p)", "kept_sorted = before <= np.float64(top_p)"),
+    ("nucleus uses inclusive mass", "before = np.concatenate(([0.0], csum[:-1]))", "before = csum"),
+    ("nucleus not renormalised", "        P = np.where(nuc, P, 0.0)\n        P = P / P.sum()",
+     "        P = np.where(nuc, P, 0.0)"),
+    ("top-k keeps one too many", "keep[order[:top_k]] = True", "keep[order[:top_k + 1]] = True"),
+    ("greedy compares with the next row", "        if x != g[j]:", "        if x != g[j + 1 if j + 1 <= k else j]:"),
+    ("greedy correction from row 0", "    tokens = [int(t) for t in draft_tokens[:n]] + [g[n]]",
+     "    tokens = [int(t) for t in draft_tokens[:n]] + [g[0]]"),
+    ("tree ignores the ancestors", "acc[i] = acc[par] and t == g[par]", "acc[i] = t == g[par]"),
+    ("tree compares with its own row", "acc[i] = acc[par] and t == g[par]", "acc[i] = acc[par] and t == g[i]"),
+    ("tree depth ties go to the larger index", "if acc[i] and depth[i] > depth[best]:",
+     "if acc[i] and depth[i] >= depth[best]:"),
+    ("tree correction from the parent", "path_tokens = [int(tokens[i]) for i in path[1:]] + [g[best]]",
+     "path_tokens = [int(tokens[i]) for i in path[1:]] + [g[path[-2] if len(path) > 1 else best]]"),
+]
+
+CALC_SRC = open(calc.__file__).read()
+CALC_MUTANTS = [
+    ("E exponent off by one", "alpha ** (gamma + 1)", "alpha ** gamma"),
+    ("cost drops the target pass", "return gamma * c + 1.0", "return gamma * c"),
+    ("series one term short", "for _ in range(gamma + 1):", "for _ in range(gamma):"),
+    ("break-even inverted", "return k / (k + 1.0)", "return (k + 1.0) / k"),
+    ("scan keeps the last tie", "if s > best_s:", "if s >= best_s:"),
+]
+
+
+def _quick_pins():
+    return [
+        pins.pin_greedy_golden, pins.pin_tree_golden, pins.pin_transform_golden,
+        pins.pin_inverse_cdf_golden, pins.pin_flags, pins.pin_greedy_invariants,
+        pins.pin_tree_path_equals_chain, pins.pin_tree_bruteforce, pins.pin_transform_softmax,
+        pins.pin_transform_topk, pins.pin_topp_minimal, pins.pin_special_cases,
+        pins.pin_residual_properties,
+        lambda m: pins.pin_enumeration(m, reps=1),
+        lambda m: pins.pin_chisq(m, trials=6000),
+        lambda m: pins.pin_constant_alpha(m, calc, trials=800),
+    ]
+
+
+def _load_mutant(src, old, new, name):
+    assert src.count(old) == 1, ("mutation site not unique", old)
+    mod = types.ModuleType("mutant_" + name.replace(" ", "_"))
+    exec(compile(src.replace(old, new), mod.__name__, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_verify_mutant_is_caught(name, old, new):
+    mod = _load_mutant(SRC, old, new, name)
+    for pin in _quick_pins():
+        try:
+            pin(mod)
+        except Exception:
+            return
+    pytest.fail("mutant survived every pin: " + name)
+
+
+@pytest.mark.parametrize("name,old,new", CALC_MUTANTS, ids=[m[0] for m in CALC_MUTANTS])
+def test_calculator_mutant_is_caught(name, old, new):
+    mod = _load_mutant(CALC_SRC, old, new, name)
+    with pytest.raises(Exception):
+        pins.pin_calculator(mod)
