@@ -88,7 +88,8 @@ def transform_row(logits: np.ndarray, temperature: float, top_k: int = 0,
       2. top_k > 0: keep exactly top_k entries under (z desc, index asc);
          the rest get probability 0
       3. softmax over the kept entries: m = max z, e = exp(z - m), P = e / sum e
-      4. top_p < 1: order by (P desc, index asc); keep the entry at rank r iff
+      4. top_p < 1: order by (P desc, index asc) -- computed as (z desc,
+         index asc), the same order in exact arithmetic; keep the entry at rank r iff
          the mass strictly before rank r is < top_p (the smallest prefix whose
          mass reaches top_p; rank 0 is always kept); renormalise
 
@@ -108,7 +109,10 @@ def transform_row(logits: np.ndarray, temperature: float, top_k: int = 0,
     P = e / e.sum()
     cut = None
     if top_p < 1.0:
-        order = rank_order(P)
+        # rank by z (exp is strictly increasing, so this is the probability
+        # order of exact arithmetic; ranking the rounded float64 P could tie
+        # two distinct logits)
+        order = rank_order(zk)
         Ps = P[order]
         csum = np.cumsum(Ps)                       # inclusive, sequential float64
         before = np.concatenate(([0.0], csum[:-1]))  # mass strictly before each rank
