@@ -1,0 +1,301 @@
+// C ABI of the verification library: argument validation (host only, before
+// any HIP call), workspace ownership, and the launch sequence per mode.
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "specverify.h"
+#include "sv_internal.h"
+
+namespace {
+
+constexpr int kMinTile = 8192;        // logits per tile, lower bound (4 groups per lane)
+constexpr int kTargetBlocks = 2048;   // workgroups the streaming pass aims for
+
+struct Plan {
+  int filt;        // sv::Filter
+  int tile_mode;   // sv::TileMode
+  int top_k;       // effective top-k (0 = off)
+  double top_p;    // effective top-p (1 = off)
+  int rows_t, rows_d, out_w;
+  int S_max;       // largest tile count per row the workspace holds
+  int S2_max;      // residual segments per sequence (plain sampling)
+  int cand_w;
+};
+
+int check_config(const sv_config* c) {
+  if (!c) return SV_ERR_NULL;
+  if (c->mode != SV_MODE_SAMPLE && c->mode != SV_MODE_GREEDY && c->mode != SV_MODE_TREE_GREEDY)
+    return SV_ERR_MODE;
+  if (c->dtype != SV_DTYPE_F32 && c->dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
+  if (c->max_batch < 1 || c->vocab < 1 || c->vocab > SV_MAX_VOCAB) return SV_ERR_SHAPE;
+  if (c->mode == SV_MODE_TREE_GREEDY) {
+    if (c->k < 1 || c->k > SV_MAX_TREE_NODES) return SV_ERR_SHAPE;
+  } else {
+    if (c->k < 1 || c->k > SV_MAX_K) return SV_ERR_SHAPE;
+  }
+  if (c->mode == SV_MODE_SAMPLE) {
+    if (!(c->temperature > 0.0) || !isfinite(c->temperature)) return SV_ERR_PARAM;
+    if (c->top_k < 0) return SV_ERR_PARAM;
+    if (c->top_k > SV_MAX_TOP_K && c->top_k < c->vocab) return SV_ERR_PARAM;
+    if (!(c->top_p > 0.0 && c->top_p <= 1.0)) return SV_ERR_PARAM;
+  }
+  return SV_OK;
+}
+
+Plan make_plan(const sv_config* c) {
+  Plan p;
+  const bool sample = c->mode == SV_MODE_SAMPLE;
+  p.top_k = (sample && c->top_k > 0 && c->top_k < c->vocab) ? c->top_k : 0;
+  p.top_p = (sample && c->top_p < 1.0) ? c->top_p : 1.0;
+  if (c->mode == SV_MODE_GREEDY) { p.filt = sv::kFiltGreedy; p.tile_mode = sv::kModeArgmax; }
+  else if (c->mode == SV_MODE_TREE_GREEDY) { p.filt = sv::kFiltTree; p.tile_mode = sv::kModeArgmax; }
+  else if (p.top_k > 0) { p.filt = sv::kFiltTopk; p.tile_mode = sv::kModeTopk; }
+  else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeArgmax; }
+  else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats; }
+  if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
+  else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
+  p.S_max = (c->vocab + kMinTile - 1) / kMinTile;
+  p.cand_w = p.top_k;
+  if (p.top_k > 0) {
+    const int cap = sv::kMergeCap / p.cand_w;
+    if (p.S_max > cap) p.S_max = cap;
+  }
+  if (p.S_max < 1) p.S_max = 1;
+  p.S2_max = (c->vocab + sv::kResidSeg - 1) / sv::kResidSeg;
+  return p;
+}
+
+struct Layout {
+  size_t tiles, cand, nuc, counters, counters_bytes, seq_n, seq_st, seq_M, zpart, spart;
+  size_t k_idx, k_e, k_cnt, k_norm, k_bad, total;
+};
+
+Layout layout(const sv_config* c, const Plan& pl) {
+  const size_t B = (size_t)c->max_batch;
+  const size_t rows = B * (size_t)(pl.rows_t + pl.rows_d);
+  const size_t K = (size_t)pl.top_k;
+  Layout L;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = (off + bytes + 255) & ~(size_t)255;
+    return at;
+  };
+  L.tiles = take(rows * (size_t)pl.S_max * sizeof(sv::TileStat));
+  L.cand = take(pl.top_k > 0 ? rows * (size_t)pl.S_max * (size_t)pl.cand_w * sizeof(uint64_t) : 0);
+  L.nuc = take(pl.filt == sv::kFiltTopp ? rows * sizeof(sv::RowNuc) : 0);
+  L.counters_bytes = (2 * B + rows) * sizeof(unsigned);
+  L.counters = take(L.counters_bytes);
+  const bool plain = pl.filt == sv::kFiltNone;
+  L.seq_n = take(B * sizeof(int));
+  L.seq_st = take(B * sizeof(int));
+  L.seq_M = take(B * 2 * sizeof(float));
+  L.zpart = take(plain ? B * (size_t)pl.S2_max * 2 * sizeof(double) : 0);
+  L.spart = take(plain ? B * (size_t)pl.S2_max * sizeof(double) : 0);
+  L.k_idx = take(rows * K * sizeof(int32_t));
+  L.k_e = take(rows * K * sizeof(double));
+  L.k_cnt = take(K ? rows * sizeof(int32_t) : 0);
+  L.k_norm = take(K ? rows * sizeof(double) : 0);
+  L.k_bad = take(K ? rows * sizeof(int32_t) : 0);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+struct specverify_ctx {
+  sv_config cfg;
+  Plan plan;
+  int device;
+  void* ws;
+  size_t ws_bytes;
+  Layout L;
+  hipEvent_t ev_begin, ev_end;   // optional instrumentation (caller-owned)
+};
+
+extern "C" {
+
+const char* specverify_status_string(int status) {
+  switch (status) {
+    case SV_OK: return "SV_OK";
+    case SV_ERR_NULL: return "SV_ERR_NULL: a required pointer is NULL";
+    case SV_ERR_SHAPE: return "SV_ERR_SHAPE: batch, k or vocab out of range";
+    case SV_ERR_DTYPE: return "SV_ERR_DTYPE: unknown dtype";
+    case SV_ERR_PARAM: return "SV_ERR_PARAM: temperature, top_k or top_p out of range";
+    case SV_ERR_CAPACITY: return "SV_ERR_CAPACITY: batch exceeds max_batch";
+    case SV_ERR_HIP: return "SV_ERR_HIP: a HIP call failed";
+    case SV_ERR_MODE: return "SV_ERR_MODE: unknown mode, or a pointer that does not fit the mode";
+    default: return "unknown status";
+  }
+}
+
+size_t specverify_workspace_bytes(const sv_config* cfg) {
+  if (check_config(cfg) != SV_OK) return 0;
+  const Plan pl = make_plan(cfg);
+  return layout(cfg, pl).total;
+}
+
+int specverify_check_args(const sv_config* cfg, int32_t batch, const void* target_logits,
+                          const void* draft_logits, const int32_t* draft_tokens,
+                          const int32_t* parents, const float* uniforms,
+                          const float* resid_uniforms, const int32_t* accepted_len,
+                          const int32_t* out_tokens, const int32_t* out_nodes) {
+  const int rc = check_config(cfg);
+  if (rc != SV_OK) return rc;
+  if (batch < 0) return SV_ERR_SHAPE;
+  if (batch > cfg->max_batch) return SV_ERR_CAPACITY;
+  if (batch == 0) return SV_OK;   // nothing to read or write; pointers may be NULL
+  if (!target_logits || !draft_tokens || !accepted_len || !out_tokens) return SV_ERR_NULL;
+  switch (cfg->mode) {
+    case SV_MODE_SAMPLE:
+      if (!draft_logits || !uniforms || !resid_uniforms) return SV_ERR_NULL;
+      if (parents || out_nodes) return SV_ERR_MODE;
+      break;
+    case SV_MODE_GREEDY:
+      if (draft_logits || parents || uniforms || resid_uniforms || out_nodes) return SV_ERR_MODE;
+      break;
+    default:  // tree
+      if (!parents) return SV_ERR_NULL;
+      if (draft_logits || uniforms || resid_uniforms) return SV_ERR_MODE;
+      break;
+  }
+  return SV_OK;
+}
+
+int specverify_create(const sv_config* cfg, int device, specverify_ctx** out) {
+  if (!out) return SV_ERR_NULL;
+  *out = nullptr;
+  const int rc = check_config(cfg);
+  if (rc != SV_OK) return rc;
+  specverify_ctx* ctx = (specverify_ctx*)calloc(1, sizeof(specverify_ctx));
+  if (!ctx) return SV_ERR_HIP;
+  ctx->cfg = *cfg;
+  ctx->plan = make_plan(cfg);
+  ctx->device = device;
+  const Layout L = layout(cfg, ctx->plan);
+  ctx->ws_bytes = L.total;
+  if (hipSetDevice(device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
+  ctx->L = L;
+  if (hipMalloc(&ctx->ws, L.total) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
+  // the "last workgroup" counters start at zero and every call leaves them at zero
+  if (hipMemset((char*)ctx->ws + L.counters, 0, L.counters_bytes) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    (void)hipFree(ctx->ws);
+    free(ctx);
+    return SV_ERR_HIP;
+  }
+  *out = ctx;
+  return SV_OK;
+}
+
+void specverify_destroy(specverify_ctx* ctx) {
+  if (!ctx) return;
+  if (ctx->ws) {
+    int cur = -1;
+    (void)hipGetDevice(&cur);
+    if (cur != ctx->device) (void)hipSetDevice(ctx->device);
+    (void)hipFree(ctx->ws);
+    if (cur >= 0 && cur != ctx->device) (void)hipSetDevice(cur);
+  }
+  free(ctx);
+}
+
+int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_end) {
+  if (!ctx) return SV_ERR_NULL;
+  if ((ev_begin == nullptr) != (ev_end == nullptr)) return SV_ERR_NULL;
+  ctx->ev_begin = (hipEvent_t)ev_begin;
+  ctx->ev_end = (hipEvent_t)ev_end;
+  return SV_OK;
+}
+
+int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits,
+                   const void* draft_logits, const int32_t* draft_tokens, const int32_t* parents,
+                   const float* uniforms, const float* resid_uniforms, int32_t* accepted_len,
+                   int32_t* out_tokens, int32_t* out_nodes, float* resid_probs,
+                   int32_t* seq_status, void* stream) {
+  if (!ctx) return SV_ERR_NULL;
+  const sv_config* c = &ctx->cfg;
+  int rc = specverify_check_args(c, batch, target_logits, draft_logits, draft_tokens, parents,
+                                 uniforms, resid_uniforms, accepted_len, out_tokens, out_nodes);
+  if (rc != SV_OK) return rc;
+  if (resid_probs && c->mode != SV_MODE_SAMPLE) return SV_ERR_MODE;
+  if (batch == 0) return SV_OK;
+  const Plan& pl = ctx->plan;
+
+  sv::Params p;
+  memset(&p, 0, sizeof(p));
+  p.target = target_logits;
+  p.draft = draft_logits;
+  p.tokens = draft_tokens;
+  p.parents = parents;
+  p.u = uniforms;
+  p.ur = resid_uniforms;
+  p.acc_len = accepted_len;
+  p.out_tokens = out_tokens;
+  p.out_nodes = out_nodes;
+  p.resid_probs = resid_probs;
+  p.seq_status = seq_status;
+  p.B = batch;
+  p.k = c->k;
+  p.V = c->vocab;
+  p.rows_t = pl.rows_t;
+  p.rows_d = pl.rows_d;
+  p.out_w = pl.out_w;
+  p.T = c->mode == SV_MODE_SAMPLE ? c->temperature : 1.0;
+  p.top_p = pl.top_p;
+  p.top_k = pl.top_k;
+  // tiling: enough workgroups to fill the chip, tiles of at least kMinTile logits
+  const long rows = (long)batch * (pl.rows_t + pl.rows_d);
+  long S = (kTargetBlocks + rows - 1) / rows;
+  if (S > pl.S_max) S = pl.S_max;
+  if (S < 1) S = 1;
+  const int per = (int)((c->vocab + S - 1) / S);
+  p.L = (per + sv::kVec - 1) / sv::kVec * sv::kVec;
+  p.S = (c->vocab + p.L - 1) / p.L;
+  const size_t es = c->dtype == SV_DTYPE_BF16 ? 2 : 4;
+  const bool rows16 = ((size_t)c->vocab * es) % 16 == 0;
+  const bool base16 = ((uintptr_t)target_logits % 16 == 0) &&
+                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0);
+  p.aligned = (rows16 && base16) ? 1 : 0;
+  char* ws = (char*)ctx->ws;
+  const Layout& L = ctx->L;
+  const size_t B = (size_t)c->max_batch;
+  const size_t maxrows = B * (size_t)(pl.rows_t + pl.rows_d);
+  p.tiles = (sv::TileStat*)(ws + L.tiles);
+  p.cand = (uint64_t*)(ws + L.cand);
+  p.cand_w = pl.cand_w;
+  p.nuc = (sv::RowNuc*)(ws + L.nuc);
+  p.seq_cnt = (unsigned*)(ws + L.counters);
+  p.aux_cnt = p.seq_cnt + B;
+  p.row_cnt = p.aux_cnt + B;
+  (void)maxrows;
+  p.seq_n = (int*)(ws + L.seq_n);
+  p.seq_st = (int*)(ws + L.seq_st);
+  p.seq_M = (float*)(ws + L.seq_M);
+  p.zpart = (double*)(ws + L.zpart);
+  p.spart = (double*)(ws + L.spart);
+  p.S2 = pl.S2_max;
+  p.k_idx = (int32_t*)(ws + L.k_idx);
+  p.k_e = (double*)(ws + L.k_e);
+  p.k_cnt = (int32_t*)(ws + L.k_cnt);
+  p.k_norm = (double*)(ws + L.k_norm);
+  p.k_bad = (int32_t*)(ws + L.k_bad);
+
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_HIP;
+  if (cur != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
+  hipStream_t st = (hipStream_t)stream;
+  const int bf16 = c->dtype == SV_DTYPE_BF16;
+  hipError_t e = hipSuccess;
+  if (ctx->ev_begin) e = hipEventRecord(ctx->ev_begin, st);
+  if (e == hipSuccess) e = sv::launch_stream(p, pl.filt, bf16, st);
+  if (e == hipSuccess && ctx->ev_end) e = hipEventRecord(ctx->ev_end, st);
+  if (e == hipSuccess && pl.filt == sv::kFiltTopp) e = sv::launch_topp_rows(p, bf16, st);
+  if (e == hipSuccess && pl.filt == sv::kFiltNone) e = sv::launch_resid(p, bf16, st);
+  if (cur != ctx->device) (void)hipSetDevice(cur);
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+}  // extern "C"

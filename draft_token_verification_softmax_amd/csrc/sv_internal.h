@@ -1,0 +1,110 @@
+// Internal declarations shared by the host dispatcher (sv_api.cpp) and the
+// gfx950 kernels (sv_kernels.hip).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kBlock = 256;            // threads per workgroup (4 wave64s)
+constexpr int kVec = 8;                // logits per group: 16 B of bf16, 32 B of fp32
+constexpr int kTopkCap = 4096;         // LDS candidate slots of the top-k tile kernel
+constexpr int kMergeCap = 4096;        // LDS slots when merging a row's top-k candidates
+constexpr int kWindowCap = 2048;       // LDS slots for the nucleus boundary window
+constexpr int kNucBins = 2048;         // histogram bins of the nucleus search
+constexpr int kResidSeg = kBlock * kVec;  // logits per workgroup in the residual kernels
+
+// Per-tile partial result of the streaming pass.
+//   m    max raw logit of the tile (NaN ignored; -inf if none)
+//   amax lowest index holding m (INT32_MAX if none)
+//   s    STATS mode: sum over the tile of exp((l - m) / T), accumulated in
+//        float64 from float32 exponentials; other modes: a probe that is NaN
+//        iff the tile holds a non-finite value (NaN, +inf or -inf)
+struct TileStat {
+  float m;
+  int32_t amax;
+  double s;
+};
+
+// Per-row nucleus (top-p) result.
+//   Z      sum_v exp(z_v - zmax) in float64 (z = l / T)
+//   N      mass of the kept set (same units); p'(v) = exp(z_v - zmax) / N on the set
+//   cut    packed (value, index) key of the last kept entry: v is kept iff
+//          pack(l_v, v) >= cut, i.e. it ranks at or before the cut in
+//          (value desc, index asc) order
+//   ok     1 found; 0 the row is invalid (NaN / +inf / all -inf); 2 the search
+//          did not settle (not expected)
+struct RowNuc {
+  double Z;
+  double N;
+  uint64_t cut;
+  int32_t ok;
+  float M;      // max raw logit of the row
+};
+
+enum TileMode { kModeArgmax = 0, kModeStats = 1, kModeTopk = 2 };
+enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4 };
+
+struct Params {
+  // inputs
+  const void* target;
+  const void* draft;
+  const int32_t* tokens;
+  const int32_t* parents;
+  const float* u;
+  const float* ur;
+  // outputs
+  int32_t* acc_len;
+  int32_t* out_tokens;
+  int32_t* out_nodes;
+  float* resid_probs;
+  int32_t* seq_status;
+  // shape
+  int B;        // batch
+  int k;        // chain: drafts per sequence; tree: nodes per tree
+  int V;
+  int rows_t;   // target rows per sequence (k+1, or N for a tree)
+  int rows_d;   // draft rows per sequence (k in SAMPLE mode, else 0)
+  int out_w;    // width of out_tokens rows (k+1 chain, N tree)
+  // sampling settings
+  double T;
+  double top_p;
+  int top_k;    // 0 = off
+  // tiling of the streaming pass
+  int S;        // tiles per row
+  int L;        // logits per tile (multiple of kVec)
+  int aligned;  // every row starts 16-byte aligned
+  // workspace
+  TileStat* tiles;   // [rows][S]
+  uint64_t* cand;    // [rows][S][cand_w] (top-k)
+  int cand_w;        // candidate slots per tile (top_k rounded up)
+  RowNuc* nuc;       // [rows] (top-p)
+  // "last workgroup" counters (zero between calls)
+  unsigned* seq_cnt; // [B]
+  unsigned* row_cnt; // [rows]
+  unsigned* aux_cnt; // [B]
+  // plain sampling: state handed from the accept step to the residual kernels
+  int* seq_n;        // [B] accepted count n, or -1 if the sequence is already emitted
+  int* seq_st;       // [B] status bits found by the accept step
+  float* seq_M;      // [B][2] max raw logit of target row n and draft row n
+  double* zpart;     // [B][S2][2] float64 row-sum partials of those rows
+  double* spart;     // [B][S2] residual-mass partials
+  int S2;            // residual segments per sequence (kResidSeg logits each)
+  // top-k: each row's kept set, rank order
+  int32_t* k_idx;    // [rows][top_k]
+  double* k_e;       // [rows][top_k] exp(z - zmax)
+  int32_t* k_cnt;    // [rows] entries kept (after the nucleus, if any)
+  double* k_norm;    // [rows] sum of k_e over the kept entries
+  int32_t* k_bad;    // [rows] 1 if the row is invalid
+};
+
+// Launchers (sv_kernels.hip).  Each returns the hipError_t of its launch.
+// launch_stream: the streaming pass, with the epilogue of `filt` run by the
+// last workgroup of each row / sequence (greedy, tree, top-k: the whole call;
+// plain sampling: the accept step; nucleus: none).
+hipError_t launch_stream(const Params& p, int filt, int bf16, hipStream_t st);
+hipError_t launch_topp_rows(const Params& p, int bf16, hipStream_t st);
+hipError_t launch_resid(const Params& p, int bf16, hipStream_t st);
+
+}  // namespace sv

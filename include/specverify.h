@@ -1,0 +1,178 @@
+/*
+ * specverify -- the verification step of speculative decoding on MI355X (gfx950).
+ *
+ * What one call computes (per sequence b of a batch):
+ *
+ *   SV_MODE_SAMPLE -- modified rejection sampling.  Source: the
+ *     edgeinferencenotes.hashnode.dev speculative-decoding / EAGLE-3 article,
+ *     section "The core idea: draft, then check": with p the target's and q the
+ *     draft's probability of a drafted token, accept it outright if p >= q and
+ *     otherwise with probability p/q; at the first rejection drop the rest and
+ *     draw one replacement from the leftover mass max(0, p - q) renormalised;
+ *     if all k drafts are accepted, draw one bonus token from the target's
+ *     last row.  Section "Why it changes nothing about the output": temperature,
+ *     top-k and nucleus (top-p) apply to both distributions before the test.
+ *       p'_j = adjust(target row j), q'_j = adjust(draft row j) with
+ *       adjust = z = logits / T, then top-k (exactly top_k entries by value,
+ *       lower index first on ties), then softmax, then top-p (the smallest
+ *       prefix in (probability desc, index asc) order whose mass reaches
+ *       top_p), renormalised.
+ *       accept draft j iff  q'_j(x_j) > 0 and u_j < min(1, p'_j(x_j)/q'_j(x_j)),
+ *                       or  q'_j(x_j) = 0 and p'_j(x_j) > 0.
+ *       n = first rejected j (k if none).  Replacement / bonus drawn with the
+ *       per-sequence uniform ur as y = min{v : C_v > ur * C_{V-1}}, C the
+ *       running sum of r = max(0, p'_n - q'_n) (n < k; p'_n if that is all
+ *       zero) or r = p'_k (n = k), in vocabulary order.
+ *       Emitted: x_0 .. x_{n-1}, y.
+ *
+ *   SV_MODE_GREEDY -- greedy longest agreed prefix.  Source: "Towards Green
+ *     Text Generation: Memory-Based Speculative Decoding", section 1 and
+ *     section 2.4 "Verifier and Acceptance": the logits of the k+1 positions
+ *     are compared greedily with the drafts; a draft is accepted iff it equals
+ *     the verifier's argmax (token-ID level).  g_j = argmax row j (lower index
+ *     on ties); n = first j with x_j != g_j (k if none); emitted x_0..x_{n-1}, g_n.
+ *
+ *   SV_MODE_TREE_GREEDY -- greedy token-tree verification.  Source: the same
+ *     article, section "One decode round, end to end": the flattened tree is
+ *     scored in one target pass, the accept-or-correct rule is applied down
+ *     the branches, the longest agreed path is committed plus one correction.
+ *     Node 0 is the root; parents[i] < i; row i is the target's distribution
+ *     for node i's children.  Node i is accepted iff its parent is accepted
+ *     and tokens[i] == argmax(row parents[i]).  d* = accepted node of largest
+ *     depth (smallest index on ties).  Emitted: the tokens on the path root ->
+ *     d* (root excluded), then argmax(row d*).
+ *
+ * Layout: all arrays are dense, row-major, vocabulary fastest, and live in
+ * device memory on the context's device.  Logits are float32 or bf16 (raw
+ * 16-bit patterns).  Tokens and outputs are int32; uniforms are float32 in
+ * [0, 1).  The library reads inputs and writes outputs only; the caller owns
+ * every buffer passed in.  The context owns a device workspace sized at
+ * create time from max_batch, k and vocab.
+ *
+ * Errors: every function returns SV_OK (0) or a negative SV_ERR_* code and
+ * never aborts.  Argument errors are found on the host before any HIP call
+ * and leave the stream untouched.  Bad data inside device buffers never
+ * traps: it sets per-sequence bits in seq_status (SV_STATUS_*):
+ *   BAD_TOKEN   a drafted / tree token outside [0, V): treated as rejected
+ *   BAD_PARENT  parents[i] not in [0, i) (or parents[0] != -1): node unreachable
+ *   BAD_LOGITS  a row the mode reads holds NaN or +inf, or only -inf: the
+ *               sequence emits nothing (accepted_len 0, outputs all -1)
+ * specverify_run is asynchronous on the given stream and does no host
+ * synchronisation; outputs are valid once the stream has reached the call.
+ * One context must not be used by two streams at the same time.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct specverify_ctx specverify_ctx;   /* opaque; owns the workspace only */
+
+enum { SV_MODE_SAMPLE = 0, SV_MODE_GREEDY = 1, SV_MODE_TREE_GREEDY = 2 };
+enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 };
+enum {
+  SV_OK = 0,
+  SV_ERR_NULL = -1,      /* a required pointer is NULL */
+  SV_ERR_SHAPE = -2,     /* batch / k / vocab out of range */
+  SV_ERR_DTYPE = -3,     /* unknown dtype */
+  SV_ERR_PARAM = -4,     /* temperature <= 0 or not finite, top_k < 0 or too large, top_p not in (0, 1] */
+  SV_ERR_CAPACITY = -5,  /* batch > max_batch */
+  SV_ERR_HIP = -6,       /* a HIP call failed (allocation, launch, no device) */
+  SV_ERR_MODE = -7,      /* unknown mode, or a pointer given / missing for this mode */
+};
+enum { SV_STATUS_BAD_TOKEN = 1, SV_STATUS_BAD_PARENT = 2, SV_STATUS_BAD_LOGITS = 4 };
+
+/* Limits checked by create / check_args. */
+#define SV_MAX_K 64          /* chain: drafted tokens per sequence */
+#define SV_MAX_TREE_NODES 1024
+#define SV_MAX_TOP_K 256
+#define SV_MAX_VOCAB (1 << 24)
+
+typedef struct {
+  int32_t mode;          /* SV_MODE_* */
+  int32_t dtype;         /* SV_DTYPE_* of both logit tensors */
+  int32_t max_batch;     /* upper bound on the batch passed to run (>= 1) */
+  int32_t k;             /* chain: drafted tokens k (1..SV_MAX_K); tree: node count N incl. root */
+  int32_t vocab;         /* V (1..SV_MAX_VOCAB) */
+  double temperature;    /* SAMPLE: T > 0 (logits are divided by T in float64); ignored otherwise */
+  int32_t top_k;         /* SAMPLE: 0 = off, else 1..SV_MAX_TOP_K (>= V acts as off) */
+  double top_p;          /* SAMPLE: 1.0 = off, else in (0, 1) */
+} sv_config;
+
+/* Validate cfg, select `device`, allocate the workspace.  On success *out
+ * holds a new context.  Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE,
+ * SV_ERR_PARAM, SV_ERR_MODE (no HIP call made), SV_ERR_HIP. */
+int specverify_create(const sv_config* cfg, int device, specverify_ctx** out);
+
+/* Host-only argument check that specverify_run performs first; makes no HIP
+ * call, so it can run anywhere.  Pointers are only tested for NULL-ness
+ * against what `cfg->mode` needs:
+ *   SAMPLE: target, draft, draft_tokens, uniforms, resid_uniforms, accepted_len,
+ *           out_tokens required; parents and out_nodes must be NULL.
+ *   GREEDY: target, draft_tokens, accepted_len, out_tokens required; draft,
+ *           parents, uniforms, resid_uniforms, out_nodes must be NULL.
+ *   TREE_GREEDY: target, draft_tokens (the node tokens), parents, accepted_len,
+ *           out_tokens required; draft, uniforms, resid_uniforms must be NULL;
+ *           out_nodes optional.
+ * batch = 0 is valid (nothing to do; every pointer may then be NULL);
+ * batch > cfg->max_batch is SV_ERR_CAPACITY. */
+int specverify_check_args(const sv_config* cfg, int32_t batch,
+                          const void* target_logits, const void* draft_logits,
+                          const int32_t* draft_tokens, const int32_t* parents,
+                          const float* uniforms, const float* resid_uniforms,
+                          const int32_t* accepted_len, const int32_t* out_tokens,
+                          const int32_t* out_nodes);
+
+/* Verify one batch.  Shapes (B = batch, k and V from the context's config):
+ *   target_logits  [B, k+1, V] chain | [B, N, V] tree      dtype per config
+ *   draft_logits   [B, k, V]   SAMPLE only
+ *   draft_tokens   [B, k] chain | [B, N] tree (entry 0, the root, is ignored)
+ *   parents        [B, N]      TREE_GREEDY only; parents[b, 0] = -1, parents[b, i] < i
+ *   uniforms       [B, k]      SAMPLE: accept-test uniforms u_j
+ *   resid_uniforms [B]         SAMPLE: the one uniform for the replacement OR bonus draw
+ *   accepted_len   [B]    out: n (tree: depth of the deepest accepted node)
+ *   out_tokens     [B, k+1] chain | [B, N] tree   out: n accepted tokens, then the
+ *                             replacement / bonus / correction; remaining entries -1
+ *   out_nodes      [B, N]  out, tree only, optional: node ids of the path root..d*
+ *                             (out_nodes[b, i] is the node whose row gave out_tokens[b, i]); rest -1
+ *   resid_probs    [B, V]  out, SAMPLE only, optional (debug): the normalised distribution
+ *                             the last token was drawn from (residual, or p'_k after full acceptance)
+ *   seq_status     [B]     out, optional: SV_STATUS_* bits
+ *   stream         hipStream_t the work is queued on (NULL = default stream)
+ * Returns SV_OK once the work is queued. */
+int specverify_run(specverify_ctx* ctx, int32_t batch,
+                   const void* target_logits, const void* draft_logits,
+                   const int32_t* draft_tokens, const int32_t* parents,
+                   const float* uniforms, const float* resid_uniforms,
+                   int32_t* accepted_len, int32_t* out_tokens, int32_t* out_nodes,
+                   float* resid_probs, int32_t* seq_status, void* stream);
+
+/* Free the workspace and the context.  NULL is allowed.  The caller must make
+ * sure no queued call still uses the context. */
+void specverify_destroy(specverify_ctx* ctx);
+
+/* Instrumentation for benchmarks: on every later specverify_run of this
+ * context, record the HIP event `ev_begin` on the run's stream just before
+ * the streaming kernel (the one pass that reads every logit) and `ev_end`
+ * just after it, so hipEventElapsedTime gives that kernel's duration.  The
+ * events are caller-owned hipEvent_t handles created on the context's device;
+ * pass NULL, NULL to stop.  Nothing is skipped or reordered.  Errors:
+ * SV_ERR_NULL (ctx NULL, or exactly one event NULL). */
+int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_end);
+
+/* Human-readable name of an SV_OK / SV_ERR_* code (static storage). */
+const char* specverify_status_string(int status);
+
+/* Workspace bytes specverify_create would allocate for cfg (0 if cfg is invalid). */
+size_t specverify_workspace_bytes(const sv_config* cfg);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

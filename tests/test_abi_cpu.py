@@ -1,0 +1,156 @@
+"""The C-ABI library on the host: it loads, exports every function the header
+declares, and rejects bad arguments before any HIP call (no GPU needed)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import draft_token_verification_softmax_amd as svm
+from draft_token_verification_softmax_amd import (
+    SV_DTYPE_BF16, SV_DTYPE_F32, SV_ERR_CAPACITY, SV_ERR_DTYPE, SV_ERR_MODE, SV_ERR_NULL,
+    SV_ERR_PARAM, SV_ERR_SHAPE, SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_TREE_GREEDY, SV_OK,
+    make_config, specverify_check_args)
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "specverify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(specverify_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_function():
+    lib = svm.load()
+    names = declared_functions()
+    assert len(names) == 7
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(svm.EXPORTED) == names
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name in ("SV_MAX_K", "SV_MAX_TREE_NODES", "SV_MAX_TOP_K"):
+        m = re.search(r"#define %s (\d+)" % name, text)
+        assert int(m.group(1)) == getattr(svm, name)
+    for name in ("SV_ERR_NULL", "SV_ERR_SHAPE", "SV_ERR_DTYPE", "SV_ERR_PARAM", "SV_ERR_CAPACITY",
+                 "SV_ERR_HIP", "SV_ERR_MODE"):
+        m = re.search(r"%s = (-\d+)" % name, text)
+        assert int(m.group(1)) == getattr(svm, name)
+
+
+def test_config_struct_layout():
+    assert ctypes.sizeof(svm.sv_config) == 48
+    assert svm.sv_config.temperature.offset == 24 and svm.sv_config.top_p.offset == 40
+    cfg = make_config(SV_MODE_SAMPLE, "bf16", 16, 5, 32000, 1.0)
+    assert svm.specverify_workspace_bytes(cfg) > 0
+    bad = make_config(SV_MODE_SAMPLE, "bf16", 16, 5, 32000, -1.0)
+    assert svm.specverify_workspace_bytes(bad) == 0
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert svm.specverify_status_string(st).startswith("SV_")
+    assert svm.specverify_status_string(-99) == "unknown status"
+
+
+P = 0x1000  # any non-NULL address: check_args never dereferences
+
+
+def sample_args(**over):
+    a = dict(target=P, draft=P, draft_tokens=P, parents=None, uniforms=P, resid_uniforms=P,
+             accepted_len=P, out_tokens=P, out_nodes=None)
+    a.update(over)
+    return a
+
+
+def check(cfg, batch=4, **args):
+    a = sample_args(**args)
+    return specverify_check_args(cfg, batch, a["target"], a["draft"], a["draft_tokens"], a["parents"],
+                                 a["uniforms"], a["resid_uniforms"], a["accepted_len"],
+                                 a["out_tokens"], a["out_nodes"])
+
+
+@pytest.mark.parametrize("over,want", [
+    (dict(), SV_OK),
+    (dict(mode=7), SV_ERR_MODE),
+    (dict(dtype=5), SV_ERR_DTYPE),
+    (dict(max_batch=0), SV_ERR_SHAPE),
+    (dict(vocab=0), SV_ERR_SHAPE),
+    (dict(vocab=(1 << 24) + 1), SV_ERR_SHAPE),
+    (dict(k=0), SV_ERR_SHAPE),
+    (dict(k=65), SV_ERR_SHAPE),
+    (dict(temperature=0.0), SV_ERR_PARAM),
+    (dict(temperature=-0.5), SV_ERR_PARAM),
+    (dict(temperature=math.nan), SV_ERR_PARAM),
+    (dict(temperature=math.inf), SV_ERR_PARAM),
+    (dict(top_k=-1), SV_ERR_PARAM),
+    (dict(top_k=257), SV_ERR_PARAM),
+    (dict(top_k=32000), SV_OK),            # >= V acts as off
+    (dict(top_k=256), SV_OK),
+    (dict(top_p=0.0), SV_ERR_PARAM),
+    (dict(top_p=1.5), SV_ERR_PARAM),
+    (dict(top_p=math.nan), SV_ERR_PARAM),
+    (dict(top_p=1.0), SV_OK),
+    (dict(top_p=0.9, top_k=50), SV_OK),
+])
+def test_sample_config_validation(over, want):
+    base = dict(mode=SV_MODE_SAMPLE, dtype=SV_DTYPE_BF16, max_batch=8, k=5, vocab=32000,
+                temperature=1.0, top_k=0, top_p=1.0)
+    base.update(over)
+    cfg = make_config(**base)
+    assert check(cfg) == want
+
+
+def test_greedy_modes_ignore_sampling_settings():
+    cfg = make_config(SV_MODE_GREEDY, SV_DTYPE_F32, 2, 4, 100, temperature=-1.0, top_k=-3, top_p=7.0)
+    assert check(cfg, batch=2, draft=None, uniforms=None, resid_uniforms=None) == SV_OK
+    tree = make_config(SV_MODE_TREE_GREEDY, SV_DTYPE_BF16, 2, 1024, 100, temperature=0.0)
+    assert check(tree, batch=2, draft=None, uniforms=None, resid_uniforms=None, parents=P) == SV_OK
+    tree = make_config(SV_MODE_TREE_GREEDY, SV_DTYPE_BF16, 2, 1025, 100)
+    assert check(tree, batch=2, draft=None, uniforms=None, resid_uniforms=None, parents=P) == SV_ERR_SHAPE
+
+
+def test_batch_and_pointer_rules():
+    cfg = make_config(SV_MODE_SAMPLE, "f32", 8, 4, 1000)
+    assert check(cfg, batch=0) == SV_OK
+    assert check(cfg, batch=0, target=None, draft=None, draft_tokens=None, uniforms=None,
+                 resid_uniforms=None, accepted_len=None, out_tokens=None) == SV_OK
+    assert check(cfg, batch=8) == SV_OK
+    assert check(cfg, batch=9) == SV_ERR_CAPACITY
+    assert check(cfg, batch=-1) == SV_ERR_SHAPE
+    for name in ("target", "draft", "draft_tokens", "uniforms", "resid_uniforms", "accepted_len", "out_tokens"):
+        assert check(cfg, **{name: None}) == SV_ERR_NULL, name
+    assert check(cfg, parents=P) == SV_ERR_MODE
+    assert check(cfg, out_nodes=P) == SV_ERR_MODE
+    g = make_config(SV_MODE_GREEDY, "f32", 8, 4, 1000)
+    ok = dict(draft=None, uniforms=None, resid_uniforms=None)
+    assert check(g, **ok) == SV_OK
+    for name in ("draft", "uniforms", "resid_uniforms", "parents", "out_nodes"):
+        kw = dict(ok)
+        kw[name] = P
+        assert check(g, **kw) == SV_ERR_MODE, name
+    t = make_config(SV_MODE_TREE_GREEDY, "bf16", 8, 60, 1000)
+    assert check(t, parents=None, **ok) == SV_ERR_NULL
+    assert check(t, parents=P, out_nodes=P, **ok) == SV_OK
+    assert check(t, parents=P, draft=P, uniforms=None, resid_uniforms=None) == SV_ERR_MODE
+
+
+def test_null_config_and_bad_create_make_no_hip_call():
+    lib = svm.load()
+    assert lib.specverify_check_args(None, 1, *([None] * 9)) == SV_ERR_NULL
+    h = ctypes.c_void_p()
+    bad = make_config(SV_MODE_SAMPLE, "bf16", 1, 5, 100, temperature=0.0)
+    assert lib.specverify_create(ctypes.byref(bad), 0, ctypes.byref(h)) == SV_ERR_PARAM
+    assert h.value is None
+    assert lib.specverify_create(ctypes.byref(bad), 0, None) == SV_ERR_NULL
+    lib.specverify_destroy(None)   # NULL-safe
+
+
+def test_run_rejects_null_context():
+    lib = svm.load()
+    assert lib.specverify_run(None, 1, *([None] * 11), None) == SV_ERR_NULL
+    assert lib.specverify_profile_events(None, None, None) == SV_ERR_NULL

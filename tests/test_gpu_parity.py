@@ -1,0 +1,207 @@
+"""HIP library vs the float64 oracle, through the C ABI, on seeded inputs.
+
+Small cases span several tiles and ragged tails (V not a multiple of the
+16-byte group, unaligned rows); full-size cases use the workloads' real
+shapes in the launch configuration the benchmark times and check a sample of
+sequences the oracle can afford.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.verify as ov
+from draft_token_verification_softmax_amd import (SV_MODE_GREEDY, SV_MODE_SAMPLE,
+                                                  SV_MODE_TREE_GREEDY)
+from draft_token_verification_softmax_amd import workloads as wl
+from gpu_common import (compare_chain, draw_drafts, oracle_chain, run_chain, run_tree, say,
+                        tree_tokens_via_oracle)
+
+pytestmark = pytest.mark.gpu
+
+
+def _planted_greedy_drafts(inp, p_match, seed):
+    rng = np.random.default_rng(seed)
+    T64 = wl.rows_f64(inp["target"], inp["dtype"])
+    g = np.argmax(T64, axis=-1)
+    B, K1, V = T64.shape
+    k = K1 - 1
+    x = np.where(rng.random((B, k)) < p_match, g[:, :k], rng.integers(0, V, size=(B, k)))
+    return x.astype(np.int32)
+
+
+# ------------------------------------------------------------------ greedy chain
+
+@pytest.mark.parametrize("dtype,V", [("f32", 5000), ("bf16", 6000), ("f32", 5003), ("bf16", 4103), ("f32", 32000)])
+def test_greedy_chain(dtype, V):
+    say("greedy chain", dtype, V)
+    inp = wl.chain_inputs(1, seed=11, B=64, V=V, k=4, dtype=dtype)
+    x = _planted_greedy_drafts(inp, 0.8, 1)
+    gpu = run_chain(inp, x, SV_MODE_GREEDY)
+    orc = oracle_chain(inp, x, SV_MODE_GREEDY, list(range(64)))
+    rep = compare_chain(gpu, orc, range(64), f"greedy {dtype} V={V}")
+    assert len(set(gpu["accepted_len"].tolist())) >= 3   # the planted drafts exercise several n
+
+
+def test_greedy_chain_ties_lowest_index():
+    say("greedy ties")
+    rng = np.random.default_rng(2)
+    B, k, V = 32, 5, 3000
+    # few distinct bf16 values: many tied maxima per row
+    t = rng.integers(0, 4, size=(B, k + 1, V)).astype(np.float64)
+    inp = dict(target=wl.bf16_from_f64(t), draft=None, dtype="bf16", u=None, ur=None)
+    g = np.argmax(t, axis=-1)
+    x = np.where(rng.random((B, k)) < 0.5, g[:, :k], rng.integers(0, V, size=(B, k))).astype(np.int32)
+    gpu = run_chain(inp, x, SV_MODE_GREEDY)
+    T64 = wl.rows_f64(inp["target"], "bf16")
+    acc, toks, st, _, _ = ov.run_chain_batch("greedy", T64, None, x, None, None)
+    assert np.array_equal(gpu["accepted_len"], acc) and np.array_equal(gpu["out_tokens"], toks)
+
+
+# ------------------------------------------------------------------ plain sampling
+
+@pytest.mark.parametrize("config,dtype,B,V,k", [
+    (1, "f32", 120, 32000, 4),      # workload 1 shape, 120 rounds in one call
+    (2, "bf16", 64, 32000, 5),      # workload 2 shape, four batches' worth
+    (2, "bf16", 40, 5003, 5),       # ragged, unaligned rows
+    (1, "f32", 40, 4099, 3),        # ragged fp32
+    (2, "bf16", 16, 6000, 1),       # k = 1
+])
+def test_sample_plain(config, dtype, B, V, k):
+    say("sample plain", config, dtype, B, V, k)
+    inp = wl.chain_inputs(config, seed=100 + B + V, B=B, V=V, k=k, dtype=dtype)
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    compare_chain(gpu, orc, range(B), f"sample cfg{config} {dtype} B={B} V={V} k={k}")
+
+
+def test_sample_plain_full_workload2():
+    say("sample workload 2 full size")
+    inp = wl.chain_inputs(2)          # B=16, k=5, V=32000 bf16, the benchmark's seed
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(16)))
+    compare_chain(gpu, orc, range(16), "workload 2")
+
+
+# ------------------------------------------------------------------ top-k
+
+@pytest.mark.parametrize("B,V,k,top_k,dtype", [
+    (32, 6000, 8, 50, "bf16"),
+    (24, 5001, 3, 50, "bf16"),
+    (16, 4000, 4, 7, "f32"),
+    (16, 3000, 2, 256, "bf16"),
+])
+def test_sample_topk(B, V, k, top_k, dtype):
+    say("sample top-k", B, V, k, top_k, dtype)
+    inp = wl.chain_inputs(3, seed=7 + V, B=B, V=V, k=k, dtype=dtype)
+    inp["top_k"] = top_k
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    compare_chain(gpu, orc, range(B), f"top-k {top_k} V={V}")
+
+
+def test_sample_topk_full_workload3():
+    say("sample workload 3 full size")
+    inp = wl.chain_inputs(3)          # B=64, k=8, V=128256 bf16, T=0.7, top-k 50
+    check = list(range(0, 64, 6))
+    x = draw_drafts(inp, check=set(check))
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, check)
+    compare_chain(gpu, orc, check, "workload 3")
+
+
+def test_topk_and_topp_together():
+    say("top-k + top-p")
+    inp = wl.chain_inputs(3, seed=5, B=16, V=3000, k=3, dtype="bf16")
+    inp["top_k"], inp["top_p"] = 40, 0.8
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(16)))
+    compare_chain(gpu, orc, range(16), "top-k 40 + top-p 0.8")
+
+
+# ------------------------------------------------------------------ top-p
+
+@pytest.mark.parametrize("B,V,k,top_p,dtype", [
+    (32, 6000, 4, 0.9, "f32"),
+    (24, 5003, 4, 0.9, "f32"),
+    (16, 4000, 3, 0.5, "bf16"),
+    (16, 3000, 2, 0.99, "bf16"),
+])
+def test_sample_topp(B, V, k, top_p, dtype):
+    say("sample top-p", B, V, k, top_p, dtype)
+    inp = wl.chain_inputs(5, seed=3 + V, B=B, V=V, k=k, dtype=dtype)
+    inp["top_p"] = top_p
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    compare_chain(gpu, orc, range(B), f"top-p {top_p} V={V} {dtype}")
+
+
+def test_sample_topp_full_workload5():
+    say("sample workload 5 full size")
+    inp = wl.chain_inputs(5)          # B=256, k=4, V=152064 fp32, T=0.8, top-p 0.9
+    check = list(range(0, 256, 37))
+    x = draw_drafts(inp, check=set(check))
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, check)
+    compare_chain(gpu, orc, check, "workload 5")
+
+
+def test_topp_heavy_ties_bf16():
+    """Thousands of equal bf16 logits around the cut: the tie must be split by index."""
+    say("top-p heavy ties")
+    rng = np.random.default_rng(9)
+    B, k, V = 8, 2, 20000
+    t = np.round(rng.normal(0, 0.3, size=(B, k + 1, V)) * 8) / 8     # few distinct values
+    d = np.round((t[:, :k] + rng.normal(0, 0.3, size=(B, k, V))) * 8) / 8
+    inp = dict(target=wl.bf16_from_f64(t), draft=wl.bf16_from_f64(d), dtype="bf16",
+               u=rng.random((B, k), dtype=np.float32), ur=rng.random(B, dtype=np.float32),
+               draw_u=rng.random((B, k)), T=1.0, top_k=0, top_p=0.7)
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    compare_chain(gpu, orc, range(B), "top-p ties")
+
+
+# ------------------------------------------------------------------ tree
+
+@pytest.mark.parametrize("B,N,V,dtype", [(16, 60, 6000, "bf16"), (8, 60, 5003, "bf16"),
+                                         (4, 200, 3000, "f32"), (3, 1, 1000, "bf16")])
+def test_tree_greedy(B, N, V, dtype):
+    say("tree", B, N, V, dtype)
+    tr = wl.tree_inputs(4, seed=N + V, B=B, N=N, V=V, dtype=dtype)
+    tokens, T64 = tree_tokens_via_oracle(tr)
+    gpu = run_tree(tr, tokens)
+    acc, toks, nodes, st = ov.run_tree_batch(T64, tr["parents"], tokens)
+    assert np.array_equal(gpu["accepted_len"], acc), (gpu["accepted_len"], acc)
+    assert np.array_equal(gpu["out_tokens"], toks)
+    assert np.array_equal(gpu["out_nodes"], nodes)
+    assert np.array_equal(gpu["seq_status"], st)
+
+
+def test_tree_full_workload4():
+    say("tree workload 4 full size")
+    tr = wl.tree_inputs(4)            # B=8, N=60, V=128256 bf16
+    tokens, T64 = tree_tokens_via_oracle(tr)
+    gpu = run_tree(tr, tokens)
+    acc, toks, nodes, st = ov.run_tree_batch(T64, tr["parents"], tokens)
+    say("tree depths", gpu["accepted_len"].tolist())
+    assert np.array_equal(gpu["accepted_len"], acc)
+    assert np.array_equal(gpu["out_tokens"], toks)
+    assert np.array_equal(gpu["out_nodes"], nodes)
+
+
+def test_tree_path_equals_chain_on_gpu():
+    say("tree path == chain")
+    inp = wl.chain_inputs(2, seed=4, B=12, V=3000, k=6, dtype="bf16")
+    x = _planted_greedy_drafts(inp, 0.85, 3)
+    chain = run_chain(inp, x, SV_MODE_GREEDY)
+    tr = dict(target=inp["target"], parents=np.tile(np.arange(-1, 6, dtype=np.int32), (12, 1)),
+              dtype="bf16")
+    tokens = np.concatenate([np.zeros((12, 1), np.int32), x], axis=1)
+    tree = run_tree(tr, tokens)
+    assert np.array_equal(chain["accepted_len"], tree["accepted_len"])
+    assert np.array_equal(chain["out_tokens"], tree["out_tokens"])
