@@ -222,27 +222,40 @@ def main():
                            c.get("u"), c.get("ur"), acc, out_tok, out_nodes, None, status, stream)
 
     hip = HipEvents()
+    hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = hip.create(2 * args.steps)
-    torch.cuda.synchronize()
+    # timed region 1 (the metric): K plain calls, nothing else on the stream
     t0 = time.perf_counter()
     for i in range(args.steps):
-        svm.specverify_profile_events(sv.ctx, evs[2 * i], evs[2 * i + 1])
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    # timed region 2 (the roofline): the same K calls with HIP events recorded
+    # on the call's stream around the streaming kernel (by the library) and
+    # around the whole call
+    evs = hip.create(4 * args.steps)
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        e = evs[4 * i: 4 * i + 4]
+        svm.specverify_profile_events(sv.ctx, e[1], e[2])
+        hip.hip.hipEventRecord(ctypes.c_void_p(e[0]), ctypes.c_void_p(stream))
+        step(i)
+        hip.hip.hipEventRecord(ctypes.c_void_p(e[3]), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
     svm.specverify_profile_events(sv.ctx, None, None)
-    kms = [hip.elapsed_ms(evs[2 * i], evs[2 * i + 1]) for i in range(args.steps)]
+    kms = np.array([hip.elapsed_ms(evs[4 * i + 1], evs[4 * i + 2]) for i in range(args.steps)])
+    cms = np.array([hip.elapsed_ms(evs[4 * i], evs[4 * i + 3]) for i in range(args.steps)])
     hip.destroy(evs)
     kern_ms = float(np.mean(kms))
+    call_ms = float(np.mean(cms))
     ms_per_step = wall * 1e3 / args.steps
     rows_per_call = B * rows_t
     value = rows_per_call * args.steps / wall
     achieved = logit_bytes / (kern_ms * 1e-3) / 1e9
-    log(f"step {ms_per_step * 1e3:.2f} us, streaming kernel {kern_ms * 1e3:.2f} us "
-        f"(p10 {np.percentile(kms, 10) * 1e3:.2f}, p90 {np.percentile(kms, 90) * 1e3:.2f}), "
+    log(f"step {ms_per_step * 1e3:.2f} us (wall), call {call_ms * 1e3:.2f} us (events), streaming kernel "
+        f"{kern_ms * 1e3:.2f} us (p10 {np.percentile(kms, 10) * 1e3:.2f}, p90 {np.percentile(kms, 90) * 1e3:.2f}), "
         f"{achieved:.1f} GB/s")
     result = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
@@ -252,9 +265,10 @@ def main():
                        logit_bytes_per_call=logit_bytes, input_copies=ncopies, **extra),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBS, "traffic": None,
-                     "kernel": "k_tiles (streaming pass)", "kernel_us": kern_ms * 1e3,
+                     "kernel": "k_stream (the pass that reads every logit)", "kernel_us": kern_ms * 1e3,
+                     "call_us_events": call_ms * 1e3,
                      "call_bytes_algorithmic": alg_bytes,
-                     "call_GBps": alg_bytes / (ms_per_step * 1e-3) / 1e9},
+                     "call_GBps": alg_bytes / (call_ms * 1e-3) / 1e9},
     }
     sv.close()
     if not args.no_cpu:

@@ -52,7 +52,7 @@ Plan make_plan(const sv_config* c) {
   if (c->mode == SV_MODE_GREEDY) { p.filt = sv::kFiltGreedy; p.tile_mode = sv::kModeArgmax; }
   else if (c->mode == SV_MODE_TREE_GREEDY) { p.filt = sv::kFiltTree; p.tile_mode = sv::kModeArgmax; }
   else if (p.top_k > 0) { p.filt = sv::kFiltTopk; p.tile_mode = sv::kModeTopk; }
-  else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeArgmax; }
+  else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeStats64; }
   else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats; }
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
@@ -68,7 +68,7 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, counters, counters_bytes, seq_n, seq_st, seq_M, zpart, spart;
+  size_t tiles, cand, nuc, seq_n, seq_st, seq_M, zpart, spart;
   size_t k_idx, k_e, k_cnt, k_norm, k_bad, total;
 };
 
@@ -86,8 +86,6 @@ Layout layout(const sv_config* c, const Plan& pl) {
   L.tiles = take(rows * (size_t)pl.S_max * sizeof(sv::TileStat));
   L.cand = take(pl.top_k > 0 ? rows * (size_t)pl.S_max * (size_t)pl.cand_w * sizeof(uint64_t) : 0);
   L.nuc = take(pl.filt == sv::kFiltTopp ? rows * sizeof(sv::RowNuc) : 0);
-  L.counters_bytes = (2 * B + rows) * sizeof(unsigned);
-  L.counters = take(L.counters_bytes);
   const bool plain = pl.filt == sv::kFiltNone;
   L.seq_n = take(B * sizeof(int));
   L.seq_st = take(B * sizeof(int));
@@ -179,13 +177,6 @@ int specverify_create(const sv_config* cfg, int device, specverify_ctx** out) {
   if (hipSetDevice(device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
   ctx->L = L;
   if (hipMalloc(&ctx->ws, L.total) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
-  // the "last workgroup" counters start at zero and every call leaves them at zero
-  if (hipMemset((char*)ctx->ws + L.counters, 0, L.counters_bytes) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
-    (void)hipFree(ctx->ws);
-    free(ctx);
-    return SV_ERR_HIP;
-  }
   *out = ctx;
   return SV_OK;
 }
@@ -267,9 +258,6 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.cand = (uint64_t*)(ws + L.cand);
   p.cand_w = pl.cand_w;
   p.nuc = (sv::RowNuc*)(ws + L.nuc);
-  p.seq_cnt = (unsigned*)(ws + L.counters);
-  p.aux_cnt = p.seq_cnt + B;
-  p.row_cnt = p.aux_cnt + B;
   (void)maxrows;
   p.seq_n = (int*)(ws + L.seq_n);
   p.seq_st = (int*)(ws + L.seq_st);
@@ -290,10 +278,9 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   const int bf16 = c->dtype == SV_DTYPE_BF16;
   hipError_t e = hipSuccess;
   if (ctx->ev_begin) e = hipEventRecord(ctx->ev_begin, st);
-  if (e == hipSuccess) e = sv::launch_stream(p, pl.filt, bf16, st);
+  if (e == hipSuccess) e = sv::launch_stream(p, pl.tile_mode, bf16, st);
   if (e == hipSuccess && ctx->ev_end) e = hipEventRecord(ctx->ev_end, st);
-  if (e == hipSuccess && pl.filt == sv::kFiltTopp) e = sv::launch_topp_rows(p, bf16, st);
-  if (e == hipSuccess && pl.filt == sv::kFiltNone) e = sv::launch_resid(p, bf16, st);
+  if (e == hipSuccess) e = sv::launch_finish(p, pl.filt, bf16, st);
   if (cur != ctx->device) (void)hipSetDevice(cur);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

@@ -43,7 +43,7 @@ struct RowNuc {
   float M;      // max raw logit of the row
 };
 
-enum TileMode { kModeArgmax = 0, kModeStats = 1, kModeTopk = 2 };
+enum TileMode { kModeArgmax = 0, kModeStats = 1, kModeTopk = 2, kModeStats64 = 3 };
 enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4 };
 
 struct Params {
@@ -80,11 +80,7 @@ struct Params {
   uint64_t* cand;    // [rows][S][cand_w] (top-k)
   int cand_w;        // candidate slots per tile (top_k rounded up)
   RowNuc* nuc;       // [rows] (top-p)
-  // "last workgroup" counters (zero between calls)
-  unsigned* seq_cnt; // [B]
-  unsigned* row_cnt; // [rows]
-  unsigned* aux_cnt; // [B]
-  // plain sampling: state handed from the accept step to the residual kernels
+  // plain sampling: state handed from k_resid_z to the later residual kernels
   int* seq_n;        // [B] accepted count n, or -1 if the sequence is already emitted
   int* seq_st;       // [B] status bits found by the accept step
   float* seq_M;      // [B][2] max raw logit of target row n and draft row n
@@ -99,12 +95,13 @@ struct Params {
   int32_t* k_bad;    // [rows] 1 if the row is invalid
 };
 
-// Launchers (sv_kernels.hip).  Each returns the hipError_t of its launch.
-// launch_stream: the streaming pass, with the epilogue of `filt` run by the
-// last workgroup of each row / sequence (greedy, tree, top-k: the whole call;
-// plain sampling: the accept step; nucleus: none).
-hipError_t launch_stream(const Params& p, int filt, int bf16, hipStream_t st);
-hipError_t launch_topp_rows(const Params& p, int bf16, hipStream_t st);
-hipError_t launch_resid(const Params& p, int bf16, hipStream_t st);
+// Launchers (sv_kernels.hip).  Each returns the hipError_t of its launches.
+// launch_stream: the one pass over every logit (tile partials).
+// launch_finish: the kernels after it for `filt` (greedy / tree: decision per
+// sequence; top-k: merge per row, decision per sequence; nucleus: exact cut
+// per row, decision per sequence; plain sampling: residual row sums, residual
+// mass per segment, draw per sequence).
+hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st);
+hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st);
 
 }  // namespace sv

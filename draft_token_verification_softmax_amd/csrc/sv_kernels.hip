@@ -274,29 +274,7 @@ DEV RowStat combine_tiles(const Params& p, int grow, bool stats) {
   return r;
 }
 
-// ================================================================== last-workgroup protocol
-//
-// A workgroup that has finished its share publishes it (its stores, then a
-// device-scope release fence), then one thread bumps a per-row or
-// per-sequence counter.  The workgroup that brings the counter to `total` is
-// the last one: it resets the counter for the next call, issues an acquire
-// fence and runs the epilogue over everyone's published results.  Nobody
-// waits for anybody, so this cannot deadlock whatever the residency.
-
-DEV bool arrive_last(unsigned* counter, unsigned total, int* sh_flag) {
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned old = atomicAdd(counter, 1u);
-    const bool last = (old == total - 1);
-    if (last) atomicExch(counter, 0u);
-    *sh_flag = last ? 1 : 0;
-  }
-  __syncthreads();
-  const bool last = *sh_flag != 0;
-  if (last) __threadfence();
-  return last;
-}
+// ================================================================== row / sequence indexing
 
 DEV int seq_of_row(const Params& p, int grow) {
   const int nt = p.B * p.rows_t;
@@ -414,9 +392,11 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int ngrou
   }
 }
 
-// The tile's top_k under (value desc, index asc), written to p.cand.
+// Exact fallback of tile_topk for inputs that would overflow its candidate
+// list: rounds of one group per lane; after each round the list is cut back
+// to the best top_k and the admission threshold raised.
 template <typename T>
-DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroups, int tile,
+DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int ngroups, int tile,
                    uint64_t* buf) {
   __shared__ int cnt;
   __shared__ float tau_f;
@@ -473,6 +453,166 @@ DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroup
     TileStat ts;
     ts.m = c > 0 ? packed_val(buf[0]) : -INFINITY;
     ts.amax = c > 0 ? packed_idx(buf[0]) : INT_MAX;
+    ts.s = bad ? (double)NAN : 0.0;
+    p.tiles[tile] = ts;
+  }
+  __syncthreads();
+}
+
+// Descending bitonic sort of kBlock floats in LDS.
+DEV void bitonic_desc_block_f(float* a) {
+  for (int size = 2; size <= kBlock; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      __syncthreads();
+      const int t = threadIdx.x;
+      if (t < kBlock / 2) {
+        const int lo = 2 * t - (t & (stride - 1));
+        const int hi = lo + stride;
+        const bool desc = (lo & size) == 0;
+        const float x = a[lo], y = a[hi];
+        if ((x < y) == desc) { a[lo] = y; a[hi] = x; }
+      }
+    }
+  }
+  __syncthreads();
+}
+
+// Max and float64 sum of exp((l - max) / T) of a tile, for nucleus rows
+// (whose cut needs the row sum to float64 accuracy).
+template <typename T>
+DEV void tile_stats64(const Params& p, const T* row, int start, int end, int ngroups, int tile) {
+  __shared__ float redm[kWaves];
+  __shared__ double redd[kWaves];
+  const double invT = 1.0 / p.T;
+  float m = -INFINITY;
+  double s = 0.0;
+  for (int g0 = threadIdx.x; g0 < ngroups; g0 += kUnroll * kBlock) {
+    float v[kUnroll][kVec];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int g = g0 + u * kBlock;
+      if (g < ngroups) {
+        load_group<T>(row, start + g * kVec, end, p.aligned, v[u]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      float gm = v[u][0];
+#pragma unroll
+      for (int e = 1; e < kVec; ++e) gm = fmaxf(gm, v[u][e]);
+      if (gm > m) {
+        if (m > -INFINITY) s *= exp(((double)m - (double)gm) * invT);
+        m = gm;
+      }
+      if (m > -INFINITY) {
+        const double zm = (double)m * invT;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) s += exp((double)v[u][e] * invT - zm);
+      } else {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) if (v[u][e] != v[u][e]) s = (double)NAN;
+      }
+    }
+  }
+  const float M = block_max(m, redm);
+  double term;
+  if (m == -INFINITY) term = s;
+  else term = s * exp(((double)m - (double)M) * invT);
+  const double tot = block_sum(term, redd);
+  if (threadIdx.x == 0) {
+    TileStat ts;
+    ts.m = M; ts.amax = INT_MAX; ts.s = tot;
+    p.tiles[tile] = ts;
+  }
+}
+
+// The tile's top_k under (value desc, index asc), written to p.cand.
+//  1. Every lane loads its first kUnroll groups; the top_k-th largest of the
+//     kBlock lane maxima is the admission threshold tau.  top_k distinct
+//     logits reach it, so it is a lower bound of the tile's top_k-th value.
+//  2. The tile streams like the other modes (kUnroll groups in flight per
+//     lane, no barriers); logits >= tau go to an LDS list.
+//  3. One sort of the list; its first top_k entries are the answer.
+// If the list would overflow, the tile is redone by tile_topk_rounds.
+template <typename T>
+DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroups, int tile,
+                   uint64_t* buf) {
+  __shared__ int cnt, overflow;
+  __shared__ float lmax[kBlock];
+  const int K = p.top_k;
+  const int tid = threadIdx.x;
+  if (tid == 0) { cnt = 0; overflow = 0; }
+  float probe = 0.f;
+  float tau = -INFINITY;
+  for (int base = 0; base < ngroups; base += kUnroll * kBlock) {
+    float v[kUnroll][kVec];
+    int nv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int g = base + tid + u * kBlock;
+      if (g < ngroups) {
+        nv[u] = load_group<T>(row, start + g * kVec, end, p.aligned, v[u]);
+      } else {
+        nv[u] = 0;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
+      }
+    }
+    if (base == 0) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u)
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) mx = fmaxf(mx, v[u][e]);
+      lmax[tid] = mx;
+      bitonic_desc_block_f(lmax);
+      tau = K <= kBlock ? lmax[K - 1] : -INFINITY;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int pos = start + (base + tid + u * kBlock) * kVec;
+      float gm = v[u][0];
+#pragma unroll
+      for (int e = 1; e < kVec; ++e) gm = fmaxf(gm, v[u][e]);
+      if (nv[u] == kVec) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) probe = fmaf(v[u][e], 0.f, probe);
+      } else {
+        for (int e = 0; e < nv[u]; ++e) probe = fmaf(v[u][e], 0.f, probe);
+      }
+      if (gm >= tau) {
+        for (int e = 0; e < nv[u]; ++e) {
+          if (v[u][e] >= tau) {
+            const int slot = atomicAdd(&cnt, 1);
+            if (slot < kTopkCap) buf[slot] = pack(v[u][e], pos + e);
+            else overflow = 1;
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (overflow) {
+    // an adversarial tile: redo it exactly with the round-based path
+    __syncthreads();
+    tile_topk_rounds<T>(p, row, start, end, ngroups, tile, buf);
+    return;
+  }
+  const bool bad = __syncthreads_or(probe != probe);
+  const int c = cnt;
+  const int P = next_pow2(c);
+  for (int i = c + tid; i < P; i += kBlock) buf[i] = 0ull;
+  bitonic_desc(buf, P);
+  const int keep = c < K ? c : K;
+  uint64_t* out = p.cand + (size_t)tile * p.cand_w;
+  for (int i = tid; i < p.cand_w; i += kBlock) out[i] = (i < keep) ? buf[i] : 0ull;
+  if (tid == 0) {
+    TileStat ts;
+    ts.m = keep > 0 ? packed_val(buf[0]) : -INFINITY;
+    ts.amax = keep > 0 ? packed_idx(buf[0]) : INT_MAX;
     ts.s = bad ? (double)NAN : 0.0;
     p.tiles[tile] = ts;
   }
@@ -749,8 +889,13 @@ DEV void epi_tree(const Params& p, int b) {
 
 // ================================================================== epilogue: plain sampling accept step
 
+// The accept step of plain sampling for sequence b.  Returns false if a row
+// is invalid (the outputs are then written by the workgroup with `emit`).
+// *n = accepted count, *st = status bits, *Mp / *Mq = raw maxima of target
+// row n and draft row n.
 template <typename T>
-DEV void epi_accept(const Params& p, int b) {
+DEV bool accept_step(const Params& p, int b, bool emit, int* n_out, int* st_out, float* Mp,
+                     float* Mq) {
   __shared__ float rM[kMaxRows];
   __shared__ double rZ[kMaxRows];
   __shared__ int rBad[kMaxRows];
@@ -768,9 +913,8 @@ DEV void epi_accept(const Params& p, int b) {
   }
   __syncthreads();
   if (rows_bad<T>(p, b, rBad, nrows)) {
-    emit_invalid(p, b, 4);
-    if (tid == 0) p.seq_n[b] = -1;
-    return;
+    if (emit) emit_invalid(p, b, 4);
+    return false;
   }
   const T* tgt = (const T*)p.target + (size_t)b * p.rows_t * V;
   const T* dft = (const T*)p.draft + (size_t)b * p.rows_d * V;
@@ -815,12 +959,12 @@ DEV void epi_accept(const Params& p, int b) {
     if (dec == 3) { st |= 1; n = j; break; }
     if (dec == 0) { n = j; break; }
   }
-  if (tid == 0) {
-    p.seq_n[b] = n;
-    p.seq_st[b] = st;
-    p.seq_M[2 * b] = rM[n];
-    p.seq_M[2 * b + 1] = n < k ? rM[p.rows_t + n] : 0.f;
-  }
+  *n_out = n;
+  *st_out = st;
+  *Mp = rM[n];
+  *Mq = n < k ? rM[p.rows_t + n] : 0.f;
+  __syncthreads();
+  return true;
 }
 
 // ================================================================== epilogues: top-k
@@ -993,11 +1137,10 @@ DEV void epi_topk_seq(const Params& p, int b, uint64_t* buf) {
   emit_tokens(p, b, x, n, sh_y, sh_st);
 }
 
-// ================================================================== streaming kernel
+// ================================================================== kernels
 
-template <typename T, int MODE, int FILT>
+template <typename T, int MODE>
 __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
-  __shared__ int sh_flag;
   const int tile = blockIdx.x;
   const int grow = tile / p.S;
   const int seg = tile - grow * p.S;
@@ -1008,39 +1151,59 @@ __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
   if constexpr (MODE == kModeTopk) {
     __shared__ uint64_t buf[kTopkCap];
     tile_topk<T>(p, row, start, end, ngroups, tile, buf);
-    if (!arrive_last(&p.row_cnt[grow], (unsigned)p.S, &sh_flag)) return;
-    epi_topk_row<T>(p, grow, buf);
-    const int b = seq_of_row(p, grow);
-    if (!arrive_last(&p.seq_cnt[b], (unsigned)(p.rows_t + p.rows_d), &sh_flag)) return;
-    epi_topk_seq<T>(p, b, buf);
+  } else if constexpr (MODE == kModeStats) {
+    tile_stats<T>(p, row, start, end, ngroups, tile);
+  } else if constexpr (MODE == kModeStats64) {
+    tile_stats64<T>(p, row, start, end, ngroups, tile);
   } else {
-    if constexpr (MODE == kModeStats) tile_stats<T>(p, row, start, end, ngroups, tile);
-    else tile_argmax<T>(p, row, start, end, ngroups, tile);
-    if constexpr (FILT == kFiltGreedy || FILT == kFiltTree || FILT == kFiltNone) {
-      const int b = seq_of_row(p, grow);
-      if (!arrive_last(&p.seq_cnt[b], (unsigned)p.S * (unsigned)(p.rows_t + p.rows_d), &sh_flag)) return;
-      if constexpr (FILT == kFiltGreedy) epi_greedy<T>(p, b);
-      else if constexpr (FILT == kFiltTree) epi_tree<T>(p, b);
-      else epi_accept<T>(p, b);
-    }
+    tile_argmax<T>(p, row, start, end, ngroups, tile);
   }
 }
 
-// ================================================================== residual kernels (plain sampling)
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_greedy_final(Params p) { epi_greedy<T>(p, blockIdx.x); }
 
-// float64 row sums of target row n and draft row n over one segment.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_tree_final(Params p) { epi_tree<T>(p, blockIdx.x); }
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
+  __shared__ uint64_t buf[kTopkCap];
+  epi_topk_row<T>(p, blockIdx.x, buf);
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_topk_final(Params p) {
+  __shared__ uint64_t buf[kTopkMax];
+  epi_topk_seq<T>(p, blockIdx.x, buf);
+}
+
+// ================================================================== residual kernels (plain sampling)
+//
+// k_resid_z    every workgroup of a sequence redoes its accept step (a few
+//              dozen partials and k logits), then sums exp(z - zmax) in
+//              float64 over one segment of target row n and draft row n;
+//              segment 0 publishes n for the next kernels.
+// k_resid_s    residual mass max(0, p' - q') per segment, float64.
+// k_resid_final one workgroup per sequence: S' = sum of the segments, the
+//              segment where ur * S' falls, the entry inside it, outputs.
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_resid_z(Params p) {
   __shared__ double red[kWaves];
   const int b = blockIdx.y, seg = blockIdx.x;
-  const int n = p.seq_n[b];
-  if (n < 0) return;
+  int n, st;
+  float Mp, Mq;
+  if (!accept_step<T>(p, b, seg == 0, &n, &st, &Mp, &Mq)) {
+    if (seg == 0 && threadIdx.x == 0) p.seq_n[b] = -1;
+    return;
+  }
   const int V = p.V, k = p.k;
   const double invT = 1.0 / p.T;
   const T* prow = row_ptr<T>(p, trow(p, b, n));
   const T* qrow = n < k ? row_ptr<T>(p, drow(p, b, n)) : nullptr;
-  const double zp = (double)p.seq_M[2 * b] * invT;
-  const double zq = (double)p.seq_M[2 * b + 1] * invT;
+  const double zp = (double)Mp * invT;
+  const double zq = (double)Mq * invT;
   const int c0 = seg * kResidSeg;
   const int c1 = min(c0 + kResidSeg, V);
   double sp = 0.0, sq = 0.0;
@@ -1053,34 +1216,56 @@ __global__ __launch_bounds__(kBlock) void k_resid_z(Params p) {
   if (threadIdx.x == 0) {
     p.zpart[((size_t)b * p.S2 + seg) * 2] = sp;
     p.zpart[((size_t)b * p.S2 + seg) * 2 + 1] = sq;
+    if (seg == 0) {
+      p.seq_n[b] = n;
+      p.seq_st[b] = st;
+      p.seq_M[2 * b] = Mp;
+      p.seq_M[2 * b + 1] = Mq;
+    }
   }
 }
 
-// Residual mass per segment; the last segment's workgroup draws the token.
+// The two residual rows of sequence b as views with their float64 sums.
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_resid_pick(Params p) {
-  __shared__ double red[kWaves];
-  __shared__ int sh_flag, sh_int, sh_c;
-  __shared__ double sh_base;
-  const int b = blockIdx.y, seg = blockIdx.x;
-  const int n = p.seq_n[b];
-  if (n < 0) return;
-  const int V = p.V, k = p.k;
+DEV void resid_views(const Params& p, int b, int n, RowView* pr, RowView* qr) {
   const double invT = 1.0 / p.T;
   double Zp = 0.0, Zq = 0.0;
   for (int s = 0; s < p.S2; ++s) {
     Zp += p.zpart[((size_t)b * p.S2 + s) * 2];
     Zq += p.zpart[((size_t)b * p.S2 + s) * 2 + 1];
   }
-  const RowView pr{row_ptr<T>(p, trow(p, b, n)), (double)p.seq_M[2 * b] * invT, Zp, 0ull};
-  const RowView qrv{n < k ? row_ptr<T>(p, drow(p, b, n)) : nullptr, (double)p.seq_M[2 * b + 1] * invT, Zq, 0ull};
-  const RowView* qr = n < k ? &qrv : nullptr;
+  *pr = RowView{row_ptr<T>(p, trow(p, b, n)), (double)p.seq_M[2 * b] * invT, Zp, 0ull};
+  *qr = RowView{n < p.k ? row_ptr<T>(p, drow(p, b, n)) : nullptr,
+                (double)p.seq_M[2 * b + 1] * invT, Zq, 0ull};
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
+  __shared__ double red[kWaves];
+  const int b = blockIdx.y, seg = blockIdx.x;
+  const int n = p.seq_n[b];
+  if (n < 0) return;
+  RowView pr, qrv;
+  resid_views<T>(p, b, n, &pr, &qrv);
   double w[kVec];
   double tot;
-  resid_chunk<T>(pr, qr, invT, V, seg * kResidSeg, w, red, &tot);
+  resid_chunk<T>(pr, n < p.k ? &qrv : nullptr, 1.0 / p.T, p.V, seg * kResidSeg, w, red, &tot);
   if (threadIdx.x == 0) p.spart[(size_t)b * p.S2 + seg] = tot;
-  if (!arrive_last(&p.aux_cnt[b], (unsigned)p.S2, &sh_flag)) return;
+}
 
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
+  __shared__ double red[kWaves];
+  __shared__ int sh_int, sh_c;
+  __shared__ double sh_base;
+  const int b = blockIdx.x;
+  const int n = p.seq_n[b];
+  if (n < 0) return;
+  const int V = p.V, k = p.k;
+  const double invT = 1.0 / p.T;
+  RowView pr, qrv;
+  resid_views<T>(p, b, n, &pr, &qrv);
+  const RowView* qr = n < k ? &qrv : nullptr;
   const int32_t* x = p.tokens + (size_t)b * k;
   const double ur = (double)p.ur[b];
   double S = 0.0;
@@ -1090,9 +1275,8 @@ __global__ __launch_bounds__(kBlock) void k_resid_pick(Params p) {
   if (S > 0.0) {
     const double t = ur * S;
     if (threadIdx.x == 0) {
-      double base = 0.0;
+      double base = 0.0, lastbase = 0.0;
       int c = -1, lastc = 0;
-      double lastbase = 0.0;
       for (int s = 0; s < p.S2; ++s) {
         const double ps = p.spart[(size_t)b * p.S2 + s];
         if (ps > 0.0) { lastc = s; lastbase = base; }
@@ -1107,6 +1291,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_pick(Params p) {
     const int c = sh_c;
     const double base = sh_base;
     __syncthreads();
+    double w[kVec];
     double tc;
     const double ex = resid_chunk<T>(pr, qr, invT, V, c * kResidSeg, w, red, &tc);
     y = pick_in_chunk(base, ex, w, c * kResidSeg, t, &sh_int);
@@ -1117,6 +1302,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_pick(Params p) {
   if (p.resid_probs) write_resid_probs<T>(p, b, pr, p_only ? nullptr : qr, invT, S);
   emit_tokens(p, b, x, n, y, p.seq_st[b]);
 }
+
 // ================================================================== nucleus
 //
 // Exact nucleus cut of one row.  The rank order is (logit desc, index asc),
@@ -1171,35 +1357,37 @@ DEV double nuc_bin_ref(const NucState& s, int b) {
 
 // Histogram sweep at the current level (the window fields are ignored).
 // hq: sum of e / ref(bin) in 2^-32 units (exact integers, so the order of the
-// LDS atomics cannot change them); hc: counts.  *A gets the exact mass of
-// everything ranked above the level's range, *below the count ranked below
-// it (and still < dmax); *Z (optional) the whole row's mass.
+// LDS atomics cannot change them; float32 exponentials suffice because these
+// masses only locate the boundary); hc: counts.  *A gets the exact float64
+// mass of everything ranked above the level's range, *below the count ranked
+// below it (and still < dmax).
 template <typename T>
 DEV void nuc_hist(const T* row, int V, NucState s, unsigned long long* hq, unsigned int* hc,
-                  unsigned int* below, double* red, double* A, double* Z, bool want_Z) {
+                  unsigned int* below, double* red, double* A) {
   for (int b = threadIdx.x; b < kNucBins; b += kBlock) { hq[b] = 0ull; hc[b] = 0u; }
   if (threadIdx.x == 0) *below = 0u;
   __syncthreads();
   s.c0 = 0; s.c1 = kNucBins - 1;   // whole level = "window"
-  double a = 0.0, z = 0.0;
+  const double ref1 = (double)s.p0lo * s.w0;
+  double a = 0.0;
   unsigned int nb = 0;
   for (int i = threadIdx.x; i < V; i += kBlock) {
     const float l = Io<T>::at(row, i);
     const double d = s.zm - (double)l * s.invT;
-    if (want_Z) z += exp(-d);
+    if (!(d < s.dmax)) continue;
     int bin;
     const int cls = nuc_class(s, l, i, d, &bin);
     if (cls == -1) a += exp(-d);
     else if (cls == 1) nb++;
     else if (cls == 0) {
-      const double rel = exp(-d) / nuc_bin_ref(s, bin);
-      atomicAdd(&hq[bin], (unsigned long long)(rel * 4294967296.0));
+      const double refd = s.level == 0 ? (double)bin * s.w0 : ref1;
+      const float rel = __expf((float)(refd - d));   // in (e^-w, 1]
+      atomicAdd(&hq[bin], (unsigned long long)(rel * 4294967296.0f));
       atomicAdd(&hc[bin], 1u);
     }
   }
   if (nb) atomicAdd(below, nb);
   *A = block_sum(a, red);
-  if (want_Z) *Z = block_sum(z, red);
   __syncthreads();
 }
 
@@ -1234,7 +1422,7 @@ DEV int nuc_locate(const NucState& s, const unsigned long long* hq, double A, do
 
 // Exact nucleus cut of one valid row (see above); fills *out.
 template <typename T>
-DEV void topp_search(const Params& p, const T* row, float Mrow, RowNuc* outp,
+DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc* outp,
                      unsigned long long* hq, unsigned int* hc, uint64_t* win, double* red,
                      unsigned long long* redu, unsigned int* below_p, unsigned int* wcnt_p,
                      int* sh_int_p, unsigned long long* sh_pmin_p, unsigned long long* sh_pmax_p) {
@@ -1249,16 +1437,17 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, RowNuc* outp,
   NucState s;
   s.invT = 1.0 / p.T;
   s.zm = (double)Mrow * s.invT;
-  s.dmax = log((double)V / (1.0 - p.top_p)) + 1.0;
+  // every kept entry has probability > (1 - top_p) / V, i.e. d < ln(V / ((1 - top_p) Z))
+  s.dmax = log((double)V / ((1.0 - p.top_p) * Z)) + 1.0;
+  if (!(s.dmax > 1.0)) s.dmax = 1.0;
   s.w0 = s.dmax / kNucBins;
   s.invw0 = 1.0 / s.w0;
   s.level = 0; s.p0lo = 0; s.p0hi = kNucBins - 1; s.plo = 0; s.phi = ~0ull; s.sh = 0;
   s.c0 = 0; s.c1 = kNucBins - 1;
 
-  double A = 0.0, Z = 0.0;
-  nuc_hist<T>(row, V, s, hq, hc, &below, red, &A, &Z, true);
+  double A = 0.0;
+  nuc_hist<T>(row, V, s, hq, hc, &below, red, &A);
   const double tgt = p.top_p * Z;
-  out.Z = Z;
   bool located = false;
   int result = 0;   // 1 found, -1 failed
   for (int iter = 0; iter < 64 && result == 0; ++iter) {
@@ -1370,7 +1559,7 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, RowNuc* outp,
       int bits = span ? 64 - __clzll((long long)span) : 0;
       s.sh = bits > 11 ? bits - 11 : 0;
       s.level += 1;
-      nuc_hist<T>(row, V, s, hq, hc, &below, red, &A, &Z, false);
+      nuc_hist<T>(row, V, s, hq, hc, &below, red, &A);
       located = false;
     }
   }
@@ -1455,63 +1644,68 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   __shared__ int sh_int;
   __shared__ unsigned long long sh_pmin, sh_pmax;
 
-  __shared__ int sh_flag;
   RowNuc out;
   out.Z = 0.0; out.N = 0.0; out.cut = 0ull; out.ok = 0; out.M = 0.f;
 
-  const RowStat rs = combine_tiles(p, grow, false);
-  bool invalid = (rs.M == INFINITY) || (rs.M == -INFINITY) || (rs.M != rs.M);
-  if (!invalid && rs.probe) invalid = row_has_nan_or_posinf<T>(row, V);
+  const RowStat rs = combine_tiles(p, grow, true);   // float64 row sum from the tiles
+  const bool invalid = (rs.Z != rs.Z) || (rs.M == INFINITY) || (rs.M == -INFINITY);
   out.M = rs.M;
+  out.Z = rs.Z;
   if (invalid) {
     if (tid == 0) p.nuc[grow] = out;
   } else {
-    topp_search<T>(p, row, rs.M, &out, hq, hc, win, red, redu, &below, &wcnt, &sh_int, &sh_pmin, &sh_pmax);
+    topp_search<T>(p, row, rs.M, rs.Z, &out, hq, hc, win, red, redu, &below, &wcnt, &sh_int, &sh_pmin, &sh_pmax);
     if (tid == 0) p.nuc[grow] = out;
   }
-  const int b = seq_of_row(p, grow);
-  if (!arrive_last(&p.seq_cnt[b], (unsigned)(p.rows_t + p.rows_d), &sh_flag)) return;
-  epi_topp_seq<T>(p, b);
 }
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_topp_final(Params p) { epi_topp_seq<T>(p, blockIdx.x); }
 
 
 // ================================================================== launchers
 
 template <typename T>
-static hipError_t launch_stream_t(const Params& p, int filt, hipStream_t st) {
+static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st) {
   const int rows = p.B * (p.rows_t + p.rows_d);
   const dim3 grid((unsigned)rows * (unsigned)p.S), block(kBlock);
-  switch (filt) {
-    case kFiltGreedy: hipLaunchKernelGGL((k_stream<T, kModeArgmax, kFiltGreedy>), grid, block, 0, st, p); break;
-    case kFiltTree: hipLaunchKernelGGL((k_stream<T, kModeArgmax, kFiltTree>), grid, block, 0, st, p); break;
-    case kFiltNone: hipLaunchKernelGGL((k_stream<T, kModeStats, kFiltNone>), grid, block, 0, st, p); break;
-    case kFiltTopk: hipLaunchKernelGGL((k_stream<T, kModeTopk, kFiltTopk>), grid, block, 0, st, p); break;
-    default: hipLaunchKernelGGL((k_stream<T, kModeArgmax, kFiltTopp>), grid, block, 0, st, p); break;
-  }
+  if (mode == kModeStats) hipLaunchKernelGGL((k_stream<T, kModeStats>), grid, block, 0, st, p);
+  else if (mode == kModeTopk) hipLaunchKernelGGL((k_stream<T, kModeTopk>), grid, block, 0, st, p);
+  else if (mode == kModeStats64) hipLaunchKernelGGL((k_stream<T, kModeStats64>), grid, block, 0, st, p);
+  else hipLaunchKernelGGL((k_stream<T, kModeArgmax>), grid, block, 0, st, p);
   return hipGetLastError();
 }
 
-hipError_t launch_stream(const Params& p, int filt, int bf16, hipStream_t st) {
-  return bf16 ? launch_stream_t<uint16_t>(p, filt, st) : launch_stream_t<float>(p, filt, st);
-}
-
-hipError_t launch_topp_rows(const Params& p, int bf16, hipStream_t st) {
+template <typename T>
+static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
   const int rows = p.B * (p.rows_t + p.rows_d);
-  if (bf16) hipLaunchKernelGGL((k_topp_rows<uint16_t>), dim3(rows), dim3(kBlock), 0, st, p);
-  else hipLaunchKernelGGL((k_topp_rows<float>), dim3(rows), dim3(kBlock), 0, st, p);
+  const dim3 block(kBlock), gb((unsigned)p.B), gr((unsigned)rows), gs((unsigned)p.S2, (unsigned)p.B);
+  switch (filt) {
+    case kFiltGreedy: hipLaunchKernelGGL((k_greedy_final<T>), gb, block, 0, st, p); break;
+    case kFiltTree: hipLaunchKernelGGL((k_tree_final<T>), gb, block, 0, st, p); break;
+    case kFiltTopk:
+      hipLaunchKernelGGL((k_topk_rows<T>), gr, block, 0, st, p);
+      hipLaunchKernelGGL((k_topk_final<T>), gb, block, 0, st, p);
+      break;
+    case kFiltTopp:
+      hipLaunchKernelGGL((k_topp_rows<T>), gr, block, 0, st, p);
+      hipLaunchKernelGGL((k_topp_final<T>), gb, block, 0, st, p);
+      break;
+    default:  // plain sampling
+      hipLaunchKernelGGL((k_resid_z<T>), gs, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_s<T>), gs, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T>), gb, block, 0, st, p);
+      break;
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_resid(const Params& p, int bf16, hipStream_t st) {
-  const dim3 grid((unsigned)p.S2, (unsigned)p.B), block(kBlock);
-  if (bf16) {
-    hipLaunchKernelGGL((k_resid_z<uint16_t>), grid, block, 0, st, p);
-    hipLaunchKernelGGL((k_resid_pick<uint16_t>), grid, block, 0, st, p);
-  } else {
-    hipLaunchKernelGGL((k_resid_z<float>), grid, block, 0, st, p);
-    hipLaunchKernelGGL((k_resid_pick<float>), grid, block, 0, st, p);
-  }
-  return hipGetLastError();
+hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st) {
+  return bf16 ? launch_stream_t<uint16_t>(p, mode, st) : launch_stream_t<float>(p, mode, st);
+}
+
+hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st) {
+  return bf16 ? launch_finish_t<uint16_t>(p, filt, st) : launch_finish_t<float>(p, filt, st);
 }
 
 }  // namespace sv
