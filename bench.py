@@ -156,6 +156,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device three times (scale reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -165,6 +168,17 @@ def main():
     import torch
     import draft_token_verification_softmax_amd as svm
     from draft_token_verification_softmax_amd import workloads as wl
+
+    if args.copy_calibrate:
+        n = args.copy_calibrate * (1 << 20) // 4
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_call": n * 4, "calls": 3}), flush=True)
+        return
 
     svm.load()
     cfg = wl.CONFIGS[args.config]

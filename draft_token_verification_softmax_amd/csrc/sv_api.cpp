@@ -11,7 +11,6 @@
 namespace {
 
 constexpr int kMinTile = 8192;        // logits per tile, lower bound (4 groups per lane)
-constexpr int kTargetBlocks = 2048;   // workgroups the streaming pass aims for
 
 struct Plan {
   int filt;        // sv::Filter
@@ -53,7 +52,7 @@ Plan make_plan(const sv_config* c) {
   else if (c->mode == SV_MODE_TREE_GREEDY) { p.filt = sv::kFiltTree; p.tile_mode = sv::kModeArgmax; }
   else if (p.top_k > 0) { p.filt = sv::kFiltTopk; p.tile_mode = sv::kModeTopk; }
   else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeStats64; }
-  else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats; }
+  else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats64; }
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
   p.S_max = (c->vocab + kMinTile - 1) / kMinTile;
@@ -68,7 +67,7 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, seq_n, seq_st, seq_M, zpart, spart;
+  size_t tiles, cand, nuc, seq_n, seq_st, spart;
   size_t k_idx, k_e, k_cnt, k_norm, k_bad, total;
 };
 
@@ -86,12 +85,10 @@ Layout layout(const sv_config* c, const Plan& pl) {
   L.tiles = take(rows * (size_t)pl.S_max * sizeof(sv::TileStat));
   L.cand = take(pl.top_k > 0 ? rows * (size_t)pl.S_max * (size_t)pl.cand_w * sizeof(uint64_t) : 0);
   L.nuc = take(pl.filt == sv::kFiltTopp ? rows * sizeof(sv::RowNuc) : 0);
-  const bool plain = pl.filt == sv::kFiltNone;
+  const bool sampled = pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp;
   L.seq_n = take(B * sizeof(int));
   L.seq_st = take(B * sizeof(int));
-  L.seq_M = take(B * 2 * sizeof(float));
-  L.zpart = take(plain ? B * (size_t)pl.S2_max * 2 * sizeof(double) : 0);
-  L.spart = take(plain ? B * (size_t)pl.S2_max * sizeof(double) : 0);
+  L.spart = take(sampled ? B * (size_t)pl.S2_max * sizeof(double) : 0);
   L.k_idx = take(rows * K * sizeof(int32_t));
   L.k_e = take(rows * K * sizeof(double));
   L.k_cnt = take(K ? rows * sizeof(int32_t) : 0);
@@ -110,6 +107,7 @@ struct specverify_ctx {
   void* ws;
   size_t ws_bytes;
   Layout L;
+  int grid;                      // resident workgroups of the streaming kernel
   hipEvent_t ev_begin, ev_end;   // optional instrumentation (caller-owned)
 };
 
@@ -176,6 +174,10 @@ int specverify_create(const sv_config* cfg, int device, specverify_ctx** out) {
   ctx->ws_bytes = L.total;
   if (hipSetDevice(device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
   ctx->L = L;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
+  const int per_cu = sv::stream_blocks_per_cu(ctx->plan.tile_mode, cfg->dtype == SV_DTYPE_BF16);
+  ctx->grid = prop.multiProcessorCount * (per_cu > 0 ? per_cu : 1);
   if (hipMalloc(&ctx->ws, L.total) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
   *out = ctx;
   return SV_OK;
@@ -237,9 +239,10 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.T = c->mode == SV_MODE_SAMPLE ? c->temperature : 1.0;
   p.top_p = pl.top_p;
   p.top_k = pl.top_k;
-  // tiling: enough workgroups to fill the chip, tiles of at least kMinTile logits
+  // tiling: about four tiles per resident workgroup of the streaming kernel
+  // (a short last wave), tiles of at least kMinTile logits
   const long rows = (long)batch * (pl.rows_t + pl.rows_d);
-  long S = (kTargetBlocks + rows - 1) / rows;
+  long S = (4L * ctx->grid + rows - 1) / rows;
   if (S > pl.S_max) S = pl.S_max;
   if (S < 1) S = 1;
   const int per = (int)((c->vocab + S - 1) / S);
@@ -250,6 +253,7 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   const bool base16 = ((uintptr_t)target_logits % 16 == 0) &&
                       (!draft_logits || (uintptr_t)draft_logits % 16 == 0);
   p.aligned = (rows16 && base16) ? 1 : 0;
+  p.grid = ctx->grid;
   char* ws = (char*)ctx->ws;
   const Layout& L = ctx->L;
   const size_t B = (size_t)c->max_batch;
@@ -261,8 +265,6 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   (void)maxrows;
   p.seq_n = (int*)(ws + L.seq_n);
   p.seq_st = (int*)(ws + L.seq_st);
-  p.seq_M = (float*)(ws + L.seq_M);
-  p.zpart = (double*)(ws + L.zpart);
   p.spart = (double*)(ws + L.spart);
   p.S2 = pl.S2_max;
   p.k_idx = (int32_t*)(ws + L.k_idx);
@@ -276,10 +278,7 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   if (cur != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
   const int bf16 = c->dtype == SV_DTYPE_BF16;
-  hipError_t e = hipSuccess;
-  if (ctx->ev_begin) e = hipEventRecord(ctx->ev_begin, st);
-  if (e == hipSuccess) e = sv::launch_stream(p, pl.tile_mode, bf16, st);
-  if (e == hipSuccess && ctx->ev_end) e = hipEventRecord(ctx->ev_end, st);
+  hipError_t e = sv::launch_stream(p, pl.tile_mode, bf16, st, ctx->ev_begin, ctx->ev_end);
   if (e == hipSuccess) e = sv::launch_finish(p, pl.filt, bf16, st);
   if (cur != ctx->device) (void)hipSetDevice(cur);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;

@@ -43,7 +43,7 @@ struct RowNuc {
   float M;      // max raw logit of the row
 };
 
-enum TileMode { kModeArgmax = 0, kModeStats = 1, kModeTopk = 2, kModeStats64 = 3 };
+enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3 };
 enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4 };
 
 struct Params {
@@ -75,16 +75,15 @@ struct Params {
   int S;        // tiles per row
   int L;        // logits per tile (multiple of kVec)
   int aligned;  // every row starts 16-byte aligned
+  int grid;     // workgroups of the streaming launch (resident capacity)
   // workspace
   TileStat* tiles;   // [rows][S]
   uint64_t* cand;    // [rows][S][cand_w] (top-k)
   int cand_w;        // candidate slots per tile (top_k rounded up)
   RowNuc* nuc;       // [rows] (top-p)
-  // plain sampling: state handed from k_resid_z to the later residual kernels
+  // sampling: state handed from k_resid_s to k_resid_final
   int* seq_n;        // [B] accepted count n, or -1 if the sequence is already emitted
   int* seq_st;       // [B] status bits found by the accept step
-  float* seq_M;      // [B][2] max raw logit of target row n and draft row n
-  double* zpart;     // [B][S2][2] float64 row-sum partials of those rows
   double* spart;     // [B][S2] residual-mass partials
   int S2;            // residual segments per sequence (kResidSeg logits each)
   // top-k: each row's kept set, rank order
@@ -101,7 +100,10 @@ struct Params {
 // sequence; top-k: merge per row, decision per sequence; nucleus: exact cut
 // per row, decision per sequence; plain sampling: residual row sums, residual
 // mass per segment, draw per sequence).
-hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st);
+hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st,
+                         hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
+// Workgroups of the streaming kernel for `mode` one CU keeps resident.
+int stream_blocks_per_cu(int mode, int bf16);
 hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st);
 
 }  // namespace sv

@@ -1,33 +1,31 @@
 // gfx950 kernels of the speculative-decoding verification step.
 //
-// One call is one to three launches on the caller's stream, with no host
-// synchronisation:
-//   k_stream      every logits row the mode reads is cut into S tiles; one
-//                 workgroup streams one tile once from HBM (16-byte
-//                 non-temporal loads, several in flight per lane) and leaves a
-//                 small partial in the workspace:
-//                   ARGMAX  max + lowest index        (greedy, tree, nucleus prep)
-//                   STATS   max + sum exp((l-max)/T)  (plain sampling)
-//                   TOPK    the tile's top_k          (top-k sampling)
-//                 The last workgroup to finish a row / sequence (an atomic
-//                 counter, no waiting) runs the epilogue: the whole greedy,
-//                 tree and top-k decision, or the accept step of plain sampling.
-//   k_topp_rows   nucleus sampling: one workgroup per row finds the exact cut;
-//                 the last row of a sequence decides the sequence.
-//   k_resid_z / k_resid_pick
-//                 plain sampling: float64 sums of the two residual rows, then
-//                 the residual mass per segment; the last segment draws.
+// One call is a short chain of launches on the caller's stream, with no host
+// synchronisation and no cross-workgroup signalling inside a launch:
+//   k_stream        the one pass over every logit the mode reads: one
+//                   workgroup per tile of a row (16-byte non-temporal loads,
+//                   four groups in flight per lane) leaves a small partial
+//                   per tile in the workspace:
+//                     ARGMAX   max + lowest index       (greedy, tree)
+//                     STATS64  max + float64 sum of exp((l - max) / T)
+//                                                         (plain and nucleus sampling)
+//                     TOPK     the tile's top_k           (top-k sampling)
+//   greedy / tree   k_greedy_final / k_tree_final: one workgroup per sequence
+//   top-k           k_topk_rows (merge per row) -> k_topk_final (per sequence)
+//   nucleus         k_topp_rows (exact cut per row) -> k_resid_s -> k_resid_final
+//   plain sampling  k_resid_s (accept step + residual mass per segment)
+//                   -> k_resid_final (draw per sequence)
 //
 // Every reduction that feeds an output is a fixed-order butterfly / tree, so
-// repeated calls give bit-identical results.  Float64 is used for every
-// quantity that decides an integer output (accept test, nucleus cut, inverse
-// CDF); the streaming pass of plain sampling uses float32 exponentials, and
-// the accept test that depends on it is redone in float64 when the uniform
-// lies within the float32 error bound of the threshold.
+// repeated calls give bit-identical results.  Float64 carries every quantity
+// that decides an integer output (row sums, accept test, nucleus cut,
+// inverse CDF).
 
 #include <float.h>
 #include <limits.h>
 #include <math.h>
+
+#include <hip/hip_ext.h>
 
 #include "sv_internal.h"
 
@@ -37,10 +35,6 @@ namespace sv {
 
 constexpr int kWaves = kBlock / 64;
 constexpr double kLog2e = 1.4426950408889634;
-// relative error bound of an accept ratio built from float32 exponentials
-// (two row sums at <= 3e-6 each, with margin); inside it the test is redone
-// in float64
-constexpr double kCertRel = 3e-5;
 constexpr int kStatusInternal = 0x100;   // a numeric search did not settle (never expected)
 constexpr int kTopkMax = 256;            // largest top_k
 
@@ -340,58 +334,6 @@ DEV void tile_argmax(const Params& p, const T* row, int start, int end, int ngro
   }
 }
 
-template <typename T>
-DEV void tile_stats(const Params& p, const T* row, int start, int end, int ngroups, int tile) {
-  __shared__ float redm[kWaves];
-  __shared__ double redd[kWaves];
-  const float cf = (float)(kLog2e / p.T);
-  const double cd = kLog2e / p.T;
-  float m = -INFINITY;
-  double s = 0.0;
-  for (int g0 = threadIdx.x; g0 < ngroups; g0 += kUnroll * kBlock) {
-    float v[kUnroll][kVec];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int g = g0 + u * kBlock;
-      if (g < ngroups) {
-        load_group<T>(row, start + g * kVec, end, p.aligned, v[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float gm = v[u][0];
-#pragma unroll
-      for (int e = 1; e < kVec; ++e) gm = fmaxf(gm, v[u][e]);
-      if (gm > m) {
-        if (m > -INFINITY) s *= exp2(((double)m - (double)gm) * cd);
-        m = gm;
-      }
-      if (m > -INFINITY) {
-        float t = 0.f;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) t += __builtin_amdgcn_exp2f((v[u][e] - m) * cf);
-        s += (double)t;
-      } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) if (v[u][e] != v[u][e]) s = (double)NAN;
-      }
-    }
-  }
-  const float M = block_max(m, redm);
-  double term;
-  if (m == -INFINITY) term = s;                       // 0, or NaN if a NaN was seen
-  else term = s * exp2(((double)m - (double)M) * cd);  // M >= m
-  const double tot = block_sum(term, redd);
-  if (threadIdx.x == 0) {
-    TileStat ts;
-    ts.m = M; ts.amax = INT_MAX; ts.s = tot;
-    p.tiles[tile] = ts;
-  }
-}
-
 // Exact fallback of tile_topk for inputs that would overflow its candidate
 // list: rounds of one group per lane; after each round the list is cut back
 // to the best top_k and the admission threshold raised.
@@ -654,41 +596,43 @@ struct RowView {
   uint64_t cut;   // nucleus: v is kept iff pack(l_v, v) >= cut; 0 = no nucleus
 };
 
-template <typename T>
-DEV double prob_of(const RowView& r, double invT, int v) {
-  const float l = Io<T>::at((const T*)r.row, v);
+DEV double prob_from(const RowView& r, double invT, float l, int v) {
   if (r.cut && pack(l, v) < r.cut) return 0.0;
   return exp((double)l * invT - r.zm) / r.norm;
 }
 
 template <typename T>
-DEV double exact_row_sum(const T* row, int V, double invT, double zm, double* red) {
-  double s = 0.0;
-  for (int i = threadIdx.x; i < V; i += kBlock) s += exp((double)Io<T>::at(row, i) * invT - zm);
-  return block_sum(s, red);
+DEV double prob_of(const RowView& r, double invT, int v) {
+  return prob_from(r, invT, Io<T>::at((const T*)r.row, v), v);
 }
 
-// Residual weight of entry v: max(0, p'(v) - q'(v)) (q absent: p'(v)).
+// One chunk of kResidSeg entries of the residual draw: thread t owns
+// [c0 + 8t, c0 + 8t + 8), loaded as one group.  w = max(0, p'(v) - q'(v)),
+// or p'(v) without q.  Returns the thread's exclusive prefix within the chunk
+// (fixed order); *tot = chunk total.
 template <typename T>
-DEV double resid_weight(const RowView& pr, const RowView* qr, double invT, int v) {
-  const double a = prob_of<T>(pr, invT, v);
-  if (!qr) return a;
-  const double d = a - prob_of<T>(*qr, invT, v);
-  return d > 0.0 ? d : 0.0;
-}
-
-// One chunk of kResidSeg entries of the inverse-CDF sweep: thread t owns
-// [c0 + 8t, c0 + 8t + 8).  Returns the thread's exclusive prefix within the
-// chunk (fixed order); *tot = chunk total; w[] = the thread's weights.
-template <typename T>
-DEV double resid_chunk(const RowView& pr, const RowView* qr, double invT, int V, int c0,
-                       double w[kVec], double* red, double* tot) {
+DEV double resid_chunk(const RowView& pr, const RowView* qr, double invT, int V, int aligned,
+                       int c0, double w[kVec], double* red, double* tot) {
+  const int pos = c0 + threadIdx.x * kVec;
+  float lp[kVec], lq[kVec];
+  int n = 0;
+  if (pos < V) {
+    n = load_group<T>((const T*)pr.row, pos, V, aligned, lp);
+    if (qr) load_group<T>((const T*)qr->row, pos, V, aligned, lq);
+  }
   double t = 0.0;
 #pragma unroll
   for (int q = 0; q < kVec; ++q) {
-    const int v = c0 + threadIdx.x * kVec + q;
-    w[q] = v < V ? resid_weight<T>(pr, qr, invT, v) : 0.0;
-    t += w[q];
+    double wq = 0.0;
+    if (q < n) {
+      wq = prob_from(pr, invT, lp[q], pos + q);
+      if (qr) {
+        wq -= prob_from(*qr, invT, lq[q], pos + q);
+        wq = wq > 0.0 ? wq : 0.0;
+      }
+    }
+    w[q] = wq;
+    t += wq;
   }
   return block_exscan(t, red, tot);
 }
@@ -722,15 +666,16 @@ DEV int pick_in_chunk(double base, double ex, const double w[kVec], int c0, doub
   return y;
 }
 
-// Inverse CDF over a whole row inside one workgroup: y = min{v : C_v > ur * S'}.
+// Inverse CDF over a whole row inside one workgroup (the empty-residual
+// fallback): y = min{v : C_v > ur * S'}.
 template <typename T>
-DEV int resid_draw(const RowView& pr, const RowView* qr, double invT, int V, double ur,
+DEV int resid_draw(const RowView& pr, const RowView* qr, double invT, int V, int aligned, double ur,
                    double* red, int* sh_int, double* S_out) {
   double w[kVec];
   double S = 0.0;
   for (int c0 = 0; c0 < V; c0 += kResidSeg) {
     double tot;
-    resid_chunk<T>(pr, qr, invT, V, c0, w, red, &tot);
+    resid_chunk<T>(pr, qr, invT, V, aligned, c0, w, red, &tot);
     S += tot;
   }
   *S_out = S;
@@ -740,23 +685,14 @@ DEV int resid_draw(const RowView& pr, const RowView* qr, double invT, int V, dou
   int lastc = 0;
   for (int c0 = 0; c0 < V; c0 += kResidSeg) {
     double tot;
-    const double ex = resid_chunk<T>(pr, qr, invT, V, c0, w, red, &tot);
+    const double ex = resid_chunk<T>(pr, qr, invT, V, aligned, c0, w, red, &tot);
     if (tot > 0.0) lastc = c0;
     if (base + tot > t) return pick_in_chunk(base, ex, w, c0, t, sh_int);
     base += tot;
   }
-  // t >= S (cannot happen for ur < 1): last positive entry of the last positive chunk
   double tot;
-  const double ex = resid_chunk<T>(pr, qr, invT, V, lastc, w, red, &tot);
+  const double ex = resid_chunk<T>(pr, qr, invT, V, aligned, lastc, w, red, &tot);
   return pick_in_chunk(-INFINITY, ex, w, lastc, INFINITY, sh_int);
-}
-
-template <typename T>
-DEV void write_resid_probs(const Params& p, int b, const RowView& pr, const RowView* qr,
-                           double invT, double S) {
-  float* rp = p.resid_probs + (size_t)b * p.V;
-  for (int v = threadIdx.x; v < p.V; v += kBlock)
-    rp[v] = (float)(resid_weight<T>(pr, qr, invT, v) / S);
 }
 
 // Block-wide check of the rows of a sequence whose probes saw a non-finite
@@ -774,13 +710,15 @@ DEV bool rows_bad(const Params& p, int b, const int* flag, int nrows) {
   return false;
 }
 
-// ================================================================== epilogue: greedy chain
+// ================================================================== greedy chain
 
 template <typename T>
-DEV void epi_greedy(const Params& p, int b) {
+__global__ __launch_bounds__(kBlock) void k_greedy_final(Params p) {
   __shared__ int rA[kMaxRows];
   __shared__ int rBad[kMaxRows];
+  __shared__ int sx[64];
   __shared__ int sh_n, sh_st;
+  const int b = blockIdx.x;
   const int k = p.k, V = p.V;
   const int32_t* x = p.tokens + (size_t)b * k;
   for (int j = threadIdx.x; j <= k; j += kBlock) {
@@ -789,13 +727,14 @@ DEV void epi_greedy(const Params& p, int b) {
     int bad = (rs.M == INFINITY) || (rs.M == -INFINITY) || (rs.M != rs.M) || (rs.amax == INT_MAX);
     if (!bad && rs.probe) bad = 2;
     rBad[j] = bad;
+    if (j < k) sx[j] = x[j];
   }
   __syncthreads();
   if (rows_bad<T>(p, b, rBad, k + 1)) { emit_invalid(p, b, 4); return; }
   if (threadIdx.x == 0) {
     int n = k, st = 0;
     for (int j = 0; j < k; ++j) {
-      const int xj = x[j];
+      const int xj = sx[j];
       if (xj < 0 || xj >= V) { st |= 1; n = j; break; }
       if (xj != rA[j]) { n = j; break; }
     }
@@ -805,16 +744,19 @@ DEV void epi_greedy(const Params& p, int b) {
   emit_tokens(p, b, x, sh_n, rA[sh_n], sh_st);
 }
 
-// ================================================================== epilogue: token tree
+// ================================================================== token tree
 
 template <typename T>
-DEV void epi_tree(const Params& p, int b) {
+__global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
   __shared__ int g[kMaxTree];
+  __shared__ int spar[kMaxTree];
+  __shared__ int stok[kMaxTree];
   __shared__ short jmp[2][kMaxTree];
   __shared__ short dep[2][kMaxTree];
   __shared__ unsigned char val[2][kMaxTree];
   __shared__ int rBad[kMaxTree];
   __shared__ int sh_st, sh_best;
+  const int b = blockIdx.x;
   const int N = p.k, V = p.V, tid = threadIdx.x;
   const int32_t* par = p.parents + (size_t)b * N;
   const int32_t* tok = p.tokens + (size_t)b * N;
@@ -825,12 +767,14 @@ DEV void epi_tree(const Params& p, int b) {
     int bad = (rs.M == INFINITY) || (rs.M == -INFINITY) || (rs.M != rs.M) || (rs.amax == INT_MAX);
     if (!bad && rs.probe) bad = 2;
     rBad[i] = bad;
+    spar[i] = par[i];
+    stok[i] = tok[i];
   }
   __syncthreads();
   if (rows_bad<T>(p, b, rBad, N)) { emit_invalid(p, b, 4); return; }
   int st = 0;
   for (int i = tid; i < N; i += kBlock) {
-    const int pi = par[i];
+    const int pi = spar[i];
     int ok, j, d;
     if (i == 0) {
       if (pi != -1) st |= 2;
@@ -838,7 +782,7 @@ DEV void epi_tree(const Params& p, int b) {
     } else if (pi < 0 || pi >= i) {
       st |= 2; ok = 0; j = -1; d = 0;
     } else {
-      const int t = tok[i];
+      const int t = stok[i];
       if (t < 0 || t >= V) { st |= 1; ok = 0; }
       else ok = (t == g[pi]);
       j = pi; d = 1;
@@ -872,109 +816,35 @@ DEV void epi_tree(const Params& p, int b) {
   __syncthreads();
   const int best = 2047 - (sh_best & 2047);
   const int n = sh_best >> 11;
+  // the path root..best, written from LDS by the lanes of one wave
   if (tid == 0) {
     int32_t* ot = p.out_tokens + (size_t)b * p.out_w;
     int32_t* on = p.out_nodes ? p.out_nodes + (size_t)b * p.out_w : nullptr;
-    for (int i = n + 1; i < p.out_w; ++i) { ot[i] = -1; if (on) on[i] = -1; }
     ot[n] = g[best];
     int node = best;
     for (int d = n; d >= 0; --d) {
       if (on) on[d] = node;
-      if (d > 0) { ot[d - 1] = tok[node]; node = par[node]; }
+      if (d > 0) { ot[d - 1] = stok[node]; node = spar[node]; }
     }
     p.acc_len[b] = n;
     if (p.seq_status) p.seq_status[b] = sh_st;
   }
+  for (int i = n + 1 + tid; i < p.out_w; i += kBlock) {
+    p.out_tokens[(size_t)b * p.out_w + i] = -1;
+    if (p.out_nodes) p.out_nodes[(size_t)b * p.out_w + i] = -1;
+  }
 }
 
-// ================================================================== epilogue: plain sampling accept step
+// ================================================================== top-k
 
-// The accept step of plain sampling for sequence b.  Returns false if a row
-// is invalid (the outputs are then written by the workgroup with `emit`).
-// *n = accepted count, *st = status bits, *Mp / *Mq = raw maxima of target
-// row n and draft row n.
+// Merge the S tile lists of one row and publish its kept set.
 template <typename T>
-DEV bool accept_step(const Params& p, int b, bool emit, int* n_out, int* st_out, float* Mp,
-                     float* Mq) {
-  __shared__ float rM[kMaxRows];
-  __shared__ double rZ[kMaxRows];
-  __shared__ int rBad[kMaxRows];
-  __shared__ int sh_dec[64];
-  __shared__ double red[kWaves];
-  const int k = p.k, V = p.V, tid = threadIdx.x;
-  const double invT = 1.0 / p.T;
-  const int nrows = p.rows_t + p.rows_d;
-  const int32_t* x = p.tokens + (size_t)b * k;
-  for (int r = tid; r < nrows; r += kBlock) {
-    const int grow = r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t);
-    const RowStat rs = combine_tiles(p, grow, true);
-    rM[r] = rs.M; rZ[r] = rs.Z;
-    rBad[r] = (rs.Z != rs.Z) || (rs.M == INFINITY) || (rs.M == -INFINITY);
-  }
-  __syncthreads();
-  if (rows_bad<T>(p, b, rBad, nrows)) {
-    if (emit) emit_invalid(p, b, 4);
-    return false;
-  }
-  const T* tgt = (const T*)p.target + (size_t)b * p.rows_t * V;
-  const T* dft = (const T*)p.draft + (size_t)b * p.rows_d * V;
-  // decisions per position: 0 reject, 1 accept, 2 inside the float32 error
-  // bound (redo in float64), 3 bad token
-  for (int j = tid; j < k; j += kBlock) {
-    const int xj = x[j];
-    int dec;
-    if (xj < 0 || xj >= V) dec = 3;
-    else {
-      RowView pv{tgt + (size_t)j * V, (double)rM[j] * invT, rZ[j], 0ull};
-      RowView qv{dft + (size_t)j * V, (double)rM[p.rows_t + j] * invT, rZ[p.rows_t + j], 0ull};
-      const double a = prob_of<T>(pv, invT, xj);
-      const double bq = prob_of<T>(qv, invT, xj);
-      const double u = (double)p.u[(size_t)b * k + j];
-      if (bq > 0.0) {
-        const double ratio = a / bq;
-        if (fabs(u - ratio) <= kCertRel * ratio) dec = 2;
-        else dec = u < fmin(1.0, ratio) ? 1 : 0;
-      } else {
-        dec = a > 0.0 ? 1 : 0;
-      }
-    }
-    sh_dec[j] = dec;
-  }
-  __syncthreads();
-  int n = k, st = 0;
-  for (int j = 0; j < k; ++j) {
-    int dec = sh_dec[j];
-    if (dec == 2) {
-      const T* trw = tgt + (size_t)j * V;
-      const T* drw = dft + (size_t)j * V;
-      const double zp = (double)rM[j] * invT, zq = (double)rM[p.rows_t + j] * invT;
-      const double Zp = exact_row_sum<T>(trw, V, invT, zp, red);
-      const double Zq = exact_row_sum<T>(drw, V, invT, zq, red);
-      const int xj = x[j];
-      const double a = exp((double)Io<T>::at(trw, xj) * invT - zp) / Zp;
-      const double bq = exp((double)Io<T>::at(drw, xj) * invT - zq) / Zq;
-      const double u = (double)p.u[(size_t)b * k + j];
-      dec = bq > 0.0 ? (u < fmin(1.0, a / bq) ? 1 : 0) : (a > 0.0 ? 1 : 0);
-    }
-    if (dec == 3) { st |= 1; n = j; break; }
-    if (dec == 0) { n = j; break; }
-  }
-  *n_out = n;
-  *st_out = st;
-  *Mp = rM[n];
-  *Mq = n < k ? rM[p.rows_t + n] : 0.f;
-  __syncthreads();
-  return true;
-}
-
-// ================================================================== epilogues: top-k
-
-// Merge the S tile lists of row `grow` and publish its kept set.
-template <typename T>
-DEV void epi_topk_row(const Params& p, int grow, uint64_t* buf) {
+__global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
+  __shared__ uint64_t buf[kTopkCap];
   __shared__ double red[kWaves];
   __shared__ int sh_n, sh_kept, sh_probe;
   __shared__ double sh_mass;
+  const int grow = blockIdx.x;
   const int tid = threadIdx.x;
   const int K = p.top_k;
   const int total = p.S * p.cand_w;             // <= kTopkCap (host-checked)
@@ -1013,7 +883,6 @@ DEV void epi_topk_row(const Params& p, int grow, uint64_t* buf) {
   double norm = Z;
   if (p.top_p < 1.0 && n > 0 && !bad) {
     // nucleus on the kept set: rank order is already probability order
-    __threadfence_block();
     __syncthreads();
     if (tid == 0) {
       double before = 0.0, mass = 0.0;
@@ -1050,18 +919,21 @@ DEV double kept_prob_1(const Params& p, int grow, int x) {
 }
 
 template <typename T>
-DEV void epi_topk_seq(const Params& p, int b, uint64_t* buf) {
+__global__ __launch_bounds__(kBlock) void k_topk_final(Params p) {
+  __shared__ uint64_t buf[kTopkMax];
   __shared__ double rw[kTopkMax];
+  __shared__ int sidx[kTopkMax];
   __shared__ int sh_dec[64];
   __shared__ int sh_bad, sh_n, sh_st, sh_y;
   __shared__ double sh_S;
+  const int b = blockIdx.x;
   const int k = p.k, V = p.V, tid = threadIdx.x, K = p.top_k;
   const int32_t* x = p.tokens + (size_t)b * k;
-  if (tid == 0) {
-    int bad = 0;
-    for (int j = 0; j <= k; ++j) bad |= p.k_bad[trow(p, b, j)];
-    for (int j = 0; j < k; ++j) bad |= p.k_bad[drow(p, b, j)];
-    sh_bad = bad;
+  if (tid == 0) sh_bad = 0;
+  __syncthreads();
+  for (int r = tid; r < p.rows_t + p.rows_d; r += kBlock) {
+    const int grow = r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t);
+    if (p.k_bad[grow]) sh_bad = 1;
   }
   __syncthreads();
   if (sh_bad) { emit_invalid(p, b, 4); return; }
@@ -1095,6 +967,7 @@ DEV void epi_topk_seq(const Params& p, int b, uint64_t* buf) {
   const double* pe = p.k_e + (size_t)gp * K;
   for (int i = tid; i < np; i += kBlock) {
     const double pa = pe[i] / normp;
+    sidx[i] = pidx[i];
     if (n < k) {
       const double qa = kept_prob_1(p, drow(p, b, n), pidx[i]);
       const double d = pa - qa;
@@ -1121,8 +994,8 @@ DEV void epi_topk_seq(const Params& p, int b, uint64_t* buf) {
     for (int i = 0; i < np; ++i) {
       const int sl = (int)(buf[i] & 0xffffffffu);
       c += rw[sl];
-      if (rw[sl] > 0.0) lastpos = pidx[sl];
-      if (y < 0 && rw[sl] > 0.0 && c > t) y = pidx[sl];
+      if (rw[sl] > 0.0) lastpos = sidx[sl];
+      if (y < 0 && rw[sl] > 0.0 && c > t) y = sidx[sl];
     }
     sh_y = y < 0 ? lastpos : y;
     sh_S = S;
@@ -1132,128 +1005,111 @@ DEV void epi_topk_seq(const Params& p, int b, uint64_t* buf) {
     float* rp = p.resid_probs + (size_t)b * V;
     for (int v = tid; v < V; v += kBlock) rp[v] = 0.f;
     __syncthreads();
-    for (int i = tid; i < np; i += kBlock) rp[pidx[i]] = (float)(rw[i] / sh_S);
+    for (int i = tid; i < np; i += kBlock) rp[sidx[i]] = (float)(rw[i] / sh_S);
   }
   emit_tokens(p, b, x, n, sh_y, sh_st);
 }
 
-// ================================================================== kernels
-
-template <typename T, int MODE>
-__global__ __launch_bounds__(kBlock) void k_stream(Params p) {
-  const int tile = blockIdx.x;
-  const int grow = tile / p.S;
-  const int seg = tile - grow * p.S;
-  const T* row = row_ptr<T>(p, grow);
-  const int start = seg * p.L;
-  const int end = min(start + p.L, p.V);
-  const int ngroups = (end - start + kVec - 1) / kVec;
-  if constexpr (MODE == kModeTopk) {
-    __shared__ uint64_t buf[kTopkCap];
-    tile_topk<T>(p, row, start, end, ngroups, tile, buf);
-  } else if constexpr (MODE == kModeStats) {
-    tile_stats<T>(p, row, start, end, ngroups, tile);
-  } else if constexpr (MODE == kModeStats64) {
-    tile_stats64<T>(p, row, start, end, ngroups, tile);
-  } else {
-    tile_argmax<T>(p, row, start, end, ngroups, tile);
-  }
-}
-
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_greedy_final(Params p) { epi_greedy<T>(p, blockIdx.x); }
-
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_tree_final(Params p) { epi_tree<T>(p, blockIdx.x); }
-
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
-  __shared__ uint64_t buf[kTopkCap];
-  epi_topk_row<T>(p, blockIdx.x, buf);
-}
-
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_topk_final(Params p) {
-  __shared__ uint64_t buf[kTopkMax];
-  epi_topk_seq<T>(p, blockIdx.x, buf);
-}
-
-// ================================================================== residual kernels (plain sampling)
+// ================================================================== plain and nucleus sampling
 //
-// k_resid_z    every workgroup of a sequence redoes its accept step (a few
-//              dozen partials and k logits), then sums exp(z - zmax) in
-//              float64 over one segment of target row n and draft row n;
-//              segment 0 publishes n for the next kernels.
-// k_resid_s    residual mass max(0, p' - q') per segment, float64.
-// k_resid_final one workgroup per sequence: S' = sum of the segments, the
-//              segment where ur * S' falls, the entry inside it, outputs.
+// After the stream pass (float64 row sums per tile) -- and, for the nucleus,
+// the exact cut per row (k_topp_rows) -- two kernels finish a call:
+//   k_resid_s     grid (segment, sequence): every workgroup of a sequence
+//                 redoes its accept step (k tests on a few dozen partials and
+//                 2k logits), then sums the residual max(0, p' - q') (or p'_k
+//                 after full acceptance) over its segment of kResidSeg
+//                 entries in float64; segment 0 publishes the sequence state.
+//   k_resid_final one workgroup per sequence: S' = sum of the segments, the
+//                 segment where ur * S' falls, the entry inside it, outputs.
 
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_resid_z(Params p) {
-  __shared__ double red[kWaves];
-  const int b = blockIdx.y, seg = blockIdx.x;
-  int n, st;
-  float Mp, Mq;
-  if (!accept_step<T>(p, b, seg == 0, &n, &st, &Mp, &Mq)) {
-    if (seg == 0 && threadIdx.x == 0) p.seq_n[b] = -1;
-    return;
+// The adjusted view of row `grow` (FILT: kFiltNone or kFiltTopp).
+template <typename T, int FILT>
+DEV RowView sample_view(const Params& p, int grow, double invT, bool* bad) {
+  if constexpr (FILT == kFiltTopp) {
+    const RowNuc nu = p.nuc[grow];
+    *bad = nu.ok != 1;
+    return RowView{row_ptr<T>(p, grow), (double)nu.M * invT, nu.N, nu.cut};
+  } else {
+    const RowStat rs = combine_tiles(p, grow, true);
+    *bad = (rs.Z != rs.Z) || (rs.M == INFINITY) || (rs.M == -INFINITY);
+    return RowView{row_ptr<T>(p, grow), (double)rs.M * invT, rs.Z, 0ull};
   }
-  const int V = p.V, k = p.k;
+}
+
+// The accept step of sequence b.  Returns false if a row is invalid (the
+// outputs are then written by the workgroup with `emit`).
+template <typename T, int FILT>
+DEV bool accept_step(const Params& p, int b, bool emit, int* n_out, int* st_out) {
+  __shared__ int rBad[kMaxRows];
+  __shared__ int sh_dec[64];
+  __shared__ int sh_internal;
+  const int k = p.k, V = p.V, tid = threadIdx.x;
   const double invT = 1.0 / p.T;
-  const T* prow = row_ptr<T>(p, trow(p, b, n));
-  const T* qrow = n < k ? row_ptr<T>(p, drow(p, b, n)) : nullptr;
-  const double zp = (double)Mp * invT;
-  const double zq = (double)Mq * invT;
-  const int c0 = seg * kResidSeg;
-  const int c1 = min(c0 + kResidSeg, V);
-  double sp = 0.0, sq = 0.0;
-  for (int i = c0 + threadIdx.x; i < c1; i += kBlock) {
-    sp += exp((double)Io<T>::at(prow, i) * invT - zp);
-    if (qrow) sq += exp((double)Io<T>::at(qrow, i) * invT - zq);
+  const int nrows = p.rows_t + p.rows_d;
+  const int32_t* x = p.tokens + (size_t)b * k;
+  if (tid == 0) sh_internal = 0;
+  __syncthreads();
+  for (int r = tid; r < nrows; r += kBlock) {
+    const int grow = r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t);
+    bool bad;
+    sample_view<T, FILT>(p, grow, invT, &bad);
+    rBad[r] = bad ? 1 : 0;
+    if (FILT == kFiltTopp && p.nuc[grow].ok == 2) sh_internal = kStatusInternal;
   }
-  sp = block_sum(sp, red);
-  sq = block_sum(sq, red);
-  if (threadIdx.x == 0) {
-    p.zpart[((size_t)b * p.S2 + seg) * 2] = sp;
-    p.zpart[((size_t)b * p.S2 + seg) * 2 + 1] = sq;
-    if (seg == 0) {
-      p.seq_n[b] = n;
-      p.seq_st[b] = st;
-      p.seq_M[2 * b] = Mp;
-      p.seq_M[2 * b + 1] = Mq;
+  __syncthreads();
+  if (rows_bad<T>(p, b, rBad, nrows)) {
+    if (emit) emit_invalid(p, b, 4 | sh_internal);
+    return false;
+  }
+  for (int j = tid; j < k; j += kBlock) {
+    const int xj = x[j];
+    int dec;
+    if (xj < 0 || xj >= V) dec = 3;
+    else {
+      bool dummy;
+      const double a = prob_of<T>(sample_view<T, FILT>(p, trow(p, b, j), invT, &dummy), invT, xj);
+      const double bq = prob_of<T>(sample_view<T, FILT>(p, drow(p, b, j), invT, &dummy), invT, xj);
+      const double u = (double)p.u[(size_t)b * k + j];
+      dec = bq > 0.0 ? (u < fmin(1.0, a / bq) ? 1 : 0) : (a > 0.0 ? 1 : 0);
     }
+    sh_dec[j] = dec;
   }
+  __syncthreads();
+  int n = k, st = 0;
+  for (int j = 0; j < k; ++j) {
+    if (sh_dec[j] == 3) { st |= 1; n = j; break; }
+    if (sh_dec[j] == 0) { n = j; break; }
+  }
+  *n_out = n;
+  *st_out = st;
+  __syncthreads();
+  return true;
 }
 
-// The two residual rows of sequence b as views with their float64 sums.
-template <typename T>
-DEV void resid_views(const Params& p, int b, int n, RowView* pr, RowView* qr) {
-  const double invT = 1.0 / p.T;
-  double Zp = 0.0, Zq = 0.0;
-  for (int s = 0; s < p.S2; ++s) {
-    Zp += p.zpart[((size_t)b * p.S2 + s) * 2];
-    Zq += p.zpart[((size_t)b * p.S2 + s) * 2 + 1];
-  }
-  *pr = RowView{row_ptr<T>(p, trow(p, b, n)), (double)p.seq_M[2 * b] * invT, Zp, 0ull};
-  *qr = RowView{n < p.k ? row_ptr<T>(p, drow(p, b, n)) : nullptr,
-                (double)p.seq_M[2 * b + 1] * invT, Zq, 0ull};
-}
-
-template <typename T>
+template <typename T, int FILT>
 __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   __shared__ double red[kWaves];
   const int b = blockIdx.y, seg = blockIdx.x;
-  const int n = p.seq_n[b];
-  if (n < 0) return;
-  RowView pr, qrv;
-  resid_views<T>(p, b, n, &pr, &qrv);
+  int n, st;
+  if (!accept_step<T, FILT>(p, b, seg == 0, &n, &st)) {
+    if (seg == 0 && threadIdx.x == 0) p.seq_n[b] = -1;
+    return;
+  }
+  const double invT = 1.0 / p.T;
+  bool dummy;
+  const RowView pr = sample_view<T, FILT>(p, trow(p, b, n), invT, &dummy);
+  RowView qrv{nullptr, 0.0, 1.0, 0ull};
+  if (n < p.k) qrv = sample_view<T, FILT>(p, drow(p, b, n), invT, &dummy);
   double w[kVec];
   double tot;
-  resid_chunk<T>(pr, n < p.k ? &qrv : nullptr, 1.0 / p.T, p.V, seg * kResidSeg, w, red, &tot);
-  if (threadIdx.x == 0) p.spart[(size_t)b * p.S2 + seg] = tot;
+  resid_chunk<T>(pr, n < p.k ? &qrv : nullptr, invT, p.V, p.aligned, seg * kResidSeg, w, red, &tot);
+  if (threadIdx.x == 0) {
+    p.spart[(size_t)b * p.S2 + seg] = tot;
+    if (seg == 0) { p.seq_n[b] = n; p.seq_st[b] = st; }
+  }
 }
 
-template <typename T>
+template <typename T, int FILT>
 __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   __shared__ double red[kWaves];
   __shared__ int sh_int, sh_c;
@@ -1263,8 +1119,10 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   if (n < 0) return;
   const int V = p.V, k = p.k;
   const double invT = 1.0 / p.T;
-  RowView pr, qrv;
-  resid_views<T>(p, b, n, &pr, &qrv);
+  bool dummy;
+  const RowView pr = sample_view<T, FILT>(p, trow(p, b, n), invT, &dummy);
+  RowView qrv{nullptr, 0.0, 1.0, 0ull};
+  if (n < k) qrv = sample_view<T, FILT>(p, drow(p, b, n), invT, &dummy);
   const RowView* qr = n < k ? &qrv : nullptr;
   const int32_t* x = p.tokens + (size_t)b * k;
   const double ur = (double)p.ur[b];
@@ -1293,14 +1151,50 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
     __syncthreads();
     double w[kVec];
     double tc;
-    const double ex = resid_chunk<T>(pr, qr, invT, V, c * kResidSeg, w, red, &tc);
+    const double ex = resid_chunk<T>(pr, qr, invT, V, p.aligned, c * kResidSeg, w, red, &tc);
     y = pick_in_chunk(base, ex, w, c * kResidSeg, t, &sh_int);
   } else {
-    y = resid_draw<T>(pr, nullptr, invT, V, ur, red, &sh_int, &S);   // empty residual: p'_n
+    y = resid_draw<T>(pr, nullptr, invT, V, p.aligned, ur, red, &sh_int, &S);   // empty residual: p'_n
     p_only = true;
   }
-  if (p.resid_probs) write_resid_probs<T>(p, b, pr, p_only ? nullptr : qr, invT, S);
+  if (p.resid_probs) {
+    float* rp = p.resid_probs + (size_t)b * V;
+    const RowView* q2 = p_only ? nullptr : qr;
+    for (int c0 = 0; c0 < V; c0 += kResidSeg) {
+      double w[kVec];
+      double tot;
+      resid_chunk<T>(pr, q2, invT, V, p.aligned, c0, w, red, &tot);
+#pragma unroll
+      for (int q = 0; q < kVec; ++q) {
+        const int v = c0 + threadIdx.x * kVec + q;
+        if (v < V) rp[v] = (float)(w[q] / S);
+      }
+    }
+  }
   emit_tokens(p, b, x, n, y, p.seq_st[b]);
+}
+
+// ================================================================== stream kernel
+
+// One workgroup per tile; the host picks about four tiles per resident
+// workgroup so that the last, partial wave of workgroups is short.
+template <typename T, int MODE>
+__global__ __launch_bounds__(kBlock) void k_stream(Params p) {
+  const int tile = blockIdx.x;
+  const int grow = tile / p.S;
+  const int seg = tile - grow * p.S;
+  const T* row = row_ptr<T>(p, grow);
+  const int start = seg * p.L;
+  const int end = min(start + p.L, p.V);
+  const int ngroups = (end - start + kVec - 1) / kVec;
+  if constexpr (MODE == kModeTopk) {
+    __shared__ uint64_t buf[kTopkCap];
+    tile_topk<T>(p, row, start, end, ngroups, tile, buf);
+  } else if constexpr (MODE == kModeStats64) {
+    tile_stats64<T>(p, row, start, end, ngroups, tile);
+  } else {
+    tile_argmax<T>(p, row, start, end, ngroups, tile);
+  }
 }
 
 // ================================================================== nucleus
@@ -1362,8 +1256,8 @@ DEV double nuc_bin_ref(const NucState& s, int b) {
 // mass of everything ranked above the level's range, *below the count ranked
 // below it (and still < dmax).
 template <typename T>
-DEV void nuc_hist(const T* row, int V, NucState s, unsigned long long* hq, unsigned int* hc,
-                  unsigned int* below, double* red, double* A) {
+DEV void nuc_hist(const T* row, int V, int aligned, NucState s, unsigned long long* hq,
+                  unsigned int* hc, unsigned int* below, double* red, double* A) {
   for (int b = threadIdx.x; b < kNucBins; b += kBlock) { hq[b] = 0ull; hc[b] = 0u; }
   if (threadIdx.x == 0) *below = 0u;
   __syncthreads();
@@ -1371,8 +1265,12 @@ DEV void nuc_hist(const T* row, int V, NucState s, unsigned long long* hq, unsig
   const double ref1 = (double)s.p0lo * s.w0;
   double a = 0.0;
   unsigned int nb = 0;
-  for (int i = threadIdx.x; i < V; i += kBlock) {
-    const float l = Io<T>::at(row, i);
+  for (int g = threadIdx.x; g * kVec < V; g += kBlock) {
+   float vv[kVec];
+   const int ng = load_group<T>(row, g * kVec, V, aligned, vv);
+   for (int e = 0; e < ng; ++e) {
+    const int i = g * kVec + e;
+    const float l = vv[e];
     const double d = s.zm - (double)l * s.invT;
     if (!(d < s.dmax)) continue;
     int bin;
@@ -1385,6 +1283,7 @@ DEV void nuc_hist(const T* row, int V, NucState s, unsigned long long* hq, unsig
       atomicAdd(&hq[bin], (unsigned long long)(rel * 4294967296.0f));
       atomicAdd(&hc[bin], 1u);
     }
+   }
   }
   if (nb) atomicAdd(below, nb);
   *A = block_sum(a, red);
@@ -1446,7 +1345,7 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
   s.c0 = 0; s.c1 = kNucBins - 1;
 
   double A = 0.0;
-  nuc_hist<T>(row, V, s, hq, hc, &below, red, &A);
+  nuc_hist<T>(row, V, p.aligned, s, hq, hc, &below, red, &A);
   const double tgt = p.top_p * Z;
   bool located = false;
   int result = 0;   // 1 found, -1 failed
@@ -1473,15 +1372,21 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
       if (tid == 0) wcnt = 0u;
       __syncthreads();
       double a = 0.0;
-      for (int i = tid; i < V; i += kBlock) {
-        const float l = Io<T>::at(row, i);
-        const double d = s.zm - (double)l * s.invT;
-        int bin;
-        const int cls = nuc_class(s, l, i, d, &bin);
-        if (cls == -1) a += exp(-d);
-        else if (cls == 0) {
-          const unsigned slot = atomicAdd(&wcnt, 1u);
-          if (slot < (unsigned)kWindowCap) win[slot] = pack(l, i);
+      for (int g = tid; g * kVec < V; g += kBlock) {
+        float vv[kVec];
+        const int ng = load_group<T>(row, g * kVec, V, p.aligned, vv);
+        for (int e = 0; e < ng; ++e) {
+          const int i = g * kVec + e;
+          const float l = vv[e];
+          const double d = s.zm - (double)l * s.invT;
+          if (!(d < s.dmax)) continue;
+          int bin;
+          const int cls = nuc_class(s, l, i, d, &bin);
+          if (cls == -1) a += exp(-d);
+          else if (cls == 0) {
+            const unsigned slot = atomicAdd(&wcnt, 1u);
+            if (slot < (unsigned)kWindowCap) win[slot] = pack(l, i);
+          }
         }
       }
       const double Aw = block_sum(a, red);
@@ -1539,14 +1444,19 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
       if (tid == 0) { sh_pmin = ~0ull; sh_pmax = 0ull; }
       __syncthreads();
       unsigned long long pmin = ~0ull, pmax = 0ull;
-      for (int i = tid; i < V; i += kBlock) {
-        const float l = Io<T>::at(row, i);
-        const double d = s.zm - (double)l * s.invT;
-        int bin;
-        if (nuc_class(s, l, i, d, &bin) == 0) {
-          const unsigned long long pk = pack(l, i);
-          pmin = pk < pmin ? pk : pmin;
-          pmax = pk > pmax ? pk : pmax;
+      for (int g = tid; g * kVec < V; g += kBlock) {
+        float vv[kVec];
+        const int ng = load_group<T>(row, g * kVec, V, p.aligned, vv);
+        for (int e = 0; e < ng; ++e) {
+          const int i = g * kVec + e;
+          const float l = vv[e];
+          const double d = s.zm - (double)l * s.invT;
+          int bin;
+          if (nuc_class(s, l, i, d, &bin) == 0) {
+            const unsigned long long pk = pack(l, i);
+            pmin = pk < pmin ? pk : pmin;
+            pmax = pk > pmax ? pk : pmax;
+          }
         }
       }
       atomicMin(&sh_pmin, pmin);
@@ -1559,74 +1469,13 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
       int bits = span ? 64 - __clzll((long long)span) : 0;
       s.sh = bits > 11 ? bits - 11 : 0;
       s.level += 1;
-      nuc_hist<T>(row, V, s, hq, hc, &below, red, &A);
+      nuc_hist<T>(row, V, p.aligned, s, hq, hc, &below, red, &A);
       located = false;
     }
   }
   out.ok = result == 1 ? 1 : 2;
 }
 
-
-// ================================================================== epilogue: nucleus sampling
-
-template <typename T>
-DEV void epi_topp_seq(const Params& p, int b) {
-  __shared__ int sh_dec[64];
-  __shared__ int sh_bad, sh_int;
-  __shared__ double red[kWaves];
-  const int k = p.k, V = p.V, tid = threadIdx.x;
-  const double invT = 1.0 / p.T;
-  const int32_t* x = p.tokens + (size_t)b * k;
-  if (tid == 0) {
-    int bad = 0;
-    for (int r = 0; r < p.rows_t + p.rows_d; ++r) {
-      const int grow = r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t);
-      const int ok = p.nuc[grow].ok;
-      if (ok != 1) bad |= 4;
-      if (ok == 2) bad |= kStatusInternal;
-    }
-    sh_bad = bad;
-  }
-  __syncthreads();
-  if (sh_bad) { emit_invalid(p, b, sh_bad); return; }
-  auto view = [&](int grow) {
-    const RowNuc nu = p.nuc[grow];
-    RowView v{row_ptr<T>(p, grow), (double)nu.M * invT, nu.N, nu.cut};
-    return v;
-  };
-  for (int j = tid; j < k; j += kBlock) {
-    const int xj = x[j];
-    int dec;
-    if (xj < 0 || xj >= V) dec = 3;
-    else {
-      const double a = prob_of<T>(view(trow(p, b, j)), invT, xj);
-      const double bq = prob_of<T>(view(drow(p, b, j)), invT, xj);
-      const double u = (double)p.u[(size_t)b * k + j];
-      dec = bq > 0.0 ? (u < fmin(1.0, a / bq) ? 1 : 0) : (a > 0.0 ? 1 : 0);
-    }
-    sh_dec[j] = dec;
-  }
-  __syncthreads();
-  int n = k, st = 0;
-  for (int j = 0; j < k; ++j) {
-    if (sh_dec[j] == 3) { st |= 1; n = j; break; }
-    if (sh_dec[j] == 0) { n = j; break; }
-  }
-  const RowView pr = view(trow(p, b, n));
-  RowView qrv;
-  const RowView* qr = nullptr;
-  if (n < k) { qrv = view(drow(p, b, n)); qr = &qrv; }
-  double S;
-  const double ur = (double)p.ur[b];
-  int y = resid_draw<T>(pr, qr, invT, V, ur, red, &sh_int, &S);
-  bool p_only = (qr == nullptr);
-  if (y < 0) {
-    y = resid_draw<T>(pr, nullptr, invT, V, ur, red, &sh_int, &S);
-    p_only = true;
-  }
-  if (p.resid_probs) write_resid_probs<T>(p, b, pr, p_only ? nullptr : qr, invT, S);
-  emit_tokens(p, b, x, n, y, st);
-}
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
@@ -1659,20 +1508,36 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   }
 }
 
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_topp_final(Params p) { epi_topp_seq<T>(p, blockIdx.x); }
-
 
 // ================================================================== launchers
 
 template <typename T>
-static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st) {
-  const int rows = p.B * (p.rows_t + p.rows_d);
-  const dim3 grid((unsigned)rows * (unsigned)p.S), block(kBlock);
-  if (mode == kModeStats) hipLaunchKernelGGL((k_stream<T, kModeStats>), grid, block, 0, st, p);
-  else if (mode == kModeTopk) hipLaunchKernelGGL((k_stream<T, kModeTopk>), grid, block, 0, st, p);
-  else if (mode == kModeStats64) hipLaunchKernelGGL((k_stream<T, kModeStats64>), grid, block, 0, st, p);
-  else hipLaunchKernelGGL((k_stream<T, kModeArgmax>), grid, block, 0, st, p);
+static int capacity_t(int mode) {
+  int per_cu = 0;
+  hipError_t e;
+  if (mode == kModeStats64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeStats64>, kBlock, 0);
+  else if (mode == kModeTopk) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopk>, kBlock, 0);
+  else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeArgmax>, kBlock, 0);
+  return e == hipSuccess ? per_cu : 0;
+}
+
+int stream_blocks_per_cu(int mode, int bf16) {
+  return bf16 ? capacity_t<uint16_t>(mode) : capacity_t<float>(mode);
+}
+
+// With ev_begin / ev_end the dispatch packet itself records the two events
+// (hipExtLaunchKernelGGL), so their difference is the kernel's duration.
+template <typename T>
+static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hipEvent_t e0,
+                                  hipEvent_t e1) {
+  const unsigned grid = (unsigned)((long)p.B * (p.rows_t + p.rows_d) * p.S);
+  const dim3 block(kBlock);
+  if (mode == kModeStats64)
+    hipExtLaunchKernelGGL((k_stream<T, kModeStats64>), dim3(grid), block, 0, st, e0, e1, 0, p);
+  else if (mode == kModeTopk)
+    hipExtLaunchKernelGGL((k_stream<T, kModeTopk>), dim3(grid), block, 0, st, e0, e1, 0, p);
+  else
+    hipExtLaunchKernelGGL((k_stream<T, kModeArgmax>), dim3(grid), block, 0, st, e0, e1, 0, p);
   return hipGetLastError();
 }
 
@@ -1689,19 +1554,21 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
       break;
     case kFiltTopp:
       hipLaunchKernelGGL((k_topp_rows<T>), gr, block, 0, st, p);
-      hipLaunchKernelGGL((k_topp_final<T>), gb, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_s<T, kFiltTopp>), gs, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T, kFiltTopp>), gb, block, 0, st, p);
       break;
     default:  // plain sampling
-      hipLaunchKernelGGL((k_resid_z<T>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_s<T>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T>), gb, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_s<T, kFiltNone>), gs, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), gb, block, 0, st, p);
       break;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st) {
-  return bf16 ? launch_stream_t<uint16_t>(p, mode, st) : launch_stream_t<float>(p, mode, st);
+hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st, hipEvent_t e0,
+                         hipEvent_t e1) {
+  return bf16 ? launch_stream_t<uint16_t>(p, mode, st, e0, e1)
+              : launch_stream_t<float>(p, mode, st, e0, e1);
 }
 
 hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st) {

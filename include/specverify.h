@@ -157,11 +157,11 @@ int specverify_run(specverify_ctx* ctx, int32_t batch,
 void specverify_destroy(specverify_ctx* ctx);
 
 /* Instrumentation for benchmarks: on every later specverify_run of this
- * context, record the HIP event `ev_begin` on the run's stream just before
- * the streaming kernel (the one pass that reads every logit) and `ev_end`
- * just after it, so hipEventElapsedTime gives that kernel's duration.  The
- * events are caller-owned hipEvent_t handles created on the context's device;
- * pass NULL, NULL to stop.  Nothing is skipped or reordered.  Errors:
+ * context, the dispatch of the streaming kernel (the one pass that reads
+ * every logit) records the HIP event `ev_begin` when it starts and `ev_end`
+ * when it completes, so hipEventElapsedTime gives that kernel's duration.
+ * The events are caller-owned hipEvent_t handles created on the context's
+ * device; pass NULL, NULL to stop.  Nothing is skipped or reordered.  Errors:
  * SV_ERR_NULL (ctx NULL, or exactly one event NULL). */
 int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_end);
 
