@@ -56,6 +56,7 @@ Plan make_plan(const sv_config* c) {
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
   p.S_max = (c->vocab + kMinTile - 1) / kMinTile;
+  if (p.S_max > sv::kMaxTiles) p.S_max = sv::kMaxTiles;
   p.cand_w = p.top_k;
   if (p.top_k > 0) {
     const int cap = sv::kMergeCap / p.cand_w;
@@ -67,8 +68,8 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, seq_n, seq_st, spart;
-  size_t k_idx, k_e, k_cnt, k_norm, k_bad, total;
+  size_t tiles, cand, nuc, row_lx, seq, spart;
+  size_t k_idx, k_e, k_cnt, k_norm, k_bad, k_px, total;
 };
 
 Layout layout(const sv_config* c, const Plan& pl) {
@@ -86,14 +87,15 @@ Layout layout(const sv_config* c, const Plan& pl) {
   L.cand = take(pl.top_k > 0 ? rows * (size_t)pl.S_max * (size_t)pl.cand_w * sizeof(uint64_t) : 0);
   L.nuc = take(pl.filt == sv::kFiltTopp ? rows * sizeof(sv::RowNuc) : 0);
   const bool sampled = pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp;
-  L.seq_n = take(B * sizeof(int));
-  L.seq_st = take(B * sizeof(int));
+  L.row_lx = take(sampled ? rows * sizeof(float) : 0);
+  L.seq = take(sampled ? B * sizeof(sv::SeqState) : 0);
   L.spart = take(sampled ? B * (size_t)pl.S2_max * sizeof(double) : 0);
   L.k_idx = take(rows * K * sizeof(int32_t));
   L.k_e = take(rows * K * sizeof(double));
   L.k_cnt = take(K ? rows * sizeof(int32_t) : 0);
   L.k_norm = take(K ? rows * sizeof(double) : 0);
   L.k_bad = take(K ? rows * sizeof(int32_t) : 0);
+  L.k_px = take(K ? rows * sizeof(double) : 0);
   L.total = off;
   return L;
 }
@@ -263,8 +265,8 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.cand_w = pl.cand_w;
   p.nuc = (sv::RowNuc*)(ws + L.nuc);
   (void)maxrows;
-  p.seq_n = (int*)(ws + L.seq_n);
-  p.seq_st = (int*)(ws + L.seq_st);
+  p.row_lx = (float*)(ws + L.row_lx);
+  p.seq = (sv::SeqState*)(ws + L.seq);
   p.spart = (double*)(ws + L.spart);
   p.S2 = pl.S2_max;
   p.k_idx = (int32_t*)(ws + L.k_idx);
@@ -272,6 +274,7 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.k_cnt = (int32_t*)(ws + L.k_cnt);
   p.k_norm = (double*)(ws + L.k_norm);
   p.k_bad = (int32_t*)(ws + L.k_bad);
+  p.k_px = (double*)(ws + L.k_px);
 
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_HIP;

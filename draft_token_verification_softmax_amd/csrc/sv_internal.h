@@ -9,18 +9,19 @@ namespace sv {
 
 constexpr int kBlock = 256;            // threads per workgroup (4 wave64s)
 constexpr int kVec = 8;                // logits per group: 16 B of bf16, 32 B of fp32
-constexpr int kTopkCap = 4096;         // LDS candidate slots of the top-k tile kernel
+constexpr int kTopkCap = 2560;         // LDS candidate slots of the top-k tile kernel
 constexpr int kMergeCap = 4096;        // LDS slots when merging a row's top-k candidates
 constexpr int kWindowCap = 2048;       // LDS slots for the nucleus boundary window
 constexpr int kNucBins = 2048;         // histogram bins of the nucleus search
 constexpr int kResidSeg = kBlock * kVec;  // logits per workgroup in the residual kernels
+constexpr int kMaxTiles = 64;          // tiles per row (one wave combines a row's partials)
 
 // Per-tile partial result of the streaming pass.
 //   m    max raw logit of the tile (NaN ignored; -inf if none)
 //   amax lowest index holding m (INT32_MAX if none)
-//   s    STATS mode: sum over the tile of exp((l - m) / T), accumulated in
-//        float64 from float32 exponentials; other modes: a probe that is NaN
-//        iff the tile holds a non-finite value (NaN, +inf or -inf)
+//   s    NaN iff the tile holds a NaN or +inf (exact, every mode); otherwise
+//        STATS mode: float64 sum over the tile of exp((l - m) / T), other
+//        modes: 0
 struct TileStat {
   float m;
   int32_t amax;
@@ -41,6 +42,17 @@ struct RowNuc {
   uint64_t cut;
   int32_t ok;
   float M;      // max raw logit of the row
+};
+
+// State of one sequence handed from k_resid_s to k_resid_final: the
+// accepted count n (-1: outputs already written), status bits, and the
+// views of the rows the residual reads (target row n; draft row n if n < k).
+// Row views: nmc = -M * 64 log2e / T (M = row max), inv = 1 / normaliser,
+// cut = nucleus cut (0 = none).
+struct SeqState {
+  double nmc_p, inv_p, nmc_q, inv_q;
+  uint64_t cut_p, cut_q;
+  int32_t n, st;
 };
 
 enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3 };
@@ -81,9 +93,10 @@ struct Params {
   uint64_t* cand;    // [rows][S][cand_w] (top-k)
   int cand_w;        // candidate slots per tile (top_k rounded up)
   RowNuc* nuc;       // [rows] (top-p)
+  float* row_lx;     // [rows] logit of the drafted token a row's accept test reads
+                     // (written by the tile holding it; sampling modes)
   // sampling: state handed from k_resid_s to k_resid_final
-  int* seq_n;        // [B] accepted count n, or -1 if the sequence is already emitted
-  int* seq_st;       // [B] status bits found by the accept step
+  SeqState* seq;     // [B]
   double* spart;     // [B][S2] residual-mass partials
   int S2;            // residual segments per sequence (kResidSeg logits each)
   // top-k: each row's kept set, rank order
@@ -92,6 +105,7 @@ struct Params {
   int32_t* k_cnt;    // [rows] entries kept (after the nucleus, if any)
   double* k_norm;    // [rows] sum of k_e over the kept entries
   int32_t* k_bad;    // [rows] 1 if the row is invalid
+  double* k_px;      // [rows] p'(x_j) of the drafted token the row's accept test reads
 };
 
 // Launchers (sv_kernels.hip).  Each returns the hipError_t of its launches.

@@ -10,11 +10,18 @@
 //                     STATS64  max + float64 sum of exp((l - max) / T)
 //                                                         (plain and nucleus sampling)
 //                     TOPK     the tile's top_k           (top-k sampling)
+//                   Every tile also records, exactly, whether it holds a NaN
+//                   or +inf, so no row is ever scanned a second time for that.
 //   greedy / tree   k_greedy_final / k_tree_final: one workgroup per sequence
 //   top-k           k_topk_rows (merge per row) -> k_topk_final (per sequence)
 //   nucleus         k_topp_rows (exact cut per row) -> k_resid_s -> k_resid_final
 //   plain sampling  k_resid_s (accept step + residual mass per segment)
-//                   -> k_resid_final (draw per sequence)
+//                   -> k_resid_final (draw; one workgroup per segment)
+//
+// The finishing kernels are latency-bound: each one is written as a few
+// rounds of independent loads (tile partials are combined by lane segments of
+// one wave, all rows of a sequence at once) rather than chains of dependent
+// loads.
 //
 // Every reduction that feeds an output is a fixed-order butterfly / tree, so
 // repeated calls give bit-identical results.  Float64 carries every quantity
@@ -37,32 +44,68 @@ constexpr int kWaves = kBlock / 64;
 constexpr double kLog2e = 1.4426950408889634;
 constexpr int kStatusInternal = 0x100;   // a numeric search did not settle (never expected)
 constexpr int kTopkMax = 256;            // largest top_k
+constexpr int kUnroll = 4;               // groups of kVec logits each lane has in flight
+constexpr int kMaxTree = 1024;
+constexpr int kMaxRows = 2 * 64 + 1;
 
 // ------------------------------------------------------------------ loads
 
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Io;
 template <> struct Io<float> {
   static DEV float at(const float* p, long i) { return p[i]; }
-  static DEV void vec(const float* p, float v[kVec]) {
-    const vf4* q = reinterpret_cast<const vf4*>(p);
-    const vf4 a = __builtin_nontemporal_load(q);
-    const vf4 b = __builtin_nontemporal_load(q + 1);
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
-  }
 };
 template <> struct Io<uint16_t> {
   static DEV float at(const uint16_t* p, long i) { return __uint_as_float((uint32_t)p[i] << 16); }
-  static DEV void vec(const uint16_t* p, float v[kVec]) {
-    const vu4 q = __builtin_nontemporal_load(reinterpret_cast<const vu4*>(p));
-    v[0] = __uint_as_float(q.x << 16); v[1] = __uint_as_float(q.x & 0xffff0000u);
-    v[2] = __uint_as_float(q.y << 16); v[3] = __uint_as_float(q.y & 0xffff0000u);
-    v[4] = __uint_as_float(q.z << 16); v[5] = __uint_as_float(q.z & 0xffff0000u);
-    v[6] = __uint_as_float(q.w << 16); v[7] = __uint_as_float(q.w & 0xffff0000u);
+};
+
+// One aligned group of kVec logits as loaded (one or two 16-byte loads).
+// probe() keeps, in one register, enough to tell exactly whether any logit
+// seen was a NaN: the largest magnitude bit pattern (per 16-bit half for
+// bf16); a NaN is the only pattern above the one of infinity.
+template <typename T> struct Group;
+template <> struct Group<uint16_t> {
+  vu4 w;
+  DEV void load(const uint16_t* p) { w = __builtin_nontemporal_load(reinterpret_cast<const vu4*>(p)); }
+  DEV void values(float v[kVec]) const {
+    v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
+    v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
+    v[4] = __uint_as_float(w.z << 16); v[5] = __uint_as_float(w.z & 0xffff0000u);
+    v[6] = __uint_as_float(w.w << 16); v[7] = __uint_as_float(w.w & 0xffff0000u);
   }
+  DEV void probe(uint32_t& acc) const {
+    us2 a = __builtin_bit_cast(us2, acc);
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(us2, w.x & 0x7fff7fffu));
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(us2, w.y & 0x7fff7fffu));
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(us2, w.z & 0x7fff7fffu));
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(us2, w.w & 0x7fff7fffu));
+    acc = __builtin_bit_cast(uint32_t, a);
+  }
+  static DEV bool has_nan(uint32_t acc) { return (acc & 0xffffu) > 0x7f80u || (acc >> 16) > 0x7f80u; }
+};
+template <> struct Group<float> {
+  vf4 a, b;
+  DEV void load(const float* p) {
+    const vf4* q = reinterpret_cast<const vf4*>(p);
+    a = __builtin_nontemporal_load(q);
+    b = __builtin_nontemporal_load(q + 1);
+  }
+  DEV void values(float v[kVec]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+  DEV void probe(uint32_t& acc) const {
+    const uint32_t m = 0x7fffffffu;
+    const uint32_t x0 = max(__float_as_uint(a.x) & m, __float_as_uint(a.y) & m);
+    const uint32_t x1 = max(__float_as_uint(a.z) & m, __float_as_uint(a.w) & m);
+    const uint32_t x2 = max(__float_as_uint(b.x) & m, __float_as_uint(b.y) & m);
+    const uint32_t x3 = max(__float_as_uint(b.z) & m, __float_as_uint(b.w) & m);
+    acc = max(acc, max(max(x0, x1), max(x2, x3)));
+  }
+  static DEV bool has_nan(uint32_t acc) { return acc > 0x7f800000u; }
 };
 
 // Load the group of kVec logits starting at `pos` (< end).  Slots past `end`
@@ -71,13 +114,104 @@ template <typename T>
 DEV int load_group(const T* row, int pos, int end, int aligned, float v[kVec]) {
   int n = end - pos;
   if (n >= kVec && aligned) {
-    Io<T>::vec(row + pos, v);
+    Group<T> g;
+    g.load(row + pos);
+    g.values(v);
     return kVec;
   }
   n = n < kVec ? n : kVec;
 #pragma unroll
   for (int e = 0; e < kVec; ++e) v[e] = (e < n) ? Io<T>::at(row, (long)pos + e) : -INFINITY;
   return n;
+}
+
+// One iteration of a tile pass: the kUnroll groups g0, g0 + kBlock, ... of
+// the lane, all issued as plain vector loads with no per-group test.  A group
+// past the tile loads the tile's last full group instead (always in bounds)
+// and is then set to -inf with nv = 0.  Only a wave that holds the partial
+// last group of a row whose length is not a multiple of kVec (or a row that
+// is not 16-byte aligned) takes the element path.  NaN evidence goes to
+// `probe` (vector path) or `nanv` (element path).
+template <typename T>
+DEV void load_iter(const T* row, int start, int end, int ngroups, int nfull, int aligned, int g0,
+                   float v[kUnroll][kVec], int nv[kUnroll], uint32_t& probe, bool& nanv) {
+  const bool partial = nfull != ngroups;
+  if (aligned && nfull > 0 && __all(!partial || g0 + (kUnroll - 1) * kBlock < nfull)) {
+    Group<T> gr[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int g = g0 + u * kBlock;
+      gr[u].load(row + start + (g < nfull ? g : nfull - 1) * kVec);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      gr[u].values(v[u]);
+      gr[u].probe(probe);
+      nv[u] = kVec;
+      if (g0 + u * kBlock >= nfull) {
+        nv[u] = 0;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int g = g0 + u * kBlock;
+      if (g < ngroups) {
+        nv[u] = load_group<T>(row, start + g * kVec, end, aligned, v[u]);
+      } else {
+        nv[u] = 0;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
+      }
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) nanv |= (v[u][e] != v[u][e]);
+    }
+  }
+}
+
+// Max of three floats as one v_max3_f32.  fmaxf would first quieten each
+// operand (one more instruction per logit); NaN never needs to survive here
+// because every pass probes for it separately.
+DEV float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+DEV float max8(const float v[kVec]) {
+  return max3_raw(max3_raw(v[0], v[1], v[2]), max3_raw(v[3], v[4], v[5]), max3_raw(v[6], v[7], v[7]));
+}
+
+// ------------------------------------------------------------------ float64 exp2
+
+// 2^(y64 / 64) to a few ulp of float64, for the streaming sums.
+// y64 = 64 j + f with j = rint(y64), |f| <= 1/2:
+//   2^(y64/64) = 2^(j >> 6) * 2^((j & 63) / 64) * e^(f ln2 / 64);
+// the middle factor comes from a 64-entry table, the last from its Taylor
+// series to degree 5 (|f ln2 / 64| <= 0.0055, remainder below 4e-17).
+// Arguments below -70000 (results below 2^-1093, i.e. 0) and NaN give 0.
+constexpr double kE1 = 0.010830424696249145;     // (ln2/64)^i / i!
+constexpr double kE2 = 5.86490495505617e-05;
+constexpr double kE3 = 2.1173137155464776e-07;
+constexpr double kE4 = 5.732851688640402e-10;
+constexpr double kE5 = 1.2417843701716925e-12;
+
+DEV void exp2_table_init(double* tab) {
+  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 64.0));
+  __syncthreads();
+}
+DEV double exp2_64(double y64, const double* tab) {
+  y64 = fmax(y64, -70000.0);
+  const double j = rint(y64);
+  const double f = y64 - j;
+  double q = fma(f, kE5, kE4);
+  q = fma(q, f, kE3);
+  q = fma(q, f, kE2);
+  q = fma(q, f, kE1);
+  q = fma(q, f, 1.0);
+  const int ji = (int)j;
+  return ldexp(tab[ji & 63] * q, ji >> 6);
 }
 
 // ------------------------------------------------------------------ keys
@@ -151,6 +285,70 @@ DEV void block_argmax(float& m, int& i, float* redm, int* redi) {
   for (int q = 1; q < kWaves; ++q)
     if (redm[q] > m || (redm[q] == m && redi[q] < i)) { m = redm[q]; i = redi[q]; }
   __syncthreads();
+}
+
+// Block-wide integer reductions by shuffles (one LDS slot per wave); every
+// thread gets the result.  Many lanes updating one LDS word with atomics
+// serialise, so block-wide decisions go through these instead.
+template <typename I> DEV I wave_min_t(I v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) { const I u = __shfl_xor(v, o); v = u < v ? u : v; }
+  return v;
+}
+template <typename I> DEV I wave_max_t(I v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) { const I u = __shfl_xor(v, o); v = u > v ? u : v; }
+  return v;
+}
+DEV int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// (min a, max b) over the block in one pass
+template <typename I>
+DEV void block_minmax(I& a, I& b, I* red) {
+  a = wave_min_t(a);
+  b = wave_max_t(b);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) { red[w] = a; red[kWaves + w] = b; }
+  __syncthreads();
+  a = red[0]; b = red[kWaves];
+  for (int q = 1; q < kWaves; ++q) {
+    a = red[q] < a ? red[q] : a;
+    b = red[kWaves + q] > b ? red[kWaves + q] : b;
+  }
+  __syncthreads();
+}
+DEV int block_max_i(int v, int* red) {
+  int lo = INT_MAX;
+  block_minmax(lo, v, red);
+  return v;
+}
+DEV int block_sum_i(int v, int* red) {
+  v = wave_sum_i(v);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  v = (red[0] + red[1]) + (red[2] + red[3]);
+  __syncthreads();
+  return v;
+}
+// Wave-aggregated append: lanes with `take` get consecutive slots of a
+// shared counter with one LDS atomic per wave.  Call with every lane of the
+// wave that may append active.
+DEV int wave_append(bool take, int* counter) {
+  const unsigned long long m = __ballot(take);
+  if (m == 0ull) return -1;
+  const int lane = threadIdx.x & 63;
+  const int leader = __ffsll((unsigned long long)m) - 1;
+  int base = 0;
+  if (lane == leader) base = atomicAdd(counter, __popcll(m));
+  base = __shfl(base, leader);
+  const int below = __popcll(m & ((1ull << lane) - 1ull));
+  return take ? base + below : -1;
 }
 
 // Exclusive scan of one double per thread in thread order (fixed order).
@@ -227,96 +425,85 @@ DEV const T* row_ptr(const Params& p, int grow) {
   return grow < nt ? (const T*)p.target + (size_t)grow * p.V
                    : (const T*)p.draft + (size_t)(grow - nt) * p.V;
 }
-
-// Block-wide scan of a row for NaN or +inf (the exact test behind a probe).
-template <typename T>
-DEV bool row_has_nan_or_posinf(const T* row, int V) {
-  int bad = 0;
-  for (int i = threadIdx.x; i < V; i += kBlock) {
-    const float v = Io<T>::at(row, i);
-    bad |= (v != v) || (v == INFINITY);
-  }
-  return __syncthreads_or(bad) != 0;
-}
-
-// Combine the S tile partials of one row (one thread).
-struct RowStat {
-  float M;
-  int amax;
-  double Z;      // STATS mode: sum of exp((l - M) / T); NaN if a NaN was seen
-  bool probe;    // a tile saw a non-finite value (ARGMAX / TOPK modes)
-};
-DEV RowStat combine_tiles(const Params& p, int grow, bool stats) {
-  const TileStat* t = p.tiles + (size_t)grow * p.S;
-  RowStat r;
-  r.M = -INFINITY; r.amax = INT_MAX; r.Z = 0.0; r.probe = false;
-  for (int s = 0; s < p.S; ++s) {
-    const TileStat ts = t[s];
-    if (ts.m > r.M) { r.M = ts.m; r.amax = ts.amax; }
-    if (ts.s != ts.s) r.probe = true;
-  }
-  if (stats) {
-    const double cd = kLog2e / p.T;
-    double z = 0.0;
-    for (int s = 0; s < p.S; ++s) {
-      const TileStat ts = t[s];
-      if (ts.m == -INFINITY) { z += ts.s; continue; }
-      z += ts.s * exp2(((double)ts.m - (double)r.M) * cd);
-    }
-    r.Z = z;
-  }
-  return r;
-}
-
-// ================================================================== row / sequence indexing
-
-DEV int seq_of_row(const Params& p, int grow) {
-  const int nt = p.B * p.rows_t;
-  return grow < nt ? grow / p.rows_t : (grow - nt) / p.rows_d;
-}
 DEV int trow(const Params& p, int b, int j) { return b * p.rows_t + j; }
 DEV int drow(const Params& p, int b, int j) { return p.B * p.rows_t + b * p.rows_d + j; }
 
-constexpr int kUnroll = 4;     // groups of kVec logits each thread has in flight
-constexpr int kMaxTree = 1024;
-constexpr int kMaxRows = 2 * 64 + 1;
+// Combine the tile partials of rows 0..nrows-1 (global row ids row_of(r)).
+// A segment of W lanes (W = S rounded up to a power of two) takes one row,
+// lane s holding tile s; the butterflies over xor offsets < W give the same
+// result as one over the whole wave with idle lanes, so every kernel that
+// combines a row gets the same bits.  Each wave keeps kUnroll loads in
+// flight.  sink(r, M, amax, Z, bad) is called once per row:
+//   M     the row max; amax its lowest index (ARGMAX partials)
+//   Z     STATS: sum over tiles of s_t * 2^((m_t - M) log2e / T), else 0
+//   bad   the row holds NaN or +inf, or no finite value
+template <bool STATS, typename RowOf, typename Sink>
+DEV void combine_rows(const Params& p, int nrows, RowOf row_of, Sink sink) {
+  const int S = p.S;
+  int lw = 0;
+  while ((1 << lw) < S) ++lw;
+  const int W = 1 << lw;
+  const int R = 64 >> lw;                    // rows per wave per slot
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int seg = lane >> lw, s = lane & (W - 1);
+  const double cd = kLog2e / p.T;
+  for (int base = 0; base < nrows; base += kWaves * R * kUnroll) {
+    TileStat ts[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int r = base + (u * kWaves + wv) * R + seg;
+      if (r < nrows && s < S) {
+        ts[u] = p.tiles[(size_t)row_of(r) * S + s];
+      } else {
+        ts[u].m = -INFINITY; ts[u].amax = INT_MAX; ts[u].s = 0.0;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int r = base + (u * kWaves + wv) * R + seg;
+      float m = ts[u].m;
+      int ai = ts[u].amax;
+      int bad = ts[u].s != ts[u].s;
+      for (int o = W >> 1; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(m, o);
+        const int a2 = __shfl_xor(ai, o);
+        if (m2 > m || (m2 == m && a2 < ai)) { m = m2; ai = a2; }
+        bad |= __shfl_xor(bad, o);
+      }
+      double Z = 0.0;
+      if (STATS) {
+        double t = 0.0;
+        if (s < S) t = ts[u].m == -INFINITY ? ts[u].s : ts[u].s * exp2(((double)ts[u].m - (double)m) * cd);
+        for (int o = W >> 1; o > 0; o >>= 1) t += __shfl_xor(t, o);
+        Z = t;
+      }
+      bad |= (m == INFINITY) || (m == -INFINITY) || (Z != Z);
+      if (s == 0 && r < nrows) sink(r, m, ai, Z, bad);
+    }
+  }
+}
 
 // ================================================================== tile passes
 
+// Max and lowest index of the max of a tile.
 template <typename T>
 DEV void tile_argmax(const Params& p, const T* row, int start, int end, int ngroups, int tile) {
   __shared__ float redm[kWaves];
   __shared__ int redi[kWaves];
+  const int nfull = (end - start) / kVec;
   float m = -INFINITY;
   int mi = INT_MAX;
-  float probe = 0.f;
+  uint32_t probe = 0;
+  bool nanv = false;
   for (int g0 = threadIdx.x; g0 < ngroups; g0 += kUnroll * kBlock) {
     float v[kUnroll][kVec];
     int nv[kUnroll];
+    load_iter<T>(row, start, end, ngroups, nfull, p.aligned, g0, v, nv, probe, nanv);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int g = g0 + u * kBlock;
-      if (g < ngroups) {
-        nv[u] = load_group<T>(row, start + g * kVec, end, p.aligned, v[u]);
-      } else {
-        nv[u] = 0;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int pos = start + (g0 + u * kBlock) * kVec;
-      float gm = v[u][0];
-#pragma unroll
-      for (int e = 1; e < kVec; ++e) gm = fmaxf(gm, v[u][e]);
-      if (nv[u] == kVec) {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) probe = fmaf(v[u][e], 0.f, probe);
-      } else {
-        for (int e = 0; e < nv[u]; ++e) probe = fmaf(v[u][e], 0.f, probe);
-      }
+      const float gm = max8(v[u]);
       if (gm > m) {
+        const int pos = start + (g0 + u * kBlock) * kVec;
         int idx = pos;
 #pragma unroll
         for (int e = kVec - 1; e >= 0; --e) if (v[u][e] == gm) idx = pos + e;
@@ -325,11 +512,68 @@ DEV void tile_argmax(const Params& p, const T* row, int start, int end, int ngro
       }
     }
   }
-  const bool bad = __syncthreads_or(probe != probe);
+  const bool nan = __syncthreads_or(nanv || Group<T>::has_nan(probe));
   block_argmax(m, mi, redm, redi);
   if (threadIdx.x == 0) {
     TileStat ts;
-    ts.m = m; ts.amax = mi; ts.s = bad ? (double)NAN : 0.0;
+    ts.m = m; ts.amax = mi; ts.s = (nan || m == INFINITY) ? (double)NAN : 0.0;
+    p.tiles[tile] = ts;
+  }
+}
+
+// The logit of the drafted token an accept test reads from this row, if it
+// falls in the tile (one thread; rows without a drafted token are skipped).
+template <typename T>
+DEV void record_token_logit(const Params& p, const T* row, int grow, int start, int end) {
+  const int nt = p.B * p.rows_t;
+  int b, j;
+  if (grow < nt) { b = grow / p.rows_t; j = grow - b * p.rows_t; }
+  else { b = (grow - nt) / p.rows_d; j = (grow - nt) - b * p.rows_d; }
+  if (j >= p.k) return;
+  const int x = p.tokens[(size_t)b * p.k + j];
+  if (x >= start && x < end) p.row_lx[grow] = Io<T>::at(row, x);
+}
+
+// Max and float64 sum of exp((l - max) / T) of a tile.
+template <typename T>
+DEV void tile_stats64(const Params& p, const T* row, int start, int end, int ngroups, int tile) {
+  __shared__ float redm[kWaves];
+  __shared__ double redd[kWaves];
+  __shared__ double tab[64];
+  if (threadIdx.x == 0) record_token_logit<T>(p, row, tile / p.S, start, end);
+  exp2_table_init(tab);
+  const int nfull = (end - start) / kVec;
+  const double c64 = 64.0 * kLog2e / p.T;
+  float m = -INFINITY;
+  double nmc = 0.0;     // -m * c64
+  double s = 0.0;       // sum of 2^((l - m) c64 / 64)
+  uint32_t probe = 0;
+  bool nanv = false;
+  for (int g0 = threadIdx.x; g0 < ngroups; g0 += kUnroll * kBlock) {
+    float v[kUnroll][kVec];
+    int nv[kUnroll];
+    load_iter<T>(row, start, end, ngroups, nfull, p.aligned, g0, v, nv, probe, nanv);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float gm = max8(v[u]);
+      if (gm > m) {
+        if (m > -INFINITY) s *= exp2_64(((double)m - (double)gm) * c64, tab);
+        m = gm;
+        nmc = -(double)m * c64;
+      }
+      if (m > -INFINITY) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) s += exp2_64(fma((double)v[u][e], c64, nmc), tab);
+      }
+    }
+  }
+  const bool nan = __syncthreads_or(nanv || Group<T>::has_nan(probe));
+  const float M = block_max(m, redm);
+  const double term = m == -INFINITY ? 0.0 : s * exp2_64(((double)m - (double)M) * c64, tab);
+  const double tot = block_sum(term, redd);
+  if (threadIdx.x == 0) {
+    TileStat ts;
+    ts.m = M; ts.amax = INT_MAX; ts.s = (nan || M == INFINITY) ? (double)NAN : tot;
     p.tiles[tile] = ts;
   }
 }
@@ -339,15 +583,16 @@ DEV void tile_argmax(const Params& p, const T* row, int start, int end, int ngro
 // to the best top_k and the admission threshold raised.
 template <typename T>
 DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int ngroups, int tile,
-                   uint64_t* buf) {
+                          uint64_t* buf) {
   __shared__ int cnt;
   __shared__ float tau_f;
   __shared__ uint64_t tau_p;
+  __shared__ unsigned short rank[kTopkCap];
   const int K = p.top_k;
   const int tid = threadIdx.x;
   if (tid == 0) { cnt = 0; tau_f = -INFINITY; tau_p = 0ull; }
   __syncthreads();
-  float probe = 0.f;
+  bool badv = false;
   for (int g0 = 0; g0 < ngroups; g0 += kBlock) {
     const float tf = tau_f;
     const uint64_t tp = tau_p;
@@ -356,19 +601,13 @@ DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int
       const int pos = start + g * kVec;
       float v[kVec];
       const int n = load_group<T>(row, pos, end, p.aligned, v);
-      float gm = v[0];
-#pragma unroll
-      for (int e = 1; e < kVec; ++e) gm = fmaxf(gm, v[e]);
-      for (int e = 0; e < n; ++e) probe = fmaf(v[e], 0.f, probe);
-      if (gm >= tf) {
-        for (int e = 0; e < n; ++e) {
-          if (v[e] >= tf) {
-            const uint64_t pk = pack(v[e], pos + e);
-            if (pk > tp) {
-              const int slot = atomicAdd(&cnt, 1);
-              buf[slot] = pk;
-            }
-          }
+      const float gm = max8(v);
+      for (int e = 0; e < n; ++e) badv |= (v[e] != v[e]) || (v[e] == INFINITY);
+      if (__any(gm >= tf)) {
+        for (int e = 0; e < kVec; ++e) {
+          const uint64_t pk = pack(v[e], pos + e);
+          const int slot = wave_append(e < n && v[e] >= tf && pk > tp, &cnt);
+          if (slot >= 0) buf[slot] = pk;
         }
       }
     }
@@ -377,9 +616,20 @@ DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int
     const bool last = (g0 + kBlock >= ngroups);
     __syncthreads();   // every thread has read cnt before anyone appends again
     if (c > kTopkCap - kBlock * kVec || last) {
-      const int P = next_pow2(c);
-      for (int i = c + tid; i < P; i += kBlock) buf[i] = 0ull;
-      bitonic_desc(buf, P);
+      // keep the best K in rank order in buf[0, K): rank = entries above.
+      // Writes only reach slots < K <= kBlock, whose entries each owner
+      // thread holds in a register; every other entry is read in place.
+      const uint64_t key0 = tid < c ? buf[tid] : 0ull;
+      for (int i = tid; i < c; i += kBlock) {
+        const uint64_t key = buf[i];
+        int r = 0;
+        for (int j = 0; j < c; ++j) r += buf[j] > key;
+        rank[i] = (unsigned short)(r < K ? r : K);
+      }
+      __syncthreads();
+      for (int i = tid; i < c; i += kBlock)
+        if (rank[i] < K) buf[rank[i]] = i == tid ? key0 : buf[i];
+      __syncthreads();
       if (tid == 0) {
         cnt = c < K ? c : K;
         if (c >= K) { tau_p = buf[K - 1]; tau_f = packed_val(buf[K - 1]); }
@@ -387,7 +637,7 @@ DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int
       __syncthreads();
     }
   }
-  const bool bad = __syncthreads_or(probe != probe);
+  const bool bad = __syncthreads_or(badv);
   const int c = cnt;
   uint64_t* out = p.cand + (size_t)tile * p.cand_w;
   for (int i = tid; i < p.cand_w; i += kBlock) out[i] = (i < c) ? buf[i] : 0ull;
@@ -401,136 +651,88 @@ DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int
   __syncthreads();
 }
 
-// Descending bitonic sort of kBlock floats in LDS.
-DEV void bitonic_desc_block_f(float* a) {
-  for (int size = 2; size <= kBlock; size <<= 1) {
+// Descending sort of one float per lane across a wave (bitonic network on
+// shuffles, no LDS or barriers); lane i gets the i-th largest.
+DEV float wave_sort_desc(float x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int size = 2; size <= 64; size <<= 1) {
+#pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      __syncthreads();
-      const int t = threadIdx.x;
-      if (t < kBlock / 2) {
-        const int lo = 2 * t - (t & (stride - 1));
-        const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
-        const float x = a[lo], y = a[hi];
-        if ((x < y) == desc) { a[lo] = y; a[hi] = x; }
-      }
+      const float y = __shfl_xor(x, stride);
+      const bool lower = (lane & stride) == 0;        // this lane holds the lower index of the pair
+      const bool desc = (lane & size) == 0 || size == 64;
+      // keep the larger value at the lower index of a descending run
+      const bool keep_max = lower == desc;
+      x = keep_max ? fmaxf(x, y) : fminf(x, y);
     }
   }
-  __syncthreads();
+  return x;
 }
 
-// Max and float64 sum of exp((l - max) / T) of a tile, for nucleus rows
-// (whose cut needs the row sum to float64 accuracy).
-template <typename T>
-DEV void tile_stats64(const Params& p, const T* row, int start, int end, int ngroups, int tile) {
-  __shared__ float redm[kWaves];
-  __shared__ double redd[kWaves];
-  const double invT = 1.0 / p.T;
-  float m = -INFINITY;
-  double s = 0.0;
-  for (int g0 = threadIdx.x; g0 < ngroups; g0 += kUnroll * kBlock) {
-    float v[kUnroll][kVec];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int g = g0 + u * kBlock;
-      if (g < ngroups) {
-        load_group<T>(row, start + g * kVec, end, p.aligned, v[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      float gm = v[u][0];
-#pragma unroll
-      for (int e = 1; e < kVec; ++e) gm = fmaxf(gm, v[u][e]);
-      if (gm > m) {
-        if (m > -INFINITY) s *= exp(((double)m - (double)gm) * invT);
-        m = gm;
-      }
-      if (m > -INFINITY) {
-        const double zm = (double)m * invT;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) s += exp((double)v[u][e] * invT - zm);
-      } else {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) if (v[u][e] != v[u][e]) s = (double)NAN;
-      }
-    }
-  }
-  const float M = block_max(m, redm);
-  double term;
-  if (m == -INFINITY) term = s;
-  else term = s * exp(((double)m - (double)M) * invT);
-  const double tot = block_sum(term, redd);
-  if (threadIdx.x == 0) {
-    TileStat ts;
-    ts.m = M; ts.amax = INT_MAX; ts.s = tot;
-    p.tiles[tile] = ts;
-  }
-}
-
-// The tile's top_k under (value desc, index asc), written to p.cand.
-//  1. Every lane loads its first kUnroll groups; the top_k-th largest of the
-//     kBlock lane maxima is the admission threshold tau.  top_k distinct
-//     logits reach it, so it is a lower bound of the tile's top_k-th value.
-//  2. The tile streams like the other modes (kUnroll groups in flight per
-//     lane, no barriers); logits >= tau go to an LDS list.
-//  3. One sort of the list; its first top_k entries are the answer.
+// The tile's top_k under (value desc, index asc), written to p.cand in
+// rank order (zero-padded to cand_w).
+//  1. Admission threshold tau from the first kUnroll groups of every lane:
+//     each wave sorts its 64 lane maxima in registers and takes the
+//     ceil(top_k / 4)-th largest; tau is the smallest of the four.  Every
+//     wave then holds at least ceil(top_k / 4) logits >= tau, so the tile
+//     holds at least top_k of them and tau is a lower bound of its top_k-th.
+//  2. The tile streams; logits >= tau go to an LDS list (one atomic per wave).
+//  3. Each listed entry's rank is the number of entries above it; the first
+//     top_k ranks are written out.  No sort, no barrier beyond one.
 // If the list would overflow, the tile is redone by tile_topk_rounds.
 template <typename T>
 DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroups, int tile,
                    uint64_t* buf) {
   __shared__ int cnt, overflow;
-  __shared__ float lmax[kBlock];
+  __shared__ float wtau[kWaves];
+  __shared__ int redi[2 * kWaves];
   const int K = p.top_k;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nfull = (end - start) / kVec;
   if (tid == 0) { cnt = 0; overflow = 0; }
-  float probe = 0.f;
+  uint32_t probe = 0;
+  bool nanv = false;
   float tau = -INFINITY;
   for (int base = 0; base < ngroups; base += kUnroll * kBlock) {
     float v[kUnroll][kVec];
     int nv[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int g = base + tid + u * kBlock;
-      if (g < ngroups) {
-        nv[u] = load_group<T>(row, start + g * kVec, end, p.aligned, v[u]);
-      } else {
-        nv[u] = 0;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
-      }
-    }
+    load_iter<T>(row, start, end, ngroups, nfull, p.aligned, base + tid, v, nv, probe, nanv);
     if (base == 0) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u)
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) mx = fmaxf(mx, v[u][e]);
-      lmax[tid] = mx;
-      bitonic_desc_block_f(lmax);
-      tau = K <= kBlock ? lmax[K - 1] : -INFINITY;
+      for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, max8(v[u]));
+      const float srt = wave_sort_desc(mx);
+      const float tw = __shfl(srt, (K + kWaves - 1) / kWaves - 1);
+      if (lane == 0) wtau[tid >> 6] = tw;
+      __syncthreads();
+      tau = fminf(fminf(wtau[0], wtau[1]), fminf(wtau[2], wtau[3]));
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int pos = start + (base + tid + u * kBlock) * kVec;
-      float gm = v[u][0];
+      const float gm = max8(v[u]);
+      if (__any(gm >= tau)) {
+        unsigned msk = 0u;
 #pragma unroll
-      for (int e = 1; e < kVec; ++e) gm = fmaxf(gm, v[u][e]);
-      if (nv[u] == kVec) {
+        for (int e = 0; e < kVec; ++e) msk |= (e < nv[u] && v[u][e] >= tau) ? (1u << e) : 0u;
+        // wave-exclusive prefix of the per-lane counts, one atomic per wave
+        const int c = __popc(msk);
+        int incl = c;
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) probe = fmaf(v[u][e], 0.f, probe);
-      } else {
-        for (int e = 0; e < nv[u]; ++e) probe = fmaf(v[u][e], 0.f, probe);
-      }
-      if (gm >= tau) {
-        for (int e = 0; e < nv[u]; ++e) {
-          if (v[u][e] >= tau) {
-            const int slot = atomicAdd(&cnt, 1);
+        for (int o = 1; o < 64; o <<= 1) {
+          const int t = __shfl_up(incl, o);
+          if (lane >= o) incl += t;
+        }
+        int slot = 0;
+        if (lane == 63) slot = atomicAdd(&cnt, incl);
+        slot = __shfl(slot, 63) + incl - c;
+        const int pos = start + (base + tid + u * kBlock) * kVec;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          if ((msk >> e) & 1u) {
             if (slot < kTopkCap) buf[slot] = pack(v[u][e], pos + e);
             else overflow = 1;
+            ++slot;
           }
         }
       }
@@ -543,22 +745,31 @@ DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroup
     tile_topk_rounds<T>(p, row, start, end, ngroups, tile, buf);
     return;
   }
-  const bool bad = __syncthreads_or(probe != probe);
+  const bool nan = __syncthreads_or(nanv || Group<T>::has_nan(probe));
   const int c = cnt;
-  const int P = next_pow2(c);
-  for (int i = c + tid; i < P; i += kBlock) buf[i] = 0ull;
-  bitonic_desc(buf, P);
-  const int keep = c < K ? c : K;
   uint64_t* out = p.cand + (size_t)tile * p.cand_w;
-  for (int i = tid; i < p.cand_w; i += kBlock) out[i] = (i < keep) ? buf[i] : 0ull;
-  if (tid == 0) {
+  float top = -INFINITY;
+  int topi = INT_MAX;
+  for (int i = tid; i < c; i += kBlock) {
+    const uint64_t key = buf[i];
+    int r = 0;
+    for (int j = 0; j < c; ++j) r += buf[j] > key;
+    if (r < K) out[r] = key;
+    if (r == 0) { top = packed_val(key); topi = packed_idx(key); }
+  }
+  const int keep = c < K ? c : K;
+  for (int i = keep + tid; i < p.cand_w; i += kBlock) out[i] = 0ull;
+  // the entry of rank 0 is the tile max; its lane publishes it
+  int who = top > -INFINITY || topi != INT_MAX ? tid : INT_MAX;
+  int none = -1;
+  block_minmax(who, none, redi);
+  if (tid == (who == INT_MAX ? 0 : who)) {
     TileStat ts;
-    ts.m = keep > 0 ? packed_val(buf[0]) : -INFINITY;
-    ts.amax = keep > 0 ? packed_idx(buf[0]) : INT_MAX;
-    ts.s = bad ? (double)NAN : 0.0;
+    ts.m = top;
+    ts.amax = topi;
+    ts.s = (nan || top == INFINITY) ? (double)NAN : 0.0;
     p.tiles[tile] = ts;
   }
-  __syncthreads();
 }
 
 // ================================================================== outputs
@@ -579,6 +790,7 @@ DEV void emit_invalid(const Params& p, int b, int status) {
   }
 }
 
+// x: the sequence's drafted tokens (global or LDS)
 DEV void emit_tokens(const Params& p, int b, const int32_t* x, int n, int y, int status) {
   int32_t* ot = p.out_tokens + (size_t)b * p.out_w;
   for (int i = threadIdx.x; i < p.out_w; i += kBlock) ot[i] = i < n ? x[i] : (i == n ? y : -1);
@@ -588,60 +800,73 @@ DEV void emit_tokens(const Params& p, int b, const int32_t* x, int n, int y, int
   }
 }
 
-// Adjusted probability of one entry of a row (plain softmax or nucleus).
+// First rejected position of a chain from the per-position outcomes of wave
+// 0's lanes (lane j < k: j-th drafted token; call from all 64 lanes of wave
+// 0).  Returns n; *st gets 1 if the first failure is an invalid token.
+DEV int first_failure(bool fail, bool invalid, int k, int* st) {
+  const unsigned long long fm = __ballot(fail);
+  const unsigned long long im = __ballot(invalid);
+  const int n = fm ? (__ffsll((unsigned long long)fm) - 1) : k;
+  *st = (fm && ((im >> n) & 1ull)) ? 1 : 0;
+  return n;
+}
+
+// Adjusted probability of one entry of a row (plain softmax or nucleus):
+// p'(v) = 2^((l_v - M) c64 / 64) / norm on the kept set, c64 = 64 log2e / T.
 struct RowView {
   const void* row;
-  double zm;      // max z of the row (z = l / T)
-  double norm;    // normaliser (Z, or nucleus mass)
+  double nmc;     // -M * c64 (M = max logit of the row)
+  double inv;     // 1 / norm (Z, or nucleus mass)
   uint64_t cut;   // nucleus: v is kept iff pack(l_v, v) >= cut; 0 = no nucleus
 };
 
-DEV double prob_from(const RowView& r, double invT, float l, int v) {
+DEV double prob_from(const RowView& r, double c64, const double* tab, float l, int v) {
   if (r.cut && pack(l, v) < r.cut) return 0.0;
-  return exp((double)l * invT - r.zm) / r.norm;
+  return exp2_64(fma((double)l, c64, r.nmc), tab) * r.inv;
 }
 
+// Residual weights of the kVec entries [pos, pos + kVec) of one chunk:
+// w = max(0, p'(v) - q'(v)), or p'(v) without q.  Returns their sum.
 template <typename T>
-DEV double prob_of(const RowView& r, double invT, int v) {
-  return prob_from(r, invT, Io<T>::at((const T*)r.row, v), v);
-}
-
-// One chunk of kResidSeg entries of the residual draw: thread t owns
-// [c0 + 8t, c0 + 8t + 8), loaded as one group.  w = max(0, p'(v) - q'(v)),
-// or p'(v) without q.  Returns the thread's exclusive prefix within the chunk
-// (fixed order); *tot = chunk total.
-template <typename T>
-DEV double resid_chunk(const RowView& pr, const RowView* qr, double invT, int V, int aligned,
-                       int c0, double w[kVec], double* red, double* tot) {
-  const int pos = c0 + threadIdx.x * kVec;
+DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double c64,
+                         const double* tab, int V, int aligned, int pos, double w[kVec]) {
   float lp[kVec], lq[kVec];
   int n = 0;
   if (pos < V) {
     n = load_group<T>((const T*)pr.row, pos, V, aligned, lp);
-    if (qr) load_group<T>((const T*)qr->row, pos, V, aligned, lq);
+    if (hasq) load_group<T>((const T*)qr.row, pos, V, aligned, lq);
   }
   double t = 0.0;
 #pragma unroll
   for (int q = 0; q < kVec; ++q) {
     double wq = 0.0;
     if (q < n) {
-      wq = prob_from(pr, invT, lp[q], pos + q);
-      if (qr) {
-        wq -= prob_from(*qr, invT, lq[q], pos + q);
+      wq = prob_from(pr, c64, tab, lp[q], pos + q);
+      if (hasq) {
+        wq -= prob_from(qr, c64, tab, lq[q], pos + q);
         wq = wq > 0.0 ? wq : 0.0;
       }
     }
     w[q] = wq;
     t += wq;
   }
+  return t;
+}
+
+// One chunk of kResidSeg entries of the residual draw: thread t owns
+// [c0 + 8t, c0 + 8t + 8).  Returns the thread's exclusive prefix within the
+// chunk (fixed order); *tot = chunk total.
+template <typename T>
+DEV double resid_chunk(const RowView& pr, const RowView& qr, bool hasq, double c64,
+                       const double* tab, int V, int aligned, int c0, double w[kVec], double* red,
+                       double* tot) {
+  const double t = resid_weights<T>(pr, qr, hasq, c64, tab, V, aligned, c0 + threadIdx.x * kVec, w);
   return block_exscan(t, red, tot);
 }
 
 // Within one chunk whose total crosses t (base = mass before the chunk):
 // first v with C_v > t; if rounding leaves none, the chunk's last positive entry.
-DEV int pick_in_chunk(double base, double ex, const double w[kVec], int c0, double t, int* sh_int) {
-  if (threadIdx.x == 0) *sh_int = INT_MAX;
-  __syncthreads();
+DEV int pick_in_chunk(double base, double ex, const double w[kVec], int c0, double t, int* redi) {
   double c = base + ex;
   int mine = INT_MAX, last_pos = -1;
 #pragma unroll
@@ -651,31 +876,21 @@ DEV int pick_in_chunk(double base, double ex, const double w[kVec], int c0, doub
     if (w[q] > 0.0) last_pos = v;
     if (mine == INT_MAX && w[q] > 0.0 && c > t) mine = v;
   }
-  atomicMin(sh_int, mine);
-  __syncthreads();
-  int y = *sh_int;
-  __syncthreads();
-  if (y == INT_MAX) {
-    if (threadIdx.x == 0) *sh_int = -1;
-    __syncthreads();
-    atomicMax(sh_int, last_pos);
-    __syncthreads();
-    y = *sh_int;
-    __syncthreads();
-  }
-  return y;
+  block_minmax(mine, last_pos, redi);
+  return mine != INT_MAX ? mine : last_pos;
 }
 
 // Inverse CDF over a whole row inside one workgroup (the empty-residual
-// fallback): y = min{v : C_v > ur * S'}.
+// fallback, over p' alone): y = min{v : C_v > ur * S'}.
 template <typename T>
-DEV int resid_draw(const RowView& pr, const RowView* qr, double invT, int V, int aligned, double ur,
-                   double* red, int* sh_int, double* S_out) {
+DEV int resid_draw(const RowView& pr, double c64, const double* tab, int V, int aligned, double ur,
+                   double* red, int* redi, double* S_out) {
+  const RowView none{nullptr, 0.0, 1.0, 0ull};
   double w[kVec];
   double S = 0.0;
   for (int c0 = 0; c0 < V; c0 += kResidSeg) {
     double tot;
-    resid_chunk<T>(pr, qr, invT, V, aligned, c0, w, red, &tot);
+    resid_chunk<T>(pr, none, false, c64, tab, V, aligned, c0, w, red, &tot);
     S += tot;
   }
   *S_out = S;
@@ -685,29 +900,14 @@ DEV int resid_draw(const RowView& pr, const RowView* qr, double invT, int V, int
   int lastc = 0;
   for (int c0 = 0; c0 < V; c0 += kResidSeg) {
     double tot;
-    const double ex = resid_chunk<T>(pr, qr, invT, V, aligned, c0, w, red, &tot);
+    const double ex = resid_chunk<T>(pr, none, false, c64, tab, V, aligned, c0, w, red, &tot);
     if (tot > 0.0) lastc = c0;
-    if (base + tot > t) return pick_in_chunk(base, ex, w, c0, t, sh_int);
+    if (base + tot > t) return pick_in_chunk(base, ex, w, c0, t, redi);
     base += tot;
   }
   double tot;
-  const double ex = resid_chunk<T>(pr, qr, invT, V, aligned, lastc, w, red, &tot);
-  return pick_in_chunk(-INFINITY, ex, w, lastc, INFINITY, sh_int);
-}
-
-// Block-wide check of the rows of a sequence whose probes saw a non-finite
-// value; returns true if one of them holds NaN or +inf.  `flag[r]`: 1 bad,
-// 2 needs the exact scan.
-template <typename T>
-DEV bool rows_bad(const Params& p, int b, const int* flag, int nrows) {
-  for (int r = 0; r < nrows; ++r) {
-    if (flag[r] == 1) return true;
-    if (flag[r] == 2) {
-      const int grow = r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t);
-      if (row_has_nan_or_posinf<T>(row_ptr<T>(p, grow), p.V)) return true;
-    }
-  }
-  return false;
+  const double ex = resid_chunk<T>(pr, none, false, c64, tab, V, aligned, lastc, w, red, &tot);
+  return pick_in_chunk(-INFINITY, ex, w, lastc, INFINITY, redi);
 }
 
 // ================================================================== greedy chain
@@ -717,31 +917,28 @@ __global__ __launch_bounds__(kBlock) void k_greedy_final(Params p) {
   __shared__ int rA[kMaxRows];
   __shared__ int rBad[kMaxRows];
   __shared__ int sx[64];
-  __shared__ int sh_n, sh_st;
+  __shared__ int sh_n, sh_st, sh_bad;
   const int b = blockIdx.x;
-  const int k = p.k, V = p.V;
-  const int32_t* x = p.tokens + (size_t)b * k;
-  for (int j = threadIdx.x; j <= k; j += kBlock) {
-    const RowStat rs = combine_tiles(p, trow(p, b, j), false);
-    rA[j] = rs.amax;
-    int bad = (rs.M == INFINITY) || (rs.M == -INFINITY) || (rs.M != rs.M) || (rs.amax == INT_MAX);
-    if (!bad && rs.probe) bad = 2;
-    rBad[j] = bad;
-    if (j < k) sx[j] = x[j];
+  const int k = p.k, V = p.V, tid = threadIdx.x;
+  int xj = 0;
+  if (tid < k) xj = p.tokens[(size_t)b * k + tid];
+  combine_rows<false>(p, k + 1, [&](int r) { return trow(p, b, r); },
+                      [&](int r, float, int a, double, int bad) { rA[r] = a; rBad[r] = bad; });
+  if (tid < k) sx[tid] = xj;
+  __syncthreads();
+  if (tid < 64) {
+    int bad = 0;
+    for (int r = tid; r <= k; r += 64) bad |= rBad[r];
+    const bool inv = tid < k && (xj < 0 || xj >= V);
+    const bool fail = tid < k && (inv || xj != rA[tid]);
+    int st;
+    const int n = first_failure(fail, inv, k, &st);
+    const unsigned long long bm = __ballot(bad);
+    if (tid == 0) { sh_n = n; sh_st = st; sh_bad = bm != 0ull; }
   }
   __syncthreads();
-  if (rows_bad<T>(p, b, rBad, k + 1)) { emit_invalid(p, b, 4); return; }
-  if (threadIdx.x == 0) {
-    int n = k, st = 0;
-    for (int j = 0; j < k; ++j) {
-      const int xj = sx[j];
-      if (xj < 0 || xj >= V) { st |= 1; n = j; break; }
-      if (xj != rA[j]) { n = j; break; }
-    }
-    sh_n = n; sh_st = st;
-  }
-  __syncthreads();
-  emit_tokens(p, b, x, sh_n, rA[sh_n], sh_st);
+  if (sh_bad) { emit_invalid(p, b, 4); return; }
+  emit_tokens(p, b, sx, sh_n, rA[sh_n], sh_st);
 }
 
 // ================================================================== token tree
@@ -754,24 +951,31 @@ __global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
   __shared__ short jmp[2][kMaxTree];
   __shared__ short dep[2][kMaxTree];
   __shared__ unsigned char val[2][kMaxTree];
-  __shared__ int rBad[kMaxTree];
-  __shared__ int sh_st, sh_best;
+  __shared__ unsigned char rbad[kMaxTree];
+  __shared__ int redi[2 * kWaves];
   const int b = blockIdx.x;
   const int N = p.k, V = p.V, tid = threadIdx.x;
   const int32_t* par = p.parents + (size_t)b * N;
   const int32_t* tok = p.tokens + (size_t)b * N;
-  if (tid == 0) { sh_st = 0; sh_best = 0; }
-  for (int i = tid; i < N; i += kBlock) {
-    const RowStat rs = combine_tiles(p, trow(p, b, i), false);
-    g[i] = rs.amax;
-    int bad = (rs.M == INFINITY) || (rs.M == -INFINITY) || (rs.M != rs.M) || (rs.amax == INT_MAX);
-    if (!bad && rs.probe) bad = 2;
-    rBad[i] = bad;
-    spar[i] = par[i];
-    stok[i] = tok[i];
+  constexpr int kPer = kMaxTree / kBlock;
+  int rp[kPer], rt[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = tid + q * kBlock;
+    rp[q] = i < N ? par[i] : 0;
+    rt[q] = i < N ? tok[i] : 0;
+  }
+  combine_rows<false>(p, N, [&](int r) { return trow(p, b, r); },
+                      [&](int r, float, int a, double, int bad) { g[r] = a; rbad[r] = (unsigned char)bad; });
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = tid + q * kBlock;
+    if (i < N) { spar[i] = rp[q]; stok[i] = rt[q]; }
   }
   __syncthreads();
-  if (rows_bad<T>(p, b, rBad, N)) { emit_invalid(p, b, 4); return; }
+  int anybad = 0;
+  for (int i = tid; i < N; i += kBlock) anybad |= rbad[i];
+  if (__syncthreads_or(anybad)) { emit_invalid(p, b, 4); return; }
   int st = 0;
   for (int i = tid; i < N; i += kBlock) {
     const int pi = spar[i];
@@ -789,8 +993,7 @@ __global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
     }
     val[0][i] = (unsigned char)ok; jmp[0][i] = (short)j; dep[0][i] = (short)d;
   }
-  if (st) atomicOr(&sh_st, st);
-  __syncthreads();
+  const int sh_st = (__syncthreads_or(st & 1) ? 1 : 0) | (__syncthreads_or(st & 2) ? 2 : 0);
   // pointer jumping: val = AND of the edge tests up to the root, dep = depth
   int cur = 0;
   for (int span = 1; span < N; span <<= 1) {
@@ -812,11 +1015,9 @@ __global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
   int bestkey = -1;
   for (int i = tid; i < N; i += kBlock)
     if (val[cur][i]) bestkey = max(bestkey, ((int)dep[cur][i] << 11) | (2047 - i));
-  atomicMax(&sh_best, bestkey);
-  __syncthreads();
+  const int sh_best = block_max_i(bestkey, redi);
   const int best = 2047 - (sh_best & 2047);
   const int n = sh_best >> 11;
-  // the path root..best, written from LDS by the lanes of one wave
   if (tid == 0) {
     int32_t* ot = p.out_tokens + (size_t)b * p.out_w;
     int32_t* on = p.out_nodes ? p.out_nodes + (size_t)b * p.out_w : nullptr;
@@ -837,177 +1038,202 @@ __global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
 
 // ================================================================== top-k
 
-// Merge the S tile lists of one row and publish its kept set.
+// Merge the S tile lists of one row (each sorted, zero-padded) and publish
+// its kept set in rank order, its normaliser, and -- for the rows an accept
+// test reads -- p'(x) of the drafted token.  The merge ranks every listed
+// entry by binary searches in the other lists (no sort, one barrier).
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
-  __shared__ uint64_t buf[kTopkCap];
+  __shared__ uint64_t buf[kMergeCap];
+  __shared__ uint64_t top[kTopkMax];
   __shared__ double red[kWaves];
-  __shared__ int sh_n, sh_kept, sh_probe;
-  __shared__ double sh_mass;
+  __shared__ int redi[2 * kWaves];
+  __shared__ double sh_mass, sh_px;
   const int grow = blockIdx.x;
   const int tid = threadIdx.x;
-  const int K = p.top_k;
-  const int total = p.S * p.cand_w;             // <= kTopkCap (host-checked)
-  const uint64_t* src = p.cand + (size_t)grow * p.S * p.cand_w;
-  const int P = next_pow2(total);
-  for (int i = tid; i < P; i += kBlock) buf[i] = i < total ? src[i] : 0ull;
-  if (tid == 0) {
-    int pr = 0;
-    for (int s = 0; s < p.S; ++s) { const double ps = p.tiles[(size_t)grow * p.S + s].s; pr |= (ps != ps); }
-    sh_probe = pr;
+  const int K = p.top_k, S = p.S, cw = p.cand_w;
+  const int total = S * cw;                     // <= kMergeCap (host-checked)
+  const uint64_t* src = p.cand + (size_t)grow * total;
+  // drafted token read by this row's accept test, if any
+  const int nt = p.B * p.rows_t;
+  int j = -1, b = 0;
+  if (grow < nt) { b = grow / p.rows_t; j = grow - b * p.rows_t; if (j >= p.k) j = -1; }
+  else { b = (grow - nt) / p.rows_d; j = (grow - nt) - b * p.rows_d; }
+  const int x = (j >= 0) ? p.tokens[(size_t)b * p.k + j] : -1;
+  int pr = 0;
+  for (int s = tid; s < S; s += kBlock) { const double ps = p.tiles[(size_t)grow * S + s].s; pr |= (ps != ps); }
+  for (int i0 = 0; i0 < total; i0 += kUnroll * kBlock) {
+    uint64_t r[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) { const int i = i0 + u * kBlock + tid; r[u] = i < total ? src[i] : 0ull; }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) { const int i = i0 + u * kBlock + tid; if (i < total) buf[i] = r[u]; }
   }
-  bitonic_desc(buf, P);
-  if (tid == 0) {
-    int n = 0;
-    while (n < K && buf[n] != 0ull) ++n;
-    sh_n = n;
+  if (tid < kTopkMax) top[tid] = 0ull;
+  if (tid == 0) sh_px = 0.0;
+  const int probe = __syncthreads_or(pr);
+  int cnt = 0;
+  for (int i = tid; i < total; i += kBlock) {
+    const uint64_t key = buf[i];
+    if (key == 0ull) continue;
+    ++cnt;
+    const int a = i / cw, pos = i - a * cw;
+    if (pos >= K) continue;
+    int rank = pos;
+    for (int l = 0; l < S && rank < K; ++l) {
+      if (l == a) continue;
+      const uint64_t* lst = buf + l * cw;
+      int lo = 0, hi = cw;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (lst[mid] > key) lo = mid + 1; else hi = mid;
+      }
+      rank += lo;
+    }
+    if (rank < K) top[rank] = key;
   }
-  __syncthreads();
-  const int n = sh_n;
-  const float v0 = n > 0 ? packed_val(buf[0]) : -INFINITY;
-  bool bad = (v0 != v0) || (v0 == INFINITY) || (v0 == -INFINITY);
-  if (!bad && sh_probe) bad = row_has_nan_or_posinf<T>(row_ptr<T>(p, grow), p.V);
+  const int tot = block_sum_i(cnt, redi);
+  const int n = tot < K ? tot : K;
+  const float v0 = n > 0 ? packed_val(top[0]) : -INFINITY;
+  const bool bad = probe || (v0 != v0) || (v0 == INFINITY) || (v0 == -INFINITY);
   const double invT = 1.0 / p.T;
   const double zm = (double)v0 * invT;
   int32_t* kidx = p.k_idx + (size_t)grow * K;
   double* ke = p.k_e + (size_t)grow * K;
-  double s = 0.0;
-  for (int i = tid; i < n; i += kBlock) {
-    const double e = bad ? 0.0 : exp((double)packed_val(buf[i]) * invT - zm);
-    kidx[i] = packed_idx(buf[i]);
-    ke[i] = e;
-    s += e;
+  double e = 0.0;
+  int idx = -1;
+  if (tid < n) {
+    idx = packed_idx(top[tid]);
+    e = bad ? 0.0 : exp((double)packed_val(top[tid]) * invT - zm);
+    kidx[tid] = idx;
+    ke[tid] = e;
   }
-  const double Z = block_sum(s, red);
+  double Z;
+  const double ex = block_exscan(e, red, &Z);   // rank-order prefix of the kept set
   int kept = n;
   double norm = Z;
   if (p.top_p < 1.0 && n > 0 && !bad) {
-    // nucleus on the kept set: rank order is already probability order
+    // nucleus on the kept set: rank order is already probability order;
+    // entry i stays iff the mass ranked before it is below top_p
+    kept = block_max_i((tid < n && ex < p.top_p * Z) ? tid + 1 : 1, redi);
+    if (tid == kept - 1) sh_mass = ex + e;
     __syncthreads();
-    if (tid == 0) {
-      double before = 0.0, mass = 0.0;
-      int kk = 0;
-      for (int i = 0; i < n; ++i) {
-        if (!(before < p.top_p)) break;
-        const double e = ke[i];
-        kk = i + 1;
-        mass += e;
-        before += e / Z;
-      }
-      sh_kept = kk;
-      sh_mass = mass;
-    }
-    __syncthreads();
-    kept = sh_kept;
     norm = sh_mass;
   }
+  if (idx >= 0 && idx == x && tid < kept) sh_px = e / norm;
+  __syncthreads();
   if (tid == 0) {
     p.k_cnt[grow] = kept;
     p.k_norm[grow] = norm;
     p.k_bad[grow] = bad ? 1 : 0;
+    p.k_px[grow] = sh_px;
   }
 }
 
-// p'(x) of a published kept set (0 if x is not a member); one thread.
-DEV double kept_prob_1(const Params& p, int grow, int x) {
-  const int K = p.top_k;
-  const int n = p.k_cnt[grow];
-  const int32_t* kidx = p.k_idx + (size_t)grow * K;
-  for (int i = 0; i < n; ++i)
-    if (kidx[i] == x) return p.k_e[(size_t)grow * K + i] / p.k_norm[grow];
-  return 0.0;
-}
-
+// Accept step and residual draw of one sequence from the published kept sets.
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topk_final(Params p) {
-  __shared__ uint64_t buf[kTopkMax];
-  __shared__ double rw[kTopkMax];
+  __shared__ int qidx[kTopkMax];
+  __shared__ double qe[kTopkMax];
   __shared__ int sidx[kTopkMax];
-  __shared__ int sh_dec[64];
-  __shared__ int sh_bad, sh_n, sh_st, sh_y;
-  __shared__ double sh_S;
+  __shared__ double sw[kTopkMax];
+  __shared__ int sidx_all[kTopkMax];
+  __shared__ double red[kWaves];
+  __shared__ int sx[64];
+  __shared__ int redi[2 * kWaves];
+  __shared__ int sh_n, sh_st;
   const int b = blockIdx.x;
   const int k = p.k, V = p.V, tid = threadIdx.x, K = p.top_k;
-  const int32_t* x = p.tokens + (size_t)b * k;
-  if (tid == 0) sh_bad = 0;
-  __syncthreads();
-  for (int r = tid; r < p.rows_t + p.rows_d; r += kBlock) {
-    const int grow = r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t);
-    if (p.k_bad[grow]) sh_bad = 1;
+  const int nrows = p.rows_t + p.rows_d;
+  // round 1: row validity, drafted tokens, uniforms, p'(x) and q'(x)
+  int bad = 0;
+  for (int r = tid; r < nrows; r += kBlock)
+    bad |= p.k_bad[r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t)];
+  int xj = 0;
+  double a = 0.0, bq = 0.0, u = 0.0;
+  const double ur = (double)p.ur[b];
+  if (tid < k) {
+    xj = p.tokens[(size_t)b * k + tid];
+    a = p.k_px[trow(p, b, tid)];
+    bq = p.k_px[drow(p, b, tid)];
+    u = (double)p.u[(size_t)b * k + tid];
+    sx[tid] = xj;
   }
-  __syncthreads();
-  if (sh_bad) { emit_invalid(p, b, 4); return; }
-  for (int j = tid; j < k; j += kBlock) {
-    const int xj = x[j];
-    int dec;
-    if (xj < 0 || xj >= V) dec = 3;
-    else {
-      const double a = kept_prob_1(p, trow(p, b, j), xj);
-      const double bq = kept_prob_1(p, drow(p, b, j), xj);
-      const double u = (double)p.u[(size_t)b * k + j];
-      dec = bq > 0.0 ? (u < fmin(1.0, a / bq) ? 1 : 0) : (a > 0.0 ? 1 : 0);
-    }
-    sh_dec[j] = dec;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    int n = k, st = 0;
-    for (int j = 0; j < k; ++j) {
-      if (sh_dec[j] == 3) { st |= 1; n = j; break; }
-      if (sh_dec[j] == 0) { n = j; break; }
-    }
-    sh_n = n; sh_st = st;
+  if (__syncthreads_or(bad)) { emit_invalid(p, b, 4); return; }
+  if (tid < 64) {
+    const bool inv = tid < k && (xj < 0 || xj >= V);
+    bool acc = true;
+    if (tid < k && !inv) acc = bq > 0.0 ? (u < fmin(1.0, a / bq)) : (a > 0.0);
+    int st;
+    const int n = first_failure(tid < k && (inv || !acc), inv, k, &st);
+    if (tid == 0) { sh_n = n; sh_st = st; }
   }
   __syncthreads();
   const int n = sh_n;
+  // round 2: the kept sets of p'_n and (n < k) q'_n
   const int gp = trow(p, b, n);
   const int np = p.k_cnt[gp];
   const double normp = p.k_norm[gp];
-  const int32_t* pidx = p.k_idx + (size_t)gp * K;
-  const double* pe = p.k_e + (size_t)gp * K;
-  for (int i = tid; i < np; i += kBlock) {
-    const double pa = pe[i] / normp;
-    sidx[i] = pidx[i];
-    if (n < k) {
-      const double qa = kept_prob_1(p, drow(p, b, n), pidx[i]);
-      const double d = pa - qa;
-      rw[i] = d > 0.0 ? d : 0.0;
-    } else {
-      rw[i] = pa;
-    }
+  int pidx = -1;
+  double pe = 0.0;
+  if (tid < np) { pidx = p.k_idx[(size_t)gp * K + tid]; pe = p.k_e[(size_t)gp * K + tid]; }
+  int nq = 0;
+  double normq = 1.0;
+  if (n < k) {
+    const int gq = drow(p, b, n);
+    nq = p.k_cnt[gq];
+    normq = p.k_norm[gq];
+    if (tid < nq) { qidx[tid] = p.k_idx[(size_t)gq * K + tid]; qe[tid] = p.k_e[(size_t)gq * K + tid]; }
   }
-  // vocabulary order of the target's kept entries
-  const int P = next_pow2(np);
-  for (int i = tid; i < P; i += kBlock)
-    buf[i] = i < np ? (((uint64_t)(~(uint32_t)pidx[i])) << 32) | (uint32_t)i : 0ull;
-  bitonic_desc(buf, P);
-  if (tid == 0) {
-    double S = 0.0;
-    for (int i = 0; i < np; ++i) S += rw[(int)(buf[i] & 0xffffffffu)];
-    if (!(S > 0.0)) {   // empty residual: draw from p'_n
-      S = 0.0;
-      for (int i = 0; i < np; ++i) { const int sl = (int)(buf[i] & 0xffffffffu); rw[sl] = pe[sl] / normp; S += rw[sl]; }
+  if (tid < np) sidx_all[tid] = pidx;
+  __syncthreads();
+  double w = 0.0;
+  int rank = 0;
+  if (tid < np) {
+    const double pa = pe / normp;
+    if (n < k) {
+      double qa = 0.0;
+      for (int i = 0; i < nq; ++i) if (qidx[i] == pidx) { qa = qe[i] / normq; break; }
+      const double d = pa - qa;
+      w = d > 0.0 ? d : 0.0;
+    } else {
+      w = pa;
     }
-    const double t = (double)p.ur[b] * S;
-    double c = 0.0;
-    int y = -1, lastpos = -1;
-    for (int i = 0; i < np; ++i) {
-      const int sl = (int)(buf[i] & 0xffffffffu);
-      c += rw[sl];
-      if (rw[sl] > 0.0) lastpos = sidx[sl];
-      if (y < 0 && rw[sl] > 0.0 && c > t) y = sidx[sl];
-    }
-    sh_y = y < 0 ? lastpos : y;
-    sh_S = S;
+    for (int i = 0; i < np; ++i) rank += sidx_all[i] < pidx;   // vocabulary order
+    sidx[rank] = pidx;
+    sw[rank] = w;
   }
   __syncthreads();
+  // inverse CDF in vocabulary order over the target's kept entries
+  double ws = tid < np ? sw[tid] : 0.0;
+  double S;
+  double ex = block_exscan(ws, red, &S);
+  bool p_only = n == k;
+  if (!(S > 0.0)) {   // empty residual: draw from p'_n
+    __syncthreads();
+    if (tid < np) sw[rank] = pe / normp;
+    __syncthreads();
+    ws = tid < np ? sw[tid] : 0.0;
+    ex = block_exscan(ws, red, &S);
+    p_only = true;
+  }
+  const double t = ur * S;
+  int ymin = INT_MAX, ylast = -1;
+  if (tid < np && ws > 0.0) {
+    if (ex + ws > t) ymin = tid;
+    ylast = tid;
+  }
+  block_minmax(ymin, ylast, redi);
+  const int ys = ymin != INT_MAX ? ymin : ylast;
+  const int y = ys >= 0 ? sidx[ys] : -1;
   if (p.resid_probs) {
     float* rp = p.resid_probs + (size_t)b * V;
     for (int v = tid; v < V; v += kBlock) rp[v] = 0.f;
     __syncthreads();
-    for (int i = tid; i < np; i += kBlock) rp[sidx[i]] = (float)(rw[i] / sh_S);
+    if (tid < np) rp[sidx[tid]] = (float)(ws / S);
   }
-  emit_tokens(p, b, x, n, sh_y, sh_st);
+  (void)p_only;
+  emit_tokens(p, b, sx, n, y, sh_st);
 }
 
 // ================================================================== plain and nucleus sampling
@@ -1015,163 +1241,188 @@ __global__ __launch_bounds__(kBlock) void k_topk_final(Params p) {
 // After the stream pass (float64 row sums per tile) -- and, for the nucleus,
 // the exact cut per row (k_topp_rows) -- two kernels finish a call:
 //   k_resid_s     grid (segment, sequence): every workgroup of a sequence
-//                 redoes its accept step (k tests on a few dozen partials and
+//                 redoes its accept step (row views from the tile partials,
 //                 2k logits), then sums the residual max(0, p' - q') (or p'_k
 //                 after full acceptance) over its segment of kResidSeg
 //                 entries in float64; segment 0 publishes the sequence state.
-//   k_resid_final one workgroup per sequence: S' = sum of the segments, the
-//                 segment where ur * S' falls, the entry inside it, outputs.
-
-// The adjusted view of row `grow` (FILT: kFiltNone or kFiltTopp).
-template <typename T, int FILT>
-DEV RowView sample_view(const Params& p, int grow, double invT, bool* bad) {
-  if constexpr (FILT == kFiltTopp) {
-    const RowNuc nu = p.nuc[grow];
-    *bad = nu.ok != 1;
-    return RowView{row_ptr<T>(p, grow), (double)nu.M * invT, nu.N, nu.cut};
-  } else {
-    const RowStat rs = combine_tiles(p, grow, true);
-    *bad = (rs.Z != rs.Z) || (rs.M == INFINITY) || (rs.M == -INFINITY);
-    return RowView{row_ptr<T>(p, grow), (double)rs.M * invT, rs.Z, 0ull};
-  }
-}
-
-// The accept step of sequence b.  Returns false if a row is invalid (the
-// outputs are then written by the workgroup with `emit`).
-template <typename T, int FILT>
-DEV bool accept_step(const Params& p, int b, bool emit, int* n_out, int* st_out) {
-  __shared__ int rBad[kMaxRows];
-  __shared__ int sh_dec[64];
-  __shared__ int sh_internal;
-  const int k = p.k, V = p.V, tid = threadIdx.x;
-  const double invT = 1.0 / p.T;
-  const int nrows = p.rows_t + p.rows_d;
-  const int32_t* x = p.tokens + (size_t)b * k;
-  if (tid == 0) sh_internal = 0;
-  __syncthreads();
-  for (int r = tid; r < nrows; r += kBlock) {
-    const int grow = r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t);
-    bool bad;
-    sample_view<T, FILT>(p, grow, invT, &bad);
-    rBad[r] = bad ? 1 : 0;
-    if (FILT == kFiltTopp && p.nuc[grow].ok == 2) sh_internal = kStatusInternal;
-  }
-  __syncthreads();
-  if (rows_bad<T>(p, b, rBad, nrows)) {
-    if (emit) emit_invalid(p, b, 4 | sh_internal);
-    return false;
-  }
-  for (int j = tid; j < k; j += kBlock) {
-    const int xj = x[j];
-    int dec;
-    if (xj < 0 || xj >= V) dec = 3;
-    else {
-      bool dummy;
-      const double a = prob_of<T>(sample_view<T, FILT>(p, trow(p, b, j), invT, &dummy), invT, xj);
-      const double bq = prob_of<T>(sample_view<T, FILT>(p, drow(p, b, j), invT, &dummy), invT, xj);
-      const double u = (double)p.u[(size_t)b * k + j];
-      dec = bq > 0.0 ? (u < fmin(1.0, a / bq) ? 1 : 0) : (a > 0.0 ? 1 : 0);
-    }
-    sh_dec[j] = dec;
-  }
-  __syncthreads();
-  int n = k, st = 0;
-  for (int j = 0; j < k; ++j) {
-    if (sh_dec[j] == 3) { st |= 1; n = j; break; }
-    if (sh_dec[j] == 0) { n = j; break; }
-  }
-  *n_out = n;
-  *st_out = st;
-  __syncthreads();
-  return true;
-}
+//   k_resid_final grid (segment, sequence): every workgroup finds S' and the
+//                 segment where ur * S' falls; that segment's workgroup draws
+//                 the token; all of them write resid_probs if asked.
 
 template <typename T, int FILT>
 __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
+  __shared__ double vnmc[kMaxRows], vinv[kMaxRows];
+  __shared__ uint64_t vcut[kMaxRows];
+  __shared__ float vlx[kMaxRows];
+  __shared__ int vbad[kMaxRows];
   __shared__ double red[kWaves];
-  const int b = blockIdx.y, seg = blockIdx.x;
-  int n, st;
-  if (!accept_step<T, FILT>(p, b, seg == 0, &n, &st)) {
-    if (seg == 0 && threadIdx.x == 0) p.seq_n[b] = -1;
+  __shared__ double tab[64];
+  __shared__ int sh_n, sh_st;
+  const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  const int k = p.k, V = p.V, nrows = p.rows_t + p.rows_d;
+  const double c64 = 64.0 * kLog2e / p.T;
+  auto row_of = [&](int r) { return r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t); };
+  // one round of loads: drafted tokens, uniforms, the drafted tokens' logits
+  // (recorded by the streaming pass) and the row views
+  int xj = 0;
+  float uj = 0.f;
+  if (tid < k) { xj = p.tokens[(size_t)b * k + tid]; uj = p.u[(size_t)b * k + tid]; }
+  for (int r = tid; r < nrows; r += kBlock) vlx[r] = p.row_lx[row_of(r)];
+  int internal = 0;
+  if constexpr (FILT == kFiltTopp) {
+    for (int r = tid; r < nrows; r += kBlock) {
+      const RowNuc nu = p.nuc[row_of(r)];
+      vnmc[r] = -(double)nu.M * c64; vinv[r] = 1.0 / nu.N; vcut[r] = nu.cut; vbad[r] = nu.ok != 1;
+      internal |= nu.ok == 2;
+    }
+  } else {
+    combine_rows<true>(p, nrows, row_of, [&](int r, float M, int, double Z, int bad) {
+      vnmc[r] = -(double)M * c64; vinv[r] = 1.0 / Z; vcut[r] = 0ull; vbad[r] = bad;
+    });
+  }
+  exp2_table_init(tab);
+  int mybad = 0;
+  for (int r = tid; r < nrows; r += kBlock) mybad |= vbad[r];
+  internal = __syncthreads_or(internal);
+  if (__syncthreads_or(mybad)) {
+    if (seg == 0) {
+      emit_invalid(p, b, 4 | (internal ? kStatusInternal : 0));
+      if (tid == 0) p.seq[b].n = -1;
+    }
     return;
   }
-  const double invT = 1.0 / p.T;
-  bool dummy;
-  const RowView pr = sample_view<T, FILT>(p, trow(p, b, n), invT, &dummy);
-  RowView qrv{nullptr, 0.0, 1.0, 0ull};
-  if (n < p.k) qrv = sample_view<T, FILT>(p, drow(p, b, n), invT, &dummy);
+  // the accept tests (no memory access)
+  if (tid < 64) {
+    const bool inv = tid < k && (xj < 0 || xj >= V);
+    bool acc = true;
+    if (tid < k && !inv) {
+      const int rd = p.rows_t + tid;
+      const RowView vt{nullptr, vnmc[tid], vinv[tid], vcut[tid]};
+      const RowView vd{nullptr, vnmc[rd], vinv[rd], vcut[rd]};
+      const double a = prob_from(vt, c64, tab, vlx[tid], xj);
+      const double q = prob_from(vd, c64, tab, vlx[rd], xj);
+      acc = q > 0.0 ? ((double)uj < fmin(1.0, a / q)) : (a > 0.0);
+    }
+    int st;
+    const int n = first_failure(tid < k && (inv || !acc), inv, k, &st);
+    if (tid == 0) { sh_n = n; sh_st = st; }
+  }
+  __syncthreads();
+  const int n = sh_n;
+  // residual mass of this segment
+  const RowView pr{row_ptr<T>(p, trow(p, b, n)), vnmc[n], vinv[n], vcut[n]};
+  RowView qr{nullptr, 0.0, 1.0, 0ull};
+  if (n < k) {
+    const int rd = p.rows_t + n;
+    qr = RowView{row_ptr<T>(p, drow(p, b, n)), vnmc[rd], vinv[rd], vcut[rd]};
+  }
   double w[kVec];
-  double tot;
-  resid_chunk<T>(pr, n < p.k ? &qrv : nullptr, invT, p.V, p.aligned, seg * kResidSeg, w, red, &tot);
-  if (threadIdx.x == 0) {
+  const double t = resid_weights<T>(pr, qr, n < k, c64, tab, V, p.aligned, seg * kResidSeg + tid * kVec, w);
+  const double tot = block_sum(t, red);
+  if (tid == 0) {
     p.spart[(size_t)b * p.S2 + seg] = tot;
-    if (seg == 0) { p.seq_n[b] = n; p.seq_st[b] = st; }
+    if (seg == 0) {
+      SeqState ss;
+      ss.nmc_p = pr.nmc; ss.inv_p = pr.inv; ss.cut_p = pr.cut;
+      ss.nmc_q = qr.nmc; ss.inv_q = qr.inv; ss.cut_q = qr.cut;
+      ss.n = n; ss.st = sh_st;
+      p.seq[b] = ss;
+    }
   }
 }
+
+constexpr int kSegStage = 1024;   // residual segment masses staged in LDS
 
 template <typename T, int FILT>
 __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   __shared__ double red[kWaves];
-  __shared__ int sh_int, sh_c;
+  __shared__ double tab[64];
+  __shared__ double spl[kSegStage];
+  __shared__ int sx[64];
+  __shared__ int redi[2 * kWaves];
   __shared__ double sh_base;
-  const int b = blockIdx.x;
-  const int n = p.seq_n[b];
-  if (n < 0) return;
-  const int V = p.V, k = p.k;
-  const double invT = 1.0 / p.T;
-  bool dummy;
-  const RowView pr = sample_view<T, FILT>(p, trow(p, b, n), invT, &dummy);
-  RowView qrv{nullptr, 0.0, 1.0, 0ull};
-  if (n < k) qrv = sample_view<T, FILT>(p, drow(p, b, n), invT, &dummy);
-  const RowView* qr = n < k ? &qrv : nullptr;
-  const int32_t* x = p.tokens + (size_t)b * k;
+  const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  const int S2 = p.S2, V = p.V, k = p.k;
+  const double c64 = 64.0 * kLog2e / p.T;
+  // one round of loads: sequence state, segment masses, ur, drafted tokens
+  const SeqState ss = p.seq[b];
   const double ur = (double)p.ur[b];
-  double S = 0.0;
-  for (int s = 0; s < p.S2; ++s) S += p.spart[(size_t)b * p.S2 + s];
-  int y;
-  bool p_only = (qr == nullptr);
-  if (S > 0.0) {
-    const double t = ur * S;
-    if (threadIdx.x == 0) {
-      double base = 0.0, lastbase = 0.0;
-      int c = -1, lastc = 0;
-      for (int s = 0; s < p.S2; ++s) {
-        const double ps = p.spart[(size_t)b * p.S2 + s];
-        if (ps > 0.0) { lastc = s; lastbase = base; }
-        if (base + ps > t) { c = s; break; }
-        base += ps;
+  const double* spg = p.spart + (size_t)b * S2;
+  const bool staged = S2 <= kSegStage;
+  if (staged) for (int s = tid; s < S2; s += kBlock) spl[s] = spg[s];
+  if (tid < k) sx[tid] = p.tokens[(size_t)b * k + tid];
+  exp2_table_init(tab);
+  if (ss.n < 0) return;
+  auto sp = [&](int s) { return staged ? spl[s] : spg[s]; };
+  const int n = ss.n;
+  const RowView pr{row_ptr<T>(p, trow(p, b, n)), ss.nmc_p, ss.inv_p, ss.cut_p};
+  const RowView qr{n < k ? row_ptr<T>(p, drow(p, b, n)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
+  // S' = sum of the segment masses; thread t owns segments [t*per, (t+1)*per)
+  const int per = (S2 + kBlock - 1) / kBlock;
+  double lsum = 0.0;
+  for (int q = 0; q < per; ++q) { const int s = tid * per + q; if (s < S2) lsum += sp(s); }
+  double S;
+  const double ex0 = block_exscan(lsum, red, &S);
+  if (!(S > 0.0)) {
+    // empty residual: p'_n, drawn and written by one workgroup
+    if (seg != 0) return;
+    double S1;
+    const int y = resid_draw<T>(pr, c64, tab, V, p.aligned, ur, red, redi, &S1);
+    if (p.resid_probs) {
+      float* rp = p.resid_probs + (size_t)b * V;
+      for (int c0 = 0; c0 < V; c0 += kResidSeg) {
+        double w[kVec];
+        resid_weights<T>(pr, qr, false, c64, tab, V, p.aligned, c0 + tid * kVec, w);
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          const int v = c0 + tid * kVec + q;
+          if (v < V) rp[v] = (float)(w[q] / S1);
+        }
       }
-      if (c < 0) { c = lastc; base = lastbase; }
-      sh_c = c;
-      sh_base = base;
     }
-    __syncthreads();
-    const int c = sh_c;
-    const double base = sh_base;
-    __syncthreads();
-    double w[kVec];
-    double tc;
-    const double ex = resid_chunk<T>(pr, qr, invT, V, p.aligned, c * kResidSeg, w, red, &tc);
-    y = pick_in_chunk(base, ex, w, c * kResidSeg, t, &sh_int);
-  } else {
-    y = resid_draw<T>(pr, nullptr, invT, V, p.aligned, ur, red, &sh_int, &S);   // empty residual: p'_n
-    p_only = true;
+    emit_tokens(p, b, sx, n, y, ss.st);
+    return;
+  }
+  // the segment where t = ur * S' falls (or the last one with mass)
+  const double t = ur * S;
+  int cross = INT_MAX, lastpos = -1;
+  {
+    double run = ex0;
+    for (int q = 0; q < per; ++q) {
+      const int s = tid * per + q;
+      if (s >= S2) break;
+      const double ps = sp(s);
+      if (ps > 0.0) lastpos = s;
+      if (cross == INT_MAX && run + ps > t) cross = s;
+      run += ps;
+    }
+  }
+  block_minmax(cross, lastpos, redi);
+  const int c = cross != INT_MAX ? cross : lastpos;
+  if (tid == c / per) {
+    double run = ex0;
+    for (int s = tid * per; s < c; ++s) run += sp(s);
+    sh_base = run;
+  }
+  if (seg != c && !p.resid_probs) return;
+  __syncthreads();
+  const double base = sh_base;
+  double w[kVec];
+  double tc;
+  const int c0 = seg * kResidSeg;
+  const double ex = resid_chunk<T>(pr, qr, n < k, c64, tab, V, p.aligned, c0, w, red, &tc);
+  if (seg == c) {
+    const int y = pick_in_chunk(base, ex, w, c0, t, redi);
+    emit_tokens(p, b, sx, n, y, ss.st);
   }
   if (p.resid_probs) {
     float* rp = p.resid_probs + (size_t)b * V;
-    const RowView* q2 = p_only ? nullptr : qr;
-    for (int c0 = 0; c0 < V; c0 += kResidSeg) {
-      double w[kVec];
-      double tot;
-      resid_chunk<T>(pr, q2, invT, V, p.aligned, c0, w, red, &tot);
 #pragma unroll
-      for (int q = 0; q < kVec; ++q) {
-        const int v = c0 + threadIdx.x * kVec + q;
-        if (v < V) rp[v] = (float)(w[q] / S);
-      }
+    for (int q = 0; q < kVec; ++q) {
+      const int v = c0 + tid * kVec + q;
+      if (v < V) rp[v] = (float)(w[q] / S);
     }
   }
-  emit_tokens(p, b, x, n, y, p.seq_st[b]);
 }
 
 // ================================================================== stream kernel
@@ -1257,9 +1508,8 @@ DEV double nuc_bin_ref(const NucState& s, int b) {
 // below it (and still < dmax).
 template <typename T>
 DEV void nuc_hist(const T* row, int V, int aligned, NucState s, unsigned long long* hq,
-                  unsigned int* hc, unsigned int* below, double* red, double* A) {
+                  unsigned int* hc, unsigned int* below, double* red, int* redi, double* A) {
   for (int b = threadIdx.x; b < kNucBins; b += kBlock) { hq[b] = 0ull; hc[b] = 0u; }
-  if (threadIdx.x == 0) *below = 0u;
   __syncthreads();
   s.c0 = 0; s.c1 = kNucBins - 1;   // whole level = "window"
   const double ref1 = (double)s.p0lo * s.w0;
@@ -1285,14 +1535,15 @@ DEV void nuc_hist(const T* row, int V, int aligned, NucState s, unsigned long lo
     }
    }
   }
-  if (nb) atomicAdd(below, nb);
+  const int nbt = block_sum_i((int)nb, redi);
+  if (threadIdx.x == 0) *below = (unsigned)nbt;
   *A = block_sum(a, red);
   __syncthreads();
 }
 
 // First bin whose cumulative approximate mass (from A) reaches tgt.
 DEV int nuc_locate(const NucState& s, const unsigned long long* hq, double A, double tgt,
-                   double* red, int* sh_int) {
+                   double* red, int* redi) {
   double local[kNucBins / kBlock];
   double tsum = 0.0;
 #pragma unroll
@@ -1303,8 +1554,6 @@ DEV int nuc_locate(const NucState& s, const unsigned long long* hq, double A, do
   }
   double tot;
   const double ex = block_exscan(tsum, red, &tot);
-  if (threadIdx.x == 0) *sh_int = kNucBins - 1;
-  __syncthreads();
   double c = A + ex;
   int found = INT_MAX;
 #pragma unroll
@@ -1312,24 +1561,18 @@ DEV int nuc_locate(const NucState& s, const unsigned long long* hq, double A, do
     c += local[q];
     if (found == INT_MAX && c >= tgt) found = threadIdx.x * (kNucBins / kBlock) + q;
   }
-  if (found != INT_MAX) atomicMin(sh_int, found);
-  __syncthreads();
-  const int b = *sh_int;
-  __syncthreads();
-  return b;
+  int none = -1;
+  block_minmax(found, none, redi);
+  return found != INT_MAX ? found : kNucBins - 1;
 }
 
 // Exact nucleus cut of one valid row (see above); fills *out.
 template <typename T>
 DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc* outp,
                      unsigned long long* hq, unsigned int* hc, uint64_t* win, double* red,
-                     unsigned long long* redu, unsigned int* below_p, unsigned int* wcnt_p,
-                     int* sh_int_p, unsigned long long* sh_pmin_p, unsigned long long* sh_pmax_p) {
+                     unsigned long long* redu, int* redi, unsigned int* below_p, int* wcnt_p) {
   unsigned int& below = *below_p;
-  unsigned int& wcnt = *wcnt_p;
-  int& sh_int = *sh_int_p;
-  unsigned long long& sh_pmin = *sh_pmin_p;
-  unsigned long long& sh_pmax = *sh_pmax_p;
+  int& wcnt = *wcnt_p;
   RowNuc& out = *outp;
   const int V = p.V;
   const int tid = threadIdx.x;
@@ -1345,13 +1588,13 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
   s.c0 = 0; s.c1 = kNucBins - 1;
 
   double A = 0.0;
-  nuc_hist<T>(row, V, p.aligned, s, hq, hc, &below, red, &A);
+  nuc_hist<T>(row, V, p.aligned, s, hq, hc, &below, red, redi, &A);
   const double tgt = p.top_p * Z;
   bool located = false;
   int result = 0;   // 1 found, -1 failed
   for (int iter = 0; iter < 64 && result == 0; ++iter) {
     if (!located) {
-      const int b = nuc_locate(s, hq, A, tgt, red, &sh_int);
+      const int b = nuc_locate(s, hq, A, tgt, red, redi);
       s.c0 = b > 0 ? b - 1 : 0;
       s.c1 = b < kNucBins - 1 ? b + 1 : kNucBins - 1;
       located = true;
@@ -1369,28 +1612,26 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
 
     if (tw <= (unsigned long long)kWindowCap) {
       // gather the window; exact mass ranked above it
-      if (tid == 0) wcnt = 0u;
+      if (tid == 0) wcnt = 0;
       __syncthreads();
       double a = 0.0;
       for (int g = tid; g * kVec < V; g += kBlock) {
         float vv[kVec];
         const int ng = load_group<T>(row, g * kVec, V, p.aligned, vv);
-        for (int e = 0; e < ng; ++e) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
           const int i = g * kVec + e;
           const float l = vv[e];
           const double d = s.zm - (double)l * s.invT;
-          if (!(d < s.dmax)) continue;
-          int bin;
-          const int cls = nuc_class(s, l, i, d, &bin);
+          int cls = 2, bin;
+          if (e < ng && d < s.dmax) cls = nuc_class(s, l, i, d, &bin);
           if (cls == -1) a += exp(-d);
-          else if (cls == 0) {
-            const unsigned slot = atomicAdd(&wcnt, 1u);
-            if (slot < (unsigned)kWindowCap) win[slot] = pack(l, i);
-          }
+          const int slot = wave_append(cls == 0, &wcnt);
+          if (slot >= 0 && slot < kWindowCap) win[slot] = pack(l, i);
         }
       }
       const double Aw = block_sum(a, red);
-      const int n = (int)min(wcnt, (unsigned)kWindowCap);
+      const int n = min(wcnt, kWindowCap);
       const int P = next_pow2(n);
       for (int i = n + tid; i < P; i += kBlock) win[i] = 0ull;
       bitonic_desc(win, P);
@@ -1414,12 +1655,7 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
           c += e;
         }
       }
-      if (tid == 0) sh_int = 0;
-      __syncthreads();
-      atomicMax(&sh_int, kept_local);
-      __syncthreads();
-      const int kept = sh_int;
-      __syncthreads();
+      const int kept = block_max_i(kept_local, redi);
       if (kept == 0) {
         if (s.c0 == 0) result = -1;                     // cut above this level's range
         else { s.c1 = s.c0 - 1; s.c0 = s.c0 >= 3 ? s.c0 - 3 : 0; }
@@ -1441,8 +1677,6 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
       __syncthreads();
     } else {
       // too many entries near the cut: the window becomes the next level's range
-      if (tid == 0) { sh_pmin = ~0ull; sh_pmax = 0ull; }
-      __syncthreads();
       unsigned long long pmin = ~0ull, pmax = 0ull;
       for (int g = tid; g * kVec < V; g += kBlock) {
         float vv[kVec];
@@ -1459,17 +1693,15 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
           }
         }
       }
-      atomicMin(&sh_pmin, pmin);
-      atomicMax(&sh_pmax, pmax);
-      __syncthreads();
+      block_minmax(pmin, pmax, redu);
       if (s.level == 0) { s.p0lo = s.c0; s.p0hi = s.c1; }
-      s.plo = sh_pmin;
-      s.phi = sh_pmax;
+      s.plo = pmin;
+      s.phi = pmax;
       const unsigned long long span = s.phi - s.plo;
       int bits = span ? 64 - __clzll((long long)span) : 0;
       s.sh = bits > 11 ? bits - 11 : 0;
       s.level += 1;
-      nuc_hist<T>(row, V, p.aligned, s, hq, hc, &below, red, &A);
+      nuc_hist<T>(row, V, p.aligned, s, hq, hc, &below, red, redi, &A);
       located = false;
     }
   }
@@ -1481,31 +1713,28 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   const int grow = blockIdx.x;
   const T* row = row_ptr<T>(p, grow);
-  const int V = p.V;
-  const int tid = threadIdx.x;
 
   __shared__ unsigned long long hq[kNucBins];
   __shared__ unsigned int hc[kNucBins];
   __shared__ uint64_t win[kWindowCap];
   __shared__ double red[kWaves];
-  __shared__ unsigned long long redu[kWaves];
-  __shared__ unsigned int below, wcnt;
-  __shared__ int sh_int;
-  __shared__ unsigned long long sh_pmin, sh_pmax;
+  __shared__ unsigned long long redu[2 * kWaves];
+  __shared__ int redi[2 * kWaves];
+  __shared__ unsigned int below;
+  __shared__ int wcnt;
+  __shared__ float sh_M;
+  __shared__ double sh_Z;
+  __shared__ int sh_bad;
 
+  combine_rows<true>(p, 1, [&](int) { return grow; }, [&](int, float M, int, double Z, int bad) {
+    sh_M = M; sh_Z = Z; sh_bad = bad;
+  });
+  __syncthreads();
   RowNuc out;
-  out.Z = 0.0; out.N = 0.0; out.cut = 0ull; out.ok = 0; out.M = 0.f;
-
-  const RowStat rs = combine_tiles(p, grow, true);   // float64 row sum from the tiles
-  const bool invalid = (rs.Z != rs.Z) || (rs.M == INFINITY) || (rs.M == -INFINITY);
-  out.M = rs.M;
-  out.Z = rs.Z;
-  if (invalid) {
-    if (tid == 0) p.nuc[grow] = out;
-  } else {
-    topp_search<T>(p, row, rs.M, rs.Z, &out, hq, hc, win, red, redu, &below, &wcnt, &sh_int, &sh_pmin, &sh_pmax);
-    if (tid == 0) p.nuc[grow] = out;
-  }
+  out.Z = sh_Z; out.N = 0.0; out.cut = 0ull; out.ok = 0; out.M = sh_M;
+  if (!sh_bad)
+    topp_search<T>(p, row, out.M, out.Z, &out, hq, hc, win, red, redu, redi, &below, &wcnt);
+  if (threadIdx.x == 0) p.nuc[grow] = out;
 }
 
 
@@ -1555,11 +1784,11 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
     case kFiltTopp:
       hipLaunchKernelGGL((k_topp_rows<T>), gr, block, 0, st, p);
       hipLaunchKernelGGL((k_resid_s<T, kFiltTopp>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T, kFiltTopp>), gb, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T, kFiltTopp>), gs, block, 0, st, p);
       break;
     default:  // plain sampling
       hipLaunchKernelGGL((k_resid_s<T, kFiltNone>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), gb, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), gs, block, 0, st, p);
       break;
   }
   return hipGetLastError();
