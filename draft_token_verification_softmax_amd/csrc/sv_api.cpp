@@ -57,11 +57,7 @@ Plan make_plan(const sv_config* c) {
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
   p.S_max = (c->vocab + kMinTile - 1) / kMinTile;
   if (p.S_max > sv::kMaxTiles) p.S_max = sv::kMaxTiles;
-  p.cand_w = p.top_k;
-  if (p.top_k > 0) {
-    const int cap = sv::kMergeCap / p.cand_w;
-    if (p.S_max > cap) p.S_max = cap;
-  }
+  p.cand_w = p.top_k > 0 ? sv::kCandSlots : 0;
   if (p.S_max < 1) p.S_max = 1;
   p.S2_max = (c->vocab + sv::kResidSeg - 1) / sv::kResidSeg;
   return p;

@@ -11,6 +11,7 @@ constexpr int kBlock = 256;            // threads per workgroup (4 wave64s)
 constexpr int kVec = 8;                // logits per group: 16 B of bf16, 32 B of fp32
 constexpr int kTopkCap = 2560;         // LDS candidate slots of the top-k tile kernel
 constexpr int kMergeCap = 4096;        // LDS slots when merging a row's top-k candidates
+constexpr int kCandSlots = 256;        // per-tile top-k candidate slots in the workspace
 constexpr int kWindowCap = 2048;       // LDS slots for the nucleus boundary window
 constexpr int kNucBins = 2048;         // histogram bins of the nucleus search
 constexpr int kResidSeg = kBlock * kVec;  // logits per workgroup in the residual kernels
@@ -22,6 +23,8 @@ constexpr int kMaxTiles = 64;          // tiles per row (one wave combines a row
 //   s    NaN iff the tile holds a NaN or +inf (exact, every mode); otherwise
 //        STATS mode: float64 sum over the tile of exp((l - m) / T), other
 //        modes: 0
+// TOPK mode instead: m = the tile's top_k-th logit (-inf if it has fewer),
+// amax = the length of its list (its top_k in rank order, in p.cand).
 struct TileStat {
   float m;
   int32_t amax;
@@ -90,8 +93,8 @@ struct Params {
   int grid;     // workgroups of the streaming launch (resident capacity)
   // workspace
   TileStat* tiles;   // [rows][S]
-  uint64_t* cand;    // [rows][S][cand_w] (top-k)
-  int cand_w;        // candidate slots per tile (top_k rounded up)
+  uint64_t* cand;    // [rows][S][cand_w] (top-k): each tile's candidate list
+  int cand_w;        // candidate slots per tile
   RowNuc* nuc;       // [rows] (top-p)
   float* row_lx;     // [rows] logit of the drafted token a row's accept test reads
                      // (written by the tile holding it; sampling modes)

@@ -351,6 +351,23 @@ DEV int wave_append(bool take, int* counter) {
   return take ? base + below : -1;
 }
 
+// Wave-aggregated reservation of n >= 0 slots per lane: returns the lane's
+// first slot (consecutive in lane order); one LDS atomic per wave.  Call
+// with every lane of the wave active.
+DEV int wave_reserve(int n, int* counter) {
+  const int lane = threadIdx.x & 63;
+  int incl = n;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o);
+    if (lane >= o) incl += t;
+  }
+  const int total = __shfl(incl, 63);
+  int base = 0;
+  if (lane == 0 && total > 0) base = atomicAdd(counter, total);
+  return __shfl(base, 0) + incl - n;
+}
+
 // Exclusive scan of one double per thread in thread order (fixed order).
 // Returns the exclusive prefix; *total gets the block total.
 DEV double block_exscan(double v, double* red, double* total) {
@@ -485,14 +502,16 @@ DEV void combine_rows(const Params& p, int nrows, RowOf row_of, Sink sink) {
 
 // ================================================================== tile passes
 
-// Max and lowest index of the max of a tile.
+// Max and lowest index of the max of a tile.  Lanes only track their max
+// and the first group that reached it; once the tile max is known, the few
+// lanes that hold it reload that group (16 bytes) and find the index.
 template <typename T>
 DEV void tile_argmax(const Params& p, const T* row, int start, int end, int ngroups, int tile) {
   __shared__ float redm[kWaves];
-  __shared__ int redi[kWaves];
+  __shared__ int redi[2 * kWaves];
   const int nfull = (end - start) / kVec;
   float m = -INFINITY;
-  int mi = INT_MAX;
+  int gbest = 0;
   uint32_t probe = 0;
   bool nanv = false;
   for (int g0 = threadIdx.x; g0 < ngroups; g0 += kUnroll * kBlock) {
@@ -502,21 +521,26 @@ DEV void tile_argmax(const Params& p, const T* row, int start, int end, int ngro
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const float gm = max8(v[u]);
-      if (gm > m) {
-        const int pos = start + (g0 + u * kBlock) * kVec;
-        int idx = pos;
-#pragma unroll
-        for (int e = kVec - 1; e >= 0; --e) if (v[u][e] == gm) idx = pos + e;
-        m = gm;
-        mi = idx;
-      }
+      const bool better = gm > m;
+      m = better ? gm : m;
+      gbest = better ? g0 + u * kBlock : gbest;
     }
   }
   const bool nan = __syncthreads_or(nanv || Group<T>::has_nan(probe));
-  block_argmax(m, mi, redm, redi);
+  const float M = block_max(m, redm);
+  int idx = INT_MAX;
+  if (m == M && M > -INFINITY) {
+    float v[kVec];
+    const int pos = start + gbest * kVec;
+    load_group<T>(row, pos, end, p.aligned, v);
+#pragma unroll
+    for (int e = kVec - 1; e >= 0; --e) if (v[e] == M) idx = pos + e;
+  }
+  int none = -1;
+  block_minmax(idx, none, redi);
   if (threadIdx.x == 0) {
     TileStat ts;
-    ts.m = m; ts.amax = mi; ts.s = (nan || m == INFINITY) ? (double)NAN : 0.0;
+    ts.m = M; ts.amax = idx; ts.s = (nan || M == INFINITY) ? (double)NAN : 0.0;
     p.tiles[tile] = ts;
   }
 }
@@ -555,6 +579,7 @@ DEV void tile_stats64(const Params& p, const T* row, int start, int end, int ngr
     load_iter<T>(row, start, end, ngroups, nfull, p.aligned, g0, v, nv, probe, nanv);
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
+      if (nv[u] == 0) continue;   // past the tile (uniform across most waves)
       const float gm = max8(v[u]);
       if (gm > m) {
         if (m > -INFINITY) s *= exp2_64(((double)m - (double)gm) * c64, tab);
@@ -583,11 +608,10 @@ DEV void tile_stats64(const Params& p, const T* row, int start, int end, int ngr
 // to the best top_k and the admission threshold raised.
 template <typename T>
 DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int ngroups, int tile,
-                          uint64_t* buf) {
+                          uint64_t* buf, unsigned short* rank) {
   __shared__ int cnt;
   __shared__ float tau_f;
   __shared__ uint64_t tau_p;
-  __shared__ unsigned short rank[kTopkCap];
   const int K = p.top_k;
   const int tid = threadIdx.x;
   if (tid == 0) { cnt = 0; tau_f = -INFINITY; tau_p = 0ull; }
@@ -640,101 +664,179 @@ DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int
   const bool bad = __syncthreads_or(badv);
   const int c = cnt;
   uint64_t* out = p.cand + (size_t)tile * p.cand_w;
-  for (int i = tid; i < p.cand_w; i += kBlock) out[i] = (i < c) ? buf[i] : 0ull;
+  for (int i = tid; i < c; i += kBlock) out[i] = buf[i];
   if (tid == 0) {
     TileStat ts;
-    ts.m = c > 0 ? packed_val(buf[0]) : -INFINITY;
-    ts.amax = c > 0 ? packed_idx(buf[0]) : INT_MAX;
+    ts.m = c >= K ? packed_val(buf[K - 1]) : -INFINITY;   // a lower bound of the tile's top_k-th
+    ts.amax = c;
     ts.s = bad ? (double)NAN : 0.0;
     p.tiles[tile] = ts;
   }
   __syncthreads();
 }
 
-// Descending sort of one float per lane across a wave (bitonic network on
+// Descending sort of one value per lane across a wave (bitonic network on
 // shuffles, no LDS or barriers); lane i gets the i-th largest.
-DEV float wave_sort_desc(float x) {
+template <typename V>
+DEV V wave_sort_desc(V x) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
   for (int size = 2; size <= 64; size <<= 1) {
 #pragma unroll
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const float y = __shfl_xor(x, stride);
-      const bool lower = (lane & stride) == 0;        // this lane holds the lower index of the pair
+      const V y = __shfl_xor(x, stride);
+      const bool lower = (lane & stride) == 0;        // lower index of the pair
       const bool desc = (lane & size) == 0 || size == 64;
-      // keep the larger value at the lower index of a descending run
-      const bool keep_max = lower == desc;
-      x = keep_max ? fmaxf(x, y) : fminf(x, y);
+      const bool keep_max = lower == desc;            // descending runs keep the max low
+      const bool ygt = y > x;
+      x = (keep_max == ygt) ? y : x;
     }
   }
   return x;
 }
 
+// Orders the c distinct keys in lst (LDS, room for c rounded up to 64)
+// descending and calls emit(rank, key) for ranks < K.  Runs of 64 are sorted
+// in registers by the waves and written back in place (zero padded); a key's
+// rank is its place in its run plus binary searches in the other runs.
+template <typename Emit>
+DEV void rank_top(uint64_t* lst, int c, int K, Emit emit) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int nruns = (c + 63) >> 6;
+  __syncthreads();
+  for (int r0 = 0; r0 < nruns; r0 += kWaves) {
+    const int r = r0 + (tid >> 6);
+    const int i = r * 64 + lane;
+    const uint64_t key = (r < nruns && i < c) ? lst[i] : 0ull;
+    const uint64_t srt = wave_sort_desc(key);
+    if (r < nruns) lst[i] = srt;
+  }
+  __syncthreads();
+  for (int i = tid; i < c; i += kBlock) {
+    const uint64_t key = lst[i];
+    const int r = i >> 6;
+    int rank = i & 63;
+    for (int q = 0; q < nruns && rank < K; ++q) {
+      if (q == r) continue;
+      const uint64_t* run = lst + q * 64;
+      int lo = 0, hi = 64;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (run[mid] > key) lo = mid + 1; else hi = mid;
+      }
+      rank += lo;
+    }
+    if (rank < K) emit(rank, key);
+  }
+  __syncthreads();
+}
+
+// LDS of one top-k tile workgroup (u64 words): the candidate list and the
+// groups that reach the threshold; the exact fallback reuses it whole.
+constexpr int kCandCap = 1024;                        // candidate entries
+constexpr int kGrpCap = 480;                          // groups holding one
+constexpr int kTopkLds = kTopkCap + kTopkCap / 4;     // fallback: keys + u16 ranks
+static_assert(kCandCap * 8 + kGrpCap * (kVec * 4 + 4) <= kTopkLds * 8, "top-k LDS layout");
+
 // The tile's top_k under (value desc, index asc), written to p.cand in
 // rank order (zero-padded to cand_w).
-//  1. Admission threshold tau from the first kUnroll groups of every lane:
-//     each wave sorts its 64 lane maxima in registers and takes the
-//     ceil(top_k / 4)-th largest; tau is the smallest of the four.  Every
-//     wave then holds at least ceil(top_k / 4) logits >= tau, so the tile
-//     holds at least top_k of them and tau is a lower bound of its top_k-th.
-//  2. The tile streams; logits >= tau go to an LDS list (one atomic per wave).
-//  3. Each listed entry's rank is the number of entries above it; the first
-//     top_k ranks are written out.  No sort, no barrier beyond one.
-// If the list would overflow, the tile is redone by tile_topk_rounds.
+//  1. Admission threshold tau, raised after every kUnroll groups per lane:
+//     each wave sorts its 64 lane maxima (over those groups) in registers
+//     and takes the ceil(top_k / 4)-th largest; the smallest of the four
+//     waves' values has at least top_k logits at or above it in the tile,
+//     so it (and the running max of such values) bounds the tile's top_k-th
+//     logit from below.
+//  2. The tile streams; a group whose max reaches the current tau is copied
+//     to LDS (one atomic per wave and step).  Only those groups are looked
+//     at again: their logits >= the final tau become the candidate list.
+//  3. The candidates are ranked (rank_top) and the tile's exact top_k goes
+//     out in rank order (p.cand), with its length and its top_k-th logit in
+//     the tile's TileStat (amax, m).  Every entry of the row's top_k is >=
+//     the largest of those values over the row's tiles, and the per-row
+//     merge keeps only those.
+// If an LDS list would overflow, the tile is redone by tile_topk_rounds.
 template <typename T>
 DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroups, int tile,
-                   uint64_t* buf) {
-  __shared__ int cnt, overflow;
+                   uint64_t* lds) {
+  __shared__ int cnt, ncg, overflow;
   __shared__ float wtau[kWaves];
   __shared__ int redi[2 * kWaves];
+  uint64_t* cand = lds;                                           // [kCandCap]
+  float* gval = reinterpret_cast<float*>(lds + kCandCap);         // [kGrpCap][kVec]
+  unsigned* gpos = reinterpret_cast<unsigned*>(gval + kGrpCap * kVec);   // [kGrpCap]: pos | nv << 28
   const int K = p.top_k;
   const int tid = threadIdx.x, lane = tid & 63;
   const int nfull = (end - start) / kVec;
-  if (tid == 0) { cnt = 0; overflow = 0; }
+  if (tid == 0) { cnt = 0; ncg = 0; overflow = 0; }
   uint32_t probe = 0;
-  bool nanv = false;
+  bool nanv = false, posinf = false;
   float tau = -INFINITY;
   for (int base = 0; base < ngroups; base += kUnroll * kBlock) {
     float v[kUnroll][kVec];
     int nv[kUnroll];
     load_iter<T>(row, start, end, ngroups, nfull, p.aligned, base + tid, v, nv, probe, nanv);
-    if (base == 0) {
+    if ((base / (kUnroll * kBlock)) % 4 == 0) {
       float mx = -INFINITY;
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, max8(v[u]));
       const float srt = wave_sort_desc(mx);
       const float tw = __shfl(srt, (K + kWaves - 1) / kWaves - 1);
+      __syncthreads();
       if (lane == 0) wtau[tid >> 6] = tw;
       __syncthreads();
-      tau = fminf(fminf(wtau[0], wtau[1]), fminf(wtau[2], wtau[3]));
+      tau = fmaxf(tau, fminf(fminf(wtau[0], wtau[1]), fminf(wtau[2], wtau[3])));
     }
+    bool take[kUnroll];
+    int ntake = 0;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const float gm = max8(v[u]);
-      if (__any(gm >= tau)) {
-        unsigned msk = 0u;
+      posinf |= gm == INFINITY;
+      take[u] = nv[u] > 0 && gm >= tau;
+      ntake += take[u];
+    }
+    if (__any(ntake > 0)) {
+      int slot = wave_reserve(ntake, &ncg);
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) msk |= (e < nv[u] && v[u][e] >= tau) ? (1u << e) : 0u;
-        // wave-exclusive prefix of the per-lane counts, one atomic per wave
-        const int c = __popc(msk);
-        int incl = c;
+      for (int u = 0; u < kUnroll; ++u) {
+        if (take[u]) {
+          if (slot < kGrpCap) {
+            float* d = gval + slot * kVec;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int t = __shfl_up(incl, o);
-          if (lane >= o) incl += t;
-        }
-        int slot = 0;
-        if (lane == 63) slot = atomicAdd(&cnt, incl);
-        slot = __shfl(slot, 63) + incl - c;
-        const int pos = start + (base + tid + u * kBlock) * kVec;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-          if ((msk >> e) & 1u) {
-            if (slot < kTopkCap) buf[slot] = pack(v[u][e], pos + e);
-            else overflow = 1;
-            ++slot;
+            for (int e = 0; e < kVec; ++e) d[e] = v[u][e];
+            gpos[slot] = (unsigned)(start + (base + tid + u * kBlock) * kVec) | ((unsigned)nv[u] << 28);
+          } else {
+            overflow = 1;
           }
+          ++slot;
         }
+      }
+    }
+  }
+  __syncthreads();
+  // the candidate list: logits >= tau of the copied groups
+  const int ng = ncg < kGrpCap ? ncg : kGrpCap;
+  for (int b0 = 0; b0 < ng; b0 += kBlock) {
+    const int i = b0 + tid;
+    const bool act = i < ng;
+    float gv[kVec];
+    unsigned gp = 0u;
+    if (act) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) gv[e] = gval[i * kVec + e];
+      gp = gpos[i];
+    }
+    const int pos = (int)(gp & 0x0fffffffu), gn = (int)(gp >> 28);
+    unsigned msk = 0u;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) msk |= (act && e < gn && gv[e] >= tau) ? (1u << e) : 0u;
+    int slot = wave_reserve(__popc(msk), &cnt);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      if ((msk >> e) & 1u) {
+        if (slot < kCandCap) cand[slot] = pack(gv[e], pos + e);
+        else overflow = 1;
+        ++slot;
       }
     }
   }
@@ -742,32 +844,24 @@ DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroup
   if (overflow) {
     // an adversarial tile: redo it exactly with the round-based path
     __syncthreads();
-    tile_topk_rounds<T>(p, row, start, end, ngroups, tile, buf);
+    tile_topk_rounds<T>(p, row, start, end, ngroups, tile, lds,
+                        reinterpret_cast<unsigned short*>(lds + kTopkCap));
     return;
   }
-  const bool nan = __syncthreads_or(nanv || Group<T>::has_nan(probe));
+  const bool bad = __syncthreads_or(nanv || posinf || Group<T>::has_nan(probe));
   const int c = cnt;
   uint64_t* out = p.cand + (size_t)tile * p.cand_w;
-  float top = -INFINITY;
-  int topi = INT_MAX;
-  for (int i = tid; i < c; i += kBlock) {
-    const uint64_t key = buf[i];
-    int r = 0;
-    for (int j = 0; j < c; ++j) r += buf[j] > key;
-    if (r < K) out[r] = key;
-    if (r == 0) { top = packed_val(key); topi = packed_idx(key); }
-  }
-  const int keep = c < K ? c : K;
-  for (int i = keep + tid; i < p.cand_w; i += kBlock) out[i] = 0ull;
-  // the entry of rank 0 is the tile max; its lane publishes it
-  int who = top > -INFINITY || topi != INT_MAX ? tid : INT_MAX;
-  int none = -1;
-  block_minmax(who, none, redi);
-  if (tid == (who == INT_MAX ? 0 : who)) {
+  __shared__ float kth;
+  if (tid == 0) kth = -INFINITY;
+  rank_top(cand, c, K, [&](int r, uint64_t key) {
+    out[r] = key;
+    if (r == K - 1) kth = packed_val(key);
+  });
+  if (tid == 0) {
     TileStat ts;
-    ts.m = top;
-    ts.amax = topi;
-    ts.s = (nan || top == INFINITY) ? (double)NAN : 0.0;
+    ts.m = kth;
+    ts.amax = c < K ? c : K;
+    ts.s = bad ? (double)NAN : 0.0;
     p.tiles[tile] = ts;
   }
 }
@@ -1038,61 +1132,78 @@ __global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
 
 // ================================================================== top-k
 
-// Merge the S tile lists of one row (each sorted, zero-padded) and publish
-// its kept set in rank order, its normaliser, and -- for the rows an accept
-// test reads -- p'(x) of the drafted token.  The merge ranks every listed
-// entry by binary searches in the other lists (no sort, one barrier).
+// Merge the S tile lists of one row and publish its kept set in rank order,
+// its normaliser, and -- for the rows an accept test reads -- p'(x) of the
+// drafted token.  Only list entries >= the row's largest tile tau can be in
+// its top_k; they are gathered (a few more than top_k in practice) and
+// ranked.  If they would overflow the LDS list, the list is cut back to its
+// top_k every few tiles and the threshold raised.
+static_assert(kCandSlots == kBlock, "one candidate slot per thread in the merge");
+static_assert(kMergeCap % 64 == 0 && kMergeCap >= 2 * kUnroll * kBlock, "merge list size");
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
-  __shared__ uint64_t buf[kMergeCap];
+  __shared__ uint64_t surv[kMergeCap];
   __shared__ uint64_t top[kTopkMax];
+  __shared__ int tcnt[kMaxTiles];
   __shared__ double red[kWaves];
   __shared__ int redi[2 * kWaves];
   __shared__ double sh_mass, sh_px;
+  __shared__ float sh_tau;
+  __shared__ int ns;
   const int grow = blockIdx.x;
   const int tid = threadIdx.x;
   const int K = p.top_k, S = p.S, cw = p.cand_w;
-  const int total = S * cw;                     // <= kMergeCap (host-checked)
-  const uint64_t* src = p.cand + (size_t)grow * total;
+  const uint64_t* src = p.cand + (size_t)grow * S * cw;
   // drafted token read by this row's accept test, if any
   const int nt = p.B * p.rows_t;
   int j = -1, b = 0;
   if (grow < nt) { b = grow / p.rows_t; j = grow - b * p.rows_t; if (j >= p.k) j = -1; }
   else { b = (grow - nt) / p.rows_d; j = (grow - nt) - b * p.rows_d; }
   const int x = (j >= 0) ? p.tokens[(size_t)b * p.k + j] : -1;
+  // tile lengths, taus and probes (wave 0; S <= 64)
   int pr = 0;
-  for (int s = tid; s < S; s += kBlock) { const double ps = p.tiles[(size_t)grow * S + s].s; pr |= (ps != ps); }
-  for (int i0 = 0; i0 < total; i0 += kUnroll * kBlock) {
-    uint64_t r[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) { const int i = i0 + u * kBlock + tid; r[u] = i < total ? src[i] : 0ull; }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) { const int i = i0 + u * kBlock + tid; if (i < total) buf[i] = r[u]; }
+  if (tid < 64) {
+    float tt = -INFINITY;
+    if (tid < S) {
+      const TileStat ts = p.tiles[(size_t)grow * S + tid];
+      tcnt[tid] = ts.amax;
+      tt = ts.m;
+      pr = ts.s != ts.s;
+    }
+    tt = wave_max(tt);
+    if (tid == 0) { sh_tau = tt; ns = 0; }
   }
   if (tid < kTopkMax) top[tid] = 0ull;
   if (tid == 0) sh_px = 0.0;
   const int probe = __syncthreads_or(pr);
-  int cnt = 0;
-  for (int i = tid; i < total; i += kBlock) {
-    const uint64_t key = buf[i];
-    if (key == 0ull) continue;
-    ++cnt;
-    const int a = i / cw, pos = i - a * cw;
-    if (pos >= K) continue;
-    int rank = pos;
-    for (int l = 0; l < S && rank < K; ++l) {
-      if (l == a) continue;
-      const uint64_t* lst = buf + l * cw;
-      int lo = 0, hi = cw;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (lst[mid] > key) lo = mid + 1; else hi = mid;
-      }
-      rank += lo;
+  float tau = sh_tau;
+  for (int t0 = 0; t0 < S; t0 += kUnroll) {
+    uint64_t key[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = t0 + u;
+      key[u] = (t < S && tid < tcnt[t]) ? src[(size_t)t * cw + tid] : 0ull;
     }
-    if (rank < K) top[rank] = key;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const bool take = key[u] != 0ull && packed_val(key[u]) >= tau;
+      const int slot = wave_append(take, &ns);
+      if (take) surv[slot] = key[u];
+    }
+    __syncthreads();
+    if (ns > kMergeCap - kUnroll * kBlock && t0 + kUnroll < S) {
+      // cut the list back to its top_k and raise the threshold
+      const int c = ns;
+      rank_top(surv, c, K, [&](int r, uint64_t k2) { top[r] = k2; });
+      for (int i = tid; i < K; i += kBlock) surv[i] = top[i];
+      if (tid == 0) ns = c < K ? c : K;
+      __syncthreads();
+      if (c >= K) tau = fmaxf(tau, packed_val(surv[K - 1]));
+    }
   }
-  const int tot = block_sum_i(cnt, redi);
+  const int tot = ns;
+  rank_top(surv, tot, K, [&](int r, uint64_t k2) { top[r] = k2; });
   const int n = tot < K ? tot : K;
   const float v0 = n > 0 ? packed_val(top[0]) : -INFINITY;
   const bool bad = probe || (v0 != v0) || (v0 == INFINITY) || (v0 == -INFINITY);
@@ -1439,8 +1550,8 @@ __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
   const int end = min(start + p.L, p.V);
   const int ngroups = (end - start + kVec - 1) / kVec;
   if constexpr (MODE == kModeTopk) {
-    __shared__ uint64_t buf[kTopkCap];
-    tile_topk<T>(p, row, start, end, ngroups, tile, buf);
+    __shared__ uint64_t lds[kTopkLds];
+    tile_topk<T>(p, row, start, end, ngroups, tile, lds);
   } else if constexpr (MODE == kModeStats64) {
     tile_stats64<T>(p, row, start, end, ngroups, tile);
   } else {

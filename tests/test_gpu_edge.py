@@ -108,19 +108,39 @@ def test_identical_rows_accept_everything(top_k, top_p):
     compare_chain(g, orc, range(16), "q == p")
 
 
-@pytest.mark.parametrize("top_p", [1.0, 0.5])
-def test_all_equal_logits(top_p):
-    say("all-equal logits", top_p)
-    B, k, V = 6, 3, 4001
+@pytest.mark.parametrize("top_p,top_k", [(1.0, 0), (0.5, 0), (1.0, 20), (1.0, 256)])
+def test_all_equal_logits(top_p, top_k):
+    """Every logit ties: nucleus and top-k break ties by index; with top-k
+    every group of a tile reaches the admission threshold, which sends the
+    tiles down the exact fallback."""
+    say("all-equal logits", top_p, top_k)
+    B, k, V = 6, 3, 40001
     z = np.zeros((B, k + 1, V))
     rng = np.random.default_rng(1)
     inp = dict(target=z.astype(np.float32), draft=np.zeros((B, k, V), np.float32), dtype="f32",
                u=rng.random((B, k), dtype=np.float32), ur=rng.random(B, dtype=np.float32),
-               draw_u=rng.random((B, k)), T=1.0, top_k=0, top_p=top_p)
+               draw_u=rng.random((B, k)), T=1.0, top_k=top_k, top_p=top_p)
     x = draw_drafts(inp)
     gpu = run_chain(inp, x, SV_MODE_SAMPLE)
     orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
-    compare_chain(gpu, orc, range(B), f"equal logits top-p {top_p}")
+    compare_chain(gpu, orc, range(B), f"equal logits top-p {top_p} top-k {top_k}")
+
+
+def test_topk_ties_bf16():
+    """bf16 logits on a coarse grid: many exact ties around each tile's
+    top-k threshold (large candidate lists)."""
+    say("top-k ties bf16")
+    inp = wl.chain_inputs(3, seed=44, B=4, V=128256, k=3, dtype="bf16")
+    rng = np.random.default_rng(44)
+    t = np.round(rng.normal(0, 2, size=(4, 4, 128256)) * 2) / 2     # multiples of 0.5
+    d = t[:, :3] + np.round(rng.normal(0, 1, size=(4, 3, 128256)) * 2) / 2
+    inp["target"] = wl.bf16_from_f64(t)
+    inp["draft"] = wl.bf16_from_f64(d)
+    inp["top_k"] = 50
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(4)))
+    compare_chain(gpu, orc, range(4), "top-k ties")
 
 
 def test_tiny_vocab():
