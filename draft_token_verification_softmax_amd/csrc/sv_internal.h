@@ -12,7 +12,7 @@ constexpr int kVec = 8;                // logits per group: 16 B of bf16, 32 B o
 constexpr int kTopkCap = 2560;         // LDS candidate slots of the top-k tile kernel
 constexpr int kMergeCap = 4096;        // LDS slots when merging a row's top-k candidates
 constexpr int kCandSlots = 256;        // per-tile top-k candidate slots in the workspace
-constexpr int kWindowCap = 2048;       // LDS slots for the nucleus boundary window
+constexpr int kWindowCap = 1024;       // LDS slots for the nucleus boundary window
 constexpr int kNucBins = 2048;         // histogram bins of the nucleus search
 constexpr int kResidSeg = kBlock * kVec;  // logits per workgroup in the residual kernels
 constexpr int kMaxTiles = 64;          // tiles per row (one wave combines a row's partials)

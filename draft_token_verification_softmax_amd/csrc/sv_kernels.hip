@@ -132,19 +132,19 @@ DEV int load_group(const T* row, int pos, int end, int aligned, float v[kVec]) {
 // last group of a row whose length is not a multiple of kVec (or a row that
 // is not 16-byte aligned) takes the element path.  NaN evidence goes to
 // `probe` (vector path) or `nanv` (element path).
-template <typename T>
+template <typename T, int U = kUnroll>
 DEV void load_iter(const T* row, int start, int end, int ngroups, int nfull, int aligned, int g0,
-                   float v[kUnroll][kVec], int nv[kUnroll], uint32_t& probe, bool& nanv) {
+                   float v[U][kVec], int nv[U], uint32_t& probe, bool& nanv) {
   const bool partial = nfull != ngroups;
-  if (aligned && nfull > 0 && __all(!partial || g0 + (kUnroll - 1) * kBlock < nfull)) {
-    Group<T> gr[kUnroll];
+  if (aligned && nfull > 0 && __all(!partial || g0 + (U - 1) * kBlock < nfull)) {
+    Group<T> gr[U];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int g = g0 + u * kBlock;
       gr[u].load(row + start + (g < nfull ? g : nfull - 1) * kVec);
     }
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       gr[u].values(v[u]);
       gr[u].probe(probe);
       nv[u] = kVec;
@@ -156,7 +156,7 @@ DEV void load_iter(const T* row, int start, int end, int ngroups, int nfull, int
     }
   } else {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int g = g0 + u * kBlock;
       if (g < ngroups) {
         nv[u] = load_group<T>(row, start + g * kVec, end, aligned, v[u]);
@@ -1561,33 +1561,52 @@ __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
 
 // ================================================================== nucleus
 //
-// Exact nucleus cut of one row.  The rank order is (logit desc, index asc),
-// i.e. the packed u64 of pack() in descending order; e_v = exp(z_v - zmax)
-// with z = l / T; the kept set is the shortest rank prefix whose mass reaches
-// top_p * Z.  Search: histogram the row by d = zmax - z (level 0) or, inside
-// a window, by the packed key (deeper levels); locate the boundary bin from
-// exact-integer fixed-point masses; take a 3-bin window; if it holds at most
-// kWindowCap entries, gather them, sort, and walk with float64 prefix sums
-// starting from the exact mass of everything ranked above the window.
-// Otherwise the window becomes the next level's range.  Packed keys are
-// distinct, so the levels always narrow down (at most ~7).  No logit with
-// d >= dmax = ln(V / (1 - top_p)) + 1 can be kept (every kept entry has
-// probability > (1 - top_p) / V), so those are skipped.
+// Exact nucleus cut of one row.  Rank order is (logit desc, index asc), i.e.
+// the packed u64 of pack() in descending order; e_v = exp(z_v - zmax) with
+// z = l / T; the kept set is the shortest rank prefix whose mass reaches
+// top_p * Z.
+//
+// Bins: d = fmaf(l, -1/T, zmax) in float32 is non-increasing in l, and so is
+// the level-0 bin floor(d / w0) over [0, dmax); deeper levels split a
+// window of level-0 bins by the packed key.  Bin order is therefore rank
+// order, and everything in bins before a window ranks above every entry of
+// the window.  No logit with d >= dmax = ln(V / ((1 - top_p) Z)) + 1 can be
+// kept (every kept entry has probability > (1 - top_p) / V).
+//
+// Pass 1 (histogram) adds, per bin, the count and the mass of its entries as
+// exact integers: e relative to the bin's reference, exp(-delta) with
+// delta = d - (reference bin) w0 <= 3 w0, from its Taylor series to degree 9
+// in float64 (remainder below 1e-16 for every w0 this search can have), and
+// rounded to fixed point with fx fraction bits (fx leaves room for V
+// entries).  The LDS atomics cannot change such sums, and the mass above any
+// window is float64-accurate.  The bin where the cumulative mass
+// reaches top_p * Z and its two neighbours form the window; pass 2 gathers
+// the window's entries (no arithmetic beyond the bin), they are sorted, and
+// a float64 walk from the mass above the window finds the cut.  A window
+// with more than kWindowCap entries becomes the range of the next level.
+
+constexpr int kNucUnroll = 4;   // groups per lane in flight in the row passes
 
 struct NucState {
-  double zm, invT, dmax, w0, invw0;
+  float zm32, nit32;         // d = fmaf(l, nit32, zm32), nit32 = -1 / T
+  float dmax, invw0;         // d >= dmax never kept; level-0 bin = d * invw0
+  double w0;                 // level-0 bin width (in d)
+  double zm, invT;           // float64 d = zm - l * invT
+  double fx, ifx;            // fixed-point scale 2^fx and its inverse
+  double above;              // exact mass ranked above the current level's range
   int level;                 // 0: bins by d; >= 1: bins by packed key
   int p0lo, p0hi;            // level-0 window (bins), used at levels >= 1
   uint64_t plo, phi;         // packed range of the current level (>= 1)
-  int sh;                    // bin = (phi - pk) >> sh
+  int sh;                    // level >= 1: bin = (phi - pk) >> sh
   int c0, c1;                // current window, in bins of the current level
 };
 
 // Where one logit stands relative to the current level and window.
 //   cls: -1 ranked above the window, 0 in the window, 1 below it, 2 never kept
 //   *bin: its bin at the current level when it lies in the level's range, else -1
-DEV int nuc_class(const NucState& s, float l, int idx, double d, int* bin) {
+DEV int nuc_class(const NucState& s, float l, int idx, int* bin) {
   *bin = -1;
+  const float d = fmaf(l, s.nit32, s.zm32);
   if (!(d < s.dmax)) return 2;
   int b0 = (int)(d * s.invw0);
   b0 = b0 < 0 ? 0 : (b0 >= kNucBins ? kNucBins - 1 : b0);
@@ -1605,143 +1624,202 @@ DEV int nuc_class(const NucState& s, float l, int idx, double d, int* bin) {
   return b < s.c0 ? -1 : (b > s.c1 ? 1 : 0);
 }
 
-// Reference factor of a bin's fixed-point masses: an upper bound of e in it.
-DEV double nuc_bin_ref(const NucState& s, int b) {
-  if (s.level == 0) return exp(-(double)b * s.w0);
-  return exp(-(double)s.p0lo * s.w0);
+// d of a bin's reference: level 0 b w0, deeper levels p0lo w0 (every bin
+// of a level lies inside that level-0 window).  Its mass unit is exp(-ref).
+DEV double nuc_ref(const NucState& s, int b) {
+  return (double)(s.level == 0 ? b : s.p0lo) * s.w0;
 }
 
-// Histogram sweep at the current level (the window fields are ignored).
-// hq: sum of e / ref(bin) in 2^-32 units (exact integers, so the order of the
-// LDS atomics cannot change them; float32 exponentials suffice because these
-// masses only locate the boundary); hc: counts.  *A gets the exact float64
-// mass of everything ranked above the level's range, *below the count ranked
-// below it (and still < dmax).
+// exp(x) for -0.1 <= x <= 0 (and slightly above 0) to float64 accuracy:
+// Taylor series to degree 9.
+DEV double exp_small(double x) {
+  double q = fma(x, 2.7557319223985893e-06, 2.48015873015873e-05);
+  q = fma(q, x, 0.0001984126984126984);
+  q = fma(q, x, 0.001388888888888889);
+  q = fma(q, x, 0.008333333333333333);
+  q = fma(q, x, 0.041666666666666664);
+  q = fma(q, x, 0.16666666666666666);
+  q = fma(q, x, 0.5);
+  q = fma(q, x, 1.0);
+  return fma(q, x, 1.0);
+}
+
+// round(y) as an integer for 0 <= y < 2^52 (the addition rounds).
+DEV unsigned long long to_fixed(double y) {
+  const double t = y + 4503599627370496.0;   // 2^52
+  return (unsigned long long)__double_as_longlong(t) - 0x4330000000000000ull;
+}
+
+// Pass 1 at the current level (window fields ignored): hq = fixed-point mass
+// relative to the bin reference, hc = count.
 template <typename T>
 DEV void nuc_hist(const T* row, int V, int aligned, NucState s, unsigned long long* hq,
-                  unsigned int* hc, unsigned int* below, double* red, int* redi, double* A) {
+                  unsigned int* hc) {
   for (int b = threadIdx.x; b < kNucBins; b += kBlock) { hq[b] = 0ull; hc[b] = 0u; }
   __syncthreads();
-  s.c0 = 0; s.c1 = kNucBins - 1;   // whole level = "window"
-  const double ref1 = (double)s.p0lo * s.w0;
-  double a = 0.0;
-  unsigned int nb = 0;
-  for (int g = threadIdx.x; g * kVec < V; g += kBlock) {
-   float vv[kVec];
-   const int ng = load_group<T>(row, g * kVec, V, aligned, vv);
-   for (int e = 0; e < ng; ++e) {
-    const int i = g * kVec + e;
-    const float l = vv[e];
-    const double d = s.zm - (double)l * s.invT;
-    if (!(d < s.dmax)) continue;
-    int bin;
-    const int cls = nuc_class(s, l, i, d, &bin);
-    if (cls == -1) a += exp(-d);
-    else if (cls == 1) nb++;
-    else if (cls == 0) {
-      const double refd = s.level == 0 ? (double)bin * s.w0 : ref1;
-      const float rel = __expf((float)(refd - d));   // in (e^-w, 1]
-      atomicAdd(&hq[bin], (unsigned long long)(rel * 4294967296.0f));
-      atomicAdd(&hc[bin], 1u);
+  const int ngroups = (V + kVec - 1) / kVec, nfull = V / kVec;
+  uint32_t probe = 0;
+  bool nanv = false;
+  for (int base = 0; base < ngroups; base += kNucUnroll * kBlock) {
+    float v[kNucUnroll][kVec];
+    int nv[kNucUnroll];
+    load_iter<T, kNucUnroll>(row, 0, V, ngroups, nfull, aligned, base + threadIdx.x, v, nv, probe, nanv);
+#pragma unroll
+    for (int u = 0; u < kNucUnroll; ++u) {
+      const int i0 = (base + threadIdx.x + u * kBlock) * kVec;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        if (e >= nv[u]) continue;
+        const float l = v[u][e];
+        int bin;
+        const int cls = nuc_class(s, l, i0 + e, &bin);
+        if (bin >= 0 && cls != 2) {
+          const double d = fma(-(double)l, s.invT, s.zm);
+          atomicAdd(&hq[bin], to_fixed(exp_small(nuc_ref(s, bin) - d) * s.fx));
+          atomicAdd(&hc[bin], 1u);
+        }
+      }
     }
-   }
   }
-  const int nbt = block_sum_i((int)nb, redi);
-  if (threadIdx.x == 0) *below = (unsigned)nbt;
-  *A = block_sum(a, red);
   __syncthreads();
 }
 
-// First bin whose cumulative approximate mass (from A) reaches tgt.
-DEV int nuc_locate(const NucState& s, const unsigned long long* hq, double A, double tgt,
-                   double* red, int* redi) {
-  double local[kNucBins / kBlock];
+// Bin masses of the current level in float64, exclusive prefix over bins in
+// bin order (fixed order), and the first bin whose cumulative mass (from
+// s.above) reaches tgt (kNucBins - 1 if none).  *pre gets, for the window's
+// first bin c0 (after the caller sets it), nothing: callers use nuc_prefix.
+DEV int nuc_locate(const NucState& s, const unsigned long long* hq, double tgt, double* red,
+                   int* redi) {
+  constexpr int per = kNucBins / kBlock;
+  double local[per];
   double tsum = 0.0;
 #pragma unroll
-  for (int q = 0; q < kNucBins / kBlock; ++q) {
-    const int b = threadIdx.x * (kNucBins / kBlock) + q;
-    local[q] = hq[b] ? (double)hq[b] * (1.0 / 4294967296.0) * nuc_bin_ref(s, b) : 0.0;
+  for (int q = 0; q < per; ++q) {
+    const int b = threadIdx.x * per + q;
+    local[q] = hq[b] ? (double)hq[b] * s.ifx * exp(-nuc_ref(s, b)) : 0.0;
     tsum += local[q];
   }
   double tot;
   const double ex = block_exscan(tsum, red, &tot);
-  double c = A + ex;
+  double c = s.above + ex;
   int found = INT_MAX;
 #pragma unroll
-  for (int q = 0; q < kNucBins / kBlock; ++q) {
+  for (int q = 0; q < per; ++q) {
     c += local[q];
-    if (found == INT_MAX && c >= tgt) found = threadIdx.x * (kNucBins / kBlock) + q;
+    if (found == INT_MAX && c >= tgt) found = threadIdx.x * per + q;
   }
   int none = -1;
   block_minmax(found, none, redi);
   return found != INT_MAX ? found : kNucBins - 1;
 }
 
+// Exact mass of the bins before bin c0 at the current level (same order and
+// rounding as nuc_locate) plus s.above.
+DEV double nuc_prefix(const NucState& s, const unsigned long long* hq, int c0, double* red) {
+  constexpr int per = kNucBins / kBlock;
+  double tsum = 0.0;
+#pragma unroll
+  for (int q = 0; q < per; ++q) {
+    const int b = threadIdx.x * per + q;
+    if (b < c0 && hq[b]) tsum += (double)hq[b] * s.ifx * exp(-nuc_ref(s, b));
+  }
+  return s.above + block_sum(tsum, red);
+}
+
+// Count of the current level's entries in bins [lo, hi] (exact).
+DEV unsigned long long nuc_count(const unsigned int* hc, int lo, int hi, unsigned long long* redu) {
+  unsigned long long c = 0;
+  for (int b = threadIdx.x; b < kNucBins; b += kBlock) if (b >= lo && b <= hi) c += hc[b];
+  unsigned long long t;
+  block_exscan_u64(c, redu, &t);
+  return t;
+}
+
 // Exact nucleus cut of one valid row (see above); fills *out.
 template <typename T>
 DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc* outp,
                      unsigned long long* hq, unsigned int* hc, uint64_t* win, double* red,
-                     unsigned long long* redu, int* redi, unsigned int* below_p, int* wcnt_p) {
-  unsigned int& below = *below_p;
+                     unsigned long long* redu, int* redi, int* wcnt_p) {
   int& wcnt = *wcnt_p;
   RowNuc& out = *outp;
   const int V = p.V;
   const int tid = threadIdx.x;
+  const double invT = 1.0 / p.T;
   NucState s;
-  s.invT = 1.0 / p.T;
-  s.zm = (double)Mrow * s.invT;
+  s.zm32 = (float)((double)Mrow * invT);
+  s.nit32 = (float)(-invT);
   // every kept entry has probability > (1 - top_p) / V, i.e. d < ln(V / ((1 - top_p) Z))
-  s.dmax = log((double)V / ((1.0 - p.top_p) * Z)) + 1.0;
-  if (!(s.dmax > 1.0)) s.dmax = 1.0;
-  s.w0 = s.dmax / kNucBins;
-  s.invw0 = 1.0 / s.w0;
+  double dmax = log((double)V / ((1.0 - p.top_p) * Z)) + 1.0;
+  if (!(dmax > 1.0)) dmax = 1.0;
+  s.dmax = (float)dmax;
+  s.w0 = dmax / kNucBins;
+  s.invw0 = (float)(1.0 / s.w0);
+  s.zm = (double)Mrow * invT;
+  s.invT = invT;
+  int vbits = 0;
+  while ((1 << vbits) < V + 1) ++vbits;
+  s.fx = ldexp(1.0, min(61 - vbits, 50));   // sums < 2^62, one entry < 2^51
+  s.ifx = 1.0 / s.fx;
+  s.above = 0.0;
   s.level = 0; s.p0lo = 0; s.p0hi = kNucBins - 1; s.plo = 0; s.phi = ~0ull; s.sh = 0;
   s.c0 = 0; s.c1 = kNucBins - 1;
 
-  double A = 0.0;
-  nuc_hist<T>(row, V, p.aligned, s, hq, hc, &below, red, redi, &A);
+  nuc_hist<T>(row, V, p.aligned, s, hq, hc);
   const double tgt = p.top_p * Z;
+  const double zm = (double)Mrow * invT;
   bool located = false;
   int result = 0;   // 1 found, -1 failed
   for (int iter = 0; iter < 64 && result == 0; ++iter) {
     if (!located) {
-      const int b = nuc_locate(s, hq, A, tgt, red, redi);
+      const int b = nuc_locate(s, hq, tgt, red, redi);
       s.c0 = b > 0 ? b - 1 : 0;
       s.c1 = b < kNucBins - 1 ? b + 1 : kNucBins - 1;
       located = true;
     }
-    // window and below-window counts at this level
-    unsigned long long cw = 0, cb = 0;
-    for (int b = tid; b < kNucBins; b += kBlock) {
-      if (b >= s.c0 && b <= s.c1) cw += hc[b];
-      else if (b > s.c1) cb += hc[b];
-    }
-    unsigned long long tw, tb;
-    block_exscan_u64(cw, redu, &tw);
-    block_exscan_u64(cb, redu, &tb);
-    tb += below;
+    const unsigned long long tw = nuc_count(hc, s.c0, s.c1, redu);
+    const unsigned long long tb = nuc_count(hc, s.c1 + 1, kNucBins - 1, redu);
+    const double Aw = nuc_prefix(s, hq, s.c0, red);   // exact mass ranked above the window
 
     if (tw <= (unsigned long long)kWindowCap) {
-      // gather the window; exact mass ranked above it
+      // pass 2: gather the window
       if (tid == 0) wcnt = 0;
       __syncthreads();
-      double a = 0.0;
-      for (int g = tid; g * kVec < V; g += kBlock) {
-        float vv[kVec];
-        const int ng = load_group<T>(row, g * kVec, V, p.aligned, vv);
+      const int ngroups = (V + kVec - 1) / kVec, nfull = V / kVec;
+      uint32_t probe = 0;
+      bool nanv = false;
+      for (int base = 0; base < ngroups; base += kNucUnroll * kBlock) {
+        float v[kNucUnroll][kVec];
+        int nv[kNucUnroll];
+        load_iter<T, kNucUnroll>(row, 0, V, ngroups, nfull, p.aligned, base + tid, v, nv, probe, nanv);
+        unsigned msk[kNucUnroll];
+        int cnt = 0;
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-          const int i = g * kVec + e;
-          const float l = vv[e];
-          const double d = s.zm - (double)l * s.invT;
-          int cls = 2, bin;
-          if (e < ng && d < s.dmax) cls = nuc_class(s, l, i, d, &bin);
-          if (cls == -1) a += exp(-d);
-          const int slot = wave_append(cls == 0, &wcnt);
-          if (slot >= 0 && slot < kWindowCap) win[slot] = pack(l, i);
+        for (int u = 0; u < kNucUnroll; ++u) {
+          msk[u] = 0u;
+          const int i0 = (base + tid + u * kBlock) * kVec;
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            int bin;
+            if (e < nv[u] && nuc_class(s, v[u][e], i0 + e, &bin) == 0) msk[u] |= 1u << e;
+          }
+          cnt += __popc(msk[u]);
+        }
+        if (__any(cnt > 0)) {
+          int slot = wave_reserve(cnt, &wcnt);
+#pragma unroll
+          for (int u = 0; u < kNucUnroll; ++u) {
+            const int i0 = (base + tid + u * kBlock) * kVec;
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+              if ((msk[u] >> e) & 1u) {
+                if (slot < kWindowCap) win[slot] = pack(v[u][e], i0 + e);
+                ++slot;
+              }
+            }
+          }
         }
       }
-      const double Aw = block_sum(a, red);
+      __syncthreads();
       const int n = min(wcnt, kWindowCap);
       const int P = next_pow2(n);
       for (int i = n + tid; i < P; i += kBlock) win[i] = 0ull;
@@ -1751,7 +1829,7 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
       double tl = 0.0;
       for (int q = 0; q < per; ++q) {
         const int i = tid * per + q;
-        if (i < n) tl += exp((double)packed_val(win[i]) * s.invT - s.zm);
+        if (i < n) tl += exp((double)packed_val(win[i]) * invT - zm);
       }
       double tot;
       const double ex = block_exscan(tl, red, &tot);
@@ -1761,7 +1839,7 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
       for (int q = 0; q < per; ++q) {
         const int i = tid * per + q;
         if (i < n) {
-          const double e = exp((double)packed_val(win[i]) * s.invT - s.zm);
+          const double e = exp((double)packed_val(win[i]) * invT - zm);
           if (c < tgt) { kept_local = i + 1; mass_local = c + e; }
           c += e;
         }
@@ -1775,11 +1853,7 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
         if (s.c1 == kNucBins - 1) result = -1;          // cut below this level's range
         else { s.c0 = s.c1 + 1; s.c1 = s.c1 + 3 < kNucBins ? s.c1 + 3 : kNucBins - 1; }
       } else {
-        if (tid == (kept - 1) / per) {                  // owner of the last kept entry
-          out.N = mass_local;
-          out.cut = win[kept - 1];
-          red[0] = mass_local;
-        }
+        if (tid == (kept - 1) / per) red[0] = mass_local;   // owner of the last kept entry
         __syncthreads();
         out.N = red[0];
         out.cut = win[kept - 1];
@@ -1794,17 +1868,16 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
         const int ng = load_group<T>(row, g * kVec, V, p.aligned, vv);
         for (int e = 0; e < ng; ++e) {
           const int i = g * kVec + e;
-          const float l = vv[e];
-          const double d = s.zm - (double)l * s.invT;
           int bin;
-          if (nuc_class(s, l, i, d, &bin) == 0) {
-            const unsigned long long pk = pack(l, i);
+          if (nuc_class(s, vv[e], i, &bin) == 0) {
+            const unsigned long long pk = pack(vv[e], i);
             pmin = pk < pmin ? pk : pmin;
             pmax = pk > pmax ? pk : pmax;
           }
         }
       }
       block_minmax(pmin, pmax, redu);
+      s.above = Aw;
       if (s.level == 0) { s.p0lo = s.c0; s.p0hi = s.c1; }
       s.plo = pmin;
       s.phi = pmax;
@@ -1812,13 +1885,12 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
       int bits = span ? 64 - __clzll((long long)span) : 0;
       s.sh = bits > 11 ? bits - 11 : 0;
       s.level += 1;
-      nuc_hist<T>(row, V, p.aligned, s, hq, hc, &below, red, redi, &A);
+      nuc_hist<T>(row, V, p.aligned, s, hq, hc);
       located = false;
     }
   }
   out.ok = result == 1 ? 1 : 2;
 }
-
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
@@ -1831,7 +1903,6 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   __shared__ double red[kWaves];
   __shared__ unsigned long long redu[2 * kWaves];
   __shared__ int redi[2 * kWaves];
-  __shared__ unsigned int below;
   __shared__ int wcnt;
   __shared__ float sh_M;
   __shared__ double sh_Z;
@@ -1844,7 +1915,7 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   RowNuc out;
   out.Z = sh_Z; out.N = 0.0; out.cut = 0ull; out.ok = 0; out.M = sh_M;
   if (!sh_bad)
-    topp_search<T>(p, row, out.M, out.Z, &out, hq, hc, win, red, redu, redi, &below, &wcnt);
+    topp_search<T>(p, row, out.M, out.Z, &out, hq, hc, win, red, redu, redi, &wcnt);
   if (threadIdx.x == 0) p.nuc[grow] = out;
 }
 
