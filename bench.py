@@ -101,6 +101,40 @@ class HipEvents:
             self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+# ------------------------------------------------------------------ measured HBM traffic
+
+KERNEL_SOURCES = [os.path.join(ROOT, "draft_token_verification_softmax_amd", "csrc", f)
+                  for f in ("sv_kernels.hip", "sv_internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stream_traffic.md")
+
+
+def kernel_digest():
+    """sha256 of the kernel sources (the traffic counters are only valid for them)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """HBM bytes per launch of the streaming kernel for a workload, from the
+    committed FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
+    kernel sources; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    digest = kernel_digest()
+    with open(TRAFFIC_FILE) as fh:
+        for line in fh:
+            if not line.startswith("traffic:"):
+                continue
+            kv = dict(tok.split("=", 1) for tok in line.split()[1:])
+            if kv.get("workload") == str(config) and kv.get("sources") == digest:
+                return int(kv["bytes_per_launch"])
+    return None
+
+
 # ------------------------------------------------------------------ CPU baseline (oracle)
 
 def cpu_baseline(config, budget_s=12.0):
@@ -159,6 +193,7 @@ def main():
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device three times (scale reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--digest", action="store_true", help="print the kernel-source digest and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -169,6 +204,9 @@ def main():
     import draft_token_verification_softmax_amd as svm
     from draft_token_verification_softmax_amd import workloads as wl
 
+    if args.digest:
+        print(kernel_digest())
+        return
     if args.copy_calibrate:
         n = args.copy_calibrate * (1 << 20) // 4
         src = torch.ones(n, device="cuda:0")
@@ -278,7 +316,7 @@ def main():
         "config": dict(workload=workload, rows_per_call=rows_per_call,
                        logit_bytes_per_call=logit_bytes, input_copies=ncopies, **extra),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": None,
+                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.config),
                      "kernel": "k_stream (the pass that reads every logit)", "kernel_us": kern_ms * 1e3,
                      "call_us_events": call_ms * 1e3,
                      "call_bytes_algorithmic": alg_bytes,
