@@ -10,7 +10,9 @@
 
 namespace {
 
-constexpr int kMinTile = 8192;        // logits per tile, lower bound (4 groups per lane)
+constexpr int kMinTile = 8192;        // top-k pass: logits per tile, lower bound
+constexpr int kRound = 4 * sv::kBlock * sv::kVec;   // argmax / sum passes: logits per round of loads
+constexpr int kMinSmall = 2048;       // argmax / sum passes: smallest tile of small problems
 
 struct Plan {
   int filt;        // sv::Filter
@@ -18,7 +20,7 @@ struct Plan {
   int top_k;       // effective top-k (0 = off)
   double top_p;    // effective top-p (1 = off)
   int rows_t, rows_d, out_w;
-  int S_max;       // largest tile count per row the workspace holds
+  int S_max;       // largest top-k tile count per row (candidate list workspace)
   int S2_max;      // residual segments per sequence (plain sampling)
   int cand_w;
 };
@@ -55,6 +57,7 @@ Plan make_plan(const sv_config* c) {
   else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats64; }
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
+  // top-k tiles hold at least kMinTile logits (the candidate lists are sized by it)
   p.S_max = (c->vocab + kMinTile - 1) / kMinTile;
   if (p.S_max > sv::kMaxTiles) p.S_max = sv::kMaxTiles;
   p.cand_w = p.top_k > 0 ? sv::kCandSlots : 0;
@@ -79,7 +82,7 @@ Layout layout(const sv_config* c, const Plan& pl) {
     off = (off + bytes + 255) & ~(size_t)255;
     return at;
   };
-  L.tiles = take(rows * (size_t)pl.S_max * sizeof(sv::TileStat));
+  L.tiles = take(rows * (size_t)sv::kMaxPartials * sizeof(sv::TileStat));
   L.cand = take(pl.top_k > 0 ? rows * (size_t)pl.S_max * (size_t)pl.cand_w * sizeof(uint64_t) : 0);
   L.nuc = take(pl.filt == sv::kFiltTopp ? rows * sizeof(sv::RowNuc) : 0);
   const bool sampled = pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp;
@@ -106,6 +109,7 @@ struct specverify_ctx {
   size_t ws_bytes;
   Layout L;
   int grid;                      // resident workgroups of the streaming kernel
+  int cus;                       // compute units of the device
   hipEvent_t ev_begin, ev_end;   // optional instrumentation (caller-owned)
 };
 
@@ -176,6 +180,7 @@ int specverify_create(const sv_config* cfg, int device, specverify_ctx** out) {
   if (hipGetDeviceProperties(&prop, device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
   const int per_cu = sv::stream_blocks_per_cu(ctx->plan.tile_mode, cfg->dtype == SV_DTYPE_BF16);
   ctx->grid = prop.multiProcessorCount * (per_cu > 0 ? per_cu : 1);
+  ctx->cus = prop.multiProcessorCount;
   if (hipMalloc(&ctx->ws, L.total) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
   *out = ctx;
   return SV_OK;
@@ -237,15 +242,34 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.T = c->mode == SV_MODE_SAMPLE ? c->temperature : 1.0;
   p.top_p = pl.top_p;
   p.top_k = pl.top_k;
-  // tiling: about four tiles per resident workgroup of the streaming kernel
-  // (a short last wave), tiles of at least kMinTile logits
+  // tiling of the streaming pass
   const long rows = (long)batch * (pl.rows_t + pl.rows_d);
-  long S = (4L * ctx->grid + rows - 1) / rows;
-  if (S > pl.S_max) S = pl.S_max;
+  long S;
+  if (pl.tile_mode == sv::kModeTopk) {
+    // about four tiles per resident workgroup, tiles of at least kMinTile logits
+    S = (4L * ctx->grid + rows - 1) / rows;
+    const long smax = (c->vocab + kMinTile - 1) / kMinTile;
+    if (S > smax) S = smax;
+  } else {
+    // one round of loads per lane (kRound logits; 16 KB of bf16, 32 KB of
+    // fp32); rows that need more than kMaxTiles such tiles take several
+    // rounds per tile; problems with fewer tiles than CUs take smaller tiles
+    // (down to kMinSmall logits)
+    S = (c->vocab + kRound - 1) / kRound;
+    if (rows * S < ctx->cus) {
+      long want = (ctx->cus + rows - 1) / rows;
+      const long cap = (c->vocab + kMinSmall - 1) / kMinSmall;
+      if (want > cap) want = cap;
+      if (want > S) S = want;
+    }
+  }
+  if (S > sv::kMaxTiles) S = sv::kMaxTiles;
   if (S < 1) S = 1;
-  const int per = (int)((c->vocab + S - 1) / S);
+  int per = (int)((c->vocab + S - 1) / S);
+  if (pl.tile_mode != sv::kModeTopk && per > kRound) per = (per + kRound - 1) / kRound * kRound;
   p.L = (per + sv::kVec - 1) / sv::kVec * sv::kVec;
   p.S = (c->vocab + p.L - 1) / p.L;
+  p.P = pl.tile_mode == sv::kModeTopk ? p.S : p.S * (sv::kBlock / 64);
   const size_t es = c->dtype == SV_DTYPE_BF16 ? 2 : 4;
   const bool rows16 = ((size_t)c->vocab * es) % 16 == 0;
   const bool base16 = ((uintptr_t)target_logits % 16 == 0) &&

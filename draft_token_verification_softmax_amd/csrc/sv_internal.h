@@ -15,13 +15,15 @@ constexpr int kCandSlots = 256;        // per-tile top-k candidate slots in the 
 constexpr int kWindowCap = 1024;       // LDS slots for the nucleus boundary window
 constexpr int kNucBins = 2048;         // histogram bins of the nucleus search
 constexpr int kResidSeg = kBlock * kVec;  // logits per workgroup in the residual kernels
-constexpr int kMaxTiles = 64;          // tiles per row (one wave combines a row's partials)
+constexpr int kMaxTiles = 64;          // tiles per row
+constexpr int kMaxPartials = 256;      // partials per row (one wave combines a row's partials)
 
-// Per-tile partial result of the streaming pass.
-//   m    max raw logit of the tile (NaN ignored; -inf if none)
+// Partial result of the streaming pass over a part of a row: the logits one
+// wave of a tile read (argmax and sum passes), or a whole tile (top-k pass).
+//   m    max raw logit of the part (NaN ignored; -inf if none)
 //   amax lowest index holding m (INT32_MAX if none)
-//   s    NaN iff the tile holds a NaN or +inf (exact, every mode); otherwise
-//        STATS mode: float64 sum over the tile of exp((l - m) / T), other
+//   s    NaN iff the part holds a NaN or +inf (exact, every mode); otherwise
+//        STATS mode: float64 sum over the part of exp((l - m) / T), other
 //        modes: 0
 // TOPK mode instead: m = the tile's top_k-th logit (-inf if it has fewer),
 // amax = the length of its list (its top_k in rank order, in p.cand).
@@ -87,12 +89,14 @@ struct Params {
   double top_p;
   int top_k;    // 0 = off
   // tiling of the streaming pass
-  int S;        // tiles per row
+  int S;        // tiles (workgroups of the streaming pass) per row
   int L;        // logits per tile (multiple of kVec)
+  int P;        // partials per row in `tiles`: S * kWaves (one per wave) for
+                // the argmax and sum passes, S for the top-k pass
   int aligned;  // every row starts 16-byte aligned
   int grid;     // workgroups of the streaming launch (resident capacity)
   // workspace
-  TileStat* tiles;   // [rows][S]
+  TileStat* tiles;   // [rows][P]
   uint64_t* cand;    // [rows][S][cand_w] (top-k): each tile's candidate list
   int cand_w;        // candidate slots per tile
   RowNuc* nuc;       // [rows] (top-p)

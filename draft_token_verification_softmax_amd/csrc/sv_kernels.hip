@@ -66,10 +66,23 @@ template <> struct Io<uint16_t> {
 // probe() keeps, in one register, enough to tell exactly whether any logit
 // seen was a NaN: the largest magnitude bit pattern (per 16-bit half for
 // bf16); a NaN is the only pattern above the one of infinity.
+// Buffer loads: word 3 of a gfx9 buffer resource (raw, 32-bit data format),
+// and the cache-policy bit for non-temporal (single-use) loads.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kNT = 2;
+DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
 template <typename T> struct Group;
 template <> struct Group<uint16_t> {
   vu4 w;
   DEV void load(const uint16_t* p) { w = __builtin_nontemporal_load(reinterpret_cast<const vu4*>(p)); }
+  // group at byte offset voff + soff of a buffer resource (non-temporal)
+  DEV void load_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    w = __builtin_bit_cast(vu4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT));
+  }
+  static constexpr int kBytes = 16;
   DEV void values(float v[kVec]) const {
     v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
     v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
@@ -85,6 +98,17 @@ template <> struct Group<uint16_t> {
     acc = __builtin_bit_cast(uint32_t, a);
   }
   static DEV bool has_nan(uint32_t acc) { return (acc & 0xffffu) > 0x7f80u || (acc >> 16) > 0x7f80u; }
+  // the n < kVec logits at p, the rest -inf (bf16 pattern 0xff80)
+  DEV void load_part(const uint16_t* p, int n) {
+    uint32_t h[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) h[e] = e < n ? (uint32_t)p[e] : 0xff80u;
+    w.x = h[0] | (h[1] << 16); w.y = h[2] | (h[3] << 16);
+    w.z = h[4] | (h[5] << 16); w.w = h[6] | (h[7] << 16);
+  }
+  DEV void select(bool c, const Group& o) {
+    w.x = c ? o.w.x : w.x; w.y = c ? o.w.y : w.y; w.z = c ? o.w.z : w.z; w.w = c ? o.w.w : w.w;
+  }
 };
 template <> struct Group<float> {
   vf4 a, b;
@@ -93,6 +117,11 @@ template <> struct Group<float> {
     a = __builtin_nontemporal_load(q);
     b = __builtin_nontemporal_load(q + 1);
   }
+  DEV void load_buf(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    a = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT));
+    b = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, kNT));
+  }
+  static constexpr int kBytes = 32;
   DEV void values(float v[kVec]) const {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
@@ -106,6 +135,17 @@ template <> struct Group<float> {
     acc = max(acc, max(max(x0, x1), max(x2, x3)));
   }
   static DEV bool has_nan(uint32_t acc) { return acc > 0x7f800000u; }
+  DEV void load_part(const float* p, int n) {
+    float h[kVec];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) h[e] = e < n ? p[e] : -INFINITY;
+    a = vf4{h[0], h[1], h[2], h[3]};
+    b = vf4{h[4], h[5], h[6], h[7]};
+  }
+  DEV void select(bool c, const Group& o) {
+    a.x = c ? o.a.x : a.x; a.y = c ? o.a.y : a.y; a.z = c ? o.a.z : a.z; a.w = c ? o.a.w : a.w;
+    b.x = c ? o.b.x : b.x; b.y = c ? o.b.y : b.y; b.z = c ? o.b.z : b.z; b.w = c ? o.b.w : b.w;
+  }
 };
 
 // Load the group of kVec logits starting at `pos` (< end).  Slots past `end`
@@ -171,6 +211,43 @@ DEV void load_iter(const T* row, int start, int end, int ngroups, int nfull, int
   }
 }
 
+// One pass over the groups of a tile [start, end).  Tiles of whole groups
+// in 16-byte aligned rows are read through a buffer resource spanning
+// exactly the tile, U groups of kVec logits per lane in flight; a slot past
+// the tile reads zeros without touching memory, so no address is clamped and
+// nothing outside the tile is fetched.  The groups stay as loaded (raw
+// words) until the consumer unpacks them one at a time, which keeps the
+// register count -- and so the number of resident waves -- low.
+// f(groups, first index, n valid) gets the lane's U group slots (slot u
+// holds group first + u * kBlock and is valid iff u < n valid).  Other tiles
+// assemble one group per lane at a time element by element, padded with
+// -inf (f gets U = 1).
+template <typename T, int U, typename F>
+DEV void tile_groups(const T* row, int start, int end, int aligned, F&& f) {
+  const int ngroups = (end - start + kVec - 1) / kVec;
+  const int nfull = (end - start) / kVec;
+  if (aligned && nfull == ngroups && nfull > 0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, (end - start) * (int)sizeof(T));
+    for (int g0 = threadIdx.x; g0 < ngroups; g0 += U * kBlock) {
+      Group<T> gr[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        gr[u].load_buf(rs, g0 * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
+      const int nv = (ngroups - g0 + kBlock - 1) / kBlock;
+      f(gr, g0, nv);
+    }
+  } else {
+    for (int g = threadIdx.x; g < ngroups; g += kBlock) {
+      Group<T> gr[1];
+      const int pos = start + g * kVec;
+      const int n = min(kVec, end - pos);
+      if (aligned && n == kVec) gr[0].load(row + pos);
+      else gr[0].load_part(row + pos, n);
+      f(gr, g, 1);
+    }
+  }
+}
+
 // Max of three floats as one v_max3_f32.  fmaxf would first quieten each
 // operand (one more instruction per logit); NaN never needs to survive here
 // because every pass probes for it separately.
@@ -181,6 +258,17 @@ DEV float max3_raw(float a, float b, float c) {
 }
 DEV float max8(const float v[kVec]) {
   return max3_raw(max3_raw(v[0], v[1], v[2]), max3_raw(v[3], v[4], v[5]), max3_raw(v[6], v[7], v[7]));
+}
+// Max of three floats that is NaN if any operand is NaN (v_maximum3_f32, IEEE
+// 754-2019 maximum; -0 < +0), and the max of a group built from it: one
+// comparison of the result with itself then tells whether the group held a NaN.
+DEV float maximum3(float a, float b, float c) {
+  float r;
+  asm("v_maximum3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+DEV float maximum8(const float v[kVec]) {
+  return maximum3(maximum3(v[0], v[1], v[2]), maximum3(v[3], v[4], v[5]), maximum3(v[6], v[7], v[7]));
 }
 
 // ------------------------------------------------------------------ float64 exp2
@@ -212,6 +300,30 @@ DEV double exp2_64(double y64, const double* tab) {
   q = fma(q, f, 1.0);
   const int ji = (int)j;
   return ldexp(tab[ji & 63] * q, ji >> 6);
+}
+
+// 2^y for y <= 0 in float64 with few registers: y = j + f, j = rint(y),
+// 2^f = e^(f ln2) by its Taylor series to degree 13 (|f ln2| <= 0.35,
+// remainder below 1e-17), then scaled by 2^j.  Below -1100 the result is 0.
+DEV double exp2_neg(double y) {
+  if (!(y > -1100.0)) return 0.0;
+  const double j = rint(y);
+  const double t = (y - j) * 0.6931471805599453;
+  double q = 1.0 / 6227020800.0;                 // 1/13!
+  q = fma(q, t, 1.0 / 479001600.0);
+  q = fma(q, t, 1.0 / 39916800.0);
+  q = fma(q, t, 1.0 / 3628800.0);
+  q = fma(q, t, 1.0 / 362880.0);
+  q = fma(q, t, 1.0 / 40320.0);
+  q = fma(q, t, 1.0 / 5040.0);
+  q = fma(q, t, 1.0 / 720.0);
+  q = fma(q, t, 1.0 / 120.0);
+  q = fma(q, t, 1.0 / 24.0);
+  q = fma(q, t, 1.0 / 6.0);
+  q = fma(q, t, 0.5);
+  q = fma(q, t, 1.0);
+  q = fma(q, t, 1.0);
+  return ldexp(q, (int)j);
 }
 
 // ------------------------------------------------------------------ keys
@@ -445,103 +557,121 @@ DEV const T* row_ptr(const Params& p, int grow) {
 DEV int trow(const Params& p, int b, int j) { return b * p.rows_t + j; }
 DEV int drow(const Params& p, int b, int j) { return p.B * p.rows_t + b * p.rows_d + j; }
 
-// Combine the tile partials of rows 0..nrows-1 (global row ids row_of(r)).
-// A segment of W lanes (W = S rounded up to a power of two) takes one row,
-// lane s holding tile s; the butterflies over xor offsets < W give the same
-// result as one over the whole wave with idle lanes, so every kernel that
-// combines a row gets the same bits.  Each wave keeps kUnroll loads in
-// flight.  sink(r, M, amax, Z, bad) is called once per row:
-//   M     the row max; amax its lowest index (ARGMAX partials)
-//   Z     STATS: sum over tiles of s_t * 2^((m_t - M) log2e / T), else 0
+// Combine the partials of rows 0..nrows-1 (global row ids row_of(r)).  A
+// segment of W lanes (W = ceil(P / kLanePartials) rounded up to a power of
+// two) takes one row; lane s holds the kLanePartials consecutive partials
+// from s * kLanePartials, combines them in registers, and butterflies over
+// xor offsets < W (at most four steps) finish the row.  Every partial load
+// is issued before any is used, unconditionally (a slot with no partial
+// reads partial 0 of the workspace and is cleared: a load under a branch
+// would be waited for before the branch joins).  The order of every
+// operation depends only on P, so every kernel that combines a row gets the
+// same bits.  sink(r, M, amax, Z, bad) is called once per row:
+//   M     the row max; amax its lowest index (argmax partials)
+//   Z     STATS: sum over partials of s_t * 2^((m_t - M) log2e / T), else 0
 //   bad   the row holds NaN or +inf, or no finite value
+constexpr int kLanePartials = 16;
+
 template <bool STATS, typename RowOf, typename Sink>
 DEV void combine_rows(const Params& p, int nrows, RowOf row_of, Sink sink) {
-  const int S = p.S;
+  constexpr int Q = kLanePartials;
+  const int P = p.P;
   int lw = 0;
-  while ((1 << lw) < S) ++lw;
-  const int W = 1 << lw;
-  const int R = 64 >> lw;                    // rows per wave per slot
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int seg = lane >> lw, s = lane & (W - 1);
+  while ((Q << lw) < P) ++lw;
+  const int W = 1 << lw;                     // lanes per row
+  const int per_block = kBlock >> lw;        // rows per pass of the block
+  const int seg = threadIdx.x >> lw, s = threadIdx.x & (W - 1);
   const double cd = kLog2e / p.T;
-  for (int base = 0; base < nrows; base += kWaves * R * kUnroll) {
-    TileStat ts[kUnroll];
+  for (int base = 0; base < nrows; base += per_block) {
+    const int r = base + seg;
+    TileStat ts[Q];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int r = base + (u * kWaves + wv) * R + seg;
-      if (r < nrows && s < S) {
-        ts[u] = p.tiles[(size_t)row_of(r) * S + s];
-      } else {
-        ts[u].m = -INFINITY; ts[u].amax = INT_MAX; ts[u].s = 0.0;
-      }
+    for (int q = 0; q < Q; ++q) {
+      const int i = s * Q + q;
+      const bool ok = r < nrows && i < P;
+      ts[q] = p.tiles[ok ? (size_t)row_of(ok ? r : 0) * P + i : 0];
     }
+    float m = -INFINITY;
+    int ai = INT_MAX;
+    int bad = 0;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int r = base + (u * kWaves + wv) * R + seg;
-      float m = ts[u].m;
-      int ai = ts[u].amax;
-      int bad = ts[u].s != ts[u].s;
-      for (int o = W >> 1; o > 0; o >>= 1) {
-        const float m2 = __shfl_xor(m, o);
-        const int a2 = __shfl_xor(ai, o);
-        if (m2 > m || (m2 == m && a2 < ai)) { m = m2; ai = a2; }
-        bad |= __shfl_xor(bad, o);
-      }
-      double Z = 0.0;
-      if (STATS) {
-        double t = 0.0;
-        if (s < S) t = ts[u].m == -INFINITY ? ts[u].s : ts[u].s * exp2(((double)ts[u].m - (double)m) * cd);
-        for (int o = W >> 1; o > 0; o >>= 1) t += __shfl_xor(t, o);
-        Z = t;
-      }
-      bad |= (m == INFINITY) || (m == -INFINITY) || (Z != Z);
-      if (s == 0 && r < nrows) sink(r, m, ai, Z, bad);
+    for (int q = 0; q < Q; ++q) {
+      const int i = s * Q + q;
+      const bool ok = r < nrows && i < P;
+      if (!ok) { ts[q].m = -INFINITY; ts[q].amax = INT_MAX; ts[q].s = 0.0; }
+      bad |= ts[q].s != ts[q].s;
+      if (ts[q].m > m || (ts[q].m == m && ts[q].amax < ai)) { m = ts[q].m; ai = ts[q].amax; }
     }
+    for (int o = W >> 1; o > 0; o >>= 1) {
+      const float m2 = __shfl_xor(m, o);
+      const int a2 = __shfl_xor(ai, o);
+      if (m2 > m || (m2 == m && a2 < ai)) { m = m2; ai = a2; }
+      bad |= __shfl_xor(bad, o);
+    }
+    double Z = 0.0;
+    if (STATS) {
+      double t = 0.0;
+      if (m > -INFINITY && m < INFINITY) {
+#pragma unroll
+        for (int q = 0; q < Q; ++q)
+          t += ts[q].m == -INFINITY ? ts[q].s : ts[q].s * exp2_neg(((double)ts[q].m - (double)m) * cd);
+      }
+      for (int o = W >> 1; o > 0; o >>= 1) t += __shfl_xor(t, o);
+      Z = t;
+    }
+    bad |= (m == INFINITY) || (m == -INFINITY) || (Z != Z);
+    if (s == 0 && r < nrows) sink(r, m, ai, Z, bad);
   }
 }
 
 // ================================================================== tile passes
 
-// Max and lowest index of the max of a tile.  Lanes only track their max
-// and the first group that reached it; once the tile max is known, the few
-// lanes that hold it reload that group (16 bytes) and find the index.
+// Max and lowest index of the max over the logits each wave of a tile reads
+// (one partial per wave).  Each lane keeps the first of its groups that
+// reached its running max (raw words, in registers), so the lane's lowest
+// index of its max is found at the end without touching memory again; the
+// wave then takes the largest packed (value desc, index asc) key with one
+// butterfly.  NaN: the group max propagates it, one ballot per group.
 template <typename T>
-DEV void tile_argmax(const Params& p, const T* row, int start, int end, int ngroups, int tile) {
-  __shared__ float redm[kWaves];
-  __shared__ int redi[2 * kWaves];
-  const int nfull = (end - start) / kVec;
+DEV void tile_argmax(const Params& p, const T* row, int start, int end, int grow, int seg) {
   float m = -INFINITY;
-  int gbest = 0;
-  uint32_t probe = 0;
-  bool nanv = false;
-  for (int g0 = threadIdx.x; g0 < ngroups; g0 += kUnroll * kBlock) {
-    float v[kUnroll][kVec];
-    int nv[kUnroll];
-    load_iter<T>(row, start, end, ngroups, nfull, p.aligned, g0, v, nv, probe, nanv);
+  int gbest = -1;
+  Group<T> best;
+  best.load_part(row, 0);
+  uint64_t nanm = 0;
+  tile_groups<T, kUnroll>(row, start, end, p.aligned, [&](const auto& gr, int g0, int nv) {
+    constexpr int n = sizeof(gr) / sizeof(gr[0]);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const float gm = max8(v[u]);
-      const bool better = gm > m;
+    for (int u = 0; u < n; ++u) {
+      float v[kVec];
+      gr[u].values(v);
+      const float gm = maximum8(v);
+      nanm |= __ballot(gm != gm);
+      const bool better = u < nv && gm > m;
       m = better ? gm : m;
       gbest = better ? g0 + u * kBlock : gbest;
+      best.select(better, gr[u]);
     }
-  }
-  const bool nan = __syncthreads_or(nanv || Group<T>::has_nan(probe));
-  const float M = block_max(m, redm);
+  });
   int idx = INT_MAX;
-  if (m == M && M > -INFINITY) {
+  if (gbest >= 0) {
     float v[kVec];
-    const int pos = start + gbest * kVec;
-    load_group<T>(row, pos, end, p.aligned, v);
+    best.values(v);
 #pragma unroll
-    for (int e = kVec - 1; e >= 0; --e) if (v[e] == M) idx = pos + e;
+    for (int e = kVec - 1; e >= 0; --e) if (v[e] == m) idx = start + gbest * kVec + e;
   }
-  int none = -1;
-  block_minmax(idx, none, redi);
-  if (threadIdx.x == 0) {
+  uint64_t key = idx == INT_MAX ? 0ull : pack(m, idx);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint64_t k2 = __shfl_xor(key, o);
+    key = k2 > key ? k2 : key;
+  }
+  if ((threadIdx.x & 63) == 0) {
     TileStat ts;
-    ts.m = M; ts.amax = idx; ts.s = (nan || M == INFINITY) ? (double)NAN : 0.0;
-    p.tiles[tile] = ts;
+    ts.m = key ? packed_val(key) : -INFINITY;
+    ts.amax = key ? packed_idx(key) : INT_MAX;
+    ts.s = (nanm || ts.m == INFINITY) ? (double)NAN : 0.0;
+    p.tiles[(size_t)grow * p.P + seg * kWaves + (threadIdx.x >> 6)] = ts;
   }
 }
 
@@ -558,48 +688,64 @@ DEV void record_token_logit(const Params& p, const T* row, int grow, int start, 
   if (x >= start && x < end) p.row_lx[grow] = Io<T>::at(row, x);
 }
 
-// Max and float64 sum of exp((l - max) / T) of a tile.
+// Max and sum of exp((l - max) / T) = 2^((l - max) c), c = log2(e) / T, over
+// the logits each wave of a tile reads (one partial per wave).  Per lane:
+// each round of groups first raises the lane max m over them (rescaling the
+// lane sum, in float64, if it rose), then adds 2^((l - m) c) of every logit
+// with the hardware float32 exp2 (relative error below 1e-7).  The exponent
+// is (l - m) * c with c split into two floats (c_hi + c_lo carries c to
+// about 48 bits), so the only float32 roundings per term are the difference,
+// the product and exp2 itself; eight terms are summed in float32 (a fixed
+// tree), groups in float64.  The wave combines its lanes in float64 by one
+// fixed butterfly.  The relative error of a partial sum is a few float32
+// roundings, about 1e-7.
 template <typename T>
-DEV void tile_stats64(const Params& p, const T* row, int start, int end, int ngroups, int tile) {
-  __shared__ float redm[kWaves];
-  __shared__ double redd[kWaves];
-  __shared__ double tab[64];
-  if (threadIdx.x == 0) record_token_logit<T>(p, row, tile / p.S, start, end);
-  exp2_table_init(tab);
-  const int nfull = (end - start) / kVec;
-  const double c64 = 64.0 * kLog2e / p.T;
+DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow, int seg) {
+  if (threadIdx.x == 0) record_token_logit<T>(p, row, grow, start, end);
+  const double cd = kLog2e / p.T;
+  const float c_hi = (float)cd;
+  const float c_lo = (float)(cd - (double)c_hi);
   float m = -INFINITY;
-  double nmc = 0.0;     // -m * c64
-  double s = 0.0;       // sum of 2^((l - m) c64 / 64)
-  uint32_t probe = 0;
-  bool nanv = false;
-  for (int g0 = threadIdx.x; g0 < ngroups; g0 += kUnroll * kBlock) {
-    float v[kUnroll][kVec];
-    int nv[kUnroll];
-    load_iter<T>(row, start, end, ngroups, nfull, p.aligned, g0, v, nv, probe, nanv);
+  double s = 0.0;
+  uint64_t nanm = 0;
+  tile_groups<T, kUnroll>(row, start, end, p.aligned, [&](const auto& gr, int, int nv) {
+    constexpr int n = sizeof(gr) / sizeof(gr[0]);
+    float mi = m;
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (nv[u] == 0) continue;   // past the tile (uniform across most waves)
-      const float gm = max8(v[u]);
-      if (gm > m) {
-        if (m > -INFINITY) s *= exp2_64(((double)m - (double)gm) * c64, tab);
-        m = gm;
-        nmc = -(double)m * c64;
-      }
-      if (m > -INFINITY) {
+    for (int u = 0; u < n; ++u) {
+      float v[kVec];
+      gr[u].values(v);
+      const float gm = maximum8(v);
+      nanm |= __ballot(gm != gm);
+      mi = (u < nv && gm > mi) ? gm : mi;
+    }
+    if (mi > m) {
+      if (m > -INFINITY) s *= exp2_neg(((double)m - (double)mi) * cd);
+      m = mi;
+    }
+    if (m > -INFINITY) {
 #pragma unroll
-        for (int e = 0; e < kVec; ++e) s += exp2_64(fma((double)v[u][e], c64, nmc), tab);
+      for (int u = 0; u < n; ++u) {
+        float v[kVec], e[kVec];
+        gr[u].values(v);
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          // -inf logits: clamp d so that d * c_lo cannot be +inf (c_lo < 0)
+          const float d = fmaxf(v[q] - m, -FLT_MAX);
+          e[q] = __builtin_amdgcn_exp2f(fmaf(d, c_hi, d * c_lo));
+        }
+        const float gs = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+        s += u < nv ? (double)gs : 0.0;
       }
     }
-  }
-  const bool nan = __syncthreads_or(nanv || Group<T>::has_nan(probe));
-  const float M = block_max(m, redm);
-  const double term = m == -INFINITY ? 0.0 : s * exp2_64(((double)m - (double)M) * c64, tab);
-  const double tot = block_sum(term, redd);
-  if (threadIdx.x == 0) {
+  });
+  const float M = wave_max(m);
+  double term = m == -INFINITY ? 0.0 : s * exp2_neg(((double)m - (double)M) * cd);
+  term = wave_sum(term);
+  if ((threadIdx.x & 63) == 0) {
     TileStat ts;
-    ts.m = M; ts.amax = INT_MAX; ts.s = (nan || M == INFINITY) ? (double)NAN : tot;
-    p.tiles[tile] = ts;
+    ts.m = M; ts.amax = INT_MAX; ts.s = (nanm || M == INFINITY) ? (double)NAN : term;
+    p.tiles[(size_t)grow * p.P + seg * kWaves + (threadIdx.x >> 6)] = ts;
   }
 }
 
@@ -1553,9 +1699,9 @@ __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
     __shared__ uint64_t lds[kTopkLds];
     tile_topk<T>(p, row, start, end, ngroups, tile, lds);
   } else if constexpr (MODE == kModeStats64) {
-    tile_stats64<T>(p, row, start, end, ngroups, tile);
+    tile_stats<T>(p, row, start, end, grow, seg);
   } else {
-    tile_argmax<T>(p, row, start, end, ngroups, tile);
+    tile_argmax<T>(p, row, start, end, grow, seg);
   }
 }
 
