@@ -12,7 +12,8 @@ namespace {
 
 constexpr int kMinTile = 8192;        // top-k pass: logits per tile, lower bound
 constexpr int kRound = 4 * sv::kBlock * sv::kVec;   // argmax / sum passes: logits per round of loads
-constexpr int kMinSmall = 2048;       // argmax / sum passes: smallest tile of small problems
+constexpr int kMinSmall = 2048;       // argmax / sum / filter passes: smallest tile of small problems
+constexpr int kSmallTiles = 256;      // problems with fewer tiles than this take smaller tiles
 
 struct Plan {
   int filt;        // sv::Filter
@@ -20,7 +21,7 @@ struct Plan {
   int top_k;       // effective top-k (0 = off)
   double top_p;    // effective top-p (1 = off)
   int rows_t, rows_d, out_w;
-  int S_max;       // largest top-k tile count per row (candidate list workspace)
+  int S_max;       // most tiles per row of the top-k list passes (candidate list workspace)
   int S2_max;      // residual segments per sequence (plain sampling)
   int cand_w;
 };
@@ -57,9 +58,19 @@ Plan make_plan(const sv_config* c) {
   else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats64; }
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
-  // top-k tiles hold at least kMinTile logits (the candidate lists are sized by it)
-  p.S_max = (c->vocab + kMinTile - 1) / kMinTile;
-  if (p.S_max > sv::kMaxTiles) p.S_max = sv::kMaxTiles;
+  // most tiles per row of the list passes at any batch size (see the tiling
+  // in specverify_run): the exact pass, or the filter pass at batch 1
+  {
+    const long rows1 = p.rows_t + p.rows_d;
+    long s_exact = (c->vocab + kMinTile - 1) / kMinTile;
+    long s_round = (c->vocab + kRound - 1) / kRound;
+    long s_small = (kSmallTiles + rows1 - 1) / rows1;
+    const long cap = (c->vocab + kMinSmall - 1) / kMinSmall;
+    if (s_small > cap) s_small = cap;
+    long sm = s_exact > s_round ? s_exact : s_round;
+    if (s_small > sm) sm = s_small;
+    p.S_max = (int)(sm > sv::kMaxTiles ? sv::kMaxTiles : sm);
+  }
   p.cand_w = p.top_k > 0 ? sv::kCandSlots : 0;
   if (p.S_max < 1) p.S_max = 1;
   p.S2_max = (c->vocab + sv::kResidSeg - 1) / sv::kResidSeg;
@@ -109,7 +120,6 @@ struct specverify_ctx {
   size_t ws_bytes;
   Layout L;
   int grid;                      // resident workgroups of the streaming kernel
-  int cus;                       // compute units of the device
   hipEvent_t ev_begin, ev_end;   // optional instrumentation (caller-owned)
 };
 
@@ -180,7 +190,6 @@ int specverify_create(const sv_config* cfg, int device, specverify_ctx** out) {
   if (hipGetDeviceProperties(&prop, device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
   const int per_cu = sv::stream_blocks_per_cu(ctx->plan.tile_mode, cfg->dtype == SV_DTYPE_BF16);
   ctx->grid = prop.multiProcessorCount * (per_cu > 0 ? per_cu : 1);
-  ctx->cus = prop.multiProcessorCount;
   if (hipMalloc(&ctx->ws, L.total) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
   *out = ctx;
   return SV_OK;
@@ -243,9 +252,20 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.top_p = pl.top_p;
   p.top_k = pl.top_k;
   // tiling of the streaming pass
+  const size_t es = c->dtype == SV_DTYPE_BF16 ? 2 : 4;
+  const bool rows16 = ((size_t)c->vocab * es) % 16 == 0;
+  const bool base16 = ((uintptr_t)target_logits % 16 == 0) &&
+                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0);
+  p.aligned = (rows16 && base16) ? 1 : 0;
+  // top-k: the certified filter pass takes tiles of one round of loads in
+  // aligned rows; other shapes take the exact per-tile pass
+  int tile_mode = pl.tile_mode;
+  const int round = tile_mode == sv::kModeTopk ? (int)(sv::kFilterRound * 2 / es) : kRound;
+  if (tile_mode == sv::kModeTopk && p.aligned && c->vocab <= (long)sv::kMaxTiles * round)
+    tile_mode = sv::kModeTopkFilter;
   const long rows = (long)batch * (pl.rows_t + pl.rows_d);
   long S;
-  if (pl.tile_mode == sv::kModeTopk) {
+  if (tile_mode == sv::kModeTopk) {
     // about four tiles per resident workgroup, tiles of at least kMinTile logits
     S = (4L * ctx->grid + rows - 1) / rows;
     const long smax = (c->vocab + kMinTile - 1) / kMinTile;
@@ -253,11 +273,11 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   } else {
     // one round of loads per lane (kRound logits; 16 KB of bf16, 32 KB of
     // fp32); rows that need more than kMaxTiles such tiles take several
-    // rounds per tile; problems with fewer tiles than CUs take smaller tiles
-    // (down to kMinSmall logits)
-    S = (c->vocab + kRound - 1) / kRound;
-    if (rows * S < ctx->cus) {
-      long want = (ctx->cus + rows - 1) / rows;
+    // rounds per tile; problems with fewer than kSmallTiles tiles take
+    // smaller tiles (down to kMinSmall logits)
+    S = (c->vocab + round - 1) / round;
+    if (rows * S < kSmallTiles) {
+      long want = (kSmallTiles + rows - 1) / rows;
       const long cap = (c->vocab + kMinSmall - 1) / kMinSmall;
       if (want > cap) want = cap;
       if (want > S) S = want;
@@ -266,15 +286,13 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   if (S > sv::kMaxTiles) S = sv::kMaxTiles;
   if (S < 1) S = 1;
   int per = (int)((c->vocab + S - 1) / S);
-  if (pl.tile_mode != sv::kModeTopk && per > kRound) per = (per + kRound - 1) / kRound * kRound;
+  if (tile_mode != sv::kModeTopk && per > round) per = (per + round - 1) / round * round;
   p.L = (per + sv::kVec - 1) / sv::kVec * sv::kVec;
   p.S = (c->vocab + p.L - 1) / p.L;
-  p.P = pl.tile_mode == sv::kModeTopk ? p.S : p.S * (sv::kBlock / 64);
-  const size_t es = c->dtype == SV_DTYPE_BF16 ? 2 : 4;
-  const bool rows16 = ((size_t)c->vocab * es) % 16 == 0;
-  const bool base16 = ((uintptr_t)target_logits % 16 == 0) &&
-                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0);
-  p.aligned = (rows16 && base16) ? 1 : 0;
+  const bool lists = tile_mode == sv::kModeTopk || tile_mode == sv::kModeTopkFilter;
+  p.P = lists ? p.S : p.S * (sv::kBlock / 64);
+  // the workspace holds S_max candidate lists and kMaxPartials partials per row
+  if ((lists && p.S > pl.S_max) || p.P > sv::kMaxPartials || p.S > sv::kMaxTiles) return SV_ERR_SHAPE;
   p.grid = ctx->grid;
   char* ws = (char*)ctx->ws;
   const Layout& L = ctx->L;
@@ -301,7 +319,7 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   if (cur != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
   hipStream_t st = (hipStream_t)stream;
   const int bf16 = c->dtype == SV_DTYPE_BF16;
-  hipError_t e = sv::launch_stream(p, pl.tile_mode, bf16, st, ctx->ev_begin, ctx->ev_end);
+  hipError_t e = sv::launch_stream(p, tile_mode, bf16, st, ctx->ev_begin, ctx->ev_end);
   if (e == hipSuccess) e = sv::launch_finish(p, pl.filt, bf16, st);
   if (cur != ctx->device) (void)hipSetDevice(cur);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;

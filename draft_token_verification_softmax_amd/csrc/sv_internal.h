@@ -17,6 +17,9 @@ constexpr int kNucBins = 2048;         // histogram bins of the nucleus search
 constexpr int kResidSeg = kBlock * kVec;  // logits per workgroup in the residual kernels
 constexpr int kMaxTiles = 64;          // tiles per row
 constexpr int kMaxPartials = 256;      // partials per row (one wave combines a row's partials)
+// logits per tile of the top-k filter pass for bf16 (one round of loads:
+// eight 16-byte groups per lane); fp32 tiles hold half as many
+constexpr int kFilterRound = 8 * kBlock * kVec;
 
 // Partial result of the streaming pass over a part of a row: the logits one
 // wave of a tile read (argmax and sum passes), or a whole tile (top-k pass).
@@ -25,8 +28,12 @@ constexpr int kMaxPartials = 256;      // partials per row (one wave combines a 
 //   s    NaN iff the part holds a NaN or +inf (exact, every mode); otherwise
 //        STATS mode: float64 sum over the part of exp((l - m) / T), other
 //        modes: 0
-// TOPK mode instead: m = the tile's top_k-th logit (-inf if it has fewer),
-// amax = the length of its list (its top_k in rank order, in p.cand).
+// Top-k passes instead: m = a lower bound of the tile's top_k-th logit such
+// that the tile's list (in p.cand, amax entries) holds every logit of the
+// tile >= m (-inf if the tile has fewer than top_k logits).  The exact pass
+// lists the tile's top_k in rank order with m its top_k-th logit; the
+// filter pass lists, unordered, every logit >= its bound, and amax above
+// cand_w means the list overflowed (the row merge then redoes the tile).
 struct TileStat {
   float m;
   int32_t amax;
@@ -60,7 +67,10 @@ struct SeqState {
   int32_t n, st;
 };
 
-enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3 };
+// Passes of the streaming kernel: argmax (greedy, tree), top-k lists (exact
+// per tile: any tile shape; certified filter: tiles of one round of loads in
+// aligned rows), max + sum of exponentials (plain and nucleus sampling).
+enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4 };
 enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4 };
 
 struct Params {

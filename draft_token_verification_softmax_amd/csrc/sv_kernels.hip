@@ -45,6 +45,7 @@ constexpr double kLog2e = 1.4426950408889634;
 constexpr int kStatusInternal = 0x100;   // a numeric search did not settle (never expected)
 constexpr int kTopkMax = 256;            // largest top_k
 constexpr int kUnroll = 4;               // groups of kVec logits each lane has in flight
+constexpr int kFilterGroups = kFilterRound / (kBlock * kVec) * 2;   // groups per lane of a top-k filter tile, times sizeof(T) / 2
 constexpr int kMaxTree = 1024;
 constexpr int kMaxRows = 2 * 64 + 1;
 
@@ -83,6 +84,13 @@ template <> struct Group<uint16_t> {
     w = __builtin_bit_cast(vu4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT));
   }
   static constexpr int kBytes = 16;
+  // the same words through an empty asm: values() of the copy are recomputed
+  // instead of kept alive from an earlier unpack (registers)
+  DEV Group opaque() const {
+    Group g = *this;
+    asm volatile("" : "+v"(g.w.x), "+v"(g.w.y), "+v"(g.w.z), "+v"(g.w.w));
+    return g;
+  }
   DEV void values(float v[kVec]) const {
     v[0] = __uint_as_float(w.x << 16); v[1] = __uint_as_float(w.x & 0xffff0000u);
     v[2] = __uint_as_float(w.y << 16); v[3] = __uint_as_float(w.y & 0xffff0000u);
@@ -122,6 +130,12 @@ template <> struct Group<float> {
     b = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, kNT));
   }
   static constexpr int kBytes = 32;
+  DEV Group opaque() const {
+    Group g = *this;
+    asm volatile("" : "+v"(g.a.x), "+v"(g.a.y), "+v"(g.a.z), "+v"(g.a.w));
+    asm volatile("" : "+v"(g.b.x), "+v"(g.b.y), "+v"(g.b.z), "+v"(g.b.w));
+    return g;
+  }
   DEV void values(float v[kVec]) const {
     v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
     v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
@@ -727,7 +741,7 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
 #pragma unroll
       for (int u = 0; u < n; ++u) {
         float v[kVec], e[kVec];
-        gr[u].values(v);
+        gr[u].opaque().values(v);
 #pragma unroll
         for (int q = 0; q < kVec; ++q) {
           // -inf logits: clamp d so that d * c_lo cannot be +inf (c_lo < 0)
@@ -754,7 +768,8 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
 // to the best top_k and the admission threshold raised.
 template <typename T>
 DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int ngroups, int tile,
-                          uint64_t* buf, unsigned short* rank) {
+                          uint64_t* buf, unsigned short* rank, int* n_out = nullptr,
+                          float* m_out = nullptr) {
   __shared__ int cnt;
   __shared__ float tau_f;
   __shared__ uint64_t tau_p;
@@ -809,15 +824,18 @@ DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int
   }
   const bool bad = __syncthreads_or(badv);
   const int c = cnt;
+  const float m = c >= K ? packed_val(buf[K - 1]) : -INFINITY;   // the tile's top_k-th
   uint64_t* out = p.cand + (size_t)tile * p.cand_w;
   for (int i = tid; i < c; i += kBlock) out[i] = buf[i];
   if (tid == 0) {
     TileStat ts;
-    ts.m = c >= K ? packed_val(buf[K - 1]) : -INFINITY;   // a lower bound of the tile's top_k-th
+    ts.m = m;
     ts.amax = c;
     ts.s = bad ? (double)NAN : 0.0;
     p.tiles[tile] = ts;
   }
+  if (n_out) *n_out = c;
+  if (m_out) *m_out = m;
   __syncthreads();
 }
 
@@ -1007,6 +1025,147 @@ DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroup
     TileStat ts;
     ts.m = kth;
     ts.amax = c < K ? c : K;
+    ts.s = bad ? (double)NAN : 0.0;
+    p.tiles[tile] = ts;
+  }
+}
+
+// r-th largest (1 <= r <= 64 * Q) of the keys k[q] held by the lanes of one
+// wave: radix select from the top bit, one ballot per key slot and bit (no
+// shuffles, no LDS).  Every lane gets it.  BITS = 16 is for keys of bf16
+// values, whose low 16 bits follow from the top bit (all ones for a negative
+// value, zeros otherwise): only the top 16 bits are selected, the rest is
+// restored, so the result is the r-th largest key exactly in both cases.
+template <int Q, int BITS>
+DEV uint32_t wave_kth_key(const uint32_t (&k)[Q], int r) {
+  uint32_t pre = 0u;
+#pragma unroll
+  for (int bit = 31; bit >= 32 - BITS; --bit) {
+    const uint32_t c = pre | (1u << bit);
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < Q; ++q) n += __popcll(__ballot(k[q] >= c));
+    if (n >= r) pre = c;
+  }
+  if (BITS < 32 && !(pre >> 31)) pre |= (1u << (32 - BITS)) - 1u;
+  return pre;
+}
+
+// Exclusive prefix over the lanes of a wave of small counts c (0 <= c < 64),
+// bit-sliced through ballots; *total gets the wave's sum.
+DEV int wave_exclusive_small(int c, int* total) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  int ex = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < 6; ++b) {
+    const uint64_t m = __ballot((c >> b) & 1);
+    ex += __popcll(m & below) << b;
+    tot += __popcll(m) << b;
+  }
+  *total = tot;
+  return ex;
+}
+
+// Certified top-k filter over a tile of one round of loads (U groups per
+// lane; whole groups, 16-byte aligned row).  Every lane reduces its groups
+// to a lane max.  Each wave finds the r1-th largest of its 64 lane maxima
+// (r1 = max(16, ceil(top_k / 4))) by a radix select and publishes r1 lane
+// maxima at or above it; wave 0 then takes the top_k-th largest, tau, of
+// those 4 r1 values.  They are maxima of distinct lanes, so at least top_k
+// logits of the tile are >= tau: tau bounds the tile's top_k-th logit from
+// below (lanes with no logit hold -inf, which can only make tau -inf: then
+// the whole tile is listed).  bf16 keys need only their top 16 bits.  Every
+// logit >= tau goes to the tile's list, unordered, at a slot from a
+// ballot-sliced wave prefix and one LDS atomic per wave.  m = tau, amax =
+// list length (above cand_w: overflow; the row merge then redoes the tile
+// exactly).
+template <typename T, int U>
+DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int tile) {
+  constexpr int BITS = sizeof(T) == 2 ? 16 : 32;
+  __shared__ uint32_t pub[kBlock];
+  __shared__ uint32_t sh_tau;
+  __shared__ int cnt;
+  __shared__ int redb[kWaves];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int K = p.top_k;
+  const int r1 = max(16, (K + kWaves - 1) / kWaves);
+  const int ngroups = (end - start) / kVec;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, (end - start) * (int)sizeof(T));
+  Group<T> gr[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) gr[u].load_buf(rs, tid * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
+  if (tid == 0) cnt = 0;
+  float gm[U];
+  float lm = -INFINITY;
+  uint64_t nanm = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    float v[kVec];
+    gr[u].values(v);
+    const float g = maximum8(v);
+    nanm |= __ballot(g != g);
+    gm[u] = (tid + u * kBlock < ngroups && g == g) ? g : -INFINITY;
+    lm = fmaxf(lm, gm[u]);
+  }
+  // each wave publishes r1 of its largest lane maxima
+  {
+    const uint32_t key[1] = {ord_key(lm)};
+    const uint32_t t1 = wave_kth_key<1, BITS>(key, r1);
+    const bool sel = key[0] >= t1;
+    const uint64_t msk = __ballot(sel);
+    const int pos = __popcll(msk & ((1ull << lane) - 1ull));
+    if (sel && pos < r1) pub[w * r1 + pos] = key[0];
+    if (lane == 0) redb[w] = nanm != 0ull || __ballot(lm == INFINITY) != 0ull;
+  }
+  __syncthreads();
+  if (w == 0) {
+    uint32_t k4[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) { const int i = lane + 64 * q; k4[q] = i < kWaves * r1 ? pub[i] : 0u; }
+    const uint32_t tk = wave_kth_key<4, BITS>(k4, K);
+    if (lane == 0) sh_tau = tk;
+  }
+  __syncthreads();
+  const float tau = key_value(sh_tau);
+  const bool bad = redb[0] | redb[1] | redb[2] | redb[3];
+  // the lane's logits >= tau: count, wave prefix, one LDS atomic per wave
+  int c = 0;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (tid + u * kBlock < ngroups && gm[u] >= tau) {
+      float v[kVec];
+      gr[u].opaque().values(v);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) c += v[e] >= tau;
+    }
+  }
+  int total;
+  const int ex = wave_exclusive_small(c, &total);
+  int base = 0;
+  if (lane == 0 && total > 0) base = atomicAdd(&cnt, total);
+  int slot = __shfl(base, 0) + ex;
+  uint64_t* out = p.cand + (size_t)tile * p.cand_w;
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (tid + u * kBlock < ngroups && gm[u] >= tau) {
+      float v[kVec];
+      gr[u].opaque().values(v);
+      const int pos = start + (tid + u * kBlock) * kVec;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        if (v[e] >= tau) {
+          if (slot < p.cand_w) out[slot] = pack(v[e], pos + e);
+          ++slot;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  if (tid == 0) {
+    TileStat ts;
+    ts.m = tau;
+    ts.amax = cnt;
     ts.s = bad ? (double)NAN : 0.0;
     p.tiles[tile] = ts;
   }
@@ -1278,6 +1437,80 @@ __global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
 
 // ================================================================== top-k
 
+// Threshold of the K largest of c >= K distinct u64 keys in LDS: keys >= the
+// result are exactly the K largest.  Radix select by 8-bit digits from the
+// top: an LDS histogram of the digit among the keys that match the prefix
+// so far, then wave 0 finds the digit where the count from the top reaches
+// the rank still needed.  Stops as soon as that digit holds exactly the
+// keys still needed (then the prefix with zero low bits is the threshold).
+DEV uint64_t block_topk_threshold(const uint64_t* keys, int c, int K, unsigned* hist, int* shv) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  uint64_t prefix = 0ull, mask = 0ull;
+  int need = K;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int b = tid; b < 256; b += kBlock) hist[b] = 0u;
+    __syncthreads();
+    for (int i = tid; i < c; i += kBlock) {
+      const uint64_t x = keys[i];
+      if ((x & mask) == prefix) atomicAdd(&hist[(unsigned)(x >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      unsigned h[4];
+      unsigned s4 = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) { h[q] = hist[255 - 4 * lane - q]; s4 += h[q]; }
+      unsigned incl = s4;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned t = __shfl_up(incl, o);
+        if (lane >= o) incl += t;
+      }
+      unsigned cb = incl - s4;   // keys with a larger digit
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (cb < (unsigned)need && cb + h[q] >= (unsigned)need) {
+          shv[0] = 255 - 4 * lane - q;
+          shv[1] = need - (int)cb;
+          shv[2] = (int)h[q];
+        }
+        cb += h[q];
+      }
+    }
+    __syncthreads();
+    const int d = shv[0];
+    need = shv[1];
+    const int hd = shv[2];
+    prefix |= (uint64_t)d << shift;
+    mask |= (uint64_t)255 << shift;
+    __syncthreads();
+    if (hd == need) break;   // every key with this prefix is kept
+  }
+  return prefix;
+}
+
+// Keeps the min(c, K) largest of c distinct keys: writes them, unordered, to
+// dst[0, n) and returns n (c <= K: all of them).
+DEV int block_keep_top(const uint64_t* keys, int c, int K, uint64_t* dst, unsigned* hist, int* shv,
+                       int* counter) {
+  if (c <= K) {
+    for (int i = threadIdx.x; i < c; i += kBlock) dst[i] = keys[i];
+    __syncthreads();
+    return c;
+  }
+  const uint64_t thr = block_topk_threshold(keys, c, K, hist, shv);
+  if (threadIdx.x == 0) *counter = 0;
+  __syncthreads();
+  for (int i0 = 0; i0 < c; i0 += kBlock) {
+    const int i = i0 + threadIdx.x;
+    const uint64_t x = i < c ? keys[i] : 0ull;
+    const int slot = wave_append(i < c && x >= thr, counter);
+    if (slot >= 0) dst[slot] = x;
+  }
+  __syncthreads();
+  return K;
+}
+
 // Merge the S tile lists of one row and publish its kept set in rank order,
 // its normaliser, and -- for the rows an accept test reads -- p'(x) of the
 // drafted token.  Only list entries >= the row's largest tile tau can be in
@@ -1286,12 +1519,18 @@ __global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
 // top_k every few tiles and the threshold raised.
 static_assert(kCandSlots == kBlock, "one candidate slot per thread in the merge");
 static_assert(kMergeCap % 64 == 0 && kMergeCap >= 2 * kUnroll * kBlock, "merge list size");
+static_assert(kTopkCap * 8 + kTopkCap * 2 <= kMergeCap * 8, "the exact tile pass fits in the merge list");
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
   __shared__ uint64_t surv[kMergeCap];
   __shared__ uint64_t top[kTopkMax];
   __shared__ int tcnt[kMaxTiles];
+  __shared__ float ttau[kMaxTiles];
+  __shared__ unsigned hist[256];
+  __shared__ int shv[3];
+  __shared__ int cnt2;
+  __shared__ uint64_t redu[kWaves];
   __shared__ double red[kWaves];
   __shared__ int redi[2 * kWaves];
   __shared__ double sh_mass, sh_px;
@@ -1307,22 +1546,37 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
   if (grow < nt) { b = grow / p.rows_t; j = grow - b * p.rows_t; if (j >= p.k) j = -1; }
   else { b = (grow - nt) / p.rows_d; j = (grow - nt) - b * p.rows_d; }
   const int x = (j >= 0) ? p.tokens[(size_t)b * p.k + j] : -1;
-  // tile lengths, taus and probes (wave 0; S <= 64)
+  // tile lengths, taus and probes (S <= 64)
   int pr = 0;
-  if (tid < 64) {
-    float tt = -INFINITY;
-    if (tid < S) {
-      const TileStat ts = p.tiles[(size_t)grow * S + tid];
-      tcnt[tid] = ts.amax;
-      tt = ts.m;
-      pr = ts.s != ts.s;
-    }
-    tt = wave_max(tt);
-    if (tid == 0) { sh_tau = tt; ns = 0; }
+  if (tid < S) {
+    const TileStat ts = p.tiles[(size_t)grow * S + tid];
+    tcnt[tid] = ts.amax;
+    ttau[tid] = ts.m;
+    pr = ts.s != ts.s;
   }
   if (tid < kTopkMax) top[tid] = 0ull;
-  if (tid == 0) sh_px = 0.0;
+  if (tid == 0) { sh_px = 0.0; ns = 0; }
   const int probe = __syncthreads_or(pr);
+  // a filter list that overflowed (rare: many logits tie near the tile's
+  // top_k-th): redo that tile exactly, in rank order, into its list
+  for (int t = 0; t < S; ++t) {
+    if (tcnt[t] > cw) {
+      const T* row = row_ptr<T>(p, grow);
+      const int start = t * p.L, end = min(start + p.L, p.V);
+      int n;
+      float m;
+      tile_topk_rounds<T>(p, row, start, end, (end - start + kVec - 1) / kVec, grow * S + t, surv,
+                          reinterpret_cast<unsigned short*>(surv + kTopkCap), &n, &m);
+      if (tid == 0) { tcnt[t] = n; ttau[t] = m; }
+      __syncthreads();
+    }
+  }
+  if (tid < 64) {
+    float tt = tid < S ? ttau[tid] : -INFINITY;
+    tt = wave_max(tt);
+    if (tid == 0) sh_tau = tt;
+  }
+  __syncthreads();
   float tau = sh_tau;
   for (int t0 = 0; t0 < S; t0 += kUnroll) {
     uint64_t key[kUnroll];
@@ -1341,16 +1595,32 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
     if (ns > kMergeCap - kUnroll * kBlock && t0 + kUnroll < S) {
       // cut the list back to its top_k and raise the threshold
       const int c = ns;
-      rank_top(surv, c, K, [&](int r, uint64_t k2) { top[r] = k2; });
-      for (int i = tid; i < K; i += kBlock) surv[i] = top[i];
-      if (tid == 0) ns = c < K ? c : K;
+      const int n = block_keep_top(surv, c, K, top, hist, shv, &cnt2);
+      uint64_t mn = ~0ull;
+      for (int i = tid; i < n; i += kBlock) { surv[i] = top[i]; mn = top[i] < mn ? top[i] : mn; }
+      mn = wave_min_t(mn);
+      if ((tid & 63) == 0) redu[tid >> 6] = mn;
+      if (tid == 0) ns = n;
       __syncthreads();
-      if (c >= K) tau = fmaxf(tau, packed_val(surv[K - 1]));
+      if (c >= K) {
+        const uint64_t kth = min(min(redu[0], redu[1]), min(redu[2], redu[3]));
+        tau = fmaxf(tau, packed_val(kth));
+      }
+      __syncthreads();
     }
   }
-  const int tot = ns;
-  rank_top(surv, tot, K, [&](int r, uint64_t k2) { top[r] = k2; });
-  const int n = tot < K ? tot : K;
+  // the top_k of the survivors, then their ranks by counting
+  const int n = block_keep_top(surv, ns, K, top, hist, shv, &cnt2);
+  {
+    const uint64_t key = tid < n ? top[tid] : 0ull;
+    int r = 0;
+    for (int j = 0; j < n; ++j) r += top[j] > key;
+    __syncthreads();
+    if (tid < n) surv[r] = key;
+    __syncthreads();
+    if (tid < n) top[tid] = surv[tid];
+    __syncthreads();
+  }
   const float v0 = n > 0 ? packed_val(top[0]) : -INFINITY;
   const bool bad = probe || (v0 != v0) || (v0 == INFINITY) || (v0 == -INFINITY);
   const double invT = 1.0 / p.T;
@@ -1698,6 +1968,8 @@ __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
   if constexpr (MODE == kModeTopk) {
     __shared__ uint64_t lds[kTopkLds];
     tile_topk<T>(p, row, start, end, ngroups, tile, lds);
+  } else if constexpr (MODE == kModeTopkFilter) {
+    tile_topk_filter<T, kFilterGroups / (int)sizeof(T)>(p, row, start, end, tile);
   } else if constexpr (MODE == kModeStats64) {
     tile_stats<T>(p, row, start, end, grow, seg);
   } else {
@@ -2074,6 +2346,7 @@ static int capacity_t(int mode) {
   hipError_t e;
   if (mode == kModeStats64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeStats64>, kBlock, 0);
   else if (mode == kModeTopk) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopk>, kBlock, 0);
+  else if (mode == kModeTopkFilter) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopkFilter>, kBlock, 0);
   else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeArgmax>, kBlock, 0);
   return e == hipSuccess ? per_cu : 0;
 }
@@ -2093,6 +2366,8 @@ static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hip
     hipExtLaunchKernelGGL((k_stream<T, kModeStats64>), dim3(grid), block, 0, st, e0, e1, 0, p);
   else if (mode == kModeTopk)
     hipExtLaunchKernelGGL((k_stream<T, kModeTopk>), dim3(grid), block, 0, st, e0, e1, 0, p);
+  else if (mode == kModeTopkFilter)
+    hipExtLaunchKernelGGL((k_stream<T, kModeTopkFilter>), dim3(grid), block, 0, st, e0, e1, 0, p);
   else
     hipExtLaunchKernelGGL((k_stream<T, kModeArgmax>), dim3(grid), block, 0, st, e0, e1, 0, p);
   return hipGetLastError();
