@@ -55,7 +55,7 @@ Plan make_plan(const sv_config* c) {
   else if (c->mode == SV_MODE_TREE_GREEDY) { p.filt = sv::kFiltTree; p.tile_mode = sv::kModeArgmax; }
   else if (p.top_k > 0) { p.filt = sv::kFiltTopk; p.tile_mode = sv::kModeTopk; }
   else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeStats64; }
-  else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats64; }
+  else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats32; }
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
   // most tiles per row of the list passes at any batch size (see the tiling

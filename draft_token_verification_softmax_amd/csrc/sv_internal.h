@@ -69,8 +69,9 @@ struct SeqState {
 
 // Passes of the streaming kernel: argmax (greedy, tree), top-k lists (exact
 // per tile: any tile shape; certified filter: tiles of one round of loads in
-// aligned rows), max + sum of exponentials (plain and nucleus sampling).
-enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4 };
+// aligned rows), max + sum of exponentials (float64 terms for nucleus rows,
+// float32 terms for plain sampling).
+enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4, kModeStats32 = 5 };
 enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4 };
 
 struct Params {

@@ -235,30 +235,72 @@ DEV void load_iter(const T* row, int start, int end, int ngroups, int nfull, int
 // f(groups, first index, n valid) gets the lane's U group slots (slot u
 // holds group first + u * kBlock and is valid iff u < n valid).  Other tiles
 // assemble one group per lane at a time element by element, padded with
-// -inf (f gets U = 1).
+// -inf (f gets U = 1).  Every lane of the block runs every round (lanes past
+// the tile get no valid slot), so f may use wave-wide operations.
 template <typename T, int U, typename F>
 DEV void tile_groups(const T* row, int start, int end, int aligned, F&& f) {
   const int ngroups = (end - start + kVec - 1) / kVec;
   const int nfull = (end - start) / kVec;
   if (aligned && nfull == ngroups && nfull > 0) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, (end - start) * (int)sizeof(T));
-    for (int g0 = threadIdx.x; g0 < ngroups; g0 += U * kBlock) {
+    for (int base = 0; base < ngroups; base += U * kBlock) {
+      const int g0 = base + threadIdx.x;
       Group<T> gr[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
         gr[u].load_buf(rs, g0 * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
-      const int nv = (ngroups - g0 + kBlock - 1) / kBlock;
+      const int nv = g0 < ngroups ? (ngroups - g0 + kBlock - 1) / kBlock : 0;
       f(gr, g0, nv);
     }
   } else {
-    for (int g = threadIdx.x; g < ngroups; g += kBlock) {
+    for (int base = 0; base < ngroups; base += kBlock) {
+      const int g = base + threadIdx.x;
       Group<T> gr[1];
       const int pos = start + g * kVec;
-      const int n = min(kVec, end - pos);
+      const int n = g < ngroups ? min(kVec, end - pos) : 0;
       if (aligned && n == kVec) gr[0].load(row + pos);
       else gr[0].load_part(row + pos, n);
-      f(gr, g, 1);
+      f(gr, g, g < ngroups ? 1 : 0);
     }
+  }
+}
+
+// tile_groups for long ranges (many rounds), as one workgroup's sweep of a
+// whole row: the next round's loads are issued before the current round is
+// consumed (two sets of U groups in registers), and the rounds start at
+// round `rot` (mod the round count) and wrap around.  Many workgroups that
+// sweep equally strided rows in step would otherwise hit the same memory
+// channels at the same time; a different rotation per row spreads them.
+// Same contract for f as tile_groups (in rotated round order).
+template <typename T, int U, typename F>
+DEV void tile_groups_pipe(const T* row, int start, int end, int aligned, int rot, F&& f) {
+  const int ngroups = (end - start + kVec - 1) / kVec;
+  const int nfull = (end - start) / kVec;
+  if (!(aligned && nfull == ngroups && nfull > 0)) {
+    tile_groups<T, U>(row, start, end, aligned, f);
+    return;
+  }
+  constexpr int R = U * kBlock;                 // groups per round
+  const int nr = (ngroups + R - 1) / R;
+  rot = rot % nr;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, (end - start) * (int)sizeof(T));
+  Group<T> cur[U], nxt[U];
+  int g0 = rot * R + (int)threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < U; ++u) cur[u].load_buf(rs, g0 * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
+  for (int j = 0; j < nr; ++j) {
+    int r2 = rot + j + 1;
+    if (r2 >= nr) r2 -= nr;
+    const int g1 = r2 * R + (int)threadIdx.x;
+    if (j + 1 < nr) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) nxt[u].load_buf(rs, g1 * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
+    }
+    const int nv = g0 < ngroups ? (ngroups - g0 + kBlock - 1) / kBlock : 0;
+    f(cur, g0, nv < U ? nv : U);
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+    g0 = g1;
   }
 }
 
@@ -572,10 +614,10 @@ DEV int trow(const Params& p, int b, int j) { return b * p.rows_t + j; }
 DEV int drow(const Params& p, int b, int j) { return p.B * p.rows_t + b * p.rows_d + j; }
 
 // Combine the partials of rows 0..nrows-1 (global row ids row_of(r)).  A
-// segment of W lanes (W = ceil(P / kLanePartials) rounded up to a power of
-// two) takes one row; lane s holds the kLanePartials consecutive partials
-// from s * kLanePartials, combines them in registers, and butterflies over
-// xor offsets < W (at most four steps) finish the row.  Every partial load
+// segment of W lanes (W = ceil(P / Q) rounded up to a power of two, Q =
+// kLanePartials unless a kernel short of registers asks for fewer) takes one
+// row; lane s holds the Q consecutive partials from s * Q, combines them in
+// registers, and butterflies over xor offsets < W finish the row.  Every partial load
 // is issued before any is used, unconditionally (a slot with no partial
 // reads partial 0 of the workspace and is cleared: a load under a branch
 // would be waited for before the branch joins).  The order of every
@@ -586,9 +628,8 @@ DEV int drow(const Params& p, int b, int j) { return p.B * p.rows_t + b * p.rows
 //   bad   the row holds NaN or +inf, or no finite value
 constexpr int kLanePartials = 16;
 
-template <bool STATS, typename RowOf, typename Sink>
+template <bool STATS, int Q = kLanePartials, typename RowOf, typename Sink>
 DEV void combine_rows(const Params& p, int nrows, RowOf row_of, Sink sink) {
-  constexpr int Q = kLanePartials;
   const int P = p.P;
   int lw = 0;
   while ((Q << lw) < P) ++lw;
@@ -705,18 +746,24 @@ DEV void record_token_logit(const Params& p, const T* row, int grow, int start, 
 // Max and sum of exp((l - max) / T) = 2^((l - max) c), c = log2(e) / T, over
 // the logits each wave of a tile reads (one partial per wave).  Per lane:
 // each round of groups first raises the lane max m over them (rescaling the
-// lane sum, in float64, if it rose), then adds 2^((l - m) c) of every logit
-// with the hardware float32 exp2 (relative error below 1e-7).  The exponent
-// is (l - m) * c with c split into two floats (c_hi + c_lo carries c to
-// about 48 bits), so the only float32 roundings per term are the difference,
-// the product and exp2 itself; eight terms are summed in float32 (a fixed
-// tree), groups in float64.  The wave combines its lanes in float64 by one
-// fixed butterfly.  The relative error of a partial sum is a few float32
-// roundings, about 1e-7.
-template <typename T>
+// lane sum, in float64, if it rose), then adds 2^((l - m) c) of every logit.
+//   EXACT = false (plain sampling): the hardware float32 exp2 (relative
+//   error below 1e-7) of (l - m) * c with c split into two floats (c_hi +
+//   c_lo carries c to about 48 bits), so the only float32 roundings per
+//   term are the difference, the product and exp2 itself; eight terms are
+//   summed in float32 (a fixed tree), groups in float64.  The relative error
+//   of a sum is a few float32 roundings (about 1e-7 at worst, far less on
+//   average over many terms).
+//   EXACT = true (nucleus rows, whose cut is a discontinuous function of the
+//   row sum): every term in float64 (exp2_64, a few ulp).
+// The wave combines its lanes in float64 by one fixed butterfly.
+template <typename T, bool EXACT>
 DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow, int seg) {
+  __shared__ double tab[64];
   if (threadIdx.x == 0) record_token_logit<T>(p, row, grow, start, end);
+  if (EXACT) exp2_table_init(tab);
   const double cd = kLog2e / p.T;
+  const double c64 = 64.0 * cd;
   const float c_hi = (float)cd;
   const float c_lo = (float)(cd - (double)c_hi);
   float m = -INFINITY;
@@ -740,16 +787,25 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
     if (m > -INFINITY) {
 #pragma unroll
       for (int u = 0; u < n; ++u) {
-        float v[kVec], e[kVec];
+        float v[kVec];
         gr[u].opaque().values(v);
+        if (EXACT) {
+          const double nmc = -(double)m * c64;
+          double gs = 0.0;
 #pragma unroll
-        for (int q = 0; q < kVec; ++q) {
-          // -inf logits: clamp d so that d * c_lo cannot be +inf (c_lo < 0)
-          const float d = fmaxf(v[q] - m, -FLT_MAX);
-          e[q] = __builtin_amdgcn_exp2f(fmaf(d, c_hi, d * c_lo));
+          for (int q = 0; q < kVec; ++q) gs += exp2_64(fma((double)v[q], c64, nmc), tab);
+          s += u < nv ? gs : 0.0;
+        } else {
+          float e[kVec];
+#pragma unroll
+          for (int q = 0; q < kVec; ++q) {
+            // -inf logits: clamp d so that d * c_lo cannot be +inf (c_lo < 0)
+            const float d = fmaxf(v[q] - m, -FLT_MAX);
+            e[q] = __builtin_amdgcn_exp2f(fmaf(d, c_hi, d * c_lo));
+          }
+          const float gs = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
+          s += u < nv ? (double)gs : 0.0;
         }
-        const float gs = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
-        s += u < nv ? (double)gs : 0.0;
       }
     }
   });
@@ -1971,7 +2027,9 @@ __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
   } else if constexpr (MODE == kModeTopkFilter) {
     tile_topk_filter<T, kFilterGroups / (int)sizeof(T)>(p, row, start, end, tile);
   } else if constexpr (MODE == kModeStats64) {
-    tile_stats<T>(p, row, start, end, grow, seg);
+    tile_stats<T, true>(p, row, start, end, grow, seg);
+  } else if constexpr (MODE == kModeStats32) {
+    tile_stats<T, false>(p, row, start, end, grow, seg);
   } else {
     tile_argmax<T>(p, row, start, end, grow, seg);
   }
@@ -2310,11 +2368,213 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
   out.ok = result == 1 ? 1 : 2;
 }
 
+// Fast exact nucleus cut of one valid row; returns false (and leaves *out
+// alone) when it cannot settle the row, which then takes topp_search.
+// d = fmaf(l, -1/T, M/T) in float32 (monotone in l, so bins follow the rank
+// order) over [0, dmax) with dmax = ln(V / ((1 - top_p) Z)) + 1 (every
+// kept logit lies below it), kFastBins bins.
+//  pass 1: a float32 histogram of exp(-d) (hardware exp2, one LDS float
+//          atomic per binned logit).  Its masses only locate the bin where
+//          the mass from the top reaches top_p Z; the window is that bin and
+//          its two neighbours.
+//  pass 2: the exact float64 mass A of every logit binned above the window
+//          (exp in float64 through a per-wave queue, per-lane sums in a
+//          fixed order, fixed block reduction), and the window's logits
+//          gathered as packed keys.
+// The window is sorted in rank order and walked from A exactly as in
+// topp_search.  A window that overflows, or a cut that falls outside it
+// (the float32 masses misplaced it), returns false.
+constexpr int kFastBins = 4096;
+constexpr int kNucPipe = 8;   // bytes per logit times groups per lane per round of the row sweeps (bf16 4, fp32 2)
+static_assert(kFastBins * 4 <= kNucBins * 8, "the fast nucleus histogram fits in the exact one's");
+
+template <typename T>
+DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* outp, float* hist,
+                   uint64_t* win, float* aq, double* red, int* redi, int* wcnt_p, int rot) {
+  int& wcnt = *wcnt_p;
+  const int V = p.V, tid = threadIdx.x;
+  const double invT = 1.0 / p.T;
+  const float zm32 = (float)((double)Mrow * invT);
+  const float nit32 = (float)(-invT);
+  double dmaxd = log((double)V / ((1.0 - p.top_p) * Z)) + 1.0;
+  if (!(dmaxd > 1.0)) dmaxd = 1.0;
+  const float dmax = (float)dmaxd;
+  const float invw = (float)((double)kFastBins / dmaxd);
+  const double tgt = p.top_p * Z;
+  const double zm = (double)Mrow * invT;
+  auto bin_of = [&](float d) {
+    const int b = (int)(d * invw);
+    return b < 0 ? 0 : (b >= kFastBins ? kFastBins - 1 : b);
+  };
+  for (int b = tid; b < kFastBins; b += kBlock) hist[b] = 0.f;
+  __syncthreads();
+  // pass 1
+  tile_groups_pipe<T, kNucPipe / (int)sizeof(T)>(row, 0, V, p.aligned, rot, [&](const auto& gr, int, int nv) {
+    constexpr int n = sizeof(gr) / sizeof(gr[0]);
+#pragma unroll
+    for (int u = 0; u < n; ++u) {
+      float v[kVec];
+      gr[u].values(v);
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const float d = fmaf(v[e], nit32, zm32);
+        if (u < nv && d < dmax) atomicAdd(&hist[bin_of(d)], __builtin_amdgcn_exp2f(-d * 1.4426950408889634f));
+      }
+    }
+  });
+  __syncthreads();
+  // the bin where the (float32) mass from the top reaches top_p Z
+  int bc;
+  {
+    constexpr int per = kFastBins / kBlock;
+    double local[per];
+    double ts = 0.0;
+#pragma unroll
+    for (int q = 0; q < per; ++q) { local[q] = (double)hist[tid * per + q]; ts += local[q]; }
+    double tot;
+    const double ex = block_exscan(ts, red, &tot);
+    double c = ex;   // bin masses are exp(-d): the same units as Z
+    int found = INT_MAX;
+#pragma unroll
+    for (int q = 0; q < per; ++q) {
+      c += local[q];
+      if (found == INT_MAX && c >= tgt) found = tid * per + q;
+    }
+    int none = -1;
+    block_minmax(found, none, redi);
+    bc = found != INT_MAX ? found : kFastBins - 1;
+  }
+  const int lo = bc > 0 ? bc - 1 : 0;
+  const int hi = bc < kFastBins - 1 ? bc + 1 : kFastBins - 1;
+  // pass 2.  The logits above the window are queued per wave in LDS (ballot
+  // and prefix count, no divergent float64 work); every 64 queued ones, each
+  // lane adds the float64 exponential of one.  Each lane's sum follows the
+  // queue order, which is fixed, so A is reproducible.
+  if (tid == 0) wcnt = 0;
+  __syncthreads();
+  const int lane = tid & 63;
+  float* q = aq + (tid >> 6) * 128;
+  int qn = 0;
+  double above = 0.0;
+  tile_groups_pipe<T, kNucPipe / (int)sizeof(T)>(row, 0, V, p.aligned, rot, [&](const auto& gr, int g0, int nv) {
+    constexpr int n = sizeof(gr) / sizeof(gr[0]);
+#pragma unroll
+    for (int u = 0; u < n; ++u) {
+      float v[kVec];
+      gr[u].opaque().values(v);
+      unsigned msk = 0u;
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        const float d = fmaf(v[e], nit32, zm32);
+        const bool in = u < nv && d < dmax;
+        const int b = bin_of(d);
+        const bool ab = in && b < lo;
+        if (in && b >= lo && b <= hi) msk |= 1u << e;
+        const uint64_t m = __ballot(ab);
+        if (m) {
+          if (ab) q[qn + __popcll(m & ((1ull << lane) - 1ull))] = v[e];
+          qn += __popcll(m);
+          if (qn >= 64) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            above += exp2_neg(((double)q[lane] * invT - zm) * kLog2e);
+            const float rest = lane < qn - 64 ? q[64 + lane] : 0.f;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            if (lane < qn - 64) q[lane] = rest;
+            qn -= 64;
+          }
+        }
+      }
+      if (__any(msk != 0u)) {
+        int slot = wave_reserve(__popc(msk), &wcnt);
+        const int i0 = (g0 + u * kBlock) * kVec;
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          if ((msk >> e) & 1u) {
+            if (slot < kWindowCap) win[slot] = pack(v[e], i0 + e);
+            ++slot;
+          }
+        }
+      }
+    }
+  });
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (lane < qn) above += exp2_neg(((double)q[lane] * invT - zm) * kLog2e);
+  const double A = block_sum(above, red);
+  const int nw = wcnt;
+  if (nw > kWindowCap || nw == 0) return false;
+  const int P2 = next_pow2(nw);
+  for (int i = nw + tid; i < P2; i += kBlock) win[i] = 0ull;
+  bitonic_desc(win, P2);
+  // exclusive float64 prefix of e in rank order, from A
+  const int per = (nw + kBlock - 1) / kBlock;
+  double tl = 0.0;
+  for (int q = 0; q < per; ++q) {
+    const int i = tid * per + q;
+    if (i < nw) tl += exp2_neg(((double)packed_val(win[i]) * invT - zm) * kLog2e);
+  }
+  double tot;
+  const double ex = block_exscan(tl, red, &tot);
+  double c = A + ex;
+  int kept_local = 0;
+  double mass_local = 0.0;
+  for (int q = 0; q < per; ++q) {
+    const int i = tid * per + q;
+    if (i < nw) {
+      const double e = exp2_neg(((double)packed_val(win[i]) * invT - zm) * kLog2e);
+      if (c < tgt) { kept_local = i + 1; mass_local = c + e; }
+      c += e;
+    }
+  }
+  const int kept = block_max_i(kept_local, redi);
+  // the cut must fall inside the window: some entry kept, and not every one
+  // unless the window reaches the end of the kept range
+  const bool inside = kept > 0 && (kept < nw || A + tot >= tgt);
+  if (!inside) return false;
+  __syncthreads();
+  if (tid == (kept - 1) / per) red[0] = mass_local;
+  __syncthreads();
+  outp->N = red[0];
+  outp->cut = win[kept - 1];
+  outp->ok = 1;
+  __syncthreads();
+  return true;
+}
+
+// Nucleus cut per row: topp_fast; a row it cannot settle is left with ok =
+// kNucRetry for k_topp_rows_exact.
+constexpr int kNucRetry = 3;
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   const int grow = blockIdx.x;
   const T* row = row_ptr<T>(p, grow);
+  __shared__ float hist[kFastBins];
+  __shared__ uint64_t win[kWindowCap];
+  __shared__ float aq[kWaves * 128];
+  __shared__ double red[kWaves];
+  __shared__ int redi[2 * kWaves];
+  __shared__ int wcnt;
+  __shared__ float sh_M;
+  __shared__ double sh_Z;
+  __shared__ int sh_bad;
+  auto sink = [&](int, float M, int, double Z, int bad) { sh_M = M; sh_Z = Z; sh_bad = bad; };
+  combine_rows<true, 4>(p, 1, [grow](int) { return grow; }, sink);
+  __syncthreads();
+  RowNuc out;
+  out.Z = sh_Z; out.N = 0.0; out.cut = 0ull; out.ok = 0; out.M = sh_M;
+  if (!sh_bad && !topp_fast<T>(p, row, out.M, out.Z, &out, hist, win, aq, red, redi, &wcnt, grow * 7))
+    out.ok = kNucRetry;
+  if (threadIdx.x == 0) p.nuc[grow] = out;
+}
 
+// The multi-level exact search for the rows k_topp_rows left to it (rare);
+// every other workgroup returns at once.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_topp_rows_exact(Params p) {
+  const int grow = blockIdx.x;
+  RowNuc out = p.nuc[grow];
+  if (out.ok != kNucRetry) return;
+  const T* row = row_ptr<T>(p, grow);
   __shared__ unsigned long long hq[kNucBins];
   __shared__ unsigned int hc[kNucBins];
   __shared__ uint64_t win[kWindowCap];
@@ -2322,18 +2582,8 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   __shared__ unsigned long long redu[2 * kWaves];
   __shared__ int redi[2 * kWaves];
   __shared__ int wcnt;
-  __shared__ float sh_M;
-  __shared__ double sh_Z;
-  __shared__ int sh_bad;
-
-  combine_rows<true>(p, 1, [&](int) { return grow; }, [&](int, float M, int, double Z, int bad) {
-    sh_M = M; sh_Z = Z; sh_bad = bad;
-  });
-  __syncthreads();
-  RowNuc out;
-  out.Z = sh_Z; out.N = 0.0; out.cut = 0ull; out.ok = 0; out.M = sh_M;
-  if (!sh_bad)
-    topp_search<T>(p, row, out.M, out.Z, &out, hq, hc, win, red, redu, redi, &wcnt);
+  out.N = 0.0; out.cut = 0ull; out.ok = 0;
+  topp_search<T>(p, row, out.M, out.Z, &out, hq, hc, win, red, redu, redi, &wcnt);
   if (threadIdx.x == 0) p.nuc[grow] = out;
 }
 
@@ -2345,6 +2595,7 @@ static int capacity_t(int mode) {
   int per_cu = 0;
   hipError_t e;
   if (mode == kModeStats64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeStats64>, kBlock, 0);
+  else if (mode == kModeStats32) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeStats32>, kBlock, 0);
   else if (mode == kModeTopk) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopk>, kBlock, 0);
   else if (mode == kModeTopkFilter) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopkFilter>, kBlock, 0);
   else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeArgmax>, kBlock, 0);
@@ -2364,6 +2615,8 @@ static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hip
   const dim3 block(kBlock);
   if (mode == kModeStats64)
     hipExtLaunchKernelGGL((k_stream<T, kModeStats64>), dim3(grid), block, 0, st, e0, e1, 0, p);
+  else if (mode == kModeStats32)
+    hipExtLaunchKernelGGL((k_stream<T, kModeStats32>), dim3(grid), block, 0, st, e0, e1, 0, p);
   else if (mode == kModeTopk)
     hipExtLaunchKernelGGL((k_stream<T, kModeTopk>), dim3(grid), block, 0, st, e0, e1, 0, p);
   else if (mode == kModeTopkFilter)
@@ -2386,6 +2639,7 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
       break;
     case kFiltTopp:
       hipLaunchKernelGGL((k_topp_rows<T>), gr, block, 0, st, p);
+      hipLaunchKernelGGL((k_topp_rows_exact<T>), gr, block, 0, st, p);
       hipLaunchKernelGGL((k_resid_s<T, kFiltTopp>), gs, block, 0, st, p);
       hipLaunchKernelGGL((k_resid_final<T, kFiltTopp>), gs, block, 0, st, p);
       break;
