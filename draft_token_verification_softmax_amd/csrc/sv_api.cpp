@@ -290,7 +290,7 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.L = (per + sv::kVec - 1) / sv::kVec * sv::kVec;
   p.S = (c->vocab + p.L - 1) / p.L;
   const bool lists = tile_mode == sv::kModeTopk || tile_mode == sv::kModeTopkFilter;
-  p.P = lists ? p.S : p.S * (sv::kBlock / 64);
+  p.P = tile_mode == sv::kModeTopk ? p.S : p.S * (sv::kBlock / 64);
   // the workspace holds S_max candidate lists and kMaxPartials partials per row
   if ((lists && p.S > pl.S_max) || p.P > sv::kMaxPartials || p.S > sv::kMaxTiles) return SV_ERR_SHAPE;
   p.grid = ctx->grid;

@@ -18,8 +18,8 @@ constexpr int kResidSeg = kBlock * kVec;  // logits per workgroup in the residua
 constexpr int kMaxTiles = 64;          // tiles per row
 constexpr int kMaxPartials = 256;      // partials per row (one wave combines a row's partials)
 // logits per tile of the top-k filter pass for bf16 (one round of loads:
-// eight 16-byte groups per lane); fp32 tiles hold half as many
-constexpr int kFilterRound = 8 * kBlock * kVec;
+// sixteen 16-byte groups per lane); fp32 tiles hold half as many
+constexpr int kFilterRound = 16 * kBlock * kVec;
 
 // Partial result of the streaming pass over a part of a row: the logits one
 // wave of a tile read (argmax and sum passes), or a whole tile (top-k pass).

@@ -883,7 +883,7 @@ DEV void tile_topk_rounds(const Params& p, const T* row, int start, int end, int
   const float m = c >= K ? packed_val(buf[K - 1]) : -INFINITY;   // the tile's top_k-th
   uint64_t* out = p.cand + (size_t)tile * p.cand_w;
   for (int i = tid; i < c; i += kBlock) out[i] = buf[i];
-  if (tid == 0) {
+  if (tid == 0 && !n_out) {   // the row merge's redo keeps the result to itself
     TileStat ts;
     ts.m = m;
     ts.amax = c;
@@ -1127,22 +1127,22 @@ DEV int wave_exclusive_small(int c, int* total) {
 // lane; whole groups, 16-byte aligned row).  Every lane reduces its groups
 // to a lane max.  Each wave finds the r1-th largest of its 64 lane maxima
 // (r1 = max(16, ceil(top_k / 4))) by a radix select and publishes r1 lane
-// maxima at or above it; wave 0 then takes the top_k-th largest, tau, of
-// those 4 r1 values.  They are maxima of distinct lanes, so at least top_k
-// logits of the tile are >= tau: tau bounds the tile's top_k-th logit from
-// below (lanes with no logit hold -inf, which can only make tau -inf: then
-// the whole tile is listed).  bf16 keys need only their top 16 bits.  Every
-// logit >= tau goes to the tile's list, unordered, at a slot from a
-// ballot-sliced wave prefix and one LDS atomic per wave.  m = tau, amax =
-// list length (above cand_w: overflow; the row merge then redoes the tile
-// exactly).
+// maxima at or above it; after the tile's one barrier every wave takes the
+// top_k-th largest, tau, of those 4 r1 values (the same in every wave).
+// They are maxima of distinct lanes, so at least top_k logits of the tile
+// are >= tau: tau bounds the tile's top_k-th logit from below (lanes with no
+// logit hold -inf, which can only make tau -inf: then the whole tile is
+// listed).  bf16 keys need only their top 16 bits.  Each wave lists its
+// logits >= tau, unordered, in its own kWaveList slots of the tile's list
+// (slot from a ballot-sliced prefix count), and writes its own partial: m =
+// tau, amax = its count (above kWaveList: overflow; the row merge then
+// redoes the tile exactly), s = NaN if its logits hold a NaN or +inf.
+constexpr int kWaveList = kCandSlots / kWaves;
+
 template <typename T, int U>
-DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int tile) {
+DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int grow, int seg) {
   constexpr int BITS = sizeof(T) == 2 ? 16 : 32;
   __shared__ uint32_t pub[kBlock];
-  __shared__ uint32_t sh_tau;
-  __shared__ int cnt;
-  __shared__ int redb[kWaves];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int K = p.top_k;
   const int r1 = max(16, (K + kWaves - 1) / kWaves);
@@ -1151,7 +1151,6 @@ DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int
   Group<T> gr[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) gr[u].load_buf(rs, tid * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
-  if (tid == 0) cnt = 0;
   float gm[U];
   float lm = -INFINITY;
   uint64_t nanm = 0;
@@ -1164,6 +1163,7 @@ DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int
     gm[u] = (tid + u * kBlock < ngroups && g == g) ? g : -INFINITY;
     lm = fmaxf(lm, gm[u]);
   }
+  const bool bad = nanm != 0ull || __ballot(lm == INFINITY) != 0ull;
   // each wave publishes r1 of its largest lane maxima
   {
     const uint32_t key[1] = {ord_key(lm)};
@@ -1172,20 +1172,16 @@ DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int
     const uint64_t msk = __ballot(sel);
     const int pos = __popcll(msk & ((1ull << lane) - 1ull));
     if (sel && pos < r1) pub[w * r1 + pos] = key[0];
-    if (lane == 0) redb[w] = nanm != 0ull || __ballot(lm == INFINITY) != 0ull;
   }
   __syncthreads();
-  if (w == 0) {
+  float tau;
+  {
     uint32_t k4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) { const int i = lane + 64 * q; k4[q] = i < kWaves * r1 ? pub[i] : 0u; }
-    const uint32_t tk = wave_kth_key<4, BITS>(k4, K);
-    if (lane == 0) sh_tau = tk;
+    tau = key_value(wave_kth_key<4, BITS>(k4, K));
   }
-  __syncthreads();
-  const float tau = key_value(sh_tau);
-  const bool bad = redb[0] | redb[1] | redb[2] | redb[3];
-  // the lane's logits >= tau: count, wave prefix, one LDS atomic per wave
+  // the wave's logits >= tau into its own sublist
   int c = 0;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -1197,11 +1193,9 @@ DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int
     }
   }
   int total;
-  const int ex = wave_exclusive_small(c, &total);
-  int base = 0;
-  if (lane == 0 && total > 0) base = atomicAdd(&cnt, total);
-  int slot = __shfl(base, 0) + ex;
-  uint64_t* out = p.cand + (size_t)tile * p.cand_w;
+  int slot = wave_exclusive_small(c, &total);
+  const size_t tile = (size_t)grow * p.S + seg;
+  uint64_t* out = p.cand + tile * p.cand_w + w * kWaveList;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (tid + u * kBlock < ngroups && gm[u] >= tau) {
@@ -1211,19 +1205,18 @@ DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
         if (v[e] >= tau) {
-          if (slot < p.cand_w) out[slot] = pack(v[e], pos + e);
+          if (slot < kWaveList) out[slot] = pack(v[e], pos + e);
           ++slot;
         }
       }
     }
   }
-  __syncthreads();
-  if (tid == 0) {
+  if (lane == 0) {
     TileStat ts;
     ts.m = tau;
-    ts.amax = cnt;
+    ts.amax = total;
     ts.s = bad ? (double)NAN : 0.0;
-    p.tiles[tile] = ts;
+    p.tiles[(size_t)grow * p.P + seg * kWaves + w] = ts;
   }
 }
 
@@ -1583,6 +1576,7 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
   __shared__ uint64_t top[kTopkMax];
   __shared__ int tcnt[kMaxTiles];
   __shared__ float ttau[kMaxTiles];
+  __shared__ int wcnt4[kMaxTiles * kWaves];
   __shared__ unsigned hist[256];
   __shared__ int shv[3];
   __shared__ int cnt2;
@@ -1602,9 +1596,20 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
   if (grow < nt) { b = grow / p.rows_t; j = grow - b * p.rows_t; if (j >= p.k) j = -1; }
   else { b = (grow - nt) / p.rows_d; j = (grow - nt) - b * p.rows_d; }
   const int x = (j >= 0) ? p.tokens[(size_t)b * p.k + j] : -1;
-  // tile lengths, taus and probes (S <= 64)
+  // tile lengths, taus and probes (S <= 64).  Filter tiles (P = 4 S) keep
+  // one sublist of kWaveList slots per wave, with counts in wcnt4 (255 =
+  // overflow) and tcnt[t] = 0; an exact tile (P = S), or a filter tile
+  // redone here, has one list of tcnt[t] entries.
+  const bool sub = p.P != S;
   int pr = 0;
-  if (tid < S) {
+  if (sub) {
+    for (int i = tid; i < p.P; i += kBlock) {
+      const TileStat ts = p.tiles[(size_t)grow * p.P + i];
+      pr |= ts.s != ts.s;
+      if ((i & (kWaves - 1)) == 0) ttau[i / kWaves] = ts.m;
+      wcnt4[i] = ts.amax > kWaveList ? 255 : ts.amax;
+    }
+  } else if (tid < S) {
     const TileStat ts = p.tiles[(size_t)grow * S + tid];
     tcnt[tid] = ts.amax;
     ttau[tid] = ts.m;
@@ -1613,6 +1618,12 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
   if (tid < kTopkMax) top[tid] = 0ull;
   if (tid == 0) { sh_px = 0.0; ns = 0; }
   const int probe = __syncthreads_or(pr);
+  if (sub && tid < S) {
+    int ov = 0;
+    for (int q = 0; q < kWaves; ++q) ov |= wcnt4[tid * kWaves + q] == 255;
+    tcnt[tid] = ov ? cw + 1 : 0;   // 0: sublists; cw + 1: redo
+  }
+  __syncthreads();
   // a filter list that overflowed (rare: many logits tie near the tile's
   // top_k-th): redo that tile exactly, in rank order, into its list
   for (int t = 0; t < S; ++t) {
@@ -1624,6 +1635,7 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
       tile_topk_rounds<T>(p, row, start, end, (end - start + kVec - 1) / kVec, grow * S + t, surv,
                           reinterpret_cast<unsigned short*>(surv + kTopkCap), &n, &m);
       if (tid == 0) { tcnt[t] = n; ttau[t] = m; }
+      if (sub && tid < kWaves) wcnt4[t * kWaves + tid] = 0;   // now one list of n
       __syncthreads();
     }
   }
@@ -1639,7 +1651,15 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int t = t0 + u;
-      key[u] = (t < S && tid < tcnt[t]) ? src[(size_t)t * cw + tid] : 0ull;
+      // slot tid of tile t: sublist tid / kWaveList, entry tid % kWaveList
+      // (sublists), or entry tid of one list
+      bool has = false;
+      if (t < S) {
+        has = tid < tcnt[t];
+        if (sub && tcnt[t] == 0) has = (tid % kWaveList) < wcnt4[t * kWaves + tid / kWaveList];
+      }
+      key[u] = src[has ? (size_t)t * cw + tid : 0];
+      if (!has) key[u] = 0ull;
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -2025,7 +2045,7 @@ __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
     __shared__ uint64_t lds[kTopkLds];
     tile_topk<T>(p, row, start, end, ngroups, tile, lds);
   } else if constexpr (MODE == kModeTopkFilter) {
-    tile_topk_filter<T, kFilterGroups / (int)sizeof(T)>(p, row, start, end, tile);
+    tile_topk_filter<T, kFilterGroups / (int)sizeof(T)>(p, row, start, end, grow, seg);
   } else if constexpr (MODE == kModeStats64) {
     tile_stats<T, true>(p, row, start, end, grow, seg);
   } else if constexpr (MODE == kModeStats32) {
