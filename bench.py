@@ -108,13 +108,39 @@ KERNEL_SOURCES = [os.path.join(ROOT, "draft_token_verification_softmax_amd", "cs
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stream_traffic.md")
 
 
+def source_code(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed: what the
+    compiler sees, so a comment edit does not count as a kernel change."""
+    import re
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                               # string / char literal
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return re.sub(r"\s+", " ", "".join(out)).strip()
+
+
 def kernel_digest():
-    """sha256 of the kernel sources (the traffic counters are only valid for them)."""
+    """sha256 of the kernel sources' code (comments and whitespace removed);
+    the traffic counters are only valid for it."""
     import hashlib
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(source_code(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

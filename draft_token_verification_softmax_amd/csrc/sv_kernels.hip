@@ -3,30 +3,36 @@
 // One call is a short chain of launches on the caller's stream, with no host
 // synchronisation and no cross-workgroup signalling inside a launch:
 //   k_stream        the one pass over every logit the mode reads: one
-//                   workgroup per tile of a row (16-byte non-temporal loads,
-//                   four groups in flight per lane) leaves a small partial
-//                   per tile in the workspace:
-//                     ARGMAX   max + lowest index       (greedy, tree)
-//                     STATS64  max + float64 sum of exp((l - max) / T)
-//                                                         (plain and nucleus sampling)
-//                     TOPK     the tile's top_k           (top-k sampling)
-//                   Every tile also records, exactly, whether it holds a NaN
-//                   or +inf, so no row is ever scanned a second time for that.
+//                   workgroup per tile of a row (one round of 16-byte
+//                   non-temporal buffer loads per lane), leaving small
+//                   partials in the workspace:
+//                     ARGMAX   max + lowest index, per wave   (greedy, tree)
+//                     STATS32  max + sum of exp((l - max) / T), per wave,
+//                              float32 exp2 terms       (plain sampling)
+//                     STATS64  the same with float64 terms (nucleus rows)
+//                     TOPK     a certified filter: every logit above a
+//                              lower bound of the tile's top_k-th, per wave
+//                              (aligned rows); or the tile's exact top_k
+//                              (other shapes)             (top-k sampling)
+//                   Every part also records, exactly, whether it holds a
+//                   NaN or +inf, so no row is ever scanned a second time
+//                   for that.
 //   greedy / tree   k_greedy_final / k_tree_final: one workgroup per sequence
 //   top-k           k_topk_rows (merge per row) -> k_topk_final (per sequence)
-//   nucleus         k_topp_rows (exact cut per row) -> k_resid_s -> k_resid_final
+//   nucleus         k_topp_rows (exact cut per row) -> k_topp_rows_exact
+//                   (rows it could not settle) -> k_resid_s -> k_resid_final
 //   plain sampling  k_resid_s (accept step + residual mass per segment)
 //                   -> k_resid_final (draw; one workgroup per segment)
 //
 // The finishing kernels are latency-bound: each one is written as a few
-// rounds of independent loads (tile partials are combined by lane segments of
-// one wave, all rows of a sequence at once) rather than chains of dependent
-// loads.
+// rounds of independent loads (partials are combined in registers first,
+// all rows of a sequence at once) rather than chains of dependent loads.
 //
-// Every reduction that feeds an output is a fixed-order butterfly / tree, so
-// repeated calls give bit-identical results.  Float64 carries every quantity
-// that decides an integer output (row sums, accept test, nucleus cut,
-// inverse CDF).
+// Every reduction that feeds an output has a fixed order, so repeated calls
+// give bit-identical results.  Float64 carries every quantity that decides
+// an integer output (accept test, nucleus cut, inverse CDF, nucleus row
+// sums); plain-sampling row sums use float32 exp2 terms summed in float64
+// (relative error about 1e-7).
 
 #include <float.h>
 #include <limits.h>
