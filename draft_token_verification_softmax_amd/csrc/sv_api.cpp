@@ -14,6 +14,7 @@ constexpr int kMinTile = 8192;        // top-k pass: logits per tile, lower boun
 constexpr int kRound = 4 * sv::kBlock * sv::kVec;   // argmax / sum passes: logits per round of loads
 constexpr int kMinSmall = 2048;       // argmax / sum / filter passes: smallest tile of small problems
 constexpr int kSmallTiles = 256;      // problems with fewer tiles than this take smaller tiles
+constexpr size_t kKeepBytes = 32u << 20;   // residual weights kept for the draw up to this size
 
 struct Plan {
   int filt;        // sv::Filter
@@ -78,7 +79,7 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, row_lx, seq, spart;
+  size_t tiles, cand, nuc, row_lx, seq, spart, wpart;
   size_t k_idx, k_e, k_cnt, k_norm, k_bad, k_px, total;
 };
 
@@ -100,6 +101,8 @@ Layout layout(const sv_config* c, const Plan& pl) {
   L.row_lx = take(sampled ? rows * sizeof(float) : 0);
   L.seq = take(sampled ? B * sizeof(sv::SeqState) : 0);
   L.spart = take(sampled ? B * (size_t)pl.S2_max * sizeof(double) : 0);
+  const bool keep = sampled && B * (size_t)pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes;
+  L.wpart = take(keep ? B * (size_t)pl.S2_max * sv::kResidSeg * sizeof(double) : 0);
   L.k_idx = take(rows * K * sizeof(int32_t));
   L.k_e = take(rows * K * sizeof(double));
   L.k_cnt = take(K ? rows * sizeof(int32_t) : 0);
@@ -306,6 +309,9 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.row_lx = (float*)(ws + L.row_lx);
   p.seq = (sv::SeqState*)(ws + L.seq);
   p.spart = (double*)(ws + L.spart);
+  p.wpart = (double*)(ws + L.wpart);
+  p.keep_w = (pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp) &&
+             (size_t)c->max_batch * pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes ? 1 : 0;
   p.S2 = pl.S2_max;
   p.k_idx = (int32_t*)(ws + L.k_idx);
   p.k_e = (double*)(ws + L.k_e);

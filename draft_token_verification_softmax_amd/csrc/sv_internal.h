@@ -116,6 +116,9 @@ struct Params {
   // sampling: state handed from k_resid_s to k_resid_final
   SeqState* seq;     // [B]
   double* spart;     // [B][S2] residual-mass partials
+  double* wpart;     // [B][S2][kResidSeg] residual weights of each segment (keep_w)
+  int keep_w;        // small problem: k_resid_s keeps its weights for
+                     // k_resid_final (loaded in its first round, no recompute)
   int S2;            // residual segments per sequence (kResidSeg logits each)
   // top-k: each row's kept set, rank order
   int32_t* k_idx;    // [rows][top_k]

@@ -60,6 +60,7 @@ constexpr int kMaxRows = 2 * 64 + 1;
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+typedef double d2 __attribute__((ext_vector_type(2)));
 
 template <typename T> struct Io;
 template <> struct Io<float> {
@@ -1281,15 +1282,12 @@ DEV double prob_from(const RowView& r, double c64, const double* tab, float l, i
 
 // Residual weights of the kVec entries [pos, pos + kVec) of one chunk:
 // w = max(0, p'(v) - q'(v)), or p'(v) without q.  Returns their sum.
-template <typename T>
-DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double c64,
-                         const double* tab, int V, int aligned, int pos, double w[kVec]) {
-  float lp[kVec], lq[kVec];
-  int n = 0;
-  if (pos < V) {
-    n = load_group<T>((const T*)pr.row, pos, V, aligned, lp);
-    if (hasq) load_group<T>((const T*)qr.row, pos, V, aligned, lq);
-  }
+// Residual weights of kVec entries from their logits (lp: target row n,
+// lq: draft row n; n valid entries): w = max(0, p'(v) - q'(v)), or p'(v)
+// without q.  Returns their sum.
+DEV double resid_weights_of(const RowView& pr, const RowView& qr, bool hasq, double c64,
+                            const double* tab, int pos, int n, const float lp[kVec],
+                            const float lq[kVec], double w[kVec]) {
   double t = 0.0;
 #pragma unroll
   for (int q = 0; q < kVec; ++q) {
@@ -1305,6 +1303,19 @@ DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double
     t += wq;
   }
   return t;
+}
+
+// The same for the kVec entries [pos, pos + kVec) loaded from the rows.
+template <typename T>
+DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double c64,
+                         const double* tab, int V, int aligned, int pos, double w[kVec]) {
+  float lp[kVec], lq[kVec];
+  int n = 0;
+  if (pos < V) {
+    n = load_group<T>((const T*)pr.row, pos, V, aligned, lp);
+    if (hasq) load_group<T>((const T*)qr.row, pos, V, aligned, lq);
+  }
+  return resid_weights_of(pr, qr, hasq, c64, tab, pos, n, lp, lq, w);
 }
 
 // One chunk of kResidSeg entries of the residual draw: thread t owns
@@ -1871,24 +1882,30 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   const int k = p.k, V = p.V, nrows = p.rows_t + p.rows_d;
   const double c64 = 64.0 * kLog2e / p.T;
   auto row_of = [&](int r) { return r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t); };
-  // one round of loads: drafted tokens, uniforms, the drafted tokens' logits
-  // (recorded by the streaming pass) and the row views
-  int xj = 0;
-  float uj = 0.f;
-  if (tid < k) { xj = p.tokens[(size_t)b * k + tid]; uj = p.u[(size_t)b * k + tid]; }
-  for (int r = tid; r < nrows; r += kBlock) vlx[r] = p.row_lx[row_of(r)];
+  // one round of loads, all unconditional (clamped indices): drafted
+  // tokens, uniforms, the drafted tokens' logits (recorded by the streaming
+  // pass) and the row views (nrows <= kMaxRows < kBlock: one row per thread)
+  const int ti = tid < k ? tid : 0, ri = tid < nrows ? tid : 0;
+  const int xj_l = p.tokens[(size_t)b * k + ti];
+  const float uj_l = p.u[(size_t)b * k + ti];
+  const float lx = p.row_lx[row_of(ri)];
+  const int pos0 = seg * kResidSeg + tid * kVec;
   int internal = 0;
   if constexpr (FILT == kFiltTopp) {
-    for (int r = tid; r < nrows; r += kBlock) {
-      const RowNuc nu = p.nuc[row_of(r)];
-      vnmc[r] = -(double)nu.M * c64; vinv[r] = 1.0 / nu.N; vcut[r] = nu.cut; vbad[r] = nu.ok != 1;
-      internal |= nu.ok == 2;
+    const RowNuc nu = p.nuc[row_of(ri)];
+    if (tid < nrows) {
+      vnmc[tid] = -(double)nu.M * c64; vinv[tid] = 1.0 / nu.N; vcut[tid] = nu.cut; vbad[tid] = nu.ok != 1;
+      internal = nu.ok == 2;
     }
   } else {
-    combine_rows<true>(p, nrows, row_of, [&](int r, float M, int, double Z, int bad) {
+    // four partials per lane: short float64 chains for this latency-bound kernel
+    combine_rows<true, 4>(p, nrows, row_of, [&](int r, float M, int, double Z, int bad) {
       vnmc[r] = -(double)M * c64; vinv[r] = 1.0 / Z; vcut[r] = 0ull; vbad[r] = bad;
     });
   }
+  if (tid < nrows) vlx[tid] = lx;
+  const int xj = tid < k ? xj_l : 0;
+  const float uj = tid < k ? uj_l : 0.f;
   exp2_table_init(tab);
   int mybad = 0;
   for (int r = tid; r < nrows; r += kBlock) mybad |= vbad[r];
@@ -1926,7 +1943,13 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
     qr = RowView{row_ptr<T>(p, drow(p, b, n)), vnmc[rd], vinv[rd], vcut[rd]};
   }
   double w[kVec];
-  const double t = resid_weights<T>(pr, qr, n < k, c64, tab, V, p.aligned, seg * kResidSeg + tid * kVec, w);
+  const double t = resid_weights<T>(pr, qr, n < k, c64, tab, V, p.aligned, pos0, w);
+  // small problems: the weights themselves, for k_resid_final
+  if (p.keep_w) {
+    d2* wp = reinterpret_cast<d2*>(p.wpart + ((size_t)b * p.S2 + seg) * kResidSeg + tid * kVec);
+#pragma unroll
+    for (int q = 0; q < kVec / 2; ++q) wp[q] = d2{w[2 * q], w[2 * q + 1]};
+  }
   const double tot = block_sum(t, red);
   if (tid == 0) {
     p.spart[(size_t)b * p.S2 + seg] = tot;
@@ -1940,52 +1963,69 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   }
 }
 
-constexpr int kSegStage = 1024;   // residual segment masses staged in LDS
+constexpr int kSegStage = 1024;   // residual segment masses held in registers (per sequence)
 
 template <typename T, int FILT>
 __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   __shared__ double red[kWaves];
   __shared__ double tab[64];
-  __shared__ double spl[kSegStage];
   __shared__ int sx[64];
   __shared__ int redi[2 * kWaves];
   __shared__ double sh_base;
+  constexpr int kPer = kSegStage / kBlock;   // segment masses per thread
   const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int S2 = p.S2, V = p.V, k = p.k;
   const double c64 = 64.0 * kLog2e / p.T;
-  // one round of loads: sequence state, segment masses, ur, drafted tokens
+  // one round of loads, all unconditional: sequence state, ur, the segment
+  // masses this thread owns ([tid*per, (tid+1)*per)), drafted tokens, and
+  // this workgroup's own segment weights (written by k_resid_s)
   const SeqState ss = p.seq[b];
   const double ur = (double)p.ur[b];
   const double* spg = p.spart + (size_t)b * S2;
-  const bool staged = S2 <= kSegStage;
-  if (staged) for (int s = tid; s < S2; s += kBlock) spl[s] = spg[s];
-  if (tid < k) sx[tid] = p.tokens[(size_t)b * k + tid];
-  exp2_table_init(tab);
-  if (ss.n < 0) return;
-  auto sp = [&](int s) { return staged ? spl[s] : spg[s]; };
-  const int n = ss.n;
-  const RowView pr{row_ptr<T>(p, trow(p, b, n)), ss.nmc_p, ss.inv_p, ss.cut_p};
-  const RowView qr{n < k ? row_ptr<T>(p, drow(p, b, n)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
-  // S' = sum of the segment masses; thread t owns segments [t*per, (t+1)*per)
   const int per = (S2 + kBlock - 1) / kBlock;
+  double sm[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int s2 = tid * per + q;
+    const bool ok = q < per && s2 < S2;
+    sm[q] = spg[ok ? s2 : 0];
+    if (!ok) sm[q] = 0.0;
+  }
+  const int xl = p.tokens[(size_t)b * k + (tid < k ? tid : 0)];
+  double w[kVec];
+  if (p.keep_w) {
+    const d2* wp = reinterpret_cast<const d2*>(p.wpart + ((size_t)b * S2 + seg) * kResidSeg + tid * kVec);
+#pragma unroll
+    for (int q = 0; q < kVec / 2; ++q) { const d2 x = wp[q]; w[2 * q] = x.x; w[2 * q + 1] = x.y; }
+  }
+  if (tid < k) sx[tid] = xl;
+  if (ss.n < 0) return;
+  const int n = ss.n;
+  // S' = sum of the segment masses (a thread owning more than kPer reads
+  // the rest from global memory: vocabularies above kSegStage * kResidSeg)
   double lsum = 0.0;
-  for (int q = 0; q < per; ++q) { const int s = tid * per + q; if (s < S2) lsum += sp(s); }
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) lsum += sm[q];
+  for (int q = kPer; q < per; ++q) { const int s2 = tid * per + q; if (s2 < S2) lsum += spg[s2]; }
   double S;
   const double ex0 = block_exscan(lsum, red, &S);
   if (!(S > 0.0)) {
     // empty residual: p'_n, drawn and written by one workgroup
     if (seg != 0) return;
+    exp2_table_init(tab);
+    const RowView pr{row_ptr<T>(p, trow(p, b, n)), ss.nmc_p, ss.inv_p, ss.cut_p};
+    const RowView none{nullptr, 0.0, 1.0, 0ull};
     double S1;
     const int y = resid_draw<T>(pr, c64, tab, V, p.aligned, ur, red, redi, &S1);
     if (p.resid_probs) {
       float* rp = p.resid_probs + (size_t)b * V;
       for (int c0 = 0; c0 < V; c0 += kResidSeg) {
-        double w[kVec];
-        resid_weights<T>(pr, qr, false, c64, tab, V, p.aligned, c0 + tid * kVec, w);
+        double w1[kVec];
+        resid_weights<T>(pr, none, false, c64, tab, V, p.aligned, c0 + tid * kVec, w1);
 #pragma unroll
         for (int q = 0; q < kVec; ++q) {
           const int v = c0 + tid * kVec + q;
-          if (v < V) rp[v] = (float)(w[q] / S1);
+          if (v < V) rp[v] = (float)(w1[q] / S1);
         }
       }
     }
@@ -1997,30 +2037,51 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   int cross = INT_MAX, lastpos = -1;
   {
     double run = ex0;
-    for (int q = 0; q < per; ++q) {
-      const int s = tid * per + q;
-      if (s >= S2) break;
-      const double ps = sp(s);
-      if (ps > 0.0) lastpos = s;
-      if (cross == INT_MAX && run + ps > t) cross = s;
-      run += ps;
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) {
+      const int s2 = tid * per + q;
+      if (q < per && s2 < S2) {
+        if (sm[q] > 0.0) lastpos = s2;
+        if (cross == INT_MAX && run + sm[q] > t) cross = s2;
+        run += sm[q];
+      }
+    }
+    for (int q = kPer; q < per; ++q) {
+      const int s2 = tid * per + q;
+      if (s2 < S2) {
+        const double ps = spg[s2];
+        if (ps > 0.0) lastpos = s2;
+        if (cross == INT_MAX && run + ps > t) cross = s2;
+        run += ps;
+      }
     }
   }
   block_minmax(cross, lastpos, redi);
   const int c = cross != INT_MAX ? cross : lastpos;
   if (tid == c / per) {
     double run = ex0;
-    for (int s = tid * per; s < c; ++s) run += sp(s);
+#pragma unroll
+    for (int q = 0; q < kPer; ++q) if (q < per && tid * per + q < c) run += sm[q];
+    for (int q = kPer; q < per && tid * per + q < c; ++q) run += spg[tid * per + q];
     sh_base = run;
   }
   if (seg != c && !p.resid_probs) return;
   __syncthreads();
   const double base = sh_base;
-  double w[kVec];
-  double tc;
   const int c0 = seg * kResidSeg;
-  const double ex = resid_chunk<T>(pr, qr, n < k, c64, tab, V, p.aligned, c0, w, red, &tc);
+  if (!p.keep_w) {
+    // large problems: recompute this segment's weights
+    exp2_table_init(tab);
+    const RowView pr{row_ptr<T>(p, trow(p, b, n)), ss.nmc_p, ss.inv_p, ss.cut_p};
+    const RowView qr{n < k ? row_ptr<T>(p, drow(p, b, n)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
+    resid_weights<T>(pr, qr, n < k, c64, tab, V, p.aligned, c0 + tid * kVec, w);
+  }
   if (seg == c) {
+    double tl = 0.0;
+#pragma unroll
+    for (int q = 0; q < kVec; ++q) tl += w[q];
+    double tc;
+    const double ex = block_exscan(tl, red, &tc);
     const int y = pick_in_chunk(base, ex, w, c0, t, redi);
     emit_tokens(p, b, sx, n, y, ss.st);
   }
