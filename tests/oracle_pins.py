@@ -433,3 +433,103 @@ ALL_ORACLE_PINS = [
     pin_topp_minimal, pin_inverse_cdf_golden, pin_enumeration, pin_special_cases,
     pin_residual_properties, pin_flags,
 ]
+
+
+# ---------------------------------------------------------------- acceptance statistics, tree mask, commit map
+
+def _frac(x):
+    return None if x is None else x[0] / x[1]
+
+
+def pin_aux_golden(ax):
+    g = _load("aux.json")
+    for c in g["stats"]:
+        r = ax.accept_stats(c["n"], c["k"], c["c"], c["status"])
+        for key in ("accepted", "drafted", "tested", "sequences"):
+            assert r[key] == c[key], (c["name"], key, r[key])
+        for key in ("acceptance", "mal", "tokens_per_step", "alpha", "expected_tokens"):
+            if c[key] is not None:
+                assert abs(r[key] - _frac(c[key])) <= 1e-15, (c["name"], key, r[key])
+    for c in g["masks"]:
+        if "chain" in c:
+            m, d = ax.tree_attention_mask([-1] + list(range(c["chain"] - 1)))
+            assert [int(w) for w in m[c["row"]]] == c["words"] and int(d[c["row"]]) == c["depth_last"], c["name"]
+        else:
+            m, d = ax.tree_attention_mask(c["parents"])
+            assert [[int(w) for w in row] for row in m] == c["rows"], (c["name"], m)
+            assert [int(x) for x in d] == c["depth"], (c["name"], d)
+    for c in g["commits"]:
+        pos = ax.tree_commit_map(c["path"], c["n"], c["N"])
+        assert [int(x) for x in pos] == c["pos"], (c["name"], pos)
+
+
+def _random_tree(rng, N, bad=False):
+    par = [-1]
+    for i in range(1, N):
+        par.append(int(rng.integers(0, i)))
+    if bad and N > 3:
+        par[int(rng.integers(2, N))] = N + 5          # out of range: that node and its subtree unreachable
+    return par
+
+
+def pin_mask_recursion(ax):
+    """Row i = row(parent i) with bit i added, for every reachable node; the
+    row of a node has depth + 1 bits; siblings never see each other; an
+    unreachable node sees only itself."""
+    rng = np.random.default_rng(123)
+    for t in range(60):
+        N = int(rng.integers(1, 90))
+        par = _random_tree(rng, N, bad=(t % 4 == 3))
+        m, d = ax.tree_attention_mask(par)
+        bits = lambda i: {j for j in range(N) if (int(m[i, j // 32]) >> (j % 32)) & 1}
+        for i in range(N):
+            bi = bits(i)
+            if d[i] < 0:
+                assert bi == {i}, (par, i)
+                continue
+            assert len(bi) == d[i] + 1, (par, i)
+            if i == 0:
+                assert bi == {0}
+            else:
+                assert d[par[i]] >= 0 and bi == bits(par[i]) | {i}, (par, i)
+                for s in range(1, N):
+                    if s != i and par[s] == par[i]:
+                        assert s not in bi, (par, i, s)
+
+
+def pin_commit_inverse(ax):
+    """The commit map inverts the accepted path: path node d goes to d, the
+    other nodes collapse."""
+    rng = np.random.default_rng(7)
+    for _ in range(40):
+        N = int(rng.integers(2, 50))
+        par = _random_tree(rng, N)
+        leaf = int(rng.integers(0, N))
+        path = [leaf]
+        while path[-1] != 0:
+            path.append(par[path[-1]])
+        path.reverse()
+        pos = ax.tree_commit_map(path, len(path) - 1, N)
+        assert sorted(int(x) for x in pos if x >= 0) == list(range(len(path)))
+        for d, node in enumerate(path):
+            assert pos[node] == d
+        assert int((pos < 0).sum()) == N - len(path)
+
+
+def pin_alpha_recovery(ax, calc):
+    """Sequences drawn from the calculator's own model (each tested draft
+    accepted independently with probability alpha, stop at the first
+    rejection, at most k): the measured alpha recovers alpha within 4
+    standard errors, and mean tokens per step matches E(alpha, k)."""
+    rng = np.random.default_rng(2024)
+    for alpha, k in ((0.3, 3), (0.7, 5), (0.9, 8)):
+        S = 200000
+        u = rng.random((S, k))
+        fail = u >= alpha
+        n = np.where(fail.any(axis=1), fail.argmax(axis=1), k)
+        r = ax.accept_stats(n, k, 0.05)
+        se = math.sqrt(alpha * (1 - alpha) / r["tested"])
+        assert abs(r["alpha"] - alpha) < 4 * se, (alpha, k, r["alpha"])
+        tps_se = float(np.std(n + 1)) / math.sqrt(S)
+        assert abs(r["tokens_per_step"] - calc.expected_tokens_closed(alpha, k)) < 4 * tps_se, (alpha, k)
+        assert abs(r["expected_tokens"] - calc.expected_tokens_closed(r["alpha"], k)) < 1e-15

@@ -22,3 +22,22 @@ def test_constant_alpha_matches_calculator():
 
 def test_calculator():
     pins.pin_calculator(calc)
+
+
+import oracle.aux as ax
+
+
+def test_aux_golden():
+    pins.pin_aux_golden(ax)
+
+
+def test_tree_mask_recursion():
+    pins.pin_mask_recursion(ax)
+
+
+def test_commit_map_inverts_the_path():
+    pins.pin_commit_inverse(ax)
+
+
+def test_measured_alpha_recovers_the_model():
+    pins.pin_alpha_recovery(ax, calc)

@@ -95,3 +95,43 @@ def test_calculator_mutant_is_caught(name, old, new):
     mod = _load_mutant(CALC_SRC, old, new, name)
     with pytest.raises(Exception):
         pins.pin_calculator(mod)
+
+
+import oracle.aux as aux_real
+
+AUX_SRC = open(aux_real.__file__).read()
+AUX_MUTANTS = [
+    ("tested counts only the accepted", "tested = int(np.minimum(n + 1, k).sum())", "tested = int(n.sum())"),
+    ("tested ignores the cap at k", "tested = int(np.minimum(n + 1, k).sum())", "tested = int((n + 1).sum())"),
+    ("acceptance over tested tokens", '"acceptance": accepted / drafted if drafted else 0.0',
+     '"acceptance": accepted / tested if tested else 0.0'),
+    ("MAL counts the correction token", '"mal": accepted / seqs if seqs else 0.0',
+     '"mal": (accepted + seqs) / seqs if seqs else 0.0'),
+    ("bad-logits sequences kept", "keep = (np.asarray(seq_status) & STATUS_BAD_LOGITS) == 0",
+     "keep = np.ones(n.shape, dtype=bool)"),
+    ("mask row misses the node itself", "        chain = [i]\n", "        chain = []\n"),
+    ("mask stops below the root", "        while j != 0:", "        while parents[j] != 0 and j != 0:"),
+    ("depth counts the node itself", "            depth.append(len(chain) - 1)", "            depth.append(len(chain))"),
+    ("commit positions off by one", "        pos[int(path_nodes[d])] = d", "        pos[int(path_nodes[d])] = d + 1"),
+    ("commit drops the last path node", "    for d in range(int(n) + 1):", "    for d in range(int(n)):"),
+]
+
+
+def _load_aux_mutant(old, new, name):
+    assert AUX_SRC.count(old) == 1, ("mutation site not unique", old)
+    mod = types.ModuleType("oracle.mutant_aux_" + name.replace(" ", "_"))
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(AUX_SRC.replace(old, new), mod.__name__, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", AUX_MUTANTS, ids=[m[0] for m in AUX_MUTANTS])
+def test_aux_mutant_is_caught(name, old, new):
+    mod = _load_aux_mutant(old, new, name)
+    for pin in (pins.pin_aux_golden, pins.pin_mask_recursion, pins.pin_commit_inverse,
+                lambda m: pins.pin_alpha_recovery(m, calc)):
+        try:
+            pin(mod)
+        except Exception:
+            return
+    pytest.fail("mutant survived every pin: " + name)
