@@ -38,7 +38,9 @@ Readings (numbered as in DESIGN.md):
        and its depth is -1.  Node 0 is the root whatever parents[0] holds (the
        verification flags a root parent other than -1).
   R23  commit map: node i of the accepted root-to-d* path moves to position
-       depth(i) (root 0); every other node collapses (-1).
+       depth(i) (root 0); every other node collapses (-1).  A sequence that
+       emitted nothing (n outside [0, N) or a path node outside [0, N))
+       commits nothing.
 
 Parity status: pinned by hand-worked examples (tests/golden/aux.json), the
 mask recursion and popcount invariants, brute-force ancestor enumeration,
@@ -132,8 +134,11 @@ def tree_attention_mask(parents):
 def tree_commit_map(path_nodes, n: int, N: int):
     """R23: commit_pos[i] = position of node i on the accepted path (the
     root at 0, the node at depth d at d) for the n + 1 path nodes; -1 for
-    every node that collapses."""
+    every node that collapses.  An n outside [0, N), or a path node outside
+    [0, N) (a sequence that emitted nothing), commits nothing."""
     pos = np.full(N, -1, dtype=np.int32)
+    if not (0 <= int(n) < N) or any(not (0 <= int(path_nodes[d]) < N) for d in range(int(n) + 1)):
+        return pos
     for d in range(int(n) + 1):
         pos[int(path_nodes[d])] = d
     return pos
