@@ -348,6 +348,42 @@ def main():
                      "call_bytes_algorithmic": alg_bytes,
                      "call_GBps": alg_bytes / (call_ms * 1e-3) / 1e9},
     }
+    # the kernels around the step, on this workload's outputs: acceptance
+    # statistics (every mode); tree attention mask and commit map (tree)
+    extras = {}
+
+    def time_launches(fn, reps=100):
+        e = hip.create(2)
+        fn()
+        torch.cuda.synchronize()
+        hip.hip.hipEventRecord(ctypes.c_void_p(e[0]), ctypes.c_void_p(stream))
+        for _ in range(reps):
+            fn()
+        hip.hip.hipEventRecord(ctypes.c_void_p(e[1]), ctypes.c_void_p(stream))
+        torch.cuda.synchronize()
+        us = hip.elapsed_ms(e[0], e[1]) * 1e3 / reps
+        hip.destroy(e)
+        return us
+
+    kk = k if cfg["kind"] != "tree" else cfg["max_depth"]
+    stats_out = torch.empty(svm.SV_STATS_LEN, dtype=torch.float64, device=dev)
+    extras["accept_stats_us"] = time_launches(
+        lambda: svm.specverify_accept_stats(acc, status, B, kk, 0.1, stats_out, stream))
+    st = stats_out.cpu().numpy()
+    extras["acceptance"] = float(st[svm.SV_STATS_ACCEPTANCE])
+    extras["mal"] = float(st[svm.SV_STATS_MAL])
+    extras["alpha"] = float(st[svm.SV_STATS_ALPHA])
+    if cfg["kind"] == "tree":
+        mask = torch.empty(B, N, (N + 31) // 32, dtype=torch.int32, device=dev)
+        depth = torch.empty(B, N, dtype=torch.int32, device=dev)
+        pos = torch.empty(B, N, dtype=torch.int32, device=dev)
+        extras["tree_mask_us"] = time_launches(
+            lambda: svm.specverify_tree_mask(inputs["parents"], B, N, mask, depth, stream))
+        extras["tree_commit_us"] = time_launches(
+            lambda: svm.specverify_tree_commit(out_nodes, acc, B, N, pos, stream))
+    extras["note"] = ("mean per launch by HIP events over 100 back-to-back launches on the call's "
+                      "stream; acceptance statistics of the last timed call (draft cost c = 0.1)")
+    result["extras"] = extras
     sv.close()
     if not args.no_cpu:
         log("CPU baseline (oracle)")

@@ -28,7 +28,14 @@ SV_MAX_K, SV_MAX_TREE_NODES, SV_MAX_TOP_K, SV_MAX_VOCAB = 64, 1024, 256, 1 << 24
 
 EXPORTED = ("specverify_create", "specverify_check_args", "specverify_run",
             "specverify_destroy", "specverify_profile_events", "specverify_status_string",
-            "specverify_workspace_bytes")
+            "specverify_workspace_bytes", "specverify_accept_stats", "specverify_tree_mask",
+            "specverify_tree_commit")
+
+# Slots of specverify_accept_stats' output (SV_STATS_* of the header).
+SV_STATS_SEQUENCES, SV_STATS_ACCEPTED, SV_STATS_DRAFTED, SV_STATS_TESTED = 0, 1, 2, 3
+SV_STATS_ACCEPTANCE, SV_STATS_MAL, SV_STATS_TOKENS_PER_STEP, SV_STATS_ALPHA = 4, 5, 6, 7
+SV_STATS_EXPECTED_TOKENS, SV_STATS_GAMMA_BEST, SV_STATS_SPEEDUP_BEST = 8, 9, 10
+SV_STATS_SPEEDUP_GAMMA1, SV_STATS_LEN = 11, 23
 
 
 class sv_config(ctypes.Structure):
@@ -71,6 +78,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_status_string.restype = ctypes.c_char_p
     lib.specverify_workspace_bytes.argtypes = [P(sv_config)]
     lib.specverify_workspace_bytes.restype = ctypes.c_size_t
+    lib.specverify_accept_stats.argtypes = [vp, vp, i32, i32, ctypes.c_double, vp, vp]
+    lib.specverify_accept_stats.restype = ctypes.c_int
+    lib.specverify_tree_mask.argtypes = [vp, i32, i32, vp, vp, vp]
+    lib.specverify_tree_mask.restype = ctypes.c_int
+    lib.specverify_tree_commit.argtypes = [vp, vp, i32, i32, vp, vp]
+    lib.specverify_tree_commit.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -145,6 +158,65 @@ def specverify_profile_events(ctx: int, ev_begin, ev_end) -> None:
 def specverify_destroy(ctx) -> None:
     if ctx:
         load().specverify_destroy(ctypes.c_void_p(ctx))
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
+
+
+def specverify_accept_stats(accepted_len, seq_status, batch, k, draft_cost, out, stream=None) -> None:
+    """out: SV_STATS_LEN float64 on the device (written)."""
+    st = load().specverify_accept_stats(_ptr(accepted_len), _ptr(seq_status), int(batch), int(k),
+                                        float(draft_cost), _ptr(out),
+                                        ctypes.c_void_p(_stream_handle(stream)))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "specverify_accept_stats")
+
+
+def specverify_tree_mask(parents, batch, nodes, mask, depth=None, stream=None) -> None:
+    """mask: [B, N, ceil(N/32)] uint32-sized (int32 tensor) written; depth: [B, N] int32 or None."""
+    st = load().specverify_tree_mask(_ptr(parents), int(batch), int(nodes), _ptr(mask), _ptr(depth),
+                                     ctypes.c_void_p(_stream_handle(stream)))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "specverify_tree_mask")
+
+
+def specverify_tree_commit(path_nodes, accepted_len, batch, nodes, commit_pos, stream=None) -> None:
+    st = load().specverify_tree_commit(_ptr(path_nodes), _ptr(accepted_len), int(batch), int(nodes),
+                                       _ptr(commit_pos), ctypes.c_void_p(_stream_handle(stream)))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "specverify_tree_commit")
+
+
+def accept_stats(accepted_len, k, draft_cost=0.0, seq_status=None, stream=None):
+    """Allocates the output and queues specverify_accept_stats; returns the
+    float64 tensor of SV_STATS_LEN values."""
+    import torch
+    out = torch.empty(SV_STATS_LEN, dtype=torch.float64, device=accepted_len.device)
+    specverify_accept_stats(accepted_len, seq_status, accepted_len.numel(), k, draft_cost, out, stream)
+    return out
+
+
+def tree_mask(parents, want_depth=True, stream=None):
+    """parents [B, N] int32 -> (mask [B, N, ceil(N/32)] int32 holding the uint32 words, depth [B, N])."""
+    import torch
+    B, N = parents.shape
+    mask = torch.empty(B, N, (N + 31) // 32, dtype=torch.int32, device=parents.device)
+    depth = torch.empty(B, N, dtype=torch.int32, device=parents.device) if want_depth else None
+    specverify_tree_mask(parents, B, N, mask, depth, stream)
+    return mask, depth
+
+
+def tree_commit(path_nodes, accepted_len, stream=None):
+    """out_nodes [B, N] and accepted_len [B] of a tree call -> commit_pos [B, N]."""
+    import torch
+    B, N = path_nodes.shape
+    pos = torch.empty(B, N, dtype=torch.int32, device=path_nodes.device)
+    specverify_tree_commit(path_nodes, accepted_len, B, N, pos, stream)
+    return pos
 
 
 # ------------------------------------------------------------------ convenience wrapper

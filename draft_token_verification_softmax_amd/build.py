@@ -2,7 +2,7 @@
 
     python -m draft_token_verification_softmax_amd.build
 
-Compiles csrc/sv_kernels.hip and csrc/sv_api.cpp with hipcc into
+Compiles csrc/sv_kernels.hip, csrc/sv_aux.hip and csrc/sv_api.cpp with hipcc into
 draft_token_verification_softmax_amd/libspecverify.so.  Packed-FP32 VALU
 instructions are disabled for the device code.
 """
@@ -29,7 +29,8 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    srcs = [os.path.join(CSRC, "sv_kernels.hip"), os.path.join(CSRC, "sv_api.cpp")]
+    srcs = [os.path.join(CSRC, "sv_kernels.hip"), os.path.join(CSRC, "sv_aux.hip"),
+            os.path.join(CSRC, "sv_api.cpp")]
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-shared",
            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

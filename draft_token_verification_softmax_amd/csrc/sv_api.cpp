@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include "specverify.h"
+#include "sv_aux.h"
 #include "sv_internal.h"
 
 namespace {
@@ -328,6 +329,39 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   hipError_t e = sv::launch_stream(p, tile_mode, bf16, st, ctx->ev_begin, ctx->ev_end);
   if (e == hipSuccess) e = sv::launch_finish(p, pl.filt, bf16, st);
   if (cur != ctx->device) (void)hipSetDevice(cur);
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+static_assert(SV_STATS_LEN == sv::kStatsLen && SV_STATS_SPEEDUP_GAMMA1 == sv::kStatsSpeedup1 &&
+                  SV_STATS_ALPHA == sv::kStatsAlpha && SV_STATS_GAMMA_BEST == sv::kStatsGammaBest,
+              "statistics layout");
+
+int specverify_accept_stats(const int32_t* accepted_len, const int32_t* seq_status, int32_t batch,
+                            int32_t k, double draft_cost, double* out, void* stream) {
+  if (!out || (batch > 0 && !accepted_len)) return SV_ERR_NULL;
+  if (batch < 0 || k < 1) return SV_ERR_SHAPE;
+  if (!(draft_cost >= 0.0) || !isfinite(draft_cost)) return SV_ERR_PARAM;
+  const hipError_t e = sv::launch_accept_stats(accepted_len, seq_status, batch, k, draft_cost, out,
+                                               (hipStream_t)stream);
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int specverify_tree_mask(const int32_t* parents, int32_t batch, int32_t nodes, uint32_t* mask,
+                         int32_t* depth, void* stream) {
+  if (batch < 0 || nodes < 1 || nodes > SV_MAX_TREE_NODES) return SV_ERR_SHAPE;
+  if (batch == 0) return SV_OK;
+  if (!parents || !mask) return SV_ERR_NULL;
+  const hipError_t e = sv::launch_tree_mask(parents, batch, nodes, mask, depth, (hipStream_t)stream);
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+int specverify_tree_commit(const int32_t* path_nodes, const int32_t* accepted_len, int32_t batch,
+                           int32_t nodes, int32_t* commit_pos, void* stream) {
+  if (batch < 0 || nodes < 1 || nodes > SV_MAX_TREE_NODES) return SV_ERR_SHAPE;
+  if (batch == 0) return SV_OK;
+  if (!path_nodes || !accepted_len || !commit_pos) return SV_ERR_NULL;
+  const hipError_t e = sv::launch_tree_commit(path_nodes, accepted_len, batch, nodes, commit_pos,
+                                              (hipStream_t)stream);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 

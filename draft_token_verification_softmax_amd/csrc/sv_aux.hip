@@ -1,0 +1,186 @@
+// gfx950 kernels around the verification step: acceptance statistics of a
+// batch with the speedup model fed by the measured acceptance, and the token
+// tree's attention mask and commit map.  All are small (latency-bound): one
+// workgroup per batch or per tree.
+
+#include <limits.h>
+#include <math.h>
+
+#include "sv_aux.h"
+
+namespace sv {
+
+#define DEV __device__ __forceinline__
+
+constexpr int kAuxBlock = 256;
+constexpr int kAuxWaves = kAuxBlock / 64;
+constexpr int kMaxNodes = 1024;
+constexpr int kBadLogits = 4;
+
+DEV long long wave_sum_ll(long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// E(alpha, gamma) = (1 - alpha^(gamma+1)) / (1 - alpha); gamma + 1 at alpha = 1.
+DEV double expected_tokens(double a, int g) {
+  if (a == 1.0) return (double)(g + 1);
+  return (1.0 - pow(a, (double)(g + 1))) / (1.0 - a);
+}
+
+// One workgroup: exact integer sums in a fixed order (per-thread strided
+// sums, wave butterflies, then the four waves in order); then wave 0 derives
+// the rates, lane g (1..12) the speedup at gamma = g and lane 13 E(alpha, k),
+// and the best gamma comes from a butterfly (smallest gamma on ties).
+__global__ __launch_bounds__(kAuxBlock) void k_accept_stats(const int32_t* __restrict__ acc,
+                                                            const int32_t* __restrict__ status,
+                                                            int batch, int k, double c, double* out) {
+  __shared__ long long red[3][kAuxWaves];
+  long long seqs = 0, accepted = 0, tested = 0;
+  for (int b = threadIdx.x; b < batch; b += kAuxBlock) {
+    const int n = acc[b];
+    const bool keep = !status || !(status[b] & kBadLogits);
+    if (keep) {
+      seqs += 1;
+      accepted += n;
+      tested += (n + 1 < k ? n + 1 : k);
+    }
+  }
+  seqs = wave_sum_ll(seqs);
+  accepted = wave_sum_ll(accepted);
+  tested = wave_sum_ll(tested);
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) { red[0][w] = seqs; red[1][w] = accepted; red[2][w] = tested; }
+  __syncthreads();
+  if (w != 0) return;
+  seqs = accepted = tested = 0;
+  for (int q = 0; q < kAuxWaves; ++q) { seqs += red[0][q]; accepted += red[1][q]; tested += red[2][q]; }
+  const long long drafted = seqs * (long long)k;
+  const double A = (double)accepted, S = (double)seqs, D = (double)drafted, Tt = (double)tested;
+  const double alpha = tested ? A / Tt : 0.0;
+  // lane g in 1..12: speedup at gamma = g
+  double s = -1.0;
+  int g = lane;
+  if (lane >= 1 && lane <= kGammaScan) {
+    s = expected_tokens(alpha, lane) / ((double)lane * c + 1.0);
+    out[kStatsSpeedup1 + lane - 1] = s;
+  }
+  if (lane == kGammaScan + 1) out[kStatsExpectedTokens] = expected_tokens(alpha, k);
+  if (lane == 0) {
+    out[kStatsSequences] = S;
+    out[kStatsAccepted] = A;
+    out[kStatsDrafted] = D;
+    out[kStatsTested] = Tt;
+    out[kStatsAcceptance] = drafted ? A / D : 0.0;
+    out[kStatsMal] = seqs ? A / S : 0.0;
+    out[kStatsTokensPerStep] = seqs ? (A + S) / S : 0.0;
+    out[kStatsAlpha] = alpha;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double s2 = __shfl_xor(s, o);
+    const int g2 = __shfl_xor(g, o);
+    if (s2 > s || (s2 == s && g2 < g)) { s = s2; g = g2; }
+  }
+  if (lane == 0) {
+    out[kStatsGammaBest] = (double)g;
+    out[kStatsSpeedupBest] = s;
+  }
+}
+
+// Validity and depth of every node of one tree by pointer jumping (parents
+// in LDS); then every node writes its row, walking its parent chain: the
+// ancestors come in decreasing index order, so the row's words are built
+// from the top word down and each is stored once.
+__global__ __launch_bounds__(kAuxBlock) void k_tree_mask(const int32_t* __restrict__ parents, int N,
+                                                         uint32_t* __restrict__ mask,
+                                                         int32_t* __restrict__ depth) {
+  __shared__ int spar[kMaxNodes];
+  __shared__ short jmp[2][kMaxNodes];
+  __shared__ short dep[2][kMaxNodes];
+  __shared__ unsigned char val[2][kMaxNodes];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int32_t* par = parents + (size_t)b * N;
+  const int W = (N + 31) / 32;
+  for (int i = tid; i < N; i += kAuxBlock) {
+    const int pi = par[i];
+    spar[i] = pi;
+    int ok, j, d;
+    if (i == 0) { ok = 1; j = -1; d = 0; }
+    else if (pi < 0 || pi >= i) { ok = 0; j = -1; d = 0; }
+    else { ok = 1; j = pi; d = 1; }
+    val[0][i] = (unsigned char)ok; jmp[0][i] = (short)j; dep[0][i] = (short)d;
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int span = 1; span < N; span <<= 1) {
+    for (int i = tid; i < N; i += kAuxBlock) {
+      const int j = jmp[cur][i];
+      if (j >= 0) {
+        val[cur ^ 1][i] = val[cur][i] & val[cur][j];
+        dep[cur ^ 1][i] = (short)(dep[cur][i] + dep[cur][j]);
+        jmp[cur ^ 1][i] = jmp[cur][j];
+      } else {
+        val[cur ^ 1][i] = val[cur][i];
+        dep[cur ^ 1][i] = dep[cur][i];
+        jmp[cur ^ 1][i] = -1;
+      }
+    }
+    cur ^= 1;
+    __syncthreads();
+  }
+  for (int i = tid; i < N; i += kAuxBlock) {
+    const bool ok = val[cur][i] != 0;
+    if (depth) depth[(size_t)b * N + i] = ok ? (int)dep[cur][i] : -1;
+    uint32_t* row = mask + ((size_t)b * N + i) * W;
+    int cw = W - 1;                 // next word to store (from the top down)
+    uint32_t acc = 0u;
+    auto add = [&](int j) {         // j decreasing
+      const int wj = j >> 5;
+      while (cw > wj) { row[cw] = acc; acc = 0u; --cw; }
+      acc |= 1u << (j & 31);
+    };
+    add(i);
+    if (ok) for (int j = i; j != 0;) { j = spar[j]; add(j); }
+    while (cw >= 0) { row[cw] = acc; acc = 0u; --cw; }
+  }
+}
+
+// Commit map of one tree: -1 everywhere, then the path nodes get their
+// depth; a sequence that emitted nothing commits nothing.
+__global__ __launch_bounds__(kAuxBlock) void k_tree_commit(const int32_t* __restrict__ path,
+                                                           const int32_t* __restrict__ acc, int N,
+                                                           int32_t* __restrict__ pos) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = acc[b];
+  const int32_t* pb = path + (size_t)b * N;
+  int32_t* ob = pos + (size_t)b * N;
+  int bad = !(n >= 0 && n < N);
+  for (int d = tid; d <= n && d < N; d += kAuxBlock) { const int v = pb[d]; bad |= !(v >= 0 && v < N); }
+  bad = __syncthreads_or(bad);
+  for (int i = tid; i < N; i += kAuxBlock) ob[i] = -1;
+  __syncthreads();
+  if (bad) return;
+  for (int d = tid; d <= n; d += kAuxBlock) ob[pb[d]] = d;
+}
+
+hipError_t launch_accept_stats(const int32_t* acc, const int32_t* status, int batch, int k, double c,
+                               double* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_accept_stats, dim3(1), dim3(kAuxBlock), 0, st, acc, status, batch, k, c, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_mask(const int32_t* parents, int batch, int N, uint32_t* mask, int32_t* depth,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_tree_mask, dim3(batch), dim3(kAuxBlock), 0, st, parents, N, mask, depth);
+  return hipGetLastError();
+}
+
+hipError_t launch_tree_commit(const int32_t* path, const int32_t* acc, int batch, int N, int32_t* pos,
+                              hipStream_t st) {
+  hipLaunchKernelGGL(k_tree_commit, dim3(batch), dim3(kAuxBlock), 0, st, path, acc, N, pos);
+  return hipGetLastError();
+}
+
+}  // namespace sv

@@ -171,6 +171,80 @@ const char* specverify_status_string(int status);
 /* Workspace bytes specverify_create would allocate for cfg (0 if cfg is invalid). */
 size_t specverify_workspace_bytes(const sv_config* cfg);
 
+/* ---------------------------------------------------------------------------
+ * Around the verification step: acceptance statistics, and the token tree's
+ * attention mask and commit map.  These need no context; they run on the
+ * current HIP device (the one that holds the buffers), asynchronously on
+ * `stream`, and allocate nothing.  Argument errors are found on the host
+ * before any HIP call (SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_PARAM); a launch
+ * failure is SV_ERR_HIP.  batch = 0 writes the statistics of an empty batch
+ * (specverify_accept_stats) or nothing (the tree functions).
+ * ------------------------------------------------------------------------- */
+
+/* Layout of specverify_accept_stats' output (doubles; counts are exact). */
+enum {
+  SV_STATS_SEQUENCES = 0,        /* sequences counted (bad-logits ones left out) */
+  SV_STATS_ACCEPTED = 1,         /* sum of accepted_len */
+  SV_STATS_DRAFTED = 2,          /* k * sequences */
+  SV_STATS_TESTED = 3,           /* sum of min(accepted_len + 1, k) */
+  SV_STATS_ACCEPTANCE = 4,       /* accepted / drafted */
+  SV_STATS_MAL = 5,              /* accepted / sequences: mean accepted length */
+  SV_STATS_TOKENS_PER_STEP = 6,  /* (accepted + sequences) / sequences */
+  SV_STATS_ALPHA = 7,            /* accepted / tested: the measured per-token acceptance */
+  SV_STATS_EXPECTED_TOKENS = 8,  /* E(alpha, k) = (1 - alpha^(k+1)) / (1 - alpha) */
+  SV_STATS_GAMMA_BEST = 9,       /* gamma in 1..12 with the largest speedup (smallest on ties) */
+  SV_STATS_SPEEDUP_BEST = 10,    /* that speedup */
+  SV_STATS_SPEEDUP_GAMMA1 = 11,  /* speedup(alpha, gamma, c) for gamma = 1..12 at 11..22 */
+  SV_STATS_LEN = 23
+};
+
+/* Acceptance statistics of one batch of verification results, and the
+ * speedup model fed with the measured acceptance.  Sources: "Towards Green
+ * Text Generation: Memory-Based Speculative Decoding", Appendix A (acceptance
+ * = fraction of drafted tokens accepted; MAL = mean number of draft tokens
+ * accepted per verification step); the edgeinferencenotes.hashnode.dev
+ * speculative-decoding article, "One decode round, end to end" (a pass
+ * commits the accepted tokens plus one); "Speculative Decoding Speedup
+ * Calculator", steps 1-3 (alpha = probability that the target accepts a
+ * given draft token, measured; E = (1 - alpha^(gamma+1)) / (1 - alpha); cost =
+ * gamma c + 1; speedup = E / cost; scan gamma = 1..12).
+ *   accepted_len [B] device int32 (specverify_run's output); seq_status [B]
+ *   device int32, optional: sequences with SV_STATUS_BAD_LOGITS are left out;
+ *   k >= 1: drafted tokens per sequence (a tree caller passes the depth bound
+ *   or node count it wants the rate against); draft_cost = c >= 0, finite;
+ *   out [SV_STATS_LEN] device doubles, written.  alpha = accepted / tested,
+ *   tested counting each sequence's tokens up to and including its first
+ *   rejection (min(n + 1, k)); 0 when nothing was tested. */
+int specverify_accept_stats(const int32_t* accepted_len, const int32_t* seq_status,
+                            int32_t batch, int32_t k, double draft_cost, double* out,
+                            void* stream);
+
+/* Tree attention mask.  Source: the edgeinferencenotes.hashnode.dev
+ * speculative-decoding article, "One decode round, end to end": the
+ * flattened tree is scored under a mask that lets each candidate see only
+ * its own ancestors (and the context), never sibling branches.
+ *   parents [B, N] device int32 (node 0 is the root; parents[b, i] < i);
+ *   mask [B, N, ceil(N/32)] device uint32, written: bit j of row i (word
+ *   j / 32, bit j % 32) is set iff j == i or j is an ancestor of i;
+ *   depth [B, N] device int32, optional, written.  A node whose parent chain
+ *   holds an index outside [0, i) is unreachable: its row holds only itself
+ *   and its depth is -1.  1 <= N <= SV_MAX_TREE_NODES. */
+int specverify_tree_mask(const int32_t* parents, int32_t batch, int32_t nodes, uint32_t* mask,
+                         int32_t* depth, void* stream);
+
+/* Commit map after tree verification.  Sources: the same article (the single
+ * longest agreed path is committed, the rest collapse) and "Towards Green
+ * Text Generation...", section 2.4 (upon rejection the KV cache is truncated
+ * to the accepted prefix).
+ *   path_nodes [B, N] device int32 and accepted_len [B]: specverify_run's
+ *   out_nodes and accepted_len of a SV_MODE_TREE_GREEDY call;
+ *   commit_pos [B, N] device int32, written: node path_nodes[b, d] (d <= n)
+ *   goes to position d, every other node to -1.  A sequence whose n is
+ *   outside [0, N) or whose path holds a node outside [0, N) (a sequence
+ *   that emitted nothing) commits nothing: all -1. */
+int specverify_tree_commit(const int32_t* path_nodes, const int32_t* accepted_len, int32_t batch,
+                           int32_t nodes, int32_t* commit_pos, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -25,7 +25,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = svm.load()
     names = declared_functions()
-    assert len(names) == 7
+    assert len(names) == 10
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(svm.EXPORTED) == names
@@ -154,3 +154,37 @@ def test_run_rejects_null_context():
     lib = svm.load()
     assert lib.specverify_run(None, 1, *([None] * 11), None) == SV_ERR_NULL
     assert lib.specverify_profile_events(None, None, None) == SV_ERR_NULL
+
+
+def test_stats_layout_matches_header():
+    text = open(HEADER).read()
+    for name in ("SV_STATS_SEQUENCES", "SV_STATS_ACCEPTED", "SV_STATS_DRAFTED", "SV_STATS_TESTED",
+                 "SV_STATS_ACCEPTANCE", "SV_STATS_MAL", "SV_STATS_TOKENS_PER_STEP", "SV_STATS_ALPHA",
+                 "SV_STATS_EXPECTED_TOKENS", "SV_STATS_GAMMA_BEST", "SV_STATS_SPEEDUP_BEST",
+                 "SV_STATS_SPEEDUP_GAMMA1", "SV_STATS_LEN"):
+        m = re.search(r"%s = (\d+)" % name, text)
+        assert m and int(m.group(1)) == getattr(svm, name), name
+
+
+def test_aux_entry_points_reject_bad_arguments_on_the_host():
+    """Argument errors come back before any HIP call (so no GPU is needed)."""
+    lib = svm.load()
+    stats, mask, commit = lib.specverify_accept_stats, lib.specverify_tree_mask, lib.specverify_tree_commit
+    assert stats(P, None, 4, 4, 0.1, None, None) == SV_ERR_NULL           # no output
+    assert stats(None, None, 4, 4, 0.1, P, None) == SV_ERR_NULL           # no input with batch > 0
+    assert stats(P, None, -1, 4, 0.1, P, None) == SV_ERR_SHAPE
+    assert stats(P, None, 4, 0, 0.1, P, None) == SV_ERR_SHAPE             # k >= 1
+    assert stats(P, None, 4, 4, -0.5, P, None) == SV_ERR_PARAM
+    assert stats(P, None, 4, 4, float("nan"), P, None) == SV_ERR_PARAM
+    assert stats(P, None, 4, 4, float("inf"), P, None) == SV_ERR_PARAM
+    assert mask(P, 2, 0, P, None, None) == SV_ERR_SHAPE
+    assert mask(P, 2, 1025, P, None, None) == SV_ERR_SHAPE
+    assert mask(P, -1, 10, P, None, None) == SV_ERR_SHAPE
+    assert mask(None, 2, 10, P, None, None) == SV_ERR_NULL
+    assert mask(P, 2, 10, None, None, None) == SV_ERR_NULL
+    assert mask(None, 0, 10, None, None, None) == SV_OK                  # empty batch: nothing to do
+    assert commit(P, P, 2, 0, P, None) == SV_ERR_SHAPE
+    assert commit(None, P, 2, 10, P, None) == SV_ERR_NULL
+    assert commit(P, None, 2, 10, P, None) == SV_ERR_NULL
+    assert commit(P, P, 2, 10, None, None) == SV_ERR_NULL
+    assert commit(None, None, 0, 10, None, None) == SV_OK
