@@ -262,10 +262,11 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
                       (!draft_logits || (uintptr_t)draft_logits % 16 == 0);
   p.aligned = (rows16 && base16) ? 1 : 0;
   // top-k: the certified filter pass takes tiles of one round of loads in
-  // aligned rows; other shapes take the exact per-tile pass
+  // aligned rows of whole groups; other shapes take the exact per-tile pass
   int tile_mode = pl.tile_mode;
   const int round = tile_mode == sv::kModeTopk ? (int)(sv::kFilterRound * 2 / es) : kRound;
-  if (tile_mode == sv::kModeTopk && p.aligned && c->vocab <= (long)sv::kMaxTiles * round)
+  if (tile_mode == sv::kModeTopk && p.aligned && c->vocab % sv::kVec == 0 &&
+      c->vocab <= (long)sv::kMaxTiles * round)
     tile_mode = sv::kModeTopkFilter;
   const long rows = (long)batch * (pl.rows_t + pl.rows_d);
   long S;

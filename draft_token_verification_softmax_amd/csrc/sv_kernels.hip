@@ -1139,17 +1139,25 @@ DEV int wave_exclusive_small(int c, int* total) {
 // They are maxima of distinct lanes, so at least top_k logits of the tile
 // are >= tau: tau bounds the tile's top_k-th logit from below (lanes with no
 // logit hold -inf, which can only make tau -inf: then the whole tile is
-// listed).  bf16 keys need only their top 16 bits.  Each wave lists its
-// logits >= tau, unordered, in its own kWaveList slots of the tile's list
-// (slot from a ballot-sliced prefix count), and writes its own partial: m =
-// tau, amax = its count (above kWaveList: overflow; the row merge then
-// redoes the tile exactly), s = NaN if its logits hold a NaN or +inf.
+// listed).  bf16 keys need only their top 16 bits.
+//
+// Listing: few groups reach tau (about one per wave and group slot), so a
+// wave first copies its groups whose max is >= tau into its own LDS stage
+// (a short predicated store per group slot), then each lane takes one staged
+// group and lists its logits >= tau, unordered, in the wave's own kWaveList
+// slots of the tile's list (slot from a ballot-sliced prefix count).  Each
+// wave writes its own partial: m = tau, amax = its count (above kWaveList,
+// or a stage overflow: the row merge then redoes the tile exactly), s = NaN
+// if its logits hold a NaN or +inf.
 constexpr int kWaveList = kCandSlots / kWaves;
+constexpr int kStageCap = 64;   // staged groups per wave (one per lane)
 
 template <typename T, int U>
 DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int grow, int seg) {
   constexpr int BITS = sizeof(T) == 2 ? 16 : 32;
   __shared__ uint32_t pub[kBlock];
+  __shared__ Group<T> stage[kWaves][kStageCap];
+  __shared__ int spos[kWaves][kStageCap];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int K = p.top_k;
   const int r1 = max(16, (K + kWaves - 1) / kWaves);
@@ -1158,19 +1166,32 @@ DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int
   Group<T> gr[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) gr[u].load_buf(rs, tid * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
+  // group maxima (NaN-propagating, so one test of the lane max finds a NaN);
+  // groups past the tile (partial tiles only) hold -inf
   float gm[U];
-  float lm = -INFINITY;
-  uint64_t nanm = 0;
+  uint32_t vm = (1u << U) - 1u;   // the lane's groups inside the tile
+  if (ngroups == U * kBlock) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    float v[kVec];
-    gr[u].values(v);
-    const float g = maximum8(v);
-    nanm |= __ballot(g != g);
-    gm[u] = (tid + u * kBlock < ngroups && g == g) ? g : -INFINITY;
-    lm = fmaxf(lm, gm[u]);
+    for (int u = 0; u < U; ++u) {
+      float v[kVec];
+      gr[u].values(v);
+      gm[u] = maximum8(v);
+    }
+  } else {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float v[kVec];
+      gr[u].values(v);
+      const bool in = tid + u * kBlock < ngroups;
+      gm[u] = in ? maximum8(v) : -INFINITY;
+      if (!in) vm &= ~(1u << u);
+    }
   }
-  const bool bad = nanm != 0ull || __ballot(lm == INFINITY) != 0ull;
+  float lm = gm[0];
+#pragma unroll
+  for (int u = 1; u + 1 < U; u += 2) lm = maximum3(lm, gm[u], gm[u + 1]);
+  if (U % 2 == 0) lm = maximum3(lm, gm[U - 1], gm[U - 1]);
+  const bool bad = __ballot(lm != lm || lm == INFINITY) != 0ull;
   // each wave publishes r1 of its largest lane maxima
   {
     const uint32_t key[1] = {ord_key(lm)};
@@ -1182,39 +1203,56 @@ DEV void tile_topk_filter(const Params& p, const T* row, int start, int end, int
   }
   __syncthreads();
   float tau;
-  {
+  if (kWaves * r1 <= 64) {
+    const uint32_t k1[1] = {lane < kWaves * r1 ? pub[lane] : 0u};
+    tau = key_value(wave_kth_key<1, BITS>(k1, K));
+  } else {
     uint32_t k4[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) { const int i = lane + 64 * q; k4[q] = i < kWaves * r1 ? pub[i] : 0u; }
     tau = key_value(wave_kth_key<4, BITS>(k4, K));
   }
-  // the wave's logits >= tau into its own sublist
-  int c = 0;
+  // stage the wave's groups that reach tau
+  uint32_t pm = 0u;
+#pragma unroll
+  for (int u = 0; u < U; ++u) pm |= (gm[u] >= tau ? 1u : 0u) << u;
+  pm &= vm;
+  int nstaged;
+  int slot = wave_exclusive_small(__popc(pm), &nstaged);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (tid + u * kBlock < ngroups && gm[u] >= tau) {
-      float v[kVec];
-      gr[u].opaque().values(v);
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) c += v[e] >= tau;
+    if ((pm >> u) & 1u) {
+      if (slot < kStageCap) {
+        stage[w][slot] = gr[u];
+        spos[w][slot] = tid + u * kBlock;
+      }
+      ++slot;
     }
   }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  // one staged group per lane: its logits >= tau into the wave's sublist
+  int c = 0;
+  float v[kVec];
+  int gpos = 0;
+  const bool have = lane < nstaged && lane < kStageCap;
+  if (have) {
+    stage[w][lane].values(v);
+    gpos = spos[w][lane];
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) c += v[e] >= tau;
+  }
   int total;
-  int slot = wave_exclusive_small(c, &total);
+  int at = wave_exclusive_small(c, &total);
+  if (nstaged > kStageCap) total = kWaveList + 1;
   const size_t tile = (size_t)grow * p.S + seg;
   uint64_t* out = p.cand + tile * p.cand_w + w * kWaveList;
+  if (have && c) {
+    const int pos = start + gpos * kVec;
 #pragma unroll
-  for (int u = 0; u < U; ++u) {
-    if (tid + u * kBlock < ngroups && gm[u] >= tau) {
-      float v[kVec];
-      gr[u].opaque().values(v);
-      const int pos = start + (tid + u * kBlock) * kVec;
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) {
-        if (v[e] >= tau) {
-          if (slot < kWaveList) out[slot] = pack(v[e], pos + e);
-          ++slot;
-        }
+    for (int e = 0; e < kVec; ++e) {
+      if (v[e] >= tau) {
+        if (at < kWaveList) out[at] = pack(v[e], pos + e);
+        ++at;
       }
     }
   }

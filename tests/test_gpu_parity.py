@@ -90,6 +90,7 @@ def test_sample_plain_full_workload2():
     (32, 6000, 8, 50, "bf16"),
     (24, 5001, 3, 50, "bf16"),
     (16, 4000, 4, 7, "f32"),
+    (16, 4004, 4, 50, "f32"),         # aligned rows whose last group is half full
     (16, 3000, 2, 256, "bf16"),
 ])
 def test_sample_topk(B, V, k, top_k, dtype):
