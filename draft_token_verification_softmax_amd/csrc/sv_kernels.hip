@@ -36,6 +36,7 @@
 
 #include <float.h>
 #include <limits.h>
+#include <limits>
 #include <math.h>
 
 #include <hip/hip_ext.h>
@@ -409,24 +410,78 @@ DEV int packed_idx(uint64_t pk) { return (int)(~(uint32_t)(pk & 0xffffffffu)); }
 DEV float packed_val(uint64_t pk) { return key_value((uint32_t)(pk >> 32)); }
 
 // ------------------------------------------------------------------ reductions
+//
+// Cross-lane steps go through DPP (an operand taken from another lane of the
+// same row of 16 lanes, or a row broadcast, as a modifier of an ordinary VALU
+// instruction) rather than LDS permutes, whose round trips serialise a
+// reduction.  Row shifts by 1, 2, 4 and 8 give every lane the inclusive
+// prefix of its row (Hillis-Steele); broadcasts of lane 15 to rows 1 and 3,
+// then of lane 31 to rows 2 and 3, carry the rows' totals forward.  Lane i
+// then holds the inclusive prefix over lanes 0..i, lane 63 the wave's total;
+// the order of operations is fixed, so results are reproducible.  Lanes
+// whose source is outside the row, or not written by a broadcast, take the
+// identity.  A reduction reads lane 63, so every lane must be active.
+enum : int {
+  kDppShr1 = 0x111, kDppShr2 = 0x112, kDppShr4 = 0x114, kDppShr8 = 0x118,
+  kDppWaveShr1 = 0x138, kDppBcast15 = 0x142, kDppBcast31 = 0x143,
+  kDppQuadXor1 = 0xb1, kDppQuadXor2 = 0x4e, kDppHalfMirror = 0x141, kDppMirror = 0x140,
+};
+
+template <int CTRL, int ROWS>
+DEV uint32_t dpp32(uint32_t id, uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, CTRL, ROWS, 0xf, false);
+}
+// v of the lane CTRL selects (id where there is none), for 4- and 8-byte types
+template <int CTRL, int ROWS = 0xf, typename T>
+DEV T dpp_move(T id, T v) {
+  static_assert(sizeof(T) == 4 || sizeof(T) == 8, "32- or 64-bit values");
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, dpp32<CTRL, ROWS>(__builtin_bit_cast(uint32_t, id), __builtin_bit_cast(uint32_t, v)));
+  } else {
+    const uint64_t a = __builtin_bit_cast(uint64_t, id), b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = dpp32<CTRL, ROWS>((uint32_t)a, (uint32_t)b);
+    const uint32_t hi = dpp32<CTRL, ROWS>((uint32_t)(a >> 32), (uint32_t)(b >> 32));
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+// v of one lane (uniform index), in every lane
+template <typename T>
+DEV T read_lane(T v, int lane) {
+  if constexpr (sizeof(T) == 4) {
+    return __builtin_bit_cast(T, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+  } else {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(T, ((uint64_t)hi << 32) | lo);
+  }
+}
+// Inclusive scan over the lanes of a wave for an associative op with
+// identity id: lane i gets op over lanes 0..i.
+template <typename T, typename Op>
+DEV T wave_scan(T v, T id, Op op) {
+  v = op(v, dpp_move<kDppShr1>(id, v));
+  v = op(v, dpp_move<kDppShr2>(id, v));
+  v = op(v, dpp_move<kDppShr4>(id, v));
+  v = op(v, dpp_move<kDppShr8>(id, v));
+  v = op(v, dpp_move<kDppBcast15, 0xa>(id, v));
+  v = op(v, dpp_move<kDppBcast31, 0xc>(id, v));
+  return v;
+}
+// op over all lanes of a wave, in every lane
+template <typename T, typename Op>
+DEV T wave_all(T v, T id, Op op) {
+  return read_lane(wave_scan(v, id, op), 63);
+}
+// The value of lane - 1 (id in lane 0).
+template <typename T>
+DEV T lane_before(T v, T id) { return dpp_move<kDppWaveShr1>(id, v); }
 
 DEV float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  return wave_all(v, -INFINITY, [](float a, float b) { return fmaxf(a, b); });
 }
 DEV double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-DEV void wave_argmax(float& m, int& i) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float m2 = __shfl_xor(m, o);
-    int i2 = __shfl_xor(i, o);
-    if (m2 > m || (m2 == m && i2 < i)) { m = m2; i = i2; }
-  }
+  return wave_all(v, 0.0, [](double a, double b) { return a + b; });
 }
 
 // Block-wide sum in a fixed order; every thread gets the same value.
@@ -450,35 +505,18 @@ DEV float block_max(float v, float* red) {
   __syncthreads();
   return t;
 }
-DEV void block_argmax(float& m, int& i, float* redm, int* redi) {
-  wave_argmax(m, i);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) { redm[w] = m; redi[w] = i; }
-  __syncthreads();
-  m = redm[0]; i = redi[0];
-  for (int q = 1; q < kWaves; ++q)
-    if (redm[q] > m || (redm[q] == m && redi[q] < i)) { m = redm[q]; i = redi[q]; }
-  __syncthreads();
-}
 
 // Block-wide integer reductions by shuffles (one LDS slot per wave); every
 // thread gets the result.  Many lanes updating one LDS word with atomics
 // serialise, so block-wide decisions go through these instead.
 template <typename I> DEV I wave_min_t(I v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) { const I u = __shfl_xor(v, o); v = u < v ? u : v; }
-  return v;
+  return wave_all(v, std::numeric_limits<I>::max(), [](I a, I b) { return b < a ? b : a; });
 }
 template <typename I> DEV I wave_max_t(I v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) { const I u = __shfl_xor(v, o); v = u > v ? u : v; }
-  return v;
+  return wave_all(v, std::numeric_limits<I>::lowest(), [](I a, I b) { return b > a ? b : a; });
 }
 DEV int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return wave_all(v, 0, [](int a, int b) { return a + b; });
 }
 // (min a, max b) over the block in one pass
 template <typename I>
@@ -521,7 +559,7 @@ DEV int wave_append(bool take, int* counter) {
   const int leader = __ffsll((unsigned long long)m) - 1;
   int base = 0;
   if (lane == leader) base = atomicAdd(counter, __popcll(m));
-  base = __shfl(base, leader);
+  base = read_lane(base, leader);
   const int below = __popcll(m & ((1ull << lane) - 1ull));
   return take ? base + below : -1;
 }
@@ -531,30 +569,19 @@ DEV int wave_append(bool take, int* counter) {
 // with every lane of the wave active.
 DEV int wave_reserve(int n, int* counter) {
   const int lane = threadIdx.x & 63;
-  int incl = n;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int t = __shfl_up(incl, o);
-    if (lane >= o) incl += t;
-  }
-  const int total = __shfl(incl, 63);
+  const int incl = wave_scan(n, 0, [](int a, int b) { return a + b; });
+  const int total = read_lane(incl, 63);
   int base = 0;
   if (lane == 0 && total > 0) base = atomicAdd(counter, total);
-  return __shfl(base, 0) + incl - n;
+  return read_lane(base, 0) + incl - n;
 }
 
 // Exclusive scan of one double per thread in thread order (fixed order).
 // Returns the exclusive prefix; *total gets the block total.
 DEV double block_exscan(double v, double* red, double* total) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  double inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    double t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
-  double exl = __shfl_up(inc, 1);
-  if (lane == 0) exl = 0.0;
+  const double inc = wave_scan(v, 0.0, [](double a, double b) { return a + b; });
+  const double exl = lane_before(inc, 0.0);
   __syncthreads();
   if (lane == 63) red[w] = inc;
   __syncthreads();
@@ -569,12 +596,8 @@ DEV double block_exscan(double v, double* red, double* total) {
 DEV unsigned long long block_exscan_u64(unsigned long long v, unsigned long long* red,
                                         unsigned long long* total) {
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  unsigned long long inc = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    unsigned long long t = __shfl_up(inc, o);
-    if (lane >= o) inc += t;
-  }
+  const unsigned long long inc =
+      wave_scan(v, 0ull, [](unsigned long long a, unsigned long long b) { return a + b; });
   __syncthreads();
   if (lane == 63) red[w] = inc;
   __syncthreads();
@@ -723,11 +746,7 @@ DEV void tile_argmax(const Params& p, const T* row, int start, int end, int grow
     for (int e = kVec - 1; e >= 0; --e) if (v[e] == m) idx = start + gbest * kVec + e;
   }
   uint64_t key = idx == INT_MAX ? 0ull : pack(m, idx);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint64_t k2 = __shfl_xor(key, o);
-    key = k2 > key ? k2 : key;
-  }
+  key = wave_max_t(key);
   if ((threadIdx.x & 63) == 0) {
     TileStat ts;
     ts.m = key ? packed_val(key) : -INFINITY;
@@ -737,17 +756,19 @@ DEV void tile_argmax(const Params& p, const T* row, int start, int end, int grow
   }
 }
 
-// The logit of the drafted token an accept test reads from this row, if it
-// falls in the tile (one thread; rows without a drafted token are skipped).
-template <typename T>
-DEV void record_token_logit(const Params& p, const T* row, int grow, int start, int end) {
+// The drafted token whose logit an accept test reads from this row, in
+// every lane; *has = false for rows without one (the value is then
+// meaningless).  A buffer load with no branch: it is issued ahead of a
+// tile's own loads and waited for with them, so its latency overlaps theirs
+// instead of preceding them.
+DEV int row_token(const Params& p, int grow, bool* has) {
   const int nt = p.B * p.rows_t;
   int b, j;
   if (grow < nt) { b = grow / p.rows_t; j = grow - b * p.rows_t; }
   else { b = (grow - nt) / p.rows_d; j = (grow - nt) - b * p.rows_d; }
-  if (j >= p.k) return;
-  const int x = p.tokens[(size_t)b * p.k + j];
-  if (x >= start && x < end) p.row_lx[grow] = Io<T>::at(row, x);
+  *has = j < p.k;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.tokens, p.B * p.k * 4);
+  return __builtin_amdgcn_raw_buffer_load_b32(rs, (*has ? b * p.k + j : 0) * 4, 0, 0);
 }
 
 // Max and sum of exp((l - max) / T) = 2^((l - max) c), c = log2(e) / T, over
@@ -767,17 +788,28 @@ DEV void record_token_logit(const Params& p, const T* row, int grow, int start, 
 template <typename T, bool EXACT>
 DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow, int seg) {
   __shared__ double tab[64];
-  if (threadIdx.x == 0) record_token_logit<T>(p, row, grow, start, end);
+  bool xhas;
+  const int xt = row_token(p, grow, &xhas);
+  float lx = 0.f;
+  bool hx = false;
   if (EXACT) exp2_table_init(tab);
   const double cd = kLog2e / p.T;
   const double c64 = 64.0 * cd;
-  const float c_hi = (float)cd;
-  const float c_lo = (float)(cd - (double)c_hi);
+  // c_hi <= c and c_lo > 0, so that a -inf logit gives d * c_lo = -inf and
+  // a term of exactly 0 (never inf - inf)
+  float c_hi = (float)cd;
+  if ((double)c_hi > cd) c_hi = __uint_as_float(__float_as_uint(c_hi) - 1u);   // c > 0
+  const float c_lo = fmaxf((float)(cd - (double)c_hi), FLT_MIN);
   float m = -INFINITY;
   double s = 0.0;
   uint64_t nanm = 0;
-  tile_groups<T, kUnroll>(row, start, end, p.aligned, [&](const auto& gr, int, int nv) {
+  tile_groups<T, kUnroll>(row, start, end, p.aligned, [&](const auto& gr, int g0, int nv) {
     constexpr int n = sizeof(gr) / sizeof(gr[0]);
+    // the token's first use stays here, after this round's loads are issued
+    // (its wait then overlaps theirs)
+    int xr = xt;
+    asm volatile("" : "+v"(xr));
+    xr = xhas ? xr - start : -kVec;
     float mi = m;
 #pragma unroll
     for (int u = 0; u < n; ++u) {
@@ -786,6 +818,13 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
       const float gm = maximum8(v);
       nanm |= __ballot(gm != gm);
       mi = (u < nv && gm > mi) ? gm : mi;
+      // the drafted token's logit, from the one lane whose group holds it
+      const unsigned off = (unsigned)(xr - (g0 + u * kBlock) * kVec);
+      if (u < nv && off < (unsigned)kVec) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) lx = off == (unsigned)e ? v[e] : lx;
+        hx = true;
+      }
     }
     if (mi > m) {
       if (m > -INFINITY) s *= exp2_neg(((double)m - (double)mi) * cd);
@@ -806,8 +845,7 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
           float e[kVec];
 #pragma unroll
           for (int q = 0; q < kVec; ++q) {
-            // -inf logits: clamp d so that d * c_lo cannot be +inf (c_lo < 0)
-            const float d = fmaxf(v[q] - m, -FLT_MAX);
+            const float d = v[q] - m;
             e[q] = __builtin_amdgcn_exp2f(fmaf(d, c_hi, d * c_lo));
           }
           const float gs = ((e[0] + e[1]) + (e[2] + e[3])) + ((e[4] + e[5]) + (e[6] + e[7]));
@@ -816,6 +854,7 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
       }
     }
   });
+  if (hx) p.row_lx[grow] = lx;
   const float M = wave_max(m);
   double term = m == -INFINITY ? 0.0 : s * exp2_neg(((double)m - (double)M) * cd);
   term = wave_sum(term);
@@ -1007,7 +1046,7 @@ DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroup
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) mx = fmaxf(mx, max8(v[u]));
       const float srt = wave_sort_desc(mx);
-      const float tw = __shfl(srt, (K + kWaves - 1) / kWaves - 1);
+      const float tw = read_lane(srt, (K + kWaves - 1) / kWaves - 1);
       __syncthreads();
       if (lane == 0) wtau[tid >> 6] = tw;
       __syncthreads();
@@ -1564,12 +1603,7 @@ DEV uint64_t block_topk_threshold(const uint64_t* keys, int c, int K, unsigned* 
       unsigned s4 = 0u;
 #pragma unroll
       for (int q = 0; q < 4; ++q) { h[q] = hist[255 - 4 * lane - q]; s4 += h[q]; }
-      unsigned incl = s4;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const unsigned t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
+      const unsigned incl = wave_scan(s4, 0u, [](unsigned a, unsigned b) { return a + b; });
       unsigned cb = incl - s4;   // keys with a larger digit
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
