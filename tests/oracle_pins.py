@@ -533,3 +533,151 @@ def pin_alpha_recovery(ax, calc):
         tps_se = float(np.std(n + 1)) / math.sqrt(S)
         assert abs(r["tokens_per_step"] - calc.expected_tokens_closed(alpha, k)) < 4 * tps_se, (alpha, k)
         assert abs(r["expected_tokens"] - calc.expected_tokens_closed(r["alpha"], k)) < 1e-15
+
+
+# ---------------------------------------------------------------- tree sampling (readings R24-R27)
+
+def _tree_logits(rows):
+    with np.errstate(divide="ignore"):
+        return np.log(np.array(rows, dtype=np.float64))
+
+
+def pin_tree_sample_golden(ts):
+    """Hand-worked trees (tests/golden/tree_sample.json)."""
+    for c in _load("tree_sample.json")["cases"]:
+        o = ts.tree_sample(_tree_logits(c["target"]), _tree_logits(c["draft"]), np.array(c["parents"]),
+                           np.array(c["tokens"]), np.array(c["u"]), c["ur"], 1.0)
+        got = (o["n"], o["tokens"], o["nodes"], o["status"])
+        want = (c["n"], c["out_tokens"], c["out_nodes"], c["status"])
+        assert got == want, (c["name"], got, want)
+        assert np.allclose(o["resid"], c["resid"], rtol=0, atol=1e-12), (c["name"], o["resid"])
+
+
+def pin_tree_sample_is_chain(ts, ov, trials=150, seed=11):
+    """A path-shaped tree (one child per node) is the chain: node i + 1 carries
+    draft token i, target and draft row i are the chain's rows i, node i + 1's
+    uniform is the chain's u_i.  Same tokens, length, status and residual."""
+    rng = np.random.default_rng(seed)
+    for t in range(trials):
+        s = SETTINGS[t % len(SETTINGS)]
+        k = int(rng.integers(1, 6))
+        V = int(rng.integers(3, 9))
+        tgt = rng.normal(0, 1.5, size=(k + 1, V))
+        dft = tgt[:k] + rng.normal(0, 1.0, size=(k, V))
+        q = [ov.transform_row(dft[j], s["T"], s["top_k"], s["top_p"]) for j in range(k)]
+        x = [ov.draw_from(q[j], rng.random()) if rng.random() < 0.9 else int(rng.integers(0, V))
+             for j in range(k)]
+        u = rng.random(k)
+        ur = rng.random()
+        c = ov.sample_chain(tgt, dft, x, u, ur, s["T"], s["top_k"], s["top_p"])
+        parents = np.arange(-1, k)
+        tokens = np.array([0] + list(x))
+        draft_rows = np.vstack([dft, np.zeros((1, V))])
+        o = ts.tree_sample(tgt, draft_rows, parents, tokens, np.concatenate(([0.0], u)), ur,
+                           s["T"], s["top_k"], s["top_p"])
+        assert (o["n"], o["tokens"], o["status"]) == (c["n"], c["tokens"], c["status"]), (t, o, c)
+        assert o["nodes"] == list(range(o["n"] + 1))
+        assert np.allclose(o["resid"], c["resid"], rtol=0, atol=1e-14), (t, o["resid"], c["resid"])
+
+
+def tree_first_token_law(ts, ov, tgt, dft, m, T, top_k, top_p):
+    """Exact law of the first emitted token of a root with m leaf children
+    whose tokens are drawn independently from q'_root, with the oracle as a
+    black box: every token tuple weighted by its draft probability; child i's
+    accept region in u_i (earlier children forced to reject) and the residual
+    draw's regions in ur found by bisection."""
+    V = tgt.shape[1]
+    q = ov.transform_row(dft[0], T, top_k, top_p)
+    parents = np.array([-1] + [0] * m)
+    never = np.nextafter(1.0, 0.0)
+
+    def run(xs, us, ur):
+        return ts.tree_sample(tgt, dft, parents, np.array([0] + list(xs)), np.array([0.0] + list(us)),
+                              ur, T, top_k, top_p)
+
+    law = np.zeros(V)
+    resid = None
+    support = [v for v in range(V) if q[v] > 0.0]
+    for xs in np.array(np.meshgrid(*[support] * m, indexing="ij")).reshape(m, -1).T:
+        w = float(np.prod([q[x] for x in xs]))
+        surv = 1.0
+        for i in range(m):
+            def acc_i(u, i=i):
+                us = [never] * i + [u] + [never] * (m - i - 1)
+                o = run(xs, us, 0.5)
+                return o["n"] >= 1 and o["nodes"][1] == i + 1
+            th = _threshold(acc_i)
+            law[xs[i]] += w * surv * th
+            surv *= 1.0 - th
+            if surv == 0.0:
+                break
+        if surv > 0.0:
+            if resid is None:
+                resid = _step_measure(lambda ur: run(xs, [never] * m, ur)["tokens"][0], V)
+            law += w * surv * resid
+    return law
+
+
+def pin_tree_sample_enumeration(ts, ov, seed=12, cases=((2, 6), (3, 5))):
+    """Distribution preservation over a tree ([Explainer] "Why it changes
+    nothing about the output", applied down the branches): whatever the draft,
+    the first emitted token of a root with m independently drafted children
+    follows p'_root exactly, under temperature, top-k and top-p."""
+    rng = np.random.default_rng(seed)
+    worst = 0.0
+    for j, (m, V) in enumerate(cases):
+        for s in (SETTINGS[j % len(SETTINGS)], SETTINGS[(j + 3) % len(SETTINGS)]):
+            tgt = rng.normal(0, 1.5, size=(m + 1, V))
+            dft = rng.normal(0, 1.5, size=(m + 1, V))
+            law = tree_first_token_law(ts, ov, tgt, dft, m, s["T"], s["top_k"], s["top_p"])
+            p = ov.transform_row(tgt[0], s["T"], s["top_k"], s["top_p"])
+            worst = max(worst, float(np.max(np.abs(law - p))))
+    assert worst < 1e-12, worst
+    return worst
+
+
+def pin_tree_sample_chisq(ts, ov, trials=6000, seed=13, alpha=1e-3):
+    """Brute force on a depth-3 tree (V = 8, two or three children per inner
+    node, children drawn from the draft row of their parent): the first
+    emitted token follows p'_root, and the second, given that the walk went
+    to the root's first child c, follows p'_c."""
+    rng = np.random.default_rng(seed)
+    V = 8
+    parents = np.array([-1, 0, 0, 0, 1, 1, 2, 4, 4])
+    N = len(parents)
+    tgt = rng.normal(0, 1.0, size=(N, V))
+    dft = tgt + rng.normal(0, 1.0, size=(N, V))
+    q = [ov.transform_row(dft[i], 1.0) for i in range(N)]
+    p = [ov.transform_row(tgt[i], 1.0) for i in range(N)]
+    first = np.zeros(V)
+    second = np.zeros(V)
+    for _ in range(trials):
+        tokens = np.array([0] + [ov.draw_from(q[parents[i]], rng.random()) for i in range(1, N)])
+        o = ts.tree_sample(tgt, dft, parents, tokens, rng.random(N), rng.random(), 1.0)
+        first[o["tokens"][0]] += 1
+        if o["n"] >= 1 and o["nodes"][1] == 1:
+            second[o["tokens"][1]] += 1
+    for counts, probs in ((first, p[0]), (second, p[1])):
+        assert counts.sum() > 500
+        pval = scipy.stats.chisquare(counts, probs * counts.sum()).pvalue
+        assert pval > alpha, (counts, probs * counts.sum(), pval)
+
+
+def pin_tree_sample_status(ts):
+    """R26: a NaN in a target row, or in the draft row of a node with a child,
+    empties the output; the draft row of a leaf is never read."""
+    V = 4
+    parents = np.array([-1, 0, 1])
+    tgt = np.zeros((3, V))
+    dft = np.zeros((3, V))
+    toks = np.array([0, 1, 2])
+    u = np.full(3, 0.5)
+    ok = ts.tree_sample(tgt, dft, parents, toks, u, 0.5, 1.0)
+    assert ok["status"] == 0 and len(ok["tokens"]) == ok["n"] + 1
+    d2 = dft.copy(); d2[2, 1] = np.nan          # leaf's draft row: not read
+    assert ts.tree_sample(tgt, d2, parents, toks, u, 0.5, 1.0)["status"] == 0
+    d1 = dft.copy(); d1[1, 1] = np.nan          # node 1 has a child
+    o = ts.tree_sample(tgt, d1, parents, toks, u, 0.5, 1.0)
+    assert o["status"] == 4 and o["tokens"] == [] and o["nodes"] == []
+    t2 = tgt.copy(); t2[2, :] = -np.inf          # a target row with no finite logit
+    assert ts.tree_sample(t2, dft, parents, toks, u, 0.5, 1.0)["status"] == 4

@@ -41,3 +41,26 @@ def test_commit_map_inverts_the_path():
 
 def test_measured_alpha_recovers_the_model():
     pins.pin_alpha_recovery(ax, calc)
+
+
+import oracle.tree_sample as ts
+
+
+def test_tree_sample_golden():
+    pins.pin_tree_sample_golden(ts)
+
+
+def test_tree_sample_path_is_chain():
+    pins.pin_tree_sample_is_chain(ts, ov)
+
+
+def test_tree_sample_enumeration():
+    pins.pin_tree_sample_enumeration(ts, ov)
+
+
+def test_tree_sample_chisq():
+    pins.pin_tree_sample_chisq(ts, ov)
+
+
+def test_tree_sample_status():
+    pins.pin_tree_sample_status(ts)

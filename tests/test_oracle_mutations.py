@@ -135,3 +135,47 @@ def test_aux_mutant_is_caught(name, old, new):
         except Exception:
             return
     pytest.fail("mutant survived every pin: " + name)
+
+
+import oracle.tree_sample as ts_real
+
+TS_SRC = open(ts_real.__file__).read()
+TS_MUTANTS = [
+    ("running target not replaced by the residual", "                if s > 0.0:\n                    r = res / s",
+     "                if s > 0.0:\n                    pass"),
+    ("residual not clamped at zero", "                res = np.maximum(0.0, r - q)", "                res = np.abs(r - q)"),
+    ("residual subtracts the target", "                res = np.maximum(0.0, r - q)", "                res = np.maximum(0.0, q - r)"),
+    ("test against p'_u instead of the running target", "                    a, b = r[x], q[x]",
+     "                    a, b = p[x], q[x]"),
+    ("children tried in reverse order", "            for c in children[cur]:", "            for c in reversed(children[cur]):"),
+    ("walk stops after the first accepted child", "        path.append(nxt)\n        cur = nxt",
+     "        path.append(nxt)\n        cur = nxt\n        break"),
+    ("the draw after a full walk uses the parent's row", "        p, cut = transform_row(T[cur]",
+     "        p, cut = transform_row(T[path[-2] if len(path) > 1 else cur]"),
+    ("bad parent still a child", "        if 0 <= par < i:", "        if par < i:"),
+    ("leaf draft rows read", "        all(row_is_valid(D[u]) for u in range(N) if children[u])",
+     "        all(row_is_valid(D[u]) for u in range(N))"),
+    ("uniform of the parent used", "                    u = np.float64(uniforms[c])",
+     "                    u = np.float64(uniforms[cur])"),
+]
+
+
+def _load_ts_mutant(old, new, name):
+    assert TS_SRC.count(old) == 1, ("mutation site not unique", old)
+    mod = types.ModuleType("oracle.mutant_ts_" + name.replace(" ", "_"))
+    mod.__dict__["__package__"] = "oracle"
+    exec(compile(TS_SRC.replace(old, new), mod.__name__, "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name,old,new", TS_MUTANTS, ids=[m[0] for m in TS_MUTANTS])
+def test_tree_sample_mutant_is_caught(name, old, new):
+    mod = _load_ts_mutant(old, new, name)
+    for pin in (pins.pin_tree_sample_golden, lambda m: pins.pin_tree_sample_is_chain(m, real),
+                pins.pin_tree_sample_status, lambda m: pins.pin_tree_sample_enumeration(m, real),
+                lambda m: pins.pin_tree_sample_chisq(m, real, trials=3000)):
+        try:
+            pin(mod)
+        except Exception:
+            return
+    pytest.fail("mutant survived every pin: " + name)
