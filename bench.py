@@ -172,7 +172,28 @@ def cpu_baseline(config, budget_s=12.0):
     t0 = time.perf_counter()
     rows = 0
     seqs = 0
-    if cfg["kind"] == "tree":
+    if cfg["kind"] == "tree_sample":
+        import oracle.tree_sample as ts
+        ti = wl.tree_sample_inputs(wl.DEFAULT_SEED[config], B=cfg["B"], N=cfg["N"], V=cfg["V"],
+                                   dtype=cfg["dtype"], T=cfg["T"], sd=cfg["sd"], noise=cfg["noise"],
+                                   max_depth=cfg["max_depth"], max_children=cfg["max_children"])
+        T64 = wl.rows_f64(ti["target"], ti["dtype"])
+        D64 = wl.rows_f64(ti["draft"], ti["dtype"])
+        B, N = ti["B"], ti["N"]
+        tokens = np.zeros((B, N), np.int32)
+        for b in range(B):
+            for i in range(1, N):
+                q = ov.transform_row(D64[b, ti["parents"][b, i]], ti["T"])
+                tokens[b, i] = ov.draw_from(q, ti["draw_u"][b, i])
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < budget_s:
+            b = seqs % B
+            ts.tree_sample(T64[b], D64[b], ti["parents"][b], tokens[b], ti["u"][b], ti["ur"][b], ti["T"])
+            rows += N
+            seqs += 1
+        el = time.perf_counter() - t0
+        nbytes = rows * 2 * ti["V"] * (2 if ti["dtype"] == "bf16" else 4)
+    elif cfg["kind"] == "tree":
         tr = wl.tree_inputs(config)
         T64 = wl.rows_f64(tr["target"], tr["dtype"])
         tokens = wl.tree_tokens(tr, np.argmax(T64, axis=-1))
@@ -249,7 +270,26 @@ def main():
     torch.cuda.set_device(0)
     dev = torch.device("cuda:0")
     log(f"workload {args.config}: generating inputs")
-    if cfg["kind"] == "tree":
+    if cfg["kind"] == "tree_sample":
+        ti = wl.tree_sample_inputs(wl.DEFAULT_SEED[args.config], B=cfg["B"], N=cfg["N"], V=cfg["V"], dtype=cfg["dtype"],
+                                   T=cfg["T"], sd=cfg["sd"], noise=cfg["noise"],
+                                   max_depth=cfg["max_depth"], max_children=cfg["max_children"])
+        B, N, V, dtype, T = ti["B"], ti["N"], ti["V"], ti["dtype"], ti["T"]
+        tgt = logits_to_device(ti["target"], dtype)
+        dft = logits_to_device(ti["draft"], dtype)
+        parents = torch.from_numpy(ti["parents"]).to(dev)
+        par = parents.clamp(min=0).long()
+        rows = dft[torch.arange(B, device=dev).unsqueeze(1), par]       # draft row of each node's parent
+        tokens = draft_tokens_torch(rows, T, 0, 1.0, ti["draw_u"])
+        tokens[:, 0] = 0
+        inputs = dict(target=tgt, draft=dft, tokens=tokens, parents=parents,
+                      u=torch.from_numpy(ti["u"]).to(dev), ur=torch.from_numpy(ti["ur"]).to(dev))
+        mode, k, rows_t, rows_d = svm.SV_MODE_TREE_SAMPLE, N, N, N
+        top_k, top_p = 0, 1.0
+        workload = f"tree sampling verification, B={B}, N={N} nodes, V={V}, {dtype} logits, T={T}"
+        extra = dict(B=B, N=N, V=V, logits_dtype=dtype, T=T, depth_max=cfg["max_depth"],
+                     children_max=cfg["max_children"])
+    elif cfg["kind"] == "tree":
         tr = wl.tree_inputs(args.config)
         B, N, V, dtype = tr["B"], tr["N"], tr["V"], tr["dtype"]
         tgt = logits_to_device(tr["target"], dtype)
@@ -278,7 +318,8 @@ def main():
     es = 2 if dtype == "bf16" else 4
     logit_bytes = B * (rows_t + rows_d) * V * es
     small_bytes = sum(t.numel() * t.element_size() for n, t in inputs.items() if n not in ("target", "draft"))
-    out_bytes = B * 4 * (2 + (k + 1 if cfg["kind"] != "tree" else 2 * N))
+    tree = cfg["kind"] in ("tree", "tree_sample")
+    out_bytes = B * 4 * (2 + (k + 1 if not tree else 2 * N))
     alg_bytes = logit_bytes + small_bytes + out_bytes
     ncopies = max(1, math.ceil(1e9 / logit_bytes))
     ncopies = min(ncopies, max(1, int(48e9 // logit_bytes)))
@@ -288,9 +329,9 @@ def main():
     sv = svm.SpecVerify(mode=mode, dtype=dtype, max_batch=B, k=k, vocab=V,
                         temperature=T, top_k=top_k, top_p=top_p)
     acc = torch.empty(B, dtype=torch.int32, device=dev)
-    out_w = N if cfg["kind"] == "tree" else k + 1
+    out_w = N if tree else k + 1
     out_tok = torch.empty(B, out_w, dtype=torch.int32, device=dev)
-    out_nodes = torch.empty(B, out_w, dtype=torch.int32, device=dev) if cfg["kind"] == "tree" else None
+    out_nodes = torch.empty(B, out_w, dtype=torch.int32, device=dev) if tree else None
     status = torch.empty(B, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
 
@@ -365,7 +406,7 @@ def main():
         hip.destroy(e)
         return us
 
-    kk = k if cfg["kind"] != "tree" else cfg["max_depth"]
+    kk = k if not tree else cfg["max_depth"]
     stats_out = torch.empty(svm.SV_STATS_LEN, dtype=torch.float64, device=dev)
     extras["accept_stats_us"] = time_launches(
         lambda: svm.specverify_accept_stats(acc, status, B, kk, 0.1, stats_out, stream))
@@ -373,7 +414,7 @@ def main():
     extras["acceptance"] = float(st[svm.SV_STATS_ACCEPTANCE])
     extras["mal"] = float(st[svm.SV_STATS_MAL])
     extras["alpha"] = float(st[svm.SV_STATS_ALPHA])
-    if cfg["kind"] == "tree":
+    if tree:
         mask = torch.empty(B, N, (N + 31) // 32, dtype=torch.int32, device=dev)
         depth = torch.empty(B, N, dtype=torch.int32, device=dev)
         pos = torch.empty(B, N, dtype=torch.int32, device=dev)

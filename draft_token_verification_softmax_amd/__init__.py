@@ -19,7 +19,7 @@ import os
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecverify.so")
 
-SV_MODE_SAMPLE, SV_MODE_GREEDY, SV_MODE_TREE_GREEDY = 0, 1, 2
+SV_MODE_SAMPLE, SV_MODE_GREEDY, SV_MODE_TREE_GREEDY, SV_MODE_TREE_SAMPLE = 0, 1, 2, 3
 SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_PARAM = 0, -1, -2, -3, -4
 SV_ERR_CAPACITY, SV_ERR_HIP, SV_ERR_MODE = -5, -6, -7
@@ -265,10 +265,10 @@ class SpecVerify:
         B = int(target.shape[0])
         V, k = c.vocab, c.k
         ldt = (torch.bfloat16, torch.int16, torch.uint16) if c.dtype == SV_DTYPE_BF16 else (torch.float32,)
-        tree = c.mode == SV_MODE_TREE_GREEDY
+        tree = c.mode in (SV_MODE_TREE_GREEDY, SV_MODE_TREE_SAMPLE)
         rows_t = k if tree else k + 1
         self._check("target", target, (B, rows_t, V), ldt)
-        if c.mode == SV_MODE_SAMPLE:
+        if c.mode in (SV_MODE_SAMPLE, SV_MODE_TREE_SAMPLE):
             self._check("draft", draft, (B, k, V), ldt)
             self._check("uniforms", uniforms, (B, k), (torch.float32,))
             self._check("resid_uniforms", resid_uniforms, (B,), (torch.float32,))

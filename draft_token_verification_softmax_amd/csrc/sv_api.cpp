@@ -30,35 +30,43 @@ struct Plan {
 
 int check_config(const sv_config* c) {
   if (!c) return SV_ERR_NULL;
-  if (c->mode != SV_MODE_SAMPLE && c->mode != SV_MODE_GREEDY && c->mode != SV_MODE_TREE_GREEDY)
+  if (c->mode != SV_MODE_SAMPLE && c->mode != SV_MODE_GREEDY && c->mode != SV_MODE_TREE_GREEDY &&
+      c->mode != SV_MODE_TREE_SAMPLE)
     return SV_ERR_MODE;
   if (c->dtype != SV_DTYPE_F32 && c->dtype != SV_DTYPE_BF16) return SV_ERR_DTYPE;
   if (c->max_batch < 1 || c->vocab < 1 || c->vocab > SV_MAX_VOCAB) return SV_ERR_SHAPE;
-  if (c->mode == SV_MODE_TREE_GREEDY) {
+  const bool tree = c->mode == SV_MODE_TREE_GREEDY || c->mode == SV_MODE_TREE_SAMPLE;
+  if (tree) {
     if (c->k < 1 || c->k > SV_MAX_TREE_NODES) return SV_ERR_SHAPE;
   } else {
     if (c->k < 1 || c->k > SV_MAX_K) return SV_ERR_SHAPE;
   }
-  if (c->mode == SV_MODE_SAMPLE) {
+  if (c->mode == SV_MODE_SAMPLE || c->mode == SV_MODE_TREE_SAMPLE) {
     if (!(c->temperature > 0.0) || !isfinite(c->temperature)) return SV_ERR_PARAM;
     if (c->top_k < 0) return SV_ERR_PARAM;
     if (c->top_k > SV_MAX_TOP_K && c->top_k < c->vocab) return SV_ERR_PARAM;
     if (!(c->top_p > 0.0 && c->top_p <= 1.0)) return SV_ERR_PARAM;
   }
+  // tree sampling: temperature only (no top-k or top-p)
+  if (c->mode == SV_MODE_TREE_SAMPLE && ((c->top_k > 0 && c->top_k < c->vocab) || c->top_p < 1.0))
+    return SV_ERR_PARAM;
   return SV_OK;
 }
 
 Plan make_plan(const sv_config* c) {
   Plan p;
   const bool sample = c->mode == SV_MODE_SAMPLE;
+  const bool tsample = c->mode == SV_MODE_TREE_SAMPLE;
   p.top_k = (sample && c->top_k > 0 && c->top_k < c->vocab) ? c->top_k : 0;
   p.top_p = (sample && c->top_p < 1.0) ? c->top_p : 1.0;
   if (c->mode == SV_MODE_GREEDY) { p.filt = sv::kFiltGreedy; p.tile_mode = sv::kModeArgmax; }
   else if (c->mode == SV_MODE_TREE_GREEDY) { p.filt = sv::kFiltTree; p.tile_mode = sv::kModeArgmax; }
+  else if (tsample) { p.filt = sv::kFiltTreeSample; p.tile_mode = sv::kModeStats32; }
   else if (p.top_k > 0) { p.filt = sv::kFiltTopk; p.tile_mode = sv::kModeTopk; }
   else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeStats64; }
   else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats32; }
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
+  else if (tsample) { p.rows_t = c->k; p.rows_d = c->k; p.out_w = c->k; }
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
   // most tiles per row of the list passes at any batch size (see the tiling
   // in specverify_run): the exact pass, or the filter pass at batch 1
@@ -80,7 +88,7 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, row_lx, seq, spart, wpart;
+  size_t tiles, cand, nuc, row_lx, seq, spart, wpart, tpart;
   size_t k_idx, k_e, k_cnt, k_norm, k_bad, k_px, total;
 };
 
@@ -98,12 +106,14 @@ Layout layout(const sv_config* c, const Plan& pl) {
   L.tiles = take(rows * (size_t)sv::kMaxPartials * sizeof(sv::TileStat));
   L.cand = take(pl.top_k > 0 ? rows * (size_t)pl.S_max * (size_t)pl.cand_w * sizeof(uint64_t) : 0);
   L.nuc = take(pl.filt == sv::kFiltTopp ? rows * sizeof(sv::RowNuc) : 0);
-  const bool sampled = pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp;
+  const bool sampled = pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample;
   L.row_lx = take(sampled ? rows * sizeof(float) : 0);
   L.seq = take(sampled ? B * sizeof(sv::SeqState) : 0);
   L.spart = take(sampled ? B * (size_t)pl.S2_max * sizeof(double) : 0);
   const bool keep = sampled && B * (size_t)pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes;
   L.wpart = take(keep ? B * (size_t)pl.S2_max * sv::kResidSeg * sizeof(double) : 0);
+  L.tpart = take(pl.filt == sv::kFiltTreeSample
+                     ? B * (size_t)sv::kTreePasses * (size_t)c->k * (size_t)pl.S2_max * sizeof(double) : 0);
   L.k_idx = take(rows * K * sizeof(int32_t));
   L.k_e = take(rows * K * sizeof(double));
   L.k_cnt = take(K ? rows * sizeof(int32_t) : 0);
@@ -168,7 +178,10 @@ int specverify_check_args(const sv_config* cfg, int32_t batch, const void* targe
     case SV_MODE_GREEDY:
       if (draft_logits || parents || uniforms || resid_uniforms || out_nodes) return SV_ERR_MODE;
       break;
-    default:  // tree
+    case SV_MODE_TREE_SAMPLE:
+      if (!parents || !draft_logits || !uniforms || !resid_uniforms) return SV_ERR_NULL;
+      break;
+    default:  // greedy tree
       if (!parents) return SV_ERR_NULL;
       if (draft_logits || uniforms || resid_uniforms) return SV_ERR_MODE;
       break;
@@ -229,7 +242,7 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   int rc = specverify_check_args(c, batch, target_logits, draft_logits, draft_tokens, parents,
                                  uniforms, resid_uniforms, accepted_len, out_tokens, out_nodes);
   if (rc != SV_OK) return rc;
-  if (resid_probs && c->mode != SV_MODE_SAMPLE) return SV_ERR_MODE;
+  if (resid_probs && c->mode != SV_MODE_SAMPLE && c->mode != SV_MODE_TREE_SAMPLE) return SV_ERR_MODE;
   if (batch == 0) return SV_OK;
   const Plan& pl = ctx->plan;
 
@@ -252,7 +265,8 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.rows_t = pl.rows_t;
   p.rows_d = pl.rows_d;
   p.out_w = pl.out_w;
-  p.T = c->mode == SV_MODE_SAMPLE ? c->temperature : 1.0;
+  p.T = (c->mode == SV_MODE_SAMPLE || c->mode == SV_MODE_TREE_SAMPLE) ? c->temperature : 1.0;
+  p.tree = (c->mode == SV_MODE_TREE_GREEDY || c->mode == SV_MODE_TREE_SAMPLE) ? 1 : 0;
   p.top_p = pl.top_p;
   p.top_k = pl.top_k;
   // tiling of the streaming pass
@@ -312,7 +326,8 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.seq = (sv::SeqState*)(ws + L.seq);
   p.spart = (double*)(ws + L.spart);
   p.wpart = (double*)(ws + L.wpart);
-  p.keep_w = (pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp) &&
+  p.tpart = (double*)(ws + L.tpart);
+  p.keep_w = (pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample) &&
              (size_t)c->max_batch * pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes ? 1 : 0;
   p.S2 = pl.S2_max;
   p.k_idx = (int32_t*)(ws + L.k_idx);

@@ -65,6 +65,8 @@ struct SeqState {
   double nmc_p, inv_p, nmc_q, inv_q;
   uint64_t cut_p, cut_q;
   int32_t n, st;
+  int32_t node;   // row index of the residual within the sequence (chain: n; tree: final node)
+  int32_t hasq;   // the draft row enters the residual
 };
 
 // Passes of the streaming kernel: argmax (greedy, tree), top-k lists (exact
@@ -72,7 +74,13 @@ struct SeqState {
 // aligned rows), max + sum of exponentials (float64 terms for nucleus rows,
 // float32 terms for plain sampling).
 enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4, kModeStats32 = 5 };
-enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4 };
+enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4,
+              kFiltTreeSample = 5 };
+// Speculative residual passes of tree sampling: pass m (1..kTreePasses)
+// finds the residual normaliser after the m-th rejected child at every node
+// with at least m children.  A walk that rejects more children at one node
+// computes the rest itself.
+constexpr int kTreePasses = 4;
 
 struct Params {
   // inputs
@@ -119,6 +127,8 @@ struct Params {
   double* wpart;     // [B][S2][kResidSeg] residual weights of each segment (keep_w)
   int keep_w;        // small problem: k_resid_s keeps its weights for
                      // k_resid_final (loaded in its first round, no recompute)
+  int tree;          // tree modes: rows have no single drafted token to record
+  double* tpart;     // tree sampling: [B][kTreePasses][N][S2] residual masses per segment
   int S2;            // residual segments per sequence (kResidSeg logits each)
   // top-k: each row's kept set, rank order
   int32_t* k_idx;    // [rows][top_k]

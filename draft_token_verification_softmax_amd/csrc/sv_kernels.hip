@@ -766,7 +766,7 @@ DEV int row_token(const Params& p, int grow, bool* has) {
   int b, j;
   if (grow < nt) { b = grow / p.rows_t; j = grow - b * p.rows_t; }
   else { b = (grow - nt) / p.rows_d; j = (grow - nt) - b * p.rows_d; }
-  *has = j < p.k;
+  *has = !p.tree && j < p.k;
   const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.tokens, p.B * p.k * 4);
   return __builtin_amdgcn_raw_buffer_load_b32(rs, (*has ? b * p.k + j : 0) * 4, 0, 0);
 }
@@ -1329,6 +1329,16 @@ DEV void emit_tokens(const Params& p, int b, const int32_t* x, int n, int y, int
   if (threadIdx.x == 0) {
     p.acc_len[b] = n;
     if (p.seq_status) p.seq_status[b] = status;
+  }
+}
+
+// The drawn token of a sequence whose other outputs are already written
+// (tree sampling: the walk wrote the path), or every output (chain).
+DEV void emit_final(const Params& p, int b, const int32_t* x, int n, int y, int status) {
+  if (p.tree) {
+    if (threadIdx.x == 0) p.out_tokens[(size_t)b * p.out_w + n] = y;
+  } else {
+    emit_tokens(p, b, x, n, y, status);
   }
 }
 
@@ -2029,7 +2039,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
       SeqState ss;
       ss.nmc_p = pr.nmc; ss.inv_p = pr.inv; ss.cut_p = pr.cut;
       ss.nmc_q = qr.nmc; ss.inv_q = qr.inv; ss.cut_q = qr.cut;
-      ss.n = n; ss.st = sh_st;
+      ss.n = n; ss.st = sh_st; ss.node = n; ss.hasq = n < k;
       p.seq[b] = ss;
     }
   }
@@ -2070,9 +2080,10 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
 #pragma unroll
     for (int q = 0; q < kVec / 2; ++q) { const d2 x = wp[q]; w[2 * q] = x.x; w[2 * q + 1] = x.y; }
   }
-  if (tid < k) sx[tid] = xl;
+  if (!p.tree && tid < k) sx[tid] = xl;   // chain: k <= 64
   if (ss.n < 0) return;
-  const int n = ss.n;
+  const int n = ss.n, node = ss.node;
+  const bool hasq = ss.hasq != 0;
   // S' = sum of the segment masses (a thread owning more than kPer reads
   // the rest from global memory: vocabularies above kSegStage * kResidSeg)
   double lsum = 0.0;
@@ -2085,7 +2096,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
     // empty residual: p'_n, drawn and written by one workgroup
     if (seg != 0) return;
     exp2_table_init(tab);
-    const RowView pr{row_ptr<T>(p, trow(p, b, n)), ss.nmc_p, ss.inv_p, ss.cut_p};
+    const RowView pr{row_ptr<T>(p, trow(p, b, node)), ss.nmc_p, ss.inv_p, ss.cut_p};
     const RowView none{nullptr, 0.0, 1.0, 0ull};
     double S1;
     const int y = resid_draw<T>(pr, c64, tab, V, p.aligned, ur, red, redi, &S1);
@@ -2101,7 +2112,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
         }
       }
     }
-    emit_tokens(p, b, sx, n, y, ss.st);
+    emit_final(p, b, sx, n, y, ss.st);
     return;
   }
   // the segment where t = ur * S' falls (or the last one with mass)
@@ -2144,9 +2155,9 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   if (!p.keep_w) {
     // large problems: recompute this segment's weights
     exp2_table_init(tab);
-    const RowView pr{row_ptr<T>(p, trow(p, b, n)), ss.nmc_p, ss.inv_p, ss.cut_p};
-    const RowView qr{n < k ? row_ptr<T>(p, drow(p, b, n)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
-    resid_weights<T>(pr, qr, n < k, c64, tab, V, p.aligned, c0 + tid * kVec, w);
+    const RowView pr{row_ptr<T>(p, trow(p, b, node)), ss.nmc_p, ss.inv_p, ss.cut_p};
+    const RowView qr{hasq ? row_ptr<T>(p, drow(p, b, node)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
+    resid_weights<T>(pr, qr, hasq, c64, tab, V, p.aligned, c0 + tid * kVec, w);
   }
   if (seg == c) {
     double tl = 0.0;
@@ -2155,7 +2166,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
     double tc;
     const double ex = block_exscan(tl, red, &tc);
     const int y = pick_in_chunk(base, ex, w, c0, t, redi);
-    emit_tokens(p, b, sx, n, y, ss.st);
+    emit_final(p, b, sx, n, y, ss.st);
   }
   if (p.resid_probs) {
     float* rp = p.resid_probs + (size_t)b * V;
@@ -2165,6 +2176,289 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
       if (v < V) rp[v] = (float)(w[q] / S);
     }
   }
+}
+
+// ================================================================== tree sampling
+//
+// Modified rejection sampling down a token tree: the children of the
+// accepted node are tried in index order against a running target, which a
+// rejected child replaces by the renormalised residual.  With p' and q' the
+// node's adjusted target and draft rows, the running target after some
+// rejected children is r = max(0, p' - c q') / D: (c, D) = (0, 1) at first,
+// and a rejection gives (c, D) <- (c + D, F(c + D)), F(c) = sum_v max(0,
+// p'(v) - c q'(v)), unless F(c + D) = 0 (then r stays), because
+// max(0, r - q') = max(0, p' - (c + D) q') / D.  Every F needs a pass over
+// the node's two rows, so the passes run ahead, wide: pass m (grid: segment x
+// tree x node) adds one segment's share of F after m rejections at every
+// node with more than m children, the states rebuilt from the earlier
+// passes in a fixed order.  The walk (one workgroup per tree) then only
+// reads them, unless one node rejects more than kTreePasses children.  The
+// final draw is the plain-sampling draw over max(0, p' - c q') at the final
+// node.
+
+// F of pass m (0-based) at node u: the pass's segment sums in a fixed order
+// (lane l adds segments l, l + 64, ...; then the wave's fixed-order sum).
+// Call from all 64 lanes of one wave.
+DEV double tree_F(const Params& p, int b, int m, int u) {
+  const double* src = p.tpart + (((size_t)b * kTreePasses + m) * p.k + u) * p.S2;
+  double t = 0.0;
+  for (int s = threadIdx.x & 63; s < p.S2; s += 64) t += src[s];
+  return wave_sum(t);
+}
+
+// Views of node u's target row (sv[0], sv[1]) and draft row (sv[2], sv[3]):
+// -M * c64 and 1 / Z from the row partials; sbad[0..1] their bad flags.
+// Every thread calls it; the results are in LDS after the call.  (Four
+// partials per lane, as in the residual passes, so both see the same bits.)
+DEV void tree_views(const Params& p, int b, int u, double c64, double* sv, int* sbad) {
+  combine_rows<true, 4>(p, 2, [&](int r) { return r == 0 ? trow(p, b, u) : drow(p, b, u); },
+                        [&](int r, float M, int, double Z, int bad) {
+                          sv[2 * r] = -(double)M * c64;
+                          sv[2 * r + 1] = 1.0 / Z;
+                          sbad[r] = bad;
+                        });
+  __syncthreads();
+}
+
+// Indices i < n with pred(i), in increasing order, into out; returns their
+// count.  Every thread calls it.
+template <typename Pred>
+DEV int block_list(int n, Pred pred, int* out, int* wsum) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int total = 0;
+  for (int base = 0; base < n; base += kBlock) {
+    const int i = base + (int)threadIdx.x;
+    const bool f = i < n && pred(i);
+    const uint64_t msk = __ballot(f);
+    if (lane == 0) wsum[w] = __popcll(msk);
+    __syncthreads();
+    int off = total, tot = 0;
+    for (int q = 0; q < kWaves; ++q) { if (q < w) off += wsum[q]; tot += wsum[q]; }
+    if (f) out[off + __popcll(msk & ((1ull << lane) - 1ull))] = i;
+    total += tot;
+    __syncthreads();
+  }
+  return total;
+}
+
+constexpr int kTreeMax = 1024;   // nodes per tree (the API's limit)
+constexpr int kPassBatch = 4;    // nodes whose segment loads are in flight together
+
+// Pass m (0-based): grid (segment, tree).  For every node u with more than
+// m children, segment `seg` of F(c_m + D_m) at u.  The nodes' row views and
+// states are gathered first (all loads of a kind in one round); the segment
+// sums then run kPassBatch nodes at a time.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
+  __shared__ int nch[kTreeMax], lst[kTreeMax];
+  __shared__ double vv[kTreeMax][4];
+  __shared__ double cn[kTreeMax];
+  __shared__ double red[kPassBatch][kWaves];
+  __shared__ double tab[64];
+  __shared__ int wsum[kWaves];
+  const int seg = blockIdx.x, b = blockIdx.y;
+  const int N = p.k, V = p.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const double c64 = 64.0 * kLog2e / p.T;
+  for (int i = tid; i < N; i += kBlock) nch[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < N; i += kBlock) {
+    const int q = p.parents[(size_t)b * N + i];
+    if (i > 0 && q >= 0 && q < i) atomicAdd(&nch[q], 1);
+  }
+  __syncthreads();
+  const int nl = block_list(N, [&](int i) { return nch[i] > m; }, lst, wsum);
+  if (nl == 0) return;
+  exp2_table_init(tab);
+  combine_rows<true, 4>(p, 2 * nl,
+                        [&](int r) { return r < nl ? trow(p, b, lst[r]) : drow(p, b, lst[r - nl]); },
+                        [&](int r, float M, int, double Z, int) {
+                          const int l = r < nl ? r : r - nl, o = r < nl ? 0 : 2;
+                          vv[l][o] = -(double)M * c64;
+                          vv[l][o + 1] = 1.0 / Z;
+                        });
+  // states after m rejections (one wave per node)
+  for (int l = w; l < nl; l += kWaves) {
+    double c = 0.0, D = 1.0;
+    for (int j = 0; j < m; ++j) {
+      const double F = tree_F(p, b, j, lst[l]);
+      if (F > 0.0) { c = c + D; D = F; }
+    }
+    if (lane == 0) cn[l] = c + D;
+  }
+  __syncthreads();
+  const int pos = seg * kResidSeg + tid * kVec;
+  for (int l0 = 0; l0 < nl; l0 += kPassBatch) {
+    double t[kPassBatch];
+#pragma unroll
+    for (int q = 0; q < kPassBatch; ++q) {
+      const int l = l0 + q < nl ? l0 + q : l0;
+      const int u = lst[l];
+      const RowView pr{row_ptr<T>(p, trow(p, b, u)), vv[l][0], vv[l][1], 0ull};
+      const RowView qr{row_ptr<T>(p, drow(p, b, u)), vv[l][2], vv[l][3] * cn[l], 0ull};
+      double wq[kVec];
+      t[q] = resid_weights<T>(pr, qr, true, c64, tab, V, p.aligned, pos, wq);
+    }
+#pragma unroll
+    for (int q = 0; q < kPassBatch; ++q) {
+      const double ws = wave_sum(t[q]);
+      if (lane == 0) red[q][w] = ws;
+    }
+    __syncthreads();
+    if (tid < kPassBatch && l0 + tid < nl) {
+      const double tot = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
+      p.tpart[(((size_t)b * kTreePasses + m) * N + lst[l0 + tid]) * p.S2 + seg] = tot;
+    }
+    __syncthreads();
+  }
+}
+
+
+// The walk of one tree (one workgroup per tree): validity, the accept tests
+// down the branches, the outputs but the drawn token, and the state of the
+// final draw.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
+  __shared__ int par[kTreeMax], nch[kTreeMax], tok[kTreeMax], lst[kTreeMax], path[kTreeMax];
+  __shared__ float uu[kTreeMax], lpx[kTreeMax], lqx[kTreeMax];
+  __shared__ unsigned char rbad[2 * kTreeMax];
+  __shared__ double red[kWaves];
+  __shared__ double tab[64];
+  __shared__ double sv[4];
+  __shared__ int sbad[2];
+  __shared__ int wsum[kWaves];
+  __shared__ double sh_F;
+  const int b = blockIdx.x, N = p.k, V = p.V, tid = threadIdx.x;
+  const double c64 = 64.0 * kLog2e / p.T;
+  // one round of loads: parents, tokens, uniforms
+  int badpar = 0;
+  for (int i = tid; i < N; i += kBlock) {
+    const int q = p.parents[(size_t)b * N + i];
+    const int ok = i > 0 ? (q >= 0 && q < i) : 1;
+    par[i] = (i > 0 && ok) ? q : -1;
+    badpar |= i > 0 ? !ok : (q != -1);
+    tok[i] = p.tokens[(size_t)b * N + i];
+    uu[i] = p.u[(size_t)b * N + i];
+    nch[i] = 0;
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += kBlock) if (par[i] >= 0) atomicAdd(&nch[par[i]], 1);
+  // rows: every target row, and the draft row of every node with a child
+  combine_rows<true>(p, 2 * N, [&](int r) { return r < N ? trow(p, b, r) : drow(p, b, r - N); },
+                     [&](int r, float, int, double, int bad) { rbad[r] = (unsigned char)bad; });
+  badpar = __syncthreads_or(badpar);
+  int mybad = 0;
+  for (int i = tid; i < N; i += kBlock) mybad |= rbad[i] | (nch[i] > 0 ? rbad[N + i] : 0);
+  if (__syncthreads_or(mybad)) {
+    emit_invalid(p, b, 4);
+    if (tid == 0) p.seq[b].n = -1;
+    return;
+  }
+  // the logits the tests read: child c's token in its parent's two rows
+  for (int i = tid; i < N; i += kBlock) {
+    const int x = tok[i], q = par[i];
+    float a = 0.f, d = 0.f;
+    if (q >= 0 && x >= 0 && x < V) {
+      a = Io<T>::at(row_ptr<T>(p, trow(p, b, q)), x);
+      d = Io<T>::at(row_ptr<T>(p, drow(p, b, q)), x);
+    }
+    lpx[i] = a;
+    lqx[i] = d;
+  }
+  exp2_table_init(tab);
+  // the walk (every thread follows it; F values from wave 0)
+  int st = 0, cur = 0, n = 0;
+  double c = 0.0, D = 1.0;
+  if (tid == 0) path[0] = 0;
+  for (;;) {
+    c = 0.0;   // a new node: the running target is p'
+    D = 1.0;
+    const int nk = block_list(N, [&](int i) { return par[i] == cur; }, lst, wsum);
+    if (nk == 0) break;
+    tree_views(p, b, cur, c64, sv, sbad);
+    int nxt = -1;
+    for (int j = 0; j < nk; ++j) {
+      const int ch = lst[j];
+      const int x = tok[ch];
+      bool acc = false;
+      if (x < 0 || x >= V) {
+        st |= 1;
+      } else {
+        const double pa = exp2_64(fma((double)lpx[ch], c64, sv[0]), tab) * sv[1];
+        const double qa = exp2_64(fma((double)lqx[ch], c64, sv[2]), tab) * sv[3];
+        const double dd = pa - c * qa;
+        const double a = (dd > 0.0 ? dd : 0.0) / D;
+        acc = qa > 0.0 ? ((double)uu[ch] < fmin(1.0, a / qa)) : (a > 0.0);
+      }
+      if (acc) { nxt = ch; break; }
+      // rejected: F at c + D, from pass j, or from a pass of this workgroup
+      double F;
+      if (j < kTreePasses) {
+        if (tid < 64) {
+          const double f = tree_F(p, b, j, cur);
+          if (tid == 0) sh_F = f;
+        }
+        __syncthreads();
+        F = sh_F;
+        __syncthreads();
+      } else {
+        const double cn = c + D;
+        const RowView pr{row_ptr<T>(p, trow(p, b, cur)), sv[0], sv[1], 0ull};
+        const RowView qr{row_ptr<T>(p, drow(p, b, cur)), sv[2], sv[3] * cn, 0ull};
+        double t = 0.0;
+        for (int c0 = 0; c0 < V; c0 += kResidSeg) {
+          double w[kVec];
+          t += resid_weights<T>(pr, qr, true, c64, tab, V, p.aligned, c0 + tid * kVec, w);
+        }
+        F = block_sum(t, red);
+      }
+      if (F > 0.0) { c = c + D; D = F; }
+    }
+    if (nxt < 0) break;
+    ++n;
+    cur = nxt;
+    if (tid == 0) path[n] = cur;
+  }
+  __syncthreads();
+  // outputs but the drawn token (position n), and the draw's state
+  int32_t* ot = p.out_tokens + (size_t)b * p.out_w;
+  for (int i = tid; i < p.out_w; i += kBlock) {
+    if (i != n) ot[i] = i < n ? tok[path[i + 1]] : -1;
+    if (p.out_nodes) p.out_nodes[(size_t)b * p.out_w + i] = i <= n ? path[i] : -1;
+  }
+  tree_views(p, b, cur, c64, sv, sbad);
+  if (tid == 0) {
+    p.acc_len[b] = n;
+    const int status = st | (badpar ? 2 : 0);
+    if (p.seq_status) p.seq_status[b] = status;
+    SeqState ss;
+    ss.nmc_p = sv[0]; ss.inv_p = sv[1]; ss.cut_p = 0ull;
+    ss.nmc_q = sv[2]; ss.inv_q = sv[3] * c; ss.cut_q = 0ull;
+    ss.n = n; ss.st = status; ss.node = cur; ss.hasq = c > 0.0;
+    p.seq[b] = ss;
+  }
+}
+
+// Residual mass per segment of the final draw: grid (segment, tree).
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_tsample_mass(Params p) {
+  __shared__ double red[kWaves];
+  __shared__ double tab[64];
+  const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  const double c64 = 64.0 * kLog2e / p.T;
+  const SeqState ss = p.seq[b];
+  exp2_table_init(tab);
+  if (ss.n < 0) return;
+  const RowView pr{row_ptr<T>(p, trow(p, b, ss.node)), ss.nmc_p, ss.inv_p, ss.cut_p};
+  const RowView qr{ss.hasq ? row_ptr<T>(p, drow(p, b, ss.node)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
+  double w[kVec];
+  const double t = resid_weights<T>(pr, qr, ss.hasq != 0, c64, tab, p.V, p.aligned, seg * kResidSeg + tid * kVec, w);
+  if (p.keep_w) {
+    d2* wp = reinterpret_cast<d2*>(p.wpart + ((size_t)b * p.S2 + seg) * kResidSeg + tid * kVec);
+#pragma unroll
+    for (int q = 0; q < kVec / 2; ++q) wp[q] = d2{w[2 * q], w[2 * q + 1]};
+  }
+  const double tot = block_sum(t, red);
+  if (tid == 0) p.spart[(size_t)b * p.S2 + seg] = tot;
 }
 
 // ================================================================== stream kernel
@@ -2802,6 +3096,14 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
       hipLaunchKernelGGL((k_resid_s<T, kFiltTopp>), gs, block, 0, st, p);
       hipLaunchKernelGGL((k_resid_final<T, kFiltTopp>), gs, block, 0, st, p);
       break;
+    case kFiltTreeSample: {
+      const int passes = p.k - 1 < kTreePasses ? p.k - 1 : kTreePasses;
+      for (int m = 0; m < passes; ++m) hipLaunchKernelGGL((k_tsample_pass<T>), gs, block, 0, st, p, m);
+      hipLaunchKernelGGL((k_tsample_walk<T>), gb, block, 0, st, p);
+      hipLaunchKernelGGL((k_tsample_mass<T>), gs, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), gs, block, 0, st, p);
+      break;
+    }
     default:  // plain sampling
       hipLaunchKernelGGL((k_resid_s<T, kFiltNone>), gs, block, 0, st, p);
       hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), gs, block, 0, st, p);

@@ -21,6 +21,8 @@ the verifier's and the draft model's outputs):
      V=128256, bf16 t ~ N(0, 3^2) per node
   5  chain, B=256, k=4, V=152064, fp32: t ~ N(0, 2.5^2), d = 0.8 t + N(0, 1^2);
      T=0.8, top-p 0.9
+  6  sampled tree, the shape of workload 4 with draft rows d = t + N(0, 1^2)
+     per node and tokens drawn by the caller from the draft row at the parent
 
 Draft logits are made from the unrounded target before both are rounded to
 the storage dtype (bf16 with round-to-nearest-even).
@@ -40,6 +42,9 @@ CONFIGS = {
             rho=0.5, sd=3.0),
     5: dict(kind="chain", B=256, k=4, V=152064, dtype="f32", T=0.8, top_k=0, top_p=0.9,
             recipe="gauss", sd=2.5, noise=1.0, draft_scale=0.8),
+    # the sampling twin of workload 4 (tree_sample_inputs)
+    6: dict(kind="tree_sample", B=8, N=60, V=128256, dtype="bf16", T=1.0, max_depth=6,
+            max_children=4, sd=3.0, noise=1.0),
 }
 
 DEFAULT_SEED = {c: 1000 + c for c in CONFIGS}
@@ -204,3 +209,36 @@ def rows_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return bf16_to_f32(a).astype(np.float64)
     return np.asarray(a, dtype=np.float64)
+
+
+def tree_sample_inputs(seed: int = 1006, B: int = 8, N: int = 60, V: int = 128256,
+                       dtype: str = "bf16", T: float = 1.0, sd: float = 3.0, noise: float = 1.0,
+                       max_depth: int = 6, max_children: int = 4):
+    """Seeded inputs of a sampled token tree (the sampling twin of workload 4).
+
+    The tree shape follows ``tree_inputs`` (parent uniform over the earlier
+    nodes below max_depth with fewer than max_children children).  Target
+    rows t ~ N(0, sd^2) per node, draft rows d = t + N(0, noise^2) (made
+    before rounding to the storage dtype); uniforms u [B, N] and ur [B] for
+    the tests, and draw_u [B, N] with which the caller draws node i's token
+    from the draft's adjusted distribution at its parent (the draft model's
+    own draw, done by the caller).
+    """
+    rng = np.random.default_rng(seed)
+    t64 = rng.normal(0.0, sd, size=(B, N, V))
+    d64 = t64 + rng.normal(0.0, noise, size=(B, N, V))
+    parents = np.full((B, N), -1, dtype=np.int32)
+    for b in range(B):
+        depth = [0] * N
+        nchild = [0] * N
+        for i in range(1, N):
+            elig = [j for j in range(i) if depth[j] < max_depth and nchild[j] < max_children]
+            par = elig[int(rng.integers(len(elig)))]
+            parents[b, i] = par
+            depth[i] = depth[par] + 1
+            nchild[par] += 1
+    u = rng.random((B, N)).astype(np.float32)
+    ur = rng.random(B).astype(np.float32)
+    draw_u = rng.random((B, N))
+    return dict(target=_store(t64, dtype), draft=_store(d64, dtype), parents=parents, u=u, ur=ur,
+                draw_u=draw_u, dtype=dtype, T=T, B=B, N=N, V=V)

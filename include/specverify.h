@@ -42,6 +42,24 @@
  *     depth (smallest index on ties).  Emitted: the tokens on the path root ->
  *     d* (root excluded), then argmax(row d*).
  *
+ *   SV_MODE_TREE_SAMPLE -- modified rejection sampling down a token tree.
+ *     Source: the same article, "One decode round, end to end" (the
+ *     accept-or-correct rule of "The core idea" applied down the branches,
+ *     one correction resampled at the first rejection) and "Why it changes
+ *     nothing about the output".  The pages give no rule for several
+ *     children of one node; this library tries them in index order against
+ *     a running target: at the accepted node u (root first), r = p'_u;
+ *     child c with token x is accepted iff q'_u(x) > 0 and u_c < min(1,
+ *     r(x)/q'_u(x)), or q'_u(x) = 0 and r(x) > 0; a rejected child replaces r
+ *     by max(0, r - q'_u) renormalised (unless that is all zero).  The
+ *     first accepted child becomes the node; when none is, or u has no
+ *     child, y is drawn from r with the tree's uniform as in SV_MODE_SAMPLE.
+ *     Row i of the target and of the draft is that model's distribution for
+ *     node i's children (adjusted by the temperature; top-k and top-p are
+ *     not available in this mode); the children of a node are taken to be
+ *     drawn independently from q'_u, which makes the emitted tokens follow
+ *     the target.  Emitted: the path's tokens (root excluded), then y.
+ *
  * Layout: all arrays are dense, row-major, vocabulary fastest, and live in
  * device memory on the context's device.  Logits are float32 or bf16 (raw
  * 16-bit patterns).  Tokens and outputs are int32; uniforms are float32 in
@@ -73,14 +91,15 @@ extern "C" {
 
 typedef struct specverify_ctx specverify_ctx;   /* opaque; owns the workspace only */
 
-enum { SV_MODE_SAMPLE = 0, SV_MODE_GREEDY = 1, SV_MODE_TREE_GREEDY = 2 };
+enum { SV_MODE_SAMPLE = 0, SV_MODE_GREEDY = 1, SV_MODE_TREE_GREEDY = 2, SV_MODE_TREE_SAMPLE = 3 };
 enum { SV_DTYPE_F32 = 0, SV_DTYPE_BF16 = 1 };
 enum {
   SV_OK = 0,
   SV_ERR_NULL = -1,      /* a required pointer is NULL */
   SV_ERR_SHAPE = -2,     /* batch / k / vocab out of range */
   SV_ERR_DTYPE = -3,     /* unknown dtype */
-  SV_ERR_PARAM = -4,     /* temperature <= 0 or not finite, top_k < 0 or too large, top_p not in (0, 1] */
+  SV_ERR_PARAM = -4,     /* temperature <= 0 or not finite, top_k < 0 or too large, top_p not in (0, 1];
+                            TREE_SAMPLE with top-k or top-p */
   SV_ERR_CAPACITY = -5,  /* batch > max_batch */
   SV_ERR_HIP = -6,       /* a HIP call failed (allocation, launch, no device) */
   SV_ERR_MODE = -7,      /* unknown mode, or a pointer given / missing for this mode */
@@ -119,6 +138,9 @@ int specverify_create(const sv_config* cfg, int device, specverify_ctx** out);
  *   TREE_GREEDY: target, draft_tokens (the node tokens), parents, accepted_len,
  *           out_tokens required; draft, uniforms, resid_uniforms must be NULL;
  *           out_nodes optional.
+ *   TREE_SAMPLE: target, draft, draft_tokens (the node tokens), parents,
+ *           uniforms, resid_uniforms, accepted_len, out_tokens required;
+ *           out_nodes optional.
  * batch = 0 is valid (nothing to do; every pointer may then be NULL);
  * batch > cfg->max_batch is SV_ERR_CAPACITY. */
 int specverify_check_args(const sv_config* cfg, int32_t batch,
@@ -130,18 +152,20 @@ int specverify_check_args(const sv_config* cfg, int32_t batch,
 
 /* Verify one batch.  Shapes (B = batch, k and V from the context's config):
  *   target_logits  [B, k+1, V] chain | [B, N, V] tree      dtype per config
- *   draft_logits   [B, k, V]   SAMPLE only
+ *   draft_logits   [B, k, V]   SAMPLE | [B, N, V] TREE_SAMPLE
  *   draft_tokens   [B, k] chain | [B, N] tree (entry 0, the root, is ignored)
- *   parents        [B, N]      TREE_GREEDY only; parents[b, 0] = -1, parents[b, i] < i
- *   uniforms       [B, k]      SAMPLE: accept-test uniforms u_j
- *   resid_uniforms [B]         SAMPLE: the one uniform for the replacement OR bonus draw
+ *   parents        [B, N]      tree modes; parents[b, 0] = -1, parents[b, i] < i
+ *   uniforms       [B, k]      SAMPLE: accept-test uniforms u_j | [B, N] TREE_SAMPLE: node i's
+ *                             uniform (entry 0 unused)
+ *   resid_uniforms [B]         SAMPLE, TREE_SAMPLE: the one uniform for the replacement OR bonus draw
  *   accepted_len   [B]    out: n (tree: depth of the deepest accepted node)
  *   out_tokens     [B, k+1] chain | [B, N] tree   out: n accepted tokens, then the
  *                             replacement / bonus / correction; remaining entries -1
  *   out_nodes      [B, N]  out, tree only, optional: node ids of the path root..d*
  *                             (out_nodes[b, i] is the node whose row gave out_tokens[b, i]); rest -1
- *   resid_probs    [B, V]  out, SAMPLE only, optional (debug): the normalised distribution
- *                             the last token was drawn from (residual, or p'_k after full acceptance)
+ *   resid_probs    [B, V]  out, SAMPLE and TREE_SAMPLE, optional (debug): the normalised
+ *                             distribution the last token was drawn from (residual, or p' of the
+ *                             last row after full acceptance)
  *   seq_status     [B]     out, optional: SV_STATUS_* bits
  *   stream         hipStream_t the work is queued on (NULL = default stream)
  * Returns SV_OK once the work is queued. */

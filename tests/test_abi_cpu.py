@@ -10,7 +10,8 @@ import pytest
 import draft_token_verification_softmax_amd as svm
 from draft_token_verification_softmax_amd import (
     SV_DTYPE_BF16, SV_DTYPE_F32, SV_ERR_CAPACITY, SV_ERR_DTYPE, SV_ERR_MODE, SV_ERR_NULL,
-    SV_ERR_PARAM, SV_ERR_SHAPE, SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_TREE_GREEDY, SV_OK,
+    SV_ERR_PARAM, SV_ERR_SHAPE, SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_TREE_GREEDY,
+    SV_MODE_TREE_SAMPLE, SV_OK,
     make_config, specverify_check_args)
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "specverify.h")
@@ -137,6 +138,24 @@ def test_batch_and_pointer_rules():
     assert check(t, parents=None, **ok) == SV_ERR_NULL
     assert check(t, parents=P, out_nodes=P, **ok) == SV_OK
     assert check(t, parents=P, draft=P, uniforms=None, resid_uniforms=None) == SV_ERR_MODE
+
+
+def test_tree_sample_rules():
+    t = make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, temperature=0.8)
+    assert check(t, parents=P) == SV_OK
+    assert check(t, parents=P, out_nodes=P) == SV_OK
+    for name in ("parents", "draft", "uniforms", "resid_uniforms", "target", "draft_tokens"):
+        kw = dict(parents=P)
+        kw[name] = None
+        assert check(t, **kw) == SV_ERR_NULL, name
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 1024, 1000), parents=P) == SV_OK
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 1025, 1000), parents=P) == SV_ERR_SHAPE
+    # temperature only: top-k or top-p are refused; top_k >= V means off
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_k=50), parents=P) == SV_ERR_PARAM
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_p=0.9), parents=P) == SV_ERR_PARAM
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_k=1000), parents=P) == SV_OK
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, temperature=0.0), parents=P) == SV_ERR_PARAM
+    assert svm.load().specverify_workspace_bytes(ctypes.byref(t)) > 0
 
 
 def test_null_config_and_bad_create_make_no_hip_call():
