@@ -1670,7 +1670,7 @@ static_assert(kMergeCap % 64 == 0 && kMergeCap >= 2 * kUnroll * kBlock, "merge l
 static_assert(kTopkCap * 8 + kTopkCap * 2 <= kMergeCap * 8, "the exact tile pass fits in the merge list");
 
 template <typename T>
-__global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
+DEV void merge_row_block(const Params& p, const int grow) {
   __shared__ uint64_t surv[kMergeCap];
   __shared__ uint64_t top[kTopkMax];
   __shared__ int tcnt[kMaxTiles];
@@ -1685,7 +1685,6 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
   __shared__ double sh_mass, sh_px;
   __shared__ float sh_tau;
   __shared__ int ns;
-  const int grow = blockIdx.x;
   const int tid = threadIdx.x;
   const int K = p.top_k, S = p.S, cw = p.cand_w;
   const uint64_t* src = p.cand + (size_t)grow * S * cw;
@@ -1830,6 +1829,320 @@ __global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
     p.k_bad[grow] = bad ? 1 : 0;
     p.k_px[grow] = sh_px;
   }
+  __syncthreads();
+}
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_topk_rows(Params p) {
+  merge_row_block<T>(p, blockIdx.x);
+}
+
+// The drafted token whose p'(x) the row's accept test reads (-1 if none).
+DEV int merge_row_token(const Params& p, int grow) {
+  const int nt = p.B * p.rows_t;
+  int j, b;
+  if (grow < nt) { b = grow / p.rows_t; j = grow - b * p.rows_t; if (j >= p.k) j = -1; }
+  else { b = (grow - nt) / p.rows_d; j = (grow - nt) - b * p.rows_d; }
+  return j >= 0 ? p.tokens[(size_t)b * p.k + j] : -1;
+}
+
+// The same merge for one row in one wave (top_k <= 64, filter lists): the
+// row's partials (one round of loads), the sublists' entries at or above
+// the largest tile bound (one more round) into the wave's LDS list, ranks
+// by counting over that list, the kept set in rank order, and its float64
+// softmax (nucleus on top if asked) with DPP scans.  Returns false, having
+// written nothing, for a row the wave cannot take (a tile whose list
+// overflowed, or more than kWaveCand survivors); the block merge does it.
+constexpr int kWaveCand = 256;   // survivors one wave ranks (four per lane)
+constexpr int kWaveSubl = 16;    // sublists whose entries are loaded per round
+
+template <typename T>
+DEV bool merge_row_wave(const Params& p, int grow, uint64_t* lst, int x) {
+  const int lane = threadIdx.x & 63;
+  const int K = p.top_k, S = p.S, P = p.P, cw = p.cand_w;
+  constexpr int BITS = sizeof(T) == 2 ? 16 : 32;
+  const uint64_t* src = p.cand + (size_t)grow * S * cw;
+  // one round of loads: the partials (lane holds l, l + 64, l + 128, l + 192)
+  // and, unconditionally, slot `lane` of the first kWaveSubl sublists
+  // (sublist i = tile i / kWaves, wave i % kWaves; masked by the counts
+  // once they arrive)
+  TileStat ts[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = lane + 64 * q;
+    ts[q] = p.tiles[(size_t)grow * P + (i < P ? i : 0)];
+  }
+  uint64_t key[kWaveSubl];
+#pragma unroll
+  for (int q = 0; q < kWaveSubl; ++q) {
+    const int i = q < P ? q : 0;
+    key[q] = src[(size_t)(i / kWaves) * cw + (i % kWaves) * kWaveList + lane];
+  }
+  float tau = -INFINITY;
+  int cnt[4];
+  bool nanr = false, over = false;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = lane + 64 * q;
+    cnt[q] = i < P ? ts[q].amax : 0;
+    if (i < P) {
+      tau = fmaxf(tau, ts[q].m);
+      nanr |= ts[q].s != ts[q].s;
+      over |= ts[q].amax > kWaveList;
+    }
+  }
+  if (__ballot(over)) return false;
+  tau = wave_max(tau);
+  const bool bad_partial = __ballot(nanr) != 0ull;
+  // entries at or above the largest tile bound (all of the row's top_k)
+  int n = 0;
+  for (int i0 = 0; i0 < P; i0 += kWaveSubl) {
+    if (i0 > 0) {
+#pragma unroll
+      for (int q = 0; q < kWaveSubl; ++q) {
+        const int i = i0 + q < P ? i0 + q : 0;
+        key[q] = src[(size_t)(i / kWaves) * cw + (i % kWaves) * kWaveList + lane];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kWaveSubl; ++q) {
+      const int i = i0 + q;
+      const int c = read_lane(cnt[(i >> 6) & 3], i & 63);   // uniform index
+      const bool take = i < P && lane < c && packed_val(key[q]) >= tau;
+      const uint64_t m = __ballot(take);
+      const int at = n + __popcll(m & ((1ull << lane) - 1ull));
+      if (take && at < kWaveCand) lst[at] = key[q];
+      n += __popcll(m);
+    }
+  }
+  if (n > kWaveCand) return false;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  uint64_t mine[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) mine[q] = lane + 64 * q < n ? lst[lane + 64 * q] : 0ull;
+  const int nk = n < K ? n : K;
+  uint64_t key_l = 0ull;   // this lane's kept entry (lane < nk)
+  if (p.top_p < 1.0) {
+    // the nucleus needs rank order: ranks by counting (keys are distinct)
+    int rank[4] = {0, 0, 0, 0};
+    for (int j = 0; j < n; ++j) {
+      const uint64_t o = lst[j];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) rank[q] += o > mine[q];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (lane + 64 * q < n && rank[q] < nk) lst[rank[q]] = mine[q];
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    key_l = lane < nk ? lst[lane] : 0ull;
+  } else {
+    // any fixed order will do: the top_k-th largest key by radix selects
+    // (value bits, then index bits among the ties); the kept entries are
+    // compacted in list order
+    uint64_t thr = 0ull;
+    if (n > K) {
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) hi[q] = (uint32_t)(mine[q] >> 32);
+      const uint32_t h = wave_kth_key<4, BITS>(hi, K);
+      int gt = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        gt += __popcll(__ballot(hi[q] > h));
+        lo[q] = hi[q] == h ? (uint32_t)mine[q] : 0u;
+      }
+      const uint32_t l = wave_kth_key<4, 32>(lo, K - gt);
+      thr = ((uint64_t)h << 32) | l;
+    }
+    int at = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool kp = lane + 64 * q < n && mine[q] >= thr;
+      const uint64_t m = __ballot(kp);
+      const int pos = at + __popcll(m & ((1ull << lane) - 1ull));
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      if (kp) lst[pos] = mine[q];
+      at += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    key_l = lane < nk ? lst[lane] : 0ull;
+  }
+  const float v0 = nk > 0 ? packed_val(wave_max_t(key_l)) : -INFINITY;
+  const bool bad = bad_partial || (v0 != v0) || (v0 == INFINITY) || (v0 == -INFINITY);
+  const double invT = 1.0 / p.T;
+  const double zm = (double)v0 * invT;
+  double e = 0.0;
+  int idx = -1;
+  if (lane < nk) {
+    idx = packed_idx(key_l);
+    e = bad ? 0.0 : exp((double)packed_val(key_l) * invT - zm);
+    p.k_idx[(size_t)grow * K + lane] = idx;
+    p.k_e[(size_t)grow * K + lane] = e;
+  }
+  const double inc = wave_scan(e, 0.0, [](double a, double b2) { return a + b2; });
+  const double Z = read_lane(inc, 63);
+  int kept = nk;
+  double norm = Z;
+  if (p.top_p < 1.0 && nk > 0 && !bad) {
+    const double ex = lane_before(inc, 0.0);
+    kept = wave_max_t((lane < nk && ex < p.top_p * Z) ? lane + 1 : 1);
+    norm = read_lane(inc, kept - 1);
+  }
+  const uint64_t hit = __ballot(idx >= 0 && idx == x && lane < kept);
+  const double px = hit ? read_lane(e, __ffsll((unsigned long long)hit) - 1) / norm : 0.0;
+  if (lane == 0) {
+    p.k_cnt[grow] = kept;
+    p.k_norm[grow] = norm;
+    p.k_bad[grow] = bad ? 1 : 0;
+    p.k_px[grow] = px;
+  }
+  return true;
+}
+
+// One row per wave, four per workgroup; rows a wave cannot take go to the
+// block merge, one after another, with the whole workgroup.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_topk_rows_w(Params p) {
+  __shared__ uint64_t wl[kWaves][kWaveCand];
+  __shared__ int need[kWaves];
+  const int w = threadIdx.x >> 6;
+  const int rows = p.B * (p.rows_t + p.rows_d);
+  const int grow = blockIdx.x * kWaves + w;
+  bool ok = true;
+  if (grow < rows) ok = merge_row_wave<T>(p, grow, wl[w], merge_row_token(p, grow));
+  if ((threadIdx.x & 63) == 0) need[w] = ok ? 0 : 1;
+  __syncthreads();
+  for (int q = 0; q < kWaves; ++q)
+    if (need[q]) merge_row_block<T>(p, blockIdx.x * kWaves + q);
+}
+
+// The same for top_k <= 64 and k < 64, in wave 0 without barriers: one
+// round of loads for everything the accept step reads (and every row's
+// count and normaliser), one for the two kept sets of row n; q'(v) of p's
+// entries and their vocabulary ranks by lane reads; the inverse CDF by a
+// DPP scan.  The other waves only help write the outputs.
+constexpr int kFinalSpec = 8;   // chains up to this k load every row's kept set in round 1
+
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_topk_final_w(Params p) {
+  __shared__ int sx[64];
+  __shared__ int sidx[64];
+  __shared__ double sw[64];
+  __shared__ int sh_n, sh_st, sh_y, sh_np, sh_bad;
+  __shared__ double sh_S;
+  const int b = blockIdx.x;
+  const int k = p.k, V = p.V, K = p.top_k, tid = threadIdx.x, lane = tid & 63;
+  const int nrows = p.rows_t + p.rows_d;
+  if (tid < 64) {
+    int bad = 0;
+    for (int r = lane; r < nrows; r += 64)
+      bad |= p.k_bad[r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t)];
+    const int j = lane < k ? lane : 0;
+    const int jt = lane <= k ? lane : 0;
+    const int xj = p.tokens[(size_t)b * k + j];
+    const double a = p.k_px[trow(p, b, j)], bq = p.k_px[drow(p, b, j)];
+    const double u = (double)p.u[(size_t)b * k + j];
+    const double ur = (double)p.ur[b];
+    const int cntp = p.k_cnt[trow(p, b, jt)];
+    const double normp_l = p.k_norm[trow(p, b, jt)];
+    const int cntq = p.k_cnt[drow(p, b, j)];
+    const double normq_l = p.k_norm[drow(p, b, j)];
+    // short chains: the kept sets of every target and draft row as well
+    // (entry `lane`), so that row n's are in registers once n is known
+    int tidx[kFinalSpec + 1], didx[kFinalSpec];
+    double te[kFinalSpec + 1], de[kFinalSpec];
+    if (k <= kFinalSpec) {
+      const int e = lane < K ? lane : 0;
+#pragma unroll
+      for (int r = 0; r <= kFinalSpec; ++r) {
+        const size_t gt = (size_t)trow(p, b, r <= k ? r : 0) * K + e;
+        tidx[r] = p.k_idx[gt];
+        te[r] = p.k_e[gt];
+        if (r < kFinalSpec) {
+          const size_t gd = (size_t)drow(p, b, r < k ? r : 0) * K + e;
+          didx[r] = p.k_idx[gd];
+          de[r] = p.k_e[gd];
+        }
+      }
+    }
+    if (lane < k) sx[lane] = xj;
+    const bool anybad = __ballot(bad != 0) != 0ull;
+    if (lane == 0) sh_bad = anybad;
+    if (!anybad) {
+      const bool inv = lane < k && (xj < 0 || xj >= V);
+      bool acc = true;
+      if (lane < k && !inv) acc = bq > 0.0 ? (u < fmin(1.0, a / bq)) : (a > 0.0);
+      int st;
+      const int n = first_failure(lane < k && (inv || !acc), inv, k, &st);
+      const bool hq = n < k;
+      const int np = read_lane(cntp, n);
+      const double normp = read_lane(normp_l, n);
+      const int nq = hq ? read_lane(cntq, hq ? n : 0) : 0;
+      const double normq = hq ? read_lane(normq_l, n) : 1.0;
+      int pidx_l, qidx_l;
+      double pe_l, qe_l;
+      if (k <= kFinalSpec) {
+        // loaded with round 1 for every row n could be
+        pidx_l = tidx[0]; pe_l = te[0]; qidx_l = didx[0]; qe_l = de[0];
+#pragma unroll
+        for (int r = 1; r <= kFinalSpec; ++r) {
+          if (r == n) { pidx_l = tidx[r]; pe_l = te[r]; }
+          if (r < kFinalSpec && r == n) { qidx_l = didx[r]; qe_l = de[r]; }
+        }
+      } else {
+        const size_t gp = (size_t)trow(p, b, n) * K, gq = (size_t)drow(p, b, hq ? n : 0) * K;
+        const int e = lane < K ? lane : 0;
+        pidx_l = p.k_idx[gp + e];
+        pe_l = p.k_e[gp + e];
+        qidx_l = p.k_idx[gq + e];
+        qe_l = p.k_e[gq + e];
+      }
+      const int pidx = lane < np ? pidx_l : -1;
+      const double pa = lane < np ? pe_l / normp : 0.0;
+      double qa = 0.0;
+      for (int i = 0; i < nq; ++i) {
+        const int qi = read_lane(qidx_l, i);
+        const double qv = read_lane(qe_l, i);
+        if (qi == pidx) qa = qv / normq;
+      }
+      const double d = pa - qa;
+      double w = hq ? (d > 0.0 ? d : 0.0) : pa;
+      if (lane >= np) w = 0.0;
+      int rank = 0;
+      for (int i = 0; i < np; ++i) rank += read_lane(pidx, i) < pidx;   // vocabulary order
+      if (lane < np) { sidx[rank] = pidx; sw[rank] = w; }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      double ws = lane < np ? sw[lane] : 0.0;
+      const int yi = lane < np ? sidx[lane] : -1;
+      double inc = wave_scan(ws, 0.0, [](double x, double y) { return x + y; });
+      double S = read_lane(inc, 63);
+      if (!(S > 0.0)) {   // empty residual: draw from p'_n
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        if (lane < np) sw[rank] = pa;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        ws = lane < np ? sw[lane] : 0.0;
+        inc = wave_scan(ws, 0.0, [](double x, double y) { return x + y; });
+        S = read_lane(inc, 63);
+      }
+      const double ex = lane_before(inc, 0.0);
+      const double t = ur * S;
+      const uint64_t m1 = __ballot(lane < np && ws > 0.0 && ex + ws > t);
+      const uint64_t m2 = __ballot(lane < np && ws > 0.0);
+      const int ys = m1 ? __ffsll((unsigned long long)m1) - 1 : (m2 ? 63 - __clzll((long long)m2) : -1);
+      const int y = ys >= 0 ? read_lane(yi, ys) : -1;
+      if (lane == 0) { sh_n = n; sh_st = st; sh_y = y; sh_np = np; sh_S = S; }
+    }
+  }
+  __syncthreads();
+  if (sh_bad) { emit_invalid(p, b, 4); return; }
+  if (p.resid_probs) {
+    float* rp = p.resid_probs + (size_t)b * V;
+    for (int v = tid; v < V; v += kBlock) rp[v] = 0.f;
+    __syncthreads();
+    if (tid < sh_np) rp[sidx[tid]] = (float)(sw[tid] / sh_S);
+  }
+  emit_tokens(p, b, sx, sh_n, sh_y, sh_st);
 }
 
 // Accept step and residual draw of one sequence from the published kept sets.
@@ -3087,8 +3400,14 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
     case kFiltGreedy: hipLaunchKernelGGL((k_greedy_final<T>), gb, block, 0, st, p); break;
     case kFiltTree: hipLaunchKernelGGL((k_tree_final<T>), gb, block, 0, st, p); break;
     case kFiltTopk:
-      hipLaunchKernelGGL((k_topk_rows<T>), gr, block, 0, st, p);
-      hipLaunchKernelGGL((k_topk_final<T>), gb, block, 0, st, p);
+      if (p.top_k <= 64 && p.P != p.S)
+        hipLaunchKernelGGL((k_topk_rows_w<T>), dim3((unsigned)((rows + kWaves - 1) / kWaves)), block, 0, st, p);
+      else
+        hipLaunchKernelGGL((k_topk_rows<T>), gr, block, 0, st, p);
+      if (p.top_k <= 64 && p.k < 64)
+        hipLaunchKernelGGL((k_topk_final_w<T>), gb, block, 0, st, p);
+      else
+        hipLaunchKernelGGL((k_topk_final<T>), gb, block, 0, st, p);
       break;
     case kFiltTopp:
       hipLaunchKernelGGL((k_topp_rows<T>), gr, block, 0, st, p);
