@@ -3139,10 +3139,10 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
 // d = fmaf(l, -1/T, M/T) in float32 (monotone in l, so bins follow the rank
 // order) over [0, dmax) with dmax = ln(V / ((1 - top_p) Z)) + 1 (every
 // kept logit lies below it), kFastBins bins.
-//  pass 1: a float32 histogram of exp(-d) (hardware exp2, one LDS float
-//          atomic per binned logit).  Its masses only locate the bin where
-//          the mass from the top reaches top_p Z; the window is that bin and
-//          its two neighbours.
+//  pass 1: a histogram of exp(-d) (hardware float32 exp2, rounded to 24
+//          fraction bits, one LDS integer atomic per binned logit).  Its
+//          masses only locate the bin where the mass from the top reaches
+//          top_p Z; the window is that bin and its two neighbours.
 //  pass 2: the exact float64 mass A of every logit binned above the window
 //          (exp in float64 through a per-wave queue, per-lane sums in a
 //          fixed order, fixed block reduction), and the window's logits
@@ -3151,6 +3151,11 @@ DEV void topp_search(const Params& p, const T* row, float Mrow, double Z, RowNuc
 // topp_search.  A window that overflows, or a cut that falls outside it
 // (the float32 masses misplaced it), returns false.
 constexpr int kFastBins = 4096;
+// Fixed-point scale of the pass-1 masses: LDS integer atomics are several
+// times faster than float ones.  A bin whose sum would overflow (hundreds of
+// logits within 1/4096 of the range of the maximum) only misplaces the
+// window, which the walk detects.
+constexpr float kFastScale = 16777216.f;
 constexpr int kNucPipe = 8;   // bytes per logit times groups per lane per round of the row sweeps (bf16 4, fp32 2)
 static_assert(kFastBins * 4 <= kNucBins * 8, "the fast nucleus histogram fits in the exact one's");
 
@@ -3169,10 +3174,10 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
   const double tgt = p.top_p * Z;
   const double zm = (double)Mrow * invT;
   auto bin_of = [&](float d) {
-    const int b = (int)(d * invw);
-    return b < 0 ? 0 : (b >= kFastBins ? kFastBins - 1 : b);
+    return (int)__builtin_amdgcn_fmed3f(d * invw, 0.f, (float)(kFastBins - 1));
   };
-  for (int b = tid; b < kFastBins; b += kBlock) hist[b] = 0.f;
+  unsigned* hfix = reinterpret_cast<unsigned*>(hist);
+  for (int b = tid; b < kFastBins; b += kBlock) hfix[b] = 0u;
   __syncthreads();
   // pass 1
   tile_groups_pipe<T, kNucPipe / (int)sizeof(T)>(row, 0, V, p.aligned, rot, [&](const auto& gr, int, int nv) {
@@ -3184,7 +3189,8 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
         const float d = fmaf(v[e], nit32, zm32);
-        if (u < nv && d < dmax) atomicAdd(&hist[bin_of(d)], __builtin_amdgcn_exp2f(-d * 1.4426950408889634f));
+        if (u < nv && d < dmax)
+          atomicAdd(&hfix[bin_of(d)], (unsigned)__builtin_rintf(__builtin_amdgcn_exp2f(-d * 1.4426950408889634f) * kFastScale));
       }
     }
   });
@@ -3196,7 +3202,7 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
     double local[per];
     double ts = 0.0;
 #pragma unroll
-    for (int q = 0; q < per; ++q) { local[q] = (double)hist[tid * per + q]; ts += local[q]; }
+    for (int q = 0; q < per; ++q) { local[q] = (double)hfix[tid * per + q] * (1.0 / kFastScale); ts += local[q]; }
     double tot;
     const double ex = block_exscan(ts, red, &tot);
     double c = ex;   // bin masses are exp(-d): the same units as Z
@@ -3222,31 +3228,40 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
   float* q = aq + (tid >> 6) * 128;
   int qn = 0;
   double above = 0.0;
+  // pass 2 classifies by d against the window's edges (monotone in the
+  // logit, so the classes follow rank order; they need not repeat pass 1's
+  // bins exactly: the walk below checks that the cut lies in the window)
+  const float d_lo = (float)lo / invw, d_hi = fminf((float)(hi + 1) / invw, dmax);
   tile_groups_pipe<T, kNucPipe / (int)sizeof(T)>(row, 0, V, p.aligned, rot, [&](const auto& gr, int g0, int nv) {
     constexpr int n = sizeof(gr) / sizeof(gr[0]);
 #pragma unroll
     for (int u = 0; u < n; ++u) {
       float v[kVec];
       gr[u].opaque().values(v);
-      unsigned msk = 0u;
+      unsigned msk = 0u, amsk = 0u;
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
         const float d = fmaf(v[e], nit32, zm32);
-        const bool in = u < nv && d < dmax;
-        const int b = bin_of(d);
-        const bool ab = in && b < lo;
-        if (in && b >= lo && b <= hi) msk |= 1u << e;
-        const uint64_t m = __ballot(ab);
-        if (m) {
-          if (ab) q[qn + __popcll(m & ((1ull << lane) - 1ull))] = v[e];
-          qn += __popcll(m);
-          if (qn >= 64) {
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            above += exp2_neg(((double)q[lane] * invT - zm) * kLog2e);
-            const float rest = lane < qn - 64 ? q[64 + lane] : 0.f;
-            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-            if (lane < qn - 64) q[lane] = rest;
-            qn -= 64;
+        if (d < d_lo) amsk |= 1u << e;
+        else if (d < d_hi) msk |= 1u << e;
+      }
+      if (u >= nv) { amsk = 0u; msk = 0u; }
+      if (__ballot(amsk != 0u)) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          const bool ab = (amsk >> e) & 1u;
+          const uint64_t m = __ballot(ab);
+          if (m) {
+            if (ab) q[qn + __popcll(m & ((1ull << lane) - 1ull))] = v[e];
+            qn += __popcll(m);
+            if (qn >= 64) {
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+              above += exp2_neg(((double)q[lane] * invT - zm) * kLog2e);
+              const float rest = lane < qn - 64 ? q[64 + lane] : 0.f;
+              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+              if (lane < qn - 64) q[lane] = rest;
+              qn -= 64;
+            }
           }
         }
       }
