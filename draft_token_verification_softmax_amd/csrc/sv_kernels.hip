@@ -2368,8 +2368,14 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   __shared__ int redi[2 * kWaves];
   __shared__ double sh_base;
   constexpr int kPer = kSegStage / kBlock;   // segment masses per thread
-  const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  // one workgroup per segment when resid_probs is written or the weights
+  // were kept; otherwise one per sequence (gridDim.x == 1), which draws in
+  // the segment it finds
+  const int b = blockIdx.y, tid = threadIdx.x;
+  int seg = blockIdx.x;
   const int S2 = p.S2, V = p.V, k = p.k;
+  const bool single = gridDim.x == 1 && S2 > 1;
+  const bool use_w = p.keep_w && !single;
   const double c64 = 64.0 * kLog2e / p.T;
   // one round of loads, all unconditional: sequence state, ur, the segment
   // masses this thread owns ([tid*per, (tid+1)*per)), drafted tokens, and
@@ -2388,7 +2394,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   }
   const int xl = p.tokens[(size_t)b * k + (tid < k ? tid : 0)];
   double w[kVec];
-  if (p.keep_w) {
+  if (use_w) {
     const d2* wp = reinterpret_cast<const d2*>(p.wpart + ((size_t)b * S2 + seg) * kResidSeg + tid * kVec);
 #pragma unroll
     for (int q = 0; q < kVec / 2; ++q) { const d2 x = wp[q]; w[2 * q] = x.x; w[2 * q + 1] = x.y; }
@@ -2461,12 +2467,14 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
     for (int q = kPer; q < per && tid * per + q < c; ++q) run += spg[tid * per + q];
     sh_base = run;
   }
+  if (single) seg = c;
   if (seg != c && !p.resid_probs) return;
   __syncthreads();
   const double base = sh_base;
   const int c0 = seg * kResidSeg;
-  if (!p.keep_w) {
-    // large problems: recompute this segment's weights
+  if (!use_w) {
+    // large problems (or one workgroup per sequence): recompute this
+    // segment's weights
     exp2_table_init(tab);
     const RowView pr{row_ptr<T>(p, trow(p, b, node)), ss.nmc_p, ss.inv_p, ss.cut_p};
     const RowView qr{hasq ? row_ptr<T>(p, drow(p, b, node)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
@@ -3410,7 +3418,8 @@ static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hip
 template <typename T>
 static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
   const int rows = p.B * (p.rows_t + p.rows_d);
-  const dim3 block(kBlock), gb((unsigned)p.B), gr((unsigned)rows), gs((unsigned)p.S2, (unsigned)p.B);
+  const dim3 block(kBlock), gb((unsigned)p.B), gr((unsigned)rows), gs((unsigned)p.S2, (unsigned)p.B),
+      gb1(1u, (unsigned)p.B);
   switch (filt) {
     case kFiltGreedy: hipLaunchKernelGGL((k_greedy_final<T>), gb, block, 0, st, p); break;
     case kFiltTree: hipLaunchKernelGGL((k_tree_final<T>), gb, block, 0, st, p); break;
@@ -3428,19 +3437,19 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
       hipLaunchKernelGGL((k_topp_rows<T>), gr, block, 0, st, p);
       hipLaunchKernelGGL((k_topp_rows_exact<T>), gr, block, 0, st, p);
       hipLaunchKernelGGL((k_resid_s<T, kFiltTopp>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T, kFiltTopp>), gs, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T, kFiltTopp>), (p.resid_probs || p.keep_w) ? gs : gb1, block, 0, st, p);
       break;
     case kFiltTreeSample: {
       const int passes = p.k - 1 < kTreePasses ? p.k - 1 : kTreePasses;
       for (int m = 0; m < passes; ++m) hipLaunchKernelGGL((k_tsample_pass<T>), gs, block, 0, st, p, m);
       hipLaunchKernelGGL((k_tsample_walk<T>), gb, block, 0, st, p);
       hipLaunchKernelGGL((k_tsample_mass<T>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), gs, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), (p.resid_probs || p.keep_w) ? gs : gb1, block, 0, st, p);
       break;
     }
     default:  // plain sampling
       hipLaunchKernelGGL((k_resid_s<T, kFiltNone>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), gs, block, 0, st, p);
+      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), (p.resid_probs || p.keep_w) ? gs : gb1, block, 0, st, p);
       break;
   }
   return hipGetLastError();

@@ -206,3 +206,26 @@ def test_tree_path_equals_chain_on_gpu():
     tree = run_tree(tr, tokens)
     assert np.array_equal(chain["accepted_len"], tree["accepted_len"])
     assert np.array_equal(chain["out_tokens"], tree["out_tokens"])
+
+
+# ------------------------------------------------------------------ draws without resid_probs
+
+@pytest.mark.parametrize("config,dtype,B,V,k,top_p", [
+    (2, "bf16", 32, 32000, 5, 1.0),   # small: weights kept, one draw workgroup per segment
+    (1, "f32", 32, 152064, 4, 1.0),   # large (B * segments > 2048): one draw workgroup per sequence
+    (5, "f32", 32, 152064, 4, 0.9),   # nucleus, large
+])
+def test_sample_without_resid_probs(config, dtype, B, V, k, top_p):
+    """Without resid_probs the draw runs one workgroup per sequence: the
+    tokens must still match the oracle, and equal the per-segment run's."""
+    say("sample without resid_probs", config, dtype, B, V, k, top_p)
+    inp = wl.chain_inputs(config, seed=300 + V, B=B, V=V, k=k, dtype=dtype)
+    inp["top_p"] = top_p
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE, want_resid=False)
+    full = run_chain(inp, x, SV_MODE_SAMPLE, want_resid=True)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    gpu["resid_probs"] = full["resid_probs"]
+    compare_chain(gpu, orc, range(B), f"no resid_probs cfg{config}")
+    assert np.array_equal(gpu["out_tokens"], full["out_tokens"])
+    assert np.array_equal(gpu["accepted_len"], full["accepted_len"])

@@ -185,6 +185,15 @@ def test_tree_sample_bad_data():
     assert (gpu["out_tokens"][0] == -1).all() and gpu["accepted_len"][0] == 0
 
 
+def test_tree_sample_without_resid_probs():
+    inp = wl.tree_sample_inputs(seed=4, B=8, N=30, V=4096, dtype="bf16")
+    tok = tree_tokens(inp)
+    a = run_gpu(inp, tok, want_resid=True)
+    b = run_gpu(inp, tok, want_resid=False)
+    for key in ("accepted_len", "out_tokens", "out_nodes", "seq_status"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 def test_tree_sample_deterministic():
     inp = wl.tree_sample_inputs(seed=3, B=8, N=30, V=4096, dtype="bf16")
     tok = tree_tokens(inp)
