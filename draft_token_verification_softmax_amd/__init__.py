@@ -62,6 +62,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise OSError(f"{path} is not built; run python -m draft_token_verification_softmax_amd.build")
+    # torch carries its own HIP runtime under the same soname; loading torch
+    # first makes this library bind to that one, so the process has a single
+    # runtime (two would each claim the device)
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     vp, i32, P = ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER
     lib.specverify_create.argtypes = [P(sv_config), ctypes.c_int, P(vp)]
