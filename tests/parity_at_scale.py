@@ -30,9 +30,10 @@ sys.path.insert(0, ROOT)
 
 import torch  # noqa: E402  (loads the HIP runtime before the library)
 
+import oracle.tree_sample as ts  # noqa: E402
 import oracle.verify as ov  # noqa: E402
 from draft_token_verification_softmax_amd import (SV_MODE_GREEDY, SV_MODE_SAMPLE,  # noqa: E402
-                                                  SV_MODE_TREE_GREEDY, SpecVerify)
+                                                  SV_MODE_TREE_GREEDY, SV_MODE_TREE_SAMPLE, SpecVerify)
 from draft_token_verification_softmax_amd import workloads as wl  # noqa: E402
 
 RESID_TOL = 1e-5
@@ -110,6 +111,29 @@ def run_tree_batch(tr, B, pool, sv):
     return gpu, list(pool.map(one, range(B)))
 
 
+def run_tree_sample_batch(ti, B, pool, sv):
+    dtype, T = ti["dtype"], ti["T"]
+    tgt = to_dev(ti["target"], dtype)
+    dft = to_dev(ti["draft"], dtype)
+    parents = torch.from_numpy(ti["parents"]).cuda()
+    par = parents.clamp(min=0).long()
+    rows = dft[torch.arange(B, device="cuda").unsqueeze(1), par]   # each node's parent's draft row
+    tok_dev = draw_device(rows, dtype, T, 0, 1.0, ti["draw_u"])
+    tok_dev[:, 0] = 0
+    out = sv.run(tgt, dft, tok_dev.contiguous(), to_dev(ti["u"], None), to_dev(ti["ur"], None),
+                 parents=parents, want_resid_probs=True)
+    torch.cuda.synchronize()
+    tokens = tok_dev.cpu().numpy()
+    gpu = {key: (v.cpu().numpy() if v is not None else None) for key, v in out.items()}
+    T64, D64 = ti["T64"], ti["D64"]
+
+    def one(b):
+        o = ts.tree_sample(T64[b], D64[b], ti["parents"][b], tokens[b], ti["u"][b], ti["ur"][b], T)
+        return o["n"], o["tokens"], o["status"], o["flagged"], o["resid"], o["nodes"]
+
+    return gpu, list(pool.map(one, range(B)))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--config", type=int, required=True)
@@ -122,11 +146,16 @@ def main():
     args = ap.parse_args()
     c = args.config
     cfg = wl.CONFIGS[c]
-    tree = cfg["kind"] == "tree"
-    mode = SV_MODE_TREE_GREEDY if tree else (SV_MODE_SAMPLE if args.mode == "sample" else SV_MODE_GREEDY)
+    tsample = cfg["kind"] == "tree_sample"
+    tree = cfg["kind"] == "tree" or tsample
+    mode = (SV_MODE_TREE_SAMPLE if tsample else SV_MODE_TREE_GREEDY) if tree else \
+        (SV_MODE_SAMPLE if args.mode == "sample" else SV_MODE_GREEDY)
     B = args.batch or (cfg["B"] if cfg["B"] > 1 else 64)
     nb = (args.sequences + B - 1) // B
-    if tree:
+    if tsample:
+        sv = SpecVerify(mode=mode, dtype=cfg["dtype"], max_batch=B, k=cfg["N"], vocab=cfg["V"],
+                        temperature=cfg["T"])
+    elif tree:
         sv = SpecVerify(mode=mode, dtype=cfg["dtype"], max_batch=B, k=cfg["N"], vocab=cfg["V"])
     else:
         sv = SpecVerify(mode=mode, dtype=cfg["dtype"], max_batch=B, k=cfg["k"], vocab=cfg["V"],
@@ -138,6 +167,13 @@ def main():
     with ThreadPoolExecutor(args.threads) as pool, ThreadPoolExecutor(args.gen_threads) as gen:
         def make(i):
             seed = 9000 + 100 * c + i
+            if tsample:
+                ti = wl.tree_sample_inputs(seed, B=B, N=cfg["N"], V=cfg["V"], dtype=cfg["dtype"], T=cfg["T"],
+                                           sd=cfg["sd"], noise=cfg["noise"], max_depth=cfg["max_depth"],
+                                           max_children=cfg["max_children"])
+                ti["T64"] = wl.rows_f64(ti["target"], ti["dtype"])
+                ti["D64"] = wl.rows_f64(ti["draft"], ti["dtype"])
+                return ti
             if tree:
                 tr = wl.tree_inputs(4, seed=seed, B=B)
                 tr["T64"] = wl.rows_f64(tr["target"], tr["dtype"])
@@ -150,7 +186,9 @@ def main():
             cur = ahead.pop(0).result()
             if i + len(ahead) + 1 < nb:
                 ahead.append(gen.submit(make, i + len(ahead) + 1))
-            if tree:
+            if tsample:
+                gpu, res = run_tree_sample_batch(cur, B, pool, sv)
+            elif tree:
                 gpu, res = run_tree_batch(cur, B, pool, sv)
             else:
                 gpu, res = run_chain_batch(c, cur, mode, pool, sv)
@@ -181,7 +219,8 @@ def main():
     unflagged = stats["mismatches"] - stats["flagged_mismatches"]
     ok = unflagged == 0 and stats["flagged_mismatches"] <= 1e-4 * stats["sequences"] and \
         stats["resid_max_abs"] <= RESID_TOL
-    stats.update(config=c, mode=("tree greedy" if tree else args.mode), batch=B, ok=bool(ok),
+    stats.update(config=c, mode=("tree sampling" if tsample else "tree greedy" if tree else args.mode),
+                 batch=B, ok=bool(ok),
                  unflagged_mismatches=unflagged, examples=bad,
                  mean_accepted=stats["accepted"] / max(1, stats["sequences"]),
                  seconds=round(time.perf_counter() - t0, 1))
