@@ -16,8 +16,7 @@ import numpy as np
 import torch
 
 import oracle.verify as ov
-from draft_token_verification_softmax_amd import (SV_MODE_GREEDY, SV_MODE_SAMPLE,
-                                                  SV_MODE_TREE_GREEDY, SpecVerify)
+from draft_token_verification_softmax_amd import SV_MODE_SAMPLE, SV_MODE_TREE_GREEDY, SpecVerify
 from draft_token_verification_softmax_amd import workloads as wl
 
 RESID_TOL = 1e-5

@@ -7,7 +7,6 @@ import pytest
 import torch
 
 import oracle.aux as ax
-import oracle.verify as ov
 from draft_token_verification_softmax_amd import (SV_MODE_SAMPLE, SV_MODE_TREE_GREEDY,
                                                   SV_STATS_ACCEPTANCE, SV_STATS_ACCEPTED,
                                                   SV_STATS_ALPHA, SV_STATS_DRAFTED,

@@ -5,10 +5,9 @@ import scipy.stats
 import torch
 
 import oracle.verify as ov
-from draft_token_verification_softmax_amd import (SV_MODE_GREEDY, SV_MODE_SAMPLE,
-                                                  SV_MODE_TREE_GREEDY, SpecVerify)
+from draft_token_verification_softmax_amd import SV_MODE_GREEDY, SV_MODE_SAMPLE, SpecVerify
 from draft_token_verification_softmax_amd import workloads as wl
-from gpu_common import compare_chain, dev, draw_drafts, oracle_chain, run_chain, run_tree, say
+from gpu_common import compare_chain, draw_drafts, oracle_chain, run_chain, run_tree, say
 
 pytestmark = pytest.mark.gpu
 

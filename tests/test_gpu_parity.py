@@ -7,11 +7,9 @@ sequences the oracle can afford.
 """
 import numpy as np
 import pytest
-import torch
 
 import oracle.verify as ov
-from draft_token_verification_softmax_amd import (SV_MODE_GREEDY, SV_MODE_SAMPLE,
-                                                  SV_MODE_TREE_GREEDY)
+from draft_token_verification_softmax_amd import SV_MODE_GREEDY, SV_MODE_SAMPLE
 from draft_token_verification_softmax_amd import workloads as wl
 from gpu_common import (compare_chain, draw_drafts, oracle_chain, run_chain, run_tree, say,
                         tree_tokens_via_oracle)
