@@ -138,6 +138,18 @@ template <> struct Group<float> {
     b = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, kNT));
   }
   static constexpr int kBytes = 32;
+  // split slot: quad a at byte voff + soff, quad b kBlock * 16 bytes further
+  // (a workgroup's 256 lanes read two 4 KB runs)
+  DEV void load_split(__amdgpu_buffer_rsrc_t r, int voff, int soff) {
+    a = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT));
+    b = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff + kBlock * 16, kNT));
+  }
+  // -inf in the quads of a split slot whose first logit (pa for a) is at or
+  // past n (n a multiple of 4: quads are wholly in or out)
+  DEV void pad_split(int pa, int n) {
+    if (pa >= n) a = vf4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+    if (pa + kBlock * 4 >= n) b = vf4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  }
   DEV Group opaque() const {
     Group g = *this;
     asm volatile("" : "+v"(g.a.x), "+v"(g.a.y), "+v"(g.a.z), "+v"(g.a.w));
@@ -273,42 +285,81 @@ DEV void tile_groups(const T* row, int start, int end, int aligned, F&& f) {
   }
 }
 
+// Where element e of a lane's group slot u sits in a swept range (logit
+// offset from the range start).  Contiguous slots hold kVec consecutive
+// logits (slot u of the lane is group base + u * kBlock); split slots (float32
+// sweeps) hold two quads kBlock * 4 logits apart, base being the round's
+// first logit, so that every 16-byte load instruction of a wave reads 1 KB
+// of consecutive memory.
+struct SlotMap {
+  int base;
+  int split;
+  DEV int index(int u, int e) const {
+    if (!split) return (base + u * kBlock) * kVec + e;
+    return base + u * (kBlock * kVec) + 4 * (int)threadIdx.x + (e < 4 ? e : kBlock * 4 + e - 4);
+  }
+};
+
 // tile_groups for long ranges (many rounds), as one workgroup's sweep of a
 // whole row: the next round's loads are issued before the current round is
 // consumed (two sets of U groups in registers), and the rounds start at
 // round `rot` (mod the round count) and wrap around.  Many workgroups that
 // sweep equally strided rows in step would otherwise hit the same memory
 // channels at the same time; a different rotation per row spreads them.
-// Same contract for f as tile_groups (in rotated round order).
+// f(groups, slot map, n valid): as tile_groups, the first index replaced by
+// the slot map.  Float32 rows of whole groups are read in split slots
+// (32-byte groups, two per load instruction's 2 KB span at half density, read
+// a bare 1.4 GB sweep 14% slower on one MI355X); their slots past the range
+// hold -inf and all count as valid.
 template <typename T, int U, typename F>
 DEV void tile_groups_pipe(const T* row, int start, int end, int aligned, int rot, F&& f) {
   const int ngroups = (end - start + kVec - 1) / kVec;
   const int nfull = (end - start) / kVec;
   if (!(aligned && nfull == ngroups && nfull > 0)) {
-    tile_groups<T, U>(row, start, end, aligned, f);
+    tile_groups<T, U>(row, start, end, aligned, [&](const auto& gr, int g0, int nv) { f(gr, SlotMap{g0, 0}, nv); });
     return;
   }
+  constexpr bool kSplit = sizeof(T) == 4;
   constexpr int R = U * kBlock;                 // groups per round
+  const int n = end - start;
   const int nr = (ngroups + R - 1) / R;
   rot = rot % nr;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, (end - start) * (int)sizeof(T));
-  Group<T> cur[U], nxt[U];
-  int g0 = rot * R + (int)threadIdx.x;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(row + start, n * (int)sizeof(T));
+  const int tid = threadIdx.x;
+  auto load_round = [&](Group<T>* g, int r) {
 #pragma unroll
-  for (int u = 0; u < U; ++u) cur[u].load_buf(rs, g0 * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
-  for (int j = 0; j < nr; ++j) {
-    int r2 = rot + j + 1;
-    if (r2 >= nr) r2 -= nr;
-    const int g1 = r2 * R + (int)threadIdx.x;
-    if (j + 1 < nr) {
-#pragma unroll
-      for (int u = 0; u < U; ++u) nxt[u].load_buf(rs, g1 * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
+    for (int u = 0; u < U; ++u) {
+      if constexpr (kSplit) g[u].load_split(rs, tid * 16, (r * R + u * kBlock) * Group<T>::kBytes);
+      else g[u].load_buf(rs, (r * R + tid) * Group<T>::kBytes, u * kBlock * Group<T>::kBytes);
     }
-    const int nv = g0 < ngroups ? (ngroups - g0 + kBlock - 1) / kBlock : 0;
-    f(cur, g0, nv < U ? nv : U);
+  };
+  Group<T> cur[U], nxt[U];
+  int rc = rot;
+  load_round(cur, rc);
+  // Take the first round's registers here, before the loop.  Left pending
+  // into the loop, they make the compiler's wait inside the body (which
+  // cannot tell the first iteration from the others) also wait for the
+  // next round's prefetch on every iteration, and no load overlaps work.
+#pragma unroll
+  for (int u = 0; u < U; ++u) cur[u] = cur[u].opaque();
+  for (int j = 0; j < nr; ++j) {
+    int rn = rc + 1;
+    if (rn >= nr) rn -= nr;
+    if (j + 1 < nr) load_round(nxt, rn);
+    if constexpr (kSplit) {
+      if ((rc + 1) * R > ngroups) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) cur[u].pad_split(rc * R * kVec + u * kBlock * kVec + 4 * tid, n);
+      }
+      f(cur, SlotMap{rc * R * kVec, 1}, U);
+    } else {
+      const int g0 = rc * R + tid;
+      const int nv = g0 < ngroups ? (ngroups - g0 + kBlock - 1) / kBlock : 0;
+      f(cur, SlotMap{g0, 0}, nv < U ? nv : U);
+    }
 #pragma unroll
     for (int u = 0; u < U; ++u) cur[u] = nxt[u];
-    g0 = g1;
+    rc = rn;
   }
 }
 
@@ -3163,7 +3214,8 @@ constexpr int kFastBins = 4096;
 // times faster than float ones.  A bin whose sum would overflow (hundreds of
 // logits within 1/4096 of the range of the maximum) only misplaces the
 // window, which the walk detects.
-constexpr float kFastScale = 16777216.f;
+constexpr int kFastFrac = 24;
+constexpr float kFastScale = (float)(1 << kFastFrac);
 constexpr int kNucPipe = 8;   // bytes per logit times groups per lane per round of the row sweeps (bf16 4, fp32 2)
 static_assert(kFastBins * 4 <= kNucBins * 8, "the fast nucleus histogram fits in the exact one's");
 
@@ -3181,14 +3233,17 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
   const float invw = (float)((double)kFastBins / dmaxd);
   const double tgt = p.top_p * Z;
   const double zm = (double)Mrow * invT;
-  auto bin_of = [&](float d) {
-    return (int)__builtin_amdgcn_fmed3f(d * invw, 0.f, (float)(kFastBins - 1));
-  };
   unsigned* hfix = reinterpret_cast<unsigned*>(hist);
   for (int b = tid; b < kFastBins; b += kBlock) hfix[b] = 0u;
   __syncthreads();
-  // pass 1
-  tile_groups_pipe<T, kNucPipe / (int)sizeof(T)>(row, 0, V, p.aligned, rot, [&](const auto& gr, int, int nv) {
+  // pass 1.  The bin position d * invw and the weight's exponent
+  // -d log2(e) + kFastFrac (the fixed point's fraction bits) are each one
+  // fma of the logit; a position below kFastBins is one below dmax.  Near
+  // the maximum the rounding of the fma can make it slightly negative: those
+  // go to bin 0.
+  const float a1 = nit32 * invw, b1 = zm32 * invw;
+  const float a2 = (float)(invT * kLog2e), b2 = (float)(kFastFrac - zm * kLog2e);
+  tile_groups_pipe<T, kNucPipe / (int)sizeof(T)>(row, 0, V, p.aligned, rot, [&](const auto& gr, const SlotMap&, int nv) {
     constexpr int n = sizeof(gr) / sizeof(gr[0]);
 #pragma unroll
     for (int u = 0; u < n; ++u) {
@@ -3196,9 +3251,9 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
       gr[u].values(v);
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
-        const float d = fmaf(v[e], nit32, zm32);
-        if (u < nv && d < dmax)
-          atomicAdd(&hfix[bin_of(d)], (unsigned)__builtin_rintf(__builtin_amdgcn_exp2f(-d * 1.4426950408889634f) * kFastScale));
+        const float pos = fmaf(v[e], a1, b1);
+        if (u < nv && pos < (float)kFastBins)
+          atomicAdd(&hfix[(int)__builtin_amdgcn_fmed3f(pos, 0.f, (float)(kFastBins - 1))], (unsigned)(__builtin_amdgcn_exp2f(fmaf(v[e], a2, b2)) + 0.5f));
       }
     }
   });
@@ -3240,47 +3295,43 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
   // logit, so the classes follow rank order; they need not repeat pass 1's
   // bins exactly: the walk below checks that the cut lies in the window)
   const float d_lo = (float)lo / invw, d_hi = fminf((float)(hi + 1) / invw, dmax);
-  tile_groups_pipe<T, kNucPipe / (int)sizeof(T)>(row, 0, V, p.aligned, rot, [&](const auto& gr, int g0, int nv) {
+  tile_groups_pipe<T, kNucPipe / (int)sizeof(T)>(row, 0, V, p.aligned, rot, [&](const auto& gr, const SlotMap& sm, int nv) {
     constexpr int n = sizeof(gr) / sizeof(gr[0]);
 #pragma unroll
     for (int u = 0; u < n; ++u) {
       float v[kVec];
       gr[u].opaque().values(v);
-      unsigned msk = 0u, amsk = 0u;
+      const bool live = u < nv;
+      const uint64_t lm = __builtin_amdgcn_ballot_w64(live);
+      // each logit's class from two compares, each straight into a scalar
+      // lane mask: above the window -> the queue (slot = queue length +
+      // the lanes below with the same class), inside it -> the window list
 #pragma unroll
       for (int e = 0; e < kVec; ++e) {
         const float d = fmaf(v[e], nit32, zm32);
-        if (d < d_lo) amsk |= 1u << e;
-        else if (d < d_hi) msk |= 1u << e;
-      }
-      if (u >= nv) { amsk = 0u; msk = 0u; }
-      if (__ballot(amsk != 0u)) {
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-          const bool ab = (amsk >> e) & 1u;
-          const uint64_t m = __ballot(ab);
-          if (m) {
-            if (ab) q[qn + __popcll(m & ((1ull << lane) - 1ull))] = v[e];
-            qn += __popcll(m);
-            if (qn >= 64) {
-              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-              above += exp2_neg(((double)q[lane] * invT - zm) * kLog2e);
-              const float rest = lane < qn - 64 ? q[64 + lane] : 0.f;
-              __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-              if (lane < qn - 64) q[lane] = rest;
-              qn -= 64;
-            }
+        const bool ab = d < d_lo;
+        const uint64_t m = __builtin_amdgcn_ballot_w64(ab) & lm;
+        if (m) {
+          if (ab && live)
+            q[__builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)m, (unsigned)qn))] = v[e];
+          qn += __popcll(m);
+          if (qn >= 64) {
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            above += exp2_neg(((double)q[lane] * invT - zm) * kLog2e);
+            const float rest = lane < qn - 64 ? q[64 + lane] : 0.f;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            if (lane < qn - 64) q[lane] = rest;
+            qn -= 64;
           }
         }
-      }
-      if (__any(msk != 0u)) {
-        int slot = wave_reserve(__popc(msk), &wcnt);
-        const int i0 = (g0 + u * kBlock) * kVec;
-#pragma unroll
-        for (int e = 0; e < kVec; ++e) {
-          if ((msk >> e) & 1u) {
-            if (slot < kWindowCap) win[slot] = pack(v[e], i0 + e);
-            ++slot;
+        const uint64_t wm = __builtin_amdgcn_ballot_w64(d < d_hi) & lm & ~m;
+        if (wm) {
+          int base = 0;
+          if (lane == 0) base = atomicAdd(&wcnt, (int)__popcll(wm));
+          base = read_lane(base, 0);
+          if ((wm >> lane) & 1ull) {
+            const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(wm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)wm, 0u));
+            if (slot < kWindowCap) win[slot] = pack(v[e], sm.index(u, e));
           }
         }
       }
