@@ -1456,6 +1456,65 @@ DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double
   return resid_weights_of(pr, qr, hasq, c64, tab, pos, n, lp, lq, w);
 }
 
+// The residual mass of the kVec entries [pos, pos + kVec) of nucleus rows
+// (the sum resid_weights returns, in another fixed order).  Only entries
+// kept in the target's nucleus can weigh anything, and those are a few
+// percent of a row at the usual top_p: each wave queues them in LDS (ballot
+// and lane-prefix slot, per entry) and every 64 queued ones cost one float64
+// evaluation per lane instead of one per entry of the row.  Queue slots:
+// 128 per wave (64 + at most 63 before a flush).
+template <typename T>
+DEV double resid_nuc_sparse(const RowView& pr, const RowView& qr, bool hasq, double c64,
+                            const double* tab, int V, int aligned, int pos, float* qlp,
+                            float* qlq, int* qix) {
+  float lp[kVec], lq[kVec];
+  int nv = 0;
+  if (pos < V) {
+    nv = load_group<T>((const T*)pr.row, pos, V, aligned, lp);
+    if (hasq) load_group<T>((const T*)qr.row, pos, V, aligned, lq);
+  }
+  const int lane = threadIdx.x & 63;
+  auto weight = [&](float a, float b, int v) {
+    double w = exp2_64(fma((double)a, c64, pr.nmc), tab) * pr.inv;
+    if (hasq) {
+      w -= prob_from(qr, c64, tab, b, v);
+      w = w > 0.0 ? w : 0.0;
+    }
+    return w;
+  };
+  double t = 0.0;
+  int qn = 0;
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    const bool kp = e < nv && (pr.cut == 0ull || pack(lp[e], pos + e) >= pr.cut);
+    const uint64_t m = __builtin_amdgcn_ballot_w64(kp);
+    if (m) {
+      if (kp) {
+        const unsigned sl = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((unsigned)m, (unsigned)qn));
+        qlp[sl] = lp[e];
+        qlq[sl] = hasq ? lq[e] : 0.f;
+        qix[sl] = pos + e;
+      }
+      qn += __popcll(m);
+      if (qn >= 64) {
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        t += weight(qlp[lane], qlq[lane], qix[lane]);
+        const int rest = qn - 64;
+        float a = 0.f, b = 0.f;
+        int v = 0;
+        if (lane < rest) { a = qlp[64 + lane]; b = qlq[64 + lane]; v = qix[64 + lane]; }
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        if (lane < rest) { qlp[lane] = a; qlq[lane] = b; qix[lane] = v; }
+        qn = rest;
+      }
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (lane < qn) t += weight(qlp[lane], qlq[lane], qix[lane]);
+  return t;
+}
+
 // One chunk of kResidSeg entries of the residual draw: thread t owns
 // [c0 + 8t, c0 + 8t + 8).  Returns the thread's exclusive prefix within the
 // chunk (fixed order); *tot = chunk total.
@@ -2389,7 +2448,16 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
     qr = RowView{row_ptr<T>(p, drow(p, b, n)), vnmc[rd], vinv[rd], vcut[rd]};
   }
   double w[kVec];
-  const double t = resid_weights<T>(pr, qr, n < k, c64, tab, V, p.aligned, pos0, w);
+  double t;
+  if (FILT == kFiltTopp && !p.keep_w) {
+    __shared__ float nq_lp[kWaves * 128], nq_lq[kWaves * 128];
+    __shared__ int nq_ix[kWaves * 128];
+    const int wo = (tid >> 6) * 128;
+    t = resid_nuc_sparse<T>(pr, qr, n < k, c64, tab, V, p.aligned, pos0, nq_lp + wo, nq_lq + wo,
+                            nq_ix + wo);
+  } else {
+    t = resid_weights<T>(pr, qr, n < k, c64, tab, V, p.aligned, pos0, w);
+  }
   // small problems: the weights themselves, for k_resid_final
   if (p.keep_w) {
     d2* wp = reinterpret_cast<d2*>(p.wpart + ((size_t)b * p.S2 + seg) * kResidSeg + tid * kVec);

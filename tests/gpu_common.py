@@ -52,14 +52,15 @@ def draw_drafts(inp, check=None, planted=None):
     return x
 
 
-def run_chain(inp, x, mode, want_resid=None, B=None):
+def run_chain(inp, x, mode, want_resid=None, B=None, max_batch=None):
     B = inp["target"].shape[0] if B is None else B
     k = x.shape[1]
     V = inp["target"].shape[-1]
     sample = mode == SV_MODE_SAMPLE
     if want_resid is None:
         want_resid = sample
-    sv = SpecVerify(mode=mode, dtype=inp["dtype"], max_batch=max(B, 1), k=k, vocab=V,
+    sv = SpecVerify(mode=mode, dtype=inp["dtype"], max_batch=max(B, 1) if max_batch is None else max_batch,
+                    k=k, vocab=V,
                     temperature=inp.get("T", 1.0), top_k=inp.get("top_k", 0),
                     top_p=inp.get("top_p", 1.0))
     tgt = dev(inp["target"][:B], inp["dtype"])

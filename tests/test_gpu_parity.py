@@ -128,6 +128,13 @@ def test_topk_and_topp_together():
     (24, 5003, 4, 0.9, "f32"),
     (16, 4000, 3, 0.5, "bf16"),
     (16, 3000, 2, 0.99, "bf16"),
+    # float32 row sweeps read rounds of 4096 logits, each lane two quads
+    # 1024 apart per slot: a row inside one quad, quads past the end in the
+    # first slot, a last round of a few quads, a last round of one full slot
+    (8, 8, 2, 0.9, "f32"),
+    (8, 1032, 3, 0.9, "f32"),
+    (8, 4104, 3, 0.8, "f32"),
+    (8, 6144, 3, 0.95, "f32"),
 ])
 def test_sample_topp(B, V, k, top_p, dtype):
     say("sample top-p", B, V, k, top_p, dtype)
@@ -137,6 +144,24 @@ def test_sample_topp(B, V, k, top_p, dtype):
     gpu = run_chain(inp, x, SV_MODE_SAMPLE)
     orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
     compare_chain(gpu, orc, range(B), f"top-p {top_p} V={V} {dtype}")
+
+
+@pytest.mark.parametrize("B,V,k,top_p,dtype", [
+    (16, 6000, 4, 0.9, "f32"),
+    (16, 4104, 3, 0.5, "bf16"),
+    (12, 3000, 2, 0.99, "f32"),
+])
+def test_sample_topp_large_context(B, V, k, top_p, dtype):
+    """A context sized for a large batch does not keep the residual weights
+    between its two residual kernels: the per-segment masses then come from
+    the queue of nucleus-kept entries instead of every entry."""
+    say("sample top-p, large context", B, V, k, top_p, dtype)
+    inp = wl.chain_inputs(5, seed=11 + V, B=B, V=V, k=k, dtype=dtype)
+    inp["top_p"] = top_p
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE, max_batch=4096)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    compare_chain(gpu, orc, range(B), f"top-p {top_p} V={V} {dtype} large context")
 
 
 def test_sample_topp_full_workload5():
