@@ -2684,19 +2684,26 @@ DEV int block_list(int n, Pred pred, int* out, int* wsum) {
 constexpr int kTreeMax = 1024;   // nodes per tree (the API's limit)
 constexpr int kPassBatch = 4;    // nodes whose segment loads are in flight together
 
-// Pass m (0-based): grid (segment, tree).  For every node u with more than
-// m children, segment `seg` of F(c_m + D_m) at u.  The nodes' row views and
-// states are gathered first (all loads of a kind in one round); the segment
-// sums then run kPassBatch nodes at a time.
+// Pass m (0-based): grid (segment, G, tree).  The nodes u with more than m
+// children, listed in index order, are taken kPassBatch at a time; workgroup
+// (seg, g) computes segment `seg` of F(c_m + D_m) at the nodes of batches
+// g, g + G, ... (none: it returns at once).  A tree has tens of nodes with
+// children, and one workgroup running them all in turn left one or two
+// waves per SIMD to carry long dependent float64 chains; G is bounded by
+// the largest batch count pass m can have (a node with more than m children
+// has m + 1 of the other N - 1 nodes as children).  Each batch's row views
+// and states are gathered first (all loads of a kind in one round).
+constexpr int kPassGroups = 8;
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
   __shared__ int nch[kTreeMax], lst[kTreeMax];
-  __shared__ double vv[kTreeMax][4];
-  __shared__ double cn[kTreeMax];
+  __shared__ double vv[kPassBatch][4];
+  __shared__ double cn[kPassBatch];
   __shared__ double red[kPassBatch][kWaves];
   __shared__ double tab[64];
   __shared__ int wsum[kWaves];
-  const int seg = blockIdx.x, b = blockIdx.y;
+  const int seg = blockIdx.x, b = blockIdx.z;
   const int N = p.k, V = p.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const double c64 = 64.0 * kLog2e / p.T;
   for (int i = tid; i < N; i += kBlock) nch[i] = 0;
@@ -2707,36 +2714,52 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
   }
   __syncthreads();
   const int nl = block_list(N, [&](int i) { return nch[i] > m; }, lst, wsum);
-  if (nl == 0) return;
+  if ((int)blockIdx.y * kPassBatch >= nl) return;
   exp2_table_init(tab);
-  combine_rows<true, 4>(p, 2 * nl,
-                        [&](int r) { return r < nl ? trow(p, b, lst[r]) : drow(p, b, lst[r - nl]); },
-                        [&](int r, float M, int, double Z, int) {
-                          const int l = r < nl ? r : r - nl, o = r < nl ? 0 : 2;
-                          vv[l][o] = -(double)M * c64;
-                          vv[l][o + 1] = 1.0 / Z;
-                        });
-  // states after m rejections (one wave per node)
-  for (int l = w; l < nl; l += kWaves) {
-    double c = 0.0, D = 1.0;
-    for (int j = 0; j < m; ++j) {
-      const double F = tree_F(p, b, j, lst[l]);
-      if (F > 0.0) { c = c + D; D = F; }
-    }
-    if (lane == 0) cn[l] = c + D;
-  }
-  __syncthreads();
   const int pos = seg * kResidSeg + tid * kVec;
-  for (int l0 = 0; l0 < nl; l0 += kPassBatch) {
+  for (int l0 = blockIdx.y * kPassBatch; l0 < nl; l0 += gridDim.y * kPassBatch) {
+    const int nbl = nl - l0 < kPassBatch ? nl - l0 : kPassBatch;   // this batch: lst[l0, l0 + nbl)
+    // the batch's segments first: their loads are in flight while the row
+    // views and states below are gathered
+    // (raw words, unpacked one node at a time below)
+    Group<T> gp[kPassBatch], gq[kPassBatch];
+    const int nv = pos < V ? (V - pos < kVec ? V - pos : kVec) : 0;
+#pragma unroll
+    for (int q = 0; q < kPassBatch; ++q) {
+      const int u = lst[l0 + (q < nbl ? q : 0)];
+      const T* rp = row_ptr<T>(p, trow(p, b, u)) + pos;
+      const T* rq = row_ptr<T>(p, drow(p, b, u)) + pos;
+      if (p.aligned && nv == kVec) { gp[q].load(rp); gq[q].load(rq); }
+      else { gp[q].load_part(rp, nv); gq[q].load_part(rq, nv); }
+    }
+    combine_rows<true, 4>(p, 2 * nbl,
+                          [&](int r) { return r < nbl ? trow(p, b, lst[l0 + r]) : drow(p, b, lst[l0 + r - nbl]); },
+                          [&](int r, float M, int, double Z, int) {
+                            const int l = r < nbl ? r : r - nbl, o = r < nbl ? 0 : 2;
+                            vv[l][o] = -(double)M * c64;
+                            vv[l][o + 1] = 1.0 / Z;
+                          });
+    // states after m rejections (one wave per node)
+    if (w < nbl) {
+      double c = 0.0, D = 1.0;
+      for (int j = 0; j < m; ++j) {
+        const double F = tree_F(p, b, j, lst[l0 + w]);
+        if (F > 0.0) { c = c + D; D = F; }
+      }
+      if (lane == 0) cn[w] = c + D;
+    }
+    __syncthreads();
     double t[kPassBatch];
 #pragma unroll
     for (int q = 0; q < kPassBatch; ++q) {
-      const int l = l0 + q < nl ? l0 + q : l0;
-      const int u = lst[l];
-      const RowView pr{row_ptr<T>(p, trow(p, b, u)), vv[l][0], vv[l][1], 0ull};
-      const RowView qr{row_ptr<T>(p, drow(p, b, u)), vv[l][2], vv[l][3] * cn[l], 0ull};
+      const int l = q < nbl ? q : 0;
+      const RowView pr{nullptr, vv[l][0], vv[l][1], 0ull};
+      const RowView qr{nullptr, vv[l][2], vv[l][3] * cn[l], 0ull};
+      float lp[kVec], lq[kVec];
+      gp[q].opaque().values(lp);
+      gq[q].opaque().values(lq);
       double wq[kVec];
-      t[q] = resid_weights<T>(pr, qr, true, c64, tab, V, p.aligned, pos, wq);
+      t[q] = resid_weights_of(pr, qr, true, c64, tab, pos, nv, lp, lq, wq);
     }
 #pragma unroll
     for (int q = 0; q < kPassBatch; ++q) {
@@ -2744,11 +2767,11 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
       if (lane == 0) red[q][w] = ws;
     }
     __syncthreads();
-    if (tid < kPassBatch && l0 + tid < nl) {
+    if (tid < nbl) {
       const double tot = (red[tid][0] + red[tid][1]) + (red[tid][2] + red[tid][3]);
       p.tpart[(((size_t)b * kTreePasses + m) * N + lst[l0 + tid]) * p.S2 + seg] = tot;
     }
-    __syncthreads();
+    __syncthreads();   // vv, cn and red are rewritten by the next batch
   }
 }
 
@@ -3560,7 +3583,12 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
       break;
     case kFiltTreeSample: {
       const int passes = p.k - 1 < kTreePasses ? p.k - 1 : kTreePasses;
-      for (int m = 0; m < passes; ++m) hipLaunchKernelGGL((k_tsample_pass<T>), gs, block, 0, st, p, m);
+      for (int m = 0; m < passes; ++m) {
+        const int most = (p.k - 1) / (m + 1);   // nodes that can have more than m children
+        int G = (most + kPassBatch - 1) / kPassBatch;
+        G = G < 1 ? 1 : (G > kPassGroups ? kPassGroups : G);
+        hipLaunchKernelGGL((k_tsample_pass<T>), dim3((unsigned)p.S2, (unsigned)G, (unsigned)p.B), block, 0, st, p, m);
+      }
       hipLaunchKernelGGL((k_tsample_walk<T>), gb, block, 0, st, p);
       hipLaunchKernelGGL((k_tsample_mass<T>), gs, block, 0, st, p);
       hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), (p.resid_probs || p.keep_w) ? gs : gb1, block, 0, st, p);
