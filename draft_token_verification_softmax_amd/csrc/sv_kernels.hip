@@ -1077,7 +1077,6 @@ DEV void tile_topk(const Params& p, const T* row, int start, int end, int ngroup
                    uint64_t* lds) {
   __shared__ int cnt, ncg, overflow;
   __shared__ float wtau[kWaves];
-  __shared__ int redi[2 * kWaves];
   uint64_t* cand = lds;                                           // [kCandCap]
   float* gval = reinterpret_cast<float*>(lds + kCandCap);         // [kGrpCap][kVec]
   unsigned* gpos = reinterpret_cast<unsigned*>(gval + kGrpCap * kVec);   // [kGrpCap]: pos | nv << 28
