@@ -88,7 +88,7 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, row_lx, seq, spart, wpart, tpart;
+  size_t tiles, cand, nuc, row_lx, seq, spart, wpart, tpart, tview;
   size_t k_idx, k_e, k_cnt, k_norm, k_bad, k_px, total;
 };
 
@@ -114,6 +114,7 @@ Layout layout(const sv_config* c, const Plan& pl) {
   L.wpart = take(keep ? B * (size_t)pl.S2_max * sv::kResidSeg * sizeof(double) : 0);
   L.tpart = take(pl.filt == sv::kFiltTreeSample
                      ? B * (size_t)sv::kTreePasses * (size_t)c->k * (size_t)pl.S2_max * sizeof(double) : 0);
+  L.tview = take(pl.filt == sv::kFiltTreeSample ? B * (size_t)c->k * 4 * sizeof(double) : 0);
   L.k_idx = take(rows * K * sizeof(int32_t));
   L.k_e = take(rows * K * sizeof(double));
   L.k_cnt = take(K ? rows * sizeof(int32_t) : 0);
@@ -327,6 +328,7 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   p.spart = (double*)(ws + L.spart);
   p.wpart = (double*)(ws + L.wpart);
   p.tpart = (double*)(ws + L.tpart);
+  p.tview = (double*)(ws + L.tview);
   p.keep_w = (pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample) &&
              (size_t)c->max_batch * pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes ? 1 : 0;
   p.S2 = pl.S2_max;

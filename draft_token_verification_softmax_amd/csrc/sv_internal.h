@@ -129,6 +129,7 @@ struct Params {
                      // k_resid_final (loaded in its first round, no recompute)
   int tree;          // tree modes: rows have no single drafted token to record
   double* tpart;     // tree sampling: [B][kTreePasses][N][S2] residual masses per segment
+  double* tview;     // tree sampling: [B][N][4] row views (-M c64, 1/Z of target, draft) of nodes with children
   int S2;            // residual segments per sequence (kResidSeg logits each)
   // top-k: each row's kept set, rank order
   int32_t* k_idx;    // [rows][top_k]

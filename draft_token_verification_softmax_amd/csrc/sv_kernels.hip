@@ -2737,6 +2737,11 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
                             const int l = r < nbl ? r : r - nbl, o = r < nbl ? 0 : 2;
                             vv[l][o] = -(double)M * c64;
                             vv[l][o + 1] = 1.0 / Z;
+                            // pass 0 covers every node with children: the walk reads its views here
+                            if (m == 0 && seg == 0) {
+                              p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o] = -(double)M * c64;
+                              p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o + 1] = 1.0 / Z;
+                            }
                           });
     // states after m rejections (one wave per node)
     if (w < nbl) {
@@ -2788,7 +2793,9 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
   __shared__ double sv[4];
   __shared__ int sbad[2];
   __shared__ int wsum[kWaves];
-  __shared__ double sh_F;
+  __shared__ double vw[kTreeMax][4];
+  __shared__ double Fv[kTreePasses][kTreeMax];
+  __shared__ int pr_l[kTreePasses * kTreeMax];
   const int b = blockIdx.x, N = p.k, V = p.V, tid = threadIdx.x;
   const double c64 = 64.0 * kLog2e / p.T;
   // one round of loads: parents, tokens, uniforms
@@ -2804,18 +2811,12 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
   }
   __syncthreads();
   for (int i = tid; i < N; i += kBlock) if (par[i] >= 0) atomicAdd(&nch[par[i]], 1);
-  // rows: every target row, and the draft row of every node with a child
-  combine_rows<true>(p, 2 * N, [&](int r) { return r < N ? trow(p, b, r) : drow(p, b, r - N); },
-                     [&](int r, float, int, double, int bad) { rbad[r] = (unsigned char)bad; });
-  badpar = __syncthreads_or(badpar);
-  int mybad = 0;
-  for (int i = tid; i < N; i += kBlock) mybad |= rbad[i] | (nch[i] > 0 ? rbad[N + i] : 0);
-  if (__syncthreads_or(mybad)) {
-    emit_invalid(p, b, 4);
-    if (tid == 0) p.seq[b].n = -1;
-    return;
-  }
-  // the logits the tests read: child c's token in its parent's two rows
+  __syncthreads();
+  // the logits the tests read (child c's token in its parent's two rows),
+  // the views of every node with children (written by pass 0) and, for the
+  // first kTreePasses rejections at a node, F from the passes' segment
+  // masses (summed as tree_F sums them, so the bits are the same): all
+  // issued before the walk needs any of them
   for (int i = tid; i < N; i += kBlock) {
     const int x = tok[i], q = par[i];
     float a = 0.f, d = 0.f;
@@ -2825,6 +2826,43 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
     }
     lpx[i] = a;
     lqx[i] = d;
+  }
+  for (int i = tid; i < N * 4; i += kBlock) {
+    const int u = i >> 2;
+    vw[u][i & 3] = nch[u] > 0 ? p.tview[((size_t)b * N + u) * 4 + (i & 3)] : 0.0;
+  }
+  const int passes = N - 1 < kTreePasses ? N - 1 : kTreePasses;
+  const int npairs = block_list(passes * N, [&](int k) { return nch[k % N] > k / N; }, pr_l, wsum);
+  constexpr int kFBatch = 8;
+  const int fl = tid & 63;
+  for (int k0 = tid >> 6; k0 < npairs; k0 += kWaves * kFBatch) {
+    double t[kFBatch];
+#pragma unroll
+    for (int q = 0; q < kFBatch; ++q) {
+      const int k = k0 + q * kWaves;
+      const int pk = pr_l[k < npairs ? k : 0];
+      const double* src = p.tpart + (((size_t)b * kTreePasses + pk / N) * N + pk % N) * p.S2;
+      t[q] = 0.0;
+      for (int s2 = fl; s2 < p.S2; s2 += 64) t[q] += src[s2];
+    }
+#pragma unroll
+    for (int q = 0; q < kFBatch; ++q) {
+      const int k = k0 + q * kWaves;
+      const double f = wave_sum(t[q]);
+      if (k < npairs && fl == 0) Fv[pr_l[k] / N][pr_l[k] % N] = f;
+    }
+  }
+  // rows: every target row, and the draft row of every node with a child
+  // (validity only: a NaN partial or an infinite maximum; no row sums)
+  combine_rows<false>(p, 2 * N, [&](int r) { return r < N ? trow(p, b, r) : drow(p, b, r - N); },
+                      [&](int r, float, int, double, int bad) { rbad[r] = (unsigned char)bad; });
+  badpar = __syncthreads_or(badpar);
+  int mybad = 0;
+  for (int i = tid; i < N; i += kBlock) mybad |= rbad[i] | (nch[i] > 0 ? rbad[N + i] : 0);
+  if (__syncthreads_or(mybad)) {
+    emit_invalid(p, b, 4);
+    if (tid == 0) p.seq[b].n = -1;
+    return;
   }
   exp2_table_init(tab);
   // the walk (every thread follows it; F values from wave 0)
@@ -2836,7 +2874,7 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
     D = 1.0;
     const int nk = block_list(N, [&](int i) { return par[i] == cur; }, lst, wsum);
     if (nk == 0) break;
-    tree_views(p, b, cur, c64, sv, sbad);
+    const double* vc = vw[cur];   // the views of cur's two rows
     int nxt = -1;
     for (int j = 0; j < nk; ++j) {
       const int ch = lst[j];
@@ -2845,8 +2883,8 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
       if (x < 0 || x >= V) {
         st |= 1;
       } else {
-        const double pa = exp2_64(fma((double)lpx[ch], c64, sv[0]), tab) * sv[1];
-        const double qa = exp2_64(fma((double)lqx[ch], c64, sv[2]), tab) * sv[3];
+        const double pa = exp2_64(fma((double)lpx[ch], c64, vc[0]), tab) * vc[1];
+        const double qa = exp2_64(fma((double)lqx[ch], c64, vc[2]), tab) * vc[3];
         const double dd = pa - c * qa;
         const double a = (dd > 0.0 ? dd : 0.0) / D;
         acc = qa > 0.0 ? ((double)uu[ch] < fmin(1.0, a / qa)) : (a > 0.0);
@@ -2855,17 +2893,11 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
       // rejected: F at c + D, from pass j, or from a pass of this workgroup
       double F;
       if (j < kTreePasses) {
-        if (tid < 64) {
-          const double f = tree_F(p, b, j, cur);
-          if (tid == 0) sh_F = f;
-        }
-        __syncthreads();
-        F = sh_F;
-        __syncthreads();
+        F = Fv[j][cur];
       } else {
         const double cn = c + D;
-        const RowView pr{row_ptr<T>(p, trow(p, b, cur)), sv[0], sv[1], 0ull};
-        const RowView qr{row_ptr<T>(p, drow(p, b, cur)), sv[2], sv[3] * cn, 0ull};
+        const RowView pr{row_ptr<T>(p, trow(p, b, cur)), vc[0], vc[1], 0ull};
+        const RowView qr{row_ptr<T>(p, drow(p, b, cur)), vc[2], vc[3] * cn, 0ull};
         double t = 0.0;
         for (int c0 = 0; c0 < V; c0 += kResidSeg) {
           double w[kVec];
