@@ -2683,14 +2683,16 @@ DEV int block_list(int n, Pred pred, int* out, int* wsum) {
 constexpr int kTreeMax = 1024;   // nodes per tree (the API's limit)
 constexpr int kPassBatch = 4;    // nodes whose segment loads are in flight together
 
-// Pass m (0-based): grid (segment, G, tree).  The nodes u with more than m
+// Pass m (0-based): grid (segment, tree, G).  The nodes u with more than m
 // children, listed in index order, are taken kPassBatch at a time; workgroup
 // (seg, g) computes segment `seg` of F(c_m + D_m) at the nodes of batches
 // g, g + G, ... (none: it returns at once).  A tree has tens of nodes with
 // children, and one workgroup running them all in turn left one or two
 // waves per SIMD to carry long dependent float64 chains; G is bounded by
 // the largest batch count pass m can have (a node with more than m children
-// has m + 1 of the other N - 1 nodes as children).  Each batch's row views
+// has m + 1 of the other N - 1 nodes as children), and g is the slowest grid
+// dimension, so the workgroups of batch 0, which every pass with work has,
+// are dispatched first.  Each batch's row views
 // and states are gathered first (all loads of a kind in one round).
 constexpr int kPassGroups = 8;
 
@@ -2702,7 +2704,7 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
   __shared__ double red[kPassBatch][kWaves];
   __shared__ double tab[64];
   __shared__ int wsum[kWaves];
-  const int seg = blockIdx.x, b = blockIdx.z;
+  const int seg = blockIdx.x, b = blockIdx.y;
   const int N = p.k, V = p.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const double c64 = 64.0 * kLog2e / p.T;
   for (int i = tid; i < N; i += kBlock) nch[i] = 0;
@@ -2713,10 +2715,10 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
   }
   __syncthreads();
   const int nl = block_list(N, [&](int i) { return nch[i] > m; }, lst, wsum);
-  if ((int)blockIdx.y * kPassBatch >= nl) return;
+  if ((int)blockIdx.z * kPassBatch >= nl) return;
   exp2_table_init(tab);
   const int pos = seg * kResidSeg + tid * kVec;
-  for (int l0 = blockIdx.y * kPassBatch; l0 < nl; l0 += gridDim.y * kPassBatch) {
+  for (int l0 = blockIdx.z * kPassBatch; l0 < nl; l0 += gridDim.z * kPassBatch) {
     const int nbl = nl - l0 < kPassBatch ? nl - l0 : kPassBatch;   // this batch: lst[l0, l0 + nbl)
     // the batch's segments first: their loads are in flight while the row
     // views and states below are gathered
@@ -2743,12 +2745,26 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
                               p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o + 1] = 1.0 / Z;
                             }
                           });
-    // states after m rejections (one wave per node)
+    // states after m rejections (one wave per node): F of the earlier passes
+    // summed as tree_F sums them, every pass's loads issued together
+    // (unconditionally: a pass not yet run reads pass 0's slots, unused)
     if (w < nbl) {
+      const int u = lst[l0 + w];
+      double f[kTreePasses - 1];
+#pragma unroll
+      for (int j = 0; j < kTreePasses - 1; ++j) f[j] = 0.0;
+      for (int s2 = lane; s2 < p.S2; s2 += 64) {
+#pragma unroll
+        for (int j = 0; j < kTreePasses - 1; ++j)
+          f[j] += p.tpart[(((size_t)b * kTreePasses + (j < m ? j : 0)) * N + u) * p.S2 + s2];
+      }
       double c = 0.0, D = 1.0;
-      for (int j = 0; j < m; ++j) {
-        const double F = tree_F(p, b, j, lst[l0 + w]);
-        if (F > 0.0) { c = c + D; D = F; }
+#pragma unroll
+      for (int j = 0; j < kTreePasses - 1; ++j) {
+        if (j < m) {
+          const double F = wave_sum(f[j]);
+          if (F > 0.0) { c = c + D; D = F; }
+        }
       }
       if (lane == 0) cn[w] = c + D;
     }
@@ -3618,7 +3634,7 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
         const int most = (p.k - 1) / (m + 1);   // nodes that can have more than m children
         int G = (most + kPassBatch - 1) / kPassBatch;
         G = G < 1 ? 1 : (G > kPassGroups ? kPassGroups : G);
-        hipLaunchKernelGGL((k_tsample_pass<T>), dim3((unsigned)p.S2, (unsigned)G, (unsigned)p.B), block, 0, st, p, m);
+        hipLaunchKernelGGL((k_tsample_pass<T>), dim3((unsigned)p.S2, (unsigned)p.B, (unsigned)G), block, 0, st, p, m);
       }
       hipLaunchKernelGGL((k_tsample_walk<T>), gb, block, 0, st, p);
       hipLaunchKernelGGL((k_tsample_mass<T>), gs, block, 0, st, p);
