@@ -93,6 +93,10 @@ def compare(gpu, orc, which, label):
     (8, 20, 4000, "f32", 1.0, 1),       # path-shaped trees
     (10, 2, 2048, "bf16", 1.0, 4),
     (10, 1, 2048, "f32", 1.0, 4),       # a root alone: the bonus draw
+    # more nodes with children than one launch's workgroups take in one
+    # batch each (a workgroup then runs several batches of its pass)
+    (6, 80, 2048, "bf16", 1.0, 1),
+    (6, 120, 2048, "f32", 1.0, 2),
 ])
 def test_tree_sample_parity(B, N, V, dtype, T, mc):
     say("tree sample", B, N, V, dtype, T, mc)
