@@ -2692,8 +2692,8 @@ constexpr int kPassBatch = 4;    // nodes whose segment loads are in flight toge
 // the largest batch count pass m can have (a node with more than m children
 // has m + 1 of the other N - 1 nodes as children), and g is the slowest grid
 // dimension, so the workgroups of batch 0, which every pass with work has,
-// are dispatched first.  Each batch's row views
-// and states are gathered first (all loads of a kind in one round).
+// are dispatched first.  Each batch's segment loads are issued first, then
+// its row views and states are gathered (all loads of a kind in one round).
 constexpr int kPassGroups = 8;
 
 template <typename T>
