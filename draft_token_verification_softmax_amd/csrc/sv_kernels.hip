@@ -388,33 +388,37 @@ DEV float maximum8(const float v[kVec]) {
 
 // ------------------------------------------------------------------ float64 exp2
 
-// 2^(y64 / 64) to a few ulp of float64, for the streaming sums.
-// y64 = 64 j + f with j = rint(y64), |f| <= 1/2:
-//   2^(y64/64) = 2^(j >> 6) * 2^((j & 63) / 64) * e^(f ln2 / 64);
-// the middle factor comes from a 64-entry table, the last from its Taylor
-// series to degree 5 (|f ln2 / 64| <= 0.0055, remainder below 4e-17).
-// Arguments below -70000 (results below 2^-1093, i.e. 0) and NaN give 0.
-constexpr double kE1 = 0.010830424696249145;     // (ln2/64)^i / i!
-constexpr double kE2 = 5.86490495505617e-05;
-constexpr double kE3 = 2.1173137155464776e-07;
-constexpr double kE4 = 5.732851688640402e-10;
-constexpr double kE5 = 1.2417843701716925e-12;
+// 2^(y / kExpTab) to a few ulp of float64, for the streaming sums; callers
+// scale their arguments by kExpTab (cs = kExpTab log2(e) / T).
+// y = kExpTab j + f with j = rint(y), |f| <= 1/2:
+//   2^(y/kExpTab) = 2^(j >> 8) * 2^((j & 255) / 256) * e^(f ln2 / 256);
+// the middle factor comes from a 256-entry table in LDS, the last from its
+// Taylor series to degree 4 (|f ln2 / 256| <= 0.00136, remainder below
+// 4e-17: one fma less than a 64-entry table needs for the same bound).
+// Arguments below -280000 (results below 2^-1093, i.e. 0) and NaN give 0.
+constexpr int kExpTabBits = 8;
+constexpr int kExpTab = 1 << kExpTabBits;
+constexpr double kExpScale = (double)kExpTab;
+constexpr double kE1 = 0.0027076061740622863;    // (ln2/256)^i / i!
+constexpr double kE2 = 3.6655655969101062e-06;
+constexpr double kE3 = 3.3083026805413713e-09;
+constexpr double kE4 = 2.239395190875157e-12;
+static_assert(kExpTab == kBlock, "one table entry per thread of the block");
 
 DEV void exp2_table_init(double* tab) {
-  if (threadIdx.x < 64) tab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / 64.0));
+  tab[threadIdx.x] = exp2((double)threadIdx.x * (1.0 / kExpScale));
   __syncthreads();
 }
-DEV double exp2_64(double y64, const double* tab) {
-  y64 = fmax(y64, -70000.0);
-  const double j = rint(y64);
-  const double f = y64 - j;
-  double q = fma(f, kE5, kE4);
-  q = fma(q, f, kE3);
+DEV double exp2_64(double y, const double* tab) {
+  y = fmax(y, -280000.0);
+  const double j = rint(y);
+  const double f = y - j;
+  double q = fma(f, kE4, kE3);
   q = fma(q, f, kE2);
   q = fma(q, f, kE1);
   q = fma(q, f, 1.0);
   const int ji = (int)j;
-  return ldexp(tab[ji & 63] * q, ji >> 6);
+  return ldexp(tab[ji & (kExpTab - 1)] * q, ji >> kExpTabBits);
 }
 
 // 2^y for y <= 0 in float64 with few registers: y = j + f, j = rint(y),
@@ -838,14 +842,14 @@ DEV int row_token(const Params& p, int grow, bool* has) {
 // The wave combines its lanes in float64 by one fixed butterfly.
 template <typename T, bool EXACT>
 DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow, int seg) {
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   bool xhas;
   const int xt = row_token(p, grow, &xhas);
   float lx = 0.f;
   bool hx = false;
   if (EXACT) exp2_table_init(tab);
   const double cd = kLog2e / p.T;
-  const double c64 = 64.0 * cd;
+  const double cs = kExpScale * cd;
   // c_hi <= c and c_lo > 0, so that a -inf logit gives d * c_lo = -inf and
   // a term of exactly 0 (never inf - inf)
   float c_hi = (float)cd;
@@ -887,10 +891,10 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
         float v[kVec];
         gr[u].opaque().values(v);
         if (EXACT) {
-          const double nmc = -(double)m * c64;
+          const double nmc = -(double)m * cs;
           double gs = 0.0;
 #pragma unroll
-          for (int q = 0; q < kVec; ++q) gs += exp2_64(fma((double)v[q], c64, nmc), tab);
+          for (int q = 0; q < kVec; ++q) gs += exp2_64(fma((double)v[q], cs, nmc), tab);
           s += u < nv ? gs : 0.0;
         } else {
           float e[kVec];
@@ -1404,17 +1408,17 @@ DEV int first_failure(bool fail, bool invalid, int k, int* st) {
 }
 
 // Adjusted probability of one entry of a row (plain softmax or nucleus):
-// p'(v) = 2^((l_v - M) c64 / 64) / norm on the kept set, c64 = 64 log2e / T.
+// p'(v) = 2^((l_v - M) cs / kExpTab) / norm on the kept set, cs = kExpTab log2e / T.
 struct RowView {
   const void* row;
-  double nmc;     // -M * c64 (M = max logit of the row)
+  double nmc;     // -M * cs (M = max logit of the row)
   double inv;     // 1 / norm (Z, or nucleus mass)
   uint64_t cut;   // nucleus: v is kept iff pack(l_v, v) >= cut; 0 = no nucleus
 };
 
-DEV double prob_from(const RowView& r, double c64, const double* tab, float l, int v) {
+DEV double prob_from(const RowView& r, double cs, const double* tab, float l, int v) {
   if (r.cut && pack(l, v) < r.cut) return 0.0;
-  return exp2_64(fma((double)l, c64, r.nmc), tab) * r.inv;
+  return exp2_64(fma((double)l, cs, r.nmc), tab) * r.inv;
 }
 
 // Residual weights of the kVec entries [pos, pos + kVec) of one chunk:
@@ -1422,7 +1426,7 @@ DEV double prob_from(const RowView& r, double c64, const double* tab, float l, i
 // Residual weights of kVec entries from their logits (lp: target row n,
 // lq: draft row n; n valid entries): w = max(0, p'(v) - q'(v)), or p'(v)
 // without q.  Returns their sum.
-DEV double resid_weights_of(const RowView& pr, const RowView& qr, bool hasq, double c64,
+DEV double resid_weights_of(const RowView& pr, const RowView& qr, bool hasq, double cs,
                             const double* tab, int pos, int n, const float lp[kVec],
                             const float lq[kVec], double w[kVec]) {
   double t = 0.0;
@@ -1430,9 +1434,9 @@ DEV double resid_weights_of(const RowView& pr, const RowView& qr, bool hasq, dou
   for (int q = 0; q < kVec; ++q) {
     double wq = 0.0;
     if (q < n) {
-      wq = prob_from(pr, c64, tab, lp[q], pos + q);
+      wq = prob_from(pr, cs, tab, lp[q], pos + q);
       if (hasq) {
-        wq -= prob_from(qr, c64, tab, lq[q], pos + q);
+        wq -= prob_from(qr, cs, tab, lq[q], pos + q);
         wq = wq > 0.0 ? wq : 0.0;
       }
     }
@@ -1444,7 +1448,7 @@ DEV double resid_weights_of(const RowView& pr, const RowView& qr, bool hasq, dou
 
 // The same for the kVec entries [pos, pos + kVec) loaded from the rows.
 template <typename T>
-DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double c64,
+DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double cs,
                          const double* tab, int V, int aligned, int pos, double w[kVec]) {
   float lp[kVec], lq[kVec];
   int n = 0;
@@ -1452,7 +1456,7 @@ DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double
     n = load_group<T>((const T*)pr.row, pos, V, aligned, lp);
     if (hasq) load_group<T>((const T*)qr.row, pos, V, aligned, lq);
   }
-  return resid_weights_of(pr, qr, hasq, c64, tab, pos, n, lp, lq, w);
+  return resid_weights_of(pr, qr, hasq, cs, tab, pos, n, lp, lq, w);
 }
 
 // The residual mass of the kVec entries [pos, pos + kVec) of nucleus rows
@@ -1463,7 +1467,7 @@ DEV double resid_weights(const RowView& pr, const RowView& qr, bool hasq, double
 // evaluation per lane instead of one per entry of the row.  Queue slots:
 // 128 per wave (64 + at most 63 before a flush).
 template <typename T>
-DEV double resid_nuc_sparse(const RowView& pr, const RowView& qr, bool hasq, double c64,
+DEV double resid_nuc_sparse(const RowView& pr, const RowView& qr, bool hasq, double cs,
                             const double* tab, int V, int aligned, int pos, float* qlp,
                             float* qlq, int* qix) {
   float lp[kVec], lq[kVec];
@@ -1474,9 +1478,9 @@ DEV double resid_nuc_sparse(const RowView& pr, const RowView& qr, bool hasq, dou
   }
   const int lane = threadIdx.x & 63;
   auto weight = [&](float a, float b, int v) {
-    double w = exp2_64(fma((double)a, c64, pr.nmc), tab) * pr.inv;
+    double w = exp2_64(fma((double)a, cs, pr.nmc), tab) * pr.inv;
     if (hasq) {
-      w -= prob_from(qr, c64, tab, b, v);
+      w -= prob_from(qr, cs, tab, b, v);
       w = w > 0.0 ? w : 0.0;
     }
     return w;
@@ -1518,10 +1522,10 @@ DEV double resid_nuc_sparse(const RowView& pr, const RowView& qr, bool hasq, dou
 // [c0 + 8t, c0 + 8t + 8).  Returns the thread's exclusive prefix within the
 // chunk (fixed order); *tot = chunk total.
 template <typename T>
-DEV double resid_chunk(const RowView& pr, const RowView& qr, bool hasq, double c64,
+DEV double resid_chunk(const RowView& pr, const RowView& qr, bool hasq, double cs,
                        const double* tab, int V, int aligned, int c0, double w[kVec], double* red,
                        double* tot) {
-  const double t = resid_weights<T>(pr, qr, hasq, c64, tab, V, aligned, c0 + threadIdx.x * kVec, w);
+  const double t = resid_weights<T>(pr, qr, hasq, cs, tab, V, aligned, c0 + threadIdx.x * kVec, w);
   return block_exscan(t, red, tot);
 }
 
@@ -1544,14 +1548,14 @@ DEV int pick_in_chunk(double base, double ex, const double w[kVec], int c0, doub
 // Inverse CDF over a whole row inside one workgroup (the empty-residual
 // fallback, over p' alone): y = min{v : C_v > ur * S'}.
 template <typename T>
-DEV int resid_draw(const RowView& pr, double c64, const double* tab, int V, int aligned, double ur,
+DEV int resid_draw(const RowView& pr, double cs, const double* tab, int V, int aligned, double ur,
                    double* red, int* redi, double* S_out) {
   const RowView none{nullptr, 0.0, 1.0, 0ull};
   double w[kVec];
   double S = 0.0;
   for (int c0 = 0; c0 < V; c0 += kResidSeg) {
     double tot;
-    resid_chunk<T>(pr, none, false, c64, tab, V, aligned, c0, w, red, &tot);
+    resid_chunk<T>(pr, none, false, cs, tab, V, aligned, c0, w, red, &tot);
     S += tot;
   }
   *S_out = S;
@@ -1561,13 +1565,13 @@ DEV int resid_draw(const RowView& pr, double c64, const double* tab, int V, int 
   int lastc = 0;
   for (int c0 = 0; c0 < V; c0 += kResidSeg) {
     double tot;
-    const double ex = resid_chunk<T>(pr, none, false, c64, tab, V, aligned, c0, w, red, &tot);
+    const double ex = resid_chunk<T>(pr, none, false, cs, tab, V, aligned, c0, w, red, &tot);
     if (tot > 0.0) lastc = c0;
     if (base + tot > t) return pick_in_chunk(base, ex, w, c0, t, redi);
     base += tot;
   }
   double tot;
-  const double ex = resid_chunk<T>(pr, none, false, c64, tab, V, aligned, lastc, w, red, &tot);
+  const double ex = resid_chunk<T>(pr, none, false, cs, tab, V, aligned, lastc, w, red, &tot);
   return pick_in_chunk(-INFINITY, ex, w, lastc, INFINITY, redi);
 }
 
@@ -2380,11 +2384,11 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   __shared__ float vlx[kMaxRows];
   __shared__ int vbad[kMaxRows];
   __shared__ double red[kWaves];
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   __shared__ int sh_n, sh_st;
   const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
   const int k = p.k, V = p.V, nrows = p.rows_t + p.rows_d;
-  const double c64 = 64.0 * kLog2e / p.T;
+  const double cs = kExpScale * kLog2e / p.T;
   auto row_of = [&](int r) { return r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t); };
   // one round of loads, all unconditional (clamped indices): drafted
   // tokens, uniforms, the drafted tokens' logits (recorded by the streaming
@@ -2398,13 +2402,13 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   if constexpr (FILT == kFiltTopp) {
     const RowNuc nu = p.nuc[row_of(ri)];
     if (tid < nrows) {
-      vnmc[tid] = -(double)nu.M * c64; vinv[tid] = 1.0 / nu.N; vcut[tid] = nu.cut; vbad[tid] = nu.ok != 1;
+      vnmc[tid] = -(double)nu.M * cs; vinv[tid] = 1.0 / nu.N; vcut[tid] = nu.cut; vbad[tid] = nu.ok != 1;
       internal = nu.ok == 2;
     }
   } else {
     // four partials per lane: short float64 chains for this latency-bound kernel
     combine_rows<true, 4>(p, nrows, row_of, [&](int r, float M, int, double Z, int bad) {
-      vnmc[r] = -(double)M * c64; vinv[r] = 1.0 / Z; vcut[r] = 0ull; vbad[r] = bad;
+      vnmc[r] = -(double)M * cs; vinv[r] = 1.0 / Z; vcut[r] = 0ull; vbad[r] = bad;
     });
   }
   if (tid < nrows) vlx[tid] = lx;
@@ -2429,8 +2433,8 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
       const int rd = p.rows_t + tid;
       const RowView vt{nullptr, vnmc[tid], vinv[tid], vcut[tid]};
       const RowView vd{nullptr, vnmc[rd], vinv[rd], vcut[rd]};
-      const double a = prob_from(vt, c64, tab, vlx[tid], xj);
-      const double q = prob_from(vd, c64, tab, vlx[rd], xj);
+      const double a = prob_from(vt, cs, tab, vlx[tid], xj);
+      const double q = prob_from(vd, cs, tab, vlx[rd], xj);
       acc = q > 0.0 ? ((double)uj < fmin(1.0, a / q)) : (a > 0.0);
     }
     int st;
@@ -2452,10 +2456,10 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
     __shared__ float nq_lp[kWaves * 128], nq_lq[kWaves * 128];
     __shared__ int nq_ix[kWaves * 128];
     const int wo = (tid >> 6) * 128;
-    t = resid_nuc_sparse<T>(pr, qr, n < k, c64, tab, V, p.aligned, pos0, nq_lp + wo, nq_lq + wo,
+    t = resid_nuc_sparse<T>(pr, qr, n < k, cs, tab, V, p.aligned, pos0, nq_lp + wo, nq_lq + wo,
                             nq_ix + wo);
   } else {
-    t = resid_weights<T>(pr, qr, n < k, c64, tab, V, p.aligned, pos0, w);
+    t = resid_weights<T>(pr, qr, n < k, cs, tab, V, p.aligned, pos0, w);
   }
   // small problems: the weights themselves, for k_resid_final
   if (p.keep_w) {
@@ -2481,7 +2485,7 @@ constexpr int kSegStage = 1024;   // residual segment masses held in registers (
 template <typename T, int FILT>
 __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   __shared__ double red[kWaves];
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   __shared__ int sx[64];
   __shared__ int redi[2 * kWaves];
   __shared__ double sh_base;
@@ -2494,7 +2498,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
   const int S2 = p.S2, V = p.V, k = p.k;
   const bool single = gridDim.x == 1 && S2 > 1;
   const bool use_w = p.keep_w && !single;
-  const double c64 = 64.0 * kLog2e / p.T;
+  const double cs = kExpScale * kLog2e / p.T;
   // one round of loads, all unconditional: sequence state, ur, the segment
   // masses this thread owns ([tid*per, (tid+1)*per)), drafted tokens, and
   // this workgroup's own segment weights (written by k_resid_s)
@@ -2536,12 +2540,12 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
     const RowView pr{row_ptr<T>(p, trow(p, b, node)), ss.nmc_p, ss.inv_p, ss.cut_p};
     const RowView none{nullptr, 0.0, 1.0, 0ull};
     double S1;
-    const int y = resid_draw<T>(pr, c64, tab, V, p.aligned, ur, red, redi, &S1);
+    const int y = resid_draw<T>(pr, cs, tab, V, p.aligned, ur, red, redi, &S1);
     if (p.resid_probs) {
       float* rp = p.resid_probs + (size_t)b * V;
       for (int c0 = 0; c0 < V; c0 += kResidSeg) {
         double w1[kVec];
-        resid_weights<T>(pr, none, false, c64, tab, V, p.aligned, c0 + tid * kVec, w1);
+        resid_weights<T>(pr, none, false, cs, tab, V, p.aligned, c0 + tid * kVec, w1);
 #pragma unroll
         for (int q = 0; q < kVec; ++q) {
           const int v = c0 + tid * kVec + q;
@@ -2596,7 +2600,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
     exp2_table_init(tab);
     const RowView pr{row_ptr<T>(p, trow(p, b, node)), ss.nmc_p, ss.inv_p, ss.cut_p};
     const RowView qr{hasq ? row_ptr<T>(p, drow(p, b, node)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
-    resid_weights<T>(pr, qr, hasq, c64, tab, V, p.aligned, c0 + tid * kVec, w);
+    resid_weights<T>(pr, qr, hasq, cs, tab, V, p.aligned, c0 + tid * kVec, w);
   }
   if (seg == c) {
     double tl = 0.0;
@@ -2646,13 +2650,13 @@ DEV double tree_F(const Params& p, int b, int m, int u) {
 }
 
 // Views of node u's target row (sv[0], sv[1]) and draft row (sv[2], sv[3]):
-// -M * c64 and 1 / Z from the row partials; sbad[0..1] their bad flags.
+// -M * cs and 1 / Z from the row partials; sbad[0..1] their bad flags.
 // Every thread calls it; the results are in LDS after the call.  (Four
 // partials per lane, as in the residual passes, so both see the same bits.)
-DEV void tree_views(const Params& p, int b, int u, double c64, double* sv, int* sbad) {
+DEV void tree_views(const Params& p, int b, int u, double cs, double* sv, int* sbad) {
   combine_rows<true, 4>(p, 2, [&](int r) { return r == 0 ? trow(p, b, u) : drow(p, b, u); },
                         [&](int r, float M, int, double Z, int bad) {
-                          sv[2 * r] = -(double)M * c64;
+                          sv[2 * r] = -(double)M * cs;
                           sv[2 * r + 1] = 1.0 / Z;
                           sbad[r] = bad;
                         });
@@ -2702,11 +2706,11 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
   __shared__ double vv[kPassBatch][4];
   __shared__ double cn[kPassBatch];
   __shared__ double red[kPassBatch][kWaves];
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   __shared__ int wsum[kWaves];
   const int seg = blockIdx.x, b = blockIdx.y;
   const int N = p.k, V = p.V, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const double c64 = 64.0 * kLog2e / p.T;
+  const double cs = kExpScale * kLog2e / p.T;
   for (int i = tid; i < N; i += kBlock) nch[i] = 0;
   __syncthreads();
   for (int i = tid; i < N; i += kBlock) {
@@ -2737,11 +2741,11 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
                           [&](int r) { return r < nbl ? trow(p, b, lst[l0 + r]) : drow(p, b, lst[l0 + r - nbl]); },
                           [&](int r, float M, int, double Z, int) {
                             const int l = r < nbl ? r : r - nbl, o = r < nbl ? 0 : 2;
-                            vv[l][o] = -(double)M * c64;
+                            vv[l][o] = -(double)M * cs;
                             vv[l][o + 1] = 1.0 / Z;
                             // pass 0 covers every node with children: the walk reads its views here
                             if (m == 0 && seg == 0) {
-                              p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o] = -(double)M * c64;
+                              p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o] = -(double)M * cs;
                               p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o + 1] = 1.0 / Z;
                             }
                           });
@@ -2779,7 +2783,7 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
       gp[q].opaque().values(lp);
       gq[q].opaque().values(lq);
       double wq[kVec];
-      t[q] = resid_weights_of(pr, qr, true, c64, tab, pos, nv, lp, lq, wq);
+      t[q] = resid_weights_of(pr, qr, true, cs, tab, pos, nv, lp, lq, wq);
     }
 #pragma unroll
     for (int q = 0; q < kPassBatch; ++q) {
@@ -2805,7 +2809,7 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
   __shared__ float uu[kTreeMax], lpx[kTreeMax], lqx[kTreeMax];
   __shared__ unsigned char rbad[2 * kTreeMax];
   __shared__ double red[kWaves];
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   __shared__ double sv[4];
   __shared__ int sbad[2];
   __shared__ int wsum[kWaves];
@@ -2813,7 +2817,7 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
   __shared__ double Fv[kTreePasses][kTreeMax];
   __shared__ int pr_l[kTreePasses * kTreeMax];
   const int b = blockIdx.x, N = p.k, V = p.V, tid = threadIdx.x;
-  const double c64 = 64.0 * kLog2e / p.T;
+  const double cs = kExpScale * kLog2e / p.T;
   // one round of loads: parents, tokens, uniforms
   int badpar = 0;
   for (int i = tid; i < N; i += kBlock) {
@@ -2899,8 +2903,8 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
       if (x < 0 || x >= V) {
         st |= 1;
       } else {
-        const double pa = exp2_64(fma((double)lpx[ch], c64, vc[0]), tab) * vc[1];
-        const double qa = exp2_64(fma((double)lqx[ch], c64, vc[2]), tab) * vc[3];
+        const double pa = exp2_64(fma((double)lpx[ch], cs, vc[0]), tab) * vc[1];
+        const double qa = exp2_64(fma((double)lqx[ch], cs, vc[2]), tab) * vc[3];
         const double dd = pa - c * qa;
         const double a = (dd > 0.0 ? dd : 0.0) / D;
         acc = qa > 0.0 ? ((double)uu[ch] < fmin(1.0, a / qa)) : (a > 0.0);
@@ -2917,7 +2921,7 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
         double t = 0.0;
         for (int c0 = 0; c0 < V; c0 += kResidSeg) {
           double w[kVec];
-          t += resid_weights<T>(pr, qr, true, c64, tab, V, p.aligned, c0 + tid * kVec, w);
+          t += resid_weights<T>(pr, qr, true, cs, tab, V, p.aligned, c0 + tid * kVec, w);
         }
         F = block_sum(t, red);
       }
@@ -2935,7 +2939,7 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
     if (i != n) ot[i] = i < n ? tok[path[i + 1]] : -1;
     if (p.out_nodes) p.out_nodes[(size_t)b * p.out_w + i] = i <= n ? path[i] : -1;
   }
-  tree_views(p, b, cur, c64, sv, sbad);
+  tree_views(p, b, cur, cs, sv, sbad);
   if (tid == 0) {
     p.acc_len[b] = n;
     const int status = st | (badpar ? 2 : 0);
@@ -2952,16 +2956,16 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tsample_mass(Params p) {
   __shared__ double red[kWaves];
-  __shared__ double tab[64];
+  __shared__ double tab[kExpTab];
   const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
-  const double c64 = 64.0 * kLog2e / p.T;
+  const double cs = kExpScale * kLog2e / p.T;
   const SeqState ss = p.seq[b];
   exp2_table_init(tab);
   if (ss.n < 0) return;
   const RowView pr{row_ptr<T>(p, trow(p, b, ss.node)), ss.nmc_p, ss.inv_p, ss.cut_p};
   const RowView qr{ss.hasq ? row_ptr<T>(p, drow(p, b, ss.node)) : nullptr, ss.nmc_q, ss.inv_q, ss.cut_q};
   double w[kVec];
-  const double t = resid_weights<T>(pr, qr, ss.hasq != 0, c64, tab, p.V, p.aligned, seg * kResidSeg + tid * kVec, w);
+  const double t = resid_weights<T>(pr, qr, ss.hasq != 0, cs, tab, p.V, p.aligned, seg * kResidSeg + tid * kVec, w);
   if (p.keep_w) {
     d2* wp = reinterpret_cast<d2*>(p.wpart + ((size_t)b * p.S2 + seg) * kResidSeg + tid * kVec);
 #pragma unroll
