@@ -97,6 +97,7 @@ def compare(gpu, orc, which, label):
     # batch each (a workgroup then runs several batches of its pass)
     (6, 80, 2048, "bf16", 1.0, 1),
     (6, 120, 2048, "f32", 1.0, 2),
+    (2, 1024, 1024, "bf16", 1.0, 4),    # the largest tree the API takes
 ])
 def test_tree_sample_parity(B, N, V, dtype, T, mc):
     say("tree sample", B, N, V, dtype, T, mc)
