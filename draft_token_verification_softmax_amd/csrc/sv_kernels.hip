@@ -550,16 +550,6 @@ DEV double block_sum(double v, double* red) {
   __syncthreads();
   return t;
 }
-DEV float block_max(float v, float* red) {
-  v = wave_max(v);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  float t = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  __syncthreads();
-  return t;
-}
 
 // Block-wide integer reductions by shuffles (one LDS slot per wave); every
 // thread gets the result.  Many lanes updating one LDS word with atomics
@@ -569,9 +559,6 @@ template <typename I> DEV I wave_min_t(I v) {
 }
 template <typename I> DEV I wave_max_t(I v) {
   return wave_all(v, std::numeric_limits<I>::lowest(), [](I a, I b) { return b > a ? b : a; });
-}
-DEV int wave_sum_i(int v) {
-  return wave_all(v, 0, [](int a, int b) { return a + b; });
 }
 // (min a, max b) over the block in one pass
 template <typename I>
@@ -592,16 +579,6 @@ DEV void block_minmax(I& a, I& b, I* red) {
 DEV int block_max_i(int v, int* red) {
   int lo = INT_MAX;
   block_minmax(lo, v, red);
-  return v;
-}
-DEV int block_sum_i(int v, int* red) {
-  v = wave_sum_i(v);
-  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  __syncthreads();
-  if (lane == 0) red[w] = v;
-  __syncthreads();
-  v = (red[0] + red[1]) + (red[2] + red[3]);
-  __syncthreads();
   return v;
 }
 // Wave-aggregated append: lanes with `take` get consecutive slots of a
@@ -2639,16 +2616,6 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
 // final draw is the plain-sampling draw over max(0, p' - c q') at the final
 // node.
 
-// F of pass m (0-based) at node u: the pass's segment sums in a fixed order
-// (lane l adds segments l, l + 64, ...; then the wave's fixed-order sum).
-// Call from all 64 lanes of one wave.
-DEV double tree_F(const Params& p, int b, int m, int u) {
-  const double* src = p.tpart + (((size_t)b * kTreePasses + m) * p.k + u) * p.S2;
-  double t = 0.0;
-  for (int s = threadIdx.x & 63; s < p.S2; s += 64) t += src[s];
-  return wave_sum(t);
-}
-
 // Views of node u's target row (sv[0], sv[1]) and draft row (sv[2], sv[3]):
 // -M * cs and 1 / Z from the row partials; sbad[0..1] their bad flags.
 // Every thread calls it; the results are in LDS after the call.  (Four
@@ -2749,9 +2716,11 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
                               p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o + 1] = 1.0 / Z;
                             }
                           });
-    // states after m rejections (one wave per node): F of the earlier passes
-    // summed as tree_F sums them, every pass's loads issued together
-    // (unconditionally: a pass not yet run reads pass 0's slots, unused)
+    // states after m rejections (one wave per node): F of each earlier pass
+    // j at u is its segment sums in a fixed order (lane l adds segments l,
+    // l + 64, ...; then the wave's fixed-order sum), every pass's loads
+    // issued together (unconditionally: a pass not yet run reads pass 0's
+    // slots, unused)
     if (w < nbl) {
       const int u = lst[l0 + w];
       double f[kTreePasses - 1];
@@ -2835,8 +2804,8 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
   // the logits the tests read (child c's token in its parent's two rows),
   // the views of every node with children (written by pass 0) and, for the
   // first kTreePasses rejections at a node, F from the passes' segment
-  // masses (summed as tree_F sums them, so the bits are the same): all
-  // issued before the walk needs any of them
+  // masses (summed in the order the passes use, so the bits are the same):
+  // all issued before the walk needs any of them
   for (int i = tid; i < N; i += kBlock) {
     const int x = tok[i], q = par[i];
     float a = 0.f, d = 0.f;
