@@ -94,14 +94,18 @@ def test_topk_at_least_vocab_is_off():
     assert np.array_equal(a["resid_probs"], b["resid_probs"])
 
 
-@pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (5, 1.0), (0, 0.6)])
-def test_identical_rows_accept_everything(top_k, top_p):
-    say("q == p", top_k, top_p)
+@pytest.mark.parametrize("top_k,top_p,max_batch", [(0, 1.0, None), (5, 1.0, None), (0, 0.6, None),
+                                                   (0, 0.6, 4096)])
+def test_identical_rows_accept_everything(top_k, top_p, max_batch):
+    """Every draft accepted: the bonus draw from the last target row (with a
+    context sized for a large batch, the nucleus residual masses come from
+    the queue of kept entries, here with no draft row)."""
+    say("q == p", top_k, top_p, max_batch)
     inp = wl.chain_inputs(2, seed=13, B=16, V=2000, k=4, dtype="bf16")
     inp["draft"] = inp["target"][:, :4].copy()
     inp["top_k"], inp["top_p"] = top_k, top_p
     x = draw_drafts(inp)
-    g = run_chain(inp, x, SV_MODE_SAMPLE)
+    g = run_chain(inp, x, SV_MODE_SAMPLE, max_batch=max_batch)
     assert np.all(g["accepted_len"] == 4)
     orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(16)))
     compare_chain(g, orc, range(16), "q == p")
