@@ -164,6 +164,21 @@ def test_sample_topp_large_context(B, V, k, top_p, dtype):
     compare_chain(gpu, orc, range(B), f"top-p {top_p} V={V} {dtype} large context")
 
 
+@pytest.mark.parametrize("T", [0.05, 4.0])
+@pytest.mark.parametrize("top_k,top_p,dtype", [(0, 1.0, "bf16"), (20, 1.0, "f32"), (0, 0.9, "f32"),
+                                               (0, 0.9, "bf16")])
+def test_sample_extreme_temperature(T, top_k, top_p, dtype):
+    """Near one-hot (T = 0.05) and flat (T = 4) adjusted distributions: the
+    nucleus of a flat row holds thousands of entries around its cut."""
+    say("sample T", T, top_k, top_p, dtype)
+    inp = wl.chain_inputs(2, seed=71 + int(T * 100), B=16, V=6000, k=3, dtype=dtype)
+    inp["T"], inp["top_k"], inp["top_p"] = T, top_k, top_p
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(16)))
+    compare_chain(gpu, orc, range(16), f"T={T} top-k {top_k} top-p {top_p} {dtype}")
+
+
 def test_sample_topp_full_workload5():
     say("sample workload 5 full size")
     inp = wl.chain_inputs(5)          # B=256, k=4, V=152064 fp32, T=0.8, top-p 0.9
