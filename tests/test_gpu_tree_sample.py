@@ -98,6 +98,8 @@ def compare(gpu, orc, which, label):
     (6, 80, 2048, "bf16", 1.0, 1),
     (6, 120, 2048, "f32", 1.0, 2),
     (2, 1024, 1024, "bf16", 1.0, 4),    # the largest tree the API takes
+    (8, 30, 3000, "bf16", 0.05, 4),     # near one-hot rows
+    (8, 30, 3000, "f32", 4.0, 4),       # flat rows: long accepted paths
 ])
 def test_tree_sample_parity(B, N, V, dtype, T, mc):
     say("tree sample", B, N, V, dtype, T, mc)
