@@ -156,14 +156,20 @@ def test_tiny_vocab():
         compare_chain(gpu, orc, range(50), f"V={V}")
 
 
-def test_deterministic_across_calls_and_addresses():
-    say("determinism")
+@pytest.mark.parametrize("top_k,top_p,max_batch", [(0, 1.0, None), (50, 1.0, None), (0, 0.9, None),
+                                                   (0, 0.9, 4096)])
+def test_deterministic_across_calls_and_addresses(top_k, top_p, max_batch):
+    """Bit-identical outputs (resid_probs included) over repeated calls and
+    shifted buffer addresses: plain, top-k and nucleus sampling, the last
+    with a context that takes the nucleus residual through its queues."""
+    say("determinism", top_k, top_p, max_batch)
     inp = wl.chain_inputs(2, seed=31, B=16, V=32000, k=5, dtype="bf16")
+    inp["top_k"], inp["top_p"] = top_k, top_p
     x = draw_drafts(inp)
-    a = run_chain(inp, x, SV_MODE_SAMPLE)
-    b = run_chain(inp, x, SV_MODE_SAMPLE)
+    a = run_chain(inp, x, SV_MODE_SAMPLE, max_batch=max_batch)
+    b = run_chain(inp, x, SV_MODE_SAMPLE, max_batch=max_batch)
     pad = torch.empty(12345, dtype=torch.uint8, device="cuda")   # shift the next allocations
-    c = run_chain(inp, x, SV_MODE_SAMPLE)
+    c = run_chain(inp, x, SV_MODE_SAMPLE, max_batch=max_batch)
     del pad
     for key in ("accepted_len", "out_tokens", "seq_status", "resid_probs"):
         assert np.array_equal(a[key], b[key]) and np.array_equal(a[key], c[key]), key
