@@ -135,6 +135,7 @@ def test_topk_and_topp_together():
     (8, 1032, 3, 0.9, "f32"),
     (8, 4104, 3, 0.8, "f32"),
     (8, 6144, 3, 0.95, "f32"),
+    (8, 1028, 3, 0.9, "f32"),           # 16-byte rows, a half group at the end: element path
 ])
 def test_sample_topp(B, V, k, top_p, dtype):
     say("sample top-p", B, V, k, top_p, dtype)
