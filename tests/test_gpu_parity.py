@@ -180,6 +180,19 @@ def test_sample_extreme_temperature(T, top_k, top_p, dtype):
     compare_chain(gpu, orc, range(16), f"T={T} top-k {top_k} top-p {top_p} {dtype}")
 
 
+@pytest.mark.parametrize("B,V,dtype", [(128, 65536, "bf16"), (160, 131072, "f32")])
+def test_sample_plain_multi_round_tiles(B, V, dtype):
+    """Batches large enough that the float32 sum pass takes tiles of several
+    rounds of loads (two, then four), checked on a sample of sequences."""
+    say("sample plain, multi-round tiles", B, V, dtype)
+    inp = wl.chain_inputs(2, seed=5 + B, B=B, V=V, k=4, dtype=dtype)
+    check = list(range(0, B, 9))
+    x = draw_drafts(inp, check=set(check))
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, check)
+    compare_chain(gpu, orc, check, f"plain B={B} V={V} {dtype}")
+
+
 def test_sample_topp_full_workload5():
     say("sample workload 5 full size")
     inp = wl.chain_inputs(5)          # B=256, k=4, V=152064 fp32, T=0.8, top-p 0.9
