@@ -103,8 +103,10 @@ class HipEvents:
 
 # ------------------------------------------------------------------ measured HBM traffic
 
+# the kernels and the host code that picks their tiling (both decide the
+# streaming kernel's memory traffic)
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_token_verification_softmax_amd", "csrc", f)
-                  for f in ("sv_kernels.hip", "sv_internal.h")]
+                  for f in ("sv_kernels.hip", "sv_internal.h", "sv_api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stream_traffic.md")
 
 
