@@ -15,7 +15,7 @@ constexpr int kMinTile = 8192;        // top-k pass: logits per tile, lower boun
 constexpr int kRound = 4 * sv::kBlock * sv::kVec;   // argmax / sum passes: logits per round of loads
 constexpr int kMinSmall = 2048;       // argmax / sum / filter passes: smallest tile of small problems
 constexpr int kSmallTiles = 256;      // problems with fewer tiles than this take smaller tiles
-constexpr int kStatsRoundsMax = 4;     // float32 sum pass: most rounds of loads per tile
+constexpr int kStatsRoundsMax = 4;     // float32 sum / argmax passes: most rounds of loads per tile
 constexpr size_t kKeepBytes = 32u << 20;   // residual weights kept for the draw up to this size
 
 struct Plan {
@@ -281,16 +281,19 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   // aligned rows of whole groups; other shapes take the exact per-tile pass
   int tile_mode = pl.tile_mode;
   const long rows = (long)batch * (pl.rows_t + pl.rows_d);
-  // float32 row sums of large problems: tiles of 4 (or 2) rounds of loads,
-  // as long as that leaves two resident waves of workgroups; each tile's
-  // fixed work (the float64 rescale and wave sums, the partial) then spreads
-  // over more logits (workload 6: 55.0 -> 48.8 -> 45.5 us for 1, 2, 4
-  // rounds; the 11 MB of workload 2 are faster with one).  The float64 sums
-  // of nucleus rows are bound by their exponentials and stay at one round.
+  // float32 row sums and argmax of large problems: tiles of 4 (or 2) rounds
+  // of loads, as long as that still fills three quarters of the resident
+  // workgroup slots.  Each tile's fixed work (the float64 rescale and wave
+  // sums, the partials) spreads over more logits, and the kernels after the
+  // pass combine four times fewer partials per row (workload 6: pass 55.0 ->
+  // 48.8 -> 45.5 us for 1, 2, 4 rounds; workload 4: pass 21.0 -> 21.1 us,
+  // tree_final 7.6 -> 6.0 us; the 11 MB of workload 2 are faster with one).
+  // The float64 sums of nucleus rows are bound by their exponentials and
+  // stay at one round.
   int rounds = 1;
-  if (tile_mode == sv::kModeStats32) {
+  if (tile_mode == sv::kModeStats32 || tile_mode == sv::kModeArgmax) {
     for (int r = kStatsRoundsMax; r > 1; r >>= 1) {
-      if (rows * ((c->vocab + (long)r * kRound - 1) / ((long)r * kRound)) >= 2L * ctx->grid) {
+      if (4L * rows * ((c->vocab + (long)r * kRound - 1) / ((long)r * kRound)) >= 3L * ctx->grid) {
         rounds = r;
         break;
       }
