@@ -52,6 +52,22 @@ def test_config_struct_layout():
     assert svm.specverify_workspace_bytes(bad) == 0
 
 
+def test_workspace_keeps_residual_weights_up_to_32_mib():
+    """Small sampling contexts keep the float64 residual weights of every
+    2048-logit segment for the draw; past 32 MiB of them the draw recomputes
+    its segment instead, and the workspace drops by that much."""
+    def ws(max_batch):
+        return svm.specverify_workspace_bytes(make_config(SV_MODE_SAMPLE, "bf16", max_batch, 5, 32000, 1.0))
+    per_seq = math.ceil(32000 / 2048) * 2048 * 8      # kept weights of one sequence
+    assert 128 * per_seq == 32 << 20
+    w127, w128, w129 = ws(127), ws(128), ws(129)
+    assert w128 - w127 > per_seq                      # one more sequence, weights included
+    assert w128 - w129 > 127 * per_seq                # 128 sequences' weights gone at 129
+    greedy = [svm.specverify_workspace_bytes(make_config(SV_MODE_GREEDY, "bf16", b, 5, 32000, 1.0))
+              for b in (1, 64, 128, 129, 4096)]
+    assert all(x < y for x, y in zip(greedy, greedy[1:]))
+
+
 def test_status_strings():
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert svm.specverify_status_string(st).startswith("SV_")
