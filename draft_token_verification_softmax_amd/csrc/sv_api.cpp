@@ -203,13 +203,22 @@ int specverify_create(const sv_config* cfg, int device, specverify_ctx** out) {
   ctx->device = device;
   const Layout L = layout(cfg, ctx->plan);
   ctx->ws_bytes = L.total;
-  if (hipSetDevice(device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
   ctx->L = L;
+  // the caller's current device is restored on every return path
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
+  if (cur != device && hipSetDevice(device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
+  int rc2 = SV_OK;
   hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, device) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
-  const int per_cu = sv::stream_blocks_per_cu(ctx->plan.tile_mode, cfg->dtype == SV_DTYPE_BF16);
-  ctx->grid = prop.multiProcessorCount * (per_cu > 0 ? per_cu : 1);
-  if (hipMalloc(&ctx->ws, L.total) != hipSuccess) { free(ctx); return SV_ERR_HIP; }
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) {
+    rc2 = SV_ERR_HIP;
+  } else {
+    const int per_cu = sv::stream_blocks_per_cu(ctx->plan.tile_mode, cfg->dtype == SV_DTYPE_BF16);
+    ctx->grid = prop.multiProcessorCount * (per_cu > 0 ? per_cu : 1);
+    if (hipMalloc(&ctx->ws, L.total) != hipSuccess) rc2 = SV_ERR_HIP;
+  }
+  if (cur != device) (void)hipSetDevice(cur);
+  if (rc2 != SV_OK) { free(ctx); return rc2; }
   *out = ctx;
   return SV_OK;
 }

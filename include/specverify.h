@@ -123,8 +123,8 @@ typedef struct {
   double top_p;          /* SAMPLE: 1.0 = off, else in (0, 1) */
 } sv_config;
 
-/* Validate cfg, select `device`, allocate the workspace.  On success *out
- * holds a new context.  Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE,
+/* Validate cfg and allocate the workspace on `device`; the calling thread's
+ * current device is the same afterwards.  On success *out holds a new context.  Errors: SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE,
  * SV_ERR_PARAM, SV_ERR_MODE (no HIP call made), SV_ERR_HIP. */
 int specverify_create(const sv_config* cfg, int device, specverify_ctx** out);
 

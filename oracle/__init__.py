@@ -5,7 +5,7 @@ Only tests/, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 """
 from .verify import (  # noqa: F401
     FLAG_BAND, STATUS_BAD_LOGITS, STATUS_BAD_PARENT, STATUS_BAD_TOKEN,
-    bf16_bits_to_f64, draw_from, greedy_chain, inverse_cdf, rank_order,
+    draw_from, greedy_chain, inverse_cdf, rank_order,
     row_is_valid, run_chain_batch, run_tree_batch, sample_chain, transform_row,
     tree_greedy,
 )

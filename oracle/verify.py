@@ -49,14 +49,8 @@ FLAG_BAND = 1e-6        # a decision whose uniform lies this close to its thresh
 
 
 # --------------------------------------------------------------------------
-# helpers: exact conversions
+# helpers
 # --------------------------------------------------------------------------
-
-def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
-    """bf16 bit patterns (uint16) -> float64, exactly (bf16 is the top half of fp32)."""
-    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
-    return b.view(np.float32).astype(np.float64)
-
 
 def row_is_valid(z: np.ndarray) -> bool:
     """Reading R16: a row with NaN or +inf, or with no finite maximum, is invalid."""

@@ -395,6 +395,44 @@ def pin_flags(ov):
     assert far["n"] == 1 and near["n"] == 0
 
 
+def pin_flag_rules(ov):
+    """Reading R14's other flag rules, on hand-worked exact binary weights
+    (tests/golden/flags.json): the inverse-CDF margin in normalised units
+    (and the flag it raises, in a residual whose mass is 1/2, not 1), and the
+    nucleus cut margins on both sides of top_p, which flag a sequence only
+    when the marginal token is tested or drawn."""
+    g = _load("flags.json")
+    ic = g["inverse_cdf"]
+    w = np.array(ic["weights"])
+    for c in ic["cases"]:
+        y, m = ov.inverse_cdf(w, c["u"])
+        assert y == c["y"] and abs(m - c["margin"]) < 1e-12, ("inverse_cdf", c, y, m)
+    cd = g["chain_draw"]
+    for c in cd["cases"]:
+        o = ov.sample_chain(_rows(cd["target"]), _rows(cd["draft"]), cd["x"], cd["u"], c["ur"], 1.0)
+        assert (o["n"], o["tokens"]) == (c["n"], c["tokens"]), ("chain_draw", c, o["n"], o["tokens"])
+        assert abs(o["cdf_margin"] - c["cdf_margin"]) < 1e-12, ("chain_draw margin", c, o["cdf_margin"])
+        assert o["flagged"] == c["flagged"], ("chain_draw flag", c)
+    nc = g["nucleus_cut"]
+    for c in nc["cases"]:
+        _, cut = ov.transform_row(np.array(nc["logits"]), 1.0, 0, c["top_p"], want_cut=True)
+        for key in ("last_kept", "next_token", "size"):
+            assert cut[key] == c[key], ("nucleus_cut", key, c, cut)
+        for key in ("margin_lo", "margin_hi"):
+            assert abs(cut[key] - c[key]) < 1e-12, ("nucleus_cut", key, c, cut)
+    ch = g["nucleus_chain"]
+    rows = np.array([ch["logits"], ch["logits"]])
+    for c in ch["cases"]:
+        o = ov.sample_chain(rows, rows[:1], c["x"], c["u"], c["ur"], 1.0, 0, c["top_p"])
+        assert (o["n"], o["tokens"]) == (c["n"], c["tokens"]), ("nucleus_chain", c, o["n"], o["tokens"])
+        assert o["flagged"] == c["flagged"], ("nucleus_chain flag", c)
+    r1 = g["ratio_one"]
+    row = np.array(r1["row"])
+    o = ov.sample_chain(np.array([row, row]), row[None, :], [1], [r1["u"]], r1["chain"]["ur"], 1.0)
+    c = r1["chain"]
+    assert (o["n"], o["tokens"], o["flagged"]) == (c["n"], c["tokens"], c["flagged"]), ("ratio one", o)
+
+
 # ---------------------------------------------------------------- calculator
 
 def pin_calculator(calc):
@@ -431,7 +469,7 @@ ALL_ORACLE_PINS = [
     pin_greedy_golden, pin_greedy_invariants, pin_tree_golden, pin_tree_path_equals_chain,
     pin_tree_bruteforce, pin_transform_softmax, pin_transform_topk, pin_transform_golden,
     pin_topp_minimal, pin_inverse_cdf_golden, pin_enumeration, pin_special_cases,
-    pin_residual_properties, pin_flags,
+    pin_residual_properties, pin_flags, pin_flag_rules,
 ]
 
 
@@ -551,6 +589,27 @@ def pin_tree_sample_golden(ts):
         want = (c["n"], c["out_tokens"], c["out_nodes"], c["status"])
         assert got == want, (c["name"], got, want)
         assert np.allclose(o["resid"], c["resid"], rtol=0, atol=1e-12), (c["name"], o["resid"])
+
+
+def pin_tree_sample_flags(ts):
+    """Reading R14 in a sampled tree (tests/golden/flags.json): a child's
+    uniform near its accept threshold, and the draw near a boundary of the
+    running residual (after a rejection) or of a leaf's target row (after an
+    acceptance), flag the tree; the same walks with the uniforms moved off
+    the thresholds do not."""
+    g = _load("flags.json")["tree"]
+    for c in g["cases"]:
+        o = ts.tree_sample(_rows(g["target"]), _rows(g["draft"]), np.array(g["parents"]),
+                           np.array(g["tokens"]), np.array([0.0, c["u1"]]), c["ur"], 1.0)
+        assert (o["n"], o["tokens"]) == (c["n"], c["tokens"]), ("tree flags", c, o["n"], o["tokens"])
+        assert o["flagged"] == c["flagged"], ("tree flags", c)
+    r1 = _load("flags.json")["ratio_one"]
+    row = np.array(r1["row"])
+    leaf = np.zeros(4)
+    o = ts.tree_sample(np.array([row, leaf]), np.array([row, leaf]), np.array([-1, 0]), np.array([0, 1]),
+                       np.array([0.0, r1["u"]]), r1["tree"]["ur"], 1.0)
+    c = r1["tree"]
+    assert (o["n"], o["tokens"], o["flagged"]) == (c["n"], c["tokens"], c["flagged"]), ("tree ratio one", o)
 
 
 def pin_tree_sample_is_chain(ts, ov, trials=150, seed=11):

@@ -64,3 +64,7 @@ def test_tree_sample_chisq():
 
 def test_tree_sample_status():
     pins.pin_tree_sample_status(ts)
+
+
+def test_tree_sample_flags():
+    pins.pin_tree_sample_flags(ts)

@@ -45,6 +45,35 @@ MUTANTS = [
     ("tree compares with its own row", "acc[i] = acc[par] and t == g[par]", "acc[i] = acc[par] and t == g[i]"),
     ("tree depth ties go to the larger index", "if acc[i] and depth[i] > depth[best]:",
      "if acc[i] and depth[i] >= depth[best]:"),
+    ("inverse-CDF margin not normalised",
+     "margin = min(np.float64(uniform) - lo / S, C[y] / S - np.float64(uniform))",
+     "margin = min(np.float64(uniform) - lo, C[y] - np.float64(uniform))"),
+    ("inverse-CDF margin misses the upper edge",
+     "margin = min(np.float64(uniform) - lo / S, C[y] / S - np.float64(uniform))",
+     "margin = np.float64(uniform) - lo / S"),
+    ("draw margin left out of the flag",
+     'flagged = any(m < FLAG_BAND for m in out["accept_margins"]) or cdf_margin < FLAG_BAND',
+     'flagged = any(m < FLAG_BAND for m in out["accept_margins"])'),
+    ("accept margins left out of the flag",
+     'flagged = any(m < FLAG_BAND for m in out["accept_margins"]) or cdf_margin < FLAG_BAND',
+     'flagged = cdf_margin < FLAG_BAND'),
+    ("upper cut margin dropped",
+     '"margin_hi": float(csum[R] - np.float64(top_p)) if R + 1 < V else np.inf,',
+     '"margin_hi": np.inf,'),
+    ("lower cut margin measured from the wrong rank",
+     '"margin_lo": float(np.float64(top_p) - before[R]),',
+     '"margin_lo": float(np.float64(top_p) - before[R - 1]),'),
+    ("cut flag ignores whether the marginal token is decided",
+     '(c["margin_lo"] < FLAG_BAND and c["last_kept"] in decided)',
+     '(c["margin_lo"] < FLAG_BAND)'),
+    ("cut flag checks the wrong token",
+     '(c["margin_hi"] < FLAG_BAND and c["next_token"] in decided)',
+     '(c["margin_hi"] < FLAG_BAND and c["last_kept"] in decided)'),
+    ("accept margin kept for ratios of 1 and above",
+     '            if ratio < 1.0:\n                out["accept_margins"].append(abs(u - ratio))',
+     '            out["accept_margins"].append(abs(u - ratio))'),
+    ("drawn token not counted as decided",
+     "if 0 <= int(t) < V) | {y}", "if 0 <= int(t) < V)"),
     ("tree correction from the parent", "path_tokens = [int(tokens[i]) for i in path[1:]] + [g[best]]",
      "path_tokens = [int(tokens[i]) for i in path[1:]] + [g[path[-2] if len(path) > 1 else best]]"),
 ]
@@ -62,7 +91,7 @@ CALC_MUTANTS = [
 def _quick_pins():
     return [
         pins.pin_greedy_golden, pins.pin_tree_golden, pins.pin_transform_golden,
-        pins.pin_inverse_cdf_golden, pins.pin_flags, pins.pin_greedy_invariants,
+        pins.pin_inverse_cdf_golden, pins.pin_flags, pins.pin_flag_rules, pins.pin_greedy_invariants,
         pins.pin_tree_path_equals_chain, pins.pin_tree_bruteforce, pins.pin_transform_softmax,
         pins.pin_transform_topk, pins.pin_topp_minimal, pins.pin_special_cases,
         pins.pin_residual_properties,
@@ -157,6 +186,15 @@ TS_MUTANTS = [
      "        all(row_is_valid(D[u]) for u in range(N))"),
     ("uniform of the parent used", "                    u = np.float64(uniforms[c])",
      "                    u = np.float64(uniforms[cur])"),
+    ("tree draw margin left out of the flag",
+     'flagged = any(m < FLAG_BAND for m in out["accept_margins"]) or cdf_margin < FLAG_BAND',
+     'flagged = any(m < FLAG_BAND for m in out["accept_margins"])'),
+    ("tree accept margins left out of the flag",
+     'flagged = any(m < FLAG_BAND for m in out["accept_margins"]) or cdf_margin < FLAG_BAND',
+     'flagged = cdf_margin < FLAG_BAND'),
+    ("tree accept margin kept for ratios above 1",
+     "                        if ratio < 1.0:\n                            out[\"accept_margins\"].append(abs(u - ratio))",
+     "                        out[\"accept_margins\"].append(abs(u - ratio))"),
 ]
 
 
@@ -171,7 +209,8 @@ def _load_ts_mutant(old, new, name):
 @pytest.mark.parametrize("name,old,new", TS_MUTANTS, ids=[m[0] for m in TS_MUTANTS])
 def test_tree_sample_mutant_is_caught(name, old, new):
     mod = _load_ts_mutant(old, new, name)
-    for pin in (pins.pin_tree_sample_golden, lambda m: pins.pin_tree_sample_is_chain(m, real),
+    for pin in (pins.pin_tree_sample_golden, pins.pin_tree_sample_flags,
+                lambda m: pins.pin_tree_sample_is_chain(m, real),
                 pins.pin_tree_sample_status, lambda m: pins.pin_tree_sample_enumeration(m, real),
                 lambda m: pins.pin_tree_sample_chisq(m, real, trials=3000)):
         try:
