@@ -1,23 +1,35 @@
 #!/usr/bin/env python3
 """Benchmark of the verification step on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config C] [--also 2,3,4] [--no-cpu]
 
-One step = one specverify_run over one batch of the workload (every logit
-read once by the streaming kernel, then acceptance, residual / bonus draw and
-outputs).  Inputs are seeded synthetic logits with the workloads' shapes,
-already resident in HBM; calls rotate over identical copies at distinct
-addresses totalling >= 1 GB so that every call reads cold HBM rather than the
-256 MB Infinity Cache.  Prints one JSON line.
+One step = one specverify_run over one batch of the workload: every logit
+read once by the streaming kernel, then the acceptance step, the residual or
+bonus draw and the outputs.  Inputs are seeded synthetic logits with the
+workloads' shapes, already resident in HBM; calls rotate over identical
+copies at distinct addresses totalling >= 1 GB, so every call reads cold HBM
+rather than the 256 MB Infinity Cache.  Prints one JSON line.
 
-Metric: verified logit rows per second (target rows: B*(k+1) per chain call,
-B*N per tree call) and, in "roofline", the streaming kernel's achieved HBM
-bandwidth = algorithmic bytes per launch / its average duration, timed with
-HIP events recorded around that kernel on its own stream.
+The default workload is the largest one: 256 sequences, k = 4, V = 152064
+float32 logits, temperature 0.8, nucleus 0.9 (1.40 GB of logits per call).
+
+Metric: verified logit rows per second (target rows: B*(k+1) per chain
+call, B*N per tree call).  "roofline": algorithmic bytes of one call (every
+logit the mode reads, once, plus tokens, uniforms and outputs) / the call's
+time from its first kernel's start to its last kernel's end, both recorded
+by HIP events in the dispatch packets of those kernels on the call's stream;
+the streaming kernel alone is reported beside it.  "traffic" is the HBM
+bytes of every kernel of one call from the committed FETCH_SIZE / WRITE_SIZE
+counters (profiles/traffic.md), while those were taken on the current kernel
+sources.
 
 The draft tokens of a workload are the draft model's own draws from its
 adjusted distribution; here they are synthesised on the device with plain
 torch ops before timing (workload synthesis, not part of the verified path).
+
+Helpers for the committed profiles (no GPU needed):
+    python bench.py --trace-summary <rocprofv3 kernel_trace.csv>
+    python bench.py --pmc-summary <FETCH_SIZE counter_collection.csv> <WRITE_SIZE counter_collection.csv>
 """
 from __future__ import annotations
 
@@ -36,6 +48,8 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 METRIC = "verified logit rows/sec + achieved HBM GB/s (fraction of peak), 1 GPU"
+# kernels launched around a call by the bench itself (not part of the step)
+AUX_KERNELS = ("k_accept_stats", "k_tree_mask", "k_tree_commit")
 
 
 def log(*a):
@@ -80,6 +94,7 @@ class HipEvents:
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self, n):
         evs = []
@@ -89,6 +104,10 @@ class HipEvents:
                 raise RuntimeError("hipEventCreate failed")
             evs.append(e.value)
         return evs
+
+    def record(self, ev, stream):
+        if self.hip.hipEventRecord(ctypes.c_void_p(ev), ctypes.c_void_p(stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def elapsed_ms(self, a, b):
         ms = ctypes.c_float()
@@ -103,11 +122,11 @@ class HipEvents:
 
 # ------------------------------------------------------------------ measured HBM traffic
 
-# the kernels and the host code that picks their tiling (both decide the
-# streaming kernel's memory traffic)
+# the kernels and the host code that picks their tiling and launches (all of
+# them decide a call's memory traffic)
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_token_verification_softmax_amd", "csrc", f)
                   for f in ("sv_kernels.hip", "sv_internal.h", "sv_api.cpp")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_stream_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.md")
 
 
 def source_code(text: str) -> str:
@@ -147,11 +166,11 @@ def kernel_digest():
 
 
 def measured_traffic(config):
-    """HBM bytes per launch of the streaming kernel for a workload, from the
+    """HBM bytes of one call (every kernel of it) for a workload, from the
     committed FETCH_SIZE / WRITE_SIZE summary, if it was taken on the current
-    kernel sources; else None."""
+    kernel sources; else None.  Returns (call_bytes, stream_bytes)."""
     if not os.path.exists(TRAFFIC_FILE):
-        return None
+        return None, None
     digest = kernel_digest()
     with open(TRAFFIC_FILE) as fh:
         for line in fh:
@@ -159,11 +178,145 @@ def measured_traffic(config):
                 continue
             kv = dict(tok.split("=", 1) for tok in line.split()[1:])
             if kv.get("workload") == str(config) and kv.get("sources") == digest:
-                return int(kv["bytes_per_launch"])
-    return None
+                return int(kv["call_bytes"]), int(kv["stream_bytes"])
+    return None, None
+
+
+# ------------------------------------------------------------------ rocprofv3 summaries
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as fh:
+        return list(csv.DictReader(fh))
+
+
+def _short(name):
+    """Kernel name without the return type and the parameter list."""
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            return name[:i]
+    return name
+
+
+def _calls(rows, key_start, key_end):
+    """Group library dispatches (in dispatch order) into calls: a call starts
+    at a streaming-kernel dispatch and holds the library kernels up to the
+    next one; the bench's own kernels around the step are left out."""
+    rows = [r for r in rows if r["Kernel_Name"].startswith(("k_", "void sv::k_", "sv::k_"))
+            and not any(a in r["Kernel_Name"] for a in AUX_KERNELS)]
+    rows.sort(key=lambda r: int(r.get("Dispatch_Id", r.get("Correlation_Id", 0))))
+    calls, cur = [], None
+    for r in rows:
+        if "k_stream" in r["Kernel_Name"]:
+            cur = []
+            calls.append(cur)
+        if cur is not None:
+            cur.append(r)
+    return calls
+
+
+def trace_summary(path):
+    """Per-kernel durations and per-call spans (first kernel start to last
+    kernel end) from a rocprofv3 --kernel-trace CSV, as markdown."""
+    rows = _read_csv(path)
+    calls = _calls(rows, "Start_Timestamp", "End_Timestamp")
+    per = {}
+    for c in calls:
+        for r in c:
+            per.setdefault(_short(r["Kernel_Name"]), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    spans = np.array([(max(int(r["End_Timestamp"]) for r in c) - min(int(r["Start_Timestamp"]) for r in c)) / 1e3
+                      for c in calls if c])
+    busy = np.array([sum(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in c) / 1e3
+                     for c in calls if c])
+    out = ["| kernel | dispatches | avg us | median us | min us | max us |", "|---|---|---|---|---|---|"]
+    for name, d in sorted(per.items(), key=lambda kv: -np.mean(kv[1])):
+        d = np.array(d)
+        out.append(f"| `{name}` | {len(d)} | {d.mean():.2f} | {np.median(d):.2f} | {d.min():.2f} | {d.max():.2f} |")
+    out.append("")
+    out.append(f"calls: {len(spans)}; call span (first kernel start to last kernel end): mean {spans.mean():.2f} us, "
+               f"median {np.median(spans):.2f} us, p10 {np.percentile(spans, 10):.2f}, p90 {np.percentile(spans, 90):.2f}; "
+               f"sum of the call's kernel durations: mean {busy.mean():.2f} us")
+    print("\n".join(out))
+
+
+def pmc_summary(fetch_csv, write_csv, fetch_scale=2.0, write_scale=1.0):
+    """Per-kernel FETCH_SIZE / WRITE_SIZE (KiB per dispatch, medians) and the
+    HBM bytes of one call (sum over its kernels), from two rocprofv3 --pmc
+    runs; bytes = fetch_scale * FETCH_SIZE + write_scale * WRITE_SIZE (the
+    factors a copy of known size gives)."""
+    res = {}
+    for path, cname in ((fetch_csv, "FETCH_SIZE"), (write_csv, "WRITE_SIZE")):
+        rows = [r for r in _read_csv(path) if r.get("Counter_Name", cname) == cname]
+        calls = _calls(rows, "Start_Timestamp", "End_Timestamp")
+        per = {}
+        tot = []
+        for c in calls:
+            s = 0.0
+            for r in c:
+                v = float(r["Counter_Value"])
+                per.setdefault(_short(r["Kernel_Name"]), []).append(v)
+                s += v
+            tot.append(s)
+        res[cname] = ({k: float(np.median(v)) for k, v in per.items()}, float(np.median(tot)) if tot else 0.0,
+                      len(calls))
+    f_per, f_tot, nf = res["FETCH_SIZE"]
+    w_per, w_tot, nw = res["WRITE_SIZE"]
+    out = ["| kernel | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes per dispatch |", "|---|---|---|---|"]
+    stream_bytes = 0
+    for name in sorted(set(f_per) | set(w_per), key=lambda n: -f_per.get(n, 0.0)):
+        b = int(round(1024 * (fetch_scale * f_per.get(name, 0.0) + write_scale * w_per.get(name, 0.0))))
+        if "k_stream" in name:
+            stream_bytes = b
+        out.append(f"| `{name}` | {f_per.get(name, 0.0):.0f} | {w_per.get(name, 0.0):.0f} | {b} |")
+    call_bytes = int(round(1024 * (fetch_scale * f_tot + write_scale * w_tot)))
+    out.append("")
+    out.append(f"calls: {nf} (FETCH_SIZE run), {nw} (WRITE_SIZE run); one call, median over calls: "
+               f"FETCH_SIZE {f_tot:.0f} KiB, WRITE_SIZE {w_tot:.0f} KiB, HBM bytes {call_bytes}")
+    out.append(f"call_bytes={call_bytes} stream_bytes={stream_bytes}")
+    print("\n".join(out))
+
+
+def copy_summary(fetch_csv, write_csv, nbytes):
+    """Scale factors of FETCH_SIZE and WRITE_SIZE from the copy kernel of
+    ``bench.py --copy-calibrate``: bytes moved / counter bytes."""
+    out = []
+    for path, cname, moved in ((fetch_csv, "FETCH_SIZE", nbytes), (write_csv, "WRITE_SIZE", nbytes)):
+        rows = [r for r in _read_csv(path) if r.get("Counter_Name", cname) == cname
+                and not r["Kernel_Name"].startswith(("k_", "void sv::"))]
+        big = [float(r["Counter_Value"]) for r in rows if float(r["Counter_Value"]) * 1024 > moved / 8]
+        v = float(np.median(big))
+        out.append(f"{cname}: {v:.0f} KiB per copy of {moved} bytes: factor {moved / (v * 1024):.3f}")
+    print("\n".join(out))
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
+
+def cpu_model():
+    try:
+        import subprocess
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
 
 def cpu_baseline(config, budget_s=12.0):
     """The float64 oracle, untuned, on a bounded sample of the same workload,
@@ -171,7 +324,6 @@ def cpu_baseline(config, budget_s=12.0):
     import oracle.verify as ov
     from draft_token_verification_softmax_amd import workloads as wl
     cfg = wl.CONFIGS[config]
-    t0 = time.perf_counter()
     rows = 0
     seqs = 0
     if cfg["kind"] == "tree_sample":
@@ -227,53 +379,24 @@ def cpu_baseline(config, budget_s=12.0):
     return {"value": rows / el, "unit": "rows/s", "cores": 1, "kind": "oracle",
             "sample": f"{seqs} sequences of workload {config} ({rows} target rows, "
                       f"{nbytes / el / 1e9:.4f} GB/s of logits) in {el:.1f} s, one process",
-            "host_cpus": os.cpu_count()}
+            "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
 
 
-# ------------------------------------------------------------------ main
+# ------------------------------------------------------------------ one workload on the GPU
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", type=int, default=2)
-    ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
-                    help="only copy MIB MiB device-to-device three times (scale reference for "
-                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
-    ap.add_argument("--digest", action="store_true", help="print the kernel-source digest and exit")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
-              f"(the verification step shards by batch with no exchange, see DESIGN.md)", file=sys.stderr)
-        sys.exit(2)
-
+def measure(config, steps, warmup, hip, with_extras=True):
+    """Time `steps` calls of workload `config` (after `warmup`): wall time
+    of plain back-to-back calls (the metric), then the same calls with the
+    library's call and streaming-kernel events.  Returns a dict."""
     import torch
     import draft_token_verification_softmax_amd as svm
     from draft_token_verification_softmax_amd import workloads as wl
 
-    if args.digest:
-        print(kernel_digest())
-        return
-    if args.copy_calibrate:
-        n = args.copy_calibrate * (1 << 20) // 4
-        src = torch.ones(n, device="cuda:0")
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_per_call": n * 4, "calls": 3}), flush=True)
-        return
-
-    svm.load()
-    cfg = wl.CONFIGS[args.config]
-    torch.cuda.set_device(0)
+    cfg = wl.CONFIGS[config]
     dev = torch.device("cuda:0")
-    log(f"workload {args.config}: generating inputs")
+    log(f"workload {config}: generating inputs")
     if cfg["kind"] == "tree_sample":
-        ti = wl.tree_sample_inputs(wl.DEFAULT_SEED[args.config], B=cfg["B"], N=cfg["N"], V=cfg["V"], dtype=cfg["dtype"],
+        ti = wl.tree_sample_inputs(wl.DEFAULT_SEED[config], B=cfg["B"], N=cfg["N"], V=cfg["V"], dtype=cfg["dtype"],
                                    T=cfg["T"], sd=cfg["sd"], noise=cfg["noise"],
                                    max_depth=cfg["max_depth"], max_children=cfg["max_children"])
         B, N, V, dtype, T = ti["B"], ti["N"], ti["V"], ti["dtype"], ti["T"]
@@ -291,8 +414,9 @@ def main():
         workload = f"tree sampling verification, B={B}, N={N} nodes, V={V}, {dtype} logits, T={T}"
         extra = dict(B=B, N=N, V=V, logits_dtype=dtype, T=T, depth_max=cfg["max_depth"],
                      children_max=cfg["max_children"])
+        arith = "f64"
     elif cfg["kind"] == "tree":
-        tr = wl.tree_inputs(args.config)
+        tr = wl.tree_inputs(config)
         B, N, V, dtype = tr["B"], tr["N"], tr["V"], tr["dtype"]
         tgt = logits_to_device(tr["target"], dtype)
         g = tgt.float().argmax(dim=-1).cpu().numpy()
@@ -303,8 +427,9 @@ def main():
         T, top_k, top_p = 1.0, 0, 1.0
         workload = f"tree greedy verification, B={B}, N={N} nodes, V={V}, {dtype} logits"
         extra = dict(B=B, N=N, V=V, logits_dtype=dtype, depth_max=cfg["max_depth"], children_max=cfg["max_children"])
+        arith = "f32"
     else:
-        inp = wl.chain_inputs(args.config)
+        inp = wl.chain_inputs(config)
         B, k, V, dtype = inp["B"], inp["k"], inp["V"], inp["dtype"]
         T, top_k, top_p = inp["T"], inp["top_k"], inp["top_p"]
         tgt = logits_to_device(inp["target"], dtype)
@@ -316,6 +441,7 @@ def main():
         filt = f"top-k {top_k}" if top_k else (f"top-p {top_p}" if top_p < 1 else "no filter")
         workload = f"chain sampling verification, B={B}, k={k}, V={V}, {dtype} logits, T={T}, {filt}"
         extra = dict(B=B, k=k, V=V, logits_dtype=dtype, T=T, top_k=top_k, top_p=top_p)
+        arith = "f64"
 
     es = 2 if dtype == "bf16" else 4
     logit_bytes = B * (rows_t + rows_d) * V * es
@@ -342,92 +468,176 @@ def main():
         svm.specverify_run(sv.ctx, B, c["target"], c.get("draft"), c["tokens"], c.get("parents"),
                            c.get("u"), c.get("ur"), acc, out_tok, out_nodes, None, status, stream)
 
-    hip = HipEvents()
-    hip.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
     # timed region 1 (the metric): K plain calls, nothing else on the stream
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step(i)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # timed region 2 (the roofline): the same K calls with HIP events recorded
-    # on the call's stream around the streaming kernel (by the library) and
-    # around the whole call
-    evs = hip.create(4 * args.steps)
+    # timed region 2 (the roofline): the same K calls, the library recording
+    # per call the streaming kernel's start and end and the last kernel's end
+    evs = hip.create(3 * steps)
     torch.cuda.synchronize()
-    for i in range(args.steps):
-        e = evs[4 * i: 4 * i + 4]
-        svm.specverify_profile_events(sv.ctx, e[1], e[2])
-        hip.hip.hipEventRecord(ctypes.c_void_p(e[0]), ctypes.c_void_p(stream))
+    for i in range(steps):
+        e = evs[3 * i: 3 * i + 3]
+        svm.specverify_profile_events(sv.ctx, e[0], e[1], e[2])
         step(i)
-        hip.hip.hipEventRecord(ctypes.c_void_p(e[3]), ctypes.c_void_p(stream))
     torch.cuda.synchronize()
-    svm.specverify_profile_events(sv.ctx, None, None)
-    kms = np.array([hip.elapsed_ms(evs[4 * i + 1], evs[4 * i + 2]) for i in range(args.steps)])
-    cms = np.array([hip.elapsed_ms(evs[4 * i], evs[4 * i + 3]) for i in range(args.steps)])
+    svm.specverify_profile_events(sv.ctx, None, None, None)
+    kms = np.array([hip.elapsed_ms(evs[3 * i], evs[3 * i + 1]) for i in range(steps)])
+    cms = np.array([hip.elapsed_ms(evs[3 * i], evs[3 * i + 2]) for i in range(steps)])
     hip.destroy(evs)
-    kern_ms = float(np.mean(kms))
-    call_ms = float(np.mean(cms))
-    ms_per_step = wall * 1e3 / args.steps
-    rows_per_call = B * rows_t
-    value = rows_per_call * args.steps / wall
-    achieved = logit_bytes / (kern_ms * 1e-3) / 1e9
-    log(f"step {ms_per_step * 1e3:.2f} us (wall), call {call_ms * 1e3:.2f} us (events), streaming kernel "
-        f"{kern_ms * 1e3:.2f} us (p10 {np.percentile(kms, 10) * 1e3:.2f}, p90 {np.percentile(kms, 90) * 1e3:.2f}), "
-        f"{achieved:.1f} GB/s")
+    kern_us = float(np.mean(kms)) * 1e3
+    call_us = float(np.mean(cms)) * 1e3
+    step_us = wall * 1e6 / steps
+    achieved = alg_bytes / (call_us * 1e-6) / 1e9
+    stream_ach = logit_bytes / (kern_us * 1e-6) / 1e9
+    call_traffic, stream_traffic = measured_traffic(config)
+    log(f"workload {config}: step {step_us:.2f} us (wall), call {call_us:.2f} us (first kernel start to last "
+        f"kernel end; p10 {np.percentile(cms, 10) * 1e3:.2f}, p90 {np.percentile(cms, 90) * 1e3:.2f}), "
+        f"{achieved:.1f} GB/s = {achieved / PEAK_HBM_GBS:.3f} of peak; streaming kernel {kern_us:.2f} us, "
+        f"{stream_ach:.1f} GB/s")
+    res = dict(config=config, workload=workload, extra=extra, arith=arith, B=B, rows_per_call=B * rows_t,
+               logit_bytes=logit_bytes, alg_bytes=alg_bytes, ncopies=ncopies, wall=wall, step_us=step_us,
+               call_us=call_us, call_us_p10=float(np.percentile(cms, 10)) * 1e3,
+               call_us_p90=float(np.percentile(cms, 90)) * 1e3, kern_us=kern_us, achieved=achieved,
+               stream_achieved=stream_ach, call_traffic=call_traffic, stream_traffic=stream_traffic)
+
+    if with_extras:
+        # the kernels around the step, on this workload's outputs: acceptance
+        # statistics (every mode); tree attention mask and commit map (tree)
+        extras = {}
+
+        def time_launches(fn, reps=100):
+            e = hip.create(2)
+            fn()
+            torch.cuda.synchronize()
+            hip.record(e[0], stream)
+            for _ in range(reps):
+                fn()
+            hip.record(e[1], stream)
+            torch.cuda.synchronize()
+            us = hip.elapsed_ms(e[0], e[1]) * 1e3 / reps
+            hip.destroy(e)
+            return us
+
+        kk = k if not tree else cfg["max_depth"]
+        stats_out = torch.empty(svm.SV_STATS_LEN, dtype=torch.float64, device=dev)
+        extras["accept_stats_us"] = time_launches(
+            lambda: svm.specverify_accept_stats(acc, status, B, kk, 0.1, stats_out, stream))
+        st = stats_out.cpu().numpy()
+        extras["acceptance"] = float(st[svm.SV_STATS_ACCEPTANCE])
+        extras["mal"] = float(st[svm.SV_STATS_MAL])
+        extras["alpha"] = float(st[svm.SV_STATS_ALPHA])
+        if tree:
+            mask = torch.empty(B, N, (N + 31) // 32, dtype=torch.int32, device=dev)
+            depth = torch.empty(B, N, dtype=torch.int32, device=dev)
+            pos = torch.empty(B, N, dtype=torch.int32, device=dev)
+            extras["tree_mask_us"] = time_launches(
+                lambda: svm.specverify_tree_mask(inputs["parents"], B, N, mask, depth, stream))
+            extras["tree_commit_us"] = time_launches(
+                lambda: svm.specverify_tree_commit(out_nodes, acc, B, N, pos, stream))
+        extras["note"] = ("mean per launch by HIP events over 100 back-to-back launches on the call's "
+                          "stream; acceptance statistics of the last timed call (draft cost c = 0.1)")
+        res["extras"] = extras
+    sv.close()
+    del copies, inputs
+    torch.cuda.empty_cache()
+    return res
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=5)
+    ap.add_argument("--also", default="2,3,4",
+                    help="other workloads whose call-level roofline goes into extras (comma list, '' for none)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
+                    help="only copy MIB MiB device-to-device three times (scale reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--digest", action="store_true", help="print the kernel-source digest and exit")
+    ap.add_argument("--trace-summary", metavar="CSV", help="summarise a rocprofv3 kernel trace and exit")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarise two rocprofv3 counter runs of the bench and exit")
+    ap.add_argument("--copy-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BYTES"),
+                    help="counter scale factors from two --copy-calibrate counter runs and exit")
+    args = ap.parse_args()
+    if args.digest:
+        print(kernel_digest())
+        return
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(*args.pmc_summary)
+        return
+    if args.copy_summary:
+        copy_summary(args.copy_summary[0], args.copy_summary[1], int(args.copy_summary[2]))
+        return
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported: the verification "
+              f"step shards by batch with no exchange, so N GPUs each run this one-GPU call on B/N "
+              f"sequences", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import draft_token_verification_softmax_amd as svm
+
+    if args.copy_calibrate:
+        n = args.copy_calibrate * (1 << 20) // 4
+        src = torch.ones(n, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_call": n * 4, "calls": 3}), flush=True)
+        return
+
+    svm.load()
+    torch.cuda.set_device(0)
+    hip = HipEvents()
+    m = measure(args.config, args.steps, args.warmup, hip)
+    value = m["rows_per_call"] * args.steps / m["wall"]
     result = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": dict(workload=workload, rows_per_call=rows_per_call,
-                       logit_bytes_per_call=logit_bytes, input_copies=ncopies, **extra),
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBS, "traffic": measured_traffic(args.config),
-                     "kernel": "k_stream (the pass that reads every logit)", "kernel_us": kern_ms * 1e3,
-                     "call_us_events": call_ms * 1e3,
-                     "call_bytes_algorithmic": alg_bytes,
-                     "call_GBps": alg_bytes / (call_ms * 1e-3) / 1e9},
+        "warmup": args.warmup, "ms_per_step": m["step_us"] / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": m["arith"], "data": "synthetic",
+        "config": dict(workload=m["workload"], rows_per_call=m["rows_per_call"],
+                       logit_bytes_per_call=m["logit_bytes"], input_copies=m["ncopies"], **m["extra"]),
+        "roofline": {
+            "bound": "hbm", "achieved": m["achieved"], "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": m["achieved"] / PEAK_HBM_GBS, "traffic": m["call_traffic"],
+            "time": "one call, first kernel start to last kernel end (HIP events in the dispatch packets "
+                    "of the call's first and last kernels), mean over the timed calls",
+            "call_us": m["call_us"], "call_us_p10": m["call_us_p10"], "call_us_p90": m["call_us_p90"],
+            "bytes_algorithmic": m["alg_bytes"],
+            "stream_kernel": {"name": "k_stream (the pass that reads every logit)", "us": m["kern_us"],
+                              "achieved": m["stream_achieved"], "frac": m["stream_achieved"] / PEAK_HBM_GBS,
+                              "traffic": m["stream_traffic"], "bytes_algorithmic": m["logit_bytes"]},
+        },
     }
-    # the kernels around the step, on this workload's outputs: acceptance
-    # statistics (every mode); tree attention mask and commit map (tree)
-    extras = {}
-
-    def time_launches(fn, reps=100):
-        e = hip.create(2)
-        fn()
-        torch.cuda.synchronize()
-        hip.hip.hipEventRecord(ctypes.c_void_p(e[0]), ctypes.c_void_p(stream))
-        for _ in range(reps):
-            fn()
-        hip.hip.hipEventRecord(ctypes.c_void_p(e[1]), ctypes.c_void_p(stream))
-        torch.cuda.synchronize()
-        us = hip.elapsed_ms(e[0], e[1]) * 1e3 / reps
-        hip.destroy(e)
-        return us
-
-    kk = k if not tree else cfg["max_depth"]
-    stats_out = torch.empty(svm.SV_STATS_LEN, dtype=torch.float64, device=dev)
-    extras["accept_stats_us"] = time_launches(
-        lambda: svm.specverify_accept_stats(acc, status, B, kk, 0.1, stats_out, stream))
-    st = stats_out.cpu().numpy()
-    extras["acceptance"] = float(st[svm.SV_STATS_ACCEPTANCE])
-    extras["mal"] = float(st[svm.SV_STATS_MAL])
-    extras["alpha"] = float(st[svm.SV_STATS_ALPHA])
-    if tree:
-        mask = torch.empty(B, N, (N + 31) // 32, dtype=torch.int32, device=dev)
-        depth = torch.empty(B, N, dtype=torch.int32, device=dev)
-        pos = torch.empty(B, N, dtype=torch.int32, device=dev)
-        extras["tree_mask_us"] = time_launches(
-            lambda: svm.specverify_tree_mask(inputs["parents"], B, N, mask, depth, stream))
-        extras["tree_commit_us"] = time_launches(
-            lambda: svm.specverify_tree_commit(out_nodes, acc, B, N, pos, stream))
-    extras["note"] = ("mean per launch by HIP events over 100 back-to-back launches on the call's "
-                      "stream; acceptance statistics of the last timed call (draft cost c = 0.1)")
+    extras = m.get("extras", {})
+    others = []
+    for c in [int(t) for t in args.also.split(",") if t.strip()]:
+        if c == args.config:
+            continue
+        o = measure(c, min(args.steps, 100), args.warmup, hip, with_extras=False)
+        others.append({"workload": o["workload"], "step_us": o["step_us"], "call_us": o["call_us"],
+                       "bytes_algorithmic": o["alg_bytes"], "achieved_GBps": o["achieved"],
+                       "frac": o["achieved"] / PEAK_HBM_GBS, "stream_us": o["kern_us"],
+                       "stream_frac": o["stream_achieved"] / PEAK_HBM_GBS, "traffic": o["call_traffic"]})
+    if others:
+        extras["other_workloads"] = others
     result["extras"] = extras
-    sv.close()
     if not args.no_cpu:
         log("CPU baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(args.config)

@@ -79,7 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_run.restype = ctypes.c_int
     lib.specverify_destroy.argtypes = [vp]
     lib.specverify_destroy.restype = None
-    lib.specverify_profile_events.argtypes = [vp, vp, vp]
+    lib.specverify_profile_events.argtypes = [vp, vp, vp, vp]
     lib.specverify_profile_events.restype = ctypes.c_int
     lib.specverify_status_string.argtypes = [ctypes.c_int]
     lib.specverify_status_string.restype = ctypes.c_char_p
@@ -155,9 +155,9 @@ def specverify_run(ctx: int, batch, target, draft, draft_tokens, parents, unifor
         raise SpecVerifyError(st, "specverify_run")
 
 
-def specverify_profile_events(ctx: int, ev_begin, ev_end) -> None:
-    """ev_begin / ev_end: raw hipEvent_t handles (ints) or None to stop."""
-    st = load().specverify_profile_events(ctypes.c_void_p(ctx), ev_begin, ev_end)
+def specverify_profile_events(ctx: int, ev_begin, ev_stream_end, ev_call_end=None) -> None:
+    """Raw hipEvent_t handles (ints) or None; all None to stop."""
+    st = load().specverify_profile_events(ctypes.c_void_p(ctx), ev_begin, ev_stream_end, ev_call_end)
     if st != SV_OK:
         raise SpecVerifyError(st, "specverify_profile_events")
 

@@ -62,10 +62,10 @@ Plan make_plan(const sv_config* c) {
   p.top_p = (sample && c->top_p < 1.0) ? c->top_p : 1.0;
   if (c->mode == SV_MODE_GREEDY) { p.filt = sv::kFiltGreedy; p.tile_mode = sv::kModeArgmax; }
   else if (c->mode == SV_MODE_TREE_GREEDY) { p.filt = sv::kFiltTree; p.tile_mode = sv::kModeArgmax; }
-  else if (tsample) { p.filt = sv::kFiltTreeSample; p.tile_mode = sv::kModeStats32; }
+  else if (tsample) { p.filt = sv::kFiltTreeSample; p.tile_mode = sv::kModeStatsMix; }
   else if (p.top_k > 0) { p.filt = sv::kFiltTopk; p.tile_mode = sv::kModeTopk; }
   else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeStats64; }
-  else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStats32; }
+  else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStatsMix; }
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
   else if (tsample) { p.rows_t = c->k; p.rows_d = c->k; p.out_w = c->k; }
   else { p.rows_t = c->k + 1; p.rows_d = sample ? c->k : 0; p.out_w = c->k + 1; }
@@ -126,6 +126,128 @@ Layout layout(const sv_config* c, const Plan& pl) {
   return L;
 }
 
+// One call's launches on the current device: the tiling of the streaming
+// pass, the workspace views (ws laid out as L), the launch chain of the mode.
+// Arguments are already checked.  Returns SV_OK, SV_ERR_SHAPE (the tiling
+// would not fit the workspace) or SV_ERR_HIP.
+int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, int grid,
+                const hipEvent_t ev[3], int32_t batch, const void* target_logits,
+                const void* draft_logits, const int32_t* draft_tokens, const int32_t* parents,
+                const float* uniforms, const float* resid_uniforms, int32_t* accepted_len,
+                int32_t* out_tokens, int32_t* out_nodes, float* resid_probs, int32_t* seq_status,
+                hipStream_t st) {
+  sv::Params p;
+  memset(&p, 0, sizeof(p));
+  p.target = target_logits;
+  p.draft = draft_logits;
+  p.tokens = draft_tokens;
+  p.parents = parents;
+  p.u = uniforms;
+  p.ur = resid_uniforms;
+  p.acc_len = accepted_len;
+  p.out_tokens = out_tokens;
+  p.out_nodes = out_nodes;
+  p.resid_probs = resid_probs;
+  p.seq_status = seq_status;
+  p.B = batch;
+  p.k = c->k;
+  p.V = c->vocab;
+  p.rows_t = pl.rows_t;
+  p.rows_d = pl.rows_d;
+  p.out_w = pl.out_w;
+  p.T = (c->mode == SV_MODE_SAMPLE || c->mode == SV_MODE_TREE_SAMPLE) ? c->temperature : 1.0;
+  p.tree = (c->mode == SV_MODE_TREE_GREEDY || c->mode == SV_MODE_TREE_SAMPLE) ? 1 : 0;
+  p.top_p = pl.top_p;
+  p.top_k = pl.top_k;
+  // tiling of the streaming pass
+  const size_t es = c->dtype == SV_DTYPE_BF16 ? 2 : 4;
+  const bool rows16 = ((size_t)c->vocab * es) % 16 == 0;
+  const bool base16 = ((uintptr_t)target_logits % 16 == 0) &&
+                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0);
+  p.aligned = (rows16 && base16) ? 1 : 0;
+  // top-k: the certified filter pass takes tiles of one round of loads in
+  // aligned rows of whole groups; other shapes take the exact per-tile pass
+  int tile_mode = pl.tile_mode;
+  const long rows = (long)batch * (pl.rows_t + pl.rows_d);
+  // float32 row sums and argmax of large problems: tiles of 4 (or 2) rounds
+  // of loads, as long as that still fills three quarters of the resident
+  // workgroup slots.  Each tile's fixed work (the float64 rescale and wave
+  // sums, the partials) spreads over more logits, and the kernels after the
+  // pass combine four times fewer partials per row (workload 6: pass 55.0 ->
+  // 48.8 -> 45.5 us for 1, 2, 4 rounds; workload 4: pass 21.0 -> 21.1 us,
+  // tree_final 7.6 -> 6.0 us; the 11 MB of workload 2 are faster with one).
+  // The float64 sums of nucleus rows are bound by their exponentials and
+  // stay at one round.
+  int rounds = 1;
+  if (tile_mode == sv::kModeStatsMix || tile_mode == sv::kModeArgmax) {
+    for (int r = kStatsRoundsMax; r > 1; r >>= 1) {
+      if (4L * rows * ((c->vocab + (long)r * kRound - 1) / ((long)r * kRound)) >= 3L * grid) {
+        rounds = r;
+        break;
+      }
+    }
+  }
+  const int round = tile_mode == sv::kModeTopk ? (int)(sv::kFilterRound * 2 / es) : rounds * kRound;
+  if (tile_mode == sv::kModeTopk && p.aligned && c->vocab % sv::kVec == 0 &&
+      c->vocab <= (long)sv::kMaxTiles * round)
+    tile_mode = sv::kModeTopkFilter;
+  long S;
+  if (tile_mode == sv::kModeTopk) {
+    // about four tiles per resident workgroup, tiles of at least kMinTile logits
+    S = (4L * grid + rows - 1) / rows;
+    const long smax = (c->vocab + kMinTile - 1) / kMinTile;
+    if (S > smax) S = smax;
+  } else {
+    // one round of loads per lane (kRound logits; 16 KB of bf16, 32 KB of
+    // fp32); rows that need more than kMaxTiles such tiles take several
+    // rounds per tile; problems with fewer than kSmallTiles tiles take
+    // smaller tiles (down to kMinSmall logits)
+    S = (c->vocab + round - 1) / round;
+    if (rows * S < kSmallTiles) {
+      long want = (kSmallTiles + rows - 1) / rows;
+      const long cap = (c->vocab + kMinSmall - 1) / kMinSmall;
+      if (want > cap) want = cap;
+      if (want > S) S = want;
+    }
+  }
+  if (S > sv::kMaxTiles) S = sv::kMaxTiles;
+  if (S < 1) S = 1;
+  int per = (int)((c->vocab + S - 1) / S);
+  if (tile_mode != sv::kModeTopk && per > round) per = (per + round - 1) / round * round;
+  p.L = (per + sv::kVec - 1) / sv::kVec * sv::kVec;
+  p.S = (c->vocab + p.L - 1) / p.L;
+  const bool lists = tile_mode == sv::kModeTopk || tile_mode == sv::kModeTopkFilter;
+  p.P = tile_mode == sv::kModeTopk ? p.S : p.S * (sv::kBlock / 64);
+  // the workspace holds S_max candidate lists and kMaxPartials partials per row
+  if ((lists && p.S > pl.S_max) || p.P > sv::kMaxPartials || p.S > sv::kMaxTiles) return SV_ERR_SHAPE;
+  p.grid = grid;
+  p.tiles = (sv::TileStat*)(ws + L.tiles);
+  p.cand = (uint64_t*)(ws + L.cand);
+  p.cand_w = pl.cand_w;
+  p.nuc = (sv::RowNuc*)(ws + L.nuc);
+  p.row_lx = (float*)(ws + L.row_lx);
+  p.seq = (sv::SeqState*)(ws + L.seq);
+  p.spart = (double*)(ws + L.spart);
+  p.wpart = (double*)(ws + L.wpart);
+  p.tpart = (double*)(ws + L.tpart);
+  p.tview = (double*)(ws + L.tview);
+  p.keep_w = (pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample) &&
+             (size_t)c->max_batch * pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes ? 1 : 0;
+  p.S2 = pl.S2_max;
+  p.k_idx = (int32_t*)(ws + L.k_idx);
+  p.k_e = (double*)(ws + L.k_e);
+  p.k_cnt = (int32_t*)(ws + L.k_cnt);
+  p.k_norm = (double*)(ws + L.k_norm);
+  p.k_bad = (int32_t*)(ws + L.k_bad);
+  p.k_px = (double*)(ws + L.k_px);
+
+  const int bf16 = c->dtype == SV_DTYPE_BF16;
+  hipError_t e = sv::launch_stream(p, tile_mode, bf16, st, ev[0], ev[1]);
+  if (e == hipSuccess) e = sv::launch_finish(p, pl.filt, bf16, st, ev[2]);
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
+
 }  // namespace
 
 struct specverify_ctx {
@@ -136,7 +258,9 @@ struct specverify_ctx {
   size_t ws_bytes;
   Layout L;
   int grid;                      // resident workgroups of the streaming kernel
-  hipEvent_t ev_begin, ev_end;   // optional instrumentation (caller-owned)
+  // optional instrumentation (caller-owned events): the streaming kernel's
+  // start, its end, the end of the call's last kernel
+  hipEvent_t ev_begin, ev_stream_end, ev_call_end;
 };
 
 extern "C" {
@@ -235,11 +359,14 @@ void specverify_destroy(specverify_ctx* ctx) {
   free(ctx);
 }
 
-int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_end) {
+int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_stream_end,
+                              void* ev_call_end) {
   if (!ctx) return SV_ERR_NULL;
-  if ((ev_begin == nullptr) != (ev_end == nullptr)) return SV_ERR_NULL;
+  if (!ev_begin && (ev_stream_end || ev_call_end)) return SV_ERR_NULL;
+  if (ev_begin && !ev_stream_end && !ev_call_end) return SV_ERR_NULL;
   ctx->ev_begin = (hipEvent_t)ev_begin;
-  ctx->ev_end = (hipEvent_t)ev_end;
+  ctx->ev_stream_end = (hipEvent_t)ev_stream_end;
+  ctx->ev_call_end = (hipEvent_t)ev_call_end;
   return SV_OK;
 }
 
@@ -255,127 +382,15 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
   if (rc != SV_OK) return rc;
   if (resid_probs && c->mode != SV_MODE_SAMPLE && c->mode != SV_MODE_TREE_SAMPLE) return SV_ERR_MODE;
   if (batch == 0) return SV_OK;
-  const Plan& pl = ctx->plan;
-
-  sv::Params p;
-  memset(&p, 0, sizeof(p));
-  p.target = target_logits;
-  p.draft = draft_logits;
-  p.tokens = draft_tokens;
-  p.parents = parents;
-  p.u = uniforms;
-  p.ur = resid_uniforms;
-  p.acc_len = accepted_len;
-  p.out_tokens = out_tokens;
-  p.out_nodes = out_nodes;
-  p.resid_probs = resid_probs;
-  p.seq_status = seq_status;
-  p.B = batch;
-  p.k = c->k;
-  p.V = c->vocab;
-  p.rows_t = pl.rows_t;
-  p.rows_d = pl.rows_d;
-  p.out_w = pl.out_w;
-  p.T = (c->mode == SV_MODE_SAMPLE || c->mode == SV_MODE_TREE_SAMPLE) ? c->temperature : 1.0;
-  p.tree = (c->mode == SV_MODE_TREE_GREEDY || c->mode == SV_MODE_TREE_SAMPLE) ? 1 : 0;
-  p.top_p = pl.top_p;
-  p.top_k = pl.top_k;
-  // tiling of the streaming pass
-  const size_t es = c->dtype == SV_DTYPE_BF16 ? 2 : 4;
-  const bool rows16 = ((size_t)c->vocab * es) % 16 == 0;
-  const bool base16 = ((uintptr_t)target_logits % 16 == 0) &&
-                      (!draft_logits || (uintptr_t)draft_logits % 16 == 0);
-  p.aligned = (rows16 && base16) ? 1 : 0;
-  // top-k: the certified filter pass takes tiles of one round of loads in
-  // aligned rows of whole groups; other shapes take the exact per-tile pass
-  int tile_mode = pl.tile_mode;
-  const long rows = (long)batch * (pl.rows_t + pl.rows_d);
-  // float32 row sums and argmax of large problems: tiles of 4 (or 2) rounds
-  // of loads, as long as that still fills three quarters of the resident
-  // workgroup slots.  Each tile's fixed work (the float64 rescale and wave
-  // sums, the partials) spreads over more logits, and the kernels after the
-  // pass combine four times fewer partials per row (workload 6: pass 55.0 ->
-  // 48.8 -> 45.5 us for 1, 2, 4 rounds; workload 4: pass 21.0 -> 21.1 us,
-  // tree_final 7.6 -> 6.0 us; the 11 MB of workload 2 are faster with one).
-  // The float64 sums of nucleus rows are bound by their exponentials and
-  // stay at one round.
-  int rounds = 1;
-  if (tile_mode == sv::kModeStats32 || tile_mode == sv::kModeArgmax) {
-    for (int r = kStatsRoundsMax; r > 1; r >>= 1) {
-      if (4L * rows * ((c->vocab + (long)r * kRound - 1) / ((long)r * kRound)) >= 3L * ctx->grid) {
-        rounds = r;
-        break;
-      }
-    }
-  }
-  const int round = tile_mode == sv::kModeTopk ? (int)(sv::kFilterRound * 2 / es) : rounds * kRound;
-  if (tile_mode == sv::kModeTopk && p.aligned && c->vocab % sv::kVec == 0 &&
-      c->vocab <= (long)sv::kMaxTiles * round)
-    tile_mode = sv::kModeTopkFilter;
-  long S;
-  if (tile_mode == sv::kModeTopk) {
-    // about four tiles per resident workgroup, tiles of at least kMinTile logits
-    S = (4L * ctx->grid + rows - 1) / rows;
-    const long smax = (c->vocab + kMinTile - 1) / kMinTile;
-    if (S > smax) S = smax;
-  } else {
-    // one round of loads per lane (kRound logits; 16 KB of bf16, 32 KB of
-    // fp32); rows that need more than kMaxTiles such tiles take several
-    // rounds per tile; problems with fewer than kSmallTiles tiles take
-    // smaller tiles (down to kMinSmall logits)
-    S = (c->vocab + round - 1) / round;
-    if (rows * S < kSmallTiles) {
-      long want = (kSmallTiles + rows - 1) / rows;
-      const long cap = (c->vocab + kMinSmall - 1) / kMinSmall;
-      if (want > cap) want = cap;
-      if (want > S) S = want;
-    }
-  }
-  if (S > sv::kMaxTiles) S = sv::kMaxTiles;
-  if (S < 1) S = 1;
-  int per = (int)((c->vocab + S - 1) / S);
-  if (tile_mode != sv::kModeTopk && per > round) per = (per + round - 1) / round * round;
-  p.L = (per + sv::kVec - 1) / sv::kVec * sv::kVec;
-  p.S = (c->vocab + p.L - 1) / p.L;
-  const bool lists = tile_mode == sv::kModeTopk || tile_mode == sv::kModeTopkFilter;
-  p.P = tile_mode == sv::kModeTopk ? p.S : p.S * (sv::kBlock / 64);
-  // the workspace holds S_max candidate lists and kMaxPartials partials per row
-  if ((lists && p.S > pl.S_max) || p.P > sv::kMaxPartials || p.S > sv::kMaxTiles) return SV_ERR_SHAPE;
-  p.grid = ctx->grid;
-  char* ws = (char*)ctx->ws;
-  const Layout& L = ctx->L;
-  const size_t B = (size_t)c->max_batch;
-  const size_t maxrows = B * (size_t)(pl.rows_t + pl.rows_d);
-  p.tiles = (sv::TileStat*)(ws + L.tiles);
-  p.cand = (uint64_t*)(ws + L.cand);
-  p.cand_w = pl.cand_w;
-  p.nuc = (sv::RowNuc*)(ws + L.nuc);
-  (void)maxrows;
-  p.row_lx = (float*)(ws + L.row_lx);
-  p.seq = (sv::SeqState*)(ws + L.seq);
-  p.spart = (double*)(ws + L.spart);
-  p.wpart = (double*)(ws + L.wpart);
-  p.tpart = (double*)(ws + L.tpart);
-  p.tview = (double*)(ws + L.tview);
-  p.keep_w = (pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample) &&
-             (size_t)c->max_batch * pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes ? 1 : 0;
-  p.S2 = pl.S2_max;
-  p.k_idx = (int32_t*)(ws + L.k_idx);
-  p.k_e = (double*)(ws + L.k_e);
-  p.k_cnt = (int32_t*)(ws + L.k_cnt);
-  p.k_norm = (double*)(ws + L.k_norm);
-  p.k_bad = (int32_t*)(ws + L.k_bad);
-  p.k_px = (double*)(ws + L.k_px);
-
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return SV_ERR_HIP;
   if (cur != ctx->device && hipSetDevice(ctx->device) != hipSuccess) return SV_ERR_HIP;
-  hipStream_t st = (hipStream_t)stream;
-  const int bf16 = c->dtype == SV_DTYPE_BF16;
-  hipError_t e = sv::launch_stream(p, tile_mode, bf16, st, ctx->ev_begin, ctx->ev_end);
-  if (e == hipSuccess) e = sv::launch_finish(p, pl.filt, bf16, st);
+  const hipEvent_t ev[3] = {ctx->ev_begin, ctx->ev_stream_end, ctx->ev_call_end};
+  rc = launch_call(c, ctx->plan, ctx->L, (char*)ctx->ws, ctx->grid, ev, batch, target_logits,
+                   draft_logits, draft_tokens, parents, uniforms, resid_uniforms, accepted_len,
+                   out_tokens, out_nodes, resid_probs, seq_status, (hipStream_t)stream);
   if (cur != ctx->device) (void)hipSetDevice(cur);
-  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+  return rc;
 }
 
 static_assert(SV_STATS_LEN == sv::kStatsLen && SV_STATS_SPEEDUP_GAMMA1 == sv::kStatsSpeedup1 &&

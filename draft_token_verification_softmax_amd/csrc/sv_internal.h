@@ -71,9 +71,10 @@ struct SeqState {
 
 // Passes of the streaming kernel: argmax (greedy, tree), top-k lists (exact
 // per tile: any tile shape; certified filter: tiles of one round of loads in
-// aligned rows), max + sum of exponentials (float64 terms for nucleus rows,
-// float32 terms for plain sampling).
-enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4, kModeStats32 = 5 };
+// aligned rows), max + sum of exponentials (float64 terms for nucleus rows;
+// plain and tree sampling: float64 terms in the rows whose normaliser can
+// change a decision, float32 terms in the others).
+enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4, kModeStatsMix = 5 };
 enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4,
               kFiltTreeSample = 5 };
 // Speculative residual passes of tree sampling: pass m (1..kTreePasses)
@@ -150,6 +151,6 @@ hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st,
                          hipEvent_t ev_begin = nullptr, hipEvent_t ev_end = nullptr);
 // Workgroups of the streaming kernel for `mode` one CU keeps resident.
 int stream_blocks_per_cu(int mode, int bf16);
-hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st);
+hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st, hipEvent_t ev_end = nullptr);
 
 }  // namespace sv

@@ -7,9 +7,11 @@
 //                   non-temporal buffer loads per lane), leaving small
 //                   partials in the workspace:
 //                     ARGMAX   max + lowest index, per wave   (greedy, tree)
-//                     STATS32  max + sum of exp((l - max) / T), per wave,
-//                              float32 exp2 terms       (plain sampling)
-//                     STATS64  the same with float64 terms (nucleus rows)
+//                     STATS64  max + sum of exp((l - max) / T), per wave,
+//                              float64 terms              (nucleus rows)
+//                     STATSMIX the same with float64 terms in rows whose
+//                              normaliser can decide an output and float32
+//                              terms in the others   (plain, tree sampling)
 //                     TOPK     a certified filter: every logit above a
 //                              lower bound of the tile's top_k-th, per wave
 //                              (aligned rows); or the tile's exact top_k
@@ -30,9 +32,9 @@
 //
 // Every reduction that feeds an output has a fixed order, so repeated calls
 // give bit-identical results.  Float64 carries every quantity that decides
-// an integer output (accept test, nucleus cut, inverse CDF, nucleus row
-// sums); plain-sampling row sums use float32 exp2 terms summed in float64
-// (relative error about 1e-7).
+// an integer output (accept test, nucleus cut, inverse CDF, and the row sums
+// they divide by); only row sums that cannot change a decision (a chain's
+// bonus row, a leaf's rows) use float32 exp2 terms summed in float64.
 
 #include <float.h>
 #include <limits.h>
@@ -876,29 +878,79 @@ DEV int row_token(const Params& p, int grow, bool* has) {
   return __builtin_amdgcn_raw_buffer_load_b32(rs, (*has ? b * p.k + j : 0) * 4, 0, 0);
 }
 
+// Whether a row of a plain-sampling chain or of a sampled tree needs float64
+// row-sum terms: only rows whose normaliser can change a decision do.
+//   chain: every draft row and target rows 0..k-1 (accept ratios and the
+//          residual max(0, p' - q') depend on the ratio of two normalisers);
+//          target row k is only ever drawn from whole (the bonus), and
+//          C_v / C_{V-1} of p'_k does not depend on its normaliser.
+//   tree:  the two rows of a node with children (the tests of its children
+//          and the running residual after a rejection); a leaf's target row
+//          is only drawn from whole and its draft row is never read.
+// For a tree the answer needs the tree's parent array: tree_parents() loads
+// the part of it each lane checks (buffer loads, issued before the tile's
+// own loads; offsets past the array read 0 without a memory access) and
+// has_child() compares after the tile's loads are in flight.
+constexpr int kParentLoads = kMaxTree / kBlock;
+DEV void tree_parents(const Params& p, int grow, int pv[kParentLoads], int* node) {
+  const int N = p.k, nt = p.B * p.rows_t;
+  const int r = grow < nt ? grow : grow - nt;
+  const int b = r / N;
+  *node = r - b * N;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(p.parents + (size_t)b * N, N * 4);
+#pragma unroll
+  for (int q = 0; q < kParentLoads; ++q)
+    pv[q] = __builtin_amdgcn_raw_buffer_load_b32(rs, ((int)threadIdx.x + q * kBlock) * 4, 0, 0);
+}
+DEV int has_child(const Params& p, const int pv[kParentLoads], int node) {
+  int h = 0;
+#pragma unroll
+  for (int q = 0; q < kParentLoads; ++q) {
+    int v = pv[q];
+    asm volatile("" : "+v"(v));   // first use here, after the tile's loads are issued
+    const int i = (int)threadIdx.x + q * kBlock;
+    h |= (i < p.k && i > node && v == node) ? 1 : 0;
+  }
+  return h;
+}
+
 // Max and sum of exp((l - max) / T) = 2^((l - max) c), c = log2(e) / T, over
 // the logits each wave of a tile reads (one partial per wave).  Per lane:
 // each round of groups first raises the lane max m over them (rescaling the
 // lane sum, in float64, if it rose), then adds 2^((l - m) c) of every logit.
-//   EXACT = false (plain sampling): the hardware float32 exp2 (relative
-//   error below 1e-7) of (l - m) * c with c split into two floats (c_hi +
-//   c_lo carries c to about 48 bits), so the only float32 roundings per
-//   term are the difference, the product and exp2 itself; eight terms are
-//   summed in float32 (a fixed tree), groups in float64.  The relative error
-//   of a sum is a few float32 roundings (about 1e-7 at worst, far less on
-//   average over many terms).
-//   EXACT = true (nucleus rows, whose cut is a discontinuous function of the
-//   row sum): every term in float64 (exp2_64, a few ulp).
+// Terms:
+//   float64 (exp2_64 from a 256-entry table, a few ulp; TERMS64, and the
+//   rows of a TERMS_MIX pass that need them): the sum is the one of exact
+//   arithmetic to about 1e-15, so every decision taken from it agrees with a
+//   float64 evaluation except within rounding of its threshold.
+//   float32 (the other rows of a TERMS_MIX pass): the hardware float32 exp2
+//   (relative error below 1e-7) of (l - m) * c with c split into two floats
+//   (c_hi + c_lo carries c to about 48 bits), eight terms summed in float32 (a
+//   fixed tree), groups in float64.  Used only where the normaliser cannot
+//   change a decision (see row_needs_f64 / has_child).
 // The wave combines its lanes in float64 by one fixed butterfly.
-template <typename T, bool EXACT>
+constexpr int kTerms64 = 1, kTermsMix = 2;
+template <typename T, int TERMS>
 DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow, int seg) {
   __shared__ double tab[kExpTab];
   bool xhas;
   const int xt = row_token(p, grow, &xhas);
   float lx = 0.f;
   bool hx = false;
-  const double tv = EXACT ? exp2_table_fetch() : 0.0;
-  bool need_tab = EXACT;   // stored once the first round's loads are in flight
+  const double tv = exp2_table_fetch();
+  bool need_tab = true;   // stored once the first round's loads are in flight
+  // which terms this tile takes (uniform over the workgroup)
+  bool exact = TERMS == kTerms64;
+  int pv[kParentLoads];
+  int node = 0;
+  if constexpr (TERMS == kTermsMix) {
+    if (p.tree) {
+      tree_parents(p, grow, pv, &node);
+    } else {
+      const int nt = p.B * p.rows_t;
+      exact = grow >= nt || (grow % p.rows_t) < p.k;
+    }
+  }
   const double cd = kLog2e / p.T;
   const double cs = kExpScale * cd;
   // c_hi <= c and c_lo > 0, so that a -inf logit gives d * c_lo = -inf and
@@ -937,21 +989,28 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
       m = mi;
     }
     if (need_tab) {
-      exp2_table_store(tab, tv);
+      tab[threadIdx.x] = tv;
+      if (TERMS == kTermsMix && p.tree) exact = __syncthreads_or(has_child(p, pv, node)) != 0;
+      else __syncthreads();
       need_tab = false;
     }
     if (m > -INFINITY) {
+      if (exact) {
 #pragma unroll
-      for (int u = 0; u < n; ++u) {
-        float v[kVec];
-        gr[u].opaque().values(v);
-        if (EXACT) {
+        for (int u = 0; u < n; ++u) {
+          float v[kVec];
+          gr[u].opaque().values(v);
           const double nmc = -(double)m * cs;
           double gs = 0.0;
 #pragma unroll
           for (int q = 0; q < kVec; ++q) gs += exp2_64(fma((double)v[q], cs, nmc), tab);
           s += u < nv ? gs : 0.0;
-        } else {
+        }
+      } else if constexpr (TERMS == kTermsMix) {
+#pragma unroll
+        for (int u = 0; u < n; ++u) {
+          float v[kVec];
+          gr[u].opaque().values(v);
           float e[kVec];
 #pragma unroll
           for (int q = 0; q < kVec; ++q) {
@@ -3046,9 +3105,9 @@ __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
   } else if constexpr (MODE == kModeTopkFilter) {
     tile_topk_filter<T, kFilterGroups / (int)sizeof(T)>(p, row, start, end, grow, seg);
   } else if constexpr (MODE == kModeStats64) {
-    tile_stats<T, true>(p, row, start, end, grow, seg);
-  } else if constexpr (MODE == kModeStats32) {
-    tile_stats<T, false>(p, row, start, end, grow, seg);
+    tile_stats<T, kTerms64>(p, row, start, end, grow, seg);
+  } else if constexpr (MODE == kModeStatsMix) {
+    tile_stats<T, kTermsMix>(p, row, start, end, grow, seg);
   } else {
     tile_argmax<T>(p, row, start, end, grow, seg);
   }
@@ -3629,7 +3688,7 @@ static int capacity_t(int mode) {
   int per_cu = 0;
   hipError_t e;
   if (mode == kModeStats64) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeStats64>, kBlock, 0);
-  else if (mode == kModeStats32) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeStats32>, kBlock, 0);
+  else if (mode == kModeStatsMix) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeStatsMix>, kBlock, 0);
   else if (mode == kModeTopk) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopk>, kBlock, 0);
   else if (mode == kModeTopkFilter) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopkFilter>, kBlock, 0);
   else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeArgmax>, kBlock, 0);
@@ -3649,8 +3708,8 @@ static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hip
   const dim3 block(kBlock);
   if (mode == kModeStats64)
     hipExtLaunchKernelGGL((k_stream<T, kModeStats64>), dim3(grid), block, 0, st, e0, e1, 0, p);
-  else if (mode == kModeStats32)
-    hipExtLaunchKernelGGL((k_stream<T, kModeStats32>), dim3(grid), block, 0, st, e0, e1, 0, p);
+  else if (mode == kModeStatsMix)
+    hipExtLaunchKernelGGL((k_stream<T, kModeStatsMix>), dim3(grid), block, 0, st, e0, e1, 0, p);
   else if (mode == kModeTopk)
     hipExtLaunchKernelGGL((k_stream<T, kModeTopk>), dim3(grid), block, 0, st, e0, e1, 0, p);
   else if (mode == kModeTopkFilter)
@@ -3660,29 +3719,34 @@ static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hip
   return hipGetLastError();
 }
 
+// The kernels after the streaming pass.  With ev_end, the dispatch of the
+// call's last kernel records it when that kernel completes.
 template <typename T>
-static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
+static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st, hipEvent_t ev_end) {
   const int rows = p.B * (p.rows_t + p.rows_d);
   const dim3 block(kBlock), gb((unsigned)p.B), gr((unsigned)rows), gs((unsigned)p.S2, (unsigned)p.B),
       gb1(1u, (unsigned)p.B);
+  auto run = [&](bool last, auto kernel, dim3 grid, auto... args) {
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, nullptr, last ? ev_end : nullptr, 0, args...);
+  };
   switch (filt) {
-    case kFiltGreedy: hipLaunchKernelGGL((k_greedy_final<T>), gb, block, 0, st, p); break;
-    case kFiltTree: hipLaunchKernelGGL((k_tree_final<T>), gb, block, 0, st, p); break;
+    case kFiltGreedy: run(true, k_greedy_final<T>, gb, p); break;
+    case kFiltTree: run(true, k_tree_final<T>, gb, p); break;
     case kFiltTopk:
       if (p.top_k <= 64 && p.P != p.S)
-        hipLaunchKernelGGL((k_topk_rows_w<T>), dim3((unsigned)((rows + kWaves - 1) / kWaves)), block, 0, st, p);
+        run(false, k_topk_rows_w<T>, dim3((unsigned)((rows + kWaves - 1) / kWaves)), p);
       else
-        hipLaunchKernelGGL((k_topk_rows<T>), gr, block, 0, st, p);
+        run(false, k_topk_rows<T>, gr, p);
       if (p.top_k <= 64 && p.k < 64)
-        hipLaunchKernelGGL((k_topk_final_w<T>), gb, block, 0, st, p);
+        run(true, k_topk_final_w<T>, gb, p);
       else
-        hipLaunchKernelGGL((k_topk_final<T>), gb, block, 0, st, p);
+        run(true, k_topk_final<T>, gb, p);
       break;
     case kFiltTopp:
-      hipLaunchKernelGGL((k_topp_rows<T>), gr, block, 0, st, p);
-      hipLaunchKernelGGL((k_topp_rows_exact<T>), gr, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_s<T, kFiltTopp>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T, kFiltTopp>), (p.resid_probs || p.keep_w) ? gs : gb1, block, 0, st, p);
+      run(false, k_topp_rows<T>, gr, p);
+      run(false, k_topp_rows_exact<T>, gr, p);
+      run(false, k_resid_s<T, kFiltTopp>, gs, p);
+      run(true, k_resid_final<T, kFiltTopp>, (p.resid_probs || p.keep_w) ? gs : gb1, p);
       break;
     case kFiltTreeSample: {
       const int passes = p.k - 1 < kTreePasses ? p.k - 1 : kTreePasses;
@@ -3690,16 +3754,16 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st) {
         const int most = (p.k - 1) / (m + 1);   // nodes that can have more than m children
         int G = (most + kPassBatch - 1) / kPassBatch;
         G = G < 1 ? 1 : (G > kPassGroups ? kPassGroups : G);
-        hipLaunchKernelGGL((k_tsample_pass<T>), dim3((unsigned)p.S2, (unsigned)p.B, (unsigned)G), block, 0, st, p, m);
+        run(false, k_tsample_pass<T>, dim3((unsigned)p.S2, (unsigned)p.B, (unsigned)G), p, m);
       }
-      hipLaunchKernelGGL((k_tsample_walk<T>), gb, block, 0, st, p);
-      hipLaunchKernelGGL((k_tsample_mass<T>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), (p.resid_probs || p.keep_w) ? gs : gb1, block, 0, st, p);
+      run(false, k_tsample_walk<T>, gb, p);
+      run(false, k_tsample_mass<T>, gs, p);
+      run(true, k_resid_final<T, kFiltNone>, (p.resid_probs || p.keep_w) ? gs : gb1, p);
       break;
     }
     default:  // plain sampling
-      hipLaunchKernelGGL((k_resid_s<T, kFiltNone>), gs, block, 0, st, p);
-      hipLaunchKernelGGL((k_resid_final<T, kFiltNone>), (p.resid_probs || p.keep_w) ? gs : gb1, block, 0, st, p);
+      run(false, k_resid_s<T, kFiltNone>, gs, p);
+      run(true, k_resid_final<T, kFiltNone>, (p.resid_probs || p.keep_w) ? gs : gb1, p);
       break;
   }
   return hipGetLastError();
@@ -3711,8 +3775,8 @@ hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st, hi
               : launch_stream_t<float>(p, mode, st, e0, e1);
 }
 
-hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st) {
-  return bf16 ? launch_finish_t<uint16_t>(p, filt, st) : launch_finish_t<float>(p, filt, st);
+hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st, hipEvent_t ev_end) {
+  return bf16 ? launch_finish_t<uint16_t>(p, filt, st, ev_end) : launch_finish_t<float>(p, filt, st, ev_end);
 }
 
 }  // namespace sv

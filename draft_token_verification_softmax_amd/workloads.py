@@ -96,9 +96,10 @@ def _target_f64(rng, cfg, rows_shape, V):
 
 
 def chain_inputs(config: int, seed: int | None = None, B: int | None = None,
-                 V: int | None = None, k: int | None = None, dtype: str | None = None):
+                 V: int | None = None, k: int | None = None, dtype: str | None = None,
+                 noise: float | None = None):
     """Seeded inputs of a chain workload (configs 1, 2, 3, 5), optionally with
-    smaller B / V / k for parity cases.
+    smaller B / V / k, or another draft noise sd, for parity cases.
 
     Returns a dict:
       target  [B, k+1, V]  float32, or uint16 bf16 bit patterns
@@ -114,6 +115,8 @@ def chain_inputs(config: int, seed: int | None = None, B: int | None = None,
     V = cfg["V"] if V is None else V
     k = cfg["k"] if k is None else k
     dtype = cfg["dtype"] if dtype is None else dtype
+    if noise is not None:
+        cfg["noise"] = noise
     rng = np.random.default_rng(DEFAULT_SEED[config] if seed is None else seed)
     t64 = _target_f64(rng, cfg, (B, k + 1), V)
     d64 = cfg.get("draft_scale", 1.0) * t64[:, :k] + rng.normal(0.0, cfg["noise"], size=(B, k, V))

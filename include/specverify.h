@@ -180,14 +180,20 @@ int specverify_run(specverify_ctx* ctx, int32_t batch,
  * sure no queued call still uses the context. */
 void specverify_destroy(specverify_ctx* ctx);
 
-/* Instrumentation for benchmarks: on every later specverify_run of this
- * context, the dispatch of the streaming kernel (the one pass that reads
- * every logit) records the HIP event `ev_begin` when it starts and `ev_end`
- * when it completes, so hipEventElapsedTime gives that kernel's duration.
- * The events are caller-owned hipEvent_t handles created on the context's
- * device; pass NULL, NULL to stop.  Nothing is skipped or reordered.  Errors:
- * SV_ERR_NULL (ctx NULL, or exactly one event NULL). */
-int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_end);
+/* Instrumentation for benchmarks.  On every later specverify_run of this
+ * context the dispatch packets of the call's kernels record caller-owned HIP
+ * events (hipEvent_t handles created on the context's device):
+ *   ev_begin       when the streaming kernel (the call's first kernel, the one
+ *                  pass that reads every logit) starts;
+ *   ev_stream_end  when the streaming kernel completes (NULL: not recorded);
+ *   ev_call_end    when the call's last kernel completes (NULL: not recorded).
+ * hipEventElapsedTime(ev_begin, ev_stream_end) is then that kernel's duration
+ * and hipEventElapsedTime(ev_begin, ev_call_end) the call's time from its
+ * first kernel's start to its last kernel's end.  Pass NULL, NULL, NULL to
+ * stop.  Nothing is skipped or reordered.  Errors: SV_ERR_NULL (ctx NULL,
+ * ev_begin NULL with another event given, or ev_begin alone). */
+int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_stream_end,
+                              void* ev_call_end);
 
 /* Human-readable name of an SV_OK / SV_ERR_* code (static storage). */
 const char* specverify_status_string(int status);

@@ -188,7 +188,7 @@ def test_null_config_and_bad_create_make_no_hip_call():
 def test_run_rejects_null_context():
     lib = svm.load()
     assert lib.specverify_run(None, 1, *([None] * 11), None) == SV_ERR_NULL
-    assert lib.specverify_profile_events(None, None, None) == SV_ERR_NULL
+    assert lib.specverify_profile_events(None, None, None, None) == SV_ERR_NULL
 
 
 def test_stats_layout_matches_header():

@@ -73,6 +73,55 @@ def test_sample_plain(config, dtype, B, V, k):
     compare_chain(gpu, orc, range(B), f"sample cfg{config} {dtype} B={B} V={V} k={k}")
 
 
+@pytest.mark.parametrize("config,dtype", [(2, "bf16"), (1, "f32")])
+def test_sample_plain_close_draft(config, dtype):
+    """A draft that tracks its target closely (draft logits = target + N(0,
+    0.05^2)): the residual max(0, p' - q') holds a few percent of the mass,
+    so the draw divides any error in the rows' normalisers by that mass."""
+    B = 128
+    say("sample close draft", config, dtype, B)
+    inp = wl.chain_inputs(config, seed=4242 + config, B=B, V=32000, k=5, dtype=dtype, noise=0.05)
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    T64 = wl.rows_f64(inp["target"], dtype)
+    D64 = wl.rows_f64(inp["draft"], dtype)
+    mass = [np.maximum(0.0, ov.transform_row(T64[b, 0], 1.0) - ov.transform_row(D64[b, 0], 1.0)).sum()
+            for b in range(8)]
+    say("residual mass of row 0, first sequences:", np.round(mass, 4).tolist())
+    assert np.median(mass) < 0.05
+    compare_chain(gpu, orc, range(B), f"close draft cfg{config} {dtype}")
+
+
+@pytest.mark.parametrize("mode", [SV_MODE_SAMPLE, SV_MODE_GREEDY])
+def test_workload1_single_sequence_calls(mode):
+    """Workload 1 as the benchmark runs it: independent rounds of one
+    sequence each (B = 1, k = 4, V = 32000 float32), 200 calls on one
+    context, each checked against the oracle."""
+    import torch
+    from draft_token_verification_softmax_amd import SpecVerify
+    from gpu_common import dev
+    R = 200
+    say("workload 1, B = 1 calls", mode, R)
+    inp = wl.chain_inputs(1, seed=5151 + mode, B=R)
+    x = draw_drafts(inp) if mode == SV_MODE_SAMPLE else _planted_greedy_drafts(inp, 0.8, 3)
+    sample = mode == SV_MODE_SAMPLE
+    sv = SpecVerify(mode=mode, dtype="f32", max_batch=1, k=4, vocab=32000, temperature=inp["T"])
+    gpu = dict(accepted_len=np.zeros(R, np.int32), out_tokens=np.zeros((R, 5), np.int32),
+               seq_status=np.zeros(R, np.int32), resid_probs=np.zeros((R, 32000), np.float32) if sample else None)
+    for b in range(R):
+        out = sv.run(dev(inp["target"][b:b + 1]), dev(inp["draft"][b:b + 1]) if sample else None,
+                     dev(x[b:b + 1]), dev(inp["u"][b:b + 1]) if sample else None,
+                     dev(inp["ur"][b:b + 1]) if sample else None, want_resid_probs=sample)
+        torch.cuda.synchronize()
+        for key in ("accepted_len", "out_tokens", "seq_status") + (("resid_probs",) if sample else ()):
+            gpu[key][b] = out[key].cpu().numpy()[0]
+    sv.close()
+    orc = oracle_chain(inp, x, mode, list(range(R)))
+    compare_chain(gpu, orc, range(R), f"workload 1 B=1 mode {mode}")
+    assert len(set(gpu["accepted_len"].tolist())) >= 3
+
+
 def test_sample_plain_full_workload2():
     say("sample workload 2 full size")
     inp = wl.chain_inputs(2)          # B=16, k=5, V=32000 bf16, the benchmark's seed

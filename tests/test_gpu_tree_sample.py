@@ -111,6 +111,19 @@ def test_tree_sample_parity(B, N, V, dtype, T, mc):
     compare(gpu, orc, list(range(B)), f"tree sample N={N} V={V} {dtype}")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tree_sample_close_draft(dtype):
+    """Draft rows that track their targets closely (noise sd 0.05): after a
+    rejected child the running residual holds a few percent of the mass, and
+    every further test and the draw divide by it."""
+    say("tree sample close draft", dtype)
+    inp = wl.tree_sample_inputs(seed=808, B=24, N=30, V=32000, dtype=dtype, noise=0.05)
+    tok = tree_tokens(inp)
+    gpu = run_gpu(inp, tok)
+    orc = run_oracle(inp, tok, range(24))
+    compare(gpu, orc, list(range(24)), f"tree sample close draft {dtype}")
+
+
 def test_tree_sample_full_size():
     say("tree sample 8 x 60 nodes, V=128256 bf16")
     inp = wl.tree_sample_inputs()
