@@ -22,11 +22,12 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspecveri
 SV_MODE_SAMPLE, SV_MODE_GREEDY, SV_MODE_TREE_GREEDY, SV_MODE_TREE_SAMPLE = 0, 1, 2, 3
 SV_DTYPE_F32, SV_DTYPE_BF16 = 0, 1
 SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_PARAM = 0, -1, -2, -3, -4
-SV_ERR_CAPACITY, SV_ERR_HIP, SV_ERR_MODE = -5, -6, -7
+SV_ERR_CAPACITY, SV_ERR_HIP, SV_ERR_MODE, SV_ERR_SCRATCH = -5, -6, -7, -8
+SV_STATIC_SCRATCH_BYTES = 64 << 20
 SV_STATUS_BAD_TOKEN, SV_STATUS_BAD_PARENT, SV_STATUS_BAD_LOGITS = 1, 2, 4
 SV_MAX_K, SV_MAX_TREE_NODES, SV_MAX_TOP_K, SV_MAX_VOCAB = 64, 1024, 256, 1 << 24
 
-EXPORTED = ("specverify_create", "specverify_check_args", "specverify_run",
+EXPORTED = ("specverify_create", "specverify_check_args", "specverify_run", "specverify_run_static",
             "specverify_destroy", "specverify_profile_events", "specverify_status_string",
             "specverify_workspace_bytes", "specverify_accept_stats", "specverify_tree_mask",
             "specverify_tree_commit")
@@ -77,6 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_check_args.restype = ctypes.c_int
     lib.specverify_run.argtypes = [vp, i32] + [vp] * 11 + [vp]
     lib.specverify_run.restype = ctypes.c_int
+    lib.specverify_run_static.argtypes = [P(sv_config), i32] + [vp] * 11 + [vp]
+    lib.specverify_run_static.restype = ctypes.c_int
     lib.specverify_destroy.argtypes = [vp]
     lib.specverify_destroy.restype = None
     lib.specverify_profile_events.argtypes = [vp, vp, vp, vp]
@@ -153,6 +156,26 @@ def specverify_run(ctx: int, batch, target, draft, draft_tokens, parents, unifor
         ctypes.c_void_p(stream))
     if st != SV_OK:
         raise SpecVerifyError(st, "specverify_run")
+
+
+def specverify_run_static(cfg: sv_config, batch, target, draft, draft_tokens, parents, uniforms,
+                          resid_uniforms, accepted_len, out_tokens, out_nodes=None,
+                          resid_probs=None, seq_status=None, stream=None) -> None:
+    """The allocation-free variant: no context, workspace in the library's
+    fixed device array (at most SV_STATIC_SCRATCH_BYTES); cfg is an
+    sv_config (see make_config)."""
+    if stream is None:
+        import torch
+        stream = torch.cuda.current_stream().cuda_stream
+    elif not isinstance(stream, int):
+        stream = stream.cuda_stream
+    st = load().specverify_run_static(
+        ctypes.byref(cfg), int(batch), _ptr(target), _ptr(draft), _ptr(draft_tokens),
+        _ptr(parents), _ptr(uniforms), _ptr(resid_uniforms), _ptr(accepted_len),
+        _ptr(out_tokens), _ptr(out_nodes), _ptr(resid_probs), _ptr(seq_status),
+        ctypes.c_void_p(stream))
+    if st != SV_OK:
+        raise SpecVerifyError(st, "specverify_run_static")
 
 
 def specverify_profile_events(ctx: int, ev_begin, ev_stream_end, ev_call_end=None) -> None:

@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "specverify.h"
 #include "sv_aux.h"
 #include "sv_internal.h"
@@ -248,6 +250,54 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
 }
 
 
+// Workspace of specverify_run_static: one fixed array in device memory that
+// every GPU the library runs on holds until the process ends.  Host code never
+// uses the array's name as an address (on the host it is a stand-in, not the
+// device address): the address comes from hipGetSymbolAddress, once per device
+// with that device current, and is kept per device.
+static __device__ __align__(256) unsigned char scratch[SV_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+struct StaticDevice {
+  int ready;               // 0 not set up, 1 set up, -1 set-up failed
+  char* ptr;               // device address of `scratch` on this device
+  int cus;                 // compute units
+  int per_cu[2][8];        // resident streaming workgroups per CU, [bf16][tile mode] (0: not asked yet)
+};
+StaticDevice g_static[kMaxDevices];
+std::mutex g_static_mu;
+
+// Set-up of the current device for specverify_run_static (first call on it):
+// the scratch address and the compute-unit count; then the streaming
+// kernel's resident workgroups for this mode and dtype.  No allocation.
+int static_device(int tile_mode, int bf16, char** ptr, int* grid) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SV_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  StaticDevice& d = g_static[dev];
+  if (d.ready == 0) {
+    void* addr = nullptr;
+    int cus = 0;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) {
+      d.ready = -1;
+    } else {
+      d.ptr = (char*)addr;
+      d.cus = cus;
+      d.ready = 1;
+    }
+  }
+  if (d.ready != 1 || tile_mode < 0 || tile_mode >= 8) return SV_ERR_HIP;
+  int& pc = d.per_cu[bf16 ? 1 : 0][tile_mode];
+  if (pc == 0) {
+    pc = sv::stream_blocks_per_cu(tile_mode, bf16);
+    if (pc < 1) pc = 1;
+  }
+  *ptr = d.ptr;
+  *grid = d.cus * pc;
+  return SV_OK;
+}
+
 }  // namespace
 
 struct specverify_ctx {
@@ -275,6 +325,9 @@ const char* specverify_status_string(int status) {
     case SV_ERR_CAPACITY: return "SV_ERR_CAPACITY: batch exceeds max_batch";
     case SV_ERR_HIP: return "SV_ERR_HIP: a HIP call failed";
     case SV_ERR_MODE: return "SV_ERR_MODE: unknown mode, or a pointer that does not fit the mode";
+    case SV_ERR_SCRATCH:
+      return "SV_ERR_SCRATCH: the call needs more workspace than the static scratch array holds "
+             "(SV_STATIC_SCRATCH_BYTES); use a context (specverify_create / specverify_run) or a smaller batch";
     default: return "unknown status";
   }
 }
@@ -391,6 +444,32 @@ int specverify_run(specverify_ctx* ctx, int32_t batch, const void* target_logits
                    out_tokens, out_nodes, resid_probs, seq_status, (hipStream_t)stream);
   if (cur != ctx->device) (void)hipSetDevice(cur);
   return rc;
+}
+
+int specverify_run_static(const sv_config* cfg, int32_t batch, const void* target_logits,
+                          const void* draft_logits, const int32_t* draft_tokens, const int32_t* parents,
+                          const float* uniforms, const float* resid_uniforms, int32_t* accepted_len,
+                          int32_t* out_tokens, int32_t* out_nodes, float* resid_probs,
+                          int32_t* seq_status, void* stream) {
+  int rc = specverify_check_args(cfg, batch, target_logits, draft_logits, draft_tokens, parents,
+                                 uniforms, resid_uniforms, accepted_len, out_tokens, out_nodes);
+  if (rc != SV_OK) return rc;
+  if (resid_probs && cfg->mode != SV_MODE_SAMPLE && cfg->mode != SV_MODE_TREE_SAMPLE) return SV_ERR_MODE;
+  if (batch == 0) return SV_OK;
+  // the workspace laid out for this call's batch
+  sv_config c = *cfg;
+  c.max_batch = batch;
+  const Plan pl = make_plan(&c);
+  const Layout L = layout(&c, pl);
+  if (L.total > (size_t)SV_STATIC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
+  char* ws = nullptr;
+  int grid = 0;
+  rc = static_device(pl.tile_mode, c.dtype == SV_DTYPE_BF16, &ws, &grid);
+  if (rc != SV_OK) return rc;
+  const hipEvent_t ev[3] = {nullptr, nullptr, nullptr};
+  return launch_call(&c, pl, L, ws, grid, ev, batch, target_logits, draft_logits, draft_tokens,
+                     parents, uniforms, resid_uniforms, accepted_len, out_tokens, out_nodes,
+                     resid_probs, seq_status, (hipStream_t)stream);
 }
 
 static_assert(SV_STATS_LEN == sv::kStatsLen && SV_STATS_SPEEDUP_GAMMA1 == sv::kStatsSpeedup1 &&

@@ -103,6 +103,7 @@ enum {
   SV_ERR_CAPACITY = -5,  /* batch > max_batch */
   SV_ERR_HIP = -6,       /* a HIP call failed (allocation, launch, no device) */
   SV_ERR_MODE = -7,      /* unknown mode, or a pointer given / missing for this mode */
+  SV_ERR_SCRATCH = -8,   /* specverify_run_static: the call needs more than SV_STATIC_SCRATCH_BYTES */
 };
 enum { SV_STATUS_BAD_TOKEN = 1, SV_STATUS_BAD_PARENT = 2, SV_STATUS_BAD_LOGITS = 4 };
 
@@ -175,6 +176,30 @@ int specverify_run(specverify_ctx* ctx, int32_t batch,
                    const float* uniforms, const float* resid_uniforms,
                    int32_t* accepted_len, int32_t* out_tokens, int32_t* out_nodes,
                    float* resid_probs, int32_t* seq_status, void* stream);
+
+/* The same verification as specverify_run, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  There is no context: `cfg` describes the call (its
+ * max_batch must be >= batch, as for specverify_create), and the workspace is
+ * a fixed array of SV_STATIC_SCRATCH_BYTES in device memory that the library
+ * holds on every device it runs on until the process ends.  The call runs on
+ * the calling thread's current device (the one holding the buffers) and calls
+ * no hipMalloc, hipFree or other allocating routine; its first call on a
+ * device looks up that device's array address and compute-unit count once.
+ * Arguments, outputs and errors as specverify_run, plus SV_ERR_SCRATCH when
+ * the call's workspace -- specverify_workspace_bytes of cfg with max_batch set
+ * to batch -- exceeds SV_STATIC_SCRATCH_BYTES (no HIP call is made then).  Every call on one
+ * device shares that device's array and leaves its contents behind; no
+ * kernel reads workspace it has not written in the same call, so nothing
+ * needs clearing between calls.  Calls that overlap in time on one device
+ * (two streams, two threads) race on the array: serialise them. */
+#define SV_STATIC_SCRATCH_BYTES (64u << 20)
+int specverify_run_static(const sv_config* cfg, int32_t batch,
+                          const void* target_logits, const void* draft_logits,
+                          const int32_t* draft_tokens, const int32_t* parents,
+                          const float* uniforms, const float* resid_uniforms,
+                          int32_t* accepted_len, int32_t* out_tokens, int32_t* out_nodes,
+                          float* resid_probs, int32_t* seq_status, void* stream);
 
 /* Free the workspace and the context.  NULL is allowed.  The caller must make
  * sure no queued call still uses the context. */

@@ -26,7 +26,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = svm.load()
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(svm.EXPORTED) == names
@@ -38,9 +38,32 @@ def test_header_constants_match_binding():
         m = re.search(r"#define %s (\d+)" % name, text)
         assert int(m.group(1)) == getattr(svm, name)
     for name in ("SV_ERR_NULL", "SV_ERR_SHAPE", "SV_ERR_DTYPE", "SV_ERR_PARAM", "SV_ERR_CAPACITY",
-                 "SV_ERR_HIP", "SV_ERR_MODE"):
+                 "SV_ERR_HIP", "SV_ERR_MODE", "SV_ERR_SCRATCH"):
         m = re.search(r"%s = (-\d+)" % name, text)
         assert int(m.group(1)) == getattr(svm, name)
+
+
+def test_static_scratch_limit_is_checked_on_the_host():
+    """specverify_run_static: a call whose workspace (specverify_workspace_bytes
+    with max_batch = batch) exceeds SV_STATIC_SCRATCH_BYTES is refused with
+    SV_ERR_SCRATCH before any HIP call; argument errors as specverify_run."""
+    text = open(HEADER).read()
+    m = re.search(r"#define SV_STATIC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert int(m.group(1)) << int(m.group(2)) == svm.SV_STATIC_SCRATCH_BYTES
+    lib = svm.load()
+    fake = ctypes.c_void_p(16)   # never dereferenced: the call returns before any HIP call
+    big = make_config(SV_MODE_SAMPLE, "bf16", 512, 8, 128256, 0.7, top_k=50)
+    cfg_b = make_config(SV_MODE_SAMPLE, "bf16", 512, 8, 128256, 0.7, top_k=50)
+    cfg_b.max_batch = 512
+    assert svm.specverify_workspace_bytes(cfg_b) > svm.SV_STATIC_SCRATCH_BYTES
+    # target, draft, tokens, parents, u, ur, accepted_len, out_tokens, out_nodes, resid_probs, status
+    args = [fake, fake, fake, None, fake, fake, fake, fake, None, None, None]
+    assert lib.specverify_run_static(ctypes.byref(big), 512, *args, None) == svm.SV_ERR_SCRATCH
+    # batch 0 is a no-op, NULL config and missing pointers are argument errors
+    assert lib.specverify_run_static(ctypes.byref(big), 0, *([None] * 11), None) == SV_OK
+    assert lib.specverify_run_static(None, 1, *([None] * 11), None) == SV_ERR_NULL
+    assert lib.specverify_run_static(ctypes.byref(big), 1, *([None] * 11), None) == SV_ERR_NULL
+    assert lib.specverify_run_static(ctypes.byref(big), 513, *args, None) == svm.SV_ERR_CAPACITY
 
 
 def test_config_struct_layout():

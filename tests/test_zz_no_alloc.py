@@ -1,0 +1,133 @@
+"""specverify_run_static (no context, workspace in the library's fixed device
+array) against specverify_run (a context's workspace) through the C ABI.
+
+Both entry points run the same kernels on the same inputs, so their outputs
+must agree bit for bit.  Each case makes two calls in a row through the
+static entry point, the second with a smaller input, so the second call
+runs on an array that still holds the first call's data.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.verify as ov
+from draft_token_verification_softmax_amd import (SV_MODE_GREEDY, SV_MODE_SAMPLE, SV_MODE_TREE_GREEDY,
+                                                  SV_MODE_TREE_SAMPLE, SpecVerify, make_config,
+                                                  specverify_run_static)
+from draft_token_verification_softmax_amd import workloads as wl
+from gpu_common import dev, draw_drafts, say
+
+pytestmark = pytest.mark.gpu
+
+KEYS = ("accepted_len", "out_tokens", "out_nodes", "seq_status", "resid_probs")
+
+
+def _chain_case(config, B, V, k, dtype, T, top_k, top_p, seed):
+    inp = wl.chain_inputs(config, seed=seed, B=B, V=V, k=k, dtype=dtype)
+    inp["T"], inp["top_k"], inp["top_p"] = T, top_k, top_p
+    x = draw_drafts(inp)
+    return dict(mode=SV_MODE_SAMPLE, dtype=dtype, B=B, k=k, V=V, T=T, top_k=top_k, top_p=top_p,
+                target=inp["target"], draft=inp["draft"], tokens=x, parents=None, u=inp["u"], ur=inp["ur"])
+
+
+def _greedy_case(B, V, k, seed):
+    inp = wl.chain_inputs(1, seed=seed, B=B, V=V, k=k, dtype="f32")
+    g = np.argmax(wl.rows_f64(inp["target"], "f32"), axis=-1)[:, :k]
+    rng = np.random.default_rng(seed)
+    x = np.where(rng.random((B, k)) < 0.8, g, rng.integers(0, V, size=(B, k))).astype(np.int32)
+    return dict(mode=SV_MODE_GREEDY, dtype="f32", B=B, k=k, V=V, T=1.0, top_k=0, top_p=1.0,
+                target=inp["target"], draft=None, tokens=x, parents=None, u=None, ur=None)
+
+
+def _tree_case(B, N, V, dtype, sample, seed):
+    if sample:
+        ti = wl.tree_sample_inputs(seed=seed, B=B, N=N, V=V, dtype=dtype)
+        d64 = wl.rows_f64(ti["draft"], dtype)
+        tok = np.zeros((B, N), np.int32)
+        for b in range(B):
+            for i in range(1, N):
+                tok[b, i] = ov.draw_from(ov.transform_row(d64[b, ti["parents"][b, i]], 1.0), ti["draw_u"][b, i])
+        return dict(mode=SV_MODE_TREE_SAMPLE, dtype=dtype, B=B, k=N, V=V, T=1.0, top_k=0, top_p=1.0,
+                    target=ti["target"], draft=ti["draft"], tokens=tok, parents=ti["parents"], u=ti["u"],
+                    ur=ti["ur"])
+    tr = wl.tree_inputs(4, seed=seed, B=B, N=N, V=V, dtype=dtype)
+    tok = wl.tree_tokens(tr, np.argmax(wl.rows_f64(tr["target"], dtype), axis=-1))
+    return dict(mode=SV_MODE_TREE_GREEDY, dtype=dtype, B=B, k=N, V=V, T=1.0, top_k=0, top_p=1.0,
+                target=tr["target"], draft=None, tokens=tok, parents=tr["parents"], u=None, ur=None)
+
+
+def _buffers(c):
+    sample = c["mode"] in (SV_MODE_SAMPLE, SV_MODE_TREE_SAMPLE)
+    tree = c["mode"] in (SV_MODE_TREE_GREEDY, SV_MODE_TREE_SAMPLE)
+    B, V = c["B"], c["V"]
+    w = c["k"] if tree else c["k"] + 1
+    ins = dict(target=dev(c["target"], c["dtype"]),
+               draft=dev(c["draft"], c["dtype"]) if c["draft"] is not None else None,
+               tokens=dev(c["tokens"].astype(np.int32)),
+               parents=dev(c["parents"].astype(np.int32)) if c["parents"] is not None else None,
+               u=dev(c["u"]) if c["u"] is not None else None,
+               ur=dev(c["ur"]) if c["ur"] is not None else None)
+    outs = dict(accepted_len=torch.full((B,), -7, dtype=torch.int32, device="cuda"),
+                out_tokens=torch.full((B, w), -7, dtype=torch.int32, device="cuda"),
+                out_nodes=torch.full((B, w), -7, dtype=torch.int32, device="cuda") if tree else None,
+                resid_probs=torch.full((B, V), -7.0, dtype=torch.float32, device="cuda") if sample else None,
+                seq_status=torch.full((B,), -7, dtype=torch.int32, device="cuda"))
+    return ins, outs
+
+
+def _host(outs):
+    return {key: (v.cpu().numpy() if v is not None else None) for key, v in outs.items()}
+
+
+def run_static(c):
+    ins, outs = _buffers(c)
+    cfg = make_config(c["mode"], c["dtype"], c["B"], c["k"], c["V"], c["T"], c["top_k"], c["top_p"])
+    specverify_run_static(cfg, c["B"], ins["target"], ins["draft"], ins["tokens"], ins["parents"], ins["u"],
+                          ins["ur"], outs["accepted_len"], outs["out_tokens"], outs["out_nodes"],
+                          outs["resid_probs"], outs["seq_status"])
+    torch.cuda.synchronize()
+    return _host(outs)
+
+
+def run_context(c):
+    ins, outs = _buffers(c)
+    sv = SpecVerify(mode=c["mode"], dtype=c["dtype"], max_batch=c["B"], k=c["k"], vocab=c["V"],
+                    temperature=c["T"], top_k=c["top_k"], top_p=c["top_p"])
+    from draft_token_verification_softmax_amd import specverify_run
+    specverify_run(sv.ctx, c["B"], ins["target"], ins["draft"], ins["tokens"], ins["parents"], ins["u"],
+                   ins["ur"], outs["accepted_len"], outs["out_tokens"], outs["out_nodes"],
+                   outs["resid_probs"], outs["seq_status"])
+    torch.cuda.synchronize()
+    sv.close()
+    return _host(outs)
+
+
+def _same(a, b, label):
+    for key in KEYS:
+        if a[key] is None:
+            assert b[key] is None, (label, key)
+            continue
+        assert np.array_equal(a[key], b[key]), (label, key)
+        assert not (a[key] == -7).all(), (label, key, "not written")
+
+
+CASES = {
+    "plain sampling, workload 2 shape": lambda s: _chain_case(2, (16, 5)[s], 32000, 5, "bf16", 1.0, 0, 1.0, 61 + s),
+    "top-k 50, V = 128256": lambda s: _chain_case(3, (12, 3)[s], 128256, 8, "bf16", 0.7, 50, 1.0, 62 + s),
+    "nucleus 0.9, V = 152064 fp32": lambda s: _chain_case(5, (8, 2)[s], 152064, 4, "f32", 0.8, 0, 0.9, 63 + s),
+    "greedy chain": lambda s: _greedy_case((32, 5)[s], 32000, 4, 64 + s),
+    "tree greedy": lambda s: _tree_case((8, 3)[s], 60, 128256, "bf16", False, 65 + s),
+    "tree sampling": lambda s: _tree_case((6, 2)[s], 30, 8192, "bf16", True, 66 + s),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_static_entry_point_matches_context_entry_point(name):
+    """Two static calls in a row (the second smaller), each equal bit for
+    bit to the context entry point's output on the same inputs."""
+    for s in (0, 1):
+        c = CASES[name](s)
+        say("no-alloc entry point:", name, "call", s + 1, "B =", c["B"])
+        got = run_static(c)
+        want = run_context(c)
+        _same(got, want, f"{name}, call {s + 1}")
