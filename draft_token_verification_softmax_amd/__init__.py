@@ -28,6 +28,7 @@ SV_STATUS_BAD_TOKEN, SV_STATUS_BAD_PARENT, SV_STATUS_BAD_LOGITS = 1, 2, 4
 SV_MAX_K, SV_MAX_TREE_NODES, SV_MAX_TOP_K, SV_MAX_VOCAB = 64, 1024, 256, 1 << 24
 
 EXPORTED = ("specverify_create", "specverify_check_args", "specverify_run", "specverify_run_static",
+            "specverify_tiling",
             "specverify_destroy", "specverify_profile_events", "specverify_status_string",
             "specverify_workspace_bytes", "specverify_accept_stats", "specverify_tree_mask",
             "specverify_tree_commit")
@@ -80,6 +81,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_run.restype = ctypes.c_int
     lib.specverify_run_static.argtypes = [P(sv_config), i32] + [vp] * 11 + [vp]
     lib.specverify_run_static.restype = ctypes.c_int
+    lib.specverify_tiling.argtypes = [P(sv_config), i32, i32, i32, P(i32)]
+    lib.specverify_tiling.restype = ctypes.c_int
     lib.specverify_destroy.argtypes = [vp]
     lib.specverify_destroy.restype = None
     lib.specverify_profile_events.argtypes = [vp, vp, vp, vp]

@@ -128,6 +128,76 @@ Layout layout(const sv_config* c, const Plan& pl) {
   return L;
 }
 
+// The streaming pass's tiling for `batch` sequences when the streaming kernel
+// has `grid` resident workgroups: its tile mode (the top-k filter needs
+// aligned rows), tiles per row S, logits per tile L (a multiple of kVec),
+// partials per row P.  SV_ERR_SHAPE when it would not fit the workspace the
+// plan sized (never expected; tests/test_abi_cpu.py sweeps shapes for it).
+int tiling(const sv_config* c, const Plan& pl, int32_t batch, int grid, int aligned, int* tile_mode_out,
+           int* S_out, int* L_out, int* P_out) {
+  const size_t es = c->dtype == SV_DTYPE_BF16 ? 2 : 4;
+  // top-k: the certified filter pass takes tiles of one round of loads in
+  // aligned rows of whole groups; other shapes take the exact per-tile pass
+  int tile_mode = pl.tile_mode;
+  const long rows = (long)batch * (pl.rows_t + pl.rows_d);
+  // float32 row sums and argmax of large problems: tiles of 4 (or 2) rounds
+  // of loads, as long as that still fills three quarters of the resident
+  // workgroup slots.  Each tile's fixed work (the float64 rescale and wave
+  // sums, the partials) spreads over more logits, and the kernels after the
+  // pass combine four times fewer partials per row (workload 6: pass 55.0 ->
+  // 48.8 -> 45.5 us for 1, 2, 4 rounds; workload 4: pass 21.0 -> 21.1 us,
+  // tree_final 7.6 -> 6.0 us; the 11 MB of workload 2 are faster with one).
+  // The float64 sums of nucleus rows are bound by their exponentials and
+  // stay at one round.
+  int rounds = 1;
+  if (tile_mode == sv::kModeStatsMix || tile_mode == sv::kModeArgmax) {
+    for (int r = kStatsRoundsMax; r > 1; r >>= 1) {
+      if (4L * rows * ((c->vocab + (long)r * kRound - 1) / ((long)r * kRound)) >= 3L * grid) {
+        rounds = r;
+        break;
+      }
+    }
+  }
+  const int round = tile_mode == sv::kModeTopk ? (int)(sv::kFilterRound * 2 / es) : rounds * kRound;
+  if (tile_mode == sv::kModeTopk && aligned && c->vocab % sv::kVec == 0 &&
+      c->vocab <= (long)sv::kMaxTiles * round)
+    tile_mode = sv::kModeTopkFilter;
+  long S;
+  if (tile_mode == sv::kModeTopk) {
+    // about four tiles per resident workgroup, tiles of at least kMinTile logits
+    S = (4L * grid + rows - 1) / rows;
+    const long smax = (c->vocab + kMinTile - 1) / kMinTile;
+    if (S > smax) S = smax;
+  } else {
+    // one round of loads per lane (kRound logits; 16 KB of bf16, 32 KB of
+    // fp32); rows that need more than kMaxTiles such tiles take several
+    // rounds per tile; problems with fewer than kSmallTiles tiles take
+    // smaller tiles (down to kMinSmall logits)
+    S = (c->vocab + round - 1) / round;
+    if (rows * S < kSmallTiles) {
+      long want = (kSmallTiles + rows - 1) / rows;
+      const long cap = (c->vocab + kMinSmall - 1) / kMinSmall;
+      if (want > cap) want = cap;
+      if (want > S) S = want;
+    }
+  }
+  if (S > sv::kMaxTiles) S = sv::kMaxTiles;
+  if (S < 1) S = 1;
+  int per = (int)((c->vocab + S - 1) / S);
+  if (tile_mode != sv::kModeTopk && per > round) per = (per + round - 1) / round * round;
+  const int Lt = (per + sv::kVec - 1) / sv::kVec * sv::kVec;
+  const int St = (int)((c->vocab + Lt - 1) / Lt);
+  const bool lists = tile_mode == sv::kModeTopk || tile_mode == sv::kModeTopkFilter;
+  const int Pt = tile_mode == sv::kModeTopk ? St : St * (sv::kBlock / 64);
+  // the workspace holds S_max candidate lists and kMaxPartials partials per row
+  if ((lists && St > pl.S_max) || Pt > sv::kMaxPartials || St > sv::kMaxTiles) return SV_ERR_SHAPE;
+  *tile_mode_out = tile_mode;
+  *S_out = St;
+  *L_out = Lt;
+  *P_out = Pt;
+  return SV_OK;
+}
+
 // One call's launches on the current device: the tiling of the streaming
 // pass, the workspace views (ws laid out as L), the launch chain of the mode.
 // Arguments are already checked.  Returns SV_OK, SV_ERR_SHAPE (the tiling
@@ -167,61 +237,9 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
   const bool base16 = ((uintptr_t)target_logits % 16 == 0) &&
                       (!draft_logits || (uintptr_t)draft_logits % 16 == 0);
   p.aligned = (rows16 && base16) ? 1 : 0;
-  // top-k: the certified filter pass takes tiles of one round of loads in
-  // aligned rows of whole groups; other shapes take the exact per-tile pass
-  int tile_mode = pl.tile_mode;
-  const long rows = (long)batch * (pl.rows_t + pl.rows_d);
-  // float32 row sums and argmax of large problems: tiles of 4 (or 2) rounds
-  // of loads, as long as that still fills three quarters of the resident
-  // workgroup slots.  Each tile's fixed work (the float64 rescale and wave
-  // sums, the partials) spreads over more logits, and the kernels after the
-  // pass combine four times fewer partials per row (workload 6: pass 55.0 ->
-  // 48.8 -> 45.5 us for 1, 2, 4 rounds; workload 4: pass 21.0 -> 21.1 us,
-  // tree_final 7.6 -> 6.0 us; the 11 MB of workload 2 are faster with one).
-  // The float64 sums of nucleus rows are bound by their exponentials and
-  // stay at one round.
-  int rounds = 1;
-  if (tile_mode == sv::kModeStatsMix || tile_mode == sv::kModeArgmax) {
-    for (int r = kStatsRoundsMax; r > 1; r >>= 1) {
-      if (4L * rows * ((c->vocab + (long)r * kRound - 1) / ((long)r * kRound)) >= 3L * grid) {
-        rounds = r;
-        break;
-      }
-    }
-  }
-  const int round = tile_mode == sv::kModeTopk ? (int)(sv::kFilterRound * 2 / es) : rounds * kRound;
-  if (tile_mode == sv::kModeTopk && p.aligned && c->vocab % sv::kVec == 0 &&
-      c->vocab <= (long)sv::kMaxTiles * round)
-    tile_mode = sv::kModeTopkFilter;
-  long S;
-  if (tile_mode == sv::kModeTopk) {
-    // about four tiles per resident workgroup, tiles of at least kMinTile logits
-    S = (4L * grid + rows - 1) / rows;
-    const long smax = (c->vocab + kMinTile - 1) / kMinTile;
-    if (S > smax) S = smax;
-  } else {
-    // one round of loads per lane (kRound logits; 16 KB of bf16, 32 KB of
-    // fp32); rows that need more than kMaxTiles such tiles take several
-    // rounds per tile; problems with fewer than kSmallTiles tiles take
-    // smaller tiles (down to kMinSmall logits)
-    S = (c->vocab + round - 1) / round;
-    if (rows * S < kSmallTiles) {
-      long want = (kSmallTiles + rows - 1) / rows;
-      const long cap = (c->vocab + kMinSmall - 1) / kMinSmall;
-      if (want > cap) want = cap;
-      if (want > S) S = want;
-    }
-  }
-  if (S > sv::kMaxTiles) S = sv::kMaxTiles;
-  if (S < 1) S = 1;
-  int per = (int)((c->vocab + S - 1) / S);
-  if (tile_mode != sv::kModeTopk && per > round) per = (per + round - 1) / round * round;
-  p.L = (per + sv::kVec - 1) / sv::kVec * sv::kVec;
-  p.S = (c->vocab + p.L - 1) / p.L;
-  const bool lists = tile_mode == sv::kModeTopk || tile_mode == sv::kModeTopkFilter;
-  p.P = tile_mode == sv::kModeTopk ? p.S : p.S * (sv::kBlock / 64);
-  // the workspace holds S_max candidate lists and kMaxPartials partials per row
-  if ((lists && p.S > pl.S_max) || p.P > sv::kMaxPartials || p.S > sv::kMaxTiles) return SV_ERR_SHAPE;
+  int tile_mode;
+  const int rc = tiling(c, pl, batch, grid, p.aligned, &tile_mode, &p.S, &p.L, &p.P);
+  if (rc != SV_OK) return rc;
   p.grid = grid;
   p.tiles = (sv::TileStat*)(ws + L.tiles);
   p.cand = (uint64_t*)(ws + L.cand);
@@ -470,6 +488,28 @@ int specverify_run_static(const sv_config* cfg, int32_t batch, const void* targe
   return launch_call(&c, pl, L, ws, grid, ev, batch, target_logits, draft_logits, draft_tokens,
                      parents, uniforms, resid_uniforms, accepted_len, out_tokens, out_nodes,
                      resid_probs, seq_status, (hipStream_t)stream);
+}
+
+int specverify_tiling(const sv_config* cfg, int32_t batch, int32_t grid, int32_t aligned, int32_t* out) {
+  if (!out) return SV_ERR_NULL;
+  const int rc = check_config(cfg);
+  if (rc != SV_OK) return rc;
+  if (batch < 1) return SV_ERR_SHAPE;
+  if (batch > cfg->max_batch) return SV_ERR_CAPACITY;
+  if (grid < 1) return SV_ERR_PARAM;
+  const Plan pl = make_plan(cfg);
+  const size_t es = cfg->dtype == SV_DTYPE_BF16 ? 2 : 4;
+  const int al = (aligned && ((size_t)cfg->vocab * es) % 16 == 0) ? 1 : 0;
+  int tm = 0, S = 0, L = 0, P = 0;
+  const int r = tiling(cfg, pl, batch, grid, al, &tm, &S, &L, &P);
+  const bool lists = tm == sv::kModeTopk || tm == sv::kModeTopkFilter;
+  out[0] = tm;
+  out[1] = S;
+  out[2] = L;
+  out[3] = P;
+  out[4] = lists ? pl.S_max : sv::kMaxTiles;
+  out[5] = sv::kMaxPartials;
+  return r;
 }
 
 static_assert(SV_STATS_LEN == sv::kStatsLen && SV_STATS_SPEEDUP_GAMMA1 == sv::kStatsSpeedup1 &&

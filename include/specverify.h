@@ -220,6 +220,19 @@ void specverify_destroy(specverify_ctx* ctx);
 int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_stream_end,
                               void* ev_call_end);
 
+/* Host-only: the streaming pass's tiling that specverify_run would use for
+ * `batch` sequences of cfg when the streaming kernel has `grid` resident
+ * workgroups on the device and the logit tensors start 16-byte aligned
+ * (aligned != 0) or not.  out[6] gets: the tile mode (the library's internal
+ * number), tiles per row S, logits per tile L, partials per row P, and the
+ * workspace's room per row for tiles (of the mode's candidate lists) and for
+ * partials; S * L >= V > (S - 1) * L.  Returns SV_OK, a config or batch
+ * error (SV_ERR_NULL / SHAPE / DTYPE / PARAM / MODE / CAPACITY; grid < 1 is
+ * SV_ERR_PARAM), or SV_ERR_SHAPE when the tiling would not fit the workspace
+ * (specverify_run then refuses the call instead of launching; never
+ * expected).  Makes no HIP call, so tests can sweep shapes without a GPU. */
+int specverify_tiling(const sv_config* cfg, int32_t batch, int32_t grid, int32_t aligned, int32_t* out);
+
 /* Human-readable name of an SV_OK / SV_ERR_* code (static storage). */
 const char* specverify_status_string(int status);
 

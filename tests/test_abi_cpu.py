@@ -5,6 +5,8 @@ import math
 import os
 import re
 
+import numpy as np
+
 import pytest
 
 import draft_token_verification_softmax_amd as svm
@@ -26,7 +28,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = svm.load()
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(svm.EXPORTED) == names
@@ -64,6 +66,59 @@ def test_static_scratch_limit_is_checked_on_the_host():
     assert lib.specverify_run_static(None, 1, *([None] * 11), None) == SV_ERR_NULL
     assert lib.specverify_run_static(ctypes.byref(big), 1, *([None] * 11), None) == SV_ERR_NULL
     assert lib.specverify_run_static(ctypes.byref(big), 513, *args, None) == svm.SV_ERR_CAPACITY
+
+
+def _tiling(cfg, batch, grid, aligned):
+    out = (ctypes.c_int32 * 6)()
+    rc = svm.load().specverify_tiling(ctypes.byref(cfg), batch, grid, aligned, out)
+    return rc, list(out)
+
+
+def test_tiling_fits_the_workspace_over_a_sweep_of_shapes():
+    """The streaming pass's tiling (the host code specverify_run runs before
+    any launch) fits the workspace the context sized, for every mode, dtype,
+    batch, k, vocabulary, top-k, nucleus, device size and alignment of a
+    seeded sweep.  A mismatch between the two once made a top-k tiling
+    write more candidate lists than the workspace held (a GPU memory fault on
+    V = 3000 fp32, B = 8, top_k = 20); now it would be an SV_ERR_SHAPE
+    refusal, and this sweep fails on it."""
+    rng = np.random.default_rng(123)
+    Vs = [1, 7, 8, 9, 100, 2047, 2048, 2049, 3000, 4099, 8192, 8193, 32000, 65536, 128256, 152064,
+          262144, 524288, 1 << 20, 3_000_001, 1 << 24]
+    checked = 0
+    cases = [(SV_MODE_SAMPLE, "f32", 8, 5, 3000, 20, 1.0)]   # the shape of the fault
+    for _ in range(6000):
+        mode = int(rng.choice([SV_MODE_SAMPLE, SV_MODE_GREEDY, SV_MODE_TREE_GREEDY, SV_MODE_TREE_SAMPLE]))
+        dtype = str(rng.choice(["f32", "bf16"]))
+        tree = mode in (SV_MODE_TREE_GREEDY, SV_MODE_TREE_SAMPLE)
+        k = int(rng.choice([1, 2, 60, 200, 1024])) if tree else int(rng.choice([1, 2, 4, 5, 8, 17, 64]))
+        V = int(rng.choice(Vs))
+        top_k = int(rng.choice([0, 0, 1, 7, 20, 50, 64, 65, 256])) if mode == SV_MODE_SAMPLE else 0
+        top_p = float(rng.choice([1.0, 1.0, 0.9, 0.5])) if mode == SV_MODE_SAMPLE else 1.0
+        B = int(rng.choice([1, 2, 3, 8, 16, 64, 256, 1000]))
+        if B * k * V > 1 << 33:
+            B = max(1, (1 << 33) // (k * V))
+        cases.append((mode, dtype, B, k, V, top_k, top_p))
+    for mode, dtype, B, k, V, top_k, top_p in cases:
+        cfg = make_config(mode, dtype, B, k, V, 1.0, top_k, top_p)
+        for grid in (256, 1024, 2048):
+            for aligned in (0, 1):
+                for batch in sorted({1, max(1, B // 3), B}):
+                    rc, (tm, S, L, P, cap_tiles, cap_partials) = _tiling(cfg, batch, grid, aligned)
+                    assert rc == SV_OK, (mode, dtype, B, k, V, top_k, top_p, grid, aligned, batch, rc)
+                    assert L % 8 == 0 and L > 0 and S >= 1
+                    assert S * L >= V > (S - 1) * L, (V, S, L)
+                    assert S <= cap_tiles and P <= cap_partials, (S, cap_tiles, P, cap_partials)
+                    checked += 1
+    assert checked > 10000
+
+
+def test_tiling_rejects_bad_arguments_on_the_host():
+    cfg = make_config(SV_MODE_SAMPLE, "bf16", 4, 5, 32000, 1.0)
+    assert svm.load().specverify_tiling(ctypes.byref(cfg), 1, 256, 1, None) == SV_ERR_NULL
+    assert _tiling(cfg, 0, 256, 1)[0] == SV_ERR_SHAPE
+    assert _tiling(cfg, 5, 256, 1)[0] == svm.SV_ERR_CAPACITY
+    assert _tiling(cfg, 4, 0, 1)[0] == svm.SV_ERR_PARAM
 
 
 def test_config_struct_layout():
