@@ -207,14 +207,16 @@ def _short(name):
 
 def _calls(rows, key_start, key_end):
     """Group library dispatches (in dispatch order) into calls: a call starts
-    at a streaming-kernel dispatch and holds the library kernels up to the
-    next one; the bench's own kernels around the step are left out."""
+    at a streaming-kernel dispatch (other than the second one of a lazy call,
+    which follows its gate kernel) and holds the library kernels up to the
+    next call; the bench's own kernels around the step are left out."""
     rows = [r for r in rows if r["Kernel_Name"].startswith(("k_", "void sv::k_", "sv::k_"))
             and not any(a in r["Kernel_Name"] for a in AUX_KERNELS)]
     rows.sort(key=lambda r: int(r.get("Dispatch_Id", r.get("Correlation_Id", 0))))
     calls, cur = [], None
     for r in rows:
-        if "k_stream" in r["Kernel_Name"]:
+        # a lazy call streams twice: the second streaming launch follows its gate
+        if "k_stream" in r["Kernel_Name"] and not (cur and "k_lazy_gate" in cur[-1]["Kernel_Name"]):
             cur = []
             calls.append(cur)
         if cur is not None:
@@ -384,7 +386,7 @@ def cpu_baseline(config, budget_s=12.0):
 
 # ------------------------------------------------------------------ one workload on the GPU
 
-def measure(config, steps, warmup, hip, with_extras=True):
+def measure(config, steps, warmup, hip, with_extras=True, lazy=False):
     """Time `steps` calls of workload `config` (after `warmup`): wall time
     of plain back-to-back calls (the metric), then the same calls with the
     library's call and streaming-kernel events.  Returns a dict."""
@@ -440,6 +442,8 @@ def measure(config, steps, warmup, hip, with_extras=True):
         mode, rows_t, rows_d = svm.SV_MODE_SAMPLE, k + 1, k
         filt = f"top-k {top_k}" if top_k else (f"top-p {top_p}" if top_p < 1 else "no filter")
         workload = f"chain sampling verification, B={B}, k={k}, V={V}, {dtype} logits, T={T}, {filt}"
+        if lazy:
+            workload += ", lazy row reads (rows after position 0 only where x_0 is accepted)"
         extra = dict(B=B, k=k, V=V, logits_dtype=dtype, T=T, top_k=top_k, top_p=top_p)
         arith = "f64"
 
@@ -455,7 +459,8 @@ def measure(config, steps, warmup, hip, with_extras=True):
     copies = [inputs] + [{n: t.clone() for n, t in inputs.items()} for _ in range(ncopies - 1)]
 
     sv = svm.SpecVerify(mode=mode, dtype=dtype, max_batch=B, k=k, vocab=V,
-                        temperature=T, top_k=top_k, top_p=top_p)
+                        temperature=T, top_k=top_k, top_p=top_p,
+                        options=svm.SV_OPT_LAZY_ROWS if lazy else 0)
     acc = torch.empty(B, dtype=torch.int32, device=dev)
     out_w = N if tree else k + 1
     out_tok = torch.empty(B, out_w, dtype=torch.int32, device=dev)
@@ -500,11 +505,38 @@ def measure(config, steps, warmup, hip, with_extras=True):
         f"kernel end; p10 {np.percentile(cms, 10) * 1e3:.2f}, p90 {np.percentile(cms, 90) * 1e3:.2f}), "
         f"{achieved:.1f} GB/s = {achieved / PEAK_HBM_GBS:.3f} of peak; streaming kernel {kern_us:.2f} us, "
         f"{stream_ach:.1f} GB/s")
+    # floors for the same call: a bare read of the same logits (torch.sum over
+    # each logit tensor of the same rotating copies: every byte read once),
+    # and one tiny kernel per launch back to back on the stream
+    small = torch.zeros(1, device=dev)
+
+    def reads(i):
+        c = copies[i % ncopies]
+        c["target"].sum()
+        if c.get("draft") is not None:
+            c["draft"].sum()
+
+    fe = hip.create(4)
+    for i in range(warmup):
+        reads(i)
+    torch.cuda.synchronize()
+    hip.record(fe[0], stream)
+    for i in range(steps):
+        reads(i)
+    hip.record(fe[1], stream)
+    for i in range(steps):
+        small.add_(1.0)
+    hip.record(fe[2], stream)
+    torch.cuda.synchronize()
+    read_us = hip.elapsed_ms(fe[0], fe[1]) * 1e3 / steps
+    tiny_us = hip.elapsed_ms(fe[1], fe[2]) * 1e3 / steps
+    hip.destroy(fe)
     res = dict(config=config, workload=workload, extra=extra, arith=arith, B=B, rows_per_call=B * rows_t,
                logit_bytes=logit_bytes, alg_bytes=alg_bytes, ncopies=ncopies, wall=wall, step_us=step_us,
                call_us=call_us, call_us_p10=float(np.percentile(cms, 10)) * 1e3,
                call_us_p90=float(np.percentile(cms, 90)) * 1e3, kern_us=kern_us, achieved=achieved,
-               stream_achieved=stream_ach, call_traffic=call_traffic, stream_traffic=stream_traffic)
+               stream_achieved=stream_ach, call_traffic=call_traffic, stream_traffic=stream_traffic,
+               read_us=read_us, tiny_us=tiny_us)
 
     if with_extras:
         # the kernels around the step, on this workload's outputs: acceptance
@@ -560,6 +592,8 @@ def main():
     ap.add_argument("--also", default="2,3,4",
                     help="other workloads whose call-level roofline goes into extras (comma list, '' for none)")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--lazy", action="store_true",
+                    help="plain sampling with lazy row reads (SV_OPT_LAZY_ROWS, the rejection fast path)")
     ap.add_argument("--copy-calibrate", type=int, default=0, metavar="MIB",
                     help="only copy MIB MiB device-to-device three times (scale reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -605,7 +639,7 @@ def main():
     svm.load()
     torch.cuda.set_device(0)
     hip = HipEvents()
-    m = measure(args.config, args.steps, args.warmup, hip)
+    m = measure(args.config, args.steps, args.warmup, hip, lazy=args.lazy)
     value = m["rows_per_call"] * args.steps / m["wall"]
     result = {
         "metric": METRIC, "value": value, "unit": "rows/s", "n_gpus": 1, "steps": args.steps,
@@ -623,6 +657,11 @@ def main():
             "stream_kernel": {"name": "k_stream (the pass that reads every logit)", "us": m["kern_us"],
                               "achieved": m["stream_achieved"], "frac": m["stream_achieved"] / PEAK_HBM_GBS,
                               "traffic": m["stream_traffic"], "bytes_algorithmic": m["logit_bytes"]},
+            "floor": {"bare_read_us": m["read_us"], "bare_read_frac": m["logit_bytes"] / (m["read_us"] * 1e-6) / 1e9
+                      / PEAK_HBM_GBS, "tiny_kernel_us": m["tiny_us"],
+                      "note": "bare read: torch.sum over each logit tensor of the same rotating copies "
+                              "(HIP events, mean per call); tiny kernel: a one-element add per launch, "
+                              "back to back"},
         },
     }
     extras = m.get("extras", {})
@@ -634,7 +673,8 @@ def main():
         others.append({"workload": o["workload"], "step_us": o["step_us"], "call_us": o["call_us"],
                        "bytes_algorithmic": o["alg_bytes"], "achieved_GBps": o["achieved"],
                        "frac": o["achieved"] / PEAK_HBM_GBS, "stream_us": o["kern_us"],
-                       "stream_frac": o["stream_achieved"] / PEAK_HBM_GBS, "traffic": o["call_traffic"]})
+                       "stream_frac": o["stream_achieved"] / PEAK_HBM_GBS, "traffic": o["call_traffic"],
+                       "bare_read_us": o["read_us"], "tiny_kernel_us": o["tiny_us"]})
     if others:
         extras["other_workloads"] = others
     result["extras"] = extras

@@ -25,6 +25,7 @@ SV_OK, SV_ERR_NULL, SV_ERR_SHAPE, SV_ERR_DTYPE, SV_ERR_PARAM = 0, -1, -2, -3, -4
 SV_ERR_CAPACITY, SV_ERR_HIP, SV_ERR_MODE, SV_ERR_SCRATCH = -5, -6, -7, -8
 SV_STATIC_SCRATCH_BYTES = 64 << 20
 SV_STATUS_BAD_TOKEN, SV_STATUS_BAD_PARENT, SV_STATUS_BAD_LOGITS = 1, 2, 4
+SV_OPT_LAZY_ROWS = 1
 SV_MAX_K, SV_MAX_TREE_NODES, SV_MAX_TOP_K, SV_MAX_VOCAB = 64, 1024, 256, 1 << 24
 
 EXPORTED = ("specverify_create", "specverify_check_args", "specverify_run", "specverify_run_static",
@@ -43,7 +44,7 @@ SV_STATS_SPEEDUP_GAMMA1, SV_STATS_LEN = 11, 23
 class sv_config(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("max_batch", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("vocab", ctypes.c_int32), ("temperature", ctypes.c_double),
+                ("vocab", ctypes.c_int32), ("options", ctypes.c_int32), ("temperature", ctypes.c_double),
                 ("top_k", ctypes.c_int32), ("top_p", ctypes.c_double)]
 
 
@@ -101,11 +102,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
-def make_config(mode, dtype, max_batch, k, vocab, temperature=1.0, top_k=0, top_p=1.0) -> sv_config:
+def make_config(mode, dtype, max_batch, k, vocab, temperature=1.0, top_k=0, top_p=1.0,
+                options=0) -> sv_config:
     if isinstance(dtype, str):
         dtype = {"f32": SV_DTYPE_F32, "float32": SV_DTYPE_F32, "bf16": SV_DTYPE_BF16,
                  "bfloat16": SV_DTYPE_BF16}[dtype]
-    return sv_config(int(mode), int(dtype), int(max_batch), int(k), int(vocab),
+    return sv_config(int(mode), int(dtype), int(max_batch), int(k), int(vocab), int(options),
                      float(temperature), int(top_k), float(top_p))
 
 
@@ -258,9 +260,9 @@ class SpecVerify:
     """Owns one context; checks tensors and allocates the outputs of a call."""
 
     def __init__(self, mode=SV_MODE_SAMPLE, dtype="bf16", max_batch=1, k=1, vocab=2,
-                 temperature=1.0, top_k=0, top_p=1.0, device=None):
+                 temperature=1.0, top_k=0, top_p=1.0, device=None, options=0):
         import torch
-        self.cfg = make_config(mode, dtype, max_batch, k, vocab, temperature, top_k, top_p)
+        self.cfg = make_config(mode, dtype, max_batch, k, vocab, temperature, top_k, top_p, options)
         self.device = torch.cuda.current_device() if device is None else int(device)
         self.ctx = specverify_create(self.cfg, self.device)
 

@@ -50,8 +50,10 @@ int check_config(const sv_config* c) {
     if (c->top_k > SV_MAX_TOP_K && c->top_k < c->vocab) return SV_ERR_PARAM;
     if (!(c->top_p > 0.0 && c->top_p <= 1.0)) return SV_ERR_PARAM;
   }
-  // tree sampling: temperature only (no top-k or top-p)
-  if (c->mode == SV_MODE_TREE_SAMPLE && ((c->top_k > 0 && c->top_k < c->vocab) || c->top_p < 1.0))
+  if (c->options & ~SV_OPT_LAZY_ROWS) return SV_ERR_PARAM;
+  // lazy row reads: plain sampling only
+  if ((c->options & SV_OPT_LAZY_ROWS) &&
+      (c->mode != SV_MODE_SAMPLE || (c->top_k > 0 && c->top_k < c->vocab) || c->top_p < 1.0))
     return SV_ERR_PARAM;
   return SV_OK;
 }
@@ -60,11 +62,16 @@ Plan make_plan(const sv_config* c) {
   Plan p;
   const bool sample = c->mode == SV_MODE_SAMPLE;
   const bool tsample = c->mode == SV_MODE_TREE_SAMPLE;
-  p.top_k = (sample && c->top_k > 0 && c->top_k < c->vocab) ? c->top_k : 0;
-  p.top_p = (sample && c->top_p < 1.0) ? c->top_p : 1.0;
+  p.top_k = ((sample || tsample) && c->top_k > 0 && c->top_k < c->vocab) ? c->top_k : 0;
+  p.top_p = ((sample || tsample) && c->top_p < 1.0) ? c->top_p : 1.0;
   if (c->mode == SV_MODE_GREEDY) { p.filt = sv::kFiltGreedy; p.tile_mode = sv::kModeArgmax; }
   else if (c->mode == SV_MODE_TREE_GREEDY) { p.filt = sv::kFiltTree; p.tile_mode = sv::kModeArgmax; }
-  else if (tsample) { p.filt = sv::kFiltTreeSample; p.tile_mode = sv::kModeStatsMix; }
+  else if (tsample) {
+    // tree sampling: the adjusted rows come from the top-k merge or the
+    // nucleus cut when a filter is set, else from the row sums
+    p.filt = sv::kFiltTreeSample;
+    p.tile_mode = p.top_k > 0 ? sv::kModeTopk : (p.top_p < 1.0 ? sv::kModeStats64 : sv::kModeStatsMix);
+  }
   else if (p.top_k > 0) { p.filt = sv::kFiltTopk; p.tile_mode = sv::kModeTopk; }
   else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeStats64; }
   else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStatsMix; }
@@ -91,7 +98,7 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, row_lx, seq, spart, wpart, tpart, tview;
+  size_t tiles, cand, nuc, row_lx, seq, spart, wpart, tpart, tview, tcut, go;
   size_t k_idx, k_e, k_cnt, k_norm, k_bad, k_px, total;
 };
 
@@ -108,7 +115,8 @@ Layout layout(const sv_config* c, const Plan& pl) {
   };
   L.tiles = take(rows * (size_t)sv::kMaxPartials * sizeof(sv::TileStat));
   L.cand = take(pl.top_k > 0 ? rows * (size_t)pl.S_max * (size_t)pl.cand_w * sizeof(uint64_t) : 0);
-  L.nuc = take(pl.filt == sv::kFiltTopp ? rows * sizeof(sv::RowNuc) : 0);
+  const bool tfilt = pl.filt == sv::kFiltTreeSample && (pl.top_k > 0 || pl.top_p < 1.0);
+  L.nuc = take(pl.filt == sv::kFiltTopp || tfilt ? rows * sizeof(sv::RowNuc) : 0);
   const bool sampled = pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample;
   L.row_lx = take(sampled ? rows * sizeof(float) : 0);
   L.seq = take(sampled ? B * sizeof(sv::SeqState) : 0);
@@ -118,6 +126,8 @@ Layout layout(const sv_config* c, const Plan& pl) {
   L.tpart = take(pl.filt == sv::kFiltTreeSample
                      ? B * (size_t)sv::kTreePasses * (size_t)c->k * (size_t)pl.S2_max * sizeof(double) : 0);
   L.tview = take(pl.filt == sv::kFiltTreeSample ? B * (size_t)c->k * 4 * sizeof(double) : 0);
+  L.tcut = take(tfilt ? B * (size_t)c->k * 2 * sizeof(uint64_t) : 0);
+  L.go = take((c->options & SV_OPT_LAZY_ROWS) ? B * sizeof(int32_t) : 0);
   L.k_idx = take(rows * K * sizeof(int32_t));
   L.k_e = take(rows * K * sizeof(double));
   L.k_cnt = take(K ? rows * sizeof(int32_t) : 0);
@@ -251,6 +261,8 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
   p.wpart = (double*)(ws + L.wpart);
   p.tpart = (double*)(ws + L.tpart);
   p.tview = (double*)(ws + L.tview);
+  p.tcut = (uint64_t*)(ws + L.tcut);
+  p.tfilt = (pl.filt == sv::kFiltTreeSample && (pl.top_k > 0 || pl.top_p < 1.0)) ? 1 : 0;
   p.keep_w = (pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample) &&
              (size_t)c->max_batch * pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes ? 1 : 0;
   p.S2 = pl.S2_max;
@@ -260,9 +272,23 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
   p.k_norm = (double*)(ws + L.k_norm);
   p.k_bad = (int32_t*)(ws + L.k_bad);
   p.k_px = (double*)(ws + L.k_px);
+  p.go = (int32_t*)(ws + L.go);
 
   const int bf16 = c->dtype == SV_DTYPE_BF16;
-  hipError_t e = sv::launch_stream(p, tile_mode, bf16, st, ev[0], ev[1]);
+  hipError_t e;
+  if (c->options & SV_OPT_LAZY_ROWS) {
+    // stage 1: row pair 0 and the test of x_0; stage 2: the other rows of
+    // the sequences that passed it (the same tiling, so the partials keep
+    // the layout the finishing kernels read)
+    p.lazy = 1;
+    e = sv::launch_stream(p, tile_mode, bf16, st, ev[0], ev[1]);
+    if (e == hipSuccess) e = sv::launch_lazy_gate(p, bf16, st);
+    p.lazy = 2;
+    if (e == hipSuccess) e = sv::launch_stream(p, tile_mode, bf16, st);
+    p.lazy = 3;   // the finishing kernels: rows after position 0 only where go
+  } else {
+    e = sv::launch_stream(p, tile_mode, bf16, st, ev[0], ev[1]);
+  }
   if (e == hipSuccess) e = sv::launch_finish(p, pl.filt, bf16, st, ev[2]);
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }

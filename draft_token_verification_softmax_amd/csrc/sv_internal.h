@@ -115,11 +115,18 @@ struct Params {
                 // the argmax and sum passes, S for the top-k pass
   int aligned;  // every row starts 16-byte aligned
   int grid;     // workgroups of the streaming launch (resident capacity)
+  // lazy row reads (plain sampling, opt-in): 0 off; 1 the streaming launch
+  // of stage 1 (row pair 0 of every sequence); 2 that of stage 2 (rows 1..
+  // of the sequences whose first drafted token was accepted); 3 the
+  // finishing kernels of a lazy call (rows after position 0 were read only
+  // where go is set)
+  int lazy;
+  int32_t* go;       // [B] lazy: 1 if position 0 was accepted (stage 2 reads the rest)
   // workspace
   TileStat* tiles;   // [rows][P]
   uint64_t* cand;    // [rows][S][cand_w] (top-k): each tile's candidate list
   int cand_w;        // candidate slots per tile
-  RowNuc* nuc;       // [rows] (top-p)
+  RowNuc* nuc;       // [rows] (top-p; tree sampling with top-k or top-p: every row)
   float* row_lx;     // [rows] logit of the drafted token a row's accept test reads
                      // (written by the tile holding it; sampling modes)
   // sampling: state handed from k_resid_s to k_resid_final
@@ -131,6 +138,8 @@ struct Params {
   int tree;          // tree modes: rows have no single drafted token to record
   double* tpart;     // tree sampling: [B][kTreePasses][N][S2] residual masses per segment
   double* tview;     // tree sampling: [B][N][4] row views (-M c64, 1/Z of target, draft) of nodes with children
+  uint64_t* tcut;    // tree sampling with top-k / top-p: [B][N][2] cut keys (target, draft) of nodes with children
+  int tfilt;         // tree sampling with top-k or top-p: row views come from RowNuc (nuc, every row)
   int S2;            // residual segments per sequence (kResidSeg logits each)
   // top-k: each row's kept set, rank order
   int32_t* k_idx;    // [rows][top_k]
@@ -152,5 +161,7 @@ hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st,
 // Workgroups of the streaming kernel for `mode` one CU keeps resident.
 int stream_blocks_per_cu(int mode, int bf16);
 hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st, hipEvent_t ev_end = nullptr);
+// Lazy row reads: the accept test of position 0 per sequence (after stage 1).
+hipError_t launch_lazy_gate(const Params& p, int bf16, hipStream_t st);
 
 }  // namespace sv

@@ -2055,6 +2055,15 @@ DEV void merge_row_block(const Params& p, const int grow) {
     p.k_norm[grow] = norm;
     p.k_bad[grow] = bad ? 1 : 0;
     p.k_px[grow] = sh_px;
+    if (p.tfilt) {
+      // tree sampling reads the adjusted row as a view: v is kept iff its
+      // packed key ranks at or above the last kept one
+      RowNuc nu;
+      nu.Z = Z; nu.N = norm; nu.M = v0;
+      nu.cut = (!bad && kept > 0) ? top[kept - 1] : 0ull;
+      nu.ok = (!bad && kept > 0) ? 1 : 0;
+      p.nuc[grow] = nu;
+    }
   }
   __syncthreads();
 }
@@ -2218,11 +2227,21 @@ DEV bool merge_row_wave(const Params& p, int grow, uint64_t* lst, int x) {
   }
   const uint64_t hit = __ballot(idx >= 0 && idx == x && lane < kept);
   const double px = hit ? read_lane(e, __ffsll((unsigned long long)hit) - 1) / norm : 0.0;
+  // tree sampling: the row as a view (kept iff the packed key is at least
+  // the smallest kept one; the kept lanes are 0..kept-1)
+  const uint64_t cut = p.tfilt ? wave_min_t(lane < kept ? key_l : ~0ull) : 0ull;
   if (lane == 0) {
     p.k_cnt[grow] = kept;
     p.k_norm[grow] = norm;
     p.k_bad[grow] = bad ? 1 : 0;
     p.k_px[grow] = px;
+    if (p.tfilt) {
+      RowNuc nu;
+      nu.Z = Z; nu.N = norm; nu.M = v0;
+      nu.cut = (!bad && kept > 0) ? cut : 0ull;
+      nu.ok = (!bad && kept > 0) ? 1 : 0;
+      p.nuc[grow] = nu;
+    }
   }
   return true;
 }
@@ -2529,9 +2548,12 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   if (tid < nrows) vlx[tid] = lx;
   const int xj = tid < k ? xj_l : 0;
   const float uj = tid < k ? uj_l : 0.f;
+  // a lazy call read the rows after position 0 only where x_0 was accepted
+  const bool all_read = p.lazy != 3 || p.go[b] != 0;
   exp2_table_store(tab, tv);
   int mybad = 0;
-  for (int r = tid; r < nrows; r += kBlock) mybad |= vbad[r];
+  for (int r = tid; r < nrows; r += kBlock)
+    if (all_read || r == 0 || r == p.rows_t) mybad |= vbad[r];
   internal = __syncthreads_or(internal);
   if (__syncthreads_or(mybad)) {
     if (seg == 0) {
@@ -2759,13 +2781,31 @@ __global__ __launch_bounds__(kBlock) void k_resid_final(Params p) {
 // -M * cs and 1 / Z from the row partials; sbad[0..1] their bad flags.
 // Every thread calls it; the results are in LDS after the call.  (Four
 // partials per lane, as in the residual passes, so both see the same bits.)
-DEV void tree_views(const Params& p, int b, int u, double cs, double* sv, int* sbad) {
-  combine_rows<true, 4>(p, 2, [&](int r) { return r == 0 ? trow(p, b, u) : drow(p, b, u); },
-                        [&](int r, float M, int, double Z, int bad) {
-                          sv[2 * r] = -(double)M * cs;
-                          sv[2 * r + 1] = 1.0 / Z;
-                          sbad[r] = bad;
-                        });
+// With top-k or top-p (p.tfilt) every row's view comes from its RowNuc (the
+// row max M, the kept mass N, the cut key): p'(v) = 2^((l - M) c) / N on the
+// kept set.  scut[0..1] get the cut keys (0: no cut).
+DEV void nuc_view(const Params& p, int grow, double cs, double* nmc, double* inv, uint64_t* cut, int* bad) {
+  const RowNuc nu = p.nuc[grow];
+  *nmc = -(double)nu.M * cs;
+  *inv = 1.0 / nu.N;
+  *cut = nu.cut;
+  *bad = nu.ok != 1;
+}
+DEV void tree_views(const Params& p, int b, int u, double cs, double* sv, int* sbad, uint64_t* scut) {
+  if (p.tfilt) {
+    if (threadIdx.x < 2) {
+      const int r = threadIdx.x;
+      nuc_view(p, r == 0 ? trow(p, b, u) : drow(p, b, u), cs, &sv[2 * r], &sv[2 * r + 1], &scut[r], &sbad[r]);
+    }
+  } else {
+    combine_rows<true, 4>(p, 2, [&](int r) { return r == 0 ? trow(p, b, u) : drow(p, b, u); },
+                          [&](int r, float M, int, double Z, int bad) {
+                            sv[2 * r] = -(double)M * cs;
+                            sv[2 * r + 1] = 1.0 / Z;
+                            scut[r] = 0ull;
+                            sbad[r] = bad;
+                          });
+  }
   __syncthreads();
 }
 
@@ -2810,6 +2850,7 @@ template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
   __shared__ int nch[kTreeMax], lst[kTreeMax];
   __shared__ double vv[kPassBatch][4];
+  __shared__ uint64_t vc[kPassBatch][2];
   __shared__ double cn[kPassBatch];
   __shared__ double red[kPassBatch][kWaves];
   __shared__ double tab[kExpTab];
@@ -2844,18 +2885,34 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
       if (p.aligned && nv == kVec) { gp[q].load(rp); gq[q].load(rq); }
       else { gp[q].load_part(rp, nv); gq[q].load_part(rq, nv); }
     }
-    combine_rows<true, 4>(p, 2 * nbl,
-                          [&](int r) { return r < nbl ? trow(p, b, lst[l0 + r]) : drow(p, b, lst[l0 + r - nbl]); },
-                          [&](int r, float M, int, double Z, int) {
-                            const int l = r < nbl ? r : r - nbl, o = r < nbl ? 0 : 2;
-                            vv[l][o] = -(double)M * cs;
-                            vv[l][o + 1] = 1.0 / Z;
-                            // pass 0 covers every node with children: the walk reads its views here
-                            if (m == 0 && seg == 0) {
-                              p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o] = -(double)M * cs;
-                              p.tview[((size_t)b * N + lst[l0 + l]) * 4 + o + 1] = 1.0 / Z;
-                            }
-                          });
+    // the batch's row views; pass 0 covers every node with children, and the
+    // walk reads their views from it
+    auto put = [&](int r, double nmc, double inv, uint64_t cut) {
+      const int l = r < nbl ? r : r - nbl, o = r < nbl ? 0 : 2;
+      vv[l][o] = nmc;
+      vv[l][o + 1] = inv;
+      vc[l][o >> 1] = cut;
+      if (m == 0 && seg == 0) {
+        const size_t at = (size_t)b * N + lst[l0 + l];
+        p.tview[at * 4 + o] = nmc;
+        p.tview[at * 4 + o + 1] = inv;
+        if (p.tfilt) p.tcut[at * 2 + (o >> 1)] = cut;
+      }
+    };
+    if (p.tfilt) {
+      if (tid < 2 * nbl) {
+        const int r = tid;
+        double nmc, inv;
+        uint64_t cut;
+        int bad;
+        nuc_view(p, r < nbl ? trow(p, b, lst[l0 + r]) : drow(p, b, lst[l0 + r - nbl]), cs, &nmc, &inv, &cut, &bad);
+        put(r, nmc, inv, cut);
+      }
+    } else {
+      combine_rows<true, 4>(p, 2 * nbl,
+                            [&](int r) { return r < nbl ? trow(p, b, lst[l0 + r]) : drow(p, b, lst[l0 + r - nbl]); },
+                            [&](int r, float M, int, double Z, int) { put(r, -(double)M * cs, 1.0 / Z, 0ull); });
+    }
     // states after m rejections (one wave per node): F of each earlier pass
     // j at u is its segment sums in a fixed order (lane l adds segments l,
     // l + 64, ...; then the wave's fixed-order sum), every pass's loads
@@ -2886,8 +2943,8 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
 #pragma unroll
     for (int q = 0; q < kPassBatch; ++q) {
       const int l = q < nbl ? q : 0;
-      const RowView pr{nullptr, vv[l][0], vv[l][1], 0ull};
-      const RowView qr{nullptr, vv[l][2], vv[l][3] * cn[l], 0ull};
+      const RowView pr{nullptr, vv[l][0], vv[l][1], vc[l][0]};
+      const RowView qr{nullptr, vv[l][2], vv[l][3] * cn[l], vc[l][1]};
       float lp[kVec], lq[kVec];
       gp[q].opaque().values(lp);
       gq[q].opaque().values(lq);
@@ -2921,8 +2978,10 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
   __shared__ double tab[kExpTab];
   __shared__ double sv[4];
   __shared__ int sbad[2];
+  __shared__ uint64_t scut[2];
   __shared__ int wsum[kWaves];
   __shared__ double vw[kTreeMax][4];
+  __shared__ uint64_t vcw[kTreeMax][2];
   __shared__ double Fv[kTreePasses][kTreeMax];
   __shared__ int pr_l[kTreePasses * kTreeMax];
   const int b = blockIdx.x, N = p.k, V = p.V, tid = threadIdx.x;
@@ -2961,6 +3020,10 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
     const int u = i >> 2;
     vw[u][i & 3] = nch[u] > 0 ? p.tview[((size_t)b * N + u) * 4 + (i & 3)] : 0.0;
   }
+  for (int i = tid; i < N * 2; i += kBlock) {
+    const int u = i >> 1;
+    vcw[u][i & 1] = (p.tfilt && nch[u] > 0) ? p.tcut[((size_t)b * N + u) * 2 + (i & 1)] : 0ull;
+  }
   const int passes = N - 1 < kTreePasses ? N - 1 : kTreePasses;
   const int npairs = block_list(passes * N, [&](int k) { return nch[k % N] > k / N; }, pr_l, wsum);
   constexpr int kFBatch = 8;
@@ -2984,8 +3047,16 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
   }
   // rows: every target row, and the draft row of every node with a child
   // (validity only: a NaN partial or an infinite maximum; no row sums)
-  combine_rows<false>(p, 2 * N, [&](int r) { return r < N ? trow(p, b, r) : drow(p, b, r - N); },
-                      [&](int r, float, int, double, int bad) { rbad[r] = (unsigned char)bad; });
+  if (p.tfilt) {
+    // with top-k or top-p the filter kernel judged each row (NaN / +inf in
+    // any part, or no finite entry kept); the top-k filter pass's partials
+    // carry bounds, not row maxima, so they cannot
+    for (int r = tid; r < 2 * N; r += kBlock)
+      rbad[r] = p.nuc[r < N ? trow(p, b, r) : drow(p, b, r - N)].ok != 1 ? 1 : 0;
+  } else {
+    combine_rows<false>(p, 2 * N, [&](int r) { return r < N ? trow(p, b, r) : drow(p, b, r - N); },
+                        [&](int r, float, int, double, int bad) { rbad[r] = (unsigned char)bad; });
+  }
   badpar = __syncthreads_or(badpar);
   int mybad = 0;
   for (int i = tid; i < N; i += kBlock) mybad |= rbad[i] | (nch[i] > 0 ? rbad[N + i] : 0);
@@ -3013,8 +3084,10 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
       if (x < 0 || x >= V) {
         st |= 1;
       } else {
-        const double pa = exp2_64(fma((double)lpx[ch], cs, vc[0]), tab) * vc[1];
-        const double qa = exp2_64(fma((double)lqx[ch], cs, vc[2]), tab) * vc[3];
+        const RowView vpa{nullptr, vc[0], vc[1], vcw[cur][0]};
+        const RowView vqa{nullptr, vc[2], vc[3], vcw[cur][1]};
+        const double pa = prob_from(vpa, cs, tab, lpx[ch], x);
+        const double qa = prob_from(vqa, cs, tab, lqx[ch], x);
         const double dd = pa - c * qa;
         const double a = (dd > 0.0 ? dd : 0.0) / D;
         acc = qa > 0.0 ? ((double)uu[ch] < fmin(1.0, a / qa)) : (a > 0.0);
@@ -3026,8 +3099,8 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
         F = Fv[j][cur];
       } else {
         const double cn = c + D;
-        const RowView pr{row_ptr<T>(p, trow(p, b, cur)), vc[0], vc[1], 0ull};
-        const RowView qr{row_ptr<T>(p, drow(p, b, cur)), vc[2], vc[3] * cn, 0ull};
+        const RowView pr{row_ptr<T>(p, trow(p, b, cur)), vc[0], vc[1], vcw[cur][0]};
+        const RowView qr{row_ptr<T>(p, drow(p, b, cur)), vc[2], vc[3] * cn, vcw[cur][1]};
         double t = 0.0;
         for (int c0 = 0; c0 < V; c0 += kResidSeg) {
           double w[kVec];
@@ -3049,14 +3122,14 @@ __global__ __launch_bounds__(kBlock) void k_tsample_walk(Params p) {
     if (i != n) ot[i] = i < n ? tok[path[i + 1]] : -1;
     if (p.out_nodes) p.out_nodes[(size_t)b * p.out_w + i] = i <= n ? path[i] : -1;
   }
-  tree_views(p, b, cur, cs, sv, sbad);
+  tree_views(p, b, cur, cs, sv, sbad, scut);
   if (tid == 0) {
     p.acc_len[b] = n;
     const int status = st | (badpar ? 2 : 0);
     if (p.seq_status) p.seq_status[b] = status;
     SeqState ss;
-    ss.nmc_p = sv[0]; ss.inv_p = sv[1]; ss.cut_p = 0ull;
-    ss.nmc_q = sv[2]; ss.inv_q = sv[3] * c; ss.cut_q = 0ull;
+    ss.nmc_p = sv[0]; ss.inv_p = sv[1]; ss.cut_p = scut[0];
+    ss.nmc_q = sv[2]; ss.inv_q = sv[3] * c; ss.cut_q = scut[1];
     ss.n = n; ss.st = status; ss.node = cur; ss.hasq = c > 0.0;
     p.seq[b] = ss;
   }
@@ -3086,6 +3159,43 @@ __global__ __launch_bounds__(kBlock) void k_tsample_mass(Params p) {
   if (tid == 0) p.spart[(size_t)b * p.S2 + seg] = tot;
 }
 
+// ================================================================== lazy row reads
+//
+// The accept test of x_0 per sequence once row pair 0 has been streamed
+// (the same row views and test as k_resid_s, so both take the same
+// decision): go[b] = 1 when x_0 is accepted, and stage 2 then reads the
+// sequence's other rows.  One wave per sequence.
+template <typename T>
+__global__ __launch_bounds__(kBlock) void k_lazy_gate(Params p) {
+  __shared__ double v[2][2];
+  __shared__ int vbad[2];
+  __shared__ double tab[kExpTab];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const double cs = kExpScale * kLog2e / p.T;
+  const double tv = exp2_table_fetch();
+  const int x = p.tokens[(size_t)b * p.k];
+  const float u = p.u[(size_t)b * p.k];
+  const float lt = p.row_lx[trow(p, b, 0)], ld = p.row_lx[drow(p, b, 0)];
+  combine_rows<true, 4>(p, 2, [&](int r) { return r == 0 ? trow(p, b, 0) : drow(p, b, 0); },
+                        [&](int r, float M, int, double Z, int bad) {
+                          v[r][0] = -(double)M * cs;
+                          v[r][1] = 1.0 / Z;
+                          vbad[r] = bad;
+                        });
+  exp2_table_store(tab, tv);
+  if (tid == 0) {
+    bool acc = false;
+    if (!vbad[0] && !vbad[1] && x >= 0 && x < p.V) {
+      const RowView vt{nullptr, v[0][0], v[0][1], 0ull};
+      const RowView vd{nullptr, v[1][0], v[1][1], 0ull};
+      const double a = prob_from(vt, cs, tab, lt, x);
+      const double q = prob_from(vd, cs, tab, ld, x);
+      acc = q > 0.0 ? ((double)u < fmin(1.0, a / q)) : (a > 0.0);
+    }
+    p.go[b] = acc ? 1 : 0;
+  }
+}
+
 // ================================================================== stream kernel
 
 // One workgroup per tile; the host picks about four tiles per resident
@@ -3093,8 +3203,20 @@ __global__ __launch_bounds__(kBlock) void k_tsample_mass(Params p) {
 template <typename T, int MODE>
 __global__ __launch_bounds__(kBlock) void k_stream(Params p) {
   const int tile = blockIdx.x;
-  const int grow = tile / p.S;
-  const int seg = tile - grow * p.S;
+  const int idx = tile / p.S;
+  const int seg = tile - idx * p.S;
+  int grow = idx;
+  if (p.lazy == 1) {
+    // lazy stage 1: row pair 0 of every sequence (targets, then drafts)
+    grow = idx < p.B ? trow(p, idx, 0) : drow(p, idx - p.B, 0);
+  } else if (p.lazy == 2) {
+    // lazy stage 2: target rows 1..k and draft rows 1..k-1 of each sequence,
+    // read only where x_0 was accepted
+    const int per = 2 * p.k - 1;
+    const int b = idx / per, r = idx - b * per;
+    if (p.go[b] == 0) return;
+    grow = r < p.k ? trow(p, b, r + 1) : drow(p, b, r - p.k + 1);
+  }
   const T* row = row_ptr<T>(p, grow);
   const int start = seg * p.L;
   const int end = min(start + p.L, p.V);
@@ -3704,7 +3826,9 @@ int stream_blocks_per_cu(int mode, int bf16) {
 template <typename T>
 static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hipEvent_t e0,
                                   hipEvent_t e1) {
-  const unsigned grid = (unsigned)((long)p.B * (p.rows_t + p.rows_d) * p.S);
+  const long rows = p.lazy == 1 ? 2L * p.B : p.lazy == 2 ? (long)p.B * (2 * p.k - 1)
+                                                         : (long)p.B * (p.rows_t + p.rows_d);
+  const unsigned grid = (unsigned)(rows * p.S);
   const dim3 block(kBlock);
   if (mode == kModeStats64)
     hipExtLaunchKernelGGL((k_stream<T, kModeStats64>), dim3(grid), block, 0, st, e0, e1, 0, p);
@@ -3749,6 +3873,16 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st, hip
       run(true, k_resid_final<T, kFiltTopp>, (p.resid_probs || p.keep_w) ? gs : gb1, p);
       break;
     case kFiltTreeSample: {
+      // with top-k or top-p: every row's adjusted view first
+      if (p.top_k > 0) {
+        if (p.top_k <= 64 && p.P != p.S)
+          run(false, k_topk_rows_w<T>, dim3((unsigned)((rows + kWaves - 1) / kWaves)), p);
+        else
+          run(false, k_topk_rows<T>, gr, p);
+      } else if (p.top_p < 1.0) {
+        run(false, k_topp_rows<T>, gr, p);
+        run(false, k_topp_rows_exact<T>, gr, p);
+      }
       const int passes = p.k - 1 < kTreePasses ? p.k - 1 : kTreePasses;
       for (int m = 0; m < passes; ++m) {
         const int most = (p.k - 1) / (m + 1);   // nodes that can have more than m children
@@ -3773,6 +3907,12 @@ hipError_t launch_stream(const Params& p, int mode, int bf16, hipStream_t st, hi
                          hipEvent_t e1) {
   return bf16 ? launch_stream_t<uint16_t>(p, mode, st, e0, e1)
               : launch_stream_t<float>(p, mode, st, e0, e1);
+}
+
+hipError_t launch_lazy_gate(const Params& p, int bf16, hipStream_t st) {
+  if (bf16) hipLaunchKernelGGL((k_lazy_gate<uint16_t>), dim3((unsigned)p.B), dim3(kBlock), 0, st, p);
+  else hipLaunchKernelGGL((k_lazy_gate<float>), dim3((unsigned)p.B), dim3(kBlock), 0, st, p);
+  return hipGetLastError();
 }
 
 hipError_t launch_finish(const Params& p, int filt, int bf16, hipStream_t st, hipEvent_t ev_end) {

@@ -55,10 +55,10 @@
  *     first accepted child becomes the node; when none is, or u has no
  *     child, y is drawn from r with the tree's uniform as in SV_MODE_SAMPLE.
  *     Row i of the target and of the draft is that model's distribution for
- *     node i's children (adjusted by the temperature; top-k and top-p are
- *     not available in this mode); the children of a node are taken to be
- *     drawn independently from q'_u, which makes the emitted tokens follow
- *     the target.  Emitted: the path's tokens (root excluded), then y.
+ *     node i's children, adjusted as in SV_MODE_SAMPLE (temperature, then
+ *     top-k, then top-p, on every row); the children of a node are taken to
+ *     be drawn independently from q'_u, which makes the emitted tokens
+ *     follow the target.  Emitted: the path's tokens (root excluded), then y.
  *
  * Layout: all arrays are dense, row-major, vocabulary fastest, and live in
  * device memory on the context's device.  Logits are float32 or bf16 (raw
@@ -98,14 +98,28 @@ enum {
   SV_ERR_NULL = -1,      /* a required pointer is NULL */
   SV_ERR_SHAPE = -2,     /* batch / k / vocab out of range */
   SV_ERR_DTYPE = -3,     /* unknown dtype */
-  SV_ERR_PARAM = -4,     /* temperature <= 0 or not finite, top_k < 0 or too large, top_p not in (0, 1];
-                            TREE_SAMPLE with top-k or top-p */
+  SV_ERR_PARAM = -4,     /* temperature <= 0 or not finite, top_k < 0 or too large, top_p not in (0, 1],
+                            an unknown or unsupported option */
   SV_ERR_CAPACITY = -5,  /* batch > max_batch */
   SV_ERR_HIP = -6,       /* a HIP call failed (allocation, launch, no device) */
   SV_ERR_MODE = -7,      /* unknown mode, or a pointer given / missing for this mode */
   SV_ERR_SCRATCH = -8,   /* specverify_run_static: the call needs more than SV_STATIC_SCRATCH_BYTES */
 };
 enum { SV_STATUS_BAD_TOKEN = 1, SV_STATUS_BAD_PARENT = 2, SV_STATUS_BAD_LOGITS = 4 };
+
+/* Options (sv_config.options).
+ *   SV_OPT_LAZY_ROWS  SV_MODE_SAMPLE without top-k / top-p only (else
+ *     SV_ERR_PARAM): the rejection fast path.  Source: "Towards Green Text
+ *     Generation: Memory-Based Speculative Decoding", section 2.4 "Verifier
+ *     and Acceptance" (the first drafted token is checked against the
+ *     logits already at hand before the remaining positions are scored) and
+ *     section 5.1 (the verifier's cost).  The call first reads only the row
+ *     pair of position 0 of every sequence and tests x_0; the rows of
+ *     positions 1..k are read only for sequences whose x_0 was accepted.
+ *     Outputs equal those without the option, except that a row never read
+ *     (every row after position 0 of a sequence that rejected x_0) is not
+ *     checked for NaN / +inf. */
+enum { SV_OPT_LAZY_ROWS = 1 };
 
 /* Limits checked by create / check_args. */
 #define SV_MAX_K 64          /* chain: drafted tokens per sequence */
@@ -119,6 +133,7 @@ typedef struct {
   int32_t max_batch;     /* upper bound on the batch passed to run (>= 1) */
   int32_t k;             /* chain: drafted tokens k (1..SV_MAX_K); tree: node count N incl. root */
   int32_t vocab;         /* V (1..SV_MAX_VOCAB) */
+  int32_t options;       /* SV_OPT_* bits; 0 = none */
   double temperature;    /* SAMPLE: T > 0 (logits are divided by T in float64); ignored otherwise */
   int32_t top_k;         /* SAMPLE: 0 = off, else 1..SV_MAX_TOP_K (>= V acts as off) */
   double top_p;          /* SAMPLE: 1.0 = off, else in (0, 1) */

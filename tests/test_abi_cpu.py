@@ -121,6 +121,27 @@ def test_tiling_rejects_bad_arguments_on_the_host():
     assert _tiling(cfg, 4, 0, 1)[0] == svm.SV_ERR_PARAM
 
 
+def test_lazy_rows_option_rules():
+    """SV_OPT_LAZY_ROWS: plain sampling only; unknown option bits are refused."""
+    lib = svm.load()
+    lazy = svm.SV_OPT_LAZY_ROWS
+
+    def ws(cfg):
+        return lib.specverify_workspace_bytes(ctypes.byref(cfg))
+    assert svm.sv_config.options.offset == 20
+    assert ws(make_config(SV_MODE_SAMPLE, "f32", 1, 4, 32000, 1.0, options=lazy)) > 0
+    for bad in (make_config(SV_MODE_SAMPLE, "f32", 1, 4, 32000, 1.0, top_k=50, options=lazy),
+                make_config(SV_MODE_SAMPLE, "f32", 1, 4, 32000, 1.0, top_p=0.9, options=lazy),
+                make_config(SV_MODE_GREEDY, "f32", 1, 4, 32000, options=lazy),
+                make_config(SV_MODE_TREE_SAMPLE, "f32", 1, 4, 32000, 1.0, options=lazy),
+                make_config(SV_MODE_SAMPLE, "f32", 1, 4, 32000, 1.0, options=2)):
+        assert ws(bad) == 0
+        h = ctypes.c_void_p()
+        assert lib.specverify_create(ctypes.byref(bad), 0, ctypes.byref(h)) == svm.SV_ERR_PARAM
+    # top_k >= V is no filter, so the option stands
+    assert ws(make_config(SV_MODE_SAMPLE, "f32", 1, 4, 100, 1.0, top_k=100, options=lazy)) > 0
+
+
 def test_config_struct_layout():
     assert ctypes.sizeof(svm.sv_config) == 48
     assert svm.sv_config.temperature.offset == 24 and svm.sv_config.top_p.offset == 40
@@ -244,10 +265,15 @@ def test_tree_sample_rules():
         assert check(t, **kw) == SV_ERR_NULL, name
     assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 1024, 1000), parents=P) == SV_OK
     assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 1025, 1000), parents=P) == SV_ERR_SHAPE
-    # temperature only: top-k or top-p are refused; top_k >= V means off
-    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_k=50), parents=P) == SV_ERR_PARAM
-    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_p=0.9), parents=P) == SV_ERR_PARAM
+    # top-k and top-p as in chain sampling; top_k >= V means off
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_k=50), parents=P) == SV_OK
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_p=0.9), parents=P) == SV_OK
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_k=257), parents=P) == SV_ERR_PARAM
+    assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_p=1.5), parents=P) == SV_ERR_PARAM
     assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, top_k=1000), parents=P) == SV_OK
+    for f in (dict(top_k=50), dict(top_p=0.9), dict(top_k=20, top_p=0.8)):
+        assert svm.load().specverify_workspace_bytes(
+            ctypes.byref(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 128256, **f))) > 0
     assert check(make_config(SV_MODE_TREE_SAMPLE, "bf16", 8, 60, 1000, temperature=0.0), parents=P) == SV_ERR_PARAM
     assert svm.load().specverify_workspace_bytes(ctypes.byref(t)) > 0
 

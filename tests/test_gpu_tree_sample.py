@@ -7,6 +7,7 @@ the distribution of the last draw within 1e-5 absolute on every tree.
 """
 import numpy as np
 import pytest
+import scipy.stats
 import torch
 
 import oracle.tree_sample as ts
@@ -32,7 +33,7 @@ def tree_tokens(inp, parents=None):
             if not (0 <= par < i):
                 continue
             if par not in qs:
-                qs[par] = ov.transform_row(d64[b, par], inp["T"])
+                qs[par] = ov.transform_row(d64[b, par], inp["T"], inp.get("top_k", 0), inp.get("top_p", 1.0))
             tok[b, i] = ov.draw_from(qs[par], inp["draw_u"][b, i])
     return tok
 
@@ -41,7 +42,7 @@ def run_gpu(inp, tok, parents=None, want_resid=True):
     parents = inp["parents"] if parents is None else parents
     B, N, V = inp["target"].shape
     sv = SpecVerify(mode=SV_MODE_TREE_SAMPLE, dtype=inp["dtype"], max_batch=B, k=N, vocab=V,
-                    temperature=inp["T"])
+                    temperature=inp["T"], top_k=inp.get("top_k", 0), top_p=inp.get("top_p", 1.0))
     out = sv.run(dev(inp["target"], inp["dtype"]), dev(inp["draft"], inp["dtype"]), dev(tok.astype(np.int32)),
                  dev(inp["u"]), dev(inp["ur"]), parents=dev(parents.astype(np.int32)),
                  want_resid_probs=want_resid)
@@ -56,7 +57,8 @@ def run_oracle(inp, tok, which, parents=None):
     T64 = wl.rows_f64(inp["target"], inp["dtype"])
     D64 = wl.rows_f64(inp["draft"], inp["dtype"])
     acc, toks, nodes, st, flagged, resid = ts.run_tree_sample_batch(
-        T64, D64, parents, tok, inp["u"], inp["ur"], inp["T"], want_resid=True, which=which)
+        T64, D64, parents, tok, inp["u"], inp["ur"], inp["T"], inp.get("top_k", 0), inp.get("top_p", 1.0),
+        want_resid=True, which=which)
     return dict(accepted_len=acc, out_tokens=toks, out_nodes=nodes, seq_status=st, flagged=flagged,
                 resid=resid)
 
@@ -122,6 +124,59 @@ def test_tree_sample_close_draft(dtype):
     gpu = run_gpu(inp, tok)
     orc = run_oracle(inp, tok, range(24))
     compare(gpu, orc, list(range(24)), f"tree sample close draft {dtype}")
+
+
+@pytest.mark.parametrize("B,N,V,dtype,T,top_k,top_p", [
+    (16, 12, 3000, "bf16", 1.0, 20, 1.0),
+    (16, 12, 3000, "f32", 0.7, 0, 0.8),
+    (12, 30, 5003, "bf16", 1.0, 50, 0.9),     # ragged rows, top-k then nucleus
+    (8, 30, 3000, "f32", 1.0, 1, 1.0),        # top-k 1: one token per row
+    (8, 24, 4096, "bf16", 1.0, 256, 1.0),     # the largest top-k (block merge)
+    (8, 60, 128256, "bf16", 1.0, 50, 1.0),    # the sampled-tree workload's shape, top-k 50
+    (8, 60, 128256, "bf16", 1.0, 0, 0.9),     # the same, nucleus 0.9
+    (32, 3, 8, "f32", 1.0, 3, 1.0),           # tiny rows: the filter pass's bound is -inf
+    (16, 5, 20, "bf16", 1.0, 10, 0.9),
+])
+def test_tree_sample_filters(B, N, V, dtype, T, top_k, top_p):
+    """Top-k and nucleus applied to every target and draft row of the tree
+    before the tests (the adjusted distributions of the chain modes)."""
+    say("tree sample filters", B, N, V, dtype, T, top_k, top_p)
+    inp = wl.tree_sample_inputs(seed=57 + N + V + top_k, B=B, N=N, V=V, dtype=dtype, T=T)
+    inp["top_k"], inp["top_p"] = top_k, top_p
+    tok = tree_tokens(inp)
+    gpu = run_gpu(inp, tok)
+    orc = run_oracle(inp, tok, range(B))
+    compare(gpu, orc, list(range(B)), f"tree sample N={N} V={V} {dtype} top-k {top_k} top-p {top_p}")
+
+
+@pytest.mark.parametrize("top_k,top_p", [(0, 1.0), (3, 1.0), (0, 0.7)])
+def test_tree_sample_emitted_token_law_chisq(top_k, top_p):
+    """A root with two children drafted independently from q'_root (V = 8),
+    the same logits in 40000 trees with fresh uniforms: the first emitted
+    token follows p'_root."""
+    say("tree chi-square", top_k, top_p)
+    rng = np.random.default_rng(23 + top_k)
+    V, N, B = 8, 3, 40000
+    t = rng.normal(0, 1.0, size=(N, V))
+    d = t + rng.normal(0, 1.0, size=(N, V))
+    p0 = ov.transform_row(t[0].astype(np.float32).astype(np.float64), 1.0, top_k, top_p)
+    q0 = ov.transform_row(d[0].astype(np.float32).astype(np.float64), 1.0, top_k, top_p)
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        tok[b, 1] = ov.draw_from(q0, rng.random())
+        tok[b, 2] = ov.draw_from(q0, rng.random())
+    inp = dict(target=np.broadcast_to(t.astype(np.float32), (B, N, V)).copy(),
+               draft=np.broadcast_to(d.astype(np.float32), (B, N, V)).copy(), dtype="f32",
+               parents=np.tile(np.array([-1, 0, 0], np.int32), (B, 1)),
+               u=rng.random((B, N), dtype=np.float32), ur=rng.random(B, dtype=np.float32),
+               T=1.0, top_k=top_k, top_p=top_p)
+    gpu = run_gpu(inp, tok, want_resid=False)
+    counts = np.bincount(gpu["out_tokens"][:, 0], minlength=V)
+    sup = p0 > 0
+    assert counts[~sup].sum() == 0
+    pval = scipy.stats.chisquare(counts[sup], p0[sup] * counts.sum()).pvalue
+    say("  p-value", pval, "mean accepted", float(gpu["accepted_len"].mean()))
+    assert pval > 1e-3
 
 
 def test_tree_sample_full_size():
