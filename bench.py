@@ -205,6 +205,12 @@ def _short(name):
     return name
 
 
+def _reads_rows(name):
+    """The kernel that reads every logit of a call: the streaming pass, or the
+    one-read nucleus kernel of chain sampling with top-p."""
+    return "k_stream" in name or "k_nuc_rows" in name
+
+
 def _calls(rows, key_start, key_end):
     """Group library dispatches (in dispatch order) into calls: a call starts
     at a streaming-kernel dispatch (other than the second one of a lazy call,
@@ -216,7 +222,7 @@ def _calls(rows, key_start, key_end):
     calls, cur = [], None
     for r in rows:
         # a lazy call streams twice: the second streaming launch follows its gate
-        if "k_stream" in r["Kernel_Name"] and not (cur and "k_lazy_gate" in cur[-1]["Kernel_Name"]):
+        if _reads_rows(r["Kernel_Name"]) and not (cur and "k_lazy_gate" in cur[-1]["Kernel_Name"]):
             cur = []
             calls.append(cur)
         if cur is not None:
@@ -275,7 +281,7 @@ def pmc_summary(fetch_csv, write_csv, fetch_scale=2.0, write_scale=1.0):
     stream_bytes = 0
     for name in sorted(set(f_per) | set(w_per), key=lambda n: -f_per.get(n, 0.0)):
         b = int(round(1024 * (fetch_scale * f_per.get(name, 0.0) + write_scale * w_per.get(name, 0.0))))
-        if "k_stream" in name:
+        if _reads_rows(name):
             stream_bytes = b
         out.append(f"| `{name}` | {f_per.get(name, 0.0):.0f} | {w_per.get(name, 0.0):.0f} | {b} |")
     call_bytes = int(round(1024 * (fetch_scale * f_tot + write_scale * w_tot)))
@@ -531,7 +537,11 @@ def measure(config, steps, warmup, hip, with_extras=True, lazy=False):
     read_us = hip.elapsed_ms(fe[0], fe[1]) * 1e3 / steps
     tiny_us = hip.elapsed_ms(fe[1], fe[2]) * 1e3 / steps
     hip.destroy(fe)
+    # the kernel that reads every logit: chain sampling with top-p alone takes
+    # the one-read nucleus kernel, every other call the streaming pass
+    one_read = cfg["kind"] == "chain" and top_p < 1.0 and not top_k
     res = dict(config=config, workload=workload, extra=extra, arith=arith, B=B, rows_per_call=B * rows_t,
+               stream_name="k_nuc_rows" if one_read else "k_stream",
                logit_bytes=logit_bytes, alg_bytes=alg_bytes, ncopies=ncopies, wall=wall, step_us=step_us,
                call_us=call_us, call_us_p10=float(np.percentile(cms, 10)) * 1e3,
                call_us_p90=float(np.percentile(cms, 90)) * 1e3, kern_us=kern_us, achieved=achieved,
@@ -654,7 +664,7 @@ def main():
                     "of the call's first and last kernels), mean over the timed calls",
             "call_us": m["call_us"], "call_us_p10": m["call_us_p10"], "call_us_p90": m["call_us_p90"],
             "bytes_algorithmic": m["alg_bytes"],
-            "stream_kernel": {"name": "k_stream (the pass that reads every logit)", "us": m["kern_us"],
+            "stream_kernel": {"name": m["stream_name"] + " (the pass that reads every logit)", "us": m["kern_us"],
                               "achieved": m["stream_achieved"], "frac": m["stream_achieved"] / PEAK_HBM_GBS,
                               "traffic": m["stream_traffic"], "bytes_algorithmic": m["logit_bytes"]},
             "floor": {"bare_read_us": m["read_us"], "bare_read_frac": m["logit_bytes"] / (m["read_us"] * 1e-6) / 1e9

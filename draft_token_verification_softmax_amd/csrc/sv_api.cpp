@@ -73,7 +73,10 @@ Plan make_plan(const sv_config* c) {
     p.tile_mode = p.top_k > 0 ? sv::kModeTopk : (p.top_p < 1.0 ? sv::kModeStats64 : sv::kModeStatsMix);
   }
   else if (p.top_k > 0) { p.filt = sv::kFiltTopk; p.tile_mode = sv::kModeTopk; }
-  else if (p.top_p < 1.0) { p.filt = sv::kFiltTopp; p.tile_mode = sv::kModeStats64; }
+  else if (p.top_p < 1.0) {
+    p.filt = sv::kFiltTopp;
+    p.tile_mode = c->vocab <= sv::kNucMaxV ? sv::kModeNucRow : sv::kModeStats64;
+  }
   else { p.filt = sv::kFiltNone; p.tile_mode = sv::kModeStatsMix; }
   if (c->mode == SV_MODE_TREE_GREEDY) { p.rows_t = c->k; p.rows_d = 0; p.out_w = c->k; }
   else if (tsample) { p.rows_t = c->k; p.rows_d = c->k; p.out_w = c->k; }
@@ -172,6 +175,14 @@ int tiling(const sv_config* c, const Plan& pl, int32_t batch, int grid, int alig
   if (tile_mode == sv::kModeTopk && aligned && c->vocab % sv::kVec == 0 &&
       c->vocab <= (long)sv::kMaxTiles * round)
     tile_mode = sv::kModeTopkFilter;
+  if (tile_mode == sv::kModeNucRow) {
+    // one workgroup per row reads all of it (no tile partials)
+    *tile_mode_out = tile_mode;
+    *S_out = 1;
+    *L_out = (int)((c->vocab + sv::kVec - 1) / sv::kVec * sv::kVec);
+    *P_out = 1;
+    return SV_OK;
+  }
   long S;
   if (tile_mode == sv::kModeTopk) {
     // about four tiles per resident workgroup, tiles of at least kMinTile logits
@@ -273,6 +284,7 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
   p.k_bad = (int32_t*)(ws + L.k_bad);
   p.k_px = (double*)(ws + L.k_px);
   p.go = (int32_t*)(ws + L.go);
+  p.nucrow = tile_mode == sv::kModeNucRow ? 1 : 0;
 
   const int bf16 = c->dtype == SV_DTYPE_BF16;
   hipError_t e;

@@ -71,10 +71,15 @@ struct SeqState {
 
 // Passes of the streaming kernel: argmax (greedy, tree), top-k lists (exact
 // per tile: any tile shape; certified filter: tiles of one round of loads in
-// aligned rows), max + sum of exponentials (float64 terms for nucleus rows;
-// plain and tree sampling: float64 terms in the rows whose normaliser can
-// change a decision, float32 terms in the others).
-enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4, kModeStatsMix = 5 };
+// aligned rows), max + sum of exponentials (float64 terms for the nucleus
+// rows of a sampled tree; plain and tree sampling: float64 terms in the rows
+// whose normaliser can change a decision, float32 terms in the others).
+// Chain sampling with top-p alone takes kModeNucRow instead (rows up to
+// kNucMaxV logits): one workgroup per row reads it once and settles its
+// nucleus cut (k_nuc_rows).
+enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4, kModeStatsMix = 5,
+                kModeNucRow = 6 };
+constexpr int kNucMaxV = 1 << 20;   // longest rows k_nuc_rows takes (its candidates' 16-bit positions)
 enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4,
               kFiltTreeSample = 5 };
 // Speculative residual passes of tree sampling: pass m (1..kTreePasses)
@@ -122,6 +127,7 @@ struct Params {
   // where go is set)
   int lazy;
   int32_t* go;       // [B] lazy: 1 if position 0 was accepted (stage 2 reads the rest)
+  int nucrow;        // the nucleus rows came from k_nuc_rows (RowNuc holds M and Z of every row)
   // workspace
   TileStat* tiles;   // [rows][P]
   uint64_t* cand;    // [rows][S][cand_w] (top-k): each tile's candidate list
@@ -151,7 +157,8 @@ struct Params {
 };
 
 // Launchers (sv_kernels.hip).  Each returns the hipError_t of its launches.
-// launch_stream: the one pass over every logit (tile partials).
+// launch_stream: the one pass over every logit (tile partials; kModeNucRow:
+// each row's nucleus result).
 // launch_finish: the kernels after it for `filt` (greedy / tree: decision per
 // sequence; top-k: merge per row, decision per sequence; nucleus: exact cut
 // per row, decision per sequence; plain sampling: residual row sums, residual

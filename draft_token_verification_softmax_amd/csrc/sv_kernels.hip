@@ -39,6 +39,7 @@
 #include <float.h>
 #include <limits.h>
 #include <limits>
+#include <type_traits>
 #include <math.h>
 
 #include <hip/hip_ext.h>
@@ -3756,8 +3757,11 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
 }
 
 // Nucleus cut per row: topp_fast; a row it cannot settle is left with ok =
-// kNucRetry for k_topp_rows_exact.
+// kNucRetry for k_topp_rows_exact.  After k_nuc_rows (p.nucrow) it takes
+// only the rows that kernel left with ok = kNucFast, with their M and Z, and
+// every other workgroup returns at once.
 constexpr int kNucRetry = 3;
+constexpr int kNucFast = 4;
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
@@ -3772,12 +3776,22 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   __shared__ float sh_M;
   __shared__ double sh_Z;
   __shared__ int sh_bad;
-  auto sink = [&](int, float M, int, double Z, int bad) { sh_M = M; sh_Z = Z; sh_bad = bad; };
-  combine_rows<true, 4>(p, 1, [grow](int) { return grow; }, sink);
-  __syncthreads();
   RowNuc out;
-  out.Z = sh_Z; out.N = 0.0; out.cut = 0ull; out.ok = 0; out.M = sh_M;
-  if (!sh_bad && !topp_fast<T>(p, row, out.M, out.Z, &out, hist, win, aq, red, redi, &wcnt, grow * 7))
+  if (p.nucrow) {
+    out = p.nuc[grow];
+    if (out.ok != kNucFast) return;
+  } else {
+    auto sink = [&](int, float M, int, double Z, int bad) { sh_M = M; sh_Z = Z; sh_bad = bad; };
+    combine_rows<true, 4>(p, 1, [grow](int) { return grow; }, sink);
+    __syncthreads();
+    out.Z = sh_Z; out.N = 0.0; out.cut = 0ull; out.ok = sh_bad ? 0 : 1; out.M = sh_M;
+    if (out.ok == 0) {
+      if (threadIdx.x == 0) p.nuc[grow] = out;
+      return;
+    }
+  }
+  out.N = 0.0; out.cut = 0ull;
+  if (!topp_fast<T>(p, row, out.M, out.Z, &out, hist, win, aq, red, redi, &wcnt, grow * 7))
     out.ok = kNucRetry;
   if (threadIdx.x == 0) p.nuc[grow] = out;
 }
@@ -3803,6 +3817,553 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows_exact(Params p) {
 }
 
 
+// ================================================================== nucleus rows in one read
+//
+// k_nuc_rows: one workgroup of kNB threads per row reads the row once and
+// settles its nucleus cut from what it kept on chip (the cut kernels above
+// read a row twice more after the streaming pass; on this chip a second
+// sweep of a row finds nothing of the first one left in any cache).
+//  sweep   each lane keeps its running max m and the float64 sum of
+//          2^((l - m) c) as tile_stats does (table exp2, float64 terms), and
+//          every logit >= tau goes to its wave's candidate region in LDS:
+//          the raw value and a 16-bit position (round, lane, slot, element)
+//          from which its index follows.  A region fills in its wave's
+//          program order, so its contents do not depend on timing.  tau is
+//          set from the first round the workgroup reads (a random tenth of a
+//          large row): the 16-bit key prefix at which the round's counts
+//          would put about kNucFill candidates at or above tau over the row.
+//  settle  M, Z (fixed-order block sums); the candidates' masses
+//          e = exp((l - M) / T) in float64 go to a fixed-point histogram of
+//          d = (M - l) / T (the bins of topp_fast) that locates the bin where
+//          the mass from the top reaches top_p Z; the window is that bin and
+//          its two neighbours.  The mass A of the candidates above it is
+//          summed in float64 in a fixed order, the window's keys are ranked
+//          and walked from A as topp_fast walks them.
+// A row it cannot settle (a region full, the cut below tau or outside the
+// window, a window over kNucWin entries) keeps M and Z with ok = kNucFast and
+// k_topp_rows redoes it; an invalid row gets ok = 0.  Rows of more than
+// kNucMaxV logits (the 16-bit positions) take the streaming pass and the cut
+// kernels instead.
+constexpr int kNB = 1024;                     // threads per workgroup
+constexpr int kNW = kNB / 64;                 // its waves
+constexpr int kNucRegion = 21 * 64;           // candidate slots per wave
+constexpr int kNucCand = kNW * kNucRegion;    // 21504 candidates: 126 KB of LDS (6 bytes each)
+constexpr int kNucStride = kNucRegion + 1;    // a wave's region and a spare slot
+constexpr int kNucFill = kNucCand * 7 / 10;   // candidates aimed for over a row
+constexpr int kNucHist = 2048;                // bins locating the cut among the candidates
+constexpr int kNucWin = kNucHist / 2;         // window slots (the histogram's space, reused)
+constexpr int kNucSample = 2 * kNucHist;      // 16-bit key-prefix bins of the sample (u32)
+constexpr double kNucFix = 17592186044416.0;  // 2^44: fixed-point scale of the masses (e <= 1)
+static_assert(kNucFill <= kNucCand, "aim below capacity");
+
+template <typename T> struct NucShape;
+// groups per lane per round: 64 KB per round in flight; the 16-bit position
+// holds the round above (lane, slot, element)
+template <> struct NucShape<float> { static constexpr int U = 2, kSlotBits = 1; };
+template <> struct NucShape<uint16_t> { static constexpr int U = 4, kSlotBits = 2; };
+template <typename T> constexpr int kNucRoundShift = 6 + NucShape<T>::kSlotBits + 3;
+static_assert(kNucMaxV <= (1 << (16 - kNucRoundShift<float>)) * 2 * kNB * kVec, "positions fit 16 bits");
+static_assert(kNucMaxV <= (1 << (16 - kNucRoundShift<uint16_t>)) * 4 * kNB * kVec, "positions fit 16 bits");
+
+// Block-wide reductions for kNB threads, fixed order; every thread gets the
+// result.  Each starts with a barrier, so `red` can be reused at once.
+DEV float nb_max(float v, float* red) {
+  v = wave_max(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  float t = red[0];
+#pragma unroll
+  for (int q = 1; q < kNW; ++q) t = fmaxf(t, red[q]);
+  return t;
+}
+DEV double nb_sum(double v, double* red) {
+  v = wave_sum(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  double t = red[0];
+#pragma unroll
+  for (int q = 1; q < kNW; ++q) t += red[q];
+  return t;
+}
+template <typename I>
+DEV I nb_min(I v, I* red) {
+  v = wave_min_t(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  I t = red[0];
+#pragma unroll
+  for (int q = 1; q < kNW; ++q) t = red[q] < t ? red[q] : t;
+  return t;
+}
+template <typename I>
+DEV I nb_max_i(I v, I* red) {
+  v = wave_max_t(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+  __syncthreads();
+  I t = red[0];
+#pragma unroll
+  for (int q = 1; q < kNW; ++q) t = red[q] > t ? red[q] : t;
+  return t;
+}
+// exclusive prefix in thread order (and the total) of one value per thread
+template <typename V>
+DEV V nb_exscan(V v, V* red, V* total) {
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const V inc = wave_scan(v, (V)0, [](V a, V b) { return a + b; });
+  __syncthreads();
+  if (lane == 63) red[w] = inc;
+  __syncthreads();
+  V base = 0, tot = 0;
+#pragma unroll
+  for (int q = 0; q < kNW; ++q) {
+    base += q < w ? red[q] : (V)0;
+    tot += red[q];
+  }
+  *total = tot;
+  return base + (inc - v);
+}
+
+// Where the element e of slot u of thread t sits in round r of a sweep.
+//   split (float32 rows read whole): slot u holds two quads kNB * 4 logits
+//   apart, so every 16-byte load of a wave reads 1 KB of consecutive logits;
+//   otherwise slot u holds kVec consecutive logits (group r R + u kNB + t).
+template <int U>
+DEV int nuc_index(int split, int r, int t, int u, int e) {
+  constexpr int R = U * kNB;
+  if (!split) return ((r * R + u * kNB + t) * kVec) + e;
+  return r * R * kVec + u * (kNB * kVec) + 4 * t + (e < 4 ? e : kNB * 4 + e - 4);
+}
+template <int U>
+struct NucMap {
+  int r;
+  int split;
+  DEV int index(int u, int e) const { return nuc_index<U>(split, r, (int)threadIdx.x, u, e); }
+  // the thread whose slot (*u, *e) holds logit x this round, or -1 (x
+  // uniform, so all of it is scalar work)
+  DEV int holder(int x, int* u, int* e) const {
+    constexpr int R = U * kNB;
+    const int rel = x - r * R * kVec;
+    if (rel < 0 || rel >= R * kVec) return -1;
+    if (!split) {
+      const int g = rel / kVec;
+      *u = g / kNB;
+      *e = rel % kVec;
+      return g % kNB;
+    }
+    *u = rel / (kNB * kVec);
+    int o = rel % (kNB * kVec);
+    int hi = 0;
+    if (o >= kNB * 4) { o -= kNB * 4; hi = 4; }
+    *e = hi + o % 4;
+    return o / 4;
+  }
+};
+
+// One workgroup's sweep of a whole row in rounds of U groups per lane,
+// starting at round r0 (the rounds wrap around).  Aligned rows of whole
+// groups go through a buffer resource spanning the row, the next round's
+// loads issued before the current one is used; others element by element.
+// f(v, map, tail) with tail a std::integral_constant: the round's values
+// (slots past the row hold -inf; only a tail round may have such slots).
+template <typename T, typename F>
+DEV void nuc_sweep(const T* row, int V, int aligned, int r0, F&& f) {
+  constexpr int U = NucShape<T>::U;
+  constexpr int R = U * kNB;
+  const int tid = threadIdx.x;
+  const int ngroups = (V + kVec - 1) / kVec, nfull = V / kVec;
+  const int nr = (ngroups + R - 1) / R;
+  if (aligned && nfull == ngroups && nfull > 0) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(row, V * (int)sizeof(T));
+    constexpr bool kSplit = sizeof(T) == 4;
+    auto load_round = [&](Group<T>* g, int r) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if constexpr (kSplit) {
+          const int soff = (r * R + u * kNB) * 32;
+          g[u].a = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, soff, kNT));
+          g[u].b = __builtin_bit_cast(vf4, __builtin_amdgcn_raw_buffer_load_b128(rs, tid * 16, soff + kNB * 16, kNT));
+        } else {
+          g[u].load_buf(rs, (r * R + tid) * Group<T>::kBytes, u * kNB * Group<T>::kBytes);
+        }
+      }
+    };
+    Group<T> cur[U], nxt[U];
+    int rc = r0;
+    load_round(cur, rc);
+#pragma unroll
+    for (int u = 0; u < U; ++u) cur[u] = cur[u].opaque();
+    for (int j = 0; j < nr; ++j) {
+      int rn = rc + 1;
+      if (rn >= nr) rn = 0;
+      if (j + 1 < nr) load_round(nxt, rn);
+      float v[U][kVec];
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u].values(v[u]);
+      if ((rc + 1) * R > ngroups) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          if constexpr (kSplit) {
+            const int pa = rc * R * kVec + u * kNB * kVec + 4 * tid;   // first logit of quad a
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (pa >= V) v[u][e] = -INFINITY;
+              if (pa + kNB * 4 >= V) v[u][4 + e] = -INFINITY;
+            }
+          } else {
+            if (rc * R + u * kNB + tid >= ngroups) {
+#pragma unroll
+              for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
+            }
+          }
+        }
+        f(v, NucMap<U>{rc, kSplit ? 1 : 0}, std::true_type{});
+      } else {
+        f(v, NucMap<U>{rc, kSplit ? 1 : 0}, std::false_type{});
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
+      rc = rn;
+    }
+  } else {
+    for (int j = 0; j < nr; ++j) {
+      int rc = r0 + j;
+      if (rc >= nr) rc -= nr;
+      float v[U][kVec];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int g = rc * R + u * kNB + tid;
+        if (g < ngroups) {
+          load_group<T>(row, g * kVec, V, aligned, v[u]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
+        }
+      }
+      f(v, NucMap<U>{rc, 0}, std::true_type{});
+    }
+  }
+}
+
+// sum of exp2_64 over n values, the table reads of all n issued before any
+// is used (the LDS latency once per batch, not once per term)
+template <int N>
+DEV double exp2_64_sum(const float* v, double cs, double nmc, const double* tab) {
+  double f[N];
+  int ji[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    const double y = fmax(fma((double)v[q], cs, nmc), -280000.0);
+    const double j = rint(y);
+    f[q] = y - j;
+    ji[q] = (int)j;
+  }
+  double tv[N];
+#pragma unroll
+  for (int q = 0; q < N; ++q) tv[q] = tab[ji[q] & (kExpTab - 1)];
+  double s = 0.0;
+#pragma unroll
+  for (int q = 0; q < N; ++q) {
+    double p = fma(f[q], kE4, kE3);
+    p = fma(p, f[q], kE2);
+    p = fma(p, f[q], kE1);
+    p = fma(p, f[q], 1.0);
+    s += ldexp(tv[q] * p, ji[q] >> kExpTabBits);
+  }
+  return s;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kNB) void k_nuc_rows(Params p) {
+  constexpr int U = NucShape<T>::U;
+  constexpr int R = U * kNB;                  // groups per round
+  constexpr int kRS = kNucRoundShift<T>;
+  __shared__ float cval[kNW * kNucStride];    // candidate values
+  __shared__ uint16_t cpos[kNW * kNucStride]; // their positions: round << kRS | lane << (slot bits + 3) | slot << 3 | element
+  __shared__ uint64_t hist[kNucHist];         // sample counts (u32), then masses, then the window
+  __shared__ double tab[kExpTab];
+  __shared__ double redd[kNW];
+  __shared__ uint64_t redu[kNW];
+  __shared__ float redf[kNW];
+  __shared__ int redi[kNW];
+  __shared__ int sh_nw;
+  __shared__ double sh_N;
+  const int grow = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int V = p.V;
+  const T* row = row_ptr<T>(p, grow);
+  bool xhas;
+  const int xs = __builtin_amdgcn_readfirstlane(row_token(p, grow, &xhas));   // uniform over the row
+  if (tid < kExpTab) tab[tid] = kExp2Tab[tid];
+  const double cd = kLog2e / p.T;
+  const double cs = kExpScale * cd;
+  const int ngroups = (V + kVec - 1) / kVec;
+  const int nr = (ngroups + R - 1) / R;
+  const int nfr = (V / kVec) / R;             // rounds of whole groups only
+  const int split = (sizeof(T) == 4 && p.aligned && V % kVec == 0 && V >= kVec) ? 1 : 0;   // as nuc_sweep
+  // start at a whole round (its values set tau); rows start at different
+  // rounds so that workgroups in step do not hit the same memory channels
+  const int r0 = nfr > 0 ? (int)(((long)grow * 7) % nfr) : 0;
+  float m = -INFINITY;
+  double s = 0.0;
+  bool nan_seen = false;
+  float lx = 0.f;
+  bool hx = false;
+  int cw = 0;                                 // candidates met by this wave (uniform)
+  float tau = -INFINITY;
+  bool first = true;
+  float* rval = cval + w * kNucStride;
+  uint16_t* rpos = cpos + w * kNucStride;
+  nuc_sweep<T>(row, V, p.aligned, r0, [&](float (&v)[U][kVec], const NucMap<U>& mp, auto tailc) {
+    constexpr bool kTail = decltype(tailc)::value;
+    // max over the round, NaN evidence, the drafted token's logit
+    float mi = m;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float gm = maximum8(v[u]);
+      nan_seen |= gm != gm;
+      mi = gm > mi ? gm : mi;
+    }
+    if (xhas) {
+      // the one lane (if any) whose slots hold token xs this round
+      int ux = 0, ex = 0;
+      if (mp.holder(xs, &ux, &ex) == tid) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) lx = (u == ux && e == ex) ? v[u][e] : lx;
+        }
+        hx = true;
+      }
+    }
+    if (mi > m) {
+      // (the table exp2: exp2_neg's constants would stay in registers all loop long)
+      if (m > -INFINITY) s *= exp2_64(((double)m - (double)mi) * cs, tab);
+      m = mi;
+    }
+    if (first) {
+      first = false;
+      if (nr > 1) {
+        // tau from this (whole) round: counts of 16-bit key prefixes below the round max's
+        const float rmax = nb_max(mi, redf);
+        uint32_t* hs = reinterpret_cast<uint32_t*>(hist);
+        for (int b = tid; b < kNucSample; b += kNB) hs[b] = 0u;
+        __syncthreads();
+        const uint32_t top = ord_key(rmax) >> 16;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+#pragma unroll
+          for (int e = 0; e < kVec; ++e) {
+            const float x = v[u][e];
+            if (x == x) {
+              const uint32_t d = top - (ord_key(x) >> 16);
+              atomicAdd(&hs[d < (uint32_t)(kNucSample - 1) ? d : (uint32_t)(kNucSample - 1)], 1u);
+            }
+          }
+        }
+        __syncthreads();
+        // the first prefix bin at which the count from the top reaches want
+        const int want = (int)((long)kNucFill * (long)(R * kVec) / (long)V);
+        constexpr int per = kNucSample / kNB;
+        uint32_t c[per];
+        uint32_t tl = 0;
+#pragma unroll
+        for (int q = 0; q < per; ++q) { c[q] = hs[tid * per + q]; tl += c[q]; }
+        uint32_t tot;
+        uint32_t run = nb_exscan<uint32_t>(tl, reinterpret_cast<uint32_t*>(redi), &tot);
+        int found = INT_MAX;
+#pragma unroll
+        for (int q = 0; q < per; ++q) {
+          run += c[q];
+          if (found == INT_MAX && run >= (uint32_t)want) found = tid * per + q;
+        }
+        const int bsel = nb_min<int>(found, redi);
+        if (bsel != INT_MAX && rmax == rmax && rmax > -INFINITY) {
+          // every value whose key prefix is >= top - bsel (a prefix below
+          // 0x0080 would decode to a NaN: such a tau takes everything finite)
+          uint32_t pk = top >= (uint32_t)bsel ? top - (uint32_t)bsel : 0u;
+          pk = pk < 0x0080u ? 0x0080u : pk;
+          tau = key_value(pk << 16);
+        }
+      } else {
+        __syncthreads();   // the table
+      }
+    }
+    // float64 terms, in batches of eight
+    if (m > -INFINITY) {
+      const double nmc = -(double)m * cs;
+      double gs = 0.0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) gs += exp2_64_sum<kVec>(v[u], cs, nmc, tab);
+      s += gs;
+    }
+    // candidates: one ballot per element slot; a taking lane's slot in the
+    // region is the wave's count so far plus the lanes below taking the same
+    // element slot.  Only taking lanes store (a slot past the region is
+    // clamped to the spare one: the row then counts as full and is redone).
+    const uint32_t pbase = ((uint32_t)mp.r << kRS) | ((uint32_t)lane << (NucShape<T>::kSlotBits + 3));
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int e = 0; e < kVec; ++e) {
+        bool take = v[u][e] >= tau;
+        if constexpr (kTail) take = take && mp.index(u, e) < V;
+        const uint64_t bm = __builtin_amdgcn_ballot_w64(take);
+        if (take) {
+          int slot = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bm, (unsigned)cw));
+          slot = slot < kNucRegion ? slot : kNucRegion;
+          rval[slot] = v[u][e];
+          rpos[slot] = (uint16_t)(pbase | (uint32_t)(u << 3) | (uint32_t)e);
+        }
+        cw += (int)__popcll(bm);
+      }
+    }
+  });
+  // ---- settle
+  if (xhas && hx) p.row_lx[grow] = lx;
+  const bool bad_nan = __syncthreads_or(nan_seen) != 0;
+  const float M = nb_max(m, redf);
+  const bool bad = bad_nan || !(M > -INFINITY) || !(M < INFINITY);
+  double zl = 0.0;
+  if (!bad && m > -INFINITY) zl = s * exp2_neg(((double)m - (double)M) * cd);
+  const double Z = nb_sum(zl, redd);
+  RowNuc out;
+  out.Z = Z; out.N = 0.0; out.cut = 0ull; out.M = M;
+  out.ok = bad ? 0 : kNucFast;
+  const bool full = __syncthreads_or(cw > kNucRegion) != 0;
+  if (bad || full) {
+    if (tid == 0) p.nuc[grow] = out;
+    return;
+  }
+  const double tgt = p.top_p * Z;
+  const double invT = 1.0 / p.T;
+  const double zm = (double)M * invT;
+  // bins of d = (M - l) / T over [0, dspan): every kept logit has
+  // d < ln(V / ((1 - top_p) Z)) + 1 (the tokens below that hold less than
+  // 1 - top_p of the mass together); candidates reach down to tau
+  double dmaxd = log((double)V / ((1.0 - p.top_p) * Z)) + 1.0;
+  if (!(dmaxd > 1.0)) dmaxd = 1.0;
+  const double dtau = tau > -INFINITY ? ((double)M - (double)tau) * invT : dmaxd;
+  double dspan = dtau < dmaxd ? dtau : dmaxd;
+  if (!(dspan > 0.0)) dspan = 1e-30;
+  const float invw = (float)((double)kNucHist / dspan);
+  const float a1 = (float)(-invT) * invw, b1 = (float)zm * invw;
+  // the bin tau falls in: bins below it hold only logits > tau (monotone
+  // fma), all of them candidates
+  int bin_tau = INT_MAX;
+  if (tau > -INFINITY) {
+    const float pt = fmaf(tau, a1, b1);
+    bin_tau = pt < (float)kNucHist ? (int)__builtin_amdgcn_fmed3f(pt, 0.f, (float)(kNucHist - 1)) : kNucHist;
+  }
+  const bool no_fix = !(tgt < (double)kNucCand);   // the candidates cannot hold that much mass
+  const uint64_t tgt_fix = no_fix ? 0ull : (uint64_t)(tgt * kNucFix);
+  for (int b = tid; b < kNucHist; b += kNB) hist[b] = 0ull;
+  __syncthreads();
+  const int nc = cw;
+  constexpr int kPer = kNucRegion / 64;
+  auto bin_of = [&](float l) {
+    const float pos = fmaf(l, a1, b1);
+    return pos < (float)kNucHist ? (int)__builtin_amdgcn_fmed3f(pos, 0.f, (float)(kNucHist - 1)) : INT_MAX;
+  };
+  // e = exp((l - M) / T) = 2^((l - M) c): the table exp2, as the sweep's terms
+  const double nmcM = -(double)M * cs;
+  auto mass_of = [&](float l) { return exp2_64(fma((double)l, cs, nmcM), tab); };
+  // the histogram only locates the window (its bin and the two around it),
+  // so its masses are the hardware float32 exp2 of (l - M) c (relative error
+  // near 1e-7, far inside a bin's mass); A and the window's walk below take
+  // float64 masses.  Each lane's candidates sit in slots lane, lane + 64, ...
+  const float M32 = M, c32 = (float)cd;
+  int bq[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int sl = lane + 64 * q;
+    bq[q] = INT_MAX;
+    if (sl < nc) {
+      const float l = rval[sl];
+      bq[q] = bin_of(l);
+      if (bq[q] != INT_MAX) {
+        const float e32 = __builtin_amdgcn_exp2f((l - M32) * c32);
+        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[bq[q]]), (unsigned long long)((double)e32 * kNucFix));
+      }
+    }
+  }
+  __syncthreads();
+  // the bin where the mass from the top reaches top_p Z
+  int bc;
+  {
+    const uint64_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
+    uint64_t tot;
+    const uint64_t ex = nb_exscan<uint64_t>(h0 + h1, redu, &tot);
+    int found = INT_MAX;
+    if (!no_fix) {
+      if (ex + h0 >= tgt_fix) found = 2 * tid;
+      else if (ex + h0 + h1 >= tgt_fix) found = 2 * tid + 1;
+    }
+    bc = nb_min<int>(found, redi);
+  }
+  const int lo = bc > 0 ? bc - 1 : 0;
+  const int hi = bc < kNucHist - 1 ? bc + 1 : kNucHist - 1;
+  if (bc == INT_MAX || hi >= bin_tau) {
+    if (tid == 0) p.nuc[grow] = out;   // the cut lies below tau
+    return;
+  }
+  // the exact mass above the window (fixed order: the lane's slots, then
+  // the block sum), the window's keys gathered
+  if (tid == 0) sh_nw = 0;
+  __syncthreads();
+  uint64_t* wl = hist;                 // unsorted window keys
+  uint64_t* ws = hist + kNucWin;       // the same, ranked
+  double al = 0.0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int sl = lane + 64 * q;
+    const int b = bq[q];
+    if (b < lo) al += mass_of(rval[sl]);
+    const bool inw = b >= lo && b <= hi;
+    const int at = wave_append(inw, &sh_nw);
+    if (inw && at < kNucWin) {
+      const float l = rval[sl];
+      const uint32_t ps = rpos[sl];
+      const int rr = (int)(ps >> kRS);
+      const int ln = (int)((ps >> (NucShape<T>::kSlotBits + 3)) & 63u);
+      const int uu = (int)((ps >> 3) & ((1u << NucShape<T>::kSlotBits) - 1u));
+      const int ee = (int)(ps & 7u);
+      wl[at] = pack(l, nuc_index<U>(split, rr, w * 64 + ln, uu, ee));
+    }
+  }
+  const double A = nb_sum(al, redd);   // (its barriers also publish the window)
+  const int nw = sh_nw;
+  if (nw == 0 || nw > kNucWin) {
+    if (tid == 0) p.nuc[grow] = out;
+    return;
+  }
+  // rank of each window key (keys are distinct: the index is part of the key)
+  if (tid < nw) {
+    const uint64_t k = wl[tid];
+    int r = 0;
+    for (int j = 0; j < nw; ++j) r += wl[j] > k ? 1 : 0;
+    ws[r] = k;
+  }
+  __syncthreads();
+  double e = 0.0;
+  if (tid < nw) e = mass_of(packed_val(ws[tid]));
+  double wtot;
+  const double c0 = A + nb_exscan<double>(e, redd, &wtot);
+  const int kept_l = (tid < nw && c0 < tgt) ? tid + 1 : 0;
+  const int kept = nb_max_i<int>(kept_l, redi);
+  const bool inside = kept > 0 && (kept < nw || A + wtot >= tgt);
+  if (inside && tid == kept - 1) sh_N = c0 + e;
+  __syncthreads();
+  if (inside) {
+    out.N = sh_N;
+    out.cut = ws[kept - 1];
+    out.ok = 1;
+  }
+  if (tid == 0) p.nuc[grow] = out;
+}
+
 // ================================================================== launchers
 
 template <typename T>
@@ -3813,6 +4374,7 @@ static int capacity_t(int mode) {
   else if (mode == kModeStatsMix) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeStatsMix>, kBlock, 0);
   else if (mode == kModeTopk) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopk>, kBlock, 0);
   else if (mode == kModeTopkFilter) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeTopkFilter>, kBlock, 0);
+  else if (mode == kModeNucRow) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_nuc_rows<T>, kNB, 0);
   else e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_stream<T, kModeArgmax>, kBlock, 0);
   return e == hipSuccess ? per_cu : 0;
 }
@@ -3830,7 +4392,9 @@ static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hip
                                                          : (long)p.B * (p.rows_t + p.rows_d);
   const unsigned grid = (unsigned)(rows * p.S);
   const dim3 block(kBlock);
-  if (mode == kModeStats64)
+  if (mode == kModeNucRow)
+    hipExtLaunchKernelGGL((k_nuc_rows<T>), dim3((unsigned)rows), dim3(kNB), 0, st, e0, e1, 0, p);
+  else if (mode == kModeStats64)
     hipExtLaunchKernelGGL((k_stream<T, kModeStats64>), dim3(grid), block, 0, st, e0, e1, 0, p);
   else if (mode == kModeStatsMix)
     hipExtLaunchKernelGGL((k_stream<T, kModeStatsMix>), dim3(grid), block, 0, st, e0, e1, 0, p);

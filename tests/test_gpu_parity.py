@@ -177,9 +177,9 @@ def test_topk_and_topp_together():
     (24, 5003, 4, 0.9, "f32"),
     (16, 4000, 3, 0.5, "bf16"),
     (16, 3000, 2, 0.99, "bf16"),
-    # float32 row sweeps read rounds of 4096 logits, each lane two quads
-    # 1024 apart per slot: a row inside one quad, quads past the end in the
-    # first slot, a last round of a few quads, a last round of one full slot
+    # rows inside one round of the one-read nucleus kernel (all candidates):
+    # a row inside one quad, quads past the end in the first slot, a last
+    # round of a few quads, a last round of one full slot
     (8, 8, 2, 0.9, "f32"),
     (8, 1032, 3, 0.9, "f32"),
     (8, 4104, 3, 0.8, "f32"),
@@ -194,6 +194,51 @@ def test_sample_topp(B, V, k, top_p, dtype):
     gpu = run_chain(inp, x, SV_MODE_SAMPLE)
     orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
     compare_chain(gpu, orc, range(B), f"top-p {top_p} V={V} {dtype}")
+
+
+@pytest.mark.parametrize("B,V,k,top_p,dtype", [
+    # the one-read nucleus kernel sweeps a row in rounds of 16384 float32
+    # logits (each lane two quads 4096 apart per slot) or 32768 bf16 ones,
+    # and sets its candidate threshold from the first whole round it reads
+    (6, 20488, 3, 0.9, "f32"),          # a whole round and a ragged one
+    (6, 40000, 2, 0.9, "f32"),          # three rounds, the last a few quads
+    (6, 70001, 2, 0.9, "bf16"),         # a half group at the end: element path
+    (6, 98304, 2, 0.8, "bf16"),         # three whole rounds
+    (4, 152064, 2, 0.95, "f32"),
+])
+def test_sample_topp_row_rounds(B, V, k, top_p, dtype):
+    say("sample top-p, rows of several rounds", B, V, k, top_p, dtype)
+    inp = wl.chain_inputs(5, seed=17 + V, B=B, V=V, k=k, dtype=dtype)
+    inp["top_p"] = top_p
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    compare_chain(gpu, orc, range(B), f"top-p {top_p} V={V} {dtype} rounds")
+
+
+def test_sample_topp_wide_nucleus():
+    """A nucleus wider than the one-read kernel's candidates (flat rows, top-p
+    0.995: about a hundred thousand kept tokens of 152064): every row falls
+    back to the cut kernels, which must give the same results."""
+    say("sample top-p, wide nucleus")
+    inp = wl.chain_inputs(5, seed=23, B=3, V=152064, k=2)
+    inp["T"], inp["top_p"] = 3.0, 0.995
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(3)))
+    compare_chain(gpu, orc, range(3), "top-p 0.995, T 3, V=152064")
+
+
+def test_sample_topp_beyond_row_kernel_vocab():
+    """Rows longer than the one-read kernel takes (2^20 logits) keep the
+    streaming pass and the cut kernels."""
+    say("sample top-p, V above 2^20")
+    V = (1 << 20) + 8
+    inp = wl.chain_inputs(5, seed=29, B=1, V=V, k=1)
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, [0])
+    compare_chain(gpu, orc, [0], f"top-p 0.9 V={V}")
 
 
 @pytest.mark.parametrize("B,V,k,top_p,dtype", [
