@@ -49,7 +49,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBS = 8000.0
 METRIC = "verified logit rows/sec + achieved HBM GB/s (fraction of peak), 1 GPU"
 # kernels launched around a call by the bench itself (not part of the step)
-AUX_KERNELS = ("k_accept_stats", "k_tree_mask", "k_tree_commit")
+AUX_KERNELS = ("k_accept_stats", "k_tree_mask", "k_tree_commit", "k_read_floor")
 
 
 def log(*a):
@@ -511,32 +511,48 @@ def measure(config, steps, warmup, hip, with_extras=True, lazy=False):
         f"kernel end; p10 {np.percentile(cms, 10) * 1e3:.2f}, p90 {np.percentile(cms, 90) * 1e3:.2f}), "
         f"{achieved:.1f} GB/s = {achieved / PEAK_HBM_GBS:.3f} of peak; streaming kernel {kern_us:.2f} us, "
         f"{stream_ach:.1f} GB/s")
-    # floors for the same call: a bare read of the same logits (torch.sum over
-    # each logit tensor of the same rotating copies: every byte read once),
-    # and one tiny kernel per launch back to back on the stream
+    # floors for the same call: a bare read of the same logits (the library's
+    # read-floor kernel over each logit tensor of the same rotating copies:
+    # every byte read once, in the streaming pass's tile shape), and one tiny
+    # kernel per launch, back to back
     small = torch.zeros(1, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def reads(i):
         c = copies[i % ncopies]
-        c["target"].sum()
+        svm.read_floor(c["target"], sink)
         if c.get("draft") is not None:
-            c["draft"].sum()
+            svm.read_floor(c["draft"], sink)
 
-    fe = hip.create(4)
+    # each floor's launches are captured in a HIP graph and timed by replay,
+    # so the GPU runs them back to back whatever the host's launch rate (a
+    # loop of small launches from Python would time the host)
     for i in range(warmup):
         reads(i)
-    torch.cuda.synchronize()
-    hip.record(fe[0], stream)
-    for i in range(steps):
-        reads(i)
-    hip.record(fe[1], stream)
-    for i in range(steps):
         small.add_(1.0)
+    torch.cuda.synchronize()
+    g_read, g_tiny = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g_read):
+        for i in range(steps):
+            reads(i)
+    with torch.cuda.graph(g_tiny):
+        for i in range(steps):
+            small.add_(1.0)
+    g_read.replay()
+    g_tiny.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream().cuda_stream
+    fe = hip.create(3)
+    hip.record(fe[0], stream)
+    g_read.replay()
+    hip.record(fe[1], stream)
+    g_tiny.replay()
     hip.record(fe[2], stream)
     torch.cuda.synchronize()
     read_us = hip.elapsed_ms(fe[0], fe[1]) * 1e3 / steps
     tiny_us = hip.elapsed_ms(fe[1], fe[2]) * 1e3 / steps
     hip.destroy(fe)
+    del g_read, g_tiny
     # the kernel that reads every logit: chain sampling with top-p alone takes
     # the one-read nucleus kernel, every other call the streaming pass
     one_read = cfg["kind"] == "chain" and top_p < 1.0 and not top_k
@@ -669,9 +685,10 @@ def main():
                               "traffic": m["stream_traffic"], "bytes_algorithmic": m["logit_bytes"]},
             "floor": {"bare_read_us": m["read_us"], "bare_read_frac": m["logit_bytes"] / (m["read_us"] * 1e-6) / 1e9
                       / PEAK_HBM_GBS, "tiny_kernel_us": m["tiny_us"],
-                      "note": "bare read: torch.sum over each logit tensor of the same rotating copies "
-                              "(HIP events, mean per call); tiny kernel: a one-element add per launch, "
-                              "back to back"},
+                      "note": "bare read: specverify_read_floor over each logit tensor of the same rotating "
+                              "copies (16-byte non-temporal loads, 16 KB per workgroup), K calls captured in a "
+                              "HIP graph, HIP events around its replay, mean per call; tiny kernel: a "
+                              "one-element add per launch, K of them in a graph the same way"},
         },
     }
     extras = m.get("extras", {})

@@ -32,7 +32,7 @@ EXPORTED = ("specverify_create", "specverify_check_args", "specverify_run", "spe
             "specverify_tiling",
             "specverify_destroy", "specverify_profile_events", "specverify_status_string",
             "specverify_workspace_bytes", "specverify_accept_stats", "specverify_tree_mask",
-            "specverify_tree_commit")
+            "specverify_tree_commit", "specverify_read_floor")
 
 # Slots of specverify_accept_stats' output (SV_STATS_* of the header).
 SV_STATS_SEQUENCES, SV_STATS_ACCEPTED, SV_STATS_DRAFTED, SV_STATS_TESTED = 0, 1, 2, 3
@@ -98,6 +98,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.specverify_tree_mask.restype = ctypes.c_int
     lib.specverify_tree_commit.argtypes = [vp, vp, i32, i32, vp, vp]
     lib.specverify_tree_commit.restype = ctypes.c_int
+    lib.specverify_read_floor.argtypes = [vp, ctypes.c_int64, vp, vp]
+    lib.specverify_read_floor.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -188,6 +190,18 @@ def specverify_profile_events(ctx: int, ev_begin, ev_stream_end, ev_call_end=Non
     st = load().specverify_profile_events(ctypes.c_void_p(ctx), ev_begin, ev_stream_end, ev_call_end)
     if st != SV_OK:
         raise SpecVerifyError(st, "specverify_profile_events")
+
+
+def read_floor(t, sink, stream=None) -> None:
+    """Read every byte of the device tensor t once (specverify_read_floor):
+    the HBM read floor of its bytes, for timing beside a call.  sink: a
+    device tensor of at least one int32."""
+    import torch
+    st = stream if stream is not None else torch.cuda.current_stream()
+    rc = load().specverify_read_floor(ctypes.c_void_p(t.data_ptr()), t.numel() * t.element_size(),
+                                      ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+    if rc != SV_OK:
+        raise SpecVerifyError(rc, "specverify_read_floor")
 
 
 def specverify_destroy(ctx) -> None:

@@ -564,6 +564,15 @@ int specverify_accept_stats(const int32_t* accepted_len, const int32_t* seq_stat
   return e == hipSuccess ? SV_OK : SV_ERR_HIP;
 }
 
+int specverify_read_floor(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0) return SV_ERR_SHAPE;
+  if (bytes == 0) return SV_OK;
+  if (!src || !sink) return SV_ERR_NULL;
+  if ((uintptr_t)src % 16 != 0 || bytes % 16 != 0) return SV_ERR_SHAPE;
+  const hipError_t e = sv::launch_read_floor(src, (long long)bytes, sink, (hipStream_t)stream);
+  return e == hipSuccess ? SV_OK : SV_ERR_HIP;
+}
+
 int specverify_tree_mask(const int32_t* parents, int32_t batch, int32_t nodes, uint32_t* mask,
                          int32_t* depth, void* stream) {
   if (batch < 0 || nodes < 1 || nodes > SV_MAX_TREE_NODES) return SV_ERR_SHAPE;

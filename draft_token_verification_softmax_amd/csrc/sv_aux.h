@@ -19,5 +19,6 @@ hipError_t launch_tree_mask(const int32_t* parents, int batch, int N, uint32_t* 
                             hipStream_t st);
 hipError_t launch_tree_commit(const int32_t* path, const int32_t* acc, int batch, int N, int32_t* pos,
                               hipStream_t st);
+hipError_t launch_read_floor(const void* src, long long bytes, uint32_t* sink, hipStream_t st);
 
 }  // namespace sv

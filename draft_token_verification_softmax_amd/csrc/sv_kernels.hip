@@ -2847,7 +2847,9 @@ constexpr int kPassBatch = 4;    // nodes whose segment loads are in flight toge
 // its row views and states are gathered (all loads of a kind in one round).
 constexpr int kPassGroups = 8;
 
-template <typename T>
+// TFILT: the rows carry a top-k / top-p cut (p.tfilt); without it every
+// cut is 0 at compile time and the pass keeps no keys in registers.
+template <typename T, bool TFILT>
 __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
   __shared__ int nch[kTreeMax], lst[kTreeMax];
   __shared__ double vv[kPassBatch][4];
@@ -2897,10 +2899,10 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
         const size_t at = (size_t)b * N + lst[l0 + l];
         p.tview[at * 4 + o] = nmc;
         p.tview[at * 4 + o + 1] = inv;
-        if (p.tfilt) p.tcut[at * 2 + (o >> 1)] = cut;
+        if (TFILT) p.tcut[at * 2 + (o >> 1)] = cut;
       }
     };
-    if (p.tfilt) {
+    if (TFILT) {
       if (tid < 2 * nbl) {
         const int r = tid;
         double nmc, inv;
@@ -2944,8 +2946,8 @@ __global__ __launch_bounds__(kBlock) void k_tsample_pass(Params p, int m) {
 #pragma unroll
     for (int q = 0; q < kPassBatch; ++q) {
       const int l = q < nbl ? q : 0;
-      const RowView pr{nullptr, vv[l][0], vv[l][1], vc[l][0]};
-      const RowView qr{nullptr, vv[l][2], vv[l][3] * cn[l], vc[l][1]};
+      const RowView pr{nullptr, vv[l][0], vv[l][1], TFILT ? vc[l][0] : 0ull};
+      const RowView qr{nullptr, vv[l][2], vv[l][3] * cn[l], TFILT ? vc[l][1] : 0ull};
       float lp[kVec], lq[kVec];
       gp[q].opaque().values(lp);
       gq[q].opaque().values(lq);
@@ -4452,7 +4454,8 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st, hip
         const int most = (p.k - 1) / (m + 1);   // nodes that can have more than m children
         int G = (most + kPassBatch - 1) / kPassBatch;
         G = G < 1 ? 1 : (G > kPassGroups ? kPassGroups : G);
-        run(false, k_tsample_pass<T>, dim3((unsigned)p.S2, (unsigned)p.B, (unsigned)G), p, m);
+        if (p.tfilt) run(false, k_tsample_pass<T, true>, dim3((unsigned)p.S2, (unsigned)p.B, (unsigned)G), p, m);
+        else run(false, k_tsample_pass<T, false>, dim3((unsigned)p.S2, (unsigned)p.B, (unsigned)G), p, m);
       }
       run(false, k_tsample_walk<T>, gb, p);
       run(false, k_tsample_mass<T>, gs, p);

@@ -235,6 +235,17 @@ void specverify_destroy(specverify_ctx* ctx);
 int specverify_profile_events(specverify_ctx* ctx, void* ev_begin, void* ev_stream_end,
                               void* ev_call_end);
 
+/* Instrumentation for benchmarks: reads `bytes` of device memory at `src`
+ * once (16-byte non-temporal loads, 16 KB per workgroup of 256 threads, the
+ * shape of the streaming pass's tiles) and keeps nothing, asynchronously on
+ * `stream` (NULL: the current device's null stream).  Timed beside a call
+ * on the same logits, it gives the HBM read floor of that call's bytes.
+ * `sink` (one device word) is written only if the data XOR to one fixed
+ * value, which keeps the loads from being dropped.  src and bytes must be
+ * multiples of 16 (SV_ERR_SHAPE otherwise, or for bytes < 0); SV_ERR_NULL
+ * for a NULL src or sink with bytes > 0; bytes == 0 launches nothing. */
+int specverify_read_floor(const void* src, int64_t bytes, uint32_t* sink, void* stream);
+
 /* Host-only: the streaming pass's tiling that specverify_run would use for
  * `batch` sequences of cfg when the streaming kernel has `grid` resident
  * workgroups on the device and the logit tensors start 16-byte aligned

@@ -28,7 +28,7 @@ def declared_functions():
 def test_library_exports_every_declared_function():
     lib = svm.load()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert sorted(svm.EXPORTED) == names
@@ -293,6 +293,16 @@ def test_run_rejects_null_context():
     lib = svm.load()
     assert lib.specverify_run(None, 1, *([None] * 11), None) == SV_ERR_NULL
     assert lib.specverify_profile_events(None, None, None, None) == SV_ERR_NULL
+
+
+def test_read_floor_checks_arguments_on_the_host():
+    """Argument errors come back before any HIP call (no GPU needed)."""
+    lib = svm.load()
+    assert lib.specverify_read_floor(None, 0, None, None) == SV_OK          # nothing to read
+    assert lib.specverify_read_floor(None, 64, None, None) == SV_ERR_NULL
+    assert lib.specverify_read_floor(None, -16, None, None) == SV_ERR_SHAPE
+    assert lib.specverify_read_floor(16, 24, 64, None) == SV_ERR_SHAPE        # bytes not a multiple of 16
+    assert lib.specverify_read_floor(8, 32, 64, None) == SV_ERR_SHAPE         # src not 16-byte aligned
 
 
 def test_stats_layout_matches_header():

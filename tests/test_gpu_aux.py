@@ -120,3 +120,24 @@ def test_tree_commit_after_verification():
         assert np.array_equal(pos[b], ax.tree_commit_map(nodes[b], n[b], 60)), b
     assert np.all(pos[5] == -1)
     t.close()
+
+
+# ------------------------------------------------------------------ read floor
+
+def test_read_floor_reads_every_byte():
+    """The benchmark's read-floor kernel: data whose words XOR to the kernel's
+    marker value make it store the marker (so the loads reach the data), any
+    other data leave the sink alone; sizes of a partial last tile too."""
+    import draft_token_verification_softmax_amd as svm
+    marker = 0x9E3779B9
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for nbytes in (16, 16384 * 3 + 16, 1 << 20):
+        t = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+        svm.read_floor(t, sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) == 0, nbytes
+        t[0] = np.array(marker, dtype=np.uint32).view(np.int32).item()   # one lane's four words XOR to the marker
+        svm.read_floor(t, sink)
+        torch.cuda.synchronize()
+        assert int(sink.item()) & 0xFFFFFFFF == marker, nbytes
+        sink.zero_()
