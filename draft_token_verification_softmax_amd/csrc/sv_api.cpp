@@ -101,11 +101,14 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, row_lx, seq, spart, wpart, tpart, tview, tcut, go;
+  size_t tiles, cand, nuc, nucc, row_lx, seq, spart, wpart, tpart, tview, tcut, go;
   size_t k_idx, k_e, k_cnt, k_norm, k_bad, k_px, total;
+  int nuc_slots;   // candidate buffers of k_nuc_rows (its most workgroups)
 };
 
-Layout layout(const sv_config* c, const Plan& pl) {
+// The workspace of a call of up to c->max_batch sequences.  nuc_cap bounds the
+// candidate buffers of k_nuc_rows (fewer buffers: fewer resident workgroups).
+Layout layout(const sv_config* c, const Plan& pl, int nuc_cap = sv::kNucGridMax) {
   const size_t B = (size_t)c->max_batch;
   const size_t rows = B * (size_t)(pl.rows_t + pl.rows_d);
   const size_t K = (size_t)pl.top_k;
@@ -120,6 +123,8 @@ Layout layout(const sv_config* c, const Plan& pl) {
   L.cand = take(pl.top_k > 0 ? rows * (size_t)pl.S_max * (size_t)pl.cand_w * sizeof(uint64_t) : 0);
   const bool tfilt = pl.filt == sv::kFiltTreeSample && (pl.top_k > 0 || pl.top_p < 1.0);
   L.nuc = take(pl.filt == sv::kFiltTopp || tfilt ? rows * sizeof(sv::RowNuc) : 0);
+  L.nuc_slots = pl.tile_mode == sv::kModeNucRow ? (int)(rows < (size_t)nuc_cap ? rows : (size_t)nuc_cap) : 0;
+  L.nucc = take((size_t)L.nuc_slots * sv::kNucSlotEntries * sizeof(uint64_t));
   const bool sampled = pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample;
   L.row_lx = take(sampled ? rows * sizeof(float) : 0);
   L.seq = take(sampled ? B * sizeof(sv::SeqState) : 0);
@@ -285,6 +290,8 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
   p.k_px = (double*)(ws + L.k_px);
   p.go = (int32_t*)(ws + L.go);
   p.nucrow = tile_mode == sv::kModeNucRow ? 1 : 0;
+  p.nucc = (uint64_t*)(ws + L.nucc);
+  if (p.nucrow && p.grid > L.nuc_slots) p.grid = L.nuc_slots;   // one buffer per workgroup
 
   const int bf16 = c->dtype == SV_DTYPE_BF16;
   hipError_t e;
@@ -516,7 +523,13 @@ int specverify_run_static(const sv_config* cfg, int32_t batch, const void* targe
   sv_config c = *cfg;
   c.max_batch = batch;
   const Plan pl = make_plan(&c);
-  const Layout L = layout(&c, pl);
+  Layout L = layout(&c, pl);
+  if (L.total > (size_t)SV_STATIC_SCRATCH_BYTES && L.nuc_slots > 0) {
+    // fewer nucleus candidate buffers (fewer resident workgroups) to fit
+    const size_t per = (size_t)sv::kNucSlotEntries * sizeof(uint64_t);
+    const size_t drop = (L.total - (size_t)SV_STATIC_SCRATCH_BYTES + per - 1) / per;
+    if (drop < (size_t)L.nuc_slots) L = layout(&c, pl, L.nuc_slots - (int)drop);
+  }
   if (L.total > (size_t)SV_STATIC_SCRATCH_BYTES) return SV_ERR_SCRATCH;
   char* ws = nullptr;
   int grid = 0;

@@ -75,11 +75,14 @@ struct SeqState {
 // rows of a sampled tree; plain and tree sampling: float64 terms in the rows
 // whose normaliser can change a decision, float32 terms in the others).
 // Chain sampling with top-p alone takes kModeNucRow instead (rows up to
-// kNucMaxV logits): one workgroup per row reads it once and settles its
-// nucleus cut (k_nuc_rows).
+// kNucMaxV logits): persistent workgroups read each row once and settle its
+// nucleus cut (k_nuc_rows), each with a candidate buffer of kNucSlotEntries
+// entries (8 bytes: the raw value and the index) in the workspace.
 enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4, kModeStatsMix = 5,
                 kModeNucRow = 6 };
-constexpr int kNucMaxV = 1 << 20;   // longest rows k_nuc_rows takes (its candidates' 16-bit positions)
+constexpr int kNucMaxV = 1 << 20;        // longest rows k_nuc_rows takes (its buffer holds ~1.5% of them)
+constexpr int kNucSlotEntries = 24576;   // candidate entries per workgroup buffer (192 KB)
+constexpr int kNucGridMax = 1024;        // candidate buffers in a context's workspace (resident workgroups)
 enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4,
               kFiltTreeSample = 5 };
 // Speculative residual passes of tree sampling: pass m (1..kTreePasses)
@@ -128,6 +131,7 @@ struct Params {
   int lazy;
   int32_t* go;       // [B] lazy: 1 if position 0 was accepted (stage 2 reads the rest)
   int nucrow;        // the nucleus rows came from k_nuc_rows (RowNuc holds M and Z of every row)
+  uint64_t* nucc;    // [grid][kNucSlotEntries] k_nuc_rows: each workgroup's candidates (value bits | index << 32)
   // workspace
   TileStat* tiles;   // [rows][P]
   uint64_t* cand;    // [rows][S][cand_w] (top-k): each tile's candidate list

@@ -63,6 +63,7 @@ constexpr int kMaxRows = 2 * 64 + 1;
 
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef unsigned int vu4 __attribute__((ext_vector_type(4)));
+typedef unsigned int vu2 __attribute__((ext_vector_type(2)));
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));
 typedef double d2 __attribute__((ext_vector_type(2)));
 
@@ -3821,21 +3822,24 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows_exact(Params p) {
 
 // ================================================================== nucleus rows in one read
 //
-// k_nuc_rows: one workgroup of kNB threads per row reads the row once and
-// settles its nucleus cut from what it kept on chip (the cut kernels above
-// read a row twice more after the streaming pass; on this chip a second
-// sweep of a row finds nothing of the first one left in any cache).
+// k_nuc_rows: persistent workgroups of kNB threads; workgroup g takes rows
+// g, g + gridDim.x, ...  It reads each row once and settles its nucleus cut
+// from the candidates it kept in its own buffer in the workspace (the cut
+// kernels above read a row twice more after the streaming pass; on this chip
+// a second sweep of a row finds nothing of the first one left in any cache,
+// while a buffer of ~120 KB written and read back by one workgroup stays in
+// L2).  Four workgroups share a compute unit, so the settle of one overlaps
+// the sweeps of the others.
 //  sweep   each lane keeps its running max m and the float64 sum of
 //          2^((l - m) c) as tile_stats does (table exp2, float64 terms), and
-//          every logit >= tau goes to its wave's candidate region in LDS:
-//          the raw value and a 16-bit position (round, lane, slot, element)
-//          from which its index follows.  A region fills in its wave's
-//          program order, so its contents do not depend on timing.  tau is
-//          set from the first round the workgroup reads (a random tenth of a
-//          large row): the 16-bit key prefix at which the round's counts
-//          would put about kNucFill candidates at or above tau over the row.
+//          every logit >= tau goes to its wave's region of the buffer: the
+//          raw value and its index.  A region fills in its wave's program
+//          order, so its contents do not depend on timing.  tau is set from
+//          the first round the workgroup reads (a random share of a large
+//          row): the 16-bit key prefix at which the round's counts would put
+//          about kNucFill candidates at or above tau over the row.
 //  settle  M, Z (fixed-order block sums); the candidates' masses
-//          e = exp((l - M) / T) in float64 go to a fixed-point histogram of
+//          e = exp((l - M) / T) go to a fixed-point histogram of
 //          d = (M - l) / T (the bins of topp_fast) that locates the bin where
 //          the mass from the top reaches top_p Z; the window is that bin and
 //          its two neighbours.  The mass A of the candidates above it is
@@ -3844,28 +3848,26 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows_exact(Params p) {
 // A row it cannot settle (a region full, the cut below tau or outside the
 // window, a window over kNucWin entries) keeps M and Z with ok = kNucFast and
 // k_topp_rows redoes it; an invalid row gets ok = 0.  Rows of more than
-// kNucMaxV logits (the 16-bit positions) take the streaming pass and the cut
-// kernels instead.
-constexpr int kNB = 1024;                     // threads per workgroup
+// kNucMaxV logits take the streaming pass and the cut kernels instead.
+constexpr int kNB = 256;                      // threads per workgroup (four per CU)
 constexpr int kNW = kNB / 64;                 // its waves
-constexpr int kNucRegion = 21 * 64;           // candidate slots per wave
-constexpr int kNucCand = kNW * kNucRegion;    // 21504 candidates: 126 KB of LDS (6 bytes each)
-constexpr int kNucStride = kNucRegion + 1;    // a wave's region and a spare slot
-constexpr int kNucFill = kNucCand * 7 / 10;   // candidates aimed for over a row
+constexpr int kNucRegion = kNucSlotEntries / kNW;   // candidate slots per wave (3072)
+constexpr int kNucFill = 14000;               // candidates aimed for over a row
 constexpr int kNucHist = 2048;                // bins locating the cut among the candidates
 constexpr int kNucWin = kNucHist / 2;         // window slots (the histogram's space, reused)
 constexpr int kNucSample = 2 * kNucHist;      // 16-bit key-prefix bins of the sample (u32)
+constexpr int kNucBatch = 16;                 // candidate loads in flight per lane in the settle
+constexpr int kNucStage = 512;                // candidates one wave can stage in LDS per round
 constexpr double kNucFix = 17592186044416.0;  // 2^44: fixed-point scale of the masses (e <= 1)
-static_assert(kNucFill <= kNucCand, "aim below capacity");
+static_assert(kNucRegion * kNW == kNucSlotEntries, "regions tile the buffer");
+static_assert(3 * kNucFill <= 2 * kNucSlotEntries, "aim at two thirds of the capacity or less");
+static_assert(kNucWin % kNB == 0 && kNucSample % kNB == 0 && kNucHist % kNB == 0, "shapes");
 
 template <typename T> struct NucShape;
-// groups per lane per round: 64 KB per round in flight; the 16-bit position
-// holds the round above (lane, slot, element)
-template <> struct NucShape<float> { static constexpr int U = 2, kSlotBits = 1; };
-template <> struct NucShape<uint16_t> { static constexpr int U = 4, kSlotBits = 2; };
-template <typename T> constexpr int kNucRoundShift = 6 + NucShape<T>::kSlotBits + 3;
-static_assert(kNucMaxV <= (1 << (16 - kNucRoundShift<float>)) * 2 * kNB * kVec, "positions fit 16 bits");
-static_assert(kNucMaxV <= (1 << (16 - kNucRoundShift<uint16_t>)) * 4 * kNB * kVec, "positions fit 16 bits");
+// groups per lane per round: 16 KB (float32) or 8 KB (bf16) per round in
+// flight per workgroup (bf16 with four would spill registers)
+template <> struct NucShape<float> { static constexpr int U = 2; };
+template <> struct NucShape<uint16_t> { static constexpr int U = 2; };
 
 // Block-wide reductions for kNB threads, fixed order; every thread gets the
 // result.  Each starts with a barrier, so `red` can be reused at once.
@@ -3933,24 +3935,23 @@ DEV V nb_exscan(V v, V* red, V* total) {
 //   split (float32 rows read whole): slot u holds two quads kNB * 4 logits
 //   apart, so every 16-byte load of a wave reads 1 KB of consecutive logits;
 //   otherwise slot u holds kVec consecutive logits (group r R + u kNB + t).
-template <int U>
-DEV int nuc_index(int split, int r, int t, int u, int e) {
+template <int U, bool kSplit>
+DEV int nuc_index(int r, int t, int u, int e) {
   constexpr int R = U * kNB;
-  if (!split) return ((r * R + u * kNB + t) * kVec) + e;
+  if (!kSplit) return ((r * R + u * kNB + t) * kVec) + e;
   return r * R * kVec + u * (kNB * kVec) + 4 * t + (e < 4 ? e : kNB * 4 + e - 4);
 }
-template <int U>
+template <int U, bool kSplit>
 struct NucMap {
   int r;
-  int split;
-  DEV int index(int u, int e) const { return nuc_index<U>(split, r, (int)threadIdx.x, u, e); }
+  DEV int index(int u, int e) const { return nuc_index<U, kSplit>(r, (int)threadIdx.x, u, e); }
   // the thread whose slot (*u, *e) holds logit x this round, or -1 (x
   // uniform, so all of it is scalar work)
   DEV int holder(int x, int* u, int* e) const {
     constexpr int R = U * kNB;
     const int rel = x - r * R * kVec;
     if (rel < 0 || rel >= R * kVec) return -1;
-    if (!split) {
+    if (!kSplit) {
       const int g = rel / kVec;
       *u = g / kNB;
       *e = rel % kVec;
@@ -3971,8 +3972,11 @@ struct NucMap {
 // loads issued before the current one is used; others element by element.
 // f(v, map, tail) with tail a std::integral_constant: the round's values
 // (slots past the row hold -inf; only a tail round may have such slots).
-template <typename T, typename F>
-DEV void nuc_sweep(const T* row, int V, int aligned, int r0, F&& f) {
+// pre() runs at the top of every round after the first, before the next
+// round's loads are issued (a store it issues is then older than every load
+// a later wait is for).
+template <typename T, typename F, typename P>
+DEV void nuc_sweep(const T* row, int V, int aligned, int r0, F&& f, P&& pre) {
   constexpr int U = NucShape<T>::U;
   constexpr int R = U * kNB;
   const int tid = threadIdx.x;
@@ -4001,6 +4005,7 @@ DEV void nuc_sweep(const T* row, int V, int aligned, int r0, F&& f) {
     for (int j = 0; j < nr; ++j) {
       int rn = rc + 1;
       if (rn >= nr) rn = 0;
+      if (j > 0) pre();
       if (j + 1 < nr) load_round(nxt, rn);
       float v[U][kVec];
 #pragma unroll
@@ -4022,9 +4027,9 @@ DEV void nuc_sweep(const T* row, int V, int aligned, int r0, F&& f) {
             }
           }
         }
-        f(v, NucMap<U>{rc, kSplit ? 1 : 0}, std::true_type{});
+        f(v, NucMap<U, kSplit>{rc}, std::true_type{});
       } else {
-        f(v, NucMap<U>{rc, kSplit ? 1 : 0}, std::false_type{});
+        f(v, NucMap<U, kSplit>{rc}, std::false_type{});
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
@@ -4034,6 +4039,7 @@ DEV void nuc_sweep(const T* row, int V, int aligned, int r0, F&& f) {
     for (int j = 0; j < nr; ++j) {
       int rc = r0 + j;
       if (rc >= nr) rc -= nr;
+      if (j > 0) pre();
       float v[U][kVec];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -4045,7 +4051,7 @@ DEV void nuc_sweep(const T* row, int V, int aligned, int r0, F&& f) {
           for (int e = 0; e < kVec; ++e) v[u][e] = -INFINITY;
         }
       }
-      f(v, NucMap<U>{rc, 0}, std::true_type{});
+      f(v, NucMap<U, false>{rc}, std::true_type{});
     }
   }
 }
@@ -4078,14 +4084,36 @@ DEV double exp2_64_sum(const float* v, double cs, double nmc, const double* tab)
   return s;
 }
 
+// f(l, idx) for each candidate of this lane in its wave's region (slots
+// lane, lane + 64, ... below n), kNucBatch loads in flight at a time; the
+// order is fixed.  n is uniform over the wave, and so is every call of f's
+// loop (f may hold wave-wide operations: it is called for every batch slot,
+// with valid false past n).  The loads go through the region's buffer
+// resource unconditionally (a slot past the region reads 0), so they issue
+// back to back.
+template <typename F>
+DEV void nuc_each(__amdgpu_buffer_rsrc_t rreg, int n, F&& f) {
+  const int lane = threadIdx.x & 63;
+  for (int s0 = 0; s0 < n; s0 += 64 * kNucBatch) {
+    vu2 c[kNucBatch];
+#pragma unroll
+    for (int q = 0; q < kNucBatch; ++q)
+      c[q] = __builtin_bit_cast(vu2, __builtin_amdgcn_raw_buffer_load_b64(rreg, (s0 + 64 * q + lane) * 8, 0, 0));
+#pragma unroll
+    for (int q = 0; q < kNucBatch; ++q) {
+      const int sl = s0 + 64 * q + lane;
+      f(sl < n, __uint_as_float(c[q].x), (int)c[q].y);
+    }
+  }
+}
+
 template <typename T>
-__global__ __launch_bounds__(kNB) void k_nuc_rows(Params p) {
+__global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
   constexpr int U = NucShape<T>::U;
   constexpr int R = U * kNB;                  // groups per round
-  constexpr int kRS = kNucRoundShift<T>;
-  __shared__ float cval[kNW * kNucStride];    // candidate values
-  __shared__ uint16_t cpos[kNW * kNucStride]; // their positions: round << kRS | lane << (slot bits + 3) | slot << 3 | element
   __shared__ uint64_t hist[kNucHist];         // sample counts (u32), then masses, then the window
+  __shared__ float stv[kNW][kNucStage + 1];   // each wave's candidates of its last round (and a spare slot)
+  __shared__ uint32_t sti[kNW][kNucStage + 1];
   __shared__ double tab[kExpTab];
   __shared__ double redd[kNW];
   __shared__ uint64_t redu[kNW];
@@ -4093,277 +4121,307 @@ __global__ __launch_bounds__(kNB) void k_nuc_rows(Params p) {
   __shared__ int redi[kNW];
   __shared__ int sh_nw;
   __shared__ double sh_N;
-  const int grow = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int V = p.V;
-  const T* row = row_ptr<T>(p, grow);
-  bool xhas;
-  const int xs = __builtin_amdgcn_readfirstlane(row_token(p, grow, &xhas));   // uniform over the row
+  const int nrows = p.B * (p.rows_t + p.rows_d);
+  // this wave's region of this workgroup's buffer; the flushes store through
+  // a buffer resource spanning the region, which drops stores past its end
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint64_t* reg = p.nucc + (size_t)blockIdx.x * kNucSlotEntries + (size_t)wu * kNucRegion;
+  const __amdgpu_buffer_rsrc_t rreg = make_rsrc(reg, kNucRegion * (int)sizeof(uint64_t));
+  float* sv = stv[wu];
+  uint32_t* si = sti[wu];
   if (tid < kExpTab) tab[tid] = kExp2Tab[tid];
+  __syncthreads();
   const double cd = kLog2e / p.T;
   const double cs = kExpScale * cd;
+  const double invT = 1.0 / p.T;
   const int ngroups = (V + kVec - 1) / kVec;
   const int nr = (ngroups + R - 1) / R;
   const int nfr = (V / kVec) / R;             // rounds of whole groups only
-  const int split = (sizeof(T) == 4 && p.aligned && V % kVec == 0 && V >= kVec) ? 1 : 0;   // as nuc_sweep
-  // start at a whole round (its values set tau); rows start at different
-  // rounds so that workgroups in step do not hit the same memory channels
-  const int r0 = nfr > 0 ? (int)(((long)grow * 7) % nfr) : 0;
-  float m = -INFINITY;
-  double s = 0.0;
-  bool nan_seen = false;
-  float lx = 0.f;
-  bool hx = false;
-  int cw = 0;                                 // candidates met by this wave (uniform)
-  float tau = -INFINITY;
-  bool first = true;
-  float* rval = cval + w * kNucStride;
-  uint16_t* rpos = cpos + w * kNucStride;
-  nuc_sweep<T>(row, V, p.aligned, r0, [&](float (&v)[U][kVec], const NucMap<U>& mp, auto tailc) {
-    constexpr bool kTail = decltype(tailc)::value;
-    // max over the round, NaN evidence, the drafted token's logit
-    float mi = m;
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const float gm = maximum8(v[u]);
-      nan_seen |= gm != gm;
-      mi = gm > mi ? gm : mi;
-    }
-    if (xhas) {
-      // the one lane (if any) whose slots hold token xs this round
-      int ux = 0, ex = 0;
-      if (mp.holder(xs, &ux, &ex) == tid) {
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-#pragma unroll
-          for (int e = 0; e < kVec; ++e) lx = (u == ux && e == ex) ? v[u][e] : lx;
-        }
-        hx = true;
+  for (int grow = blockIdx.x; grow < nrows; grow += gridDim.x) {
+    const T* row = row_ptr<T>(p, grow);
+    bool xhas;
+    const int xs = __builtin_amdgcn_readfirstlane(row_token(p, grow, &xhas));   // uniform over the row
+    // start at a whole round (its values set tau); rows start at different
+    // rounds so that workgroups in step do not hit the same memory channels
+    const int r0 = nfr > 0 ? (int)(((long)grow * 7) % nfr) : 0;
+    float m = -INFINITY;
+    double s = 0.0;
+    bool nan_seen = false;
+    float lx = 0.f;
+    bool hx = false;
+    int cw = 0;                               // candidates met by this wave (uniform)
+    int cs0 = 0;                              // ... of which flushed to the region
+    bool over = false;                        // a round held more than kNucStage
+    float tau = -INFINITY;
+    bool first = true;
+    // the staged candidates of the last round to the region, entries
+    // lane, lane + 64, ... (coalesced 8-byte stores; past the region dropped)
+    // (the stage is the wave's own: its LDS accesses run in program order,
+    // and the wave barriers keep the compiler from moving them across)
+    auto flush = [&]() {
+      __builtin_amdgcn_wave_barrier();
+      const int n = cw - cs0 < kNucStage ? cw - cs0 : kNucStage;
+      for (int i = lane; i < n; i += 64) {
+        const vu2 ent = {__float_as_uint(sv[i]), si[i]};
+        __builtin_amdgcn_raw_buffer_store_b64(ent, rreg, (cs0 + i) * 8, 0, 0);
       }
-    }
-    if (mi > m) {
-      // (the table exp2: exp2_neg's constants would stay in registers all loop long)
-      if (m > -INFINITY) s *= exp2_64(((double)m - (double)mi) * cs, tab);
-      m = mi;
-    }
-    if (first) {
-      first = false;
-      if (nr > 1) {
-        // tau from this (whole) round: counts of 16-bit key prefixes below the round max's
-        const float rmax = nb_max(mi, redf);
-        uint32_t* hs = reinterpret_cast<uint32_t*>(hist);
-        for (int b = tid; b < kNucSample; b += kNB) hs[b] = 0u;
-        __syncthreads();
-        const uint32_t top = ord_key(rmax) >> 16;
+      cs0 = cw;
+      __builtin_amdgcn_wave_barrier();
+    };
+    nuc_sweep<T>(row, V, p.aligned, r0, [&](float (&v)[U][kVec], const auto& mp, auto tailc) {
+      constexpr bool kTail = decltype(tailc)::value;
+      // max over the round, NaN evidence, the drafted token's logit
+      float mi = m;
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
+      for (int u = 0; u < U; ++u) {
+        const float gm = maximum8(v[u]);
+        nan_seen |= gm != gm;
+        mi = gm > mi ? gm : mi;
+      }
+      if (xhas) {
+        // the one lane (if any) whose slots hold token xs this round
+        int ux = 0, ex = 0;
+        if (mp.holder(xs, &ux, &ex) == tid) {
 #pragma unroll
-          for (int e = 0; e < kVec; ++e) {
-            const float x = v[u][e];
-            if (x == x) {
-              const uint32_t d = top - (ord_key(x) >> 16);
-              atomicAdd(&hs[d < (uint32_t)(kNucSample - 1) ? d : (uint32_t)(kNucSample - 1)], 1u);
+          for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) lx = (u == ux && e == ex) ? v[u][e] : lx;
+          }
+          hx = true;
+        }
+      }
+      if (mi > m) {
+        // (the table exp2: exp2_neg's constants would stay in registers all loop long)
+        if (m > -INFINITY) s *= exp2_64(((double)m - (double)mi) * cs, tab);
+        m = mi;
+      }
+      if (first) {
+        first = false;
+        if (nr > 1) {
+          // tau from this (whole) round: counts of 16-bit key prefixes below the round max's
+          const float rmax = nb_max(mi, redf);
+          uint32_t* hs = reinterpret_cast<uint32_t*>(hist);
+          for (int b = tid; b < kNucSample; b += kNB) hs[b] = 0u;
+          __syncthreads();
+          const uint32_t top = ord_key(rmax) >> 16;
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int e = 0; e < kVec; ++e) {
+              const float x = v[u][e];
+              if (x == x) {
+                const uint32_t d = top - (ord_key(x) >> 16);
+                atomicAdd(&hs[d < (uint32_t)(kNucSample - 1) ? d : (uint32_t)(kNucSample - 1)], 1u);
+              }
             }
           }
-        }
-        __syncthreads();
-        // the first prefix bin at which the count from the top reaches want
-        const int want = (int)((long)kNucFill * (long)(R * kVec) / (long)V);
-        constexpr int per = kNucSample / kNB;
-        uint32_t c[per];
-        uint32_t tl = 0;
+          __syncthreads();
+          // the first prefix bin at which the count from the top reaches want
+          const int want = (int)((long)kNucFill * (long)(R * kVec) / (long)V);
+          constexpr int per = kNucSample / kNB;
+          uint32_t c[per];
+          uint32_t tl = 0;
 #pragma unroll
-        for (int q = 0; q < per; ++q) { c[q] = hs[tid * per + q]; tl += c[q]; }
-        uint32_t tot;
-        uint32_t run = nb_exscan<uint32_t>(tl, reinterpret_cast<uint32_t*>(redi), &tot);
+          for (int q = 0; q < per; ++q) { c[q] = hs[tid * per + q]; tl += c[q]; }
+          uint32_t tot;
+          uint32_t run = nb_exscan<uint32_t>(tl, reinterpret_cast<uint32_t*>(redi), &tot);
+          int found = INT_MAX;
+#pragma unroll
+          for (int q = 0; q < per; ++q) {
+            run += c[q];
+            if (found == INT_MAX && run >= (uint32_t)want) found = tid * per + q;
+          }
+          const int bsel = nb_min<int>(found, redi);
+          if (bsel != INT_MAX && rmax == rmax && rmax > -INFINITY) {
+            // every value whose key prefix is >= top - bsel (a prefix below
+            // 0x0080 would decode to a NaN: such a tau takes everything finite)
+            uint32_t pk = top >= (uint32_t)bsel ? top - (uint32_t)bsel : 0u;
+            pk = pk < 0x0080u ? 0x0080u : pk;
+            tau = key_value(pk << 16);
+          }
+        }
+      }
+      // float64 terms, in batches of four (eight hold too many registers)
+      if (m > -INFINITY) {
+        const double nmc = -(double)m * cs;
+        double gs = 0.0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          gs += exp2_64_sum<kVec / 2>(v[u], cs, nmc, tab);
+          gs += exp2_64_sum<kVec / 2>(v[u] + kVec / 2, cs, nmc, tab);
+        }
+        s += gs;
+      }
+      // candidates to the wave's stage: one ballot per element slot; a
+      // taking lane's slot is the round's count so far plus the lanes below
+      // taking the same element slot (past kNucStage: the spare slot, and
+      // the row is redone)
+      int cr = 0;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+#pragma unroll
+        for (int e = 0; e < kVec; ++e) {
+          bool take = v[u][e] >= tau;
+          if constexpr (kTail) take = take && mp.index(u, e) < V;
+          const uint64_t bm = __builtin_amdgcn_ballot_w64(take);
+          if (take) {
+            int slot = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((unsigned)bm, (unsigned)cr));
+            slot = slot < kNucStage ? slot : kNucStage;
+            sv[slot] = v[u][e];
+            si[slot] = (uint32_t)mp.index(u, e);
+          }
+          cr += (int)__popcll(bm);
+        }
+      }
+      over |= cr > kNucStage;
+      cw += cr;
+    }, flush);
+    flush();
+    // ---- settle (every early return is uniform over the workgroup)
+    if (xhas && hx) p.row_lx[grow] = lx;
+    auto settle = [&]() -> RowNuc {
+      const bool bad_nan = __syncthreads_or(nan_seen) != 0;   // (also publishes the regions)
+      const int nc = cw < kNucRegion ? cw : kNucRegion;
+      auto each = [&](auto&& f) { nuc_each(rreg, nc, f); };
+      const float M = nb_max(m, redf);
+      const bool bad = bad_nan || !(M > -INFINITY) || !(M < INFINITY);
+      double zl = 0.0;
+      if (!bad && m > -INFINITY) zl = s * exp2_neg(((double)m - (double)M) * cd);
+      const double Z = nb_sum(zl, redd);
+      RowNuc out;
+      out.Z = Z; out.N = 0.0; out.cut = 0ull; out.M = M;
+      out.ok = bad ? 0 : kNucFast;
+      const bool full = __syncthreads_or(cw > kNucRegion || over) != 0;
+      if (bad || full) return out;
+      const double tgt = p.top_p * Z;
+      const double zm = (double)M * invT;
+      // bins of d = (M - l) / T over [0, dspan): every kept logit has
+      // d < ln(V / ((1 - top_p) Z)) + 1 (the tokens below that hold less than
+      // 1 - top_p of the mass together); candidates reach down to tau
+      double dmaxd = log((double)V / ((1.0 - p.top_p) * Z)) + 1.0;
+      if (!(dmaxd > 1.0)) dmaxd = 1.0;
+      const double dtau = tau > -INFINITY ? ((double)M - (double)tau) * invT : dmaxd;
+      double dspan = dtau < dmaxd ? dtau : dmaxd;
+      if (!(dspan > 0.0)) dspan = 1e-30;
+      const float invw = (float)((double)kNucHist / dspan);
+      const float a1 = (float)(-invT) * invw, b1 = (float)zm * invw;
+      // the bin tau falls in: bins below it hold only logits > tau (monotone
+      // fma), all of them candidates
+      int bin_tau = INT_MAX;
+      if (tau > -INFINITY) {
+        const float pt = fmaf(tau, a1, b1);
+        bin_tau = pt < (float)kNucHist ? (int)__builtin_amdgcn_fmed3f(pt, 0.f, (float)(kNucHist - 1)) : kNucHist;
+      }
+      const bool no_fix = !(tgt < (double)kNucSlotEntries);   // the candidates cannot hold that much mass
+      const uint64_t tgt_fix = no_fix ? 0ull : (uint64_t)(tgt * kNucFix);
+      auto bin_of = [&](float l) {
+        const float pos = fmaf(l, a1, b1);
+        return pos < (float)kNucHist ? (int)__builtin_amdgcn_fmed3f(pos, 0.f, (float)(kNucHist - 1)) : INT_MAX;
+      };
+      // e = exp((l - M) / T) = 2^((l - M) c): the table exp2, as the sweep's terms
+      const double nmcM = -(double)M * cs;
+      auto mass_of = [&](float l) { return exp2_64(fma((double)l, cs, nmcM), tab); };
+      // the histogram only locates the window (its bin and the two around
+      // it), so its masses are the hardware float32 exp2 of (l - M) c
+      // (relative error near 1e-7, far inside a bin's mass); A and the
+      // window's walk below take float64 masses
+      const float M32 = M, c32 = (float)cd;
+      for (int b = tid; b < kNucHist; b += kNB) hist[b] = 0ull;
+      __syncthreads();
+      each([&](bool valid, float l, int) {
+        const int b = bin_of(l);
+        if (valid && b != INT_MAX) {
+          const float e32 = __builtin_amdgcn_exp2f((l - M32) * c32);
+          atomicAdd(reinterpret_cast<unsigned long long*>(&hist[b]), (unsigned long long)((double)e32 * kNucFix));
+        }
+      });
+      __syncthreads();
+      // the bin where the mass from the top reaches top_p Z
+      int bc;
+      {
+        constexpr int per = kNucHist / kNB;
+        uint64_t h[per];
+        uint64_t hl = 0;
+#pragma unroll
+        for (int q = 0; q < per; ++q) { h[q] = hist[tid * per + q]; hl += h[q]; }
+        uint64_t tot;
+        uint64_t run = nb_exscan<uint64_t>(hl, redu, &tot);
         int found = INT_MAX;
+        if (!no_fix) {
 #pragma unroll
-        for (int q = 0; q < per; ++q) {
-          run += c[q];
-          if (found == INT_MAX && run >= (uint32_t)want) found = tid * per + q;
+          for (int q = 0; q < per; ++q) {
+            run += h[q];
+            if (found == INT_MAX && run >= tgt_fix) found = tid * per + q;
+          }
         }
-        const int bsel = nb_min<int>(found, redi);
-        if (bsel != INT_MAX && rmax == rmax && rmax > -INFINITY) {
-          // every value whose key prefix is >= top - bsel (a prefix below
-          // 0x0080 would decode to a NaN: such a tau takes everything finite)
-          uint32_t pk = top >= (uint32_t)bsel ? top - (uint32_t)bsel : 0u;
-          pk = pk < 0x0080u ? 0x0080u : pk;
-          tau = key_value(pk << 16);
-        }
-      } else {
-        __syncthreads();   // the table
+        bc = nb_min<int>(found, redi);
       }
-    }
-    // float64 terms, in batches of eight
-    if (m > -INFINITY) {
-      const double nmc = -(double)m * cs;
-      double gs = 0.0;
-#pragma unroll
-      for (int u = 0; u < U; ++u) gs += exp2_64_sum<kVec>(v[u], cs, nmc, tab);
-      s += gs;
-    }
-    // candidates: one ballot per element slot; a taking lane's slot in the
-    // region is the wave's count so far plus the lanes below taking the same
-    // element slot.  Only taking lanes store (a slot past the region is
-    // clamped to the spare one: the row then counts as full and is redone).
-    const uint32_t pbase = ((uint32_t)mp.r << kRS) | ((uint32_t)lane << (NucShape<T>::kSlotBits + 3));
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) {
-        bool take = v[u][e] >= tau;
-        if constexpr (kTail) take = take && mp.index(u, e) < V;
-        const uint64_t bm = __builtin_amdgcn_ballot_w64(take);
-        if (take) {
-          int slot = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bm, (unsigned)cw));
-          slot = slot < kNucRegion ? slot : kNucRegion;
-          rval[slot] = v[u][e];
-          rpos[slot] = (uint16_t)(pbase | (uint32_t)(u << 3) | (uint32_t)e);
-        }
-        cw += (int)__popcll(bm);
+      const int lo = bc > 0 ? bc - 1 : 0;
+      const int hi = bc < kNucHist - 1 ? bc + 1 : kNucHist - 1;
+      if (bc == INT_MAX || hi >= bin_tau) return out;   // the cut lies below tau
+      // the exact mass above the window (fixed order: the lane's slots, then
+      // the block sum), the window's keys gathered
+      if (tid == 0) sh_nw = 0;
+      __syncthreads();
+      uint64_t* wl = hist;                 // unsorted window keys
+      uint64_t* ws = hist + kNucWin;       // the same, ranked
+      double al = 0.0;
+      each([&](bool valid, float l, int idx) {
+        const int b = valid ? bin_of(l) : INT_MAX;
+        if (b < lo) al += mass_of(l);
+        const bool inw = b >= lo && b <= hi;
+        const int at = wave_append(inw, &sh_nw);
+        if (inw && at < kNucWin) wl[at] = pack(l, idx);
+      });
+      const double A = nb_sum(al, redd);   // (its barriers also publish the window)
+      const int nw = sh_nw;
+      if (nw == 0 || nw > kNucWin) return out;
+      // rank of each window key (keys are distinct: the index is part of the key)
+      for (int i = tid; i < nw; i += kNB) {
+        const uint64_t k = wl[i];
+        int r = 0;
+        for (int j = 0; j < nw; ++j) r += wl[j] > k ? 1 : 0;
+        ws[r] = k;
       }
-    }
-  });
-  // ---- settle
-  if (xhas && hx) p.row_lx[grow] = lx;
-  const bool bad_nan = __syncthreads_or(nan_seen) != 0;
-  const float M = nb_max(m, redf);
-  const bool bad = bad_nan || !(M > -INFINITY) || !(M < INFINITY);
-  double zl = 0.0;
-  if (!bad && m > -INFINITY) zl = s * exp2_neg(((double)m - (double)M) * cd);
-  const double Z = nb_sum(zl, redd);
-  RowNuc out;
-  out.Z = Z; out.N = 0.0; out.cut = 0ull; out.M = M;
-  out.ok = bad ? 0 : kNucFast;
-  const bool full = __syncthreads_or(cw > kNucRegion) != 0;
-  if (bad || full) {
+      __syncthreads();
+      // thread t walks ranks t kPerT .. t kPerT + kPerT - 1
+      constexpr int kPerT = kNucWin / kNB;
+      double e[kPerT];
+      double et = 0.0;
+#pragma unroll
+      for (int q = 0; q < kPerT; ++q) {
+        const int i = tid * kPerT + q;
+        e[q] = i < nw ? mass_of(packed_val(ws[i])) : 0.0;
+        et += e[q];
+      }
+      double wtot;
+      double c0 = A + nb_exscan<double>(et, redd, &wtot);
+      int kept_l = 0;
+      double n_l = 0.0;
+#pragma unroll
+      for (int q = 0; q < kPerT; ++q) {
+        const int i = tid * kPerT + q;
+        if (i < nw && c0 < tgt) { kept_l = i + 1; n_l = c0 + e[q]; }
+        c0 += e[q];
+      }
+      const int kept = nb_max_i<int>(kept_l, redi);
+      const bool inside = kept > 0 && (kept < nw || A + wtot >= tgt);
+      if (inside && kept_l == kept) sh_N = n_l;
+      __syncthreads();
+      if (inside) {
+        out.N = sh_N;
+        out.cut = ws[kept - 1];
+        out.ok = 1;
+      }
+      return out;
+    };
+    const RowNuc out = settle();
     if (tid == 0) p.nuc[grow] = out;
-    return;
+    __syncthreads();   // the next row reuses hist and the buffer
   }
-  const double tgt = p.top_p * Z;
-  const double invT = 1.0 / p.T;
-  const double zm = (double)M * invT;
-  // bins of d = (M - l) / T over [0, dspan): every kept logit has
-  // d < ln(V / ((1 - top_p) Z)) + 1 (the tokens below that hold less than
-  // 1 - top_p of the mass together); candidates reach down to tau
-  double dmaxd = log((double)V / ((1.0 - p.top_p) * Z)) + 1.0;
-  if (!(dmaxd > 1.0)) dmaxd = 1.0;
-  const double dtau = tau > -INFINITY ? ((double)M - (double)tau) * invT : dmaxd;
-  double dspan = dtau < dmaxd ? dtau : dmaxd;
-  if (!(dspan > 0.0)) dspan = 1e-30;
-  const float invw = (float)((double)kNucHist / dspan);
-  const float a1 = (float)(-invT) * invw, b1 = (float)zm * invw;
-  // the bin tau falls in: bins below it hold only logits > tau (monotone
-  // fma), all of them candidates
-  int bin_tau = INT_MAX;
-  if (tau > -INFINITY) {
-    const float pt = fmaf(tau, a1, b1);
-    bin_tau = pt < (float)kNucHist ? (int)__builtin_amdgcn_fmed3f(pt, 0.f, (float)(kNucHist - 1)) : kNucHist;
-  }
-  const bool no_fix = !(tgt < (double)kNucCand);   // the candidates cannot hold that much mass
-  const uint64_t tgt_fix = no_fix ? 0ull : (uint64_t)(tgt * kNucFix);
-  for (int b = tid; b < kNucHist; b += kNB) hist[b] = 0ull;
-  __syncthreads();
-  const int nc = cw;
-  constexpr int kPer = kNucRegion / 64;
-  auto bin_of = [&](float l) {
-    const float pos = fmaf(l, a1, b1);
-    return pos < (float)kNucHist ? (int)__builtin_amdgcn_fmed3f(pos, 0.f, (float)(kNucHist - 1)) : INT_MAX;
-  };
-  // e = exp((l - M) / T) = 2^((l - M) c): the table exp2, as the sweep's terms
-  const double nmcM = -(double)M * cs;
-  auto mass_of = [&](float l) { return exp2_64(fma((double)l, cs, nmcM), tab); };
-  // the histogram only locates the window (its bin and the two around it),
-  // so its masses are the hardware float32 exp2 of (l - M) c (relative error
-  // near 1e-7, far inside a bin's mass); A and the window's walk below take
-  // float64 masses.  Each lane's candidates sit in slots lane, lane + 64, ...
-  const float M32 = M, c32 = (float)cd;
-  int bq[kPer];
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int sl = lane + 64 * q;
-    bq[q] = INT_MAX;
-    if (sl < nc) {
-      const float l = rval[sl];
-      bq[q] = bin_of(l);
-      if (bq[q] != INT_MAX) {
-        const float e32 = __builtin_amdgcn_exp2f((l - M32) * c32);
-        atomicAdd(reinterpret_cast<unsigned long long*>(&hist[bq[q]]), (unsigned long long)((double)e32 * kNucFix));
-      }
-    }
-  }
-  __syncthreads();
-  // the bin where the mass from the top reaches top_p Z
-  int bc;
-  {
-    const uint64_t h0 = hist[2 * tid], h1 = hist[2 * tid + 1];
-    uint64_t tot;
-    const uint64_t ex = nb_exscan<uint64_t>(h0 + h1, redu, &tot);
-    int found = INT_MAX;
-    if (!no_fix) {
-      if (ex + h0 >= tgt_fix) found = 2 * tid;
-      else if (ex + h0 + h1 >= tgt_fix) found = 2 * tid + 1;
-    }
-    bc = nb_min<int>(found, redi);
-  }
-  const int lo = bc > 0 ? bc - 1 : 0;
-  const int hi = bc < kNucHist - 1 ? bc + 1 : kNucHist - 1;
-  if (bc == INT_MAX || hi >= bin_tau) {
-    if (tid == 0) p.nuc[grow] = out;   // the cut lies below tau
-    return;
-  }
-  // the exact mass above the window (fixed order: the lane's slots, then
-  // the block sum), the window's keys gathered
-  if (tid == 0) sh_nw = 0;
-  __syncthreads();
-  uint64_t* wl = hist;                 // unsorted window keys
-  uint64_t* ws = hist + kNucWin;       // the same, ranked
-  double al = 0.0;
-#pragma unroll
-  for (int q = 0; q < kPer; ++q) {
-    const int sl = lane + 64 * q;
-    const int b = bq[q];
-    if (b < lo) al += mass_of(rval[sl]);
-    const bool inw = b >= lo && b <= hi;
-    const int at = wave_append(inw, &sh_nw);
-    if (inw && at < kNucWin) {
-      const float l = rval[sl];
-      const uint32_t ps = rpos[sl];
-      const int rr = (int)(ps >> kRS);
-      const int ln = (int)((ps >> (NucShape<T>::kSlotBits + 3)) & 63u);
-      const int uu = (int)((ps >> 3) & ((1u << NucShape<T>::kSlotBits) - 1u));
-      const int ee = (int)(ps & 7u);
-      wl[at] = pack(l, nuc_index<U>(split, rr, w * 64 + ln, uu, ee));
-    }
-  }
-  const double A = nb_sum(al, redd);   // (its barriers also publish the window)
-  const int nw = sh_nw;
-  if (nw == 0 || nw > kNucWin) {
-    if (tid == 0) p.nuc[grow] = out;
-    return;
-  }
-  // rank of each window key (keys are distinct: the index is part of the key)
-  if (tid < nw) {
-    const uint64_t k = wl[tid];
-    int r = 0;
-    for (int j = 0; j < nw; ++j) r += wl[j] > k ? 1 : 0;
-    ws[r] = k;
-  }
-  __syncthreads();
-  double e = 0.0;
-  if (tid < nw) e = mass_of(packed_val(ws[tid]));
-  double wtot;
-  const double c0 = A + nb_exscan<double>(e, redd, &wtot);
-  const int kept_l = (tid < nw && c0 < tgt) ? tid + 1 : 0;
-  const int kept = nb_max_i<int>(kept_l, redi);
-  const bool inside = kept > 0 && (kept < nw || A + wtot >= tgt);
-  if (inside && tid == kept - 1) sh_N = c0 + e;
-  __syncthreads();
-  if (inside) {
-    out.N = sh_N;
-    out.cut = ws[kept - 1];
-    out.ok = 1;
-  }
-  if (tid == 0) p.nuc[grow] = out;
 }
 
 // ================================================================== launchers
@@ -4394,8 +4452,9 @@ static hipError_t launch_stream_t(const Params& p, int mode, hipStream_t st, hip
                                                          : (long)p.B * (p.rows_t + p.rows_d);
   const unsigned grid = (unsigned)(rows * p.S);
   const dim3 block(kBlock);
-  if (mode == kModeNucRow)
-    hipExtLaunchKernelGGL((k_nuc_rows<T>), dim3((unsigned)rows), dim3(kNB), 0, st, e0, e1, 0, p);
+  if (mode == kModeNucRow)   // persistent: p.grid workgroups (one candidate buffer each) or one per row
+    hipExtLaunchKernelGGL((k_nuc_rows<T>), dim3((unsigned)(rows < p.grid ? rows : p.grid)), dim3(kNB), 0, st,
+                          e0, e1, 0, p);
   else if (mode == kModeStats64)
     hipExtLaunchKernelGGL((k_stream<T, kModeStats64>), dim3(grid), block, 0, st, e0, e1, 0, p);
   else if (mode == kModeStatsMix)

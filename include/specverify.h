@@ -203,7 +203,11 @@ int specverify_run(specverify_ctx* ctx, int32_t batch,
  * device looks up that device's array address and compute-unit count once.
  * Arguments, outputs and errors as specverify_run, plus SV_ERR_SCRATCH when
  * the call's workspace -- specverify_workspace_bytes of cfg with max_batch set
- * to batch -- exceeds SV_STATIC_SCRATCH_BYTES (no HIP call is made then).  Every call on one
+ * to batch -- exceeds SV_STATIC_SCRATCH_BYTES (no HIP call is made then).
+ * Chain sampling with top-p alone is the exception: its workspace holds one
+ * 192 KB candidate buffer per workgroup of the nucleus kernel, and when they
+ * do not all fit, the call runs that kernel with as many workgroups as fit
+ * (the same results, fewer rows in flight).  Every call on one
  * device shares that device's array and leaves its contents behind; no
  * kernel reads workspace it has not written in the same call, so nothing
  * needs clearing between calls.  Calls that overlap in time on one device

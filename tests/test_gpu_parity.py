@@ -197,13 +197,14 @@ def test_sample_topp(B, V, k, top_p, dtype):
 
 
 @pytest.mark.parametrize("B,V,k,top_p,dtype", [
-    # the one-read nucleus kernel sweeps a row in rounds of 16384 float32
-    # logits (each lane two quads 4096 apart per slot) or 32768 bf16 ones,
+    # the one-read nucleus kernel sweeps a row in rounds of 4096 logits
+    # (float32: each lane two quads 1024 apart per slot; bf16: whole groups)
     # and sets its candidate threshold from the first whole round it reads
-    (6, 20488, 3, 0.9, "f32"),          # a whole round and a ragged one
-    (6, 40000, 2, 0.9, "f32"),          # three rounds, the last a few quads
+    (6, 6152, 3, 0.9, "f32"),           # a whole round and a ragged one
+    (6, 8208, 2, 0.9, "f32"),           # three rounds, the last four quads
+    (6, 40000, 2, 0.9, "f32"),          # ten rounds, the last ragged
     (6, 70001, 2, 0.9, "bf16"),         # a half group at the end: element path
-    (6, 98304, 2, 0.8, "bf16"),         # three whole rounds
+    (6, 12288, 2, 0.8, "bf16"),         # three whole rounds
     (4, 152064, 2, 0.95, "f32"),
 ])
 def test_sample_topp_row_rounds(B, V, k, top_p, dtype):

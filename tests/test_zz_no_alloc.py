@@ -115,6 +115,10 @@ CASES = {
     "plain sampling, workload 2 shape": lambda s: _chain_case(2, (16, 5)[s], 32000, 5, "bf16", 1.0, 0, 1.0, 61 + s),
     "top-k 50, V = 128256": lambda s: _chain_case(3, (12, 3)[s], 128256, 8, "bf16", 0.7, 50, 1.0, 62 + s),
     "nucleus 0.9, V = 152064 fp32": lambda s: _chain_case(5, (8, 2)[s], 152064, 4, "f32", 0.8, 0, 0.9, 63 + s),
+    # more rows than the static array holds candidate buffers for: the static
+    # call runs the one-read nucleus kernel with fewer workgroups
+    "nucleus 0.9, 640 and 500 rows": lambda s: _chain_case(5, (128, 100)[s], 152064, 2, "f32", 0.8, 0, 0.9,
+                                                             67 + s),
     "greedy chain": lambda s: _greedy_case((32, 5)[s], 32000, 4, 64 + s),
     "tree greedy": lambda s: _tree_case((8, 3)[s], 60, 128256, "bf16", False, 65 + s),
     "tree sampling": lambda s: _tree_case((6, 2)[s], 30, 8192, "bf16", True, 66 + s),
