@@ -4112,8 +4112,9 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
   constexpr int U = NucShape<T>::U;
   constexpr int R = U * kNB;                  // groups per round
   __shared__ uint64_t hist[kNucHist];         // sample counts (u32), then masses, then the window
-  __shared__ float stv[kNW][kNucStage + 1];   // each wave's candidates of its last round (and a spare slot)
-  __shared__ uint32_t sti[kNW][kNucStage + 1];
+  // each wave's candidates of its last round: values, then indices, kNucStage
+  // slots each and one spare slot per lane (where lanes that do not take write)
+  __shared__ uint32_t stg[kNW][2][kNucStage + 64];
   __shared__ double tab[kExpTab];
   __shared__ double redd[kNW];
   __shared__ uint64_t redu[kNW];
@@ -4129,8 +4130,8 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
   const int wu = __builtin_amdgcn_readfirstlane(w);
   uint64_t* reg = p.nucc + (size_t)blockIdx.x * kNucSlotEntries + (size_t)wu * kNucRegion;
   const __amdgpu_buffer_rsrc_t rreg = make_rsrc(reg, kNucRegion * (int)sizeof(uint64_t));
-  float* sv = stv[wu];
-  uint32_t* si = sti[wu];
+  uint32_t* sv = stg[wu][0];
+  uint32_t* si = stg[wu][1];
   if (tid < kExpTab) tab[tid] = kExp2Tab[tid];
   __syncthreads();
   const double cd = kLog2e / p.T;
@@ -4164,7 +4165,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       __builtin_amdgcn_wave_barrier();
       const int n = cw - cs0 < kNucStage ? cw - cs0 : kNucStage;
       for (int i = lane; i < n; i += 64) {
-        const vu2 ent = {__float_as_uint(sv[i]), si[i]};
+        const vu2 ent = {sv[i], si[i]};
         __builtin_amdgcn_raw_buffer_store_b64(ent, rreg, (cs0 + i) * 8, 0, 0);
       }
       cs0 = cw;
@@ -4254,10 +4255,10 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
         }
         s += gs;
       }
-      // candidates to the wave's stage: one ballot per element slot; a
-      // taking lane's slot is the round's count so far plus the lanes below
-      // taking the same element slot (past kNucStage: the spare slot, and
-      // the row is redone)
+      // candidates to the wave's stage, without branches: one ballot per
+      // element slot; a taking lane's slot is the round's count so far plus
+      // the lanes below taking the same element slot (clamped: a round past
+      // kNucStage has the row redone), every other lane writes its spare slot
       int cr = 0;
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -4266,13 +4267,11 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
           bool take = v[u][e] >= tau;
           if constexpr (kTail) take = take && mp.index(u, e) < V;
           const uint64_t bm = __builtin_amdgcn_ballot_w64(take);
-          if (take) {
-            int slot = (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32),
-                                                      __builtin_amdgcn_mbcnt_lo((unsigned)bm, (unsigned)cr));
-            slot = slot < kNucStage ? slot : kNucStage;
-            sv[slot] = v[u][e];
-            si[slot] = (uint32_t)mp.index(u, e);
-          }
+          const unsigned rank = __builtin_amdgcn_mbcnt_hi((unsigned)(bm >> 32), __builtin_amdgcn_mbcnt_lo((unsigned)bm, 0u));
+          const unsigned at = (unsigned)cr + rank;
+          const unsigned slot = take ? (at < (unsigned)kNucStage ? at : (unsigned)(kNucStage - 1)) : (unsigned)(kNucStage + lane);
+          sv[slot] = __float_as_uint(v[u][e]);
+          si[slot] = (uint32_t)mp.index(u, e);
           cr += (int)__popcll(bm);
         }
       }
@@ -4379,6 +4378,51 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       const double A = nb_sum(al, redd);   // (its barriers also publish the window)
       const int nw = sh_nw;
       if (nw == 0 || nw > kNucWin) return out;
+      if (nw <= 128) {
+        // a small window in wave 0 alone: its keys in slots lane and
+        // lane + 64 (key 0, below every real key, past nw), sorted in
+        // descending order by a bitonic network (position i = r 64 + lane;
+        // partners in other lanes by lane exchange, at distance 64 within a
+        // lane), then the masses' prefix sums from A by wave scans
+        if (w == 0) {
+          uint64_t k[2] = {lane < nw ? wl[lane] : 0ull, lane + 64 < nw ? wl[lane + 64] : 0ull};
+#pragma unroll
+          for (int size = 2; size <= 128; size <<= 1) {
+#pragma unroll
+            for (int j = size >> 1; j > 0; j >>= 1) {
+              uint64_t o[2];
+#pragma unroll
+              for (int r = 0; r < 2; ++r) o[r] = j == 64 ? k[1 - r] : __shfl_xor(k[r], j);
+#pragma unroll
+              for (int r = 0; r < 2; ++r) {
+                const int i = r * 64 + lane;
+                const bool keep_max = ((i & j) == 0) == ((i & size) == 0);
+                k[r] = keep_max ? (k[r] > o[r] ? k[r] : o[r]) : (k[r] < o[r] ? k[r] : o[r]);
+              }
+            }
+          }
+          double e[2], inc[2];
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            e[r] = r * 64 + lane < nw ? mass_of(packed_val(k[r])) : 0.0;
+            inc[r] = wave_scan(e[r], 0.0, [](double a, double b) { return a + b; });
+          }
+          const double t0 = read_lane(inc[0], 63);
+          const double wtot = t0 + read_lane(inc[1], 63);
+          const double c00 = A + (inc[0] - e[0]), c01 = A + (t0 + inc[1] - e[1]);
+          const uint64_t b0 = __builtin_amdgcn_ballot_w64(lane < nw && c00 < tgt);
+          const uint64_t b1 = __builtin_amdgcn_ballot_w64(lane + 64 < nw && c01 < tgt);
+          const int kept = (int)__popcll(b0) + (int)__popcll(b1);   // (a prefix: c0 rises with the position)
+          const bool inside = kept > 0 && (kept < nw || A + wtot >= tgt);
+          if (inside) {
+            const int at = kept - 1, ln = at & 63;
+            out.N = at < 64 ? read_lane(c00 + e[0], ln) : read_lane(c01 + e[1], ln);
+            out.cut = at < 64 ? read_lane(k[0], ln) : read_lane(k[1], ln);
+            out.ok = 1;
+          }
+        }
+        return out;
+      }
       // rank of each window key (keys are distinct: the index is part of the key)
       for (int i = tid; i < nw; i += kNB) {
         const uint64_t k = wl[i];
