@@ -19,6 +19,7 @@ constexpr int kMinSmall = 2048;       // argmax / sum / filter passes: smallest 
 constexpr int kSmallTiles = 256;      // problems with fewer tiles than this take smaller tiles
 constexpr int kStatsRoundsMax = 4;     // float32 sum / argmax passes: most rounds of loads per tile
 constexpr size_t kKeepBytes = 32u << 20;   // residual weights kept for the draw up to this size
+constexpr long kResidGroupWgs = 4096;      // residual workgroups that keep a launch full
 
 struct Plan {
   int filt;        // sv::Filter
@@ -282,6 +283,14 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
   p.keep_w = (pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample) &&
              (size_t)c->max_batch * pl.S2_max * sv::kResidSeg * sizeof(double) <= kKeepBytes ? 1 : 0;
   p.S2 = pl.S2_max;
+  // segments per workgroup of the residual kernel: its setup and accept
+  // tests once for several segments, as long as 4096 workgroups remain
+  // (workload 5: 19200 -> 4800 workgroups, 110 -> 85 us for the kernels
+  // after the streaming pass; small problems keep one segment each)
+  p.rgrp = 1;
+  for (int g = 4; g > 1; g >>= 1) {
+    if ((long)batch * ((pl.S2_max + g - 1) / g) >= kResidGroupWgs) { p.rgrp = g; break; }
+  }
   p.k_idx = (int32_t*)(ws + L.k_idx);
   p.k_e = (double*)(ws + L.k_e);
   p.k_cnt = (int32_t*)(ws + L.k_cnt);

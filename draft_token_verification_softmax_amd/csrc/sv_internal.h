@@ -151,6 +151,7 @@ struct Params {
   uint64_t* tcut;    // tree sampling with top-k / top-p: [B][N][2] cut keys (target, draft) of nodes with children
   int tfilt;         // tree sampling with top-k or top-p: row views come from RowNuc (nuc, every row)
   int S2;            // residual segments per sequence (kResidSeg logits each)
+  int rgrp;          // segments per workgroup of k_resid_s
   // top-k: each row's kept set, rank order
   int32_t* k_idx;    // [rows][top_k]
   double* k_e;       // [rows][top_k] exp(z - zmax)

@@ -2521,7 +2521,9 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   __shared__ double red[kWaves];
   __shared__ double tab[kExpTab];
   __shared__ int sh_n, sh_st;
-  const int b = blockIdx.y, seg = blockIdx.x, tid = threadIdx.x;
+  // segments blockIdx.x * rgrp .. + rgrp - 1 (the setup and the accept
+  // tests once for all of them)
+  const int b = blockIdx.y, seg0 = blockIdx.x * p.rgrp, tid = threadIdx.x;
   const int k = p.k, V = p.V, nrows = p.rows_t + p.rows_d;
   const double cs = kExpScale * kLog2e / p.T;
   auto row_of = [&](int r) { return r < p.rows_t ? trow(p, b, r) : drow(p, b, r - p.rows_t); };
@@ -2533,7 +2535,6 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   const int xj_l = p.tokens[(size_t)b * k + ti];
   const float uj_l = p.u[(size_t)b * k + ti];
   const float lx = p.row_lx[row_of(ri)];
-  const int pos0 = seg * kResidSeg + tid * kVec;
   int internal = 0;
   if constexpr (FILT == kFiltTopp) {
     const RowNuc nu = p.nuc[row_of(ri)];
@@ -2558,7 +2559,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
     if (all_read || r == 0 || r == p.rows_t) mybad |= vbad[r];
   internal = __syncthreads_or(internal);
   if (__syncthreads_or(mybad)) {
-    if (seg == 0) {
+    if (seg0 == 0) {
       emit_invalid(p, b, 4 | (internal ? kStatusInternal : 0));
       if (tid == 0) p.seq[b].n = -1;
     }
@@ -2589,6 +2590,8 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
     const int rd = p.rows_t + n;
     qr = RowView{row_ptr<T>(p, drow(p, b, n)), vnmc[rd], vinv[rd], vcut[rd]};
   }
+  for (int seg = seg0; seg < seg0 + p.rgrp && seg < p.S2; ++seg) {
+  const int pos0 = seg * kResidSeg + tid * kVec;
   double w[kVec];
   double t;
   if (FILT == kFiltTopp && !p.keep_w) {
@@ -2616,6 +2619,7 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
       ss.n = n; ss.st = sh_st; ss.node = n; ss.hasq = n < k;
       p.seq[b] = ss;
     }
+  }
   }
 }
 
@@ -4538,7 +4542,7 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st, hip
     case kFiltTopp:
       run(false, k_topp_rows<T>, gr, p);
       run(false, k_topp_rows_exact<T>, gr, p);
-      run(false, k_resid_s<T, kFiltTopp>, gs, p);
+      run(false, k_resid_s<T, kFiltTopp>, dim3((unsigned)((p.S2 + p.rgrp - 1) / p.rgrp), (unsigned)p.B), p);
       run(true, k_resid_final<T, kFiltTopp>, (p.resid_probs || p.keep_w) ? gs : gb1, p);
       break;
     case kFiltTreeSample: {
@@ -4566,7 +4570,7 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st, hip
       break;
     }
     default:  // plain sampling
-      run(false, k_resid_s<T, kFiltNone>, gs, p);
+      run(false, k_resid_s<T, kFiltNone>, dim3((unsigned)((p.S2 + p.rgrp - 1) / p.rgrp), (unsigned)p.B), p);
       run(true, k_resid_final<T, kFiltNone>, (p.resid_probs || p.keep_w) ? gs : gb1, p);
       break;
   }

@@ -298,6 +298,19 @@ def test_sample_topp_full_workload5():
     compare_chain(gpu, orc, check, "workload 5")
 
 
+def test_sample_plain_grouped_residual():
+    """Enough sequences that the residual kernel takes two segments per
+    workgroup (520 sequences, 15 segments of 30000 logits: the last group
+    holds one segment)."""
+    say("sample plain, residual segments in groups")
+    inp = wl.chain_inputs(2, seed=41, B=520, V=30000, k=1, dtype="bf16")
+    check = list(range(0, 520, 13)) + [519]
+    x = draw_drafts(inp, check=set(check))
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, check)
+    compare_chain(gpu, orc, check, "plain sampling, 520 sequences")
+
+
 def test_topp_heavy_ties_bf16():
     """Thousands of equal bf16 logits around the cut: the tie must be split by index."""
     say("top-p heavy ties")
