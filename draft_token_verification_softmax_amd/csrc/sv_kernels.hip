@@ -3862,7 +3862,7 @@ constexpr int kNucWin = kNucHist / 2;         // window slots (the histogram's s
 constexpr int kNucSample = 2 * kNucHist;      // 16-bit key-prefix bins of the sample (u32)
 constexpr int kNucBatch = 16;                 // candidate loads in flight per lane in the settle
 constexpr int kNucStage = 512;                // candidates one wave can stage in LDS per round
-constexpr double kNucFix = 17592186044416.0;  // 2^44: fixed-point scale of the masses (e <= 1)
+constexpr float kNucFix = 1048576.f;          // 2^20: fixed-point scale of the histogram's masses (e <= 1)
 static_assert(kNucRegion * kNW == kNucSlotEntries, "regions tile the buffer");
 static_assert(3 * kNucFill <= 2 * kNucSlotEntries, "aim at two thirds of the capacity or less");
 static_assert(kNucWin % kNB == 0 && kNucSample % kNB == 0 && kNucHist % kNB == 0, "shapes");
@@ -4319,7 +4319,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
         bin_tau = pt < (float)kNucHist ? (int)__builtin_amdgcn_fmed3f(pt, 0.f, (float)(kNucHist - 1)) : kNucHist;
       }
       const bool no_fix = !(tgt < (double)kNucSlotEntries);   // the candidates cannot hold that much mass
-      const uint64_t tgt_fix = no_fix ? 0ull : (uint64_t)(tgt * kNucFix);
+      const uint64_t tgt_fix = no_fix ? 0ull : (uint64_t)(tgt * (double)kNucFix);
       auto bin_of = [&](float l) {
         const float pos = fmaf(l, a1, b1);
         return pos < (float)kNucHist ? (int)__builtin_amdgcn_fmed3f(pos, 0.f, (float)(kNucHist - 1)) : INT_MAX;
@@ -4328,9 +4328,12 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       const double nmcM = -(double)M * cs;
       auto mass_of = [&](float l) { return exp2_64(fma((double)l, cs, nmcM), tab); };
       // the histogram only locates the window (its bin and the two around
-      // it), so its masses are the hardware float32 exp2 of (l - M) c
-      // (relative error near 1e-7, far inside a bin's mass); A and the
-      // window's walk below take float64 masses
+      // it): 32-bit fixed-point masses (2^-20 units, rounded) of the hardware
+      // float32 exp2 of (l - M) c, summed in 64 bits by the scan.  A and the
+      // window's walk below take float64 masses and accept a cut only inside
+      // the window, so an inexact histogram (a bin past 4096 full masses
+      // wraps) can only leave the row to the cut kernels.
+      uint32_t* hist32 = reinterpret_cast<uint32_t*>(hist);
       const float M32 = M, c32 = (float)cd;
       for (int b = tid; b < kNucHist; b += kNB) hist[b] = 0ull;
       __syncthreads();
@@ -4338,7 +4341,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
         const int b = bin_of(l);
         if (valid && b != INT_MAX) {
           const float e32 = __builtin_amdgcn_exp2f((l - M32) * c32);
-          atomicAdd(reinterpret_cast<unsigned long long*>(&hist[b]), (unsigned long long)((double)e32 * kNucFix));
+          atomicAdd(&hist32[b], (unsigned)fmaf(e32, kNucFix, 0.5f));
         }
       });
       __syncthreads();
@@ -4349,7 +4352,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
         uint64_t h[per];
         uint64_t hl = 0;
 #pragma unroll
-        for (int q = 0; q < per; ++q) { h[q] = hist[tid * per + q]; hl += h[q]; }
+        for (int q = 0; q < per; ++q) { h[q] = hist32[tid * per + q]; hl += h[q]; }
         uint64_t tot;
         uint64_t run = nb_exscan<uint64_t>(hl, redu, &tot);
         int found = INT_MAX;
