@@ -230,6 +230,23 @@ def test_sample_topp_wide_nucleus():
     compare_chain(gpu, orc, range(3), "top-p 0.995, T 3, V=152064")
 
 
+def test_sample_topp_clustered_candidates():
+    """Rows whose largest logits fill one contiguous range of indices: a
+    round of the one-read kernel then holds more candidates than a wave can
+    stage (512), the row is redone by the cut kernels, and the results
+    must not change.  Half the rows are left as drawn (no cluster)."""
+    say("sample top-p, clustered candidates")
+    B, k, V = 4, 2, 40000
+    inp = wl.chain_inputs(5, seed=31, B=B, V=V, k=k)
+    for arr in (inp["target"], inp["draft"]):
+        for b in range(0, B, 2):
+            arr[b, :, 8192:8192 + 4096] += 6.0       # one round's logits all far above the rest
+    x = draw_drafts(inp)
+    gpu = run_chain(inp, x, SV_MODE_SAMPLE)
+    orc = oracle_chain(inp, x, SV_MODE_SAMPLE, list(range(B)))
+    compare_chain(gpu, orc, range(B), "top-p 0.9, clustered rows")
+
+
 def test_sample_topp_beyond_row_kernel_vocab():
     """Rows longer than the one-read kernel takes (2^20 logits) keep the
     streaming pass and the cut kernels."""
