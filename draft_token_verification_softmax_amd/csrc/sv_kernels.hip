@@ -4088,25 +4088,26 @@ DEV double exp2_64_sum(const float* v, double cs, double nmc, const double* tab)
   return s;
 }
 
-// f(l, idx) for each candidate of this lane in its wave's region (slots
-// lane, lane + 64, ... below n), kNucBatch loads in flight at a time; the
-// order is fixed.  n is uniform over the wave, and so is every call of f's
-// loop (f may hold wave-wide operations: it is called for every batch slot,
-// with valid false past n).  The loads go through the region's buffer
+// f(l, slot) for each candidate value of this lane in its wave's region
+// (slots lane, lane + 64, ... below n), kNucBatch loads in flight at a time;
+// the order is fixed.  n is uniform over the wave, and so is every call of
+// f's loop (f may hold wave-wide operations: it is called for every batch
+// slot, with valid false past n).  The loads go through the region's buffer
 // resource unconditionally (a slot past the region reads 0), so they issue
-// back to back.
+// back to back.  Only the values are read: an index is fetched by its slot
+// where it is needed (the window's keys).
 template <typename F>
-DEV void nuc_each(__amdgpu_buffer_rsrc_t rreg, int n, F&& f) {
+DEV void nuc_each(__amdgpu_buffer_rsrc_t rval, int n, F&& f) {
   const int lane = threadIdx.x & 63;
   for (int s0 = 0; s0 < n; s0 += 64 * kNucBatch) {
-    vu2 c[kNucBatch];
+    uint32_t c[kNucBatch];
 #pragma unroll
     for (int q = 0; q < kNucBatch; ++q)
-      c[q] = __builtin_bit_cast(vu2, __builtin_amdgcn_raw_buffer_load_b64(rreg, (s0 + 64 * q + lane) * 8, 0, 0));
+      c[q] = __builtin_amdgcn_raw_buffer_load_b32(rval, (s0 + 64 * q + lane) * 4, 0, 0);
 #pragma unroll
     for (int q = 0; q < kNucBatch; ++q) {
       const int sl = s0 + 64 * q + lane;
-      f(sl < n, __uint_as_float(c[q].x), (int)c[q].y);
+      f(sl < n, __uint_as_float(c[q]), sl);
     }
   }
 }
@@ -4132,8 +4133,12 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
   // this wave's region of this workgroup's buffer; the flushes store through
   // a buffer resource spanning the region, which drops stores past its end
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  uint64_t* reg = p.nucc + (size_t)blockIdx.x * kNucSlotEntries + (size_t)wu * kNucRegion;
-  const __amdgpu_buffer_rsrc_t rreg = make_rsrc(reg, kNucRegion * (int)sizeof(uint64_t));
+  // (the buffer: the candidates' values, then their indices, kNucSlotEntries
+  // 32-bit words each; a wave's region of each at w kNucRegion)
+  uint32_t* bval = reinterpret_cast<uint32_t*>(p.nucc + (size_t)blockIdx.x * kNucSlotEntries);
+  const uint32_t* bidx = bval + kNucSlotEntries;
+  const __amdgpu_buffer_rsrc_t rval = make_rsrc(bval + (size_t)wu * kNucRegion, kNucRegion * 4);
+  const __amdgpu_buffer_rsrc_t ridx = make_rsrc(bidx + (size_t)wu * kNucRegion, kNucRegion * 4);
   uint32_t* sv = stg[wu][0];
   uint32_t* si = stg[wu][1];
   if (tid < kExpTab) tab[tid] = kExp2Tab[tid];
@@ -4169,8 +4174,8 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       __builtin_amdgcn_wave_barrier();
       const int n = cw - cs0 < kNucStage ? cw - cs0 : kNucStage;
       for (int i = lane; i < n; i += 64) {
-        const vu2 ent = {sv[i], si[i]};
-        __builtin_amdgcn_raw_buffer_store_b64(ent, rreg, (cs0 + i) * 8, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(sv[i], rval, (cs0 + i) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(si[i], ridx, (cs0 + i) * 4, 0, 0);
       }
       cs0 = cw;
       __builtin_amdgcn_wave_barrier();
@@ -4288,7 +4293,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
     auto settle = [&]() -> RowNuc {
       const bool bad_nan = __syncthreads_or(nan_seen) != 0;   // (also publishes the regions)
       const int nc = cw < kNucRegion ? cw : kNucRegion;
-      auto each = [&](auto&& f) { nuc_each(rreg, nc, f); };
+      auto each = [&](auto&& f) { nuc_each(rval, nc, f); };
       const float M = nb_max(m, redf);
       const bool bad = bad_nan || !(M > -INFINITY) || !(M < INFINITY);
       double zl = 0.0;
@@ -4375,16 +4380,23 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       uint64_t* wl = hist;                 // unsorted window keys
       uint64_t* ws = hist + kNucWin;       // the same, ranked
       double al = 0.0;
-      each([&](bool valid, float l, int idx) {
+      // (a window key holds the candidate's slot in the buffer until its
+      // index is fetched below)
+      each([&](bool valid, float l, int sl) {
         const int b = valid ? bin_of(l) : INT_MAX;
         if (b < lo) al += mass_of(l);
         const bool inw = b >= lo && b <= hi;
         const int at = wave_append(inw, &sh_nw);
-        if (inw && at < kNucWin) wl[at] = pack(l, idx);
+        if (inw && at < kNucWin) wl[at] = pack(l, wu * kNucRegion + sl);
       });
       const double A = nb_sum(al, redd);   // (its barriers also publish the window)
       const int nw = sh_nw;
       if (nw == 0 || nw > kNucWin) return out;
+      for (int i = tid; i < nw; i += kNB) {
+        const uint64_t k = wl[i];
+        wl[i] = pack(packed_val(k), (int)bidx[packed_idx(k)]);
+      }
+      __syncthreads();
       if (nw <= 128) {
         // a small window in wave 0 alone: its keys in slots lane and
         // lane + 64 (key 0, below every real key, past nw), sorted in
