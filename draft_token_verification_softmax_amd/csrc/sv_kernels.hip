@@ -3830,15 +3830,16 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows_exact(Params p) {
 // g, g + gridDim.x, ...  It reads each row once and settles its nucleus cut
 // from the candidates it kept in its own buffer in the workspace (the cut
 // kernels above read a row twice more after the streaming pass; on this chip
-// a second sweep of a row finds nothing of the first one left in any cache,
-// while a buffer of ~120 KB written and read back by one workgroup stays in
-// L2).  Four workgroups share a compute unit, so the settle of one overlaps
-// the sweeps of the others.
+// a second sweep of a row finds nothing of the first one left in any cache).
+// The buffer, about a tenth of the row's bytes, goes to memory and is read
+// back twice (values only); that traffic is the price of four workgroups per
+// compute unit, where the settle of one overlaps the sweeps of the others.
 //  sweep   each lane keeps its running max m and the float64 sum of
 //          2^((l - m) c) as tile_stats does (table exp2, float64 terms), and
-//          every logit >= tau goes to its wave's region of the buffer: the
-//          raw value and its index.  A region fills in its wave's program
-//          order, so its contents do not depend on timing.  tau is set from
+//          every logit >= tau is staged in LDS and then goes to its wave's
+//          region of the buffer: the raw value and its index (in separate
+//          arrays).  A region fills in its wave's program order, so its
+//          contents do not depend on timing.  tau is set from
 //          the first round the workgroup reads (a random share of a large
 //          row): the 16-bit key prefix at which the round's counts would put
 //          about kNucFill candidates at or above tau over the row.
