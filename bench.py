@@ -292,6 +292,27 @@ def pmc_summary(fetch_csv, write_csv, fetch_scale=2.0, write_scale=1.0):
     print("\n".join(out))
 
 
+def counter_summary(csv_path):
+    """Mean per dispatch of every counter of one rocprofv3 --pmc run, per
+    library kernel, with the kernel's mean duration in that run."""
+    per, dur = {}, {}
+    for r in _read_csv(csv_path):
+        name = _short(r["Kernel_Name"])
+        if not name.startswith("sv::"):
+            continue
+        per.setdefault(name, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+        key = (name, r["Dispatch_Id"])
+        dur[key] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+    counters = sorted({c for d in per.values() for c in d})
+    out = ["| kernel | dispatches | mean us | " + " | ".join(counters) + " |",
+           "|---|---|---|" + "---|" * len(counters)]
+    for name in sorted(per, key=lambda n: -max(per[n].get(counters[0], [0.0]))):
+        d = [v for (n, _), v in dur.items() if n == name]
+        cells = [f"{float(np.mean(per[name][c])):.4g}" if c in per[name] else "" for c in counters]
+        out.append(f"| `{name}` | {len(d)} | {float(np.mean(d)):.1f} | " + " | ".join(cells) + " |")
+    print("\n".join(out))
+
+
 def copy_summary(fetch_csv, write_csv, nbytes):
     """Scale factors of FETCH_SIZE and WRITE_SIZE from the copy kernel of
     ``bench.py --copy-calibrate``: bytes moved / counter bytes."""
@@ -627,6 +648,8 @@ def main():
     ap.add_argument("--trace-summary", metavar="CSV", help="summarise a rocprofv3 kernel trace and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarise two rocprofv3 counter runs of the bench and exit")
+    ap.add_argument("--counter-summary", metavar="CSV",
+                    help="mean per dispatch of each counter of a rocprofv3 --pmc run, per kernel, and exit")
     ap.add_argument("--copy-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "BYTES"),
                     help="counter scale factors from two --copy-calibrate counter runs and exit")
     args = ap.parse_args()
@@ -638,6 +661,9 @@ def main():
         return
     if args.pmc_summary:
         pmc_summary(*args.pmc_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
         return
     if args.copy_summary:
         copy_summary(args.copy_summary[0], args.copy_summary[1], int(args.copy_summary[2]))

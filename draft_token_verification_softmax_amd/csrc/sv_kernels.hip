@@ -392,13 +392,16 @@ DEV float maximum8(const float v[kVec]) {
 
 // ------------------------------------------------------------------ float64 exp2
 
-// 2^(y / kExpTab) to a few ulp of float64, for the streaming sums; callers
+// 2^(y / kExpTab) to 1.5e-13 relative, for the streaming sums; callers
 // scale their arguments by kExpTab (cs = kExpTab log2(e) / T).
 // y = kExpTab j + f with j = rint(y), |f| <= 1/2:
 //   2^(y/kExpTab) = 2^(j >> 8) * 2^((j & 255) / 256) * e^(f ln2 / 256);
 // the middle factor comes from a 256-entry table in LDS, the last from its
-// Taylor series to degree 4 (|f ln2 / 256| <= 0.00136, remainder below
-// 4e-17: one fma less than a 64-entry table needs for the same bound).
+// Taylor series to degree 3 (|r| = |f ln2 / 256| <= 0.00136: remainder
+// below r^4 / 24 < 1.4e-13, plus a few ulp of rounding).  That is seven
+// orders of magnitude inside the 1e-6 band of the flag rule, and one fma
+// per term less than degree 4 (remainder 4e-17), where these terms are
+// most of the instructions.
 // Arguments below -280000 (results below 2^-1093, i.e. 0) and NaN give 0.
 constexpr int kExpTabBits = 8;
 constexpr int kExpTab = 1 << kExpTabBits;
@@ -406,7 +409,6 @@ constexpr double kExpScale = (double)kExpTab;
 constexpr double kE1 = 0.0027076061740622863;    // (ln2/256)^i / i!
 constexpr double kE2 = 3.6655655969101062e-06;
 constexpr double kE3 = 3.3083026805413713e-09;
-constexpr double kE4 = 2.239395190875157e-12;
 static_assert(kExpTab == kBlock, "one table entry per thread of the block");
 
 // 2^(j / kExpTab) for j = 0 .. kExpTab - 1, each the float64 nearest the
@@ -490,12 +492,45 @@ DEV double exp2_64(double y, const double* tab) {
   y = fmax(y, -280000.0);
   const double j = rint(y);
   const double f = y - j;
-  double q = fma(f, kE4, kE3);
-  q = fma(q, f, kE2);
+  double q = fma(f, kE3, kE2);
   q = fma(q, f, kE1);
   q = fma(q, f, 1.0);
   const int ji = (int)j;
   return ldexp(tab[ji & (kExpTab - 1)] * q, ji >> kExpTabBits);
+}
+
+// exp2_64(fma(l, cs, n)) for a logit l, the same value to the bit for every
+// argument that is not NaN (callers never pass one), in one instruction
+// less: y' = -y 2^-20 = fma(l, -cs 2^-20, -n 2^-20) with the fma's clamp to
+// [0, 1] in place of the lower bound (y >= -2^20; below -280000 every term
+// is 0 anyway); adding y' to -1.5 2^32, whose unit in the last place is
+// 2^-20, rounds it to a multiple of 2^-20 whose integer count, -j with
+// j = rint(y), is the low word of the sum; f = y - j = -(y' - that
+// multiple) 2^20 exactly.  The Taylor coefficients take the factor
+// (-2^20)^i, so every rounding is the one of exp2_64 scaled by a power of 2.
+constexpr double kMagic20 = 6442450944.0;                    // 1.5 * 2^32
+constexpr double kTwoM20 = 1.0 / 1048576.0;                  // 2^-20
+constexpr double kF1 = -kE1 * 1048576.0;                     // kE_i (-2^20)^i
+constexpr double kF2 = kE2 * 1048576.0 * 1048576.0;
+constexpr double kF3 = -kE3 * 1048576.0 * 1048576.0 * 1048576.0;
+struct Exp2Split {
+  double f;
+  int j;
+};
+DEV Exp2Split exp2_split(float l, double a, double b) {   // a = -cs 2^-20, b = -n 2^-20
+  const double yp = fmin(fmax(fma((double)l, a, b), 0.0), 1.0);
+  const double t = kMagic20 - yp;
+  const double jd = kMagic20 - t;
+  return Exp2Split{yp - jd, (int)(uint32_t)(uint64_t)__double_as_longlong(t)};
+}
+DEV double exp2_tail(double f) {
+  double q = fma(f, kF3, kF2);
+  q = fma(q, f, kF1);
+  return fma(q, f, 1.0);
+}
+DEV double exp2_64_l(float l, double cs, double n, const double* tab) {
+  const Exp2Split e = exp2_split(l, -cs * kTwoM20, -n * kTwoM20);
+  return ldexp(tab[e.j & (kExpTab - 1)] * exp2_tail(e.f), e.j >> kExpTabBits);
 }
 
 // 2^y for y <= 0 in float64 with few registers: y = j + f, j = rint(y),
@@ -921,10 +956,10 @@ DEV int has_child(const Params& p, const int pv[kParentLoads], int node) {
 // each round of groups first raises the lane max m over them (rescaling the
 // lane sum, in float64, if it rose), then adds 2^((l - m) c) of every logit.
 // Terms:
-//   float64 (exp2_64 from a 256-entry table, a few ulp; TERMS64, and the
-//   rows of a TERMS_MIX pass that need them): the sum is the one of exact
-//   arithmetic to about 1e-15, so every decision taken from it agrees with a
-//   float64 evaluation except within rounding of its threshold.
+//   float64 (exp2_64 from a 256-entry table, 1.5e-13 relative; TERMS64, and
+//   the rows of a TERMS_MIX pass that need them): the sum is the one of exact
+//   arithmetic to about 1e-13, so every decision taken from it agrees with a
+//   float64 evaluation except within 1e-13 of its threshold.
 //   float32 (the other rows of a TERMS_MIX pass): the hardware float32 exp2
 //   (relative error below 1e-7) of (l - m) * c with c split into two floats
 //   (c_hi + c_lo carries c to about 48 bits), eight terms summed in float32 (a
@@ -1003,9 +1038,9 @@ DEV void tile_stats(const Params& p, const T* row, int start, int end, int grow,
           float v[kVec];
           gr[u].opaque().values(v);
           const double nmc = -(double)m * cs;
-          double gs = 0.0;
+          double gs = -0.0;
 #pragma unroll
-          for (int q = 0; q < kVec; ++q) gs += exp2_64(fma((double)v[q], cs, nmc), tab);
+          for (int q = 0; q < kVec; ++q) gs += exp2_64_l(v[q], cs, nmc, tab);
           s += u < nv ? gs : 0.0;
         }
       } else if constexpr (TERMS == kTermsMix) {
@@ -1534,7 +1569,7 @@ struct RowView {
 
 DEV double prob_from(const RowView& r, double cs, const double* tab, float l, int v) {
   if (r.cut && pack(l, v) < r.cut) return 0.0;
-  return exp2_64(fma((double)l, cs, r.nmc), tab) * r.inv;
+  return exp2_64_l(l, cs, r.nmc, tab) * r.inv;
 }
 
 // Residual weights of the kVec entries [pos, pos + kVec) of one chunk:
@@ -1594,7 +1629,7 @@ DEV double resid_nuc_sparse(const RowView& pr, const RowView& qr, bool hasq, dou
   }
   const int lane = threadIdx.x & 63;
   auto weight = [&](float a, float b, int v) {
-    double w = exp2_64(fma((double)a, cs, pr.nmc), tab) * pr.inv;
+    double w = exp2_64_l(a, cs, pr.nmc, tab) * pr.inv;
     if (hasq) {
       w -= prob_from(qr, cs, tab, b, v);
       w = w > 0.0 ? w : 0.0;
@@ -4061,31 +4096,20 @@ DEV void nuc_sweep(const T* row, int V, int aligned, int r0, F&& f, P&& pre) {
   }
 }
 
-// sum of exp2_64 over n values, the table reads of all n issued before any
+// sum of exp2_64_l over n logits, the table reads of all n issued before any
 // is used (the LDS latency once per batch, not once per term)
 template <int N>
 DEV double exp2_64_sum(const float* v, double cs, double nmc, const double* tab) {
-  double f[N];
-  int ji[N];
+  const double a = -cs * kTwoM20, b = -nmc * kTwoM20;
+  Exp2Split e[N];
 #pragma unroll
-  for (int q = 0; q < N; ++q) {
-    const double y = fmax(fma((double)v[q], cs, nmc), -280000.0);
-    const double j = rint(y);
-    f[q] = y - j;
-    ji[q] = (int)j;
-  }
+  for (int q = 0; q < N; ++q) e[q] = exp2_split(v[q], a, b);
   double tv[N];
 #pragma unroll
-  for (int q = 0; q < N; ++q) tv[q] = tab[ji[q] & (kExpTab - 1)];
-  double s = 0.0;
+  for (int q = 0; q < N; ++q) tv[q] = tab[e[q].j & (kExpTab - 1)];
+  double s = -0.0;   // (-0.0 + x is x: no add for the first term)
 #pragma unroll
-  for (int q = 0; q < N; ++q) {
-    double p = fma(f[q], kE4, kE3);
-    p = fma(p, f[q], kE2);
-    p = fma(p, f[q], kE1);
-    p = fma(p, f[q], 1.0);
-    s += ldexp(tv[q] * p, ji[q] >> kExpTabBits);
-  }
+  for (int q = 0; q < N; ++q) s += ldexp(tv[q] * exp2_tail(e[q].f), e[q].j >> kExpTabBits);
   return s;
 }
 
@@ -4257,7 +4281,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       // float64 terms, in batches of four (eight hold too many registers)
       if (m > -INFINITY) {
         const double nmc = -(double)m * cs;
-        double gs = 0.0;
+        double gs = -0.0;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           gs += exp2_64_sum<kVec / 2>(v[u], cs, nmc, tab);
@@ -4332,7 +4356,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       };
       // e = exp((l - M) / T) = 2^((l - M) c): the table exp2, as the sweep's terms
       const double nmcM = -(double)M * cs;
-      auto mass_of = [&](float l) { return exp2_64(fma((double)l, cs, nmcM), tab); };
+      auto mass_of = [&](float l) { return exp2_64_l(l, cs, nmcM, tab); };
       // the histogram only locates the window (its bin and the two around
       // it): 32-bit fixed-point masses (2^-20 units, rounded) of the hardware
       // float32 exp2 of (l - M) c, summed in 64 bits by the scan.  A and the
