@@ -1759,8 +1759,102 @@ __global__ __launch_bounds__(kBlock) void k_greedy_final(Params p) {
 
 // ================================================================== token tree
 
+// k_tree_final for a tree of at most 64 nodes whose rows have at most
+// kLanePartials partials: every step in wave 0 alone, one lane per node,
+// with no barrier.  The lane combines its row's partials in registers in the
+// order combine_rows takes with one lane per row (the same argmax and bad
+// flag); the edge tests read the parent's argmax, and the pointer jumping
+// reads the pointed-to node's state, by lane shuffles (all lanes read before
+// any writes, as the double-buffered arrays of the block path); the path is
+// written from the shuffled parents and tokens of the nodes on it.
+DEV void tree_final_wave(const Params& p, int b) {
+  const int N = p.k, V = p.V, P = p.P, lane = threadIdx.x & 63;
+  const bool on = lane < N;
+  const int pi = p.parents[(size_t)b * N + (on ? lane : 0)];
+  const int ti = p.tokens[(size_t)b * N + (on ? lane : 0)];
+  TileStat ts[kLanePartials];
+#pragma unroll
+  for (int q = 0; q < kLanePartials; ++q) {
+    const bool ok = on && q < P;
+    ts[q] = p.tiles[ok ? (size_t)trow(p, b, lane) * P + q : 0];
+  }
+  float m = -INFINITY;
+  int ai = INT_MAX;
+  int bad = 0;
+#pragma unroll
+  for (int q = 0; q < kLanePartials; ++q) {
+    const bool ok = on && q < P;
+    if (!ok) { ts[q].m = -INFINITY; ts[q].amax = INT_MAX; ts[q].s = 0.0; }
+    bad |= ts[q].s != ts[q].s;
+    if (ts[q].m > m || (ts[q].m == m && ts[q].amax < ai)) { m = ts[q].m; ai = ts[q].amax; }
+  }
+  bad |= (m == INFINITY) || (m == -INFINITY);
+  int32_t* ot = p.out_tokens + (size_t)b * p.out_w;
+  int32_t* onode = p.out_nodes ? p.out_nodes + (size_t)b * p.out_w : nullptr;
+  if (__ballot(on && bad)) {
+    for (int i = lane; i < p.out_w; i += 64) {
+      ot[i] = -1;
+      if (onode) onode[i] = -1;
+    }
+    if (lane == 0) {
+      p.acc_len[b] = 0;
+      if (p.seq_status) p.seq_status[b] = 4;
+    }
+    return;
+  }
+  // the edge into each node: its token against the parent row's argmax
+  const int gpar = __shfl(ai, (pi >= 0 && pi < 64) ? pi : 0);
+  int st = 0, ok = 0, j = -1, d = 0;
+  if (on) {
+    if (lane == 0) {
+      if (pi != -1) st |= 2;
+      ok = 1;
+    } else if (pi < 0 || pi >= lane) {
+      st |= 2;
+    } else {
+      if (ti < 0 || ti >= V) st |= 1;
+      else ok = ti == gpar;
+      j = pi; d = 1;
+    }
+  }
+  const int sst = (__ballot(st & 1) ? 1 : 0) | (__ballot(st & 2) ? 2 : 0);
+  // pointer jumping: ok = AND of the edge tests up to the root, d = depth
+  for (int span = 1; span < N; span <<= 1) {
+    const int jj = j >= 0 ? j : lane;
+    const int oj = __shfl(ok, jj), dj = __shfl(d, jj), jn = __shfl(j, jj);
+    if (j >= 0) { ok &= oj; d += dj; j = jn; }
+  }
+  const int key = on && ok ? (d << 11) | (2047 - lane) : -1;
+  const int kbest = wave_max_t(key);
+  const int best = 2047 - (kbest & 2047);
+  const int n = kbest >> 11;
+  const int ybest = __shfl(ai, best);
+  int node = best;
+  for (int dd = n; dd >= 0; --dd) {
+    const int tk = __shfl(ti, node), pn = __shfl(pi, node);
+    if (lane == 0) {
+      if (onode) onode[dd] = node;
+      if (dd > 0) ot[dd - 1] = tk;
+    }
+    if (dd > 0) node = pn;
+  }
+  if (lane == 0) {
+    ot[n] = ybest;
+    p.acc_len[b] = n;
+    if (p.seq_status) p.seq_status[b] = sst;
+  }
+  for (int i = n + 1 + lane; i < p.out_w; i += 64) {
+    ot[i] = -1;
+    if (onode) onode[i] = -1;
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_tree_final(Params p) {
+  if (p.k <= 64 && p.P <= kLanePartials) {
+    if (threadIdx.x < 64) tree_final_wave(p, blockIdx.x);
+    return;
+  }
   __shared__ int g[kMaxTree];
   __shared__ int spar[kMaxTree];
   __shared__ int stok[kMaxTree];

@@ -52,6 +52,28 @@ def test_bad_logits_and_tokens(mode):
     assert np.all(gpu["out_tokens"][0] == -1) and gpu["accepted_len"][0] == 0
 
 
+@pytest.mark.parametrize("N", [20, 64, 100])
+def test_tree_bad_rows(N):
+    # a NaN, a +inf and an all -inf target row each make their tree invalid;
+    # -inf entries alone do not (trees of up to 64 nodes take the kernel's
+    # one-wave path, larger ones the block path)
+    say("tree bad rows", N)
+    tr = wl.tree_inputs(4, seed=40 + N, B=5, N=N, V=2000)
+    t = tr["target"]                  # bf16 bit patterns
+    t[0, 3, 17] = 0x7FC0              # NaN
+    t[1, N - 1, 5] = 0x7F80           # +inf
+    t[2, 0, :] = 0xFF80               # -inf
+    t[3, 1, :50] = 0xFF80
+    T64 = wl.rows_f64(t, tr["dtype"])
+    tokens = wl.tree_tokens(tr, np.argmax(np.where(np.isnan(T64), -np.inf, T64), axis=-1))
+    gpu = run_tree(tr, tokens)
+    acc, toks, nodes, st = ov.run_tree_batch(T64, tr["parents"], tokens)
+    assert list(st[:3]) == [4, 4, 4] and st[3] != 4
+    assert np.array_equal(gpu["seq_status"], st)
+    assert np.array_equal(gpu["accepted_len"], acc)
+    assert np.array_equal(gpu["out_tokens"], toks) and np.array_equal(gpu["out_nodes"], nodes)
+
+
 def test_tree_bad_parents_and_tokens():
     say("tree bad parents")
     tr = wl.tree_inputs(4, seed=5, B=4, N=20, V=2000)
