@@ -21,7 +21,7 @@
 //                   for that.
 //   greedy / tree   k_greedy_final / k_tree_final: one workgroup per sequence
 //   top-k           k_topk_rows (merge per row) -> k_topk_final (per sequence)
-//   nucleus         k_topp_rows (exact cut per row) -> k_topp_rows_exact
+//   nucleus         k_topp_rows (exact cut per row, the multi-level search inline)
 //                   (rows it could not settle) -> k_resid_s -> k_resid_final
 //   plain sampling  k_resid_s (accept step + residual mass per segment)
 //                   -> k_resid_final (draw; one workgroup per segment)
@@ -3892,21 +3892,30 @@ DEV bool topp_fast(const Params& p, const T* row, float Mrow, double Z, RowNuc* 
   return true;
 }
 
-// Nucleus cut per row: topp_fast; a row it cannot settle is left with ok =
-// kNucRetry for k_topp_rows_exact.  After k_nuc_rows (p.nucrow) it takes
-// only the rows that kernel left with ok = kNucFast, with their M and Z, and
-// every other workgroup returns at once.
-constexpr int kNucRetry = 3;
+// Nucleus cut per row: topp_fast, and for a row it cannot settle (window
+// overflow, or the cut outside the window: rare) the multi-level exact
+// search in the same workgroup, so the chain has no launch that almost
+// always has nothing to do.  After k_nuc_rows (p.nucrow) it takes only the
+// rows that kernel left with ok = kNucFast, with their M and Z, and every
+// other workgroup returns at once.
 constexpr int kNucFast = 4;
 
 template <typename T>
 __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
   const int grow = blockIdx.x;
   const T* row = row_ptr<T>(p, grow);
-  __shared__ float hist[kFastBins];
+  // the fast pass's histogram and the search's two histograms share their
+  // LDS: the search starts after a barrier that ends the fast pass
+  __shared__ uint64_t pool[kNucBins + kNucBins / 2];
+  static_assert(kFastBins * sizeof(float) <= sizeof(pool) &&
+                kNucBins * (sizeof(unsigned long long) + sizeof(unsigned)) <= sizeof(pool), "shared histograms");
+  float* hist = reinterpret_cast<float*>(pool);
+  unsigned long long* hq = reinterpret_cast<unsigned long long*>(pool);
+  unsigned* hc = reinterpret_cast<unsigned*>(pool + kNucBins);
   __shared__ uint64_t win[kWindowCap];
   __shared__ float aq[kWaves * 128];
   __shared__ double red[kWaves];
+  __shared__ unsigned long long redu[2 * kWaves];
   __shared__ int redi[2 * kWaves];
   __shared__ int wcnt;
   __shared__ float sh_M;
@@ -3927,28 +3936,11 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
     }
   }
   out.N = 0.0; out.cut = 0ull;
-  if (!topp_fast<T>(p, row, out.M, out.Z, &out, hist, win, aq, red, redi, &wcnt, grow * 7))
-    out.ok = kNucRetry;
-  if (threadIdx.x == 0) p.nuc[grow] = out;
-}
-
-// The multi-level exact search for the rows k_topp_rows left to it (rare);
-// every other workgroup returns at once.
-template <typename T>
-__global__ __launch_bounds__(kBlock) void k_topp_rows_exact(Params p) {
-  const int grow = blockIdx.x;
-  RowNuc out = p.nuc[grow];
-  if (out.ok != kNucRetry) return;
-  const T* row = row_ptr<T>(p, grow);
-  __shared__ unsigned long long hq[kNucBins];
-  __shared__ unsigned int hc[kNucBins];
-  __shared__ uint64_t win[kWindowCap];
-  __shared__ double red[kWaves];
-  __shared__ unsigned long long redu[2 * kWaves];
-  __shared__ int redi[2 * kWaves];
-  __shared__ int wcnt;
-  out.N = 0.0; out.cut = 0ull; out.ok = 0;
-  topp_search<T>(p, row, out.M, out.Z, &out, hq, hc, win, red, redu, redi, &wcnt);
+  if (!topp_fast<T>(p, row, out.M, out.Z, &out, hist, win, aq, red, redi, &wcnt, grow * 7)) {
+    __syncthreads();
+    out.N = 0.0; out.cut = 0ull; out.ok = 0;
+    topp_search<T>(p, row, out.M, out.Z, &out, hq, hc, win, red, redu, redi, &wcnt);
+  }
   if (threadIdx.x == 0) p.nuc[grow] = out;
 }
 
@@ -4675,7 +4667,6 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st, hip
       break;
     case kFiltTopp:
       run(false, k_topp_rows<T>, gr, p);
-      run(false, k_topp_rows_exact<T>, gr, p);
       run(false, k_resid_s<T, kFiltTopp>, dim3((unsigned)((p.S2 + p.rgrp - 1) / p.rgrp), (unsigned)p.B), p);
       run(true, k_resid_final<T, kFiltTopp>, (p.resid_probs || p.keep_w) ? gs : gb1, p);
       break;
@@ -4688,7 +4679,6 @@ static hipError_t launch_finish_t(const Params& p, int filt, hipStream_t st, hip
           run(false, k_topk_rows<T>, gr, p);
       } else if (p.top_p < 1.0) {
         run(false, k_topp_rows<T>, gr, p);
-        run(false, k_topp_rows_exact<T>, gr, p);
       }
       const int passes = p.k - 1 < kTreePasses ? p.k - 1 : kTreePasses;
       for (int m = 0; m < passes; ++m) {
