@@ -1,6 +1,7 @@
 // C ABI of the verification library: argument validation (host only, before
 // any HIP call), workspace ownership, and the launch sequence per mode.
 
+#include <limits.h>
 #include <math.h>
 #include <stdlib.h>
 #include <string.h>
@@ -102,14 +103,17 @@ Plan make_plan(const sv_config* c) {
 }
 
 struct Layout {
-  size_t tiles, cand, nuc, nucc, row_lx, seq, spart, wpart, tpart, tview, tcut, go;
+  size_t tiles, cand, nuc, nucc, nucm, nuck, row_lx, seq, spart, wpart, tpart, tview, tcut, go;
   size_t k_idx, k_e, k_cnt, k_norm, k_bad, k_px, total;
-  int nuc_slots;   // candidate buffers of k_nuc_rows (its most workgroups)
+  int nuc_slots;   // candidate buffers of k_nuc_rows (its most workgroups, or one per row)
+  bool nuc_keep;   // one buffer per row: the residual kernel reads the target rows' candidates
 };
 
 // The workspace of a call of up to c->max_batch sequences.  nuc_cap bounds the
 // candidate buffers of k_nuc_rows (fewer buffers: fewer resident workgroups).
-Layout layout(const sv_config* c, const Plan& pl, int nuc_cap = sv::kNucGridMax) {
+int nuc_rounds(const sv_config* c) { return (c->vocab + sv::kNucRoundLogits - 1) / sv::kNucRoundLogits; }
+
+Layout layout(const sv_config* c, const Plan& pl, int nuc_cap = INT_MAX) {
   const size_t B = (size_t)c->max_batch;
   const size_t rows = B * (size_t)(pl.rows_t + pl.rows_d);
   const size_t K = (size_t)pl.top_k;
@@ -126,6 +130,10 @@ Layout layout(const sv_config* c, const Plan& pl, int nuc_cap = sv::kNucGridMax)
   L.nuc = take(pl.filt == sv::kFiltTopp || tfilt ? rows * sizeof(sv::RowNuc) : 0);
   L.nuc_slots = pl.tile_mode == sv::kModeNucRow ? (int)(rows < (size_t)nuc_cap ? rows : (size_t)nuc_cap) : 0;
   L.nucc = take((size_t)L.nuc_slots * sv::kNucSlotEntries * sizeof(uint64_t));
+  // with a buffer per row, where each round's candidates sit and whether the row was settled in place
+  L.nuc_keep = L.nuc_slots > 0 && (size_t)L.nuc_slots >= rows;
+  L.nucm = take(L.nuc_keep ? rows * (size_t)sv::kNucWaves * (size_t)nuc_rounds(c) * sizeof(uint64_t) : 0);
+  L.nuck = take(L.nuc_keep ? rows * sizeof(int32_t) : 0);
   const bool sampled = pl.filt == sv::kFiltNone || pl.filt == sv::kFiltTopp || pl.filt == sv::kFiltTreeSample;
   L.row_lx = take(sampled ? rows * sizeof(float) : 0);
   L.seq = take(sampled ? B * sizeof(sv::SeqState) : 0);
@@ -300,7 +308,11 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
   p.go = (int32_t*)(ws + L.go);
   p.nucrow = tile_mode == sv::kModeNucRow ? 1 : 0;
   p.nucc = (uint64_t*)(ws + L.nucc);
-  if (p.nucrow && p.grid > L.nuc_slots) p.grid = L.nuc_slots;   // one buffer per workgroup
+  p.nucm = (uint64_t*)(ws + L.nucm);
+  p.nuck = (int32_t*)(ws + L.nuck);
+  p.nuc_rounds = nuc_rounds(c);
+  p.nuc_keep = (p.nucrow && L.nuc_keep) ? 1 : 0;   // (the layout's rows: at least this call's)
+  if (p.nucrow && !p.nuc_keep && p.grid > L.nuc_slots) p.grid = L.nuc_slots;   // one buffer per workgroup
 
   const int bf16 = c->dtype == SV_DTYPE_BF16;
   hipError_t e;

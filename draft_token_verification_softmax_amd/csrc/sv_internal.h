@@ -76,13 +76,17 @@ struct SeqState {
 // whose normaliser can change a decision, float32 terms in the others).
 // Chain sampling with top-p alone takes kModeNucRow instead (rows up to
 // kNucMaxV logits): persistent workgroups read each row once and settle its
-// nucleus cut (k_nuc_rows), each with a candidate buffer of kNucSlotEntries
-// entries (8 bytes: the raw value and the index) in the workspace.
+// nucleus cut (k_nuc_rows) from the candidates it keeps in a buffer of
+// kNucSlotEntries entries (8 bytes: the raw value and the index) in the
+// workspace: one buffer per row where the workspace holds them (the residual
+// kernel then reads the target rows' kept entries there), else one per
+// workgroup.
 enum TileMode { kModeArgmax = 0, kModeTopk = 2, kModeStats64 = 3, kModeTopkFilter = 4, kModeStatsMix = 5,
                 kModeNucRow = 6 };
 constexpr int kNucMaxV = 1 << 20;        // longest rows k_nuc_rows takes (its buffer holds ~1.5% of them)
-constexpr int kNucSlotEntries = 24576;   // candidate entries per workgroup buffer (192 KB)
-constexpr int kNucGridMax = 1024;        // candidate buffers in a context's workspace (resident workgroups)
+constexpr int kNucSlotEntries = 24576;   // candidate entries per buffer (192 KB)
+constexpr int kNucWaves = 4;             // waves of a k_nuc_rows workgroup (a region of the buffer each)
+constexpr int kNucRoundLogits = 4096;    // logits a k_nuc_rows workgroup reads per round
 enum Filter { kFiltGreedy = 0, kFiltNone = 1, kFiltTopk = 2, kFiltTopp = 3, kFiltTree = 4,
               kFiltTreeSample = 5 };
 // Speculative residual passes of tree sampling: pass m (1..kTreePasses)
@@ -131,7 +135,12 @@ struct Params {
   int lazy;
   int32_t* go;       // [B] lazy: 1 if position 0 was accepted (stage 2 reads the rest)
   int nucrow;        // the nucleus rows came from k_nuc_rows (RowNuc holds M and Z of every row)
-  uint64_t* nucc;    // [grid][kNucSlotEntries] k_nuc_rows: each workgroup's candidates (value bits | index << 32)
+  uint64_t* nucc;    // [slots][kNucSlotEntries] k_nuc_rows: candidate buffers (values, then indices, 32 bits each)
+  int nuc_keep;      // one candidate buffer per row (slot = row), kept for k_resid_s; else one per workgroup
+  uint64_t* nucm;    // [rows][4 waves][nuc_rounds] with nuc_keep: where each round's candidates sit in
+                     // the wave's region (start | u0 count << 16 | count << 32)
+  int32_t* nuck;     // [rows] with nuc_keep: 1 if k_nuc_rows settled the row, so its buffer holds every kept entry
+  int nuc_rounds;    // rounds of 4096 logits per row (the nucm stride)
   // workspace
   TileStat* tiles;   // [rows][P]
   uint64_t* cand;    // [rows][S][cand_w] (top-k): each tile's candidate list

@@ -2641,6 +2641,57 @@ __global__ __launch_bounds__(kBlock) void k_topk_final(Params p) {
 //                 segment where ur * S' falls; that segment's workgroup draws
 //                 the token; all of them write resid_probs if asked.
 
+// The residual mass of segment seg of a row pair from the target row's
+// candidate buffer, for a row k_nuc_rows settled (every entry its nucleus
+// keeps is a candidate), in one wave: the segment is half u = seg % 2 of
+// round seg / 2, whose entries sit in each wave region of the buffer at the
+// place the round record gives (the first half's before the second's); each
+// kept entry's weight is the one resid_nuc_sparse gives it, with the draft's
+// logit read at its index.  Returns the segment's sum (fixed order: the
+// regions' entries in turn, 64 at a time, then the wave sum).
+template <typename T>
+DEV double resid_nuc_cand(const Params& p, int tg, const RowView& pr, const RowView& qr, bool hasq,
+                          double cs, const double* tab, int seg) {
+  constexpr int kReg = kNucSlotEntries / kNucWaves;
+  const int lane = threadIdx.x & 63, V = p.V;
+  const int r = seg >> 1, half = seg & 1;
+  const uint32_t* bval = reinterpret_cast<const uint32_t*>(p.nucc + (size_t)tg * kNucSlotEntries);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(bval, kNucSlotEntries * 4);
+  const __amdgpu_buffer_rsrc_t ri = make_rsrc(bval + kNucSlotEntries, kNucSlotEntries * 4);
+  const uint64_t ml = p.nucm[((size_t)tg * kNucWaves + (lane < kNucWaves ? lane : 0)) * p.nuc_rounds + r];
+  int st[kNucWaves], len[kNucWaves], total = 0;
+#pragma unroll
+  for (int q = 0; q < kNucWaves; ++q) {
+    const uint64_t m = read_lane(ml, q);
+    const int s0 = (int)(m & 0xffffu), c0 = (int)((m >> 16) & 0xffffu), c = (int)((m >> 32) & 0xffffu);
+    st[q] = q * kReg + s0 + (half ? c0 : 0);
+    len[q] = half ? c - c0 : c0;
+    total += len[q];
+  }
+  double t = 0.0;
+  for (int j0 = 0; j0 < total; j0 += 64) {
+    int o = j0 + lane, slot = -1;
+#pragma unroll
+    for (int q = 0; q < kNucWaves; ++q) {
+      if (slot < 0 && o < len[q]) slot = st[q] + o;
+      o -= len[q];
+    }
+    // (a lane past the segment reads past the buffer: the resource returns 0)
+    const int off = slot >= 0 ? slot * 4 : kNucSlotEntries * 4;
+    const float l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rv, off, 0, 0));
+    const int v = (int)__builtin_amdgcn_raw_buffer_load_b32(ri, off, 0, 0);
+    if (slot >= 0 && v >= 0 && v < V && pack(l, v) >= pr.cut) {
+      double w = exp2_64_l(l, cs, pr.nmc, tab) * pr.inv;
+      if (hasq) {
+        w -= prob_from(qr, cs, tab, Io<T>::at((const T*)qr.row, v), v);
+        w = w > 0.0 ? w : 0.0;
+      }
+      t += w;
+    }
+  }
+  return wave_sum(t);
+}
+
 template <typename T, int FILT>
 __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   __shared__ double vnmc[kMaxRows], vinv[kMaxRows];
@@ -2718,6 +2769,24 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   if (n < k) {
     const int rd = p.rows_t + n;
     qr = RowView{row_ptr<T>(p, drow(p, b, n)), vnmc[rd], vinv[rd], vcut[rd]};
+  }
+  if constexpr (FILT == kFiltTopp) {
+    // a target row k_nuc_rows settled: its kept entries from its candidate
+    // buffer, wave w taking segment seg0 + w (rgrp <= kWaves)
+    if (p.nuc_keep && !p.keep_w && p.nuck[trow(p, b, n)] != 0) {
+      const int w = tid >> 6, seg = seg0 + w;
+      double t = 0.0;
+      if (w < p.rgrp && seg < p.S2) t = resid_nuc_cand<T>(p, trow(p, b, n), pr, qr, n < k, cs, tab, seg);
+      if ((tid & 63) == 0 && w < p.rgrp && seg < p.S2) p.spart[(size_t)b * p.S2 + seg] = t;
+      if (tid == 0 && seg0 == 0) {
+        SeqState ss;
+        ss.nmc_p = pr.nmc; ss.inv_p = pr.inv; ss.cut_p = pr.cut;
+        ss.nmc_q = qr.nmc; ss.inv_q = qr.inv; ss.cut_q = qr.cut;
+        ss.n = n; ss.st = sh_st; ss.node = n; ss.hasq = n < k;
+        p.seq[b] = ss;
+      }
+      return;
+    }
   }
   for (int seg = seg0; seg < seg0 + p.rgrp && seg < p.S2; ++seg) {
   const int pos0 = seg * kResidSeg + tid * kVec;
@@ -3977,6 +4046,7 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
 // kNucMaxV logits take the streaming pass and the cut kernels instead.
 constexpr int kNB = 256;                      // threads per workgroup (four per CU)
 constexpr int kNW = kNB / 64;                 // its waves
+static_assert(kNW == kNucWaves, "the host sizes the round records by kNucWaves");
 constexpr int kNucRegion = kNucSlotEntries / kNW;   // candidate slots per wave (3072)
 constexpr int kNucFill = 14000;               // candidates aimed for over a row
 constexpr int kNucHist = 2048;                // bins locating the cut among the candidates
@@ -4227,6 +4297,8 @@ template <typename T>
 __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
   constexpr int U = NucShape<T>::U;
   constexpr int R = U * kNB;                  // groups per round
+  static_assert(R * kVec == kNucRoundLogits && U == 2 && kNB * kVec == kResidSeg,
+                "a round is two residual segments, its slots u = 0 and u = 1");
   __shared__ uint64_t hist[kNucHist];         // sample counts (u32), then masses, then the window
   // each wave's candidates of its last round: values, then indices, kNucStage
   // slots each and one spare slot per lane (where lanes that do not take write)
@@ -4241,15 +4313,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int V = p.V;
   const int nrows = p.B * (p.rows_t + p.rows_d);
-  // this wave's region of this workgroup's buffer; the flushes store through
-  // a buffer resource spanning the region, which drops stores past its end
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  // (the buffer: the candidates' values, then their indices, kNucSlotEntries
-  // 32-bit words each; a wave's region of each at w kNucRegion)
-  uint32_t* bval = reinterpret_cast<uint32_t*>(p.nucc + (size_t)blockIdx.x * kNucSlotEntries);
-  const uint32_t* bidx = bval + kNucSlotEntries;
-  const __amdgpu_buffer_rsrc_t rval = make_rsrc(bval + (size_t)wu * kNucRegion, kNucRegion * 4);
-  const __amdgpu_buffer_rsrc_t ridx = make_rsrc(bidx + (size_t)wu * kNucRegion, kNucRegion * 4);
   uint32_t* sv = stg[wu][0];
   uint32_t* si = stg[wu][1];
   if (tid < kExpTab) tab[tid] = kExp2Tab[tid];
@@ -4261,6 +4325,15 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
   const int nr = (ngroups + R - 1) / R;
   const int nfr = (V / kVec) / R;             // rounds of whole groups only
   for (int grow = blockIdx.x; grow < nrows; grow += gridDim.x) {
+    // this wave's region of the row's buffer (p.nuc_keep: one per row, kept
+    // for the residual kernel) or of the workgroup's; the flushes store
+    // through a buffer resource spanning the region, which drops stores past
+    // its end.  (The buffer: the candidates' values, then their indices,
+    // kNucSlotEntries 32-bit words each; a wave's region of each at w kNucRegion.)
+    uint32_t* bval = reinterpret_cast<uint32_t*>(p.nucc + (size_t)(p.nuc_keep ? grow : (int)blockIdx.x) * kNucSlotEntries);
+    const uint32_t* bidx = bval + kNucSlotEntries;
+    const __amdgpu_buffer_rsrc_t rval = make_rsrc(bval + (size_t)wu * kNucRegion, kNucRegion * 4);
+    const __amdgpu_buffer_rsrc_t ridx = make_rsrc(bidx + (size_t)wu * kNucRegion, kNucRegion * 4);
     const T* row = row_ptr<T>(p, grow);
     bool xhas;
     const int xs = __builtin_amdgcn_readfirstlane(row_token(p, grow, &xhas));   // uniform over the row
@@ -4277,6 +4350,7 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
     bool over = false;                        // a round held more than kNucStage
     float tau = -INFINITY;
     bool first = true;
+    int last_rc = 0, last_cr0 = 0;            // the last round staged, and its first half's count
     // the staged candidates of the last round to the region, entries
     // lane, lane + 64, ... (coalesced 8-byte stores; past the region dropped)
     // (the stage is the wave's own: its LDS accesses run in program order,
@@ -4287,6 +4361,13 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       for (int i = lane; i < n; i += 64) {
         __builtin_amdgcn_raw_buffer_store_b32(sv[i], rval, (cs0 + i) * 4, 0, 0);
         __builtin_amdgcn_raw_buffer_store_b32(si[i], ridx, (cs0 + i) * 4, 0, 0);
+      }
+      // where the round's entries sit: the residual kernel finds a segment's
+      // (the first or second half of a round) without reading the row
+      if (p.nuc_keep && lane == 0) {
+        const uint64_t st = (uint64_t)(cs0 < 0xffff ? cs0 : 0xffff);
+        const uint64_t c = (uint64_t)(cw - cs0 < 0xffff ? cw - cs0 : 0xffff);
+        p.nucm[((size_t)grow * kNW + wu) * p.nuc_rounds + last_rc] = st | ((uint64_t)last_cr0 << 16) | (c << 32);
       }
       cs0 = cw;
       __builtin_amdgcn_wave_barrier();
@@ -4394,9 +4475,11 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
           si[slot] = (uint32_t)mp.index(u, e);
           cr += (int)__popcll(bm);
         }
+        if (u == 0) last_cr0 = cr;              // the round's first half (its first segment) comes first
       }
       over |= cr > kNucStage;
       cw += cr;
+      last_rc = mp.r;
     }, flush);
     flush();
     // ---- settle (every early return is uniform over the workgroup)
@@ -4593,7 +4676,10 @@ __global__ __launch_bounds__(kNB, 4) void k_nuc_rows(Params p) {
       return out;
     };
     const RowNuc out = settle();
-    if (tid == 0) p.nuc[grow] = out;
+    if (tid == 0) {
+      p.nuc[grow] = out;
+      if (p.nuc_keep) p.nuck[grow] = out.ok == 1 ? 1 : 0;
+    }
     __syncthreads();   // the next row reuses hist and the buffer
   }
 }
