@@ -2636,7 +2636,9 @@ __global__ __launch_bounds__(kBlock) void k_topk_final(Params p) {
 //                 redoes its accept step (row views from the tile partials,
 //                 2k logits), then sums the residual max(0, p' - q') (or p'_k
 //                 after full acceptance) over its segment of kResidSeg
-//                 entries in float64; segment 0 publishes the sequence state.
+//                 entries in float64 (for a nucleus target row k_nuc_rows
+//                 settled, from its kept entries in the row's candidate
+//                 buffer); segment 0 publishes the sequence state.
 //   k_resid_final grid (segment, sequence): every workgroup finds S' and the
 //                 segment where ur * S' falls; that segment's workgroup draws
 //                 the token; all of them write resid_probs if asked.
@@ -4018,7 +4020,10 @@ __global__ __launch_bounds__(kBlock) void k_topp_rows(Params p) {
 //
 // k_nuc_rows: persistent workgroups of kNB threads; workgroup g takes rows
 // g, g + gridDim.x, ...  It reads each row once and settles its nucleus cut
-// from the candidates it kept in its own buffer in the workspace (the cut
+// from the candidates it kept in a buffer in the workspace, the row's own
+// where the workspace holds one per row (p.nuc_keep: each flush then also
+// records where the round's entries sit, and k_resid_s takes a settled
+// target row's kept entries from there), else the workgroup's (the cut
 // kernels above read a row twice more after the streaming pass; on this chip
 // a second sweep of a row finds nothing of the first one left in any cache).
 // The buffer, about a tenth of the row's bytes, goes to memory and is read

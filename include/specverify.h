@@ -204,10 +204,11 @@ int specverify_run(specverify_ctx* ctx, int32_t batch,
  * Arguments, outputs and errors as specverify_run, plus SV_ERR_SCRATCH when
  * the call's workspace -- specverify_workspace_bytes of cfg with max_batch set
  * to batch -- exceeds SV_STATIC_SCRATCH_BYTES (no HIP call is made then).
- * Chain sampling with top-p alone is the exception: its workspace holds one
- * 192 KB candidate buffer per workgroup of the nucleus kernel, and when they
- * do not all fit, the call runs that kernel with as many workgroups as fit
- * (the same results, fewer rows in flight).  Every call on one
+ * Chain sampling with top-p alone is the exception: its workspace holds a
+ * 192 KB candidate buffer per row of the nucleus kernel; when those do not
+ * fit, one per workgroup of that kernel, with as many workgroups as fit
+ * (the same results: fewer rows in flight, and the residual kernel reads the
+ * rows instead of the buffers).  Every call on one
  * device shares that device's array and leaves its contents behind; no
  * kernel reads workspace it has not written in the same call, so nothing
  * needs clearing between calls.  Calls that overlap in time on one device

@@ -167,6 +167,24 @@ def test_workspace_keeps_residual_weights_up_to_32_mib():
     assert all(x < y for x, y in zip(greedy, greedy[1:]))
 
 
+def test_workspace_holds_a_nucleus_candidate_buffer_per_row():
+    """Chain sampling with top-p alone: a context's workspace holds one 192 KB
+    candidate buffer per row (the residual kernel reads the target rows' kept
+    entries there), plus a record per row, wave and 4096-logit round; so it
+    grows by at least a row's buffer per row of max_batch."""
+    buf = 24576 * 8
+    def ws(max_batch, top_p=0.9):
+        return svm.specverify_workspace_bytes(make_config(SV_MODE_SAMPLE, "f32", max_batch, 4, 152064, 0.8,
+                                                          top_p=top_p))
+    rows_per_seq = 4 + 5
+    w1, w2, w256 = ws(1), ws(2), ws(256)
+    assert w2 - w1 >= rows_per_seq * buf
+    assert w256 >= 256 * rows_per_seq * buf              # workload 5: 453 MB of buffers
+    rounds = math.ceil(152064 / 4096)
+    assert w2 - w1 >= rows_per_seq * (buf + 4 * rounds * 8)
+    assert ws(256, top_p=1.0) < 256 * rows_per_seq * buf  # no nucleus, no buffers
+
+
 def test_status_strings():
     for st in (0, -1, -2, -3, -4, -5, -6, -7):
         assert svm.specverify_status_string(st).startswith("SV_")
