@@ -21,6 +21,7 @@ constexpr int kSmallTiles = 256;      // problems with fewer tiles than this tak
 constexpr int kStatsRoundsMax = 4;     // float32 sum / argmax passes: most rounds of loads per tile
 constexpr size_t kKeepBytes = 32u << 20;   // residual weights kept for the draw up to this size
 constexpr long kResidGroupWgs = 4096;      // residual workgroups that keep a launch full
+constexpr long kResidCandWgs = 1024;       // ... when each wave takes a segment from the candidate buffers
 
 struct Plan {
   int filt;        // sv::Filter
@@ -298,6 +299,15 @@ int launch_call(const sv_config* c, const Plan& pl, const Layout& L, char* ws, i
   p.rgrp = 1;
   for (int g = 4; g > 1; g >>= 1) {
     if ((long)batch * ((pl.S2_max + g - 1) / g) >= kResidGroupWgs) { p.rgrp = g; break; }
+  }
+  // the nucleus residual from the target rows' candidate buffers (a wave per
+  // segment, the setup and accept tests once per workgroup): up to 16
+  // segments per workgroup while 1024 workgroups remain (workload 5: 4864 ->
+  // 1280 workgroups, the kernels after the nucleus kernel 63 -> 58 us)
+  if (L.nuc_keep && tile_mode == sv::kModeNucRow) {
+    for (int g = 16; g > p.rgrp; g >>= 1) {
+      if ((long)batch * ((pl.S2_max + g - 1) / g) >= kResidCandWgs) { p.rgrp = g; break; }
+    }
   }
   p.k_idx = (int32_t*)(ws + L.k_idx);
   p.k_e = (double*)(ws + L.k_e);

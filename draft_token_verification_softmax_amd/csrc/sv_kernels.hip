@@ -2774,12 +2774,13 @@ __global__ __launch_bounds__(kBlock) void k_resid_s(Params p) {
   }
   if constexpr (FILT == kFiltTopp) {
     // a target row k_nuc_rows settled: its kept entries from its candidate
-    // buffer, wave w taking segment seg0 + w (rgrp <= kWaves)
+    // buffer, wave w taking segments seg0 + w, seg0 + w + kWaves, ...
     if (p.nuc_keep && !p.keep_w && p.nuck[trow(p, b, n)] != 0) {
-      const int w = tid >> 6, seg = seg0 + w;
-      double t = 0.0;
-      if (w < p.rgrp && seg < p.S2) t = resid_nuc_cand<T>(p, trow(p, b, n), pr, qr, n < k, cs, tab, seg);
-      if ((tid & 63) == 0 && w < p.rgrp && seg < p.S2) p.spart[(size_t)b * p.S2 + seg] = t;
+      const int w = tid >> 6;
+      for (int seg = seg0 + w; seg < seg0 + p.rgrp && seg < p.S2; seg += kWaves) {
+        const double t = resid_nuc_cand<T>(p, trow(p, b, n), pr, qr, n < k, cs, tab, seg);
+        if ((tid & 63) == 0) p.spart[(size_t)b * p.S2 + seg] = t;
+      }
       if (tid == 0 && seg0 == 0) {
         SeqState ss;
         ss.nmc_p = pr.nmc; ss.inv_p = pr.inv; ss.cut_p = pr.cut;
