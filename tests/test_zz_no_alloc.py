@@ -2,7 +2,11 @@
 array) against specverify_run (a context's workspace) through the C ABI.
 
 Both entry points run the same kernels on the same inputs, so their outputs
-must agree bit for bit.  Each case makes two calls in a row through the
+must agree bit for bit -- but for one case: where the static array cannot
+hold a nucleus candidate buffer per row (640 rows of 152064 logits), the
+residual kernel sums each segment's mass from the rows instead of the target
+rows' buffers, in another order, so resid_probs may differ in the last bit
+there (tokens, lengths and statuses still equal).  Each case makes two calls in a row through the
 static entry point, the second with a smaller input, so the second call
 runs on an array that still holds the first call's data.
 """
@@ -102,12 +106,15 @@ def run_context(c):
     return _host(outs)
 
 
-def _same(a, b, label):
+def _same(a, b, label, resid_rtol=0.0):
     for key in KEYS:
         if a[key] is None:
             assert b[key] is None, (label, key)
             continue
-        assert np.array_equal(a[key], b[key]), (label, key)
+        if key == "resid_probs" and resid_rtol > 0.0:
+            assert np.allclose(a[key], b[key], rtol=resid_rtol, atol=0.0), (label, key)
+        else:
+            assert np.array_equal(a[key], b[key]), (label, key)
         assert not (a[key] == -7).all(), (label, key, "not written")
 
 
@@ -116,7 +123,8 @@ CASES = {
     "top-k 50, V = 128256": lambda s: _chain_case(3, (12, 3)[s], 128256, 8, "bf16", 0.7, 50, 1.0, 62 + s),
     "nucleus 0.9, V = 152064 fp32": lambda s: _chain_case(5, (8, 2)[s], 152064, 4, "f32", 0.8, 0, 0.9, 63 + s),
     # more rows than the static array holds candidate buffers for: the static
-    # call runs the one-read nucleus kernel with fewer workgroups
+    # call runs the one-read nucleus kernel with fewer workgroups, and its
+    # residual kernel reads the rows (resid_probs to 1e-6 relative)
     "nucleus 0.9, 640 and 500 rows": lambda s: _chain_case(5, (128, 100)[s], 152064, 2, "f32", 0.8, 0, 0.9,
                                                              67 + s),
     "greedy chain": lambda s: _greedy_case((32, 5)[s], 32000, 4, 64 + s),
@@ -134,4 +142,4 @@ def test_static_entry_point_matches_context_entry_point(name):
         say("no-alloc entry point:", name, "call", s + 1, "B =", c["B"])
         got = run_static(c)
         want = run_context(c)
-        _same(got, want, f"{name}, call {s + 1}")
+        _same(got, want, f"{name}, call {s + 1}", resid_rtol=1e-6 if "640" in name else 0.0)
