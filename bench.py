@@ -127,6 +127,7 @@ class HipEvents:
 KERNEL_SOURCES = [os.path.join(ROOT, "draft_token_verification_softmax_amd", "csrc", f)
                   for f in ("sv_kernels.hip", "sv_internal.h", "sv_api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.md")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "workload5_nuc_counters.md")
 
 
 def source_code(text: str) -> str:
@@ -180,6 +181,24 @@ def measured_traffic(config):
             if kv.get("workload") == str(config) and kv.get("sources") == digest:
                 return int(kv["call_bytes"]), int(kv["stream_bytes"])
     return None, None
+
+
+def measured_valu_busy():
+    """The nucleus kernel's share of cycles in which its SIMDs issue vector
+    instructions, and its vector instructions per logit, from the committed
+    hardware-counter summary of workload 5 if it was taken on the current
+    kernel sources; else None."""
+    import re
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    text = open(COUNTERS_FILE).read()
+    dm = re.search(r"digest `([0-9a-f]+)`", text)
+    bm = re.search(r"issued vector work in\s+(\d+)% of the launch's cycles", text)
+    im = re.search(r"([0-9.]+) per logit", text)
+    if not (dm and bm and im) or dm.group(1) != kernel_digest():
+        return None
+    return {"valu_busy_frac": int(bm.group(1)) / 100.0, "valu_instructions_per_logit": float(im.group(1)),
+            "source": "rocprofv3 --pmc SQ_INSTS_VALU, GRBM_GUI_ACTIVE (profiles/workload5_nuc_counters.md)"}
 
 
 # ------------------------------------------------------------------ rocprofv3 summaries
@@ -708,7 +727,11 @@ def main():
             "bytes_algorithmic": m["alg_bytes"],
             "stream_kernel": {"name": m["stream_name"] + " (the pass that reads every logit)", "us": m["kern_us"],
                               "achieved": m["stream_achieved"], "frac": m["stream_achieved"] / PEAK_HBM_GBS,
-                              "traffic": m["stream_traffic"], "bytes_algorithmic": m["logit_bytes"]},
+                              "traffic": m["stream_traffic"], "bytes_algorithmic": m["logit_bytes"],
+                              "limiter": (dict(kind="vector ALU (float64 row-sum terms, candidate staging)",
+                                               **measured_valu_busy())
+                                          if args.config == 5 and "nuc_rows" in m["stream_name"]
+                                          and measured_valu_busy() else None)},
             "floor": {"bare_read_us": m["read_us"], "bare_read_frac": m["logit_bytes"] / (m["read_us"] * 1e-6) / 1e9
                       / PEAK_HBM_GBS, "tiny_kernel_us": m["tiny_us"],
                       "note": "bare read: specverify_read_floor over each logit tensor of the same rotating "
